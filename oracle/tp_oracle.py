@@ -1,0 +1,337 @@
+"""fp64 CPU oracle for the tensor-parallel column -> activation -> row linear pair.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of bench.py may import or call this module.  The product
+path (the HIP library and its Python binding) never touches it, and this module
+imports nothing from the product package.
+
+What it computes is the plain, *unsharded* layer in float64 (numpy, with
+scipy's erf as the one special function), plus the sharded forms written out
+step by step so that the sharding identities can be checked against the
+unsharded definition.  Inputs are taken exactly as given (the caller passes
+the values the GPU received, already rounded to the run's dtype); nothing here
+rounds to a narrower type except ``reduce_partials_fp32`` and ``to_bf16``,
+which exist to pin the fixed-order fp32 reduction bit for bit.
+
+Matrices are in math layout here: a weight ``W`` is [in x out] and a linear
+layer is ``X @ W``.  (Callers holding weights in the [out x in] storage of the
+pages' PyTorch listing pass ``W.T``.)
+
+Pages cited (titles as extracted):
+  [Blog]    page at 2kiu.com whose extracted HTML title is "企业官网建设流程全解析";
+            its body is a tensor-parallelism blog post with sections 1-6.
+  [Wiki]    "张量并行" (ai-infra-wiki).
+  [Scratch] "大模型分布式训练篇——从零实现 Tensor Para..." (makesence.top).
+  [Basics]  "Tensor Parallelism基础：模型切分原理" (bjdmk.com.cn).
+
+Pinned by tests/test_oracle_*.py (identities on integer inputs, closed forms,
+textbook values, pure-Python brute force).  Every function below is pinned;
+none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf, expit
+
+__all__ = [
+    "gelu", "silu", "linear", "mlp_gelu", "mlp_swiglu", "causal_attention",
+    "attention_block", "column_shards", "row_shards", "column_linear_sharded",
+    "row_partials", "mlp_gelu_sharded", "swiglu_fused_blocks",
+    "mlp_swiglu_sharded", "attention_block_sharded", "rs_slice",
+    "reduce_partials_fp32", "to_bf16", "attention_block_rows",
+]
+
+_SQRT2 = math.sqrt(2.0)
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# activations
+# --------------------------------------------------------------------------
+def gelu(z):
+    """GELU in its exact form z * Phi(z) = z/2 * (1 + erf(z / sqrt 2)).
+
+    [Wiki] section on the two split directions writes the MLP as GELU(XA)B
+    and names no approximation, so the exact (erf) form is used; the tanh
+    approximation is not what is computed here.
+    """
+    z = _f64(z)
+    return 0.5 * z * (1.0 + erf(z / _SQRT2))
+
+
+def silu(g):
+    """SiLU / Swish with beta = 1: g * sigmoid(g).
+
+    [Blog] section 3.2 names a SwiGLU-type MLP with gate and up branches; the
+    gate branch goes through SiLU and multiplies the up branch elementwise.
+    ``expit`` is scipy's logistic function (stable for large |g|).
+    """
+    g = _f64(g)
+    return g * expit(g)
+
+
+# --------------------------------------------------------------------------
+# unsharded layers (the definitions the sharded path must reproduce)
+# --------------------------------------------------------------------------
+def linear(X, W, bias=None):
+    """Y = X W (+ bias): the dense linear layer every split starts from
+    ([Blog] section 2.1, Y = XW with W of shape (H_in, H_out))."""
+    Y = _f64(X) @ _f64(W)
+    if bias is not None:
+        Y = Y + _f64(bias)[None, :]
+    return Y
+
+
+def mlp_gelu(X, A, a, B, b):
+    """Y = GELU(X A + a) B + b, unsharded ([Wiki] two-split section, MLP
+    formula; biases as in the [Basics] listing: one per linear layer)."""
+    Z = linear(X, A, a)
+    return linear(gelu(Z), B, b)
+
+
+def mlp_swiglu(X, Wg, Wu, Wd):
+    """Y = (SiLU(X Wg) * (X Wu)) Wd, unsharded, no biases ([Blog] section 3.2)."""
+    G = linear(X, Wg)
+    U = linear(X, Wu)
+    return linear(silu(G) * U, Wd)
+
+
+def causal_attention(Q, K, V, batch, seq, heads):
+    """Per-head causal softmax attention.
+
+    Q, K, V are [batch*seq x heads*d]; token row = b*seq + s; head h owns
+    columns h*d .. h*d+d-1.  For each (b, h): S = Q K^T / sqrt(d), entries with
+    key index > query index are masked out (the diagonal is kept), P is the
+    row softmax of S and O = P V.  Heads are concatenated back in head order.
+    The whole sequence is present for every head ([Blog] section 3.1: the
+    sequence dimension stays whole, only heads are divided).
+    """
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    T, HD = Q.shape
+    assert T == batch * seq and HD % heads == 0
+    d = HD // heads
+    O = np.empty_like(Q)
+    mask = np.triu(np.ones((seq, seq), dtype=bool), k=1)  # key > query
+    scale = 1.0 / math.sqrt(d)
+    for b in range(batch):
+        rows = slice(b * seq, (b + 1) * seq)
+        for h in range(heads):
+            cols = slice(h * d, (h + 1) * d)
+            S = (Q[rows, cols] @ K[rows, cols].T) * scale
+            S[mask] = -np.inf
+            S = S - S.max(axis=1, keepdims=True)
+            P = np.exp(S)
+            P /= P.sum(axis=1, keepdims=True)
+            O[rows, cols] = P @ V[rows, cols]
+    return O
+
+
+def attention_block(X, Wq, Wk, Wv, Wo, batch, seq, heads, bo=None):
+    """Y = Attn(X Wq, X Wk, X Wv) Wo (+ bo): QKV projection, per-head causal
+    attention, output projection ([Blog] section 3.1; [Wiki] attention
+    paragraph of the two-split section)."""
+    X = _f64(X)
+    O = causal_attention(X @ _f64(Wq), X @ _f64(Wk), X @ _f64(Wv), batch, seq, heads)
+    return linear(O, Wo, bo)
+
+
+def attention_block_rows(X, Wq, Wk, Wv, Wo, batch, seq, heads, rows, bo=None):
+    """``attention_block`` evaluated at the token rows ``rows`` only.
+
+    Output row t = b*seq + s needs the query of row t and the keys/values of
+    rows b*seq .. t; this evaluates exactly that (the same definition as
+    ``attention_block``, restricted to the requested outputs).
+    """
+    X = _f64(X)
+    Wq, Wk, Wv, Wo = map(_f64, (Wq, Wk, Wv, Wo))
+    d = Wq.shape[1] // heads
+    scale = 1.0 / math.sqrt(d)
+    rows = np.asarray(rows)
+    out = np.empty((rows.size, Wo.shape[1]))
+    kv_cache = {}
+    for n, t in enumerate(rows.tolist()):
+        b, s = divmod(t, seq)
+        if b not in kv_cache:
+            Xb = X[b * seq:(b + 1) * seq]
+            kv_cache = {b: (Xb @ Wk, Xb @ Wv)}
+        Kb, Vb = kv_cache[b]
+        q = X[t] @ Wq
+        o = np.empty(Wq.shape[1])
+        for h in range(heads):
+            c = slice(h * d, (h + 1) * d)
+            sc = (Kb[: s + 1, c] @ q[c]) * scale
+            sc = sc - sc.max()
+            p = np.exp(sc)
+            p /= p.sum()
+            o[c] = p @ Vb[: s + 1, c]
+        out[n] = o @ Wo
+        if bo is not None:
+            out[n] += _f64(bo)
+    return out
+
+
+# --------------------------------------------------------------------------
+# sharded forms (each shard's work written out, then combined)
+# --------------------------------------------------------------------------
+def column_shards(W, N):
+    """Column split: shard i holds W[:, i*out/N : (i+1)*out/N] ([Blog] 2.1,
+    its split diagram; [Basics] column-split paragraph)."""
+    W = _f64(W)
+    out = W.shape[1]
+    if out % N:
+        raise ValueError(f"output width {out} is not divisible by N={N}")
+    s = out // N
+    return [W[:, i * s:(i + 1) * s] for i in range(N)]
+
+
+def row_shards(W, N):
+    """Row split: shard i holds W[i*in/N : (i+1)*in/N, :] ([Blog] 2.2)."""
+    W = _f64(W)
+    inp = W.shape[0]
+    if inp % N:
+        raise ValueError(f"input width {inp} is not divisible by N={N}")
+    s = inp // N
+    return [W[i * s:(i + 1) * s, :] for i in range(N)]
+
+
+def column_linear_sharded(X, W, bias, N):
+    """Per-shard column outputs Y_i = X W_i + bias_i; X is replicated and
+    the bias is sliced with the columns ([Basics] listing: each rank adds
+    its own bias chunk before the gather)."""
+    Ws = column_shards(W, N)
+    bs = [None] * N
+    if bias is not None:
+        bias = _f64(bias)
+        s = bias.shape[0] // N
+        bs = [bias[i * s:(i + 1) * s] for i in range(N)]
+    return [linear(X, Wi, bi) for Wi, bi in zip(Ws, bs)]
+
+
+def row_partials(Hs, W, N):
+    """Row partials P_i = H_i W_i for input slices H_i (list, or a full
+    matrix to be split by columns) ([Blog] 2.2: every partial has the full
+    output shape and the result is their elementwise sum; [Wiki] the
+    row-split equation)."""
+    Ws = row_shards(W, N)
+    if not isinstance(Hs, (list, tuple)):
+        Hs = column_shards(Hs, N)
+    return [_f64(Hi) @ Wi for Hi, Wi in zip(Hs, Ws)]
+
+
+def _fold(parts):
+    """Left fold in shard order: ((P_0 + P_1) + P_2) + ...  (the order the
+    stand-in for the all-reduce uses)."""
+    acc = _f64(parts[0]).copy()
+    for p in parts[1:]:
+        acc = acc + _f64(p)
+    return acc
+
+
+def mlp_gelu_sharded(X, A, a, B, b, N):
+    """The paired column -> GELU -> row layer over N shards: each shard
+    applies GELU to its own intermediate slice, its row partial has the full
+    output shape, partials are summed in shard order and the row bias is
+    added once after the sum ([Blog] 2.3 and 3.2; [Wiki] one all-reduce per
+    MLP; [Basics] listing: bias after the all-reduce, once)."""
+    Hs = [gelu(Zi) for Zi in column_linear_sharded(X, A, a, N)]
+    Y = _fold(row_partials(Hs, B, N))
+    if b is not None:
+        Y = Y + _f64(b)[None, :]
+    return Y
+
+
+def swiglu_fused_blocks(Wg, Wu, N):
+    """Per-shard fused gate/up blocks [Wg_i | Wu_i] ([Blog] 3.2: gate and up
+    concatenated into one larger column-parallel matrix; the intermediate
+    must divide by N so each shard gets whole, equal gate and up slices).
+
+    Block i is [H x 2*I/N] whose first I/N columns are gate columns
+    i*I/N .. (i+1)*I/N - 1 and whose last I/N columns are the matching up
+    columns.
+    """
+    G = column_shards(Wg, N)
+    U = column_shards(Wu, N)
+    return [np.concatenate([g, u], axis=1) for g, u in zip(G, U)]
+
+
+def mlp_swiglu_sharded(X, fused_blocks, Wd, N):
+    """SwiGLU MLP over N shards from the fused per-shard blocks: shard i
+    computes SiLU(gate half) * (up half) of X @ block_i, multiplies by its
+    row block of Wd, and the partials are summed in shard order."""
+    Hs = []
+    for Fi in fused_blocks:
+        Z = linear(X, Fi)
+        s = Z.shape[1] // 2
+        Hs.append(silu(Z[:, :s]) * Z[:, s:])
+    return _fold(row_partials(Hs, Wd, N))
+
+
+def attention_block_sharded(X, Wq, Wk, Wv, Wo, batch, seq, heads, N, bo=None):
+    """Head-split attention over N shards: shard i owns whole heads
+    i*heads/N .. (i+1)*heads/N - 1, projects its own Q/K/V columns, runs
+    attention on those heads alone, multiplies its head outputs by its row
+    block of Wo, and the N partials are summed in shard order, then the
+    output bias is added once ([Blog] 3.1; [Wiki] attention paragraph)."""
+    if heads % N:
+        raise ValueError(f"heads={heads} is not divisible by N={N}")
+    hl = heads // N
+    X = _f64(X)
+    Qs, Ks, Vs = (column_shards(W, N) for W in (Wq, Wk, Wv))
+    Os = [causal_attention(X @ q, X @ k, X @ v, batch, seq, hl)
+          for q, k, v in zip(Qs, Ks, Vs)]
+    Y = _fold(row_partials(Os, Wo, N))
+    if bo is not None:
+        Y = Y + _f64(bo)[None, :]
+    return Y
+
+
+def rs_slice(Y, n_slices, r):
+    """Sequence-parallel reduce-scatter output for rank r: the r-th of
+    n_slices contiguous row blocks of the reduced output ([Blog] 4.3;
+    [Wiki] Megatron-SP section)."""
+    T = Y.shape[0]
+    if T % n_slices:
+        raise ValueError(f"T={T} is not divisible by n_slices={n_slices}")
+    s = T // n_slices
+    return Y[r * s:(r + 1) * s]
+
+
+# --------------------------------------------------------------------------
+# fixed-order fp32 reduction (for the bit-exact pin of the on-device fold)
+# --------------------------------------------------------------------------
+def to_bf16(x32: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 with round-to-nearest-even, returned as the uint16 bit
+    patterns.  The rounding itself is torch's CPU cast (a library routine)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def reduce_partials_fp32(parts, bias=None, out="f32", n_slices=1, slice_=-1):
+    """Sum of partials in fp32, left-folded in shard order, bias added once
+    after the sum, then (for out='bf16') one round-to-nearest-even cast.
+
+    This is the arithmetic of the stand-in for the row all-reduce written out
+    in the precision the device uses: each ``+`` is one IEEE fp32 addition
+    (numpy float32, round to nearest even).  ``slice_`` selects one of
+    ``n_slices`` contiguous row blocks (the reduce-scatter output).
+    Returns float32 values (out='f32') or uint16 bf16 bit patterns.
+    """
+    acc = np.array(parts[0], dtype=np.float32, copy=True)
+    for p in parts[1:]:
+        acc = acc + np.asarray(p, dtype=np.float32)
+    if bias is not None:
+        acc = acc + np.asarray(bias, dtype=np.float32)[None, :]
+    if slice_ >= 0:
+        acc = rs_slice(acc, n_slices, slice_)
+    if out == "f32":
+        return acc
+    if out == "bf16":
+        return to_bf16(acc)
+    raise ValueError(out)
