@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Throughput of the tensor-parallel linear pair on one MI355X.
+
+One step = one forward pass of the whole sublayer over one batch of seeded
+synthetic input: the column GEMM with its fused activation for every shard,
+the row partial of every shard, and the fixed-order reduction of the N
+partials (the all-reduce stand-in), or, for the attention workload, QKV
+projection, causal attention, output projection and reduction.  All N shards
+run on the one GPU.  ``--share rank`` times one rank's share instead: shard 0
+plus the reduction of a partial slab holding the other shards' partials (the
+reduce-scatter slice of rank 0 for the sequence-parallel workload).
+
+Prints ONE JSON line (rank 0): throughput in TFLOP/s (algorithmic FLOP of
+the timed work / time), the roofline of the dominant kernel measured with HIP
+events around its launches, and the fp64 CPU oracle timed on a bounded sample
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s per sharded TP MLP/attn layer fwd on 1 GPU; % of bf16 MFMA peak"
+PEAK_BF16 = 2.5e15     # dense MFMA, bf16
+PEAK_F32 = 157.3e12    # dense MFMA, fp32
+PEAK_HBM = 8.0e12      # bytes/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_work(w, name, shards_per_launch, rows_reduced):
+    """Algorithmic (flops, bytes) of ONE launch of kernel `name` for workload w:
+    every input read once and every output written once."""
+    es = 2 if w.dtype == "bf16" else 4
+    T, H, N = w.T, w.H, w.N
+    c = shards_per_launch
+    if w.kind in ("mlp_gelu", "mlp_swiglu"):
+        Fs = w.F // N
+        cols = 2 * Fs if w.kind == "mlp_swiglu" else Fs
+        if name == "mlp_column_gemm":
+            return 2.0 * T * H * cols * c, es * (T * H + c * cols * H + c * T * Fs) + (es * c * Fs if w.sigma_bias else 0)
+        if name == "mlp_row_gemm":
+            return 2.0 * T * Fs * H * c, es * (c * T * Fs + c * H * Fs) + 4 * c * T * H
+    else:
+        hl = w.heads // N
+        hd = hl * w.head_dim
+        if name == "attn_qk_gemm":
+            return 2.0 * T * H * 2 * hd * c, es * (T * H + c * 2 * hd * H + c * T * 2 * hd)
+        if name == "attn_vt_gemm":
+            return 2.0 * T * H * hd * c, es * (T * H + c * hd * H + c * T * hd)
+        if name == "attn_core":
+            return (w.batch * hl * c * 4.0 * w.head_dim * w.seq * (w.seq + 1) / 2, es * 4 * c * T * hd)
+        if name == "attn_out_gemm":
+            return 2.0 * T * hd * H * c, es * (c * T * hd + c * H * hd) + 4 * c * T * H
+    if name == "reduce_partials":
+        return 0.0, 4 * N * rows_reduced * H + es * rows_reduced * H + (es * H if w.sigma_bias else 0)
+    raise KeyError(name)
+
+
+def roofline(w, name, flops, nbytes, avg_s):
+    peak_f = PEAK_BF16 if w.dtype == "bf16" else PEAK_F32
+    t_f = flops / peak_f
+    t_b = nbytes / PEAK_HBM
+    if t_f >= t_b:
+        ach = flops / avg_s
+        return {"bound": "mfma", "achieved": round(ach / 1e12, 2), "peak": round(peak_f / 1e12, 1),
+                "unit": "TFLOP/s", "frac": round(ach / peak_f, 4)}
+    ach = nbytes / avg_s
+    return {"bound": "hbm", "achieved": round(ach / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM, 4)}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tensor_transformer_layers_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload_name, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was
+    taken on the current kernel sources; otherwise None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload_name}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, host, seconds):
+    """fp64 oracle on a bounded, seeded sample of token rows of the same
+    workload; TFLOP/s counted with the same algorithmic FLOP per row."""
+    import numpy as np
+
+    from oracle import reference as R
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    chunk = 256 if w.kind != "attn" else 8
+    order = np.random.default_rng(w.seed + 98).permutation(w.T)  # seeded order of all token rows
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    while done < w.T and time.perf_counter() - t0 < seconds:
+        rows = np.sort(order[done:done + chunk])
+        R.workload(w.kind, host, w.batch, w.seq, w.heads, rows=rows)
+        if w.kind == "attn":
+            hl_all = w.heads
+            pos = rows % w.seq
+            flops += len(rows) * 8.0 * w.H * w.H + float(np.sum(hl_all * 4.0 * w.head_dim * (pos + 1)))
+        else:
+            flops += len(rows) * w.flops_layer() / w.T
+        done += len(rows)
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {w.T} token rows (seeded), fp64 numpy/scipy, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: GELU MLP bf16, T=16384, H=512, F=2048, N=4)")
+    ap.add_argument("--share", choices=["layer", "rank"], default="layer")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (PMC traffic calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on ONE GPU (all N tensor-parallel shards on one device, "
+              "an on-device reduction standing in for the all-reduce); --gpus above 1 is not supported.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from tensor_transformer_layers_amd import configs, inputs, tp, workloads
+
+    tp.lib()  # fails loudly if libtp.so is missing
+    w = configs.CONFIGS[args.config]
+    log(f"workload {w.name}: generating seeded inputs")
+    host = inputs.make_inputs(w)
+    d = workloads.device_inputs(w, host)
+    Y, ws = workloads.forward(w, d)  # allocates Y and the workspace once
+    torch.cuda.synchronize()
+    rank_slice = 0 if w.n_slices > 1 else -1
+    Yr = None
+    if args.share == "rank":
+        rows = w.T // w.n_slices if w.n_slices > 1 else w.T
+        Yr = torch.empty((rows, w.H), dtype=Y.dtype, device=Y.device)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        if args.share == "layer":
+            workloads.forward(w, d, Y=Y, ws=ws, stream=stream)
+        else:
+            workloads.forward(w, d, ws=ws, shard_begin=0, shard_count=1, stream=stream)
+            workloads.reduce_slab(w, d, ws, Y=Yr, slice=rank_slice, stream=stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region 1: the steps alone
+    log(f"timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # timed region 2: the same steps with a HIP event pair around every kernel
+    tp.tp_timing_reset()
+    tp.tp_timing_enable(1)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    tp.tp_timing_enable(0)
+    kern = tp.tp_timing_read()
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=Y.device)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    shards = w.N if args.share == "layer" else 1
+    rows_red = w.T if (args.share == "layer" or w.n_slices == 1) else w.T // w.n_slices
+    flops = w.flops_layer() if args.share == "layer" else w.flops_shard()
+    value = flops / (ms_step / 1e3) / 1e12
+
+    kernels = {}
+    for name, (ms, n) in kern.items():
+        f, b = kernel_work(w, name, shards, rows_red)
+        avg = ms / n / 1e3
+        kernels[name] = {"avg_us": round(avg * 1e6, 2), "launches": n,
+                         "share": round(ms / sum(v[0] for v in kern.values()), 4),
+                         **roofline(w, name, f, b, avg)}
+    dom = max(kern, key=lambda k: kern[k][0])
+    f, b = kernel_work(w, dom, shards, rows_red)
+    avg = kern[dom][0] / kern[dom][1] / 1e3
+    roof = roofline(w, dom, f, b, avg)
+    src_hash = kernel_source_hash()
+    roof["kernel"] = dom
+    roof["avg_us"] = round(avg * 1e6, 2)
+    roof["algorithmic"] = {"flop": f, "bytes": b}
+    roof["traffic"] = measured_traffic(dom, w.name, src_hash)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "kind": w.kind, "tokens": w.T, "batch": w.batch, "seq": w.seq, "hidden": w.H,
+            "ffn": w.F if w.kind != "attn" else None, "heads": w.heads or None, "shards": w.N,
+            "share": "all shards + reduction" if args.share == "layer" else "rank 0 shard + reduction",
+            "reduce_scatter_slices": w.n_slices, "seed": w.seed,
+        },
+        "pct_of_bf16_mfma_peak": round(100 * value * 1e12 / PEAK_BF16, 2) if w.dtype == "bf16" else None,
+        "roofline": roof,
+        "kernels": kernels,
+        "kernel_source_hash": src_hash,
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        del d, Y, ws
+        torch.cuda.empty_cache()
+        log(f"cpu baseline: fp64 oracle for ~{args.cpu_seconds:.0f} s")
+        out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+/*
+ * tp.h -- C ABI of libtp.so: the tensor-parallel column -> activation -> row
+ * linear pair (MLP and head-split attention), N shards on one MI355X (gfx950),
+ * partial sums combined by an on-device fixed-order reduction that stands in
+ * for the all-reduce.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *   allocates, frees or keeps device memory; scratch comes from a
+ *   caller-provided workspace.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *   call only enqueues work on `stream` and returns; execution errors surface
+ *   on the caller's next synchronisation.
+ * - Matrices are row-major.  Activations are [rows x features].  Weights use
+ *   the [out x in] storage of the weight chunks in the PyTorch listing of
+ *   "Tensor Parallelism基础：模型切分原理" (section on implementation details):
+ *   a linear layer computes Y = X * W^T with W of shape [out x in].  `ld*` are
+ *   leading dimensions (row strides) in elements, so a shard may be a view
+ *   into a larger matrix.
+ * - bf16 inputs accumulate in fp32; outputs are rounded once,
+ *   round-to-nearest-even.
+ * - Every argument is validated before the first HIP call.  On error the call
+ *   returns a status, launches nothing, and tp_last_error() (thread-local)
+ *   names the offending argument and, for divisibility errors, the shard
+ *   shapes (the fail-fast divisibility check of the blog post at 2kiu.com,
+ *   section 6.1).  No call aborts or throws across the ABI.
+ * - Alignment: device pointers 16-byte aligned; bf16 leading dimensions and
+ *   contraction sizes multiples of 8 elements, fp32 ones multiples of 4.
+ * - All kernels are deterministic: no atomics, fixed summation order.
+ */
+#ifndef TP_H_
+#define TP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TP_OK = 0,
+  TP_ERR_NULL = 1,          /* a required pointer is NULL                  */
+  TP_ERR_SHAPE = 2,         /* negative/zero size, ld too small, bad slice */
+  TP_ERR_DIVISIBILITY = 3,  /* F, heads or T not divisible as required     */
+  TP_ERR_DTYPE = 4,         /* dtype/activation combination not supported  */
+  TP_ERR_ALIGN = 5,         /* pointer or ld alignment                     */
+  TP_ERR_WORKSPACE = 6,     /* workspace NULL or too small                 */
+  TP_ERR_HIP = 7            /* a HIP launch failed                         */
+} tp_status;
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+typedef enum { TP_ACT_NONE = 0, TP_ACT_GELU = 1, TP_ACT_SWIGLU = 2 } tp_act;
+
+/*
+ * Column-parallel linear for one shard:  Y_i = act(X * W_i^T + bias_i).
+ * Column split of "Tensor Parallelism基础：模型切分原理" (column-wise splitting)
+ * and of the 2kiu.com blog post, section 2.1: X is replicated, shard i holds
+ * output features i*F/N .. (i+1)*F/N - 1, the bias is sliced with them and is
+ * added before the activation.  Concatenating the N outputs along features
+ * (the all-gather) is a matter of layout: pass Y_i = Y + i*Ns with ldy = F.
+ *
+ *   X    [T x K]  (ldx)        dt
+ *   W_i  NONE/GELU:  [Ns x K]  (ldw)            dt
+ *        SWIGLU:     [2Ns x K] (ldw): rows 0..Ns-1 gate, Ns..2Ns-1 up
+ *   bias_i [Ns] or NULL (must be NULL for SWIGLU)   dt
+ *   Y_i  [T x Ns] (ldy)        dt
+ * act: GELU = x*Phi(x) (erf form); SWIGLU = SiLU(gate) * up (bf16 only).
+ * T == 0 is a no-op.
+ */
+tp_status tp_column_linear(void* stream, tp_dtype dt, tp_act act, int64_t T, int64_t K,
+                           int64_t Ns, const void* X, int64_t ldx, const void* W_i,
+                           int64_t ldw, const void* bias_i, void* Y_i, int64_t ldy);
+
+/*
+ * Row-parallel partial product for one shard:  P_i = X_i * W_i^T  (fp32 out,
+ * never a bias: the row bias is added once, after the sum; the listing of
+ * "Tensor Parallelism基础" adds it after the all-reduce).  Row split of the
+ * 2kiu.com blog post, section 2.2: every partial has the full output shape.
+ *
+ *   X_i  [T x Ks] (ldx)          dt
+ *   W_i  [Nout x Ks] (ldw)       dt   (shard i's column block of the [H x F]
+ *                                      out-in matrix: W + i*Ks, ldw = F)
+ *   P_i  [T x Nout] (ldp)        fp32
+ */
+tp_status tp_row_linear_partial(void* stream, tp_dtype dt, int64_t T, int64_t Ks,
+                                int64_t Nout, const void* X_i, int64_t ldx, const void* W_i,
+                                int64_t ldw, float* P_i, int64_t ldp);
+
+/*
+ * The all-reduce stand-in:  Y = (((P_0 + P_1) + ...) + P_{n-1}) + bias, each
+ * + one fp32 IEEE addition in shard order, then one round-to-nearest-even cast
+ * to out_dt.  Row-split sum of the 2kiu.com blog post (section 2.2) and of
+ * "张量并行" (row-split equation); bias once, after the sum.
+ *
+ *   P      n_parts partials, partial k at P + k*part_stride, each [T x H], ld = H
+ *   bias   [H] in out_dt, or NULL
+ *   n_slices >= 1, slice in [-1, n_slices): slice == -1 writes all T rows to
+ *          Y [T x H]; slice == r writes only rows r*T/n .. (r+1)*T/n - 1 to
+ *          Y [T/n x H] -- the reduce-scatter along the sequence of Megatron-SP
+ *          ("张量并行", sequence section; blog post section 4.3).
+ * H must be a multiple of 8; T a multiple of n_slices.
+ */
+tp_status tp_reduce_partials(void* stream, tp_dtype out_dt, int n_parts, int64_t T, int64_t H,
+                             const float* P, int64_t part_stride, const void* bias, void* Y,
+                             int n_slices, int slice);
+
+/* Whole MLP sublayer over shards [shard_begin, shard_begin + shard_count). */
+typedef struct {
+  tp_dtype dt;      /* TP_F32 or TP_BF16 (inputs, intermediate and output)      */
+  tp_act act;       /* TP_ACT_GELU (or NONE) with A [F x H]; TP_ACT_SWIGLU with */
+                    /* A = N fused blocks [2F/N x H]: gate rows then up rows    */
+  int64_t T, H, F;  /* tokens, hidden, intermediate (SWIGLU: intermediate size) */
+  int N, shard_begin, shard_count;
+  const void* X;    /* [T x H]                                                  */
+  const void* A;    /* column weight, see act                                   */
+  const void* a;    /* [F] column bias or NULL                                  */
+  const void* B;    /* [H x F] row weight (out-in); shard i = columns i*F/N..   */
+  const void* b;    /* [H] row bias or NULL (added once, after the sum)         */
+  void* Y;          /* [T x H], or [T/n_slices x H] when slice >= 0             */
+  int n_slices, slice;
+} tp_mlp_desc;
+
+/* Whole attention sublayer over shards [shard_begin, shard_begin + shard_count).
+ * Shard i owns whole heads i*heads/N .. (i+1)*heads/N - 1 (2kiu.com post,
+ * section 3.1).  Token row = b*seq + s.  bf16 only, head_dim == 128,
+ * seq a multiple of 128. */
+typedef struct {
+  tp_dtype dt;
+  int64_t batch, seq, hidden;
+  int heads, head_dim, N, shard_begin, shard_count;
+  const void* X;    /* [batch*seq x hidden]                                      */
+  const void* Wqkv; /* N blocks [3*(heads/N)*head_dim x hidden]: Q rows, K rows, */
+                    /* V rows of the shard's heads, in head order                */
+  const void* Wo;   /* [hidden x hidden] out-in; shard i = columns i*hidden/N..  */
+  const void* bo;   /* [hidden] or NULL                                          */
+  void* Y;          /* [batch*seq x hidden] (or one slice, as for the MLP)       */
+  int n_slices, slice;
+} tp_attn_desc;
+
+/* Workspace bytes needed by tp_mlp_forward / tp_attn_forward for this desc.
+ * Layout: the fp32 partial slab comes first (slot i = shard i, each
+ * [T x H]); tp_*_partials_offset returns its byte offset.  Returns 0 when
+ * the descriptor is invalid (see tp_last_error). */
+size_t tp_mlp_workspace_size(const tp_mlp_desc* d);
+size_t tp_attn_workspace_size(const tp_attn_desc* d);
+size_t tp_mlp_partials_offset(const tp_mlp_desc* d);
+size_t tp_attn_partials_offset(const tp_attn_desc* d);
+
+/*
+ * Column GEMM (+bias, activation) and row partial of every shard in range,
+ * then -- when the range covers all N shards -- the fixed-order reduction
+ * into Y.  With shard_count < N the partials stay in the workspace slab
+ * (slot i = shard i) and Y is untouched: one rank's share is its shard plus a
+ * tp_reduce_partials over the slab.  The pairing (column output slice is the
+ * row input slice, one reduction per sublayer) is section 2.3 of the 2kiu.com
+ * post and the MLP paragraph of "张量并行".
+ */
+tp_status tp_mlp_forward(void* stream, const tp_mlp_desc* d, void* ws, size_t ws_bytes);
+
+/* QKV projection of the shard's heads, causal softmax attention per local
+ * head (scale 1/sqrt(head_dim), diagonal kept), row-parallel output
+ * projection into the partial slab, then the reduction as for the MLP. */
+tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t ws_bytes);
+
+/*
+ * Local causal attention alone (the middle step of tp_attn_forward), for
+ * `heads` heads of width 128 over `batch` sequences of length `seq`:
+ *   QK  [batch*seq x ldqk]: head h's query at columns h*128.., its key at
+ *       columns k_col0 + h*128..
+ *   Vt  [heads*128 x ldvt]: V transposed; row h*128+d, column b*seq+s
+ *   O   [batch*seq x ldo]: head h at columns h*128..
+ */
+tp_status tp_attn_local(void* stream, int64_t batch, int64_t seq, int heads, int head_dim,
+                        const void* QK, int64_t ldqk, int64_t k_col0, const void* Vt,
+                        int64_t ldvt, void* O, int64_t ldo);
+
+/*
+ * Per-kernel timing, for measurement (the pages read the share of time each
+ * kernel takes from a profiler: "大模型分布式训练篇——从零实现 Tensor Para...",
+ * section on practical advice).  While enabled, every kernel launch made by
+ * the entry points above is bracketed by a HIP event pair recorded on the
+ * caller's stream (no other effect on the work).  tp_timing_read waits for the
+ * recorded events, adds their durations into per-kernel totals and copies up
+ * to `max` of them (names stay valid until the next read; any output pointer
+ * may be NULL); it returns the number of kernels with totals.
+ * tp_timing_reset discards pending events and totals.
+ */
+tp_status tp_timing_enable(int on);
+int tp_timing_read(int max, const char** names, double* total_ms, int64_t* launches);
+void tp_timing_reset(void);
+
+const char* tp_status_string(tp_status s);
+const char* tp_last_error(void);
+/* Library version string (build id); never NULL. */
+const char* tp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TP_H_ */

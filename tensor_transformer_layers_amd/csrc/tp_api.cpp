@@ -1,0 +1,596 @@
+// C ABI of libtp: argument validation, workspace layout and kernel dispatch.
+// Every check runs before the first HIP call, so a rejected call launches
+// nothing (and never touches the GPU).
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/tp.h"
+#include "tp_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+tp_status fail(tp_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+tp_status ok() {
+  g_err.clear();
+  return TP_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t vec_of(tp_dtype dt) { return dt == TP_BF16 ? 8 : 4; }
+size_t esize(tp_dtype dt) { return dt == TP_BF16 ? 2 : 4; }
+const char* dt_name(tp_dtype dt) { return dt == TP_BF16 ? "bf16" : "f32"; }
+
+constexpr int64_t kIntMax = 0x7fffffff;
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("TP_LOG");
+    return e && *e && *e != '0';
+  }();
+  return on;
+}
+
+// ------------------------------------------------------------ kernel timing
+// When enabled, each kernel launch below is bracketed by a HIP event pair on
+// the launching stream; tp_timing_read() resolves the pairs into per-kernel
+// totals.  Off by default: no events are created or recorded.
+struct PendingPair {
+  std::string name;
+  hipEvent_t a, b;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<PendingPair> g_pending;
+std::vector<hipEvent_t> g_event_pool;
+std::map<std::string, std::pair<double, int64_t>> g_totals;
+std::vector<std::string> g_names;  // storage for tp_timing_read's name pointers
+
+hipEvent_t pooled_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct KernelTimer {
+  const char* name;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  KernelTimer(const char* n, hipStream_t st) : name(n), s(st) {
+    std::lock_guard<std::mutex> g(g_tmu);
+    if (!g_timing) return;
+    a = pooled_event();
+    if (a) hipEventRecord(a, s);
+  }
+  void stop() {
+    if (!a) return;
+    std::lock_guard<std::mutex> g(g_tmu);
+    hipEvent_t b = pooled_event();
+    if (!b) return;
+    hipEventRecord(b, s);
+    g_pending.push_back({name, a, b});
+    a = nullptr;
+  }
+};
+
+tp_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+tp_status check_dtype(tp_dtype dt) {
+  if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_DTYPE, "dtype %d is not TP_F32 or TP_BF16", (int)dt);
+  return TP_OK;
+}
+
+// One GEMM operand: rows x cols view with leading dimension ld.
+tp_status check_matrix(const char* name, const void* p, int64_t rows, int64_t cols, int64_t ld,
+                       int64_t vec) {
+  if (!p) return fail(TP_ERR_NULL, "%s is NULL", name);
+  if (ld < cols) return fail(TP_ERR_SHAPE, "%s: leading dimension %lld < %lld columns", name, (long long)ld,
+                             (long long)cols);
+  if (!aligned16(p)) return fail(TP_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  if (ld % vec) return fail(TP_ERR_ALIGN, "%s: leading dimension %lld is not a multiple of %lld", name,
+                            (long long)ld, (long long)vec);
+  if (rows > kIntMax || cols > kIntMax) return fail(TP_ERR_SHAPE, "%s: dimension exceeds 2^31-1", name);
+  return TP_OK;
+}
+
+#define TP_TRY(x)                 \
+  do {                            \
+    tp_status s_ = (x);           \
+    if (s_ != TP_OK) return s_;   \
+  } while (0)
+
+tp_status check_slices(int64_t T, int n_slices, int slice) {
+  if (n_slices < 1) return fail(TP_ERR_SHAPE, "n_slices %d < 1", n_slices);
+  if (slice < -1 || slice >= n_slices)
+    return fail(TP_ERR_SHAPE, "slice %d outside [-1, %d)", slice, n_slices);
+  if (T % n_slices)
+    return fail(TP_ERR_DIVISIBILITY, "T=%lld tokens do not split into %d sequence slices", (long long)T,
+                n_slices);
+  return TP_OK;
+}
+
+tp_status validate_reduce(tp_dtype out_dt, int n_parts, int64_t T, int64_t H, const float* P,
+                          int64_t part_stride, const void* bias, const void* Y, int n_slices, int slice) {
+  TP_TRY(check_dtype(out_dt));
+  if (n_parts < 1 || n_parts > 1024) return fail(TP_ERR_SHAPE, "n_parts %d outside [1, 1024]", n_parts);
+  if (T < 0 || H <= 0) return fail(TP_ERR_SHAPE, "T=%lld, H=%lld", (long long)T, (long long)H);
+  if (H % 8) return fail(TP_ERR_ALIGN, "H=%lld is not a multiple of 8", (long long)H);
+  TP_TRY(check_slices(T, n_slices, slice));
+  if (T == 0) return TP_OK;  // empty input: nothing to read or write
+  if (!P) return fail(TP_ERR_NULL, "P is NULL");
+  if (!Y) return fail(TP_ERR_NULL, "Y is NULL");
+  if (!aligned16(P) || !aligned16(Y)) return fail(TP_ERR_ALIGN, "P or Y is not 16-byte aligned");
+  if (bias && !aligned16(bias)) return fail(TP_ERR_ALIGN, "bias is not 16-byte aligned");
+  if (n_parts > 1 && part_stride < T * H)
+    return fail(TP_ERR_SHAPE, "part_stride %lld < T*H = %lld (partials overlap)", (long long)part_stride,
+                (long long)(T * H));
+  if (part_stride % 4) return fail(TP_ERR_ALIGN, "part_stride %lld is not a multiple of 4", (long long)part_stride);
+  return TP_OK;
+}
+
+tp_status run_reduce(hipStream_t s, tp_dtype out_dt, int n_parts, int64_t T, int64_t H, const float* P,
+                     int64_t part_stride, const void* bias, void* Y, int n_slices, int slice) {
+  tp::ReduceParams r{};
+  r.P = P;
+  r.part_stride = part_stride;
+  r.n_parts = n_parts;
+  r.H = H;
+  r.rows = slice < 0 ? T : T / n_slices;
+  r.row0 = slice < 0 ? 0 : (int64_t)slice * (T / n_slices);
+  r.bias = bias;
+  r.Y = Y;
+  KernelTimer kt("reduce_partials", s);
+  const hipError_t e = tp::launch_reduce(r, out_dt == TP_BF16, s);
+  kt.stop();
+  return hip_status(e, "reduce_partials launch");
+}
+
+tp::GemmParams gemm(const void* A, int64_t lda, int64_t sA, const void* B, int64_t ldb, int64_t sB, void* C,
+                    int64_t ldc, int64_t sC, int64_t M, int64_t N, int64_t K, int batch) {
+  tp::GemmParams p{};
+  p.A = A;
+  p.lda = lda;
+  p.sA = sA;
+  p.B = B;
+  p.ldb = ldb;
+  p.sB = sB;
+  p.C = C;
+  p.ldc = ldc;
+  p.sC = sC;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.batch = batch;
+  return p;
+}
+
+hipError_t launch(const char* name, tp_dtype dt, const tp::GemmParams& p, tp::Epilogue e, hipStream_t s) {
+  KernelTimer kt(name, s);
+  const hipError_t r = dt == TP_BF16 ? tp::launch_gemm_bf16(p, e, s) : tp::launch_gemm_f32(p, e, s);
+  kt.stop();
+  return r;
+}
+
+// ------------------------------------------------------------------ MLP desc
+struct MlpShape {
+  int64_t Fs;        // intermediate per shard
+  int64_t a_rows;    // rows of one shard's column weight block
+  size_t p_bytes;    // fp32 partial slab (N slots)
+  size_t h_offset;   // intermediate slab offset
+  size_t h_bytes;
+  size_t total;
+};
+
+tp_status validate_mlp(const tp_mlp_desc* d, MlpShape* sh) {
+  if (!d) return fail(TP_ERR_NULL, "descriptor is NULL");
+  TP_TRY(check_dtype(d->dt));
+  if (d->act != TP_ACT_NONE && d->act != TP_ACT_GELU && d->act != TP_ACT_SWIGLU)
+    return fail(TP_ERR_DTYPE, "activation %d unknown", (int)d->act);
+  if (d->act == TP_ACT_SWIGLU && d->dt != TP_BF16) return fail(TP_ERR_DTYPE, "SwiGLU path is bf16-only");
+  if (d->act == TP_ACT_SWIGLU && d->a) return fail(TP_ERR_SHAPE, "SwiGLU column bias must be NULL");
+  if (d->T < 0 || d->H <= 0 || d->F <= 0 || d->N <= 0)
+    return fail(TP_ERR_SHAPE, "T=%lld H=%lld F=%lld N=%d", (long long)d->T, (long long)d->H, (long long)d->F,
+                d->N);
+  if (d->F % d->N)
+    return fail(TP_ERR_DIVISIBILITY,
+                "intermediate F=%lld is not divisible by N=%d shards (shard would be %lld + %lld/%d columns)",
+                (long long)d->F, d->N, (long long)(d->F / d->N), (long long)(d->F % d->N), d->N);
+  if (d->shard_begin < 0 || d->shard_count < 1 || d->shard_begin + d->shard_count > d->N)
+    return fail(TP_ERR_SHAPE, "shard range [%d, %d) outside [0, %d)", d->shard_begin,
+                d->shard_begin + d->shard_count, d->N);
+  TP_TRY(check_slices(d->T, d->n_slices, d->slice));
+  const int64_t vec = vec_of(d->dt);
+  const int64_t Fs = d->F / d->N;
+  if (d->T == 0) {  // empty input: nothing to read, write or stage
+    sh->Fs = Fs;
+    sh->a_rows = d->act == TP_ACT_SWIGLU ? 2 * Fs : Fs;
+    sh->p_bytes = sh->h_offset = sh->h_bytes = sh->total = 0;
+    return TP_OK;
+  }
+  if (d->H % 8) return fail(TP_ERR_ALIGN, "hidden H=%lld is not a multiple of 8", (long long)d->H);
+  if (Fs % vec)
+    return fail(TP_ERR_ALIGN, "shard width F/N=%lld is not a multiple of %lld (%s)", (long long)Fs,
+                (long long)vec, dt_name(d->dt));
+  const int64_t a_rows = d->act == TP_ACT_SWIGLU ? 2 * Fs : Fs;
+  TP_TRY(check_matrix("X", d->X, d->T, d->H, d->H, vec));
+  TP_TRY(check_matrix("A", d->A, a_rows * d->N, d->H, d->H, vec));
+  TP_TRY(check_matrix("B", d->B, d->H, d->F, d->F, vec));
+  if (d->a && !aligned16(d->a)) return fail(TP_ERR_ALIGN, "a is not 16-byte aligned");
+  if (d->b && !aligned16(d->b)) return fail(TP_ERR_ALIGN, "b is not 16-byte aligned");
+  if (d->shard_count == d->N) {
+    if (!d->Y) return fail(TP_ERR_NULL, "Y is NULL");
+    if (!aligned16(d->Y)) return fail(TP_ERR_ALIGN, "Y is not 16-byte aligned");
+  }
+  if (d->T > kIntMax) return fail(TP_ERR_SHAPE, "T exceeds 2^31-1");
+  sh->Fs = Fs;
+  sh->a_rows = a_rows;
+  sh->p_bytes = align256((size_t)d->N * d->T * d->H * sizeof(float));
+  sh->h_offset = sh->p_bytes;
+  sh->h_bytes = align256((size_t)d->shard_count * d->T * Fs * esize(d->dt));
+  sh->total = sh->h_offset + sh->h_bytes;
+  return TP_OK;
+}
+
+// ------------------------------------------------------------ attention desc
+struct AttnShape {
+  int64_t T, hl, hd;  // tokens, local heads, local width hl*head_dim
+  size_t p_bytes, qk_off, vt_off, o_off, total;
+};
+
+tp_status validate_attn(const tp_attn_desc* d, AttnShape* sh) {
+  if (!d) return fail(TP_ERR_NULL, "descriptor is NULL");
+  TP_TRY(check_dtype(d->dt));
+  if (d->dt != TP_BF16) return fail(TP_ERR_DTYPE, "attention path is bf16-only");
+  if (d->batch < 0 || d->seq < 0 || d->hidden <= 0 || d->heads <= 0 || d->N <= 0)
+    return fail(TP_ERR_SHAPE, "batch=%lld seq=%lld hidden=%lld heads=%d N=%d", (long long)d->batch,
+                (long long)d->seq, (long long)d->hidden, d->heads, d->N);
+  if (d->head_dim != 128) return fail(TP_ERR_SHAPE, "head_dim=%d (only 128 is built)", d->head_dim);
+  if ((int64_t)d->heads * d->head_dim != d->hidden)
+    return fail(TP_ERR_SHAPE, "heads*head_dim=%lld != hidden=%lld", (long long)d->heads * d->head_dim,
+                (long long)d->hidden);
+  if (d->heads % d->N)
+    return fail(TP_ERR_DIVISIBILITY, "heads=%d are not divisible by N=%d shards (whole heads per shard)",
+                d->heads, d->N);
+  if (d->seq % 128) return fail(TP_ERR_SHAPE, "seq=%lld is not a multiple of 128", (long long)d->seq);
+  if (d->shard_begin < 0 || d->shard_count < 1 || d->shard_begin + d->shard_count > d->N)
+    return fail(TP_ERR_SHAPE, "shard range [%d, %d) outside [0, %d)", d->shard_begin,
+                d->shard_begin + d->shard_count, d->N);
+  const int64_t T = d->batch * d->seq;
+  TP_TRY(check_slices(T, d->n_slices, d->slice));
+  const int64_t hl = d->heads / d->N, hd = hl * d->head_dim;
+  if (T == 0) {  // empty input: nothing to read, write or stage
+    sh->T = 0;
+    sh->hl = hl;
+    sh->hd = hd;
+    sh->p_bytes = sh->qk_off = sh->vt_off = sh->o_off = sh->total = 0;
+    return TP_OK;
+  }
+  TP_TRY(check_matrix("X", d->X, T, d->hidden, d->hidden, 8));
+  TP_TRY(check_matrix("Wqkv", d->Wqkv, 3 * hd * d->N, d->hidden, d->hidden, 8));
+  TP_TRY(check_matrix("Wo", d->Wo, d->hidden, d->hidden, d->hidden, 8));
+  if (d->bo && !aligned16(d->bo)) return fail(TP_ERR_ALIGN, "bo is not 16-byte aligned");
+  if (d->shard_count == d->N) {
+    if (!d->Y) return fail(TP_ERR_NULL, "Y is NULL");
+    if (!aligned16(d->Y)) return fail(TP_ERR_ALIGN, "Y is not 16-byte aligned");
+  }
+  if (T > kIntMax) return fail(TP_ERR_SHAPE, "batch*seq exceeds 2^31-1");
+  const size_t c = (size_t)d->shard_count;
+  sh->T = T;
+  sh->hl = hl;
+  sh->hd = hd;
+  sh->p_bytes = align256((size_t)d->N * T * d->hidden * sizeof(float));
+  sh->qk_off = sh->p_bytes;
+  sh->vt_off = sh->qk_off + align256(c * T * 2 * hd * 2);
+  sh->o_off = sh->vt_off + align256(c * hd * T * 2);
+  sh->total = sh->o_off + align256(c * T * hd * 2);
+  return TP_OK;
+}
+
+tp_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return fail(TP_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned16(ws)) return fail(TP_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tp_status tp_column_linear(void* stream, tp_dtype dt, tp_act act, int64_t T, int64_t K, int64_t Ns,
+                           const void* X, int64_t ldx, const void* W_i, int64_t ldw, const void* bias_i,
+                           void* Y_i, int64_t ldy) {
+  TP_TRY(check_dtype(dt));
+  if (act != TP_ACT_NONE && act != TP_ACT_GELU && act != TP_ACT_SWIGLU)
+    return fail(TP_ERR_DTYPE, "activation %d unknown", (int)act);
+  if (act == TP_ACT_SWIGLU && dt != TP_BF16) return fail(TP_ERR_DTYPE, "SwiGLU path is bf16-only");
+  if (act == TP_ACT_SWIGLU && bias_i) return fail(TP_ERR_SHAPE, "SwiGLU bias must be NULL");
+  if (T < 0 || K <= 0 || Ns <= 0)
+    return fail(TP_ERR_SHAPE, "T=%lld K=%lld Ns=%lld", (long long)T, (long long)K, (long long)Ns);
+  const int64_t vec = vec_of(dt);
+  if (K % vec) return fail(TP_ERR_ALIGN, "K=%lld is not a multiple of %lld", (long long)K, (long long)vec);
+  if (T == 0) return ok();  // empty input: nothing to read or write
+  TP_TRY(check_matrix("X", X, T, K, ldx, vec));
+  TP_TRY(check_matrix("W_i", W_i, act == TP_ACT_SWIGLU ? 2 * Ns : Ns, K, ldw, vec));
+  if (!Y_i) return fail(TP_ERR_NULL, "Y_i is NULL");
+  if (ldy < Ns) return fail(TP_ERR_SHAPE, "ldy %lld < Ns %lld", (long long)ldy, (long long)Ns);
+  if (T > kIntMax || (act == TP_ACT_SWIGLU ? 2 * Ns : Ns) > kIntMax) return fail(TP_ERR_SHAPE, "size exceeds 2^31-1");
+  if (T == 0) return ok();
+  tp::GemmParams p = gemm(X, ldx, 0, W_i, ldw, 0, Y_i, ldy, 0, T, Ns, K, 1);
+  p.bias = bias_i;
+  p.upOff = Ns * ldw;
+  const tp::Epilogue e = act == TP_ACT_GELU ? tp::EPI_GELU : act == TP_ACT_SWIGLU ? tp::EPI_SWIGLU : tp::EPI_STORE;
+  return hip_status(launch("column_linear", dt, p, e, static_cast<hipStream_t>(stream)), "column_linear launch");
+}
+
+tp_status tp_row_linear_partial(void* stream, tp_dtype dt, int64_t T, int64_t Ks, int64_t Nout, const void* X_i,
+                                int64_t ldx, const void* W_i, int64_t ldw, float* P_i, int64_t ldp) {
+  TP_TRY(check_dtype(dt));
+  if (T < 0 || Ks <= 0 || Nout <= 0)
+    return fail(TP_ERR_SHAPE, "T=%lld Ks=%lld Nout=%lld", (long long)T, (long long)Ks, (long long)Nout);
+  const int64_t vec = vec_of(dt);
+  if (Ks % vec) return fail(TP_ERR_ALIGN, "Ks=%lld is not a multiple of %lld", (long long)Ks, (long long)vec);
+  if (T == 0) return ok();  // empty input: nothing to read or write
+  TP_TRY(check_matrix("X_i", X_i, T, Ks, ldx, vec));
+  TP_TRY(check_matrix("W_i", W_i, Nout, Ks, ldw, vec));
+  if (!P_i) return fail(TP_ERR_NULL, "P_i is NULL");
+  if (ldp < Nout) return fail(TP_ERR_SHAPE, "ldp %lld < Nout %lld", (long long)ldp, (long long)Nout);
+  if (T > kIntMax) return fail(TP_ERR_SHAPE, "T exceeds 2^31-1");
+  if (T == 0) return ok();
+  const tp::GemmParams p = gemm(X_i, ldx, 0, W_i, ldw, 0, P_i, ldp, 0, T, Nout, Ks, 1);
+  return hip_status(launch("row_linear_partial", dt, p, tp::EPI_PARTIAL, static_cast<hipStream_t>(stream)), "row_linear_partial launch");
+}
+
+tp_status tp_reduce_partials(void* stream, tp_dtype out_dt, int n_parts, int64_t T, int64_t H, const float* P,
+                             int64_t part_stride, const void* bias, void* Y, int n_slices, int slice) {
+  TP_TRY(validate_reduce(out_dt, n_parts, T, H, P, part_stride, bias, Y, n_slices, slice));
+  if (T == 0) return ok();
+  return run_reduce(static_cast<hipStream_t>(stream), out_dt, n_parts, T, H, P, part_stride, bias, Y, n_slices,
+                    slice);
+}
+
+size_t tp_mlp_workspace_size(const tp_mlp_desc* d) {
+  MlpShape sh;
+  return validate_mlp(d, &sh) == TP_OK ? sh.total : 0;
+}
+
+size_t tp_mlp_partials_offset(const tp_mlp_desc* d) {
+  (void)d;
+  return 0;
+}
+
+size_t tp_attn_workspace_size(const tp_attn_desc* d) {
+  AttnShape sh;
+  return validate_attn(d, &sh) == TP_OK ? sh.total : 0;
+}
+
+size_t tp_attn_partials_offset(const tp_attn_desc* d) {
+  (void)d;
+  return 0;
+}
+
+tp_status tp_mlp_forward(void* stream, const tp_mlp_desc* d, void* ws, size_t ws_bytes) {
+  MlpShape sh;
+  TP_TRY(validate_mlp(d, &sh));
+  if (d->T == 0) return ok();
+  TP_TRY(check_ws(ws, ws_bytes, sh.total));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t T = d->T, H = d->H, Fs = sh.Fs;
+  const int c = d->shard_count, i0 = d->shard_begin;
+  if (log_enabled())
+    fprintf(stderr,
+            "[tp] mlp %s act=%d N=%d shards [%d,%d): X[%lld x %lld] A_i[%lld x %lld] -> H_i[%lld x %lld] ; "
+            "B_i[%lld x %lld] -> P_i[%lld x %lld] fp32%s\n",
+            dt_name(d->dt), (int)d->act, d->N, i0, i0 + c, (long long)T, (long long)H, (long long)sh.a_rows,
+            (long long)H, (long long)T, (long long)Fs, (long long)H, (long long)Fs, (long long)T, (long long)H,
+            c == d->N ? " ; reduce" : "");
+  if (T == 0) return ok();
+  char* base = static_cast<char*>(ws);
+  float* P = reinterpret_cast<float*>(base);
+  void* Hs = base + sh.h_offset;
+  const size_t es = esize(d->dt);
+
+  // column GEMM + activation for every shard in range (X shared, one launch)
+  tp::GemmParams col = gemm(d->X, H, 0, static_cast<const char*>(d->A) + (size_t)i0 * sh.a_rows * H * es, H,
+                            sh.a_rows * H, Hs, Fs, T * Fs, T, Fs, H, c);
+  if (d->a) {
+    col.bias = static_cast<const char*>(d->a) + (size_t)i0 * Fs * es;
+    col.sBias = Fs;
+  }
+  col.upOff = Fs * H;
+  const tp::Epilogue ce = d->act == TP_ACT_SWIGLU ? tp::EPI_SWIGLU : d->act == TP_ACT_GELU ? tp::EPI_GELU : tp::EPI_STORE;
+  TP_TRY(hip_status(launch("mlp_column_gemm", d->dt, col, ce, s), "mlp column launch"));
+
+  // row partial of every shard into its slot of the fp32 slab
+  const tp::GemmParams row = gemm(Hs, Fs, T * Fs, static_cast<const char*>(d->B) + (size_t)i0 * Fs * es, d->F, Fs,
+                                  P + (size_t)i0 * T * H, H, T * H, T, H, Fs, c);
+  TP_TRY(hip_status(launch("mlp_row_gemm", d->dt, row, tp::EPI_PARTIAL, s), "mlp row launch"));
+
+  if (c < d->N) return ok();
+  return run_reduce(s, d->dt, d->N, T, H, P, T * H, d->b, d->Y, d->n_slices, d->slice);
+}
+
+tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t ws_bytes) {
+  AttnShape sh;
+  TP_TRY(validate_attn(d, &sh));
+  if (sh.T == 0) return ok();
+  TP_TRY(check_ws(ws, ws_bytes, sh.total));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t T = sh.T, Hd = d->hidden, hd = sh.hd;
+  const int c = d->shard_count, i0 = d->shard_begin;
+  if (log_enabled())
+    fprintf(stderr,
+            "[tp] attn N=%d shards [%d,%d): heads/shard=%lld X[%lld x %lld] Wqkv_i[%lld x %lld] -> Q,K[%lld x %lld] "
+            "V^T[%lld x %lld] -> O_i[%lld x %lld] ; Wo_i[%lld x %lld] -> P_i[%lld x %lld] fp32%s\n",
+            d->N, i0, i0 + c, (long long)sh.hl, (long long)T, (long long)Hd, (long long)(3 * hd), (long long)Hd,
+            (long long)T, (long long)hd, (long long)hd, (long long)T, (long long)T, (long long)hd, (long long)Hd,
+            (long long)hd, (long long)T, (long long)Hd, c == d->N ? " ; reduce" : "");
+  if (T == 0) return ok();
+  char* base = static_cast<char*>(ws);
+  float* P = reinterpret_cast<float*>(base);
+  void* QK = base + sh.qk_off;
+  void* Vt = base + sh.vt_off;
+  void* Ob = base + sh.o_off;
+  const char* W0 = static_cast<const char*>(d->Wqkv) + (size_t)i0 * 3 * hd * Hd * 2;
+
+  // Q and K of the shard's heads: [T x 2hd] = X [T x hidden] * (Q,K rows)^T
+  const tp::GemmParams qk = gemm(d->X, Hd, 0, W0, Hd, 3 * hd * Hd, QK, 2 * hd, T * 2 * hd, T, 2 * hd, Hd, c);
+  TP_TRY(hip_status(launch("attn_qk_gemm", TP_BF16, qk, tp::EPI_STORE, s), "attn qk launch"));
+  // V^T of the shard's heads: [hd x T] = (V rows) [hd x hidden] * X^T
+  const tp::GemmParams vt =
+      gemm(W0 + (size_t)2 * hd * Hd * 2, Hd, 3 * hd * Hd, d->X, Hd, 0, Vt, T, hd * T, hd, T, Hd, c);
+  TP_TRY(hip_status(launch("attn_vt_gemm", TP_BF16, vt, tp::EPI_STORE, s), "attn v launch"));
+
+  tp::AttnParams a{};
+  a.QK = QK;
+  a.ldqk = 2 * hd;
+  a.sQK = T * 2 * hd;
+  a.kcol0 = hd;
+  a.Vt = Vt;
+  a.ldvt = T;
+  a.sVt = hd * T;
+  a.O = Ob;
+  a.ldo = hd;
+  a.sO = T * hd;
+  a.batch = (int)d->batch;
+  a.seq = (int)d->seq;
+  a.heads = (int)sh.hl;
+  a.nshards = c;
+  a.scale_log2e = (float)(1.4426950408889634 / 11.313708498984761);  // log2(e) / sqrt(128)
+  {
+    KernelTimer kt("attn_core", s);
+    const hipError_t e = tp::launch_attention(a, s);
+    kt.stop();
+    TP_TRY(hip_status(e, "attn launch"));
+  }
+
+  // output projection, row-parallel: P_i = O_i [T x hd] * (Wo columns of shard i)^T
+  const tp::GemmParams op = gemm(Ob, hd, T * hd, static_cast<const char*>(d->Wo) + (size_t)i0 * hd * 2, Hd, hd,
+                                 P + (size_t)i0 * T * Hd, Hd, T * Hd, T, Hd, hd, c);
+  TP_TRY(hip_status(launch("attn_out_gemm", TP_BF16, op, tp::EPI_PARTIAL, s), "attn out-proj launch"));
+
+  if (c < d->N) return ok();
+  return run_reduce(s, TP_BF16, d->N, T, Hd, P, T * Hd, d->bo, d->Y, d->n_slices, d->slice);
+}
+
+tp_status tp_attn_local(void* stream, int64_t batch, int64_t seq, int heads, int head_dim, const void* QK,
+                        int64_t ldqk, int64_t k_col0, const void* Vt, int64_t ldvt, void* O, int64_t ldo) {
+  if (batch < 0 || seq < 0 || heads <= 0) return fail(TP_ERR_SHAPE, "batch=%lld seq=%lld heads=%d", (long long)batch, (long long)seq, heads);
+  if (head_dim != 128) return fail(TP_ERR_SHAPE, "head_dim=%d (only 128 is built)", head_dim);
+  if (seq % 128) return fail(TP_ERR_SHAPE, "seq=%lld is not a multiple of 128", (long long)seq);
+  const int64_t T = batch * seq, hd = (int64_t)heads * head_dim;
+  if (k_col0 < hd || k_col0 % 8)
+    return fail(TP_ERR_SHAPE, "k_col0=%lld must be a multiple of 8 at or after the query columns [0, %lld)",
+                (long long)k_col0, (long long)hd);
+  TP_TRY(check_matrix("QK", QK, T, k_col0 + hd, ldqk, 8));
+  TP_TRY(check_matrix("Vt", Vt, hd, T, ldvt, 8));
+  TP_TRY(check_matrix("O", O, T, hd, ldo, 8));
+  if (T > kIntMax) return fail(TP_ERR_SHAPE, "batch*seq exceeds 2^31-1");
+  if (T == 0) return ok();
+  tp::AttnParams a{};
+  a.QK = QK;
+  a.ldqk = ldqk;
+  a.kcol0 = k_col0;
+  a.Vt = Vt;
+  a.ldvt = ldvt;
+  a.O = O;
+  a.ldo = ldo;
+  a.batch = (int)batch;
+  a.seq = (int)seq;
+  a.heads = heads;
+  a.nshards = 1;
+  a.scale_log2e = (float)(1.4426950408889634 / 11.313708498984761);
+  KernelTimer kt("attn_core", static_cast<hipStream_t>(stream));
+  const hipError_t e = tp::launch_attention(a, static_cast<hipStream_t>(stream));
+  kt.stop();
+  return hip_status(e, "attn_local launch");
+}
+
+tp_status tp_timing_enable(int on) {
+  std::lock_guard<std::mutex> g(g_tmu);
+  g_timing = on != 0;
+  return ok();
+}
+
+void tp_timing_reset(void) {
+  std::lock_guard<std::mutex> g(g_tmu);
+  for (auto& p : g_pending) {
+    hipEventSynchronize(p.b);
+    g_event_pool.push_back(p.a);
+    g_event_pool.push_back(p.b);
+  }
+  g_pending.clear();
+  g_totals.clear();
+}
+
+int tp_timing_read(int max, const char** names, double* total_ms, int64_t* launches) {
+  std::lock_guard<std::mutex> g(g_tmu);
+  for (auto& p : g_pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+      auto& t = g_totals[p.name];
+      t.first += ms;
+      t.second += 1;
+    }
+    g_event_pool.push_back(p.a);
+    g_event_pool.push_back(p.b);
+  }
+  g_pending.clear();
+  g_names.clear();
+  for (auto& kv : g_totals) g_names.push_back(kv.first);
+  int i = 0;
+  for (auto& kv : g_totals) {
+    if (i >= max) break;
+    if (names) names[i] = g_names[i].c_str();
+    if (total_ms) total_ms[i] = kv.second.first;
+    if (launches) launches[i] = kv.second.second;
+    ++i;
+  }
+  return (int)g_totals.size();
+}
+
+const char* tp_status_string(tp_status s) {
+  switch (s) {
+    case TP_OK: return "TP_OK";
+    case TP_ERR_NULL: return "TP_ERR_NULL";
+    case TP_ERR_SHAPE: return "TP_ERR_SHAPE";
+    case TP_ERR_DIVISIBILITY: return "TP_ERR_DIVISIBILITY";
+    case TP_ERR_DTYPE: return "TP_ERR_DTYPE";
+    case TP_ERR_ALIGN: return "TP_ERR_ALIGN";
+    case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE";
+    case TP_ERR_HIP: return "TP_ERR_HIP";
+  }
+  return "TP_ERR_UNKNOWN";
+}
+
+const char* tp_last_error(void) { return g_err.c_str(); }
+
+const char* tp_version(void) { return "libtp 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Device-side helpers shared by the HIP kernels of libtp (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tp {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// 16-byte chunk moved between HBM, registers and LDS.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// GELU, exact form: x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)).  The pages
+// write the MLP as GELU(XA)B and name no approximation.
+__device__ __forceinline__ float gelu_erf(float x) {
+  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
+
+// SiLU with beta = 1: g * sigmoid(g) = g / (1 + e^-g).
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// fp32 -> bf16, IEEE round-to-nearest-even (the compiler emits gfx950's
+// v_cvt_pk_bf16_f32, which rounds to nearest even).
+__device__ __forceinline__ bf16 to_bf16(float x) { return static_cast<bf16>(x); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup w -> XCD w % 8).
+// Renumber so that consecutive logical tile ids land on the same XCD and
+// share its L2.  Works for any total (the last XCDs may get one tile fewer).
+__device__ __forceinline__ int xcd_remap(int pid, int total) {
+  constexpr int kXcd = 8;
+  const int per = (total + kXcd - 1) / kXcd;
+  int tall = total % kXcd;
+  if (tall == 0) tall = kXcd;
+  const int xcd = pid % kXcd;
+  const int local = pid / kXcd;
+  return xcd < tall ? xcd * per + local : tall * per + (xcd - tall) * (per - 1) + local;
+}
+
+}  // namespace tp

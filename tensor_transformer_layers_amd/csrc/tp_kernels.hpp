@@ -1,0 +1,64 @@
+// Host-visible launch interface of the libtp kernels (internal; the public
+// interface is include/tp.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tp {
+
+// Epilogue applied to the fp32 accumulator tile of a GEMM.
+enum Epilogue : int {
+  EPI_STORE = 0,   // C = acc (+ bias)              out dtype = input dtype
+  EPI_GELU = 1,    // C = GELU(acc + bias)          out dtype = input dtype
+  EPI_PARTIAL = 2, // C = acc                       out fp32 (row partial)
+  EPI_SWIGLU = 3,  // C = SiLU(acc_gate) * acc_up   out bf16
+};
+
+// C[M x N] = A[M x K] * B[N x K]^T, batched over `batch` problems whose
+// pointers advance by sA/sB/sC/sBias elements.  Both operands are K-contiguous.
+// For EPI_SWIGLU, B holds gate rows at B and up rows at B + upOff; N is the
+// output width (gate rows used: N).
+struct GemmParams {
+  const void* A;
+  int64_t lda, sA;
+  const void* B;
+  int64_t ldb, sB;
+  void* C;
+  int64_t ldc, sC;
+  const void* bias;  // [N] per batch or nullptr
+  int64_t sBias;
+  int64_t upOff;
+  int M, N, K;
+  int batch;
+};
+
+hipError_t launch_gemm_bf16(const GemmParams& p, Epilogue epi, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmParams& p, Epilogue epi, hipStream_t s);
+
+// Y[rows x H] = fold_k P[k][row0 + r, :] (+ bias), see tp_reduce_partials.
+struct ReduceParams {
+  const float* P;
+  int64_t part_stride;
+  int n_parts;
+  int64_t rows, H, row0;
+  const void* bias;
+  void* Y;
+};
+hipError_t launch_reduce(const ReduceParams& p, bool out_bf16, hipStream_t s);
+
+// Causal attention over local heads (head_dim 128), batched over `nshards`
+// problems advancing by sQK / sVt / sO elements.
+struct AttnParams {
+  const void* QK;
+  int64_t ldqk, sQK, kcol0;
+  const void* Vt;
+  int64_t ldvt, sVt;
+  void* O;
+  int64_t ldo, sO;
+  int batch, seq, heads, nshards;
+  float scale_log2e;  // log2(e) / sqrt(head_dim)
+};
+hipError_t launch_attention(const AttnParams& p, hipStream_t s);
+
+}  // namespace tp

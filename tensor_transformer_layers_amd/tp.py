@@ -1,0 +1,316 @@
+"""ctypes binding of libtp.so (C ABI in include/tp.h).
+
+Argument marshalling only: the raw functions below carry the C names and
+signatures; the tensor helpers turn torch tensors into (pointer, shape, ld,
+stream) and raise ``TPError`` on a non-OK status.  Every step of the path runs
+in the HIP kernels of libtp; there is no fallback: if the library is missing,
+``lib()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtp.so")
+
+TP_OK, TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_DIVISIBILITY, TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_WORKSPACE, TP_ERR_HIP = range(8)
+TP_F32, TP_BF16 = 0, 1
+TP_ACT_NONE, TP_ACT_GELU, TP_ACT_SWIGLU = 0, 1, 2
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+
+class MlpDesc(ctypes.Structure):
+    _fields_ = [
+        ("dt", _int), ("act", _int),
+        ("T", _i64), ("H", _i64), ("F", _i64),
+        ("N", _int), ("shard_begin", _int), ("shard_count", _int),
+        ("X", _vp), ("A", _vp), ("a", _vp), ("B", _vp), ("b", _vp),
+        ("Y", _vp),
+        ("n_slices", _int), ("slice", _int),
+    ]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("dt", _int),
+        ("batch", _i64), ("seq", _i64), ("hidden", _i64),
+        ("heads", _int), ("head_dim", _int), ("N", _int), ("shard_begin", _int), ("shard_count", _int),
+        ("X", _vp), ("Wqkv", _vp), ("Wo", _vp), ("bo", _vp),
+        ("Y", _vp),
+        ("n_slices", _int), ("slice", _int),
+    ]
+
+
+_SIGS = {
+    "tp_column_linear": (_int, [_vp, _int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64]),
+    "tp_row_linear_partial": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]),
+    "tp_reduce_partials": (_int, [_vp, _int, _int, _i64, _i64, _vp, _i64, _vp, _vp, _int, _int]),
+    "tp_mlp_workspace_size": (_sz, [ctypes.POINTER(MlpDesc)]),
+    "tp_attn_workspace_size": (_sz, [ctypes.POINTER(AttnDesc)]),
+    "tp_mlp_partials_offset": (_sz, [ctypes.POINTER(MlpDesc)]),
+    "tp_attn_partials_offset": (_sz, [ctypes.POINTER(AttnDesc)]),
+    "tp_mlp_forward": (_int, [_vp, ctypes.POINTER(MlpDesc), _vp, _sz]),
+    "tp_attn_forward": (_int, [_vp, ctypes.POINTER(AttnDesc), _vp, _sz]),
+    "tp_attn_local": (_int, [_vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp, _i64]),
+    "tp_timing_enable": (_int, [_int]),
+    "tp_timing_read": (_int, [_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                              ctypes.POINTER(_i64)]),
+    "tp_timing_reset": (None, []),
+    "tp_status_string": (ctypes.c_char_p, [_int]),
+    "tp_last_error": (ctypes.c_char_p, []),
+    "tp_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(python -m tensor_transformer_layers_amd.build_lib)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+class TPError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{status_string(status)}: {message}")
+
+
+def status_string(s: int) -> str:
+    return lib().tp_status_string(s).decode()
+
+
+def last_error() -> str:
+    return lib().tp_last_error().decode()
+
+
+def check(status: int) -> None:
+    if status != TP_OK:
+        raise TPError(status, last_error())
+
+
+# raw C entry points, same names and arguments as include/tp.h --------------
+def tp_column_linear(*args) -> int:
+    return lib().tp_column_linear(*args)
+
+
+def tp_row_linear_partial(*args) -> int:
+    return lib().tp_row_linear_partial(*args)
+
+
+def tp_reduce_partials(*args) -> int:
+    return lib().tp_reduce_partials(*args)
+
+
+def tp_mlp_forward(stream, desc: MlpDesc, ws, ws_bytes) -> int:
+    return lib().tp_mlp_forward(stream, ctypes.byref(desc), ws, ws_bytes)
+
+
+def tp_attn_forward(stream, desc: AttnDesc, ws, ws_bytes) -> int:
+    return lib().tp_attn_forward(stream, ctypes.byref(desc), ws, ws_bytes)
+
+
+def tp_attn_local(*args) -> int:
+    return lib().tp_attn_local(*args)
+
+
+def tp_mlp_workspace_size(desc: MlpDesc) -> int:
+    return lib().tp_mlp_workspace_size(ctypes.byref(desc))
+
+
+def tp_attn_workspace_size(desc: AttnDesc) -> int:
+    return lib().tp_attn_workspace_size(ctypes.byref(desc))
+
+
+def tp_timing_enable(on: int) -> int:
+    return lib().tp_timing_enable(on)
+
+
+def tp_timing_reset() -> None:
+    lib().tp_timing_reset()
+
+
+def tp_timing_read() -> dict:
+    """{kernel name: (total ms, launches)} since the last reset."""
+    L = lib()
+    n = L.tp_timing_read(0, None, None, None)
+    names = (ctypes.c_char_p * max(n, 1))()
+    ms = (ctypes.c_double * max(n, 1))()
+    cnt = (_i64 * max(n, 1))()
+    n = L.tp_timing_read(n, names, ms, cnt)
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(n)}
+
+
+# torch tensor helpers (marshalling only) ------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return TP_BF16
+    if t.dtype == torch.float32:
+        return TP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _ld(t) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a row-major 2-D tensor (unit column stride)")
+    return t.stride(0)
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def column_linear(X, W, bias=None, act=TP_ACT_GELU, out=None, stream=None):
+    """Y_i = act(X W_i^T + bias_i); W is [Ns x K] ([2Ns x K] for SwiGLU)."""
+    torch = _torch()
+    T, K = X.shape
+    Ns = W.shape[0] // 2 if act == TP_ACT_SWIGLU else W.shape[0]
+    if out is None:
+        out = torch.empty((T, Ns), dtype=X.dtype, device=X.device)
+    check(tp_column_linear(_stream(stream), _dt(X), act, T, K, Ns, _ptr(X), _ld(X), _ptr(W), _ld(W),
+                           _ptr(bias), _ptr(out), _ld(out)))
+    return out
+
+
+def row_linear_partial(X, W, out=None, stream=None):
+    """P_i = X_i W_i^T in fp32; W is [Nout x Ks]."""
+    torch = _torch()
+    T, Ks = X.shape
+    Nout = W.shape[0]
+    if out is None:
+        out = torch.empty((T, Nout), dtype=torch.float32, device=X.device)
+    check(tp_row_linear_partial(_stream(stream), _dt(X), T, Ks, Nout, _ptr(X), _ld(X), _ptr(W), _ld(W),
+                                _ptr(out), _ld(out)))
+    return out
+
+
+def reduce_partials(P, bias=None, out_dtype=None, n_slices=1, slice=-1, out=None, n_parts=None, stream=None):
+    """Fixed-order sum of P[0..n) ([n x T x H] fp32) + bias, cast to out_dtype."""
+    torch = _torch()
+    n, T, H = P.shape
+    n = n if n_parts is None else n_parts
+    out_dtype = out_dtype or (bias.dtype if bias is not None else torch.bfloat16)
+    rows = T if slice < 0 else T // n_slices
+    if out is None:
+        out = torch.empty((rows, H), dtype=out_dtype, device=P.device)
+    odt = TP_BF16 if out_dtype == torch.bfloat16 else TP_F32
+    check(tp_reduce_partials(_stream(stream), odt, n, T, H, _ptr(P), P.stride(0), _ptr(bias), _ptr(out),
+                             n_slices, slice))
+    return out
+
+
+def mlp_desc(X, A, a, B, b, N, act, Y=None, shard_begin=0, shard_count=None, n_slices=1, slice=-1, F=None):
+    T, H = X.shape
+    if F is None:
+        F = B.shape[1]
+    d = MlpDesc()
+    d.dt = _dt(X)
+    d.act = act
+    d.T, d.H, d.F = T, H, F
+    d.N = N
+    d.shard_begin = shard_begin
+    d.shard_count = N if shard_count is None else shard_count
+    d.X, d.A, d.a, d.B, d.b = _ptr(X), _ptr(A), _ptr(a), _ptr(B), _ptr(b)
+    d.Y = _ptr(Y)
+    d.n_slices, d.slice = n_slices, slice
+    return d
+
+
+def alloc_workspace(nbytes: int, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def mlp_forward(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, ws=None, shard_begin=0, shard_count=None,
+                n_slices=1, slice=-1, stream=None):
+    """Whole MLP sublayer; returns (Y, workspace).  Y is None for partial
+    shard ranges (the partials are in the workspace slab)."""
+    torch = _torch()
+    T, H = X.shape
+    cnt = N if shard_count is None else shard_count
+    if Y is None and cnt == N:
+        rows = T if slice < 0 else T // n_slices
+        Y = torch.empty((rows, H), dtype=X.dtype, device=X.device)
+    d = mlp_desc(X, A, a, B, b, N, act, Y, shard_begin, cnt, n_slices, slice)
+    need = tp_mlp_workspace_size(d)
+    if need == 0:
+        raise TPError(TP_ERR_SHAPE, last_error())
+    if ws is None or ws.numel() < need:
+        ws = alloc_workspace(need, X.device)
+    check(tp_mlp_forward(_stream(stream), d, _ptr(ws), ws.numel()))
+    return Y, ws
+
+
+def mlp_partials(ws, N, T, H):
+    """View of the fp32 partial slab at the start of an MLP/attention workspace."""
+    torch = _torch()
+    return ws[: N * T * H * 4].view(torch.float32).view(N, T, H)
+
+
+def attn_desc(X, Wqkv, Wo, bo, batch, seq, heads, N, Y=None, shard_begin=0, shard_count=None, n_slices=1,
+              slice=-1, head_dim=128):
+    d = AttnDesc()
+    d.dt = _dt(X)
+    d.batch, d.seq, d.hidden = batch, seq, X.shape[1]
+    d.heads, d.head_dim, d.N = heads, head_dim, N
+    d.shard_begin = shard_begin
+    d.shard_count = N if shard_count is None else shard_count
+    d.X, d.Wqkv, d.Wo, d.bo = _ptr(X), _ptr(Wqkv), _ptr(Wo), _ptr(bo)
+    d.Y = _ptr(Y)
+    d.n_slices, d.slice = n_slices, slice
+    return d
+
+
+def attn_forward(X, Wqkv, Wo, bo, batch, seq, heads, N, Y=None, ws=None, shard_begin=0, shard_count=None,
+                 n_slices=1, slice=-1, stream=None):
+    torch = _torch()
+    T, Hd = X.shape
+    cnt = N if shard_count is None else shard_count
+    if Y is None and cnt == N:
+        rows = T if slice < 0 else T // n_slices
+        Y = torch.empty((rows, Hd), dtype=X.dtype, device=X.device)
+    d = attn_desc(X, Wqkv, Wo, bo, batch, seq, heads, N, Y, shard_begin, cnt, n_slices, slice)
+    need = tp_attn_workspace_size(d)
+    if need == 0:
+        raise TPError(TP_ERR_SHAPE, last_error())
+    if ws is None or ws.numel() < need:
+        ws = alloc_workspace(need, X.device)
+    check(tp_attn_forward(_stream(stream), d, _ptr(ws), ws.numel()))
+    return Y, ws
+
+
+def attn_local(QK, k_col0, Vt, batch, seq, heads, out=None, stream=None):
+    torch = _torch()
+    T = batch * seq
+    if out is None:
+        out = torch.empty((T, heads * 128), dtype=QK.dtype, device=QK.device)
+    check(tp_attn_local(_stream(stream), batch, seq, heads, 128, _ptr(QK), _ld(QK), k_col0, _ptr(Vt), _ld(Vt),
+                        _ptr(out), _ld(out)))
+    return out

@@ -1,0 +1,80 @@
+"""Device-side set-up and one forward pass of a workload through libtp.
+
+Set-up (done once, outside any timed region) uploads the generator's arrays
+and arranges weights in the layout the C ABI takes: per-shard fused
+[gate | up] blocks for SwiGLU, per-shard [Q | K | V] row blocks of the shard's
+heads for attention.  The forward pass itself is one call into libtp.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import tp
+from .configs import Workload
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device(x, dtype, device="cuda"):
+    torch = _torch()
+    if x is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=dtype)
+
+
+def device_inputs(w: Workload, host: dict, device="cuda") -> dict:
+    torch = _torch()
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    d = {}
+    if w.kind == "mlp_gelu":
+        for k in ("X", "A", "a", "B", "b"):
+            d[k] = to_device(host[k], dt, device)
+    elif w.kind == "mlp_swiglu":
+        Fs = w.F // w.N
+        d["X"] = to_device(host["X"], dt, device)
+        Wg = to_device(host["Wg"], dt, device)
+        Wu = to_device(host["Wu"], dt, device)
+        # shard i: rows [gate i*Fs..(i+1)*Fs | up i*Fs..(i+1)*Fs]
+        d["A"] = torch.cat([Wg.view(w.N, Fs, w.H), Wu.view(w.N, Fs, w.H)], dim=1).reshape(w.N * 2 * Fs, w.H).contiguous()
+        del Wg, Wu
+        d["a"] = None
+        d["B"] = to_device(host["Wd"], dt, device)
+        d["b"] = None
+    elif w.kind == "attn":
+        hd = (w.heads // w.N) * w.head_dim
+        d["X"] = to_device(host["X"], dt, device)
+        Wq, Wk, Wv = (to_device(host[k], dt, device).view(w.N, hd, w.H) for k in ("Wq", "Wk", "Wv"))
+        d["Wqkv"] = torch.cat([Wq, Wk, Wv], dim=1).reshape(w.N * 3 * hd, w.H).contiguous()
+        del Wq, Wk, Wv
+        d["Wo"] = to_device(host["Wo"], dt, device)
+        d["bo"] = None
+    else:
+        raise ValueError(w.kind)
+    return d
+
+
+def act_of(w: Workload) -> int:
+    return tp.TP_ACT_SWIGLU if w.kind == "mlp_swiglu" else tp.TP_ACT_GELU
+
+
+def forward(w: Workload, d: dict, Y=None, ws=None, shard_begin=0, shard_count=None, slice=-1, stream=None):
+    """One pass of the sublayer over shards [shard_begin, shard_begin+count)."""
+    if w.kind == "attn":
+        return tp.attn_forward(d["X"], d["Wqkv"], d["Wo"], d["bo"], w.batch, w.seq, w.heads, w.N, Y=Y, ws=ws,
+                               shard_begin=shard_begin, shard_count=shard_count, n_slices=w.n_slices,
+                               slice=slice, stream=stream)
+    return tp.mlp_forward(d["X"], d["A"], d["a"], d["B"], d["b"], w.N, act=act_of(w), Y=Y, ws=ws,
+                          shard_begin=shard_begin, shard_count=shard_count, n_slices=w.n_slices, slice=slice,
+                          stream=stream)
+
+
+def reduce_slab(w: Workload, d: dict, ws, Y=None, slice=-1, stream=None):
+    """The reduction step alone over the partial slab of a workspace."""
+    torch = _torch()
+    P = tp.mlp_partials(ws, w.N, w.T, w.H)
+    bias = d.get("b") if w.kind != "attn" else d.get("bo")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return tp.reduce_partials(P, bias, out_dtype=dt, n_slices=w.n_slices, slice=slice, out=Y, stream=stream)

@@ -1,0 +1,172 @@
+"""The C-ABI library loads, exports every symbol include/tp.h declares, and
+rejects bad arguments before touching the GPU (no compute call here: every
+call below fails validation or is a no-op, so none reaches HIP)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from tensor_transformer_layers_amd import tp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp.h")
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced (validation fails first)
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tp.LIB_PATH):
+        pytest.skip("libtp.so not built")
+    return tp.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 13
+    out = subprocess.run(["nm", "-D", "--defined-only", tp.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (tp_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(L, n)
+        assert n in tp._SIGS, f"binding lacks {n}"
+
+
+def test_version_and_status_strings(L):
+    assert tp.lib().tp_version().decode().startswith("libtp")
+    assert tp.status_string(tp.TP_ERR_DIVISIBILITY) == "TP_ERR_DIVISIBILITY"
+    assert tp.status_string(99) == "TP_ERR_UNKNOWN"
+
+
+def _mlp(**kw):
+    d = tp.MlpDesc()
+    d.dt, d.act = tp.TP_BF16, tp.TP_ACT_GELU
+    d.T, d.H, d.F, d.N = 256, 512, 2048, 4
+    d.shard_begin, d.shard_count = 0, 4
+    d.X = d.A = d.a = d.B = d.b = d.Y = FAKE
+    d.n_slices, d.slice = 1, -1
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_mlp_workspace_size_is_host_only(L):
+    d = _mlp()
+    need = tp.tp_mlp_workspace_size(d)
+    p_bytes = 4 * 256 * 512 * 4
+    h_bytes = 4 * 256 * 512 * 2
+    assert need == p_bytes + h_bytes
+    d.shard_count = 1
+    assert tp.tp_mlp_workspace_size(d) == p_bytes + 256 * 512 * 2
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(F=2050), tp.TP_ERR_DIVISIBILITY, "not divisible by N=4"),
+    (dict(N=3, shard_count=3, F=3 * 2044), tp.TP_ERR_ALIGN, "F/N=2044 is not a multiple of 8"),
+    (dict(X=None), tp.TP_ERR_NULL, "X is NULL"),
+    (dict(B=None), tp.TP_ERR_NULL, "B is NULL"),
+    (dict(A=FAKE + 2), tp.TP_ERR_ALIGN, "A is not 16-byte aligned"),
+    (dict(dt=7), tp.TP_ERR_DTYPE, "dtype"),
+    (dict(act=9), tp.TP_ERR_DTYPE, "activation"),
+    (dict(act=tp.TP_ACT_SWIGLU, dt=tp.TP_F32), tp.TP_ERR_DTYPE, "bf16-only"),
+    (dict(act=tp.TP_ACT_SWIGLU), tp.TP_ERR_SHAPE, "bias must be NULL"),
+    (dict(shard_begin=3, shard_count=2), tp.TP_ERR_SHAPE, "shard range"),
+    (dict(n_slices=3), tp.TP_ERR_DIVISIBILITY, "sequence slices"),
+    (dict(n_slices=4, slice=4), tp.TP_ERR_SHAPE, "slice 4"),
+    (dict(H=500), tp.TP_ERR_ALIGN, "hidden H=500"),
+    (dict(Y=None), tp.TP_ERR_NULL, "Y is NULL"),
+])
+def test_mlp_validation(L, kw, status, needle):
+    d = _mlp(**kw)
+    s = tp.tp_mlp_forward(None, d, FAKE, 1 << 40)
+    assert s == status, (tp.status_string(s), tp.last_error())
+    assert needle in tp.last_error()
+    assert tp.tp_mlp_workspace_size(d) == 0
+
+
+def test_mlp_workspace_errors(L):
+    d = _mlp()
+    need = tp.tp_mlp_workspace_size(d)
+    assert tp.tp_mlp_forward(None, d, None, need) == tp.TP_ERR_WORKSPACE
+    assert tp.tp_mlp_forward(None, d, FAKE, need - 1) == tp.TP_ERR_WORKSPACE
+    assert "needed" in tp.last_error()
+    assert tp.tp_mlp_forward(None, d, FAKE + 8, need) == tp.TP_ERR_ALIGN
+
+
+def _attn(**kw):
+    d = tp.AttnDesc()
+    d.dt = tp.TP_BF16
+    d.batch, d.seq, d.hidden = 2, 256, 1024
+    d.heads, d.head_dim, d.N = 8, 128, 4
+    d.shard_begin, d.shard_count = 0, 4
+    d.X = d.Wqkv = d.Wo = d.Y = FAKE
+    d.bo = None
+    d.n_slices, d.slice = 1, -1
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(N=3), tp.TP_ERR_DIVISIBILITY, "heads=8 are not divisible by N=3"),
+    (dict(head_dim=64, hidden=512), tp.TP_ERR_SHAPE, "head_dim=64"),
+    (dict(hidden=2048), tp.TP_ERR_SHAPE, "heads*head_dim"),
+    (dict(seq=200), tp.TP_ERR_SHAPE, "multiple of 128"),
+    (dict(dt=tp.TP_F32), tp.TP_ERR_DTYPE, "bf16-only"),
+    (dict(Wqkv=None), tp.TP_ERR_NULL, "Wqkv is NULL"),
+])
+def test_attn_validation(L, kw, status, needle):
+    d = _attn(**kw)
+    s = tp.tp_attn_forward(None, d, FAKE, 1 << 40)
+    assert s == status, (tp.status_string(s), tp.last_error())
+    assert needle in tp.last_error()
+
+
+def test_attn_workspace_size(L):
+    d = _attn()
+    T, hd = 512, 2 * 128
+    want = 4 * T * 1024 * 4 + 4 * T * 2 * hd * 2 + 4 * hd * T * 2 + 4 * T * hd * 2
+    assert tp.tp_attn_workspace_size(d) == want
+
+
+def test_linear_and_reduce_validation(L):
+    # K not a multiple of 8 (bf16)
+    s = tp.tp_column_linear(None, tp.TP_BF16, tp.TP_ACT_GELU, 16, 12, 16, FAKE, 16, FAKE, 16, None, FAKE, 16)
+    assert s == tp.TP_ERR_ALIGN and "K=12" in tp.last_error()
+    # ld smaller than the row
+    s = tp.tp_column_linear(None, tp.TP_BF16, tp.TP_ACT_GELU, 16, 64, 16, FAKE, 32, FAKE, 64, None, FAKE, 16)
+    assert s == tp.TP_ERR_SHAPE and "leading dimension" in tp.last_error()
+    s = tp.tp_row_linear_partial(None, tp.TP_F32, 16, 64, 16, FAKE, 64, None, 64, FAKE, 16)
+    assert s == tp.TP_ERR_NULL
+    # partials overlapping
+    s = tp.tp_reduce_partials(None, tp.TP_BF16, 4, 8, 16, FAKE, 64, None, FAKE, 1, -1)
+    assert s == tp.TP_ERR_SHAPE and "overlap" in tp.last_error()
+    s = tp.tp_reduce_partials(None, tp.TP_BF16, 4, 8, 12, FAKE, 96, None, FAKE, 1, -1)
+    assert s == tp.TP_ERR_ALIGN
+    s = tp.tp_reduce_partials(None, tp.TP_BF16, 0, 8, 16, FAKE, 128, None, FAKE, 1, -1)
+    assert s == tp.TP_ERR_SHAPE
+    # empty inputs are a no-op that succeeds without any HIP call
+    assert tp.tp_column_linear(None, tp.TP_BF16, tp.TP_ACT_GELU, 0, 64, 16, FAKE, 64, FAKE, 64, None, FAKE, 16) == tp.TP_OK
+    assert tp.tp_reduce_partials(None, tp.TP_BF16, 4, 0, 16, FAKE, 0, None, FAKE, 1, -1) == tp.TP_OK
+    assert tp.tp_attn_local(None, 0, 128, 2, 128, FAKE, 512, 256, FAKE, 8, FAKE, 256) == tp.TP_OK
+
+
+def test_attn_local_validation(L):
+    s = tp.tp_attn_local(None, 1, 128, 2, 128, FAKE, 512, 128, FAKE, 128, FAKE, 256)
+    assert s == tp.TP_ERR_SHAPE and "k_col0" in tp.last_error()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(tp, "LIB_PATH", str(tmp_path / "libtp.so"))
+    monkeypatch.setattr(tp, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        tp.lib()
