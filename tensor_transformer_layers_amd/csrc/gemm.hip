@@ -8,15 +8,30 @@
 // its fp32 partial: the same post, section 2.2; activation on the shard-local
 // slice between them: section 2.3 and "张量并行" (MLP formula GELU(XA)B).
 //
-// bf16 path: 256 threads = 4 waves in a 2x2 grid; each wave owns a
-// (BM/2) x (BN/2) block of 32x32 output tiles computed with
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulate).  A and B tiles are staged
-// global -> registers -> LDS (double-buffered, rows padded by 16 bytes so the
-// per-lane 16-byte reads of 32 consecutive rows hit distinct banks); the loads
-// of tile k+1 are in flight while tile k feeds the matrix cores.  Workgroup
-// ids are renumbered so that neighbouring output tiles run on the same XCD.
+// bf16 path (gfx950):
+//  * 256 threads = 4 waves in a 2x2 grid; each wave owns a (BM/2) x (BN/2)
+//    block of 32x32 tiles computed with v_mfma_f32_32x32x16_bf16 (fp32
+//    accumulators live in AGPRs).  The weight fragment is the MFMA's first
+//    operand and the activation fragment its second, so each lane ends up
+//    holding one output row and runs of 4 consecutive output columns: the
+//    epilogue stores 8-byte (bf16) or 16-byte (fp32) vectors.
+//  * Global -> LDS staging uses the buffer-load-to-LDS path (no registers, no
+//    LDS write instructions): one wave instruction fills 1 KB of LDS, lane i
+//    landing at byte 16*i.  The lane -> global chunk assignment applies an
+//    XOR swizzle (chunk c of tile row r sits at chunk c ^ ((r >> SH) & (CPR-1)))
+//    so that the 16-byte fragment reads of consecutive rows hit distinct LDS
+//    banks.  Rows past the matrix edge and chunks past K read as zero through
+//    the buffer range check; the tail chunks are also cleared explicitly.
+//  * S-stage LDS ring: the loads of tile k+S-1 are issued right after the
+//    barrier that opens tile k, so S-1 tiles of compute hide their latency.
+//    One barrier per tile.  Fragment reads of k-step kk+1 are issued before the
+//    MFMAs of step kk.
+//  * Workgroup ids are renumbered so that neighbouring output tiles run on the
+//    same XCD (shared L2), in groups of 8 M-tiles.
 //
 // fp32 path: 64x64 tiles, v_mfma_f32_16x16x4_f32, used for fp32 workloads.
+#include <type_traits>
+
 #include "tp_device.hpp"
 #include "tp_kernels.hpp"
 
@@ -24,37 +39,78 @@ namespace tp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPad = 8;  // bf16 elements of padding per LDS row (16 bytes)
 
-template <int BM, int BN, int BK, int EPI>
-struct TileCfg {
-  static constexpr int WM = BM / 2, WN = BN / 2;    // wave tile, 2x2 waves
-  static constexpr int TM = WM / 32, TN = WN / 32;  // 32x32 MFMA tiles per wave
-  static constexpr int LDK = BK + kPad;
-  static constexpr int CPR = BK / 8;                // 16-byte chunks per tile row
-  static constexpr int RPP = kThreads / CPR;        // tile rows per load pass
-  static constexpr int CA = BM / RPP;               // load passes (chunks) per thread, A
-  static constexpr int CB = BN / RPP;
-  static constexpr int OUT_N = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns per tile
-  static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must split evenly over passes");
-  static_assert(EPI != EPI_SWIGLU || (BN / 2) % RPP == 0, "gate/up halves per pass");
-  static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU needs gate and up subtiles");
+#define TP_LDS __attribute__((address_space(3)))
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that orders LDS only (global loads stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // word 3 = 0x00020000: raw (untyped) 32-bit data format on gfx9-family parts
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TP_LDS void*)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+
+constexpr uint32_t kOob = 0x80000000u;  // beyond every range: reads as zero
+
+#ifndef TP_GEMM_SH
+#define TP_GEMM_SH 1
+#endif
+#ifndef TP_GEMM_SPREAD
+#define TP_GEMM_SPREAD 0
+#endif
+
+template <int BM_, int BN_, int BK_, int S_, int SH_, int EPI_>
+struct G {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, SH = SH_, EPI = EPI_;
+  static constexpr int CPR = BK / 8;         // 16-byte chunks per tile row
+  static constexpr int RPI = 64 / CPR;       // tile rows one wave load instruction fills
+  static constexpr int IA = BM / (4 * RPI);  // load instructions per wave per stage, A tile
+  static constexpr int IB = BN / (4 * RPI);  //                                        B tile
+  static constexpr int GROUP = IA + IB;
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int STAGE_BYTES = (BM + BN) * BK * 2;
+  static constexpr int LDS_BYTES = S * STAGE_BYTES;
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int KK = BK / 16;
+  static constexpr int OUT_N = EPI == EPI_SWIGLU ? BN / 2 : BN;
+  static_assert(IA >= 1 && IB >= 1 && BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "load split");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(S >= 2 && (S - 2) * GROUP < 64, "vmcnt range");
+  static_assert((32 >> SH) % CPR == 0, "swizzle must repeat every 32 rows");
+  static_assert(EPI != EPI_SWIGLU || (TN % 2 == 0 && (BN / 4) % 32 == 0), "SwiGLU halves");
 };
 
-// Output row of accumulator element v of a 32x32 tile for lane group lg.
-__device__ __forceinline__ int acc_row(int v, int lg) { return ((v >> 2) << 3) + (lg << 2) + (v & 3); }
+template <class C>
+__device__ __forceinline__ int swz(int r) {
+  return (r >> C::SH) & (C::CPR - 1);
+}
 
-template <int BM, int BN, int BK, int EPI>
+template <class C>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
-  using C = TileCfg<BM, BN, BK, EPI>;
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (BM + BN) * C::LDK];
-  bf16* const As = smem;                    // [2][BM][LDK]
-  bf16* const Bs = smem + 2 * BM * C::LDK;  // [2][BN][LDK]
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 31, lg = lane >> 5;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const int l32 = lane & 31, lh = lane >> 5;
 
   // tile coordinates: XCD-aware renumbering, then groups of 8 M-tiles so that
   // tiles resident on one XCD share A rows and B columns in its L2
@@ -62,157 +118,340 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
   const int pid = xcd_remap(blockIdx.x, gridDim.x);
   const int bz = pid / per_batch;
   const int t = pid - bz * per_batch;
-  constexpr int G = 8;
-  const int group = t / (G * tilesN);
-  const int first_m = group * G;
-  const int gm = min(tilesM - first_m, G);
-  const int tin = t - group * G * tilesN;
+  constexpr int GRP = 8;
+  const int group = t / (GRP * tilesN);
+  const int first_m = group * GRP;
+  const int gm = min(tilesM - first_m, GRP);
+  const int tin = t - group * GRP * tilesN;
   const int tm = first_m + tin % gm;
   const int tn = tin / gm;
-  const int m0 = tm * BM;
+  const int m0 = tm * C::BM;
   const int n0 = tn * C::OUT_N;
 
-  const bf16* const A = static_cast<const bf16*>(p.A) + bz * p.sA;
-  const bf16* const B = static_cast<const bf16*>(p.B) + bz * p.sB;
+  // buffer resources: each covers the tile's valid rows, so rows past M / N
+  // read as zero
+  const bf16* const Ab = static_cast<const bf16*>(p.A) + bz * p.sA + (int64_t)m0 * p.lda;
+  const uint32_t a_rows = (uint32_t)min(C::BM, p.M - m0);
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(Ab, a_rows * (uint32_t)p.lda * 2u);
+  const bf16* const Bb = static_cast<const bf16*>(p.B) + bz * p.sB + (int64_t)n0 * p.ldb;
+  __amdgpu_buffer_rsrc_t rB;
+  int b_row0;  // first B-tile row this wave loads, relative to its buffer
+  if constexpr (C::EPI == EPI_SWIGLU) {
+    const uint32_t rows = (uint32_t)min(C::BN / 2, p.N - n0);
+    const bool up = w >= 2;  // waves 0,1 load the gate half, waves 2,3 the up half
+    rB = make_rsrc(up ? Bb + p.upOff : Bb, rows * (uint32_t)p.ldb * 2u);
+    b_row0 = w * C::IB * C::RPI - (up ? C::BN / 2 : 0);
+  } else {
+    const uint32_t rows = (uint32_t)min(C::BN, p.N - n0);
+    rB = make_rsrc(Bb, rows * (uint32_t)p.ldb * 2u);
+    b_row0 = w * C::IB * C::RPI;
+  }
 
-  const int lrow = tid / C::CPR;
-  const int lcol = (tid % C::CPR) * 8;
-
-  u32x4 ra[C::CA], rb[C::CB];
-
-  auto load_tile = [&](int k0) {
-    const bool kok = (k0 + lcol) < p.K;  // K is a multiple of 8: chunks are all-in or all-out
+  // per-lane byte offsets of the load instructions (k advances through soffset)
+  const int lrow = lane / C::CPR, lchunk = lane % C::CPR;
+  uint32_t voA[C::IA], voB[C::IB];
+  int chA[C::IA], chB[C::IB];
 #pragma unroll
-    for (int i = 0; i < C::CA; ++i) {
-      const int gr = m0 + lrow + i * C::RPP;
-      if (kok && gr < p.M)
-        ra[i] = *reinterpret_cast<const u32x4*>(A + (int64_t)gr * p.lda + k0 + lcol);
-      else
-        ra[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int j = 0; j < C::IA; ++j) {
+    const int r = (w * C::IA + j) * C::RPI + lrow;  // tile row
+    chA[j] = lchunk ^ swz<C>(r);                     // logical chunk this lane fetches
+    voA[j] = (uint32_t)r * (uint32_t)p.lda * 2u + (uint32_t)chA[j] * 16u;
+  }
 #pragma unroll
-    for (int i = 0; i < C::CB; ++i) {
-      const int r = lrow + i * C::RPP;
-      int gr;
-      const bf16* base;
-      if constexpr (EPI == EPI_SWIGLU) {
-        const bool up = i >= (BN / 2) / C::RPP;  // gate rows fill the first passes, up rows the rest
-        gr = n0 + (up ? r - BN / 2 : r);
-        base = up ? B + p.upOff : B;
-      } else {
-        gr = n0 + r;
-        base = B;
-      }
-      if (kok && gr < p.N)
-        rb[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)gr * p.ldb + k0 + lcol);
-      else
-        rb[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int j = 0; j < C::IB; ++j) {
+    const int r = (w * C::IB + j) * C::RPI + lrow;
+    chB[j] = lchunk ^ swz<C>(r);
+    voB[j] = (uint32_t)(b_row0 + j * C::RPI + lrow) * (uint32_t)p.ldb * 2u + (uint32_t)chB[j] * 16u;
+  }
+
+  const int K = p.K;
+  const int nk = (K + C::BK - 1) / C::BK;  // k-tiles
+  const int nfull = K / C::BK;             // k-tiles with no chunk past K
+  const bool has_tail = nk > nfull;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  // K order: a partial k-tile (K not a multiple of BK) is consumed first, as
+  // tile 0, so that every later tile is full.  Tile t covers k from
+  // k_begin(t); the accumulation order is fixed, so results are
+  // deterministic.
+  auto k_begin = [&](int t) -> int { return has_tail ? (t == 0 ? nfull * C::BK : (t - 1) * C::BK) : t * C::BK; };
+
+  // Loads of full k-tile t into stage STG.  Tiles past the end are still
+  // issued, through buffer resources of size zero (they read zeros and move
+  // no data), so every wave always has the same number of load groups in
+  // flight and one vmcnt value serves every tile boundary.
+  const __amdgpu_buffer_rsrc_t rZ = make_rsrc(Ab, 0u);
+  auto issue = [&](auto stg, int t) {
+    constexpr int STG = decltype(stg)::value;
+    char* sa = smem + STG * C::STAGE_BYTES + w * C::IA * 1024;
+    char* sb = smem + STG * C::STAGE_BYTES + C::A_BYTES + w * C::IB * 1024;
+    const bool live = t < nk;
+    const __amdgpu_buffer_rsrc_t ra = live ? rA : rZ;
+    const __amdgpu_buffer_rsrc_t rb = live ? rB : rZ;
+    const uint32_t so = live ? (uint32_t)k_begin(t) * 2u : 0u;
+#pragma unroll
+    for (int j = 0; j < C::IA; ++j) dma16(ra, sa + j * 1024, voA[j], so);
+#pragma unroll
+    for (int j = 0; j < C::IB; ++j) dma16(rb, sb + j * 1024, voB[j], so);
+  };
+  // The partial tile (tile 0 of stage 0): chunks past K read as zero through
+  // the range check, and are also cleared once the loads have landed.
+  auto issue_partial = [&]() {
+    const int k0 = nfull * C::BK;
+#pragma unroll
+    for (int j = 0; j < C::IA; ++j)
+      dma16(rA, smem + (w * C::IA + j) * 1024, k0 + 8 * chA[j] < K ? voA[j] : kOob, (uint32_t)k0 * 2u);
+#pragma unroll
+    for (int j = 0; j < C::IB; ++j)
+      dma16(rB, smem + C::A_BYTES + (w * C::IB + j) * 1024, k0 + 8 * chB[j] < K ? voB[j] : kOob, (uint32_t)k0 * 2u);
+  };
+  auto clear_partial = [&]() {
+    const int k0 = nfull * C::BK;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < C::IA; ++j)
+      if (k0 + 8 * chA[j] >= K) *reinterpret_cast<u32x4*>(smem + (w * C::IA + j) * 1024 + lane * 16) = z;
+#pragma unroll
+    for (int j = 0; j < C::IB; ++j)
+      if (k0 + 8 * chB[j] >= K) *reinterpret_cast<u32x4*>(smem + C::A_BYTES + (w * C::IB + j) * 1024 + lane * 16) = z;
   };
 
-  auto store_tile = [&](int buf) {
-    bf16* as = As + buf * BM * C::LDK;
-    bf16* bs = Bs + buf * BN * C::LDK;
+  // Fragment addressing.  The swizzle of a fragment row depends on the lane
+  // only, so one per-lane offset per (stage, k-step) covers every subtile; the
+  // subtile itself is a compile-time immediate.
+  const int fsw = swz<C>(l32);
+  const int b_wave_row = C::EPI == EPI_SWIGLU ? wn * (C::BN / 4) : wn * C::WN;
+  int foA[2][C::KK], foB[2][C::KK];
 #pragma unroll
-    for (int i = 0; i < C::CA; ++i)
-      *reinterpret_cast<u32x4*>(as + (lrow + i * C::RPP) * C::LDK + lcol) = ra[i];
+  for (int st = 0; st < 2; ++st)
 #pragma unroll
-    for (int i = 0; i < C::CB; ++i)
-      *reinterpret_cast<u32x4*>(bs + (lrow + i * C::RPP) * C::LDK + lcol) = rb[i];
-  };
-
-  // LDS row of B subtile nt for this wave (gate subtiles first for SwiGLU)
-  auto brow = [&](int nt) -> int {
-    if constexpr (EPI == EPI_SWIGLU)
-      return nt < C::TN / 2 ? wn * (BN / 4) + nt * 32 : BN / 2 + wn * (BN / 4) + (nt - C::TN / 2) * 32;
+    for (int kk = 0; kk < C::KK; ++kk) {
+      const int f = l32 * (C::BK * 2) + (((2 * kk + lh) ^ fsw) << 4) + st * C::STAGE_BYTES;
+      foA[st][kk] = f + wm * C::WM * (C::BK * 2);
+      foB[st][kk] = f + C::A_BYTES + b_wave_row * (C::BK * 2);
+    }
+  auto brow = [](int jn) -> int {  // B-tile row of subtile jn, relative to the wave's first row
+    if constexpr (C::EPI == EPI_SWIGLU)
+      return jn < C::TN / 2 ? jn * 32 : C::BN / 2 + (jn - C::TN / 2) * 32;
     else
-      return wn * C::WN + nt * 32;
+      return jn * 32;
   };
 
-  floatx16 acc[C::TM][C::TN];
+  floatx16 acc[C::TN][C::TM];
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i)
+  for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+
+  bf16x8 af[2][C::TM], bfg[2][C::TN];
+  auto load_frags = [&](auto stg, int kk, int buf) {
+    constexpr int STG = decltype(stg)::value;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+      af[buf][i] = *reinterpret_cast<const bf16x8*>(smem + foA[STG][kk] + i * 32 * (C::BK * 2));
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+      bfg[buf][j] = *reinterpret_cast<const bf16x8*>(smem + foB[STG][kk] + brow(j) * (C::BK * 2));
+  };
+  auto mfmas = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  const int nk = (p.K + BK - 1) / BK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_tile((kt + 1) * BK);  // in flight during the MFMAs below
-
-    const bf16* as = As + cur * BM * C::LDK + (wm * C::WM + lr) * C::LDK + 8 * lg;
-    const bf16* bs = Bs + cur * BN * C::LDK + lr * C::LDK + 8 * lg;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[C::TM], bfr[C::TN];
-#pragma unroll
       for (int i = 0; i < C::TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(as + i * 32 * C::LDK + kk * 16);
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[buf][j], af[buf][i], acc[j][i], 0, 0, 0);
+  };
+  static_assert(C::S == 2, "two LDS stages: tile t+2 is issued at the boundary that frees tile t's stage");
+  static_assert(C::KK % 2 == 0, "fragment buffers alternate per k-step");
+  constexpr int kFrag = C::TM + C::TN;  // fragment reads per k-step
+  constexpr int kMfmaPerRead = (C::TM * C::TN) / kFrag;
+  static_assert(C::GROUP % kFrag == 0 && (C::TM * C::TN) % kFrag == 0, "interleave pattern");
+
+  // Tile t from stage STG: k-steps 0..KK-2 each prefetch the next step's
+  // fragments.  Before the last step's MFMAs comes the tile boundary: wait for
+  // tile t+1, barrier (after it stage STG is free), fetch tile t+1's first
+  // fragments and issue the loads of tile t+2 into stage STG; the last step's
+  // MFMAs cover the latency of both.
+#if TP_GEMM_SPREAD
+  // Instructions [lo, hi) of this wave's load group for tile t into stage STG
+  // (instruction g < IA is A-tile row block g, the rest B-tile row blocks).
+  auto issue_part = [&](auto stg, int t, int lo, int hi) {
+    constexpr int STG = decltype(stg)::value;
+    const bool live = t < nk;
+    const __amdgpu_buffer_rsrc_t ra = live ? rA : rZ;
+    const __amdgpu_buffer_rsrc_t rb = live ? rB : rZ;
+    const uint32_t so = live ? (uint32_t)k_begin(t) * 2u : 0u;
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(bs + brow(j) * C::LDK + kk * 16);
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int g = lo; g < hi; ++g) {
+      if (g < C::IA)
+        dma16(ra, smem + STG * C::STAGE_BYTES + (w * C::IA + g) * 1024, voA[g], so);
+      else
+        dma16(rb, smem + STG * C::STAGE_BYTES + C::A_BYTES + (w * C::IB + g - C::IA) * 1024, voB[g - C::IA], so);
     }
+  };
+  // Tile t from stage STG.  Its k-steps 0..KK-2 each prefetch the next step's
+  // fragments and issue a share of the loads of tile t+1 into the other stage
+  // (freed at the previous boundary), so the load instructions stream out
+  // evenly between the MFMAs instead of queueing up at one point.  Before the
+  // last step's MFMAs: wait for tile t+1, barrier, fetch its first fragments.
+  auto body = [&](auto stg, int t) {
+    constexpr int STG = decltype(stg)::value;
+    using NXT = std::integral_constant<int, STG ^ 1>;
+#pragma unroll
+    for (int kk = 0; kk < C::KK - 1; ++kk) {
+      load_frags(stg, kk + 1, (kk + 1) & 1);
+      issue_part(NXT{}, t + 1, (kk * C::GROUP + C::KK - 2) / (C::KK - 1),
+                 ((kk + 1) * C::GROUP + C::KK - 2) / (C::KK - 1));
+      mfmas(kk & 1);
+#pragma unroll
+      for (int q = 0; q < kFrag; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerRead / 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                 // load to LDS
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerRead - kMfmaPerRead / 2, 0);
+      }
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+    load_frags(NXT{}, 0, 0);  // past the last tile this reads a stale stage, unused
+    mfmas((C::KK - 1) & 1);
+#pragma unroll
+    for (int q = 0; q < kFrag; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerRead, 0);
+    }
+  };
 
-    if (kt + 1 < nk) store_tile(cur ^ 1);
-    __syncthreads();
+  // prologue: tile 0, then its first fragments
+  if (has_tail)
+    issue_partial();
+  else
+    issue(I0{}, 0);
+  wait_vmcnt<0>();
+  if (has_tail) clear_partial();
+  lds_barrier();
+  load_frags(I0{}, 0, 0);
+#else
+  auto body = [&](auto stg, int t) {
+    constexpr int STG = decltype(stg)::value;
+    using NXT = std::integral_constant<int, STG ^ 1>;
+#pragma unroll
+    for (int kk = 0; kk < C::KK - 1; ++kk) {
+      load_frags(stg, kk + 1, (kk + 1) & 1);
+      mfmas(kk & 1);
+#pragma unroll
+      for (int q = 0; q < kFrag; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerRead, 0);  // MFMA
+      }
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+    load_frags(NXT{}, 0, 0);  // past the last tile this reads a stale stage, unused
+    issue(stg, t + 2);
+    mfmas((C::KK - 1) & 1);
+#pragma unroll
+    for (int q = 0; q < kFrag; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x010, C::GROUP / kFrag, 0);  // loads to LDS
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerRead, 0);
+    }
+  };
+
+  // prologue: tiles 0 and 1, then tile 0's first fragments
+  if (has_tail)
+    issue_partial();
+  else
+    issue(I0{}, 0);
+  issue(I1{}, 1);
+  wait_vmcnt<C::GROUP>();
+  if (has_tail) clear_partial();
+  lds_barrier();
+  load_frags(I0{}, 0, 0);
+
+#endif
+
+  // two tiles per trip so that the stages are compile-time constants
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    body(I0{}, kt);
+    body(I1{}, kt + 1);
   }
+  if (kt < nk) body(I0{}, kt);
+  wait_vmcnt<0>();  // no load may still target this workgroup's LDS when it exits
 
   // ---------------------------------------------------------------- epilogue
-  const int mw = m0 + wm * C::WM;
-  if constexpr (EPI == EPI_SWIGLU) {
+  // acc[j][i][4g + e] = C[m][n] with m = m0 + wm*WM + i*32 + l32 and
+  // n = (B-tile row of subtile j) + 8g + 4*lh + e.
+  const int mw = m0 + wm * C::WM + l32;
+  if constexpr (C::EPI == EPI_SWIGLU) {
     bf16* Cp = static_cast<bf16*>(p.C) + bz * p.sC;
 #pragma unroll
-    for (int j = 0; j < C::TN / 2; ++j) {
-      const int n = n0 + wn * (BN / 4) + j * 32 + lr;
-      if (n >= p.N) continue;
+    for (int j = 0; j < C::TN / 2; ++j)
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i)
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * (C::BN / 4) + j * 32 + 8 * g + 4 * lh;
+        if (n >= p.N) continue;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = mw + i * 32 + acc_row(v, lg);
-          if (m < p.M) {
-            const float g = acc[i][j][v], u = acc[i][j + C::TN / 2][v];
-            Cp[(int64_t)m * p.ldc + n] = to_bf16(silu(g) * u);
+        for (int i = 0; i < C::TM; ++i) {
+          const int m = mw + i * 32;
+          if (m >= p.M) continue;
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = to_bf16(silu(acc[j][i][4 * g + e]) * acc[j + C::TN / 2][i][4 * g + e]);
+          bf16* dst = Cp + (int64_t)m * p.ldc + n;
+          if (n + 3 < p.N) {
+            *reinterpret_cast<bf16x4*>(dst) = o;
+          } else {
+            for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
           }
         }
-    }
+      }
   } else {
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int n = n0 + wn * C::WN + j * 32 + lr;
-      if (n >= p.N) continue;
-      float bias = 0.0f;
-      if constexpr (EPI != EPI_PARTIAL) {
-        if (p.bias) bias = static_cast<float>(static_cast<const bf16*>(p.bias)[bz * p.sBias + n]);
-      }
+    for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = mw + i * 32 + acc_row(v, lg);
-          if (m >= p.M) continue;
-          const int64_t off = bz * p.sC + (int64_t)m * p.ldc + n;
-          const float x = acc[i][j][v];
-          if constexpr (EPI == EPI_PARTIAL) {
-            static_cast<float*>(p.C)[off] = x;
-          } else if constexpr (EPI == EPI_GELU) {
-            static_cast<bf16*>(p.C)[off] = to_bf16(gelu_erf(x + bias));
-          } else {
-            static_cast<bf16*>(p.C)[off] = to_bf16(x + bias);
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * C::WN + j * 32 + 8 * g + 4 * lh;
+        if (n >= p.N) continue;
+        float bias[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (C::EPI != EPI_PARTIAL) {
+          if (p.bias) {
+            const bf16* bp = static_cast<const bf16*>(p.bias) + bz * p.sBias + n;
+            for (int e = 0; e < 4; ++e) bias[e] = n + e < p.N ? static_cast<float>(bp[e]) : 0.0f;
           }
         }
-    }
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+          const int m = mw + i * 32;
+          if (m >= p.M) continue;
+          const int64_t off = bz * p.sC + (int64_t)m * p.ldc + n;
+          if constexpr (C::EPI == EPI_PARTIAL) {
+            float* dst = static_cast<float*>(p.C) + off;
+            const floatx4 o = {acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]};
+            if (n + 3 < p.N) {
+              *reinterpret_cast<floatx4*>(dst) = o;
+            } else {
+              for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
+            }
+          } else {
+            bf16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x = acc[j][i][4 * g + e] + bias[e];
+              o[e] = to_bf16(C::EPI == EPI_GELU ? gelu_erf(x) : x);
+            }
+            bf16* dst = static_cast<bf16*>(p.C) + off;
+            if (n + 3 < p.N) {
+              *reinterpret_cast<bf16x4*>(dst) = o;
+            } else {
+              for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
+            }
+          }
+        }
+      }
   }
 }
 
@@ -309,28 +548,25 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p, int ti
   }
 }
 
-template <int BM, int BN, int BK, int EPI>
+template <class C>
 hipError_t launch_bf16_cfg(const GemmParams& p, hipStream_t s) {
-  using C = TileCfg<BM, BN, BK, EPI>;
-  const int tilesM = (p.M + BM - 1) / BM;
+  const int tilesM = (p.M + C::BM - 1) / C::BM;
   const int tilesN = (p.N + C::OUT_N - 1) / C::OUT_N;
   const int64_t grid = (int64_t)tilesM * tilesN * p.batch;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, EPI>), dim3((unsigned)grid), dim3(kThreads), 0, s, p,
-                     tilesM, tilesN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<C>), dim3((unsigned)grid), dim3(kThreads), 0, s, p, tilesM, tilesN);
   return hipGetLastError();
 }
 
 template <int EPI>
 hipError_t launch_bf16_epi(const GemmParams& p, hipStream_t s) {
-  // Large problems take 256x256 tiles (128x128 per wave, LDS traffic per flop
-  // halved against 64x64 waves); problems that would not put two tiles on
-  // every CU take 128x128 tiles.
+  // 256x256 tiles (128x128 per wave) when they fill every CU at least once;
+  // smaller problems take 128x128 tiles, two workgroups per CU.
   constexpr int kCUs = 256;
   const int out256 = (EPI == EPI_SWIGLU) ? 128 : 256;
   const int64_t big = (int64_t)((p.M + 255) / 256) * ((p.N + out256 - 1) / out256) * p.batch;
-  if (big >= 2 * kCUs) return launch_bf16_cfg<256, 256, 64, EPI>(p, s);
-  return launch_bf16_cfg<128, 128, 64, EPI>(p, s);
+  if (big >= kCUs) return launch_bf16_cfg<G<256, 256, 64, 2, TP_GEMM_SH, EPI>>(p, s);
+  return launch_bf16_cfg<G<128, 128, 64, 2, TP_GEMM_SH, EPI>>(p, s);
 }
 
 }  // namespace

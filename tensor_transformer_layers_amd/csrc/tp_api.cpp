@@ -340,6 +340,8 @@ tp_status tp_column_linear(void* stream, tp_dtype dt, tp_act act, int64_t T, int
   TP_TRY(check_matrix("W_i", W_i, act == TP_ACT_SWIGLU ? 2 * Ns : Ns, K, ldw, vec));
   if (!Y_i) return fail(TP_ERR_NULL, "Y_i is NULL");
   if (ldy < Ns) return fail(TP_ERR_SHAPE, "ldy %lld < Ns %lld", (long long)ldy, (long long)Ns);
+  if (!aligned16(Y_i)) return fail(TP_ERR_ALIGN, "Y_i is not 16-byte aligned");
+  if (ldy % vec) return fail(TP_ERR_ALIGN, "ldy %lld is not a multiple of %lld", (long long)ldy, (long long)vec);
   if (T > kIntMax || (act == TP_ACT_SWIGLU ? 2 * Ns : Ns) > kIntMax) return fail(TP_ERR_SHAPE, "size exceeds 2^31-1");
   if (T == 0) return ok();
   tp::GemmParams p = gemm(X, ldx, 0, W_i, ldw, 0, Y_i, ldy, 0, T, Ns, K, 1);
@@ -361,6 +363,8 @@ tp_status tp_row_linear_partial(void* stream, tp_dtype dt, int64_t T, int64_t Ks
   TP_TRY(check_matrix("W_i", W_i, Nout, Ks, ldw, vec));
   if (!P_i) return fail(TP_ERR_NULL, "P_i is NULL");
   if (ldp < Nout) return fail(TP_ERR_SHAPE, "ldp %lld < Nout %lld", (long long)ldp, (long long)Nout);
+  if (!aligned16(P_i)) return fail(TP_ERR_ALIGN, "P_i is not 16-byte aligned");
+  if (ldp % 4) return fail(TP_ERR_ALIGN, "ldp %lld is not a multiple of 4", (long long)ldp);
   if (T > kIntMax) return fail(TP_ERR_SHAPE, "T exceeds 2^31-1");
   if (T == 0) return ok();
   const tp::GemmParams p = gemm(X_i, ldx, 0, W_i, ldw, 0, P_i, ldp, 0, T, Nout, Ks, 1);

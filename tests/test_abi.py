@@ -147,6 +147,11 @@ def test_linear_and_reduce_validation(L):
     assert s == tp.TP_ERR_SHAPE and "leading dimension" in tp.last_error()
     s = tp.tp_row_linear_partial(None, tp.TP_F32, 16, 64, 16, FAKE, 64, None, 64, FAKE, 16)
     assert s == tp.TP_ERR_NULL
+    # output leading dimensions must keep the vector stores aligned
+    s = tp.tp_column_linear(None, tp.TP_BF16, tp.TP_ACT_GELU, 16, 64, 16, FAKE, 64, FAKE, 64, None, FAKE, 20)
+    assert s == tp.TP_ERR_ALIGN and "ldy" in tp.last_error()
+    s = tp.tp_row_linear_partial(None, tp.TP_BF16, 16, 64, 16, FAKE, 64, FAKE, 64, FAKE, 18)
+    assert s == tp.TP_ERR_ALIGN and "ldp" in tp.last_error()
     # partials overlapping
     s = tp.tp_reduce_partials(None, tp.TP_BF16, 4, 8, 16, FAKE, 64, None, FAKE, 1, -1)
     assert s == tp.TP_ERR_SHAPE and "overlap" in tp.last_error()
