@@ -383,75 +383,105 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
   wait_vmcnt<0>();  // no load may still target this workgroup's LDS when it exits
 
   // ---------------------------------------------------------------- epilogue
-  // acc[j][i][4g + e] = C[m][n] with m = m0 + wm*WM + i*32 + l32 and
-  // n = (B-tile row of subtile j) + 8g + 4*lh + e.
-  const int mw = m0 + wm * C::WM + l32;
-  if constexpr (C::EPI == EPI_SWIGLU) {
-    bf16* Cp = static_cast<bf16*>(p.C) + bz * p.sC;
+  // The accumulators go through LDS so that the output leaves in full row
+  // segments (16 lanes per 256-byte fp32 row piece, 8-byte bf16 pieces) from
+  // a compact loop instead of per-element code.  acc[j][i][4g + e] holds
+  // C[m][n] with m = m0 + wm*WM + i*32 + l32 and n = (B-tile row of subtile
+  // j) + 8g + 4*lh + e.  Each wave stages its rows x 64 floats per phase in
+  // its own 256-byte-row region, 16-byte chunk c of row r stored at chunk
+  // c ^ (r & 15) (conflict-free for both the column writes and the row reads).
+  // Phase h takes subtiles (2h, 2h+1), or for SwiGLU the gate subtile h and
+  // its up subtile h + TN/2.
+  lds_barrier();  // every wave is done with the operand stages
+  char* const ep = smem + w * (C::WM * 256);
+  static_assert(4 * C::WM * 256 <= C::LDS_BYTES, "epilogue staging fits the operand stages");
+  constexpr bool SWI = C::EPI == EPI_SWIGLU;
 #pragma unroll
-    for (int j = 0; j < C::TN / 2; ++j)
+  for (int h = 0; h < C::TN / 2; ++h) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * (C::BN / 4) + j * 32 + 8 * g + 4 * lh;
-        if (n >= p.N) continue;
+    for (int half = 0; half < 2; ++half) {
+      const int j = SWI ? h + half * (C::TN / 2) : 2 * h + half;
 #pragma unroll
-        for (int i = 0; i < C::TM; ++i) {
-          const int m = mw + i * 32;
-          if (m >= p.M) continue;
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r = i * 32 + l32;
+          const int c = half * 8 + 2 * g + lh;  // 16-byte chunk: columns 4c .. 4c+3
+          const floatx4 v = {acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]};
+          *reinterpret_cast<floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4)) = v;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+
+    if constexpr (SWI) {
+      // 8 lanes per row: gate chunk c, up chunk c + 8 -> 4 outputs
+      const int c = lane & 7;
+      const int n = n0 + wn * (C::BN / 4) + 32 * h + 4 * c;
+      bf16* Cp = static_cast<bf16*>(p.C) + bz * p.sC;
+#pragma unroll 2
+      for (int it = 0; it < C::WM / 8; ++it) {
+        const int r = it * 8 + (lane >> 3);
+        const int m = m0 + wm * C::WM + r;
+        const floatx4 gv = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
+        const floatx4 uv = *reinterpret_cast<const floatx4*>(ep + r * 256 + (((c + 8) ^ (r & 15)) << 4));
+        if (m < p.M && n < p.N) {
           bf16x4 o;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = to_bf16(silu(acc[j][i][4 * g + e]) * acc[j + C::TN / 2][i][4 * g + e]);
+          for (int e = 0; e < 4; ++e) o[e] = to_bf16(silu_bf16out(gv[e]) * uv[e]);
           bf16* dst = Cp + (int64_t)m * p.ldc + n;
-          if (n + 3 < p.N) {
+          if (n + 3 < p.N)
             *reinterpret_cast<bf16x4*>(dst) = o;
-          } else {
+          else
             for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
-          }
         }
       }
-  } else {
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * C::WN + j * 32 + 8 * g + 4 * lh;
-        if (n >= p.N) continue;
-        float bias[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (C::EPI != EPI_PARTIAL) {
-          if (p.bias) {
-            const bf16* bp = static_cast<const bf16*>(p.bias) + bz * p.sBias + n;
-            for (int e = 0; e < 4; ++e) bias[e] = n + e < p.N ? static_cast<float>(bp[e]) : 0.0f;
-          }
+    } else {
+      // 16 lanes per row: chunk c -> 4 outputs
+      const int c = lane & 15;
+      const int n = n0 + wn * C::WN + 64 * h + 4 * c;
+      float bias[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (C::EPI != EPI_PARTIAL) {
+        if (p.bias) {
+          const bf16* bp = static_cast<const bf16*>(p.bias) + bz * p.sBias;
+          for (int e = 0; e < 4; ++e) bias[e] = n + e < p.N ? static_cast<float>(bp[n + e]) : 0.0f;
         }
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i) {
-          const int m = mw + i * 32;
-          if (m >= p.M) continue;
+      }
+#pragma unroll 2
+      for (int it = 0; it < C::WM / 4; ++it) {
+        const int r = it * 4 + (lane >> 4);
+        const int m = m0 + wm * C::WM + r;
+        const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
+        if (m < p.M && n < p.N) {
           const int64_t off = bz * p.sC + (int64_t)m * p.ldc + n;
           if constexpr (C::EPI == EPI_PARTIAL) {
             float* dst = static_cast<float*>(p.C) + off;
-            const floatx4 o = {acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]};
-            if (n + 3 < p.N) {
-              *reinterpret_cast<floatx4*>(dst) = o;
-            } else {
-              for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
-            }
+            if (n + 3 < p.N)
+              *reinterpret_cast<floatx4*>(dst) = v;
+            else
+              for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = v[e];
           } else {
             bf16x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float x = acc[j][i][4 * g + e] + bias[e];
-              o[e] = to_bf16(C::EPI == EPI_GELU ? gelu_erf(x) : x);
+              const float x = v[e] + bias[e];
+              o[e] = to_bf16(C::EPI == EPI_GELU ? gelu_bf16out(x) : x);
             }
             bf16* dst = static_cast<bf16*>(p.C) + off;
-            if (n + 3 < p.N) {
+            if (n + 3 < p.N)
               *reinterpret_cast<bf16x4*>(dst) = o;
-            } else {
+            else
               for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
-            }
           }
         }
       }
+    }
+    if (h + 1 < C::TN / 2) {  // the next phase reuses the region
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    }
   }
 }
 

@@ -7,13 +7,15 @@
 // Reduce-scatter along the sequence (one contiguous row block per rank):
 // "张量并行", Megatron-SP section; blog post section 4.3.
 //
-// HBM-bound streaming kernel: every thread owns 8 consecutive outputs, reads
-// them from each partial with two 16-byte non-temporal loads (the partials are
-// read exactly once), adds the partials strictly in shard order
-// ((P0 + P1) + P2) + ... with plain fp32 adds (no FMA can form: there are no
-// multiplies), adds the bias, and writes 16 (bf16) or 32 (fp32) contiguous
-// bytes.  Grid-stride over the [rows x H] region; no atomics, so the result is
-// bit-identical run to run.
+// HBM-bound streaming kernel.  Thread t of a block owns 4 consecutive outputs
+// in each of U consecutive 1024-float stretches, so every load and store
+// instruction of a wave covers one contiguous span (1 KB of fp32 per load).
+// All N*U partial loads are issued before the adds, which run strictly in
+// shard order ((P0 + P1) + P2) + ... as plain fp32 adds (no FMA can form:
+// there are no multiplies); then the bias, one RNE cast, and an 8-byte (bf16)
+// or 16-byte (fp32) store per stretch.  The partials are read exactly once
+// (non-temporal loads).  Grid-stride over the [rows x H] region; no atomics,
+// so the result is bit-identical run to run.
 #include "tp_device.hpp"
 #include "tp_kernels.hpp"
 
@@ -26,78 +28,80 @@ __device__ __forceinline__ floatx4 ld_nt(const float* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
 }
 
+constexpr int kU = 2;  // 16-byte stretches per thread per trip
+
 template <bool OUT_BF16, int NP>
-__global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceParams p, int64_t n8) {
+__global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceParams p, int64_t n4) {
   const int np = NP > 0 ? NP : p.n_parts;
   const float* const src0 = p.P + p.row0 * p.H;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < n8; g += stride) {
-    const int64_t e = g * 8;
-    const float* s = src0 + e;
-    floatx4 lo = ld_nt(s), hi = ld_nt(s + 4);
+  const int64_t step = (int64_t)gridDim.x * kThreads * kU;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * kU + threadIdx.x; base < n4; base += step) {
+    floatx4 acc[kU];
+    bool ok[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      ok[u] = base + u * kThreads < n4;
+      acc[u] = ok[u] ? ld_nt(src0 + (base + u * kThreads) * 4) : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
     if constexpr (NP > 0) {
-      floatx4 plo[NP > 1 ? NP - 1 : 1], phi[NP > 1 ? NP - 1 : 1];
+      floatx4 part[NP > 1 ? NP - 1 : 1][kU];
 #pragma unroll
-      for (int k = 1; k < NP; ++k) {  // issue every load first ...
-        plo[k - 1] = ld_nt(s + k * p.part_stride);
-        phi[k - 1] = ld_nt(s + k * p.part_stride + 4);
-      }
+      for (int k = 1; k < NP; ++k)  // issue every load first ...
 #pragma unroll
-      for (int k = 1; k < NP; ++k) {  // ... then add strictly in shard order
-        lo += plo[k - 1];
-        hi += phi[k - 1];
-      }
+        for (int u = 0; u < kU; ++u)
+          part[k - 1][u] = ok[u] ? ld_nt(src0 + k * p.part_stride + (base + u * kThreads) * 4)
+                                 : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 1; k < NP; ++k)  // ... then add strictly in shard order
+#pragma unroll
+        for (int u = 0; u < kU; ++u) acc[u] += part[k - 1][u];
     } else {
-      for (int k = 1; k < np; ++k) {
-        lo += ld_nt(s + k * p.part_stride);
-        hi += ld_nt(s + k * p.part_stride + 4);
-      }
-    }
-    if (p.bias) {
-      const int64_t c = e % p.H;  // H is a multiple of 8: the 8 outputs share a row
-      if constexpr (OUT_BF16) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(p.bias) + c);
+      for (int k = 1; k < np; ++k)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          lo[j] += static_cast<float>(b[j]);
-          hi[j] += static_cast<float>(b[j + 4]);
+        for (int u = 0; u < kU; ++u)
+          if (ok[u]) acc[u] += ld_nt(src0 + k * p.part_stride + (base + u * kThreads) * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (!ok[u]) continue;
+      const int64_t e = (base + u * kThreads) * 4;
+      if (p.bias) {
+        const int64_t c = e % p.H;  // H is a multiple of 4: the 4 outputs share a row
+        if constexpr (OUT_BF16) {
+          const bf16x4 b = *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(p.bias) + c);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[u][j] += static_cast<float>(b[j]);
+        } else {
+          acc[u] += *reinterpret_cast<const floatx4*>(static_cast<const float*>(p.bias) + c);
         }
-      } else {
-        const float* b = static_cast<const float*>(p.bias) + c;
-        lo += *reinterpret_cast<const floatx4*>(b);
-        hi += *reinterpret_cast<const floatx4*>(b + 4);
       }
-    }
-    if constexpr (OUT_BF16) {
-      bf16x8 o;
+      if constexpr (OUT_BF16) {
+        bf16x4 o;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        o[j] = to_bf16(lo[j]);
-        o[j + 4] = to_bf16(hi[j]);
+        for (int j = 0; j < 4; ++j) o[j] = to_bf16(acc[u][j]);
+        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.Y) + e) = o;
+      } else {
+        *reinterpret_cast<floatx4*>(static_cast<float*>(p.Y) + e) = acc[u];
       }
-      *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.Y) + e) = o;
-    } else {
-      float* y = static_cast<float*>(p.Y) + e;
-      *reinterpret_cast<floatx4*>(y) = lo;
-      *reinterpret_cast<floatx4*>(y + 4) = hi;
     }
   }
 }
 
 template <bool OUT_BF16>
 hipError_t launch_typed(const ReduceParams& p, hipStream_t s) {
-  const int64_t n8 = p.rows * p.H / 8;
-  if (n8 <= 0) return hipSuccess;
-  // enough resident waves to keep ~8 x 32 bytes per lane in flight on every CU;
-  // beyond that the grid-stride loop takes over
-  const int64_t blocks = std::min<int64_t>((n8 + kThreads - 1) / kThreads, 256 * 16);
+  const int64_t n4 = p.rows * p.H / 4;
+  if (n4 <= 0) return hipSuccess;
+  // enough resident waves to keep every CU's memory pipeline full; beyond
+  // that the grid-stride loop takes over
+  const int64_t per_block = (int64_t)kThreads * kU;
+  const int64_t blocks = std::min<int64_t>((n4 + per_block - 1) / per_block, 256 * 8);
   const dim3 g((unsigned)blocks), b(kThreads);
   switch (p.n_parts) {
-    case 1: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 1>), g, b, 0, s, p, n8); break;
-    case 2: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 2>), g, b, 0, s, p, n8); break;
-    case 4: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 4>), g, b, 0, s, p, n8); break;
-    case 8: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 8>), g, b, 0, s, p, n8); break;
-    default: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 0>), g, b, 0, s, p, n8); break;
+    case 1: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 1>), g, b, 0, s, p, n4); break;
+    case 2: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 2>), g, b, 0, s, p, n4); break;
+    case 4: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 4>), g, b, 0, s, p, n4); break;
+    case 8: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 8>), g, b, 0, s, p, n4); break;
+    default: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 0>), g, b, 0, s, p, n4); break;
   }
   return hipGetLastError();
 }

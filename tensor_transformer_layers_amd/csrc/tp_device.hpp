@@ -26,6 +26,28 @@ __device__ __forceinline__ float gelu_erf(float x) {
 // SiLU with beta = 1: g * sigmoid(g) = g / (1 + e^-g).
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// GELU for bf16 outputs: the same exact (erf) form, with erf evaluated by the
+// rational-exponential approximation 7.1.26 of Abramowitz & Stegun, Handbook
+// of Mathematical Functions (absolute error <= 1.5e-7 in erf, far below bf16
+// resolution): erf(x) = 1 - t*(a1 + t*(a2 + t*(a3 + t*(a4 + t*a5)))) e^(-x^2),
+// t = 1 / (1 + p x), x >= 0.  With q = z/2 * (1 - erf(|z|/sqrt 2)):
+// GELU(z) = z - q for z >= 0 and q for z < 0, which avoids cancelling
+// 1 + erf near -1 for negative z.  One exp, one reciprocal, no branches.
+__device__ __forceinline__ float gelu_bf16out(float z) {
+  const float x = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  const float poly =
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f), -0.284496736f), 0.254829592f);
+  const float q = 0.5f * z * poly * __expf(-x * x);
+  return z >= 0.0f ? z - q : q;
+}
+
+// SiLU for bf16 outputs: g / (1 + e^-g) with the hardware exponential and
+// reciprocal (relative error ~1e-6, far below bf16 resolution).
+__device__ __forceinline__ float silu_bf16out(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
 // fp32 -> bf16, IEEE round-to-nearest-even (the compiler emits gfx950's
 // v_cvt_pk_bf16_f32, which rounds to nearest even).
 __device__ __forceinline__ bf16 to_bf16(float x) { return static_cast<bf16>(x); }
