@@ -88,19 +88,86 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+# launch order of the library's kernels within one step, per workload kind
+LAUNCH_ORDER = {
+    "mlp": ["mlp_column_gemm", "mlp_row_gemm", "reduce_partials"],
+    "attn": ["attn_qk_gemm", "attn_vt_gemm", "attn_core", "attn_out_gemm", "reduce_partials"],
+}
+
+
+def traffic_path(workload_name):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload_name}.txt")
+
+
 def measured_traffic(kernel, workload_name, src_hash):
-    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was
-    taken on the current kernel sources; otherwise None."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload_name}.json")
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC
+    summary of this workload, if it was taken on the current kernel sources;
+    otherwise None."""
+    p = traffic_path(workload_name)
     if not os.path.exists(p):
         return None
-    try:
-        d = json.load(open(p))
-    except (OSError, ValueError):
-        return None
-    if d.get("kernel_source_hash") != src_hash:
-        return None
-    return d.get("hbm_bytes_per_launch")
+    found, ok_hash = None, False
+    for line in open(p):
+        f = line.split()
+        if len(f) == 2 and f[0] == "kernel_source_hash":
+            ok_hash = f[1] == src_hash
+        if len(f) == 3 and f[0] == "traffic_bytes" and f[1] == kernel:
+            found = float(f[2])
+    return found if ok_hash else None
+
+
+def write_traffic(w, share, pmc_dir, src_hash, argv_line):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE, each with --calib-copy) into profiles/traffic_<workload>.txt.
+
+    Each counter is scaled by what it reads for the 1 GiB device copy
+    (2^30 bytes read, 2^30 written).  Library kernels are matched to names by
+    their launch order within a step."""
+    import csv
+    import collections
+
+    order = LAUNCH_ORDER["attn" if w.kind == "attn" else "mlp"]
+    per = {}
+    factor = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = list(csv.DictReader(open(os.path.join(pmc_dir, counter, "run_counter_collection.csv"))))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        big = max(copies, key=lambda r: int(r["Grid_Size"]))
+        factor[counter] = float(2 ** 30) / (float(big["Counter_Value"]) * 1024.0)
+        ours = [r for r in rows if "tp::" in r["Kernel_Name"]]
+        vals = collections.defaultdict(list)
+        for i, r in enumerate(ours):
+            vals[order[i % len(order)]].append(float(r["Counter_Value"]))
+        per[counter] = {k: sum(v) / len(v) for k, v in vals.items()}
+    lines = [
+        f"# HBM traffic per launch: {w.name} ({share})",
+        "#",
+        "# Commands (from /tmp on the GPU host, REPO = repository root):",
+        f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d DIR/FETCH_SIZE -o run -- python3 $REPO/bench.py {argv_line}",
+        f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d DIR/WRITE_SIZE -o run -- python3 $REPO/bench.py {argv_line}",
+        f"#   python3 $REPO/bench.py --config {w.key} --share {share} --traffic-from DIR",
+        "#",
+        f"# Calibration (1 GiB device copy): FETCH_SIZE x {factor['FETCH_SIZE']:.4f}, WRITE_SIZE x {factor['WRITE_SIZE']:.4f}",
+        "#",
+        "# kernel                 FETCH_KiB      WRITE_KiB      read_bytes      write_bytes     total_bytes",
+    ]
+    out = {}
+    for k in order:
+        if k not in per["FETCH_SIZE"]:
+            continue
+        rb = per["FETCH_SIZE"][k] * 1024.0 * factor["FETCH_SIZE"]
+        wb = per["WRITE_SIZE"].get(k, 0.0) * 1024.0 * factor["WRITE_SIZE"]
+        out[k] = rb + wb
+        lines.append(f"# {k:22s} {per['FETCH_SIZE'][k]:13.1f} {per['WRITE_SIZE'].get(k, 0.0):13.1f} "
+                     f"{rb:15.0f} {wb:15.0f} {rb + wb:15.0f}")
+    lines.append(f"kernel_source_hash {src_hash}")
+    for k, v in out.items():
+        lines.append(f"traffic_bytes {k} {v:.0f}")
+    path = traffic_path(w.name)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
 
 
 def cpu_baseline(w, host, seconds):
@@ -119,8 +186,11 @@ def cpu_baseline(w, host, seconds):
     order = np.random.default_rng(w.seed + 98).permutation(w.T)  # seeded order of all token rows
     done, flops = 0, 0.0
     t0 = time.perf_counter()
-    while done < w.T and time.perf_counter() - t0 < seconds:
-        rows = np.sort(order[done:done + chunk])
+    # cycle through the seeded row order (a small workload is passed over
+    # several times) until the time budget is spent
+    while time.perf_counter() - t0 < seconds:
+        start = done % w.T
+        rows = np.sort(order[start:start + chunk])
         R.workload(w.kind, host, w.batch, w.seq, w.heads, rows=rows)
         if w.kind == "attn":
             hl_all = w.heads
@@ -131,7 +201,8 @@ def cpu_baseline(w, host, seconds):
         done += len(rows)
     el = time.perf_counter() - t0
     return {"value": round(flops / el / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} of {w.T} token rows (seeded), fp64 numpy/scipy, {el:.1f} s"}
+            "sample": f"{done} token rows in seeded order over the workload's {w.T} "
+                      f"({done / w.T:.2f} passes), fp64 numpy/scipy, {el:.1f} s"}
 
 
 def main():
@@ -145,7 +216,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (PMC traffic calibration)")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="write profiles/traffic_<workload>.txt from rocprofv3 --pmc csv runs under DIR "
+                         "(DIR/FETCH_SIZE, DIR/WRITE_SIZE) and exit; runs on the host, no GPU")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        from tensor_transformer_layers_amd import configs
+
+        w = configs.CONFIGS[args.config]
+        argv = f"--config {args.config} --share {args.share} --steps 3 --warmup 1 --no-cpu-baseline --calib-copy"
+        print(write_traffic(w, args.share, args.traffic_from, kernel_source_hash(), argv))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -112,19 +112,28 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
   const int wm = w >> 1, wn = w & 1;
   const int l32 = lane & 31, lh = lane >> 5;
 
-  // tile coordinates: XCD-aware renumbering, then groups of 8 M-tiles so that
-  // tiles resident on one XCD share A rows and B columns in its L2
-  const int per_batch = tilesM * tilesN;
+  // Tile coordinates: XCD-aware renumbering, then groups of 8 M-tiles so that
+  // tiles resident on one XCD share A rows and B columns in its L2.  When
+  // every problem of the batch reads the same A (or B) operand -- the shards'
+  // column GEMMs all read X -- the batch index joins the N (or M) tile index,
+  // so the shards' tiles over the same rows run together and one pass over
+  // the shared operand serves all of them.
+  const bool shareA = p.sA == 0 && p.batch > 1, shareB = !shareA && p.sB == 0 && p.batch > 1;
+  const int vM = shareB ? tilesM * p.batch : tilesM;  // virtual tile grid
+  const int vN = shareA ? tilesN * p.batch : tilesN;
   const int pid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bz = pid / per_batch;
-  const int t = pid - bz * per_batch;
+  const int bz0 = (shareA || shareB) ? 0 : pid / (vM * vN);
+  const int t = pid - bz0 * (vM * vN);
   constexpr int GRP = 8;
-  const int group = t / (GRP * tilesN);
+  const int group = t / (GRP * vN);
   const int first_m = group * GRP;
-  const int gm = min(tilesM - first_m, GRP);
-  const int tin = t - group * GRP * tilesN;
-  const int tm = first_m + tin % gm;
-  const int tn = tin / gm;
+  const int gm = min(vM - first_m, GRP);
+  const int tin = t - group * GRP * vN;
+  const int vm = first_m + tin % gm;
+  const int vn = tin / gm;
+  const int bz = shareA ? vn / tilesN : shareB ? vm / tilesM : bz0;
+  const int tm = shareB ? vm - bz * tilesM : vm;
+  const int tn = shareA ? vn - bz * tilesN : vn;
   const int m0 = tm * C::BM;
   const int n0 = tn * C::OUT_N;
 
