@@ -79,12 +79,25 @@ def roofline(w, name, flops, nbytes, avg_s):
             "frac": round(ach / PEAK_HBM, 4)}
 
 
-def kernel_source_hash():
+# source files each kernel's code and launch shape come from (besides the
+# shared device headers and the dispatch code in tp_api.cpp)
+KERNEL_SOURCES = {
+    "mlp_column_gemm": "gemm.hip", "mlp_row_gemm": "gemm.hip", "attn_qk_gemm": "gemm.hip",
+    "attn_vt_gemm": "gemm.hip", "attn_out_gemm": "gemm.hip", "attn_core": "attention.hip",
+    "reduce_partials": "reduce.hip",
+}
+
+
+def kernel_source_hash(kernel=None):
+    """Hash of the sources behind one kernel (or of every kernel source)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tensor_transformer_layers_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    if kernel is None:
+        files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp", ".cpp")))
+    else:
+        files = [KERNEL_SOURCES[kernel], "tp_device.hpp", "tp_kernels.hpp", "tp_api.cpp"]
+    for f in files:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -99,24 +112,21 @@ def traffic_path(workload_name):
     return os.path.join(ROOT, "profiles", f"traffic_{workload_name}.txt")
 
 
-def measured_traffic(kernel, workload_name, src_hash):
+def measured_traffic(kernel, workload_name):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC
-    summary of this workload, if it was taken on the current kernel sources;
-    otherwise None."""
+    summary of this workload, if it was taken on the kernel's current
+    sources; otherwise None."""
     p = traffic_path(workload_name)
     if not os.path.exists(p):
         return None
-    found, ok_hash = None, False
     for line in open(p):
         f = line.split()
-        if len(f) == 2 and f[0] == "kernel_source_hash":
-            ok_hash = f[1] == src_hash
-        if len(f) == 3 and f[0] == "traffic_bytes" and f[1] == kernel:
-            found = float(f[2])
-    return found if ok_hash else None
+        if len(f) == 4 and f[0] == "traffic_bytes" and f[1] == kernel:
+            return float(f[2]) if f[3] == kernel_source_hash(kernel) else None
+    return None
 
 
-def write_traffic(w, share, pmc_dir, src_hash, argv_line):
+def write_traffic(w, share, pmc_dir, argv_line):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
     WRITE_SIZE, each with --calib-copy) into profiles/traffic_<workload>.txt.
 
@@ -161,9 +171,9 @@ def write_traffic(w, share, pmc_dir, src_hash, argv_line):
         out[k] = rb + wb
         lines.append(f"# {k:22s} {per['FETCH_SIZE'][k]:13.1f} {per['WRITE_SIZE'].get(k, 0.0):13.1f} "
                      f"{rb:15.0f} {wb:15.0f} {rb + wb:15.0f}")
-    lines.append(f"kernel_source_hash {src_hash}")
+    lines.append("# traffic_bytes <kernel> <bytes per launch> <hash of that kernel's sources>")
     for k, v in out.items():
-        lines.append(f"traffic_bytes {k} {v:.0f}")
+        lines.append(f"traffic_bytes {k} {v:.0f} {kernel_source_hash(k)}")
     path = traffic_path(w.name)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -226,7 +236,7 @@ def main():
 
         w = configs.CONFIGS[args.config]
         argv = f"--config {args.config} --share {args.share} --steps 3 --warmup 1 --no-cpu-baseline --calib-copy"
-        print(write_traffic(w, args.share, args.traffic_from, kernel_source_hash(), argv))
+        print(write_traffic(w, args.share, args.traffic_from, argv))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -316,7 +326,7 @@ def main():
     roof["kernel"] = dom
     roof["avg_us"] = round(avg * 1e6, 2)
     roof["algorithmic"] = {"flop": f, "bytes": b}
-    roof["traffic"] = measured_traffic(dom, w.name, src_hash)
+    roof["traffic"] = measured_traffic(dom, w.name)
 
     out = {
         "metric": METRIC,

@@ -16,8 +16,14 @@
 // between A and B, so the keys of a 16-wide step are taken in the order the
 // score layout hands them over.
 //
-// Workgroup = 4 waves x 32 queries; key blocks of 64 are double-buffered in
-// LDS.  Only the two key blocks that straddle the diagonal are masked.
+// Workgroup = 8 waves x 32 queries (two waves per SIMD, so one wave's softmax
+// arithmetic overlaps the other's MFMAs), or 4 waves when the grid would not
+// fill the chip.  Key blocks of 64 (K [64 x 128] and
+// V^T [128 x 64], 32 KB) stream through a 4-stage LDS ring with the
+// buffer-load-to-LDS path, three blocks ahead of use; both are XOR-swizzled at
+// 16-byte granularity so the fragment reads of consecutive rows spread over
+// the banks.  A wave skips the MFMAs of key blocks that lie wholly after its
+// last query; only the blocks that straddle its diagonal are masked.
 // Workgroups are ordered heaviest (last query block) first.
 #include <math.h>
 
@@ -27,22 +33,56 @@
 namespace tp {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int D = 128;        // head dim
-constexpr int BQ = 128;       // queries per workgroup (32 per wave)
-constexpr int BKEY = 64;      // keys per block
-constexpr int KLD = D + 8;    // LDS row (key) of K, padded
-constexpr int VLD = BKEY + 8; // LDS row (d) of V^T, padded
+#define TP_LDS __attribute__((address_space(3)))
 
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BKEY * KLD];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][D * VLD];
+constexpr int D = 128;             // head dim
+constexpr int BKEY = 64;           // keys per block
+constexpr int NST = 4;             // LDS ring stages
+constexpr int K_BYTES = BKEY * D * 2;    // K block: 64 rows of 256 bytes
+constexpr int V_BYTES = D * BKEY * 2;    // V^T block: 128 rows of 128 bytes
+constexpr int ST_BYTES = K_BYTES + V_BYTES;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // word 3 = 0x00020000: raw (untyped) 32-bit data format on gfx9-family parts
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TP_LDS void*)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+
+// 16-byte chunk position of logical chunk c in row r of a K block (16 chunks
+// per row) and of a V^T block (8 chunks per row).
+__device__ __forceinline__ int kswz(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int vswz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+template <int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
+  constexpr int BQ = 32 * kWaves;              // queries per workgroup (32 per wave)
+  constexpr int KI = K_BYTES / 1024 / kWaves;  // 1 KB load instructions per wave per block, K
+  constexpr int VI = V_BYTES / 1024 / kWaves;  //                                          V^T
+  constexpr int GROUP = KI + VI;
+  static_assert(KI * kWaves * 1024 == K_BYTES && VI * kWaves * 1024 == V_BYTES, "load split");
+  static_assert((NST - 1) * GROUP < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem[NST * ST_BYTES];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, lg = lane >> 5;
 
-  const int nqb = p.seq / BQ;
+  const int nqb = (p.seq + BQ - 1) / BQ;
   const int units = p.heads * p.batch * p.nshards;
   const int u = blockIdx.x % units;
   const int qb = nqb - 1 - blockIdx.x / units;  // heaviest query blocks first
@@ -56,37 +96,52 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnParams p) {
   const int64_t tok0 = (int64_t)b * p.seq;  // first token row of this sequence
 
   const int q0 = qb * BQ;
-  const int q = q0 + wave * 32 + lr;  // this lane's query (sequence position)
+  const int qw = q0 + w * 32;                 // this wave's first query
+  const bool wave_live = qw < p.seq;          // seq is a multiple of 32
+  const int q = qw + lr;                      // this lane's query (sequence position)
+  const int nkb = min(q0 + BQ, p.seq) / BKEY;  // key blocks up to the end of this query block
+  const int wave_kb = wave_live ? (qw + 31) / BKEY + 1 : 0;  // blocks this wave needs
 
   // query fragments (B operand of S^T = K Q^T): 8 steps of 16 dims
   bf16x8 qf[D / 16];
-  {
+  if (wave_live) {
     const bf16* qrow = QK + (tok0 + q) * p.ldqk + h * D + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16);
   }
 
-  // global -> register staging of one key block: K [64 x 128], V^T [128 x 64]
-  u32x4 rk[4], rv[4];
+  // buffer resources over this sequence's K rows and V^T columns
   const bf16* kbase = QK + tok0 * p.ldqk + p.kcol0 + h * D;
   const bf16* vbase = Vt + (int64_t)h * D * p.ldvt + tok0;
-  auto load_block = [&](int kb) {
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(kbase, (uint32_t)(((int64_t)(p.seq - 1) * p.ldqk + D) * 2));
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(vbase, (uint32_t)(((int64_t)(D - 1) * p.ldvt + p.seq) * 2));
+  const __amdgpu_buffer_rsrc_t rZ = make_rsrc(kbase, 0u);
+
+  // per-lane offsets of this wave's load instructions: K instruction j covers
+  // rows 4j..4j+3 (16 chunks each), V^T instruction j rows 8j..8j+7 (8 chunks)
+  uint32_t voK[KI], voV[VI];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = tid + r * kThreads;
-      const int key = c >> 4, col = (c & 15) * 8;
-      rk[r] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(kb * BKEY + key) * p.ldqk + col);
-      const int d = c >> 3, kc = (c & 7) * 8;
-      rv[r] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)d * p.ldvt + kb * BKEY + kc);
-    }
-  };
-  auto store_block = [&](int buf) {
+  for (int i = 0; i < KI; ++i) {
+    const int j = w * KI + i, r = 4 * j + (lane >> 4), pc = lane & 15;
+    voK[i] = (uint32_t)r * (uint32_t)p.ldqk * 2u + (uint32_t)kswz(r, pc) * 16u;
+  }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = tid + r * kThreads;
-      *reinterpret_cast<u32x4*>(&Ks[buf][(c >> 4) * KLD + (c & 15) * 8]) = rk[r];
-      *reinterpret_cast<u32x4*>(&Vs[buf][(c >> 3) * VLD + (c & 7) * 8]) = rv[r];
-    }
+  for (int i = 0; i < VI; ++i) {
+    const int j = w * VI + i, r = 8 * j + (lane >> 3), pc = lane & 7;
+    voV[i] = (uint32_t)r * (uint32_t)p.ldvt * 2u + (uint32_t)vswz(r, pc) * 16u;
+  }
+  // key block kb into stage st; blocks past the end read zeros and move no data
+  auto issue = [&](int kb, int st) {
+    const bool live = kb < nkb;
+    const __amdgpu_buffer_rsrc_t rk = live ? rK : rZ;
+    const __amdgpu_buffer_rsrc_t rv = live ? rV : rZ;
+    char* s = smem + st * ST_BYTES;
+#pragma unroll
+    for (int i = 0; i < KI; ++i)
+      dma16(rk, s + (w * KI + i) * 1024, voK[i], live ? (uint32_t)kb * BKEY * (uint32_t)p.ldqk * 2u : 0u);
+#pragma unroll
+    for (int i = 0; i < VI; ++i)
+      dma16(rv, s + K_BYTES + (w * VI + i) * 1024, voV[i], live ? (uint32_t)kb * BKEY * 2u : 0u);
   };
 
   floatx16 o[D / 32];
@@ -96,14 +151,22 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnParams p) {
     for (int v = 0; v < 16; ++v) o[i][v] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const int nkb = (q0 + BQ) / BKEY;  // key blocks up to the end of this query block
-  load_block(0);
-  store_block(0);
-  __syncthreads();
+  // fragment read offsets (the swizzles depend on the lane only)
+  const int ko = lr * 256;  // + (kswz chunk) * 16, key row lr of each 32-row tile
+  const int vo = lr * 128 + 8 * lg;
+
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) issue(s, s);
 
   for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1;
-    if (kb + 1 < nkb) load_block(kb + 1);
+    const int st = kb % NST;
+    wait_vmcnt<(NST - 2) * GROUP>();  // block kb has landed (this wave's part)
+    lds_barrier();                     // ... every wave's part; stage (kb-1)%NST is free
+    issue(kb + NST - 1, (kb + NST - 1) % NST);
+    if (kb >= wave_kb) continue;  // every key of this block is after this wave's queries
+
+    const char* ks_ = smem + st * ST_BYTES;
+    const char* vs_ = ks_ + K_BYTES;
 
     // S^T tile: rows = 64 keys (two 32-key MFMA tiles), columns = 32 queries
     floatx16 s[2];
@@ -111,31 +174,34 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnParams p) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[t][v] = 0.0f;
-    const bf16* krow = &Ks[cur][lr * KLD + 8 * lg];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+    for (int kstep = 0; kstep < D / 16; ++kstep)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + t * 32 * KLD + ks * 16);
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[t], 0, 0, 0);
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(ks_ + t * 32 * 256 + ko + (kswz(lr, 2 * kstep + lg) << 4));
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kstep], s[t], 0, 0, 0);
       }
 
-    // scale into the log2 domain, mask keys after the query, block max
-    const bool diag = kb * BKEY + BKEY - 1 > q0;  // block reaches past the first query
+    // mask keys after the query (blocks that straddle this wave's diagonal),
+    // block max of the raw scores; the scale into the log2 domain is positive,
+    // so it is applied after the max, fused into the exponent's argument
+    const bool diag = kb * BKEY + BKEY - 1 > qw;  // block reaches past the wave's first query
+    if (diag) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kb * BKEY + t * 32 + ((v >> 2) << 3) + (lg << 2) + (v & 3);
+          if (key > q) s[t][v] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = s[t][v] * p.scale_log2e;
-        if (diag) {
-          const int key = kb * BKEY + t * 32 + ((v >> 2) << 3) + (lg << 2) + (v & 3);
-          if (key > q) x = -INFINITY;
-        }
-        s[t][v] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[t][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2e;
     const float m_new = fmaxf(m_run, mx);      // finite: key 0 is in block 0 for every query
     const float alpha = exp2f(m_run - m_new);  // 0 on the first block
     m_run = m_new;
@@ -146,37 +212,39 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnParams p) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float e = exp2f(s[t][v] - m_new);
+        const float e = exp2f(fmaf(s[t][v], p.scale_log2e, -m_new));
         psum += e;
         pb[t][v >> 3][v & 7] = to_bf16(e);
       }
     l_run = l_run * alpha + psum;
+    if (__ballot(alpha != 1.0f)) {  // some running max moved: rescale the accumulators
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i)
+      for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+    }
 
     // O^T += V^T P^T.  MFMA step c covers score tile t = c/2, accumulator
     // rows v = 8*(c%2) .. +7, i.e. keys t*32 + 16*(c%2) + 4*lg + {0..3} and
-    // the same + 8: the A operand reads exactly those keys of V^T.
+    // the same + 8: the A operand reads exactly those keys of V^T (logical
+    // chunk 4t + 2*(c%2), and the next one, at byte 8*lg of each).
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int t = c >> 1, half = c & 1;
-      const int k1 = t * 32 + half * 16 + lg * 4;
+      const int ch = 4 * t + 2 * half;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) {
-        const bf16* vrow = &Vs[cur][(i * 32 + lr) * VLD];
-        const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vrow + k1);
-        const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vrow + k1 + 8);
+        const char* vrow = vs_ + i * 32 * 128 + vo;
+        const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vrow + (vswz(lr, ch) << 4));
+        const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vrow + (vswz(lr, ch + 1) << 4));
         const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t][half], o[i], 0, 0, 0);
       }
     }
-
-    if (kb + 1 < nkb) store_block(cur ^ 1);
-    __syncthreads();
   }
+  wait_vmcnt<0>();  // no load may still target this workgroup's LDS when it exits
 
+  if (!wave_live) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
   bf16* orow = O + (tok0 + q) * p.ldo + h * D;
@@ -185,19 +253,27 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int d = i * 32 + r * 8 + lg * 4;
-      bf16x4 w;
+      bf16x4 wv;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = to_bf16(o[i][r * 4 + j] * inv);
-      *reinterpret_cast<bf16x4*>(orow + d) = w;
+      for (int j = 0; j < 4; ++j) wv[j] = to_bf16(o[i][r * 4 + j] * inv);
+      *reinterpret_cast<bf16x4*>(orow + d) = wv;
     }
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
-  const int64_t grid = (int64_t)(p.seq / BQ) * p.heads * p.batch * p.nshards;
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  // 8 waves (256 queries) per workgroup when that still gives every CU a
+  // workgroup; otherwise 4 waves (128 queries)
+  const int64_t units = (int64_t)p.heads * p.batch * p.nshards;
+  const int64_t grid8 = (int64_t)((p.seq + 255) / 256) * units;
+  if (units <= 0 || p.seq <= 0) return hipSuccess;
+  if (grid8 >= 256) {
+    hipLaunchKernelGGL(attn_fwd_kernel<8>, dim3((unsigned)grid8), dim3(512), 0, s, p);
+  } else {
+    const int64_t grid4 = (int64_t)((p.seq + 127) / 128) * units;
+    hipLaunchKernelGGL(attn_fwd_kernel<4>, dim3((unsigned)grid4), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
