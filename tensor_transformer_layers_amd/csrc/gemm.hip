@@ -18,14 +18,19 @@
 //  * Global -> LDS staging uses the buffer-load-to-LDS path (no registers, no
 //    LDS write instructions): one wave instruction fills 1 KB of LDS, lane i
 //    landing at byte 16*i.  The lane -> global chunk assignment applies an
-//    XOR swizzle (chunk c of tile row r sits at chunk c ^ ((r >> SH) & (CPR-1)))
+//    XOR swizzle (chunk c of tile row r sits at chunk c ^ ((r >> 1) & 7))
 //    so that the 16-byte fragment reads of consecutive rows hit distinct LDS
 //    banks.  Rows past the matrix edge and chunks past K read as zero through
 //    the buffer range check; the tail chunks are also cleared explicitly.
-//  * S-stage LDS ring: the loads of tile k+S-1 are issued right after the
-//    barrier that opens tile k, so S-1 tiles of compute hide their latency.
-//    One barrier per tile.  Fragment reads of k-step kk+1 are issued before the
-//    MFMAs of step kk.
+//  * Two LDS stages of 64-wide k-tiles, one barrier per tile.  The barrier
+//    sits before the last k-step's MFMAs of tile t: after it, tile t's stage
+//    is free, and the loads of tile t+2 into it are issued in three parts --
+//    during that last k-step and during k-steps 0 and 1 of tile t+1 -- one
+//    load instruction after each MFMA, in an order pinned against the
+//    scheduler, so the loads stream out between the MFMAs and still have 2-4
+//    k-steps to land.  Fragment reads of k-step kk+1 are issued before the
+//    MFMAs of step kk (across the tile boundary too).  A partial k-tile is
+//    consumed first, so only the prologue handles K tails.
 //  * Workgroup ids are renumbered so that neighbouring output tiles run on the
 //    same XCD (shared L2), in groups of 8 M-tiles.
 //
@@ -68,12 +73,8 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint3
 
 constexpr uint32_t kOob = 0x80000000u;  // beyond every range: reads as zero
 
-#ifndef TP_GEMM_SH
-#define TP_GEMM_SH 1
-#endif
-#ifndef TP_GEMM_SPREAD
-#define TP_GEMM_SPREAD 0
-#endif
+// Swizzle shift of the LDS layout (16 consecutive rows hit 16 bank groups).
+constexpr int kGemmSwizzleShift = 1;
 
 template <int BM_, int BN_, int BK_, int S_, int SH_, int EPI_>
 struct G {
@@ -283,71 +284,55 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
   // tile t+1, barrier (after it stage STG is free), fetch tile t+1's first
   // fragments and issue the loads of tile t+2 into stage STG; the last step's
   // MFMAs cover the latency of both.
-#if TP_GEMM_SPREAD
-  // Instructions [lo, hi) of this wave's load group for tile t into stage STG
-  // (instruction g < IA is A-tile row block g, the rest B-tile row blocks).
-  auto issue_part = [&](auto stg, int t, int lo, int hi) {
+  // Load instruction g of this wave's group for a tile into stage STG
+  // (g < IA: A-tile row block g, else B-tile row block g - IA).
+  auto dma_one = [&](auto stg, int g, const __amdgpu_buffer_rsrc_t& ra, const __amdgpu_buffer_rsrc_t& rb,
+                     uint32_t so) {
     constexpr int STG = decltype(stg)::value;
-    const bool live = t < nk;
-    const __amdgpu_buffer_rsrc_t ra = live ? rA : rZ;
-    const __amdgpu_buffer_rsrc_t rb = live ? rB : rZ;
-    const uint32_t so = live ? (uint32_t)k_begin(t) * 2u : 0u;
-#pragma unroll
-    for (int g = lo; g < hi; ++g) {
-      if (g < C::IA)
-        dma16(ra, smem + STG * C::STAGE_BYTES + (w * C::IA + g) * 1024, voA[g], so);
-      else
-        dma16(rb, smem + STG * C::STAGE_BYTES + C::A_BYTES + (w * C::IB + g - C::IA) * 1024, voB[g - C::IA], so);
-    }
+    if (g < C::IA)
+      dma16(ra, smem + STG * C::STAGE_BYTES + (w * C::IA + g) * 1024, voA[g], so);
+    else
+      dma16(rb, smem + STG * C::STAGE_BYTES + C::A_BYTES + (w * C::IB + g - C::IA) * 1024, voB[g - C::IA], so);
   };
-  // Tile t from stage STG.  Its k-steps 0..KK-2 each prefetch the next step's
-  // fragments and issue a share of the loads of tile t+1 into the other stage
-  // (freed at the previous boundary), so the load instructions stream out
-  // evenly between the MFMAs instead of queueing up at one point.  Before the
-  // last step's MFMAs: wait for tile t+1, barrier, fetch its first fragments.
+  // A tile's load instructions are spread over the boundary step that frees
+  // its stage and the first kParts-1 k-steps of the next tile.
+  constexpr int kParts = 3;
+  static_assert(kParts >= 1 && kParts <= C::KK - 1, "load parts");
+  constexpr int kBoundaryLoads = (C::GROUP + kParts - 1) / kParts;
+  constexpr int kStepLoads = kParts > 1 ? (C::GROUP - kBoundaryLoads + kParts - 2) / (kParts - 1) : 0;
   auto body = [&](auto stg, int t) {
     constexpr int STG = decltype(stg)::value;
     using NXT = std::integral_constant<int, STG ^ 1>;
 #pragma unroll
     for (int kk = 0; kk < C::KK - 1; ++kk) {
-      load_frags(stg, kk + 1, (kk + 1) & 1);
-      issue_part(NXT{}, t + 1, (kk * C::GROUP + C::KK - 2) / (C::KK - 1),
-                 ((kk + 1) * C::GROUP + C::KK - 2) / (C::KK - 1));
-      mfmas(kk & 1);
+      if (kk < kParts - 1) {
+        // k-steps 0..kParts-2: the rest of tile t+1's loads into the other
+        // stage, one after each MFMA, with the next k-step's fragment reads
+        const bool live = t + 1 < nk;
+        const __amdgpu_buffer_rsrc_t ra = live ? rA : rZ;
+        const __amdgpu_buffer_rsrc_t rb = live ? rB : rZ;
+        const uint32_t so = live ? (uint32_t)k_begin(t + 1) * 2u : 0u;
+        constexpr int NMF = C::TM * C::TN;
+        const int lo = kBoundaryLoads + kk * kStepLoads;
+        const int nl = min(kStepLoads, C::GROUP - lo);
+        constexpr int NQ = NMF > kStepLoads ? NMF : kStepLoads;
+        const int cb = kk & 1, nb = cb ^ 1;
 #pragma unroll
-      for (int q = 0; q < kFrag; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerRead / 2, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                 // load to LDS
-        __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerRead - kMfmaPerRead / 2, 0);
+        for (int q = 0; q < NQ; ++q) {
+          if (q < C::TM)
+            af[nb][q] = *reinterpret_cast<const bf16x8*>(smem + foA[STG][kk + 1] + q * 32 * (C::BK * 2));
+          else if (q < C::TM + C::TN)
+            bfg[nb][q - C::TM] =
+                *reinterpret_cast<const bf16x8*>(smem + foB[STG][kk + 1] + brow(q - C::TM) * (C::BK * 2));
+          if (q < NMF) {
+            const int j = q / C::TM, i = q % C::TM;
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[cb][j], af[cb][i], acc[j][i], 0, 0, 0);
+          }
+          if (q < nl) dma_one(NXT{}, lo + q, ra, rb, so);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        continue;
       }
-    }
-    wait_vmcnt<0>();
-    lds_barrier();
-    load_frags(NXT{}, 0, 0);  // past the last tile this reads a stale stage, unused
-    mfmas((C::KK - 1) & 1);
-#pragma unroll
-    for (int q = 0; q < kFrag; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerRead, 0);
-    }
-  };
-
-  // prologue: tile 0, then its first fragments
-  if (has_tail)
-    issue_partial();
-  else
-    issue(I0{}, 0);
-  wait_vmcnt<0>();
-  if (has_tail) clear_partial();
-  lds_barrier();
-  load_frags(I0{}, 0, 0);
-#else
-  auto body = [&](auto stg, int t) {
-    constexpr int STG = decltype(stg)::value;
-    using NXT = std::integral_constant<int, STG ^ 1>;
-#pragma unroll
-    for (int kk = 0; kk < C::KK - 1; ++kk) {
       load_frags(stg, kk + 1, (kk + 1) & 1);
       mfmas(kk & 1);
 #pragma unroll
@@ -358,29 +343,55 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
     }
     wait_vmcnt<0>();
     lds_barrier();
-    load_frags(NXT{}, 0, 0);  // past the last tile this reads a stale stage, unused
-    issue(stg, t + 2);
-    mfmas((C::KK - 1) & 1);
+    // The boundary step, in an explicit order the scheduler may not change:
+    // each of the last k-step's MFMAs is followed by one fragment read of
+    // tile t+1 (while any remain) and one load of tile t+2 into the freed
+    // stage, so the load instructions issue between MFMAs instead of in a
+    // block (past the last tile the reads see a stale stage, unused).
+    {
+      constexpr int NB = NXT::value;
+      const bool live = t + 2 < nk;
+      const __amdgpu_buffer_rsrc_t ra = live ? rA : rZ;
+      const __amdgpu_buffer_rsrc_t rb = live ? rB : rZ;
+      const uint32_t so = live ? (uint32_t)k_begin(t + 2) * 2u : 0u;
+      constexpr int LB = (C::KK - 1) & 1;
+      constexpr int NMF = C::TM * C::TN;
+      constexpr int NQ = NMF > kBoundaryLoads ? NMF : kBoundaryLoads;
+      static_assert(C::TM + C::TN <= NQ, "every fragment read has a slot");
 #pragma unroll
-    for (int q = 0; q < kFrag; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x010, C::GROUP / kFrag, 0);  // loads to LDS
-      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerRead, 0);
+      for (int q = 0; q < NQ; ++q) {
+        if (q < C::TM)
+          af[0][q] = *reinterpret_cast<const bf16x8*>(smem + foA[NB][0] + q * 32 * (C::BK * 2));
+        else if (q < C::TM + C::TN)
+          bfg[0][q - C::TM] = *reinterpret_cast<const bf16x8*>(smem + foB[NB][0] + brow(q - C::TM) * (C::BK * 2));
+        if (q < NMF) {
+          const int j = q / C::TM, i = q % C::TM;
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[LB][j], af[LB][i], acc[j][i], 0, 0, 0);
+        }
+        if (q < kBoundaryLoads) dma_one(stg, q, ra, rb, so);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
-  // prologue: tiles 0 and 1, then tile 0's first fragments
+  // prologue: tile 0, the boundary part of tile 1, then tile 0's first fragments
   if (has_tail)
     issue_partial();
   else
     issue(I0{}, 0);
-  issue(I1{}, 1);
-  wait_vmcnt<C::GROUP>();
+  {
+    const bool live = 1 < nk;
+    const __amdgpu_buffer_rsrc_t ra = live ? rA : rZ;
+    const __amdgpu_buffer_rsrc_t rb = live ? rB : rZ;
+    const uint32_t so = live ? (uint32_t)k_begin(1) * 2u : 0u;
+#pragma unroll
+    for (int g = 0; g < kBoundaryLoads; ++g) dma_one(I1{}, g, ra, rb, so);
+  }
+  wait_vmcnt<kBoundaryLoads>();
   if (has_tail) clear_partial();
   lds_barrier();
   load_frags(I0{}, 0, 0);
 
-#endif
 
   // two tiles per trip so that the stages are compile-time constants
   int kt = 0;
@@ -604,8 +615,8 @@ hipError_t launch_bf16_epi(const GemmParams& p, hipStream_t s) {
   constexpr int kCUs = 256;
   const int out256 = (EPI == EPI_SWIGLU) ? 128 : 256;
   const int64_t big = (int64_t)((p.M + 255) / 256) * ((p.N + out256 - 1) / out256) * p.batch;
-  if (big >= kCUs) return launch_bf16_cfg<G<256, 256, 64, 2, TP_GEMM_SH, EPI>>(p, s);
-  return launch_bf16_cfg<G<128, 128, 64, 2, TP_GEMM_SH, EPI>>(p, s);
+  if (big >= kCUs) return launch_bf16_cfg<G<256, 256, 64, 2, kGemmSwizzleShift, EPI>>(p, s);
+  return launch_bf16_cfg<G<128, 128, 64, 2, kGemmSwizzleShift, EPI>>(p, s);
 }
 
 }  // namespace
