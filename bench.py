@@ -50,6 +50,9 @@ def kernel_work(w, name, shards_per_launch, rows_reduced):
             return 2.0 * T * H * cols * c, es * (T * H + c * cols * H + c * T * Fs) + (es * c * Fs if w.sigma_bias else 0)
         if name == "mlp_row_gemm":
             return 2.0 * T * Fs * H * c, es * (c * T * Fs + c * H * Fs) + 4 * c * T * H
+        if name == "mlp_fused":  # column + activation + row partial; the intermediate stays on chip
+            return (4.0 * T * H * Fs * c,
+                    es * (T * H + 2 * c * Fs * H) + (es * c * Fs if w.sigma_bias else 0) + 4 * c * T * H)
     else:
         hl = w.heads // N
         hd = hl * w.head_dim
@@ -82,7 +85,7 @@ def roofline(w, name, flops, nbytes, avg_s):
 # source files each kernel's code and launch shape come from (besides the
 # shared device headers and the dispatch code in tp_api.cpp)
 KERNEL_SOURCES = {
-    "mlp_column_gemm": "gemm.hip", "mlp_row_gemm": "gemm.hip", "attn_qk_gemm": "gemm.hip",
+    "mlp_column_gemm": "gemm.hip", "mlp_row_gemm": "gemm.hip", "mlp_fused": "mlp_fused.hip", "attn_qk_gemm": "gemm.hip",
     "attn_vt_gemm": "gemm.hip", "attn_out_gemm": "gemm.hip", "attn_core": "attention.hip",
     "reduce_partials": "reduce.hip",
 }
@@ -95,17 +98,32 @@ def kernel_source_hash(kernel=None):
     if kernel is None:
         files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp", ".cpp")))
     else:
-        files = [KERNEL_SOURCES[kernel], "tp_device.hpp", "tp_kernels.hpp", "tp_api.cpp"]
+        files = [KERNEL_SOURCES[kernel], "tp_device.hpp", "tp_dma.hpp", "tp_kernels.hpp", "tp_api.cpp"]
     for f in files:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-# launch order of the library's kernels within one step, per workload kind
-LAUNCH_ORDER = {
-    "mlp": ["mlp_column_gemm", "mlp_row_gemm", "reduce_partials"],
-    "attn": ["attn_qk_gemm", "attn_vt_gemm", "attn_core", "attn_out_gemm", "reduce_partials"],
+# launch order of the library's kernels within one step, and a piece of the
+# device function name each one has in a profiler's kernel list
+KERNEL_SYMBOL = {
+    "mlp_column_gemm": "gemm_", "mlp_row_gemm": "gemm_", "mlp_fused": "mlp_fused_kernel",
+    "attn_qk_gemm": "gemm_", "attn_vt_gemm": "gemm_", "attn_out_gemm": "gemm_",
+    "attn_core": "attn_fwd_kernel", "reduce_partials": "reduce_kernel",
 }
+
+
+def launch_order(w):
+    """Kernels one step of workload w launches, in order.  A bf16 GELU MLP
+    with hidden 256 or 512 and a shard width that is a multiple of 32 (at
+    most 4096) runs the fused kernel; every other MLP the column and row
+    GEMMs (the dispatch rule of tp_mlp_forward)."""
+    if w.kind == "attn":
+        return ["attn_qk_gemm", "attn_vt_gemm", "attn_core", "attn_out_gemm", "reduce_partials"]
+    Fs = w.F // w.N
+    if w.kind == "mlp_gelu" and w.dtype == "bf16" and w.H in (256, 512) and Fs % 32 == 0 and Fs <= 4096:
+        return ["mlp_fused", "reduce_partials"]
+    return ["mlp_column_gemm", "mlp_row_gemm", "reduce_partials"]
 
 
 def traffic_path(workload_name):
@@ -136,7 +154,7 @@ def write_traffic(w, share, pmc_dir, argv_line):
     import csv
     import collections
 
-    order = LAUNCH_ORDER["attn" if w.kind == "attn" else "mlp"]
+    order = launch_order(w)
     per = {}
     factor = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -148,7 +166,11 @@ def write_traffic(w, share, pmc_dir, argv_line):
         ours = [r for r in rows if "tp::" in r["Kernel_Name"]]
         vals = collections.defaultdict(list)
         for i, r in enumerate(ours):
-            vals[order[i % len(order)]].append(float(r["Counter_Value"]))
+            k = order[i % len(order)]
+            if KERNEL_SYMBOL[k] not in r["Kernel_Name"]:
+                raise RuntimeError(f"dispatch {r['Dispatch_Id']}: expected {k} ({KERNEL_SYMBOL[k]}), "
+                                   f"profiler has {r['Kernel_Name'][:120]}")
+            vals[k].append(float(r["Counter_Value"]))
         per[counter] = {k: sum(v) / len(v) for k, v in vals.items()}
     lines = [
         f"# HBM traffic per launch: {w.name} ({share})",

@@ -28,12 +28,11 @@
 #include <math.h>
 
 #include "tp_device.hpp"
+#include "tp_dma.hpp"
 #include "tp_kernels.hpp"
 
 namespace tp {
 namespace {
-
-#define TP_LDS __attribute__((address_space(3)))
 
 constexpr int D = 128;             // head dim
 constexpr int BKEY = 64;           // keys per block
@@ -41,26 +40,6 @@ constexpr int NST = 4;             // LDS ring stages
 constexpr int K_BYTES = BKEY * D * 2;    // K block: 64 rows of 256 bytes
 constexpr int V_BYTES = D * BKEY * 2;    // V^T block: 128 rows of 128 bytes
 constexpr int ST_BYTES = K_BYTES + V_BYTES;
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // word 3 = 0x00020000: raw (untyped) 32-bit data format on gfx9-family parts
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TP_LDS void*)lds, 16, (int)voff, (int)soff, 0, 0);
-}
 
 // 16-byte chunk position of logical chunk c in row r of a K block (16 chunks
 // per row) and of a V^T block (8 chunks per row).

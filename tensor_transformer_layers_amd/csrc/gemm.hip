@@ -38,40 +38,13 @@
 #include <type_traits>
 
 #include "tp_device.hpp"
+#include "tp_dma.hpp"
 #include "tp_kernels.hpp"
 
 namespace tp {
 namespace {
 
 constexpr int kThreads = 256;
-
-#define TP_LDS __attribute__((address_space(3)))
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier that orders LDS only (global loads stay in flight).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // word 3 = 0x00020000: raw (untyped) 32-bit data format on gfx9-family parts
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TP_LDS void*)lds, 16, (int)voff, (int)soff, 0, 0);
-}
-
-constexpr uint32_t kOob = 0x80000000u;  // beyond every range: reads as zero
 
 // Swizzle shift of the LDS layout (16 consecutive rows hit 16 bank groups).
 constexpr int kGemmSwizzleShift = 1;

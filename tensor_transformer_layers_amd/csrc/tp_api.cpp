@@ -420,6 +420,37 @@ tp_status tp_mlp_forward(void* stream, const tp_mlp_desc* d, void* ws, size_t ws
   void* Hs = base + sh.h_offset;
   const size_t es = esize(d->dt);
 
+  // Narrow hidden sizes: one kernel per shard range computes the column
+  // product, the activation and the row partial with the intermediate kept
+  // on chip (it never needs to leave the shard).
+  if (d->dt == TP_BF16 && d->act != TP_ACT_SWIGLU && tp::mlp_fused_supported(H, Fs)) {
+    tp::FusedMlpParams f{};
+    f.X = d->X;
+    f.ldx = H;
+    f.A = static_cast<const char*>(d->A) + (size_t)i0 * Fs * H * es;
+    f.lda = H;
+    f.sA = Fs * H;
+    f.bias = d->a ? static_cast<const char*>(d->a) + (size_t)i0 * Fs * es : nullptr;
+    f.sBias = Fs;
+    f.B = static_cast<const char*>(d->B) + (size_t)i0 * Fs * es;
+    f.ldb = d->F;
+    f.sB = Fs;
+    f.P = P + (size_t)i0 * T * H;
+    f.ldp = H;
+    f.sP = T * H;
+    f.T = (int)T;
+    f.H = (int)H;
+    f.Fs = (int)Fs;
+    f.shards = c;
+    f.act = d->act == TP_ACT_GELU ? tp::FUSED_GELU : tp::FUSED_NONE;
+    KernelTimer kt("mlp_fused", s);
+    const hipError_t e = tp::launch_mlp_fused(f, s);
+    kt.stop();
+    TP_TRY(hip_status(e, "mlp fused launch"));
+    if (c < d->N) return ok();
+    return run_reduce(s, d->dt, d->N, T, H, P, T * H, d->b, d->Y, d->n_slices, d->slice);
+  }
+
   // column GEMM + activation for every shard in range (X shared, one launch)
   tp::GemmParams col = gemm(d->X, H, 0, static_cast<const char*>(d->A) + (size_t)i0 * sh.a_rows * H * es, H,
                             sh.a_rows * H, Hs, Fs, T * Fs, T, Fs, H, c);

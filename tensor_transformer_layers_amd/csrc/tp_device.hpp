@@ -30,16 +30,22 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 // rational-exponential approximation 7.1.26 of Abramowitz & Stegun, Handbook
 // of Mathematical Functions (absolute error <= 1.5e-7 in erf, far below bf16
 // resolution): erf(x) = 1 - t*(a1 + t*(a2 + t*(a3 + t*(a4 + t*a5)))) e^(-x^2),
-// t = 1 / (1 + p x), x >= 0.  With q = z/2 * (1 - erf(|z|/sqrt 2)):
-// GELU(z) = z - q for z >= 0 and q for z < 0, which avoids cancelling
-// 1 + erf near -1 for negative z.  One exp, one reciprocal, no branches.
+// t = 1 / (1 + p x), x >= 0.  With x = |z|/sqrt 2 and
+// q = z/2 * (1 - erf(x)), which carries the sign of z:
+//   GELU(z) = z - q  (z >= 0),   q  (z < 0),   i.e.  max(z, 0) - |q|,
+// which avoids cancelling 1 + erf near -1 for negative z.  The constants are
+// folded: with s = sqrt(log2 e) and u = x s, e^(-x^2) = 2^(-u^2) and
+// p x = (p/s) u; the coefficients carry the factor 1/2.  One exp2, one
+// reciprocal, no branch.
 __device__ __forceinline__ float gelu_bf16out(float z) {
-  const float x = fabsf(z) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  const float u = fabsf(z) * (0.70710678118654752f * 1.2011224087864498f);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f / 1.2011224087864498f, u, 1.0f));
   const float poly =
-      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f), -0.284496736f), 0.254829592f);
-  const float q = 0.5f * z * poly * __expf(-x * x);
-  return z >= 0.0f ? z - q : q;
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f), 0.5f * 1.421413741f),
+                       0.5f * -0.284496736f),
+               0.5f * 0.254829592f);
+  const float q = z * poly * __builtin_amdgcn_exp2f(-u * u);
+  return fmaxf(z, 0.0f) - fabsf(q);
 }
 
 // SiLU for bf16 outputs: g / (1 + e^-g) with the hardware exponential and

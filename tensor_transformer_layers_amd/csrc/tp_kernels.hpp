@@ -36,6 +36,30 @@ struct GemmParams {
 hipError_t launch_gemm_bf16(const GemmParams& p, Epilogue epi, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmParams& p, Epilogue epi, hipStream_t s);
 
+// One kernel for the whole MLP of each shard s in [0, shards), narrow hidden
+// sizes only (mlp_fused_supported):
+//   P + s*sP  [T x H] fp32  =  act(X A_s^T + bias_s) B_s^T
+// with A_s = A + s*sA ([Fs x H], ld lda), bias_s = bias + s*sBias ([Fs] or
+// nullptr), B_s = B + s*sB ([H x Fs], ld ldb).  bf16 inputs; the activated
+// intermediate is rounded to bf16, as the separate column kernel stores it.
+enum FusedAct : int { FUSED_NONE = 0, FUSED_GELU = 1 };
+struct FusedMlpParams {
+  const void* X;
+  int64_t ldx;
+  const void* A;
+  int64_t lda, sA;
+  const void* bias;
+  int64_t sBias;
+  const void* B;
+  int64_t ldb, sB;
+  float* P;
+  int64_t ldp, sP;
+  int T, H, Fs, shards;
+  int act;
+};
+bool mlp_fused_supported(int64_t H, int64_t Fs);
+hipError_t launch_mlp_fused(const FusedMlpParams& p, hipStream_t s);
+
 // Y[rows x H] = fold_k P[k][row0 + r, :] (+ bias), see tp_reduce_partials.
 struct ReduceParams {
   const float* P;

@@ -234,6 +234,67 @@ def test_empty_tokens_is_noop():
     assert Y.shape == (0, 32)
 
 
+# ------------------------------------------------------------------ fused narrow-hidden MLP kernel
+# (T, H, F, N, act, bias): ragged token blocks, H = 256 / 512, odd and single
+# chunk counts per shard, no column bias, fewer tokens than one block
+FUSED = [
+    (1000, 512, 4 * 64, 4, "gelu", True),
+    (300, 256, 2 * 96, 2, "none", True),
+    (128, 512, 4 * 32, 4, "gelu", False),
+    (77, 256, 8 * 32, 8, "gelu", True),
+]
+
+
+def _fused_inputs(T, H, F, seed):
+    rng = np.random.default_rng(seed)
+    X = rng_bf16(rng, (T, H))
+    A = rng_bf16(rng, (F, H), 0.05)   # [out x in]; pre-activations ~N(0, 1.3)
+    a = rng_bf16(rng, (F,), 0.1)
+    B = rng_bf16(rng, (H, F), 0.05)
+    b = rng_bf16(rng, (H,), 0.1)
+    return X, A, a, B, b
+
+
+@pytest.mark.parametrize("T,H,F,N,act,bias", FUSED)
+def test_fused_mlp_vs_oracle(T, H, F, N, act, bias):
+    say(f"fused mlp T={T} H={H} F={F} N={N} act={act} bias={bias}")
+    X, A, a, B, b = _fused_inputs(T, H, F, seed=T + H + F + N)
+    if not bias:
+        a = None
+    code = tp.TP_ACT_GELU if act == "gelu" else tp.TP_ACT_NONE
+    Y, ws = tp.mlp_forward(dev(X), dev(A), None if a is None else dev(a), dev(B), dev(b), N, act=code)
+    torch.cuda.synchronize()
+    if act == "gelu":
+        ref = O.mlp_gelu(X, A.T, a, B.T, b)
+    else:
+        ref = O.linear(O.linear(X, A.T, a), B.T, b)
+    e = err(Y.float().cpu().numpy(), ref)
+    say(f"  err={e:.3e}")
+    assert e <= BF16_TOL
+
+
+def test_fused_mlp_matches_separate_kernels():
+    """The fused kernel's partials against the column kernel (GELU epilogue)
+    followed by the row-partial kernel, shard by shard: the same products in
+    the same k order, so they agree to fp32 rounding."""
+    T, H, F, N = 640, 512, 4 * 64, 4
+    Fs = F // N
+    say("fused vs separate kernels")
+    X, A, a, B, b = (dev(t) for t in _fused_inputs(T, H, F, seed=5))
+    Y, ws = tp.mlp_forward(X, A, a, B, b, N, act=tp.TP_ACT_GELU)
+    Pf = tp.mlp_partials(ws, N, T, H).clone()
+    worst, same = 0.0, True
+    for i in range(N):
+        Hi = tp.column_linear(X, A[i * Fs:(i + 1) * Fs], a[i * Fs:(i + 1) * Fs], act=tp.TP_ACT_GELU)
+        Pi = tp.row_linear_partial(Hi, B[:, i * Fs:(i + 1) * Fs])
+        torch.cuda.synchronize()
+        d = (Pi - Pf[i]).abs().max().item() / Pi.abs().max().item()
+        worst = max(worst, d)
+        same = same and torch.equal(Pi, Pf[i])
+    say(f"  max rel diff {worst:.3e}, bit-identical: {same}")
+    assert worst <= 1e-5
+
+
 # ------------------------------------------------------------------ the five workloads at full size
 def _sample_rows(w):
     must = [0, w.T - 1]
