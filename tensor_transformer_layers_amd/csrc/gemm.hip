@@ -95,9 +95,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
   const bool shareA = p.sA == 0 && p.batch > 1, shareB = !shareA && p.sB == 0 && p.batch > 1;
   const int vM = shareB ? tilesM * p.batch : tilesM;  // virtual tile grid
   const int vN = shareA ? tilesN * p.batch : tilesN;
-  const int pid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bz0 = (shareA || shareB) ? 0 : pid / (vM * vN);
-  const int t = pid - bz0 * (vM * vN);
+  // Problems that share nothing run one after another over the whole chip
+  // (workgroups are dispatched in id order), each spread over all XCDs, so
+  // that every XCD works on the same problem's operands at a time.
+  const int tps = vM * vN;
+  const int bz0 = (shareA || shareB) ? 0 : (int)blockIdx.x / tps;
+  const int t = (shareA || shareB) ? xcd_remap(blockIdx.x, gridDim.x) : xcd_remap((int)blockIdx.x - bz0 * tps, tps);
   constexpr int GRP = 8;
   const int group = t / (GRP * vN);
   const int first_m = group * GRP;

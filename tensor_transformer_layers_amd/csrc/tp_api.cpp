@@ -204,6 +204,8 @@ struct MlpShape {
   size_t p_bytes;    // fp32 partial slab (N slots)
   size_t h_offset;   // intermediate slab offset
   size_t h_bytes;
+  int64_t h_ld;      // row pitch of the intermediate: Fs rounded up to 128 bytes, so
+                     // that the row GEMM's operand rows start on cache-line boundaries
   size_t total;
 };
 
@@ -231,6 +233,7 @@ tp_status validate_mlp(const tp_mlp_desc* d, MlpShape* sh) {
     sh->Fs = Fs;
     sh->a_rows = d->act == TP_ACT_SWIGLU ? 2 * Fs : Fs;
     sh->p_bytes = sh->h_offset = sh->h_bytes = sh->total = 0;
+    sh->h_ld = Fs;
     return TP_OK;
   }
   if (d->H % 8) return fail(TP_ERR_ALIGN, "hidden H=%lld is not a multiple of 8", (long long)d->H);
@@ -252,7 +255,9 @@ tp_status validate_mlp(const tp_mlp_desc* d, MlpShape* sh) {
   sh->a_rows = a_rows;
   sh->p_bytes = align256((size_t)d->N * d->T * d->H * sizeof(float));
   sh->h_offset = sh->p_bytes;
-  sh->h_bytes = align256((size_t)d->shard_count * d->T * Fs * esize(d->dt));
+  const int64_t line = 128 / (int64_t)esize(d->dt);
+  sh->h_ld = (Fs + line - 1) / line * line;
+  sh->h_bytes = align256((size_t)d->shard_count * d->T * sh->h_ld * esize(d->dt));
   sh->total = sh->h_offset + sh->h_bytes;
   return TP_OK;
 }
@@ -453,7 +458,7 @@ tp_status tp_mlp_forward(void* stream, const tp_mlp_desc* d, void* ws, size_t ws
 
   // column GEMM + activation for every shard in range (X shared, one launch)
   tp::GemmParams col = gemm(d->X, H, 0, static_cast<const char*>(d->A) + (size_t)i0 * sh.a_rows * H * es, H,
-                            sh.a_rows * H, Hs, Fs, T * Fs, T, Fs, H, c);
+                            sh.a_rows * H, Hs, sh.h_ld, T * sh.h_ld, T, Fs, H, c);
   if (d->a) {
     col.bias = static_cast<const char*>(d->a) + (size_t)i0 * Fs * es;
     col.sBias = Fs;
@@ -463,7 +468,7 @@ tp_status tp_mlp_forward(void* stream, const tp_mlp_desc* d, void* ws, size_t ws
   TP_TRY(hip_status(launch("mlp_column_gemm", d->dt, col, ce, s), "mlp column launch"));
 
   // row partial of every shard into its slot of the fp32 slab
-  const tp::GemmParams row = gemm(Hs, Fs, T * Fs, static_cast<const char*>(d->B) + (size_t)i0 * Fs * es, d->F, Fs,
+  const tp::GemmParams row = gemm(Hs, sh.h_ld, T * sh.h_ld, static_cast<const char*>(d->B) + (size_t)i0 * Fs * es, d->F, Fs,
                                   P + (size_t)i0 * T * H, H, T * H, T, H, Fs, c);
   TP_TRY(hip_status(launch("mlp_row_gemm", d->dt, row, tp::EPI_PARTIAL, s), "mlp row launch"));
 
