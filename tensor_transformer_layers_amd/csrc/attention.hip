@@ -9,12 +9,11 @@
 // ONE query (its MFMA output column) and 32 of the 64 keys of a block; the
 // running max and sum are then per lane, combined with the partner lane
 // (lane ^ 32) by one cross-lane max per key block.  The output is accumulated
-// transposed as well, O^T = V^T P^T: P^T feeds the B operand straight from the
-// lane's own score registers (no data exchange), and V^T (stored d-major, key
-// contiguous, by the QKV projection) feeds the A operand with two 8-byte LDS
-// reads per lane.  The MFMA sums over k in an order that only has to agree
-// between A and B, so the keys of a 16-wide step are taken in the order the
-// score layout hands them over.
+// transposed as well, O^T = V^T P^T: P^T feeds the B operand from the lane's
+// own score registers after two v_permlane32_swap per 16 keys (which put 8
+// consecutive keys in each lane half), and V^T (stored d-major, key
+// contiguous, by the QKV projection) feeds the A operand with one 16-byte
+// LDS read per lane.
 //
 // Workgroup = 8 waves x 32 queries (two waves per SIMD, so one wave's softmax
 // arithmetic overlaps the other's MFMAs), or 4 waves when the grid would not
@@ -24,7 +23,9 @@
 // 16-byte granularity so the fragment reads of consecutive rows spread over
 // the banks.  A wave skips the MFMAs of key blocks that lie wholly after its
 // last query; only the blocks that straddle its diagonal are masked.
-// Workgroups are ordered heaviest (last query block) first.
+// Workgroups are ordered heaviest (last query block) first.  Exponentials use
+// the hardware exp2 directly (results below 2^-126 flush to zero, which no
+// softmax weight can tell apart from zero at bf16).
 #include <math.h>
 
 #include "tp_device.hpp"
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
 
   // fragment read offsets (the swizzles depend on the lane only)
   const int ko = lr * 256;  // + (kswz chunk) * 16, key row lr of each 32-row tile
-  const int vo = lr * 128 + 8 * lg;
+  const int vo = lr * 128;
 
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s) issue(s, s);
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[t][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2e;
     const float m_new = fmaxf(m_run, mx);      // finite: key 0 is in block 0 for every query
-    const float alpha = exp2f(m_run - m_new);  // 0 on the first block
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first block
     m_run = m_new;
 
     bf16x8 pb[2][2];
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float e = exp2f(fmaf(s[t][v], p.scale_log2e, -m_new));
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[t][v], p.scale_log2e, -m_new));
         psum += e;
         pb[t][v >> 3][v & 7] = to_bf16(e);
       }
@@ -204,20 +205,22 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
     }
 
     // O^T += V^T P^T.  MFMA step c covers score tile t = c/2, accumulator
-    // rows v = 8*(c%2) .. +7, i.e. keys t*32 + 16*(c%2) + 4*lg + {0..3} and
-    // the same + 8: the A operand reads exactly those keys of V^T (logical
-    // chunk 4t + 2*(c%2), and the next one, at byte 8*lg of each).
+    // rows v = 8*(c%2) .. +7: lane half lg holds keys t*32 + 16*(c%2) +
+    // 4*lg + {0..3} and the same + 8.  Two lane-half swaps give half lg the
+    // keys t*32 + 16*(c%2) + 8*lg + {0..7} instead, so that the A operand is
+    // one 16-byte read of V^T (logical chunk 4t + 2*(c%2) + lg).
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int t = c >> 1, half = c & 1;
-      const int ch = 4 * t + 2 * half;
+      const u32x4 d = __builtin_bit_cast(u32x4, pb[t][half]);
+      const auto s0 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+      const bf16x8 pk = __builtin_bit_cast(bf16x8, u32x4{s0[0], s1[0], s0[1], s1[1]});
+      const int ch = 4 * t + 2 * half + lg;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) {
-        const char* vrow = vs_ + i * 32 * 128 + vo;
-        const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vrow + (vswz(lr, ch) << 4));
-        const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vrow + (vswz(lr, ch + 1) << 4));
-        const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t][half], o[i], 0, 0, 0);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs_ + i * 32 * 128 + vo + (vswz(lr, ch) << 4));
+        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk, o[i], 0, 0, 0);
       }
     }
   }
