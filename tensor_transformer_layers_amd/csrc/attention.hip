@@ -182,8 +182,15 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[t][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2e;
-    const float m_new = fmaxf(m_run, mx);      // finite: key 0 is in block 0 for every query
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first block
+    // The reference point of the exponentials moves only when the block max
+    // exceeds it by more than kLazy (log2 units): the softmax does not depend
+    // on the point, and weights up to 2^kLazy are exact enough in fp32 and
+    // bf16, so after the first blocks the accumulators are almost never
+    // rescaled.  The first block always moves it (m_run = -inf; key 0 is in
+    // block 0 for every query, so the new point is finite).
+    constexpr float kLazy = 8.0f;
+    const float m_new = mx > m_run + kLazy ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first block, else 1 or < 2^-8
     m_run = m_new;
 
     bf16x8 pb[2][2];
