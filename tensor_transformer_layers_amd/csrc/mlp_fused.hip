@@ -31,8 +31,10 @@
 //    MFMAs), then the row product of chunk c-1, between whose MFMAs the
 //    activation of chunk c runs: a wave hides a few vector instructions
 //    behind each of its own MFMAs.
-//  * Workgroups are renumbered so that the workgroups of one XCD share a
-//    shard: its weights stay in that XCD's L2.
+//  * Workgroups are renumbered so that the shards of a token block run on
+//    one XCD: X is read from HBM once per token block (it is the largest
+//    input; each shard's weights are 1 MB and stream chunk by chunk through
+//    every XCD's L2).
 #include <type_traits>
 
 #include "tp_device.hpp"
@@ -88,10 +90,11 @@ __global__ __launch_bounds__(kFThreads, 1) void mlp_fused_kernel(FusedMlpParams 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, lh = lane >> 5;
 
-  // consecutive ids (one XCD) share a shard
+  // consecutive ids (one XCD) take the shards of one token block: its X rows
+  // come from HBM once per XCD and then from the XCD's L2
   const int pid = xcd_remap(blockIdx.x, gridDim.x);
-  const int shard = pid / tblocks;
-  const int tb = pid - shard * tblocks;
+  const int shard = pid % p.shards;
+  const int tb = pid / p.shards;
   const int tok0 = tb * kTokBlock;
   const int Fs = p.Fs;
   const int nchunk = Fs / kFC;
