@@ -6,7 +6,7 @@
 //
 // Flash-style single pass with an online softmax, on v_mfma_f32_32x32x16_bf16.
 // The score tile is computed transposed, S^T = K Q^T, so that every lane owns
-// ONE query (its MFMA output column) and 32 of the 64 keys of a block; the
+// ONE query (its MFMA output column) and half of the keys of a block; the
 // running max and sum are then per lane, combined with the partner lane
 // (lane ^ 32) by one cross-lane max per key block.  The output is accumulated
 // transposed as well, O^T = V^T P^T: P^T feeds the B operand from the lane's
@@ -17,9 +17,10 @@
 //
 // Workgroup = 8 waves x 32 queries (two waves per SIMD, so one wave's softmax
 // arithmetic overlaps the other's MFMAs), or 4 waves when the grid would not
-// fill the chip.  Key blocks of 64 (K [64 x 128] and
-// V^T [128 x 64], 32 KB) stream through a 4-stage LDS ring with the
-// buffer-load-to-LDS path, three blocks ahead of use; both are XOR-swizzled at
+// fill the chip.  Key blocks of 128 (K [128 x 128] and V^T [128 x 128],
+// 64 KB) stream through a 2-stage LDS ring with the buffer-load-to-LDS path,
+// one block ahead of use (128-key blocks halve the barriers per key against
+// 64-key blocks in a 4-stage ring of the same size); both are XOR-swizzled at
 // 16-byte granularity so the fragment reads of consecutive rows spread over
 // the banks.  A wave skips the MFMAs of key blocks that lie wholly after its
 // last query; only the blocks that straddle its diagonal are masked.
@@ -36,16 +37,18 @@ namespace tp {
 namespace {
 
 constexpr int D = 128;             // head dim
-constexpr int BKEY = 64;           // keys per block
-constexpr int NST = 4;             // LDS ring stages
-constexpr int K_BYTES = BKEY * D * 2;    // K block: 64 rows of 256 bytes
-constexpr int V_BYTES = D * BKEY * 2;    // V^T block: 128 rows of 128 bytes
+constexpr int BKEY = 128;          // keys per block
+constexpr int TT = BKEY / 32;      // 32-key score tiles per block
+constexpr int NST = 2;             // LDS ring stages
+constexpr int VROW = BKEY * 2;     // bytes of a V^T block row
+constexpr int K_BYTES = BKEY * D * 2;    // K block: 128 rows of 256 bytes
+constexpr int V_BYTES = D * BKEY * 2;    // V^T block: 128 rows of 256 bytes
 constexpr int ST_BYTES = K_BYTES + V_BYTES;
 
-// 16-byte chunk position of logical chunk c in row r of a K block (16 chunks
-// per row) and of a V^T block (8 chunks per row).
+// 16-byte chunk position of logical chunk c in row r of a K or V^T block
+// (16 chunks per row in both).
 __device__ __forceinline__ int kswz(int r, int c) { return c ^ (r & 15); }
-__device__ __forceinline__ int vswz(int r, int c) { return c ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int vswz(int r, int c) { return c ^ (r & 15); }
 
 template <int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
@@ -97,8 +100,8 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(vbase, (uint32_t)(((int64_t)(D - 1) * p.ldvt + p.seq) * 2));
   const __amdgpu_buffer_rsrc_t rZ = make_rsrc(kbase, 0u);
 
-  // per-lane offsets of this wave's load instructions: K instruction j covers
-  // rows 4j..4j+3 (16 chunks each), V^T instruction j rows 8j..8j+7 (8 chunks)
+  // per-lane offsets of this wave's load instructions: instruction j covers
+  // rows 4j..4j+3 of the K or V^T block (16 chunks each)
   uint32_t voK[KI], voV[VI];
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
   }
 #pragma unroll
   for (int i = 0; i < VI; ++i) {
-    const int j = w * VI + i, r = 8 * j + (lane >> 3), pc = lane & 7;
+    const int j = w * VI + i, r = 4 * j + (lane >> 4), pc = lane & 15;
     voV[i] = (uint32_t)r * (uint32_t)p.ldvt * 2u + (uint32_t)vswz(r, pc) * 16u;
   }
   // key block kb into stage st; blocks past the end read zeros and move no data
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
 
   // fragment read offsets (the swizzles depend on the lane only)
   const int ko = lr * 256;  // + (kswz chunk) * 16, key row lr of each 32-row tile
-  const int vo = lr * 128;
+  const int vo = lr * VROW;
 
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s) issue(s, s);
@@ -148,16 +151,16 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
     const char* ks_ = smem + st * ST_BYTES;
     const char* vs_ = ks_ + K_BYTES;
 
-    // S^T tile: rows = 64 keys (two 32-key MFMA tiles), columns = 32 queries
-    floatx16 s[2];
+    // S^T tile: rows = BKEY keys (TT 32-key MFMA tiles), columns = 32 queries
+    floatx16 s[TT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < TT; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[t][v] = 0.0f;
 #pragma unroll
     for (int kstep = 0; kstep < D / 16; ++kstep)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < TT; ++t) {
         const bf16x8 kf =
             *reinterpret_cast<const bf16x8*>(ks_ + t * 32 * 256 + ko + (kswz(lr, 2 * kstep + lg) << 4));
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kstep], s[t], 0, 0, 0);
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
     const bool diag = kb * BKEY + BKEY - 1 > qw;  // block reaches past the wave's first query
     if (diag) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < TT; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kb * BKEY + t * 32 + ((v >> 2) << 3) + (lg << 2) + (v & 3);
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < TT; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[t][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2e;
@@ -193,10 +196,10 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first block, else 1 or < 2^-8
     m_run = m_new;
 
-    bf16x8 pb[2][2];
+    bf16x8 pb[TT][2];
     float psum = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < TT; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float e = __builtin_amdgcn_exp2f(fmaf(s[t][v], p.scale_log2e, -m_new));
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
     // keys t*32 + 16*(c%2) + 8*lg + {0..7} instead, so that the A operand is
     // one 16-byte read of V^T (logical chunk 4t + 2*(c%2) + lg).
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 2 * TT; ++c) {
       const int t = c >> 1, half = c & 1;
       const u32x4 d = __builtin_bit_cast(u32x4, pb[t][half]);
       const auto s0 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
       const int ch = 4 * t + 2 * half + lg;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs_ + i * 32 * 128 + vo + (vswz(lr, ch) << 4));
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs_ + i * 32 * VROW + vo + (vswz(lr, ch) << 4));
         o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk, o[i], 0, 0, 0);
       }
     }
