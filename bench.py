@@ -240,8 +240,11 @@ def cpu_baseline(w, host, seconds):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: as many as fill about 0.5 s, at least 20)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default: as many as fill about 0.5 s, at least 5); "
+                         "the shader clock takes tens of ms to settle after idle")
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: GELU MLP bf16, T=16384, H=512, F=2048, N=4)")
     ap.add_argument("--share", choices=["layer", "rank"], default="layer")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -293,6 +296,24 @@ def main():
             workloads.forward(w, d, ws=ws, shard_begin=0, shard_count=1, stream=stream)
             workloads.reduce_slab(w, d, ws, Y=Yr, slice=rank_slice, stream=stream)
 
+    if args.steps is None or args.warmup is None:
+        # size the defaults by time: after idle the shader clock ramps for
+        # tens of ms (measured 1.3 -> 1.9 GHz over ~30 ms on the large GEMMs,
+        # 2.05 -> 2.3 GHz over ~40 ms on workload 2), so a fixed small step
+        # count would time the ramp instead of the steady state
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        est = (time.perf_counter() - t0) / 3
+        fill = max(1, int(0.5 / max(est, 1e-6)))
+        if args.warmup is None:
+            args.warmup = max(5, fill)
+        if args.steps is None:
+            args.steps = max(20, fill)
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
