@@ -261,10 +261,10 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
   const int64_t grid8 = (int64_t)((p.seq + 255) / 256) * units;
   if (units <= 0 || p.seq <= 0) return hipSuccess;
   if (grid8 >= 256) {
-    hipLaunchKernelGGL(attn_fwd_kernel<8>, dim3((unsigned)grid8), dim3(512), 0, s, p);
+    launch_kernel(attn_fwd_kernel<8>, dim3((unsigned)grid8), dim3(512), 0, s, p);
   } else {
     const int64_t grid4 = (int64_t)((p.seq + 127) / 128) * units;
-    hipLaunchKernelGGL(attn_fwd_kernel<4>, dim3((unsigned)grid4), dim3(256), 0, s, p);
+    launch_kernel(attn_fwd_kernel<4>, dim3((unsigned)grid4), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

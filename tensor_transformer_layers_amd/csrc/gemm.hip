@@ -582,7 +582,7 @@ hipError_t launch_bf16_cfg(const GemmParams& p, hipStream_t s) {
   const int tilesN = (p.N + C::OUT_N - 1) / C::OUT_N;
   const int64_t grid = (int64_t)tilesM * tilesN * p.batch;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<C>), dim3((unsigned)grid), dim3(kThreads), 0, s, p, tilesM, tilesN);
+  launch_kernel((gemm_bf16_kernel<C>), dim3((unsigned)grid), dim3(kThreads), 0, s, p, tilesM, tilesN);
   return hipGetLastError();
 }
 
@@ -615,13 +615,13 @@ hipError_t launch_gemm_f32(const GemmParams& p, Epilogue epi, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   switch (epi) {
     case EPI_STORE:
-      hipLaunchKernelGGL(gemm_f32_kernel<EPI_STORE>, dim3((unsigned)grid), dim3(kThreads), 0, s, p, tilesM, tilesN);
+      launch_kernel(gemm_f32_kernel<EPI_STORE>, dim3((unsigned)grid), dim3(kThreads), 0, s, p, tilesM, tilesN);
       break;
     case EPI_GELU:
-      hipLaunchKernelGGL(gemm_f32_kernel<EPI_GELU>, dim3((unsigned)grid), dim3(kThreads), 0, s, p, tilesM, tilesN);
+      launch_kernel(gemm_f32_kernel<EPI_GELU>, dim3((unsigned)grid), dim3(kThreads), 0, s, p, tilesM, tilesN);
       break;
     case EPI_PARTIAL:
-      hipLaunchKernelGGL(gemm_f32_kernel<EPI_PARTIAL>, dim3((unsigned)grid), dim3(kThreads), 0, s, p, tilesM, tilesN);
+      launch_kernel(gemm_f32_kernel<EPI_PARTIAL>, dim3((unsigned)grid), dim3(kThreads), 0, s, p, tilesM, tilesN);
       break;
     default:
       return hipErrorInvalidValue;

@@ -308,9 +308,9 @@ hipError_t launch_cfg(const FusedMlpParams& p, hipStream_t s) {
   const int tblocks = (p.T + kTokBlock - 1) / kTokBlock;
   const dim3 g((unsigned)(tblocks * p.shards)), b(kFThreads);
   if (p.act == FUSED_GELU)
-    hipLaunchKernelGGL((mlp_fused_kernel<C, true>), g, b, 0, s, p, tblocks);
+    launch_kernel((mlp_fused_kernel<C, true>), g, b, 0, s, p, tblocks);
   else
-    hipLaunchKernelGGL((mlp_fused_kernel<C, false>), g, b, 0, s, p, tblocks);
+    launch_kernel((mlp_fused_kernel<C, false>), g, b, 0, s, p, tblocks);
   return hipGetLastError();
 }
 

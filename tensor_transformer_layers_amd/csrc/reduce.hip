@@ -99,11 +99,11 @@ hipError_t launch_typed(const ReduceParams& p, hipStream_t s) {
   const int64_t blocks = std::min<int64_t>((n4 + per_block - 1) / per_block, int64_t(1) << 30);
   const dim3 g((unsigned)blocks), b(kThreads);
   switch (p.n_parts) {
-    case 1: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 1>), g, b, 0, s, p, n4); break;
-    case 2: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 2>), g, b, 0, s, p, n4); break;
-    case 4: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 4>), g, b, 0, s, p, n4); break;
-    case 8: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 8>), g, b, 0, s, p, n4); break;
-    default: hipLaunchKernelGGL((reduce_kernel<OUT_BF16, 0>), g, b, 0, s, p, n4); break;
+    case 1: launch_kernel((reduce_kernel<OUT_BF16, 1>), g, b, 0, s, p, n4); break;
+    case 2: launch_kernel((reduce_kernel<OUT_BF16, 2>), g, b, 0, s, p, n4); break;
+    case 4: launch_kernel((reduce_kernel<OUT_BF16, 4>), g, b, 0, s, p, n4); break;
+    case 8: launch_kernel((reduce_kernel<OUT_BF16, 8>), g, b, 0, s, p, n4); break;
+    default: launch_kernel((reduce_kernel<OUT_BF16, 0>), g, b, 0, s, p, n4); break;
   }
   return hipGetLastError();
 }

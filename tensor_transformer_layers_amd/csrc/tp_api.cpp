@@ -50,9 +50,11 @@ bool log_enabled() {
 }
 
 // ------------------------------------------------------------ kernel timing
-// When enabled, each kernel launch below is bracketed by a HIP event pair on
-// the launching stream; tp_timing_read() resolves the pairs into per-kernel
-// totals.  Off by default: no events are created or recorded.
+// When enabled, each kernel launch below carries a HIP start/stop event pair
+// attached to its own dispatch (hipExtLaunchKernelGGL), so the pair spans the
+// kernel's execution on the launching stream and nothing else;
+// tp_timing_read() resolves the pairs into per-kernel totals.  Off by
+// default: no events are created or recorded.
 struct PendingPair {
   std::string name;
   hipEvent_t a, b;
@@ -63,6 +65,7 @@ std::vector<PendingPair> g_pending;
 std::vector<hipEvent_t> g_event_pool;
 std::map<std::string, std::pair<double, int64_t>> g_totals;
 std::vector<std::string> g_names;  // storage for tp_timing_read's name pointers
+thread_local tp::LaunchEvents t_armed = {nullptr, nullptr};  // for the next launch on this thread
 
 hipEvent_t pooled_event() {
   if (!g_event_pool.empty()) {
@@ -75,24 +78,37 @@ hipEvent_t pooled_event() {
   return e;
 }
 
+// Arms an event pair for the one kernel launch inside its scope; stop()
+// files the pair if the launch took it (a launch skipped for an empty
+// problem leaves it armed, and the events go back to the pool).
 struct KernelTimer {
   const char* name;
-  hipStream_t s;
-  hipEvent_t a = nullptr;
-  KernelTimer(const char* n, hipStream_t st) : name(n), s(st) {
+  hipEvent_t a = nullptr, b = nullptr;
+  KernelTimer(const char* n, hipStream_t) : name(n) {
     std::lock_guard<std::mutex> g(g_tmu);
     if (!g_timing) return;
     a = pooled_event();
-    if (a) hipEventRecord(a, s);
+    b = pooled_event();
+    if (!a || !b) {
+      if (a) g_event_pool.push_back(a);
+      if (b) g_event_pool.push_back(b);
+      a = b = nullptr;
+      return;
+    }
+    t_armed = {a, b};
   }
   void stop() {
     if (!a) return;
+    const bool used = t_armed.start == nullptr;
+    t_armed = {nullptr, nullptr};
     std::lock_guard<std::mutex> g(g_tmu);
-    hipEvent_t b = pooled_event();
-    if (!b) return;
-    hipEventRecord(b, s);
-    g_pending.push_back({name, a, b});
-    a = nullptr;
+    if (used) {
+      g_pending.push_back({name, a, b});
+    } else {
+      g_event_pool.push_back(a);
+      g_event_pool.push_back(b);
+    }
+    a = b = nullptr;
   }
 };
 
@@ -325,6 +341,14 @@ tp_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 }
 
 }  // namespace
+
+namespace tp {
+LaunchEvents take_launch_events() {
+  const LaunchEvents e = t_armed;
+  t_armed = {nullptr, nullptr};
+  return e;
+}
+}  // namespace tp
 
 extern "C" {
 
@@ -581,7 +605,7 @@ tp_status tp_timing_enable(int on) {
 void tp_timing_reset(void) {
   std::lock_guard<std::mutex> g(g_tmu);
   for (auto& p : g_pending) {
-    hipEventSynchronize(p.b);
+    (void)hipEventSynchronize(p.b);
     g_event_pool.push_back(p.a);
     g_event_pool.push_back(p.b);
   }

@@ -2,10 +2,28 @@
 // interface is include/tp.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace tp {
+
+// Per-kernel timing.  While the library times its kernels, the host code
+// arms a start/stop event pair before a launch and the launch attaches it to
+// its own dispatch, so the pair spans exactly that kernel's execution (no
+// marker packets between kernels).  take_launch_events() returns the armed
+// pair (null events when timing is off) and disarms it; tp_api.cpp owns it.
+struct LaunchEvents {
+  hipEvent_t start, stop;
+};
+LaunchEvents take_launch_events();
+
+template <typename K, typename... Args>
+inline void launch_kernel(K kernel, const dim3& grid, const dim3& block, uint32_t shm, hipStream_t s,
+                          Args... args) {
+  const LaunchEvents ev = take_launch_events();
+  hipExtLaunchKernelGGL(kernel, grid, block, shm, s, ev.start, ev.stop, 0u, args...);
+}
 
 // Epilogue applied to the fp32 accumulator tile of a GEMM.
 enum Epilogue : int {
