@@ -41,6 +41,7 @@ __all__ = [
     "row_partials", "mlp_gelu_sharded", "swiglu_fused_blocks",
     "mlp_swiglu_sharded", "attention_block_sharded", "rs_slice",
     "reduce_partials_fp32", "to_bf16", "attention_block_rows",
+    "rmsnorm", "seq_slices", "all_gather_rows", "sp_entry", "rmsnorm_hidden_split",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -299,6 +300,58 @@ def rs_slice(Y, n_slices, r):
         raise ValueError(f"T={T} is not divisible by n_slices={n_slices}")
     s = T // n_slices
     return Y[r * s:(r + 1) * s]
+
+
+# --------------------------------------------------------------------------
+# sequence-parallel entry side: RMSNorm on sequence slices, then all-gather
+# --------------------------------------------------------------------------
+def rmsnorm(X, g, eps):
+    """RMSNorm over the hidden (last) axis: each row times 1/sqrt(mean of its
+    squares + eps), then times the per-feature gain g.
+
+    [Blog] 3.3: the norm needs the statistic of the *whole* hidden vector, and
+    RMSNorm needs only the second-order one (the mean of squares).  eps is not
+    given by the pages; it is an argument here.
+    """
+    X = _f64(X)
+    inv = 1.0 / np.sqrt(np.mean(X * X, axis=-1, keepdims=True) + eps)
+    return X * inv * _f64(g)[None, :]
+
+
+def seq_slices(X, n_slices):
+    """The sequence-parallel split: n_slices contiguous row blocks, block r
+    held by rank r ([Blog] 4.3; [Wiki] Megatron-SP section)."""
+    X = _f64(X)
+    return [rs_slice(X, n_slices, r) for r in range(n_slices)]
+
+
+def all_gather_rows(slices):
+    """All-gather along the sequence: the slices concatenated in rank order,
+    the full [T x H] tensor every rank holds afterwards ([Blog] 4.3)."""
+    return np.concatenate([_f64(s) for s in slices], axis=0)
+
+
+def sp_entry(X, g, eps, n_slices):
+    """Entry side of the sequence-parallel region before a column linear: each
+    rank normalizes its own sequence slice (the norm is row-wise, so the
+    sequence split is exact -- [Blog] 4.3), then the all-gather restores the
+    full input the column GEMM needs ([Blog] 4.3, [Wiki] Megatron-SP)."""
+    return all_gather_rows([rmsnorm(s, g, eps) for s in seq_slices(X, n_slices)])
+
+
+def rmsnorm_hidden_split(X_parts, g_parts, eps):
+    """RMSNorm of an input split along hidden across ranks ([Blog] 3.3): each
+    part's local sum of squares, the small statistic summed over the parts in
+    part order (the all-reduce of one number per row), and each part scaled
+    locally by the shared coefficient.  Equals rmsnorm of the concatenation.
+    """
+    X_parts = [_f64(x) for x in X_parts]
+    H = sum(x.shape[-1] for x in X_parts)
+    ss = np.sum(X_parts[0] * X_parts[0], axis=-1, keepdims=True)
+    for x in X_parts[1:]:
+        ss = ss + np.sum(x * x, axis=-1, keepdims=True)
+    inv = 1.0 / np.sqrt(ss / H + eps)
+    return [x * inv * _f64(gp)[None, :] for x, gp in zip(X_parts, g_parts)]
 
 
 # --------------------------------------------------------------------------

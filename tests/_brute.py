@@ -70,3 +70,12 @@ def attention(Q, K, V, batch, seq, heads):
 def attention_block(X, Wq, Wk, Wv, Wo, batch, seq, heads):
     O = attention(matmul(X, Wq), matmul(X, Wk), matmul(X, Wv), batch, seq, heads)
     return matmul(O, Wo)
+
+
+def rmsnorm(X, g, eps):
+    out = []
+    for row in X:
+        ms = sum(v * v for v in row) / len(row)
+        inv = 1.0 / math.sqrt(ms + eps)
+        out.append([v * inv * gg for v, gg in zip(row, g)])
+    return out

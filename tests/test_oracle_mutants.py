@@ -111,3 +111,35 @@ def test_naive_swiglu_split_is_caught(monkeypatch):
         return T.column_shards(full, N)
     monkeypatch.setattr(T, "swiglu_fused_blocks", naive)
     _fails(pins.test_swiglu_fused_block_layout)
+
+
+def test_local_statistic_rmsnorm_is_caught(monkeypatch):
+    """The mistake the blog post (section 3.3) warns about: each hidden part
+    normalized with its own local statistic instead of the reduced one."""
+    def local_only(X_parts, g_parts, eps):
+        return [T.rmsnorm(x, gp, eps) for x, gp in zip(X_parts, g_parts)]
+    monkeypatch.setattr(T, "rmsnorm_hidden_split", local_only)
+    _fails(pins.test_rmsnorm_hidden_split_equals_unsplit)
+
+
+def test_rmsnorm_mean_abs_instead_of_mean_square_is_caught(monkeypatch):
+    def bad(X, g, eps):
+        X = np.asarray(X, dtype=np.float64)
+        return X / (np.mean(np.abs(X), axis=-1, keepdims=True) + eps) * np.asarray(g)[None, :]
+    monkeypatch.setattr(T, "rmsnorm", bad)
+    _fails(pins.test_rmsnorm_invariants)
+
+
+def test_rmsnorm_eps_outside_sqrt_is_caught(monkeypatch, golden_dir):
+    def bad(X, g, eps):
+        X = np.asarray(X, dtype=np.float64)
+        return X / (np.sqrt(np.mean(X * X, axis=-1, keepdims=True)) + eps) * np.asarray(g)[None, :]
+    monkeypatch.setattr(T, "rmsnorm", bad)
+    _fails(pins.test_rmsnorm_hand_worked, golden_dir)
+
+
+def test_sp_gather_out_of_rank_order_is_caught(monkeypatch):
+    def bad(slices):
+        return np.concatenate([np.asarray(s, dtype=np.float64) for s in slices[::-1]], axis=0)
+    monkeypatch.setattr(T, "all_gather_rows", bad)
+    _fails(pins.test_sp_entry_equals_full_norm_bitwise)

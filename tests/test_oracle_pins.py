@@ -285,3 +285,69 @@ def test_divisibility_is_enforced():
         O.row_shards(np.zeros((10, 4)), 4)
     with pytest.raises(ValueError):
         O.attention_block_sharded(np.zeros((2, 6)), *[np.zeros((6, 6))] * 4, 1, 2, 6, 4)
+
+
+# ------------------------------------------------- sequence-parallel entry side
+def test_rmsnorm_hand_worked(golden_dir):
+    """RMSNorm values worked by hand (tests/golden/rmsnorm_hand_worked.json)."""
+    with open(os.path.join(golden_dir, "rmsnorm_hand_worked.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        y = O.rmsnorm(np.array([c["x"]]), np.array(c["g"]), c["eps"])[0]
+        assert np.allclose(y, c["y"], rtol=1e-14, atol=1e-15), c["work"]
+
+
+def test_rmsnorm_invariants():
+    """eps = 0, unit gain: every output row has mean square 1; the norm is
+    odd and invariant to positive scaling of a row; a constant row maps to
+    its sign times the gain."""
+    rng = np.random.default_rng(11)
+    X = rng.normal(size=(9, 24))
+    one = np.ones(24)
+    Y = O.rmsnorm(X, one, 0.0)
+    assert np.allclose(np.mean(Y * Y, axis=1), 1.0, rtol=1e-14)
+    assert np.allclose(O.rmsnorm(-X, one, 0.0), -Y, rtol=0, atol=1e-15)
+    alpha = rng.uniform(0.1, 10.0, size=(9, 1))
+    assert np.allclose(O.rmsnorm(alpha * X, one, 0.0), Y, rtol=1e-14)
+    g = rng.normal(size=24)
+    C = np.full((3, 24), -2.5)
+    assert np.allclose(O.rmsnorm(C, g, 0.0), -g[None, :] * np.ones((3, 1)), rtol=1e-15)
+
+
+def test_rmsnorm_matches_brute_force():
+    rng = np.random.default_rng(12)
+    X = rng.normal(size=(5, 7))
+    g = rng.normal(size=7)
+    ref = brute.rmsnorm(X.tolist(), g.tolist(), 1e-3)
+    assert np.allclose(O.rmsnorm(X, g, 1e-3), ref, rtol=1e-13)
+
+
+def test_sp_entry_equals_full_norm_bitwise():
+    """Normalizing each sequence slice and gathering the slices gives the
+    norm of the full tensor (the sequence split is exact for a row-wise op,
+    blog post section 4.3); the gather keeps rank order."""
+    rng = np.random.default_rng(13)
+    X = rng.normal(size=(24, 16))
+    g = rng.normal(size=16)
+    full = O.rmsnorm(X, g, 1e-5)
+    for n in (1, 2, 3, 4, 8):
+        assert np.array_equal(O.sp_entry(X, g, 1e-5, n), full)
+        sl = O.seq_slices(X, n)
+        assert np.array_equal(O.all_gather_rows(sl), X)
+        assert all(s.shape == (24 // n, 16) for s in sl)
+    with pytest.raises(ValueError):
+        O.sp_entry(X, g, 1e-5, 5)
+
+
+def test_rmsnorm_hidden_split_equals_unsplit():
+    """Blog post section 3.3: local sums of squares, one small reduction of the
+    statistic, local scaling -- the parts concatenate to the unsplit norm.
+    On integer inputs the statistic is exact, so the match is to rounding of
+    the final products only."""
+    rng = np.random.default_rng(14)
+    X = _ints(rng, (6, 32))
+    g = _ints(rng, (32,))
+    full = O.rmsnorm(X, g, 0.5)
+    for N in (1, 2, 4, 8):
+        parts = O.rmsnorm_hidden_split(np.split(X, N, axis=1), np.split(g, N), 0.5)
+        assert np.allclose(np.concatenate(parts, axis=1), full, rtol=1e-15, atol=0)
