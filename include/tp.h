@@ -107,6 +107,32 @@ tp_status tp_reduce_partials(void* stream, tp_dtype out_dt, int n_parts, int64_t
                              const float* P, int64_t part_stride, const void* bias, void* Y,
                              int n_slices, int slice);
 
+/*
+ * Entry side of the sequence-parallel region, before a column linear: each
+ * rank's sequence slice is RMS-normalized and written into its rows of the
+ * gathered buffer -- what every rank holds after the all-gather along the
+ * sequence.  The norm is row-wise, so it runs on sequence slices exactly
+ * (2kiu.com blog post, section 4.3; "张量并行", Megatron-SP section), and
+ * RMSNorm needs only the mean of squares over the whole hidden vector (blog
+ * post, section 3.3).
+ *
+ *   Y[r*T/n + t, :] = X_r[t, :] / sqrt(mean(X_r[t, :]^2) + eps) * gamma
+ *
+ *   X       slice r at X + r*slice_stride (elements), T/n rows of H, row stride
+ *           ldx; the slices must not overlap
+ *   gamma   [H], same dtype as X and Y
+ *   eps     finite, >= 0 (a zero row with eps == 0 divides by zero: NaN)
+ *   Y       [T x H] (ldy); slice == -1 normalizes every slice, slice == r only
+ *           rank r's (rows r*T/n .. (r+1)*T/n - 1 of Y, the other rows untouched)
+ * The statistic is an fp32 sum of squares in a fixed order (bit-identical run
+ * to run); output rounded once, round-to-nearest-even.  H a multiple of 8
+ * (bf16) or 4 (fp32), at most 16384 (bf16) / 8192 (fp32); T a multiple of
+ * n_slices.
+ */
+tp_status tp_rmsnorm_gather(void* stream, tp_dtype dt, int n_slices, int64_t T, int64_t H,
+                            const void* X, int64_t slice_stride, int64_t ldx, const void* gamma,
+                            float eps, void* Y, int64_t ldy, int slice);
+
 /* Whole MLP sublayer over shards [shard_begin, shard_begin + shard_count). */
 typedef struct {
   tp_dtype dt;      /* TP_F32 or TP_BF16 (inputs, intermediate and output)      */

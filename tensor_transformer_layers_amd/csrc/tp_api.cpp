@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <cmath>
 #include <map>
 #include <mutex>
 #include <string>
@@ -185,6 +186,30 @@ tp_status run_reduce(hipStream_t s, tp_dtype out_dt, int n_parts, int64_t T, int
   const hipError_t e = tp::launch_reduce(r, out_dt == TP_BF16, s);
   kt.stop();
   return hip_status(e, "reduce_partials launch");
+}
+
+tp_status validate_norm(tp_dtype dt, int n_slices, int64_t T, int64_t H, const void* X, int64_t slice_stride,
+                        int64_t ldx, const void* gamma, float eps, const void* Y, int64_t ldy, int slice) {
+  TP_TRY(check_dtype(dt));
+  if (T < 0 || H <= 0) return fail(TP_ERR_SHAPE, "T=%lld, H=%lld", (long long)T, (long long)H);
+  const int64_t vec = dt == TP_BF16 ? 8 : 4;
+  if (H % vec) return fail(TP_ERR_ALIGN, "H=%lld is not a multiple of %lld", (long long)H, (long long)vec);
+  const int64_t hmax = tp::rmsnorm_max_hidden(dt == TP_BF16);
+  if (H > hmax) return fail(TP_ERR_SHAPE, "H=%lld exceeds the norm kernel's limit %lld", (long long)H, (long long)hmax);
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(TP_ERR_SHAPE, "eps=%g must be finite and >= 0", (double)eps);
+  TP_TRY(check_slices(T, n_slices, slice));
+  if (T == 0) return TP_OK;  // empty input: nothing to read or write
+  const int64_t per = T / n_slices;
+  TP_TRY(check_matrix("X", X, per, H, ldx, vec));
+  TP_TRY(check_matrix("Y", Y, T, H, ldy, vec));
+  if (!gamma) return fail(TP_ERR_NULL, "gamma is NULL");
+  if (!aligned16(gamma)) return fail(TP_ERR_ALIGN, "gamma is not 16-byte aligned");
+  if (slice_stride % vec)
+    return fail(TP_ERR_ALIGN, "slice_stride %lld is not a multiple of %lld", (long long)slice_stride, (long long)vec);
+  if (n_slices > 1 && slice_stride < (per - 1) * ldx + H)
+    return fail(TP_ERR_SHAPE, "slice_stride %lld < (T/n_slices - 1)*ldx + H = %lld (slices overlap)",
+                (long long)slice_stride, (long long)((per - 1) * ldx + H));
+  return TP_OK;
 }
 
 tp::GemmParams gemm(const void* A, int64_t lda, int64_t sA, const void* B, int64_t ldb, int64_t sB, void* C,
@@ -406,6 +431,35 @@ tp_status tp_reduce_partials(void* stream, tp_dtype out_dt, int n_parts, int64_t
   if (T == 0) return ok();
   return run_reduce(static_cast<hipStream_t>(stream), out_dt, n_parts, T, H, P, part_stride, bias, Y, n_slices,
                     slice);
+}
+
+tp_status tp_rmsnorm_gather(void* stream, tp_dtype dt, int n_slices, int64_t T, int64_t H, const void* X,
+                            int64_t slice_stride, int64_t ldx, const void* gamma, float eps, void* Y, int64_t ldy,
+                            int slice) {
+  TP_TRY(validate_norm(dt, n_slices, T, H, X, slice_stride, ldx, gamma, eps, Y, ldy, slice));
+  if (T == 0) return ok();
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  tp::NormParams p{};
+  p.X = X;
+  p.slice_stride = slice_stride;
+  p.ldx = ldx;
+  p.gamma = gamma;
+  p.Y = Y;
+  p.ldy = ldy;
+  p.slice_rows = T / n_slices;
+  p.rows = slice < 0 ? T : p.slice_rows;
+  p.slice = slice;
+  p.H = (int)H;
+  p.inv_h = 1.0f / (float)H;
+  p.eps = eps;
+  if (log_enabled())
+    fprintf(stderr, "[tp] rmsnorm_gather %s: %d slices of [%lld x %lld] -> Y[%lld x %lld]%s\n", dt_name(dt), n_slices,
+            (long long)p.slice_rows, (long long)H, (long long)T, (long long)H, slice >= 0 ? " (one slice)" : "");
+  KernelTimer kt("rmsnorm_gather", s);
+  const hipError_t e = tp::launch_rmsnorm_gather(p, dt == TP_BF16, s);
+  kt.stop();
+  TP_TRY(hip_status(e, "rmsnorm_gather launch"));
+  return ok();
 }
 
 size_t tp_mlp_workspace_size(const tp_mlp_desc* d) {

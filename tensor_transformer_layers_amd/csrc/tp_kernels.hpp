@@ -89,6 +89,24 @@ struct ReduceParams {
 };
 hipError_t launch_reduce(const ReduceParams& p, bool out_bf16, hipStream_t s);
 
+// RMSNorm of sequence slices into the gathered buffer.  Row `row` of the
+// launch is row t of slice r (r = slice if slice >= 0, else row / slice_rows),
+// read at X + r*slice_stride + t*ldx and written at Y + (r*slice_rows + t)*ldy.
+struct NormParams {
+  const void* X;
+  int64_t slice_stride, ldx;
+  const void* gamma;
+  void* Y;
+  int64_t ldy;
+  int64_t rows;        // rows this launch normalizes
+  int64_t slice_rows;  // T / n_slices
+  int64_t slice;       // -1: every slice
+  int H;
+  float inv_h, eps;
+};
+int64_t rmsnorm_max_hidden(bool bf16_io);
+hipError_t launch_rmsnorm_gather(const NormParams& p, bool bf16_io, hipStream_t s);
+
 // Causal attention over local heads (head_dim 128), batched over `nshards`
 // problems advancing by sQK / sVt / sO elements.
 struct AttnParams {

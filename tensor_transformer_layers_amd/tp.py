@@ -50,6 +50,8 @@ _SIGS = {
     "tp_column_linear": (_int, [_vp, _int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64]),
     "tp_row_linear_partial": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]),
     "tp_reduce_partials": (_int, [_vp, _int, _int, _i64, _i64, _vp, _i64, _vp, _vp, _int, _int]),
+    "tp_rmsnorm_gather": (_int, [_vp, _int, _int, _i64, _i64, _vp, _i64, _i64, _vp, ctypes.c_float, _vp, _i64,
+                                 _int]),
     "tp_mlp_workspace_size": (_sz, [ctypes.POINTER(MlpDesc)]),
     "tp_attn_workspace_size": (_sz, [ctypes.POINTER(AttnDesc)]),
     "tp_mlp_partials_offset": (_sz, [ctypes.POINTER(MlpDesc)]),
@@ -115,6 +117,10 @@ def tp_row_linear_partial(*args) -> int:
 
 def tp_reduce_partials(*args) -> int:
     return lib().tp_reduce_partials(*args)
+
+
+def tp_rmsnorm_gather(*args) -> int:
+    return lib().tp_rmsnorm_gather(*args)
 
 
 def tp_mlp_forward(stream, desc: MlpDesc, ws, ws_bytes) -> int:
@@ -223,6 +229,22 @@ def reduce_partials(P, bias=None, out_dtype=None, n_slices=1, slice=-1, out=None
     odt = TP_BF16 if out_dtype == torch.bfloat16 else TP_F32
     check(tp_reduce_partials(_stream(stream), odt, n, T, H, _ptr(P), P.stride(0), _ptr(bias), _ptr(out),
                              n_slices, slice))
+    return out
+
+
+def rmsnorm_gather(X, gamma, eps, n_slices, out=None, slice=-1, slice_stride=None, stream=None):
+    """RMSNorm of each of the n_slices sequence slices of X ([T x H], slice r =
+    rows r*T/n ..) into the gathered [T x H] buffer ``out`` (allocated when
+    None).  With ``slice_stride`` the slices are read at X + r*slice_stride
+    elements instead (X then holds the first slice's [T/n x H] rows)."""
+    torch = _torch()
+    rows, H = X.shape
+    T = rows if slice_stride is None else rows * n_slices
+    stride = (T // n_slices) * X.stride(0) if slice_stride is None else slice_stride
+    if out is None:
+        out = torch.empty((T, H), dtype=X.dtype, device=X.device)
+    check(tp_rmsnorm_gather(_stream(stream), _dt(X), n_slices, T, H, _ptr(X), stride, _ld(X), _ptr(gamma),
+                            float(eps), _ptr(out), _ld(out), slice))
     return out
 
 

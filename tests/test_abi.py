@@ -175,3 +175,29 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(tp, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         tp.lib()
+
+
+def test_rmsnorm_gather_validation(L):
+    f = tp.tp_rmsnorm_gather
+    # args: stream, dt, n_slices, T, H, X, slice_stride, ldx, gamma, eps, Y, ldy, slice
+    ok = dict(dt=tp.TP_BF16, n=4, T=64, H=512, X=FAKE, ss=16 * 512, ldx=512, g=FAKE, eps=1e-6, Y=FAKE, ldy=512, sl=-1)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(None, a["dt"], a["n"], a["T"], a["H"], a["X"], a["ss"], a["ldx"], a["g"], a["eps"], a["Y"],
+                 a["ldy"], a["sl"])
+    assert call(T=0) == tp.TP_OK                        # empty: no HIP call
+    assert call(T=66) == tp.TP_ERR_DIVISIBILITY         # T not a multiple of n_slices
+    assert call(H=516) == tp.TP_ERR_ALIGN and "H=516" in tp.last_error()
+    assert call(dt=tp.TP_F32, H=20000, ss=16 * 20000, ldx=20000, ldy=20000) == tp.TP_ERR_SHAPE
+    assert "limit" in tp.last_error()
+    assert call(H=16392, ss=16 * 16392, ldx=16392, ldy=16392) == tp.TP_ERR_SHAPE
+    assert call(eps=-1.0) == tp.TP_ERR_SHAPE and "eps" in tp.last_error()
+    assert call(eps=float("inf")) == tp.TP_ERR_SHAPE
+    assert call(g=None) == tp.TP_ERR_NULL and "gamma" in tp.last_error()
+    assert call(X=None) == tp.TP_ERR_NULL
+    assert call(ldx=500) == tp.TP_ERR_SHAPE and "leading dimension" in tp.last_error()
+    assert call(ss=15 * 512) == tp.TP_ERR_SHAPE and "overlap" in tp.last_error()
+    assert call(ss=16 * 512 + 4) == tp.TP_ERR_ALIGN
+    assert call(sl=4) == tp.TP_ERR_SHAPE
+    assert call(Y=FAKE + 8) == tp.TP_ERR_ALIGN
