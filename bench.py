@@ -66,6 +66,8 @@ def kernel_work(w, name, shards_per_launch, rows_reduced):
             return 2.0 * T * hd * H * c, es * (c * T * hd + c * H * hd) + 4 * c * T * H
     if name == "reduce_partials":
         return 0.0, 4 * N * rows_reduced * H + es * rows_reduced * H + (es * H if w.sigma_bias else 0)
+    if name == "rmsnorm_gather":  # square, add, two scalings per element; X read once, Y written once
+        return 4.0 * T * H, es * (2 * T * H + H)
     raise KeyError(name)
 
 
@@ -87,7 +89,7 @@ def roofline(w, name, flops, nbytes, avg_s):
 KERNEL_SOURCES = {
     "mlp_column_gemm": "gemm.hip", "mlp_row_gemm": "gemm.hip", "mlp_fused": "mlp_fused.hip", "attn_qk_gemm": "gemm.hip",
     "attn_vt_gemm": "gemm.hip", "attn_out_gemm": "gemm.hip", "attn_core": "attention.hip",
-    "reduce_partials": "reduce.hip",
+    "reduce_partials": "reduce.hip", "rmsnorm_gather": "norm.hip",
 }
 
 
@@ -109,21 +111,23 @@ def kernel_source_hash(kernel=None):
 KERNEL_SYMBOL = {
     "mlp_column_gemm": "gemm_", "mlp_row_gemm": "gemm_", "mlp_fused": "mlp_fused_kernel",
     "attn_qk_gemm": "gemm_", "attn_vt_gemm": "gemm_", "attn_out_gemm": "gemm_",
-    "attn_core": "attn_fwd_kernel", "reduce_partials": "reduce_kernel",
+    "attn_core": "attn_fwd_kernel", "reduce_partials": "reduce_kernel", "rmsnorm_gather": "rmsnorm_gather_kernel",
 }
 
 
-def launch_order(w):
+def launch_order(w, sp_entry=False):
     """Kernels one step of workload w launches, in order.  A bf16 GELU MLP
     with hidden 256 or 512 and a shard width that is a multiple of 32 (at
     most 4096) runs the fused kernel; every other MLP the column and row
-    GEMMs (the dispatch rule of tp_mlp_forward)."""
+    GEMMs (the dispatch rule of tp_mlp_forward).  With the sequence-parallel
+    entry side, the norm-and-gather kernel comes first."""
+    head = ["rmsnorm_gather"] if sp_entry else []
     if w.kind == "attn":
-        return ["attn_qk_gemm", "attn_vt_gemm", "attn_core", "attn_out_gemm", "reduce_partials"]
+        return head + ["attn_qk_gemm", "attn_vt_gemm", "attn_core", "attn_out_gemm", "reduce_partials"]
     Fs = w.F // w.N
     if w.kind == "mlp_gelu" and w.dtype == "bf16" and w.H in (256, 512) and Fs % 32 == 0 and Fs <= 4096:
-        return ["mlp_fused", "reduce_partials"]
-    return ["mlp_column_gemm", "mlp_row_gemm", "reduce_partials"]
+        return head + ["mlp_fused", "reduce_partials"]
+    return head + ["mlp_column_gemm", "mlp_row_gemm", "reduce_partials"]
 
 
 def traffic_path(workload_name):
@@ -144,7 +148,7 @@ def measured_traffic(kernel, workload_name):
     return None
 
 
-def write_traffic(w, share, pmc_dir, argv_line):
+def write_traffic(w, share, pmc_dir, argv_line, sp_entry=False):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
     WRITE_SIZE, each with --calib-copy) into profiles/traffic_<workload>.txt.
 
@@ -154,7 +158,8 @@ def write_traffic(w, share, pmc_dir, argv_line):
     import csv
     import collections
 
-    order = launch_order(w)
+    order = launch_order(w, sp_entry)
+    name = w.name + ("_sp_entry" if sp_entry else "")
     per = {}
     factor = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -163,7 +168,7 @@ def write_traffic(w, share, pmc_dir, argv_line):
         copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
         big = max(copies, key=lambda r: int(r["Grid_Size"]))
         factor[counter] = float(2 ** 30) / (float(big["Counter_Value"]) * 1024.0)
-        ours = [r for r in rows if "tp::" in r["Kernel_Name"]]
+        ours = [r for r in rows if "tp::" in r["Kernel_Name"] or "_ZN2tp" in r["Kernel_Name"]]
         vals = collections.defaultdict(list)
         for i, r in enumerate(ours):
             k = order[i % len(order)]
@@ -173,12 +178,12 @@ def write_traffic(w, share, pmc_dir, argv_line):
             vals[k].append(float(r["Counter_Value"]))
         per[counter] = {k: sum(v) / len(v) for k, v in vals.items()}
     lines = [
-        f"# HBM traffic per launch: {w.name} ({share})",
+        f"# HBM traffic per launch: {name} ({share})",
         "#",
         "# Commands (from /tmp on the GPU host, REPO = repository root):",
         f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d DIR/FETCH_SIZE -o run -- python3 $REPO/bench.py {argv_line}",
         f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d DIR/WRITE_SIZE -o run -- python3 $REPO/bench.py {argv_line}",
-        f"#   python3 $REPO/bench.py --config {w.key} --share {share} --traffic-from DIR",
+        f"#   python3 $REPO/bench.py --config {w.key} --share {share}{' --sp-entry' if sp_entry else ''} --traffic-from DIR",
         "#",
         f"# Calibration (1 GiB device copy): FETCH_SIZE x {factor['FETCH_SIZE']:.4f}, WRITE_SIZE x {factor['WRITE_SIZE']:.4f}",
         "#",
@@ -196,7 +201,7 @@ def write_traffic(w, share, pmc_dir, argv_line):
     lines.append("# traffic_bytes <kernel> <bytes per launch> <hash of that kernel's sources>")
     for k, v in out.items():
         lines.append(f"traffic_bytes {k} {v:.0f} {kernel_source_hash(k)}")
-    path = traffic_path(w.name)
+    path = traffic_path(name)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     return path
@@ -247,6 +252,9 @@ def main():
                          "the shader clock takes tens of ms to settle after idle")
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: GELU MLP bf16, T=16384, H=512, F=2048, N=4)")
     ap.add_argument("--share", choices=["layer", "rank"], default="layer")
+    ap.add_argument("--sp-entry", action="store_true",
+                    help="MLP workloads with a reduce-scatter: start each step with the sequence-parallel entry "
+                         "side (RMSNorm of every sequence slice into the gathered input, the all-gather stand-in)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -260,8 +268,9 @@ def main():
         from tensor_transformer_layers_amd import configs
 
         w = configs.CONFIGS[args.config]
-        argv = f"--config {args.config} --share {args.share} --steps 3 --warmup 1 --no-cpu-baseline --calib-copy"
-        print(write_traffic(w, args.share, args.traffic_from, argv))
+        argv = (f"--config {args.config} --share {args.share}{' --sp-entry' if args.sp_entry else ''} "
+                "--steps 3 --warmup 1 --no-cpu-baseline --calib-copy")
+        print(write_traffic(w, args.share, args.traffic_from, argv, args.sp_entry))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -277,9 +286,20 @@ def main():
 
     tp.lib()  # fails loudly if libtp.so is missing
     w = configs.CONFIGS[args.config]
+    if args.sp_entry and (w.kind == "attn" or w.n_slices < 2 or args.share != "layer"):
+        print("bench.py: --sp-entry needs an MLP workload with a reduce-scatter (--config 5) and --share layer",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
     log(f"workload {w.name}: generating seeded inputs")
     host = inputs.make_inputs(w)
     d = workloads.device_inputs(w, host)
+    if args.sp_entry:
+        # X holds the n_slices sequence slices of the sublayer input; each step
+        # normalizes them into Xn, the gathered input of the column GEMM
+        gain = workloads.to_device(inputs.norm_gain(w), d["X"].dtype)
+        x_slices = d["X"]
+        d = dict(d, X=torch.empty_like(x_slices))
+        tp.rmsnorm_gather(x_slices, gain, inputs.NORM_EPS, w.n_slices, out=d["X"])
     Y, ws = workloads.forward(w, d)  # allocates Y and the workspace once
     torch.cuda.synchronize()
     rank_slice = 0 if w.n_slices > 1 else -1
@@ -290,6 +310,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
+        if args.sp_entry:
+            tp.rmsnorm_gather(x_slices, gain, inputs.NORM_EPS, w.n_slices, out=d["X"], stream=stream)
         if args.share == "layer":
             workloads.forward(w, d, Y=Y, ws=ws, stream=stream)
         else:
@@ -352,6 +374,8 @@ def main():
     shards = w.N if args.share == "layer" else 1
     rows_red = w.T if (args.share == "layer" or w.n_slices == 1) else w.T // w.n_slices
     flops = w.flops_layer() if args.share == "layer" else w.flops_shard()
+    if args.sp_entry:
+        flops += kernel_work(w, "rmsnorm_gather", 1, 0)[0]
     value = flops / (ms_step / 1e3) / 1e12
 
     kernels = {}
@@ -369,7 +393,7 @@ def main():
     roof["kernel"] = dom
     roof["avg_us"] = round(avg * 1e6, 2)
     roof["algorithmic"] = {"flop": f, "bytes": b}
-    roof["traffic"] = measured_traffic(dom, w.name)
+    roof["traffic"] = measured_traffic(dom, w.name + ("_sp_entry" if args.sp_entry else ""))
 
     out = {
         "metric": METRIC,
@@ -389,6 +413,8 @@ def main():
             "ffn": w.F if w.kind != "attn" else None, "heads": w.heads or None, "shards": w.N,
             "share": "all shards + reduction" if args.share == "layer" else "rank 0 shard + reduction",
             "reduce_scatter_slices": w.n_slices, "seed": w.seed,
+            **({"sp_entry": {"norm": "rmsnorm", "eps": inputs.NORM_EPS, "gain": inputs.NORM_GAIN_RECIPE}}
+               if args.sp_entry else {}),
         },
         "pct_of_bf16_mfma_peak": round(100 * value * 1e12 / PEAK_BF16, 2) if w.dtype == "bf16" else None,
         "roofline": roof,

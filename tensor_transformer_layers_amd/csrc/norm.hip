@@ -9,12 +9,16 @@
 //
 //   Y[r*T/N + t, :] = X_r[t, :] * (1 / sqrt(mean(X_r[t, :]^2) + eps)) * g
 //
-// HBM-bound streaming kernel, one wave per token row:
+// HBM-bound streaming kernel, one to four waves per token row (wide rows are
+// split so that each wave holds at most 8 KB of its row and enough waves stay
+// resident to keep HBM busy):
 //  * the row is read once into registers (U 16-byte pieces per lane, lane i
-//    taking bytes 16i.. of every KB), so X leaves HBM exactly once;
+//    taking bytes 16i.. of every KB of its wave's part), so X leaves HBM
+//    exactly once;
 //  * the sum of squares runs in fp32, per lane in piece order, then across
 //    the wave by an xor butterfly -- every pair adds the same two values, so
-//    all lanes end with the same bits and the result repeats run to run;
+//    all lanes end with the same bits -- then, for split rows, over the
+//    row's waves in wave order through LDS; the result repeats run to run;
 //  * the scale is the hardware reciprocal square root of mean + eps (about
 //    one ulp in fp32, far below the bf16 output step);
 //  * y = (x * scale) * g in fp32, one round-to-nearest-even cast, 16-byte
@@ -27,7 +31,6 @@
 namespace tp {
 namespace {
 
-constexpr int kNormThreads = 256;  // 4 waves = 4 rows per workgroup
 
 template <typename T>
 struct Vec;
@@ -42,13 +45,17 @@ struct Vec<float> {
   static constexpr int E = 4;
 };
 
-template <typename T, int U>
-__global__ __launch_bounds__(kNormThreads) void rmsnorm_gather_kernel(NormParams p) {
+template <typename T, int U, int WPR, int NT>
+__global__ __launch_bounds__(NT) void rmsnorm_gather_kernel(NormParams p) {
   using V = typename Vec<T>::V;
   constexpr int E = Vec<T>::E;
+  constexpr int kRows = NT / 64 / WPR;  // rows per workgroup
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * (kNormThreads / 64) + (threadIdx.x >> 6);
-  if (row >= p.rows) return;
+  const int wv = threadIdx.x >> 6;
+  const int part = wv % WPR;  // which part of its row this wave holds
+  const int64_t row = (int64_t)blockIdx.x * kRows + wv / WPR;
+  if (WPR == 1 && row >= p.rows) return;  // split rows keep every wave for the barrier
+  const bool live = row < p.rows;
   const int64_t per = p.slice_rows;
   const int64_t r = p.slice >= 0 ? p.slice : row / per;  // rank (slice) of this row
   const int64_t t = p.slice >= 0 ? row : row - r * per;  // row within the slice
@@ -60,8 +67,8 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_gather_kernel(NormParams
   float ss = 0.0f;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int c = (u * 64 + lane) * E;  // first element of this piece
-    if (c < p.H) {
+    const int c = ((part * U + u) * 64 + lane) * E;  // first element of this piece
+    if (live && c < p.H) {
       v[u] = *reinterpret_cast<const V*>(x + c);
     } else {
 #pragma unroll
@@ -77,12 +84,21 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_gather_kernel(NormParams
     }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+  if constexpr (WPR > 1) {
+    __shared__ float part_ss[NT / 64];
+    if (lane == 0) part_ss[wv] = ss;
+    __syncthreads();
+    const int w0 = wv - part;
+    ss = part_ss[w0];
+#pragma unroll
+    for (int k = 1; k < WPR; ++k) ss += part_ss[w0 + k];
+  }
   const float scale = __builtin_amdgcn_rsqf(ss * p.inv_h + p.eps);
 
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int c = (u * 64 + lane) * E;
-    if (c < p.H) {
+    const int c = ((part * U + u) * 64 + lane) * E;
+    if (live && c < p.H) {
       const V gv = *reinterpret_cast<const V*>(g + c);
       V o;
 #pragma unroll
@@ -98,24 +114,27 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_gather_kernel(NormParams
   }
 }
 
+template <typename T, int U, int WPR, int NT = 256>
+hipError_t launch_shape(const NormParams& p, hipStream_t s) {
+  constexpr int kRows = NT / 64 / WPR;
+  const dim3 g((unsigned)((p.rows + kRows - 1) / kRows)), b(NT);
+  launch_kernel((rmsnorm_gather_kernel<T, U, WPR, NT>), g, b, 0u, s, p);
+  return hipGetLastError();
+}
+
+// pieces = 1 KB pieces of a row; rows of more than 2 pieces are split over
+// 2 to 8 waves (at most 4 pieces, 16 registers of row data, per wave)
 template <typename T>
 hipError_t launch_typed(const NormParams& p, hipStream_t s) {
   constexpr int per_piece = 64 * Vec<T>::E;
   const int64_t pieces = (p.H + per_piece - 1) / per_piece;
-  const dim3 g((unsigned)((p.rows + kNormThreads / 64 - 1) / (kNormThreads / 64))), b(kNormThreads);
-#define TP_NORM_CASE(UU)                                                        \
-  if (pieces <= UU) {                                                           \
-    launch_kernel((rmsnorm_gather_kernel<T, UU>), g, b, 0u, s, p);              \
-    return hipGetLastError();                                                   \
-  }
-  TP_NORM_CASE(1)
-  TP_NORM_CASE(2)
-  TP_NORM_CASE(4)
-  TP_NORM_CASE(8)
-  TP_NORM_CASE(16)
-  TP_NORM_CASE(24)
-  TP_NORM_CASE(32)
-#undef TP_NORM_CASE
+  if (pieces <= 1) return launch_shape<T, 1, 1>(p, s);
+  if (pieces <= 2) return launch_shape<T, 2, 1>(p, s);
+  if (pieces <= 4) return launch_shape<T, 2, 2>(p, s);
+  if (pieces <= 8) return launch_shape<T, 2, 4>(p, s);
+  if (pieces <= 16) return launch_shape<T, 4, 4>(p, s);
+  if (pieces <= 24) return launch_shape<T, 3, 8, 512>(p, s);
+  if (pieces <= 32) return launch_shape<T, 4, 8, 512>(p, s);
   return hipErrorInvalidValue;
 }
 

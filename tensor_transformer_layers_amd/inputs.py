@@ -114,6 +114,12 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
     return out
 
 
+def make_x(w: Workload) -> np.ndarray:
+    """Only the input X of workload ``w`` (the same values make_inputs draws)."""
+    kids = np.random.SeedSequence(w.seed).spawn(len(TENSORS[w.kind]))
+    return round_to_dtype(draw(kids[0], shapes(w)["X"], w.sigma_x), w.dtype)
+
+
 def sample_rows(T: int, count: int, seed: int, must=()) -> np.ndarray:
     """Sorted, distinct token rows: ``must`` plus seeded uniform picks."""
     rng = np.random.default_rng(np.random.SeedSequence([seed, 0x5A3]))
@@ -122,3 +128,16 @@ def sample_rows(T: int, count: int, seed: int, must=()) -> np.ndarray:
     while len(rows) < count:
         rows.update(int(r) for r in rng.integers(0, T, size=count - len(rows)))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+# Sequence-parallel entry side (RMSNorm before the column linear).  The pages
+# give neither eps nor gain values: eps = 1e-6 and a gain of 1 + N(0, 0.1^2),
+# rounded to the workload dtype, drawn from its own stream of the seed.
+NORM_EPS = 1e-6
+NORM_GAIN_RECIPE = "1 + N(0, 0.1^2) per feature, rounded to the workload dtype, SeedSequence([seed, 1])"
+
+
+def norm_gain(w: Workload) -> np.ndarray:
+    """The RMSNorm gain [H] of workload w (recipe above)."""
+    g = np.float32(1.0) + draw(np.random.SeedSequence([w.seed, 1]), (w.H,), 0.1)
+    return round_to_dtype(g.astype(np.float32), w.dtype)

@@ -145,3 +145,23 @@ def test_sp_round_trip_vs_oracle(T, H, F, N, ns):
         assert e <= 2e-2, f"slice {r}: normwise error {e:.3e}"
     # the gathered normalized input itself
     _check_norm(Xn, xn64, "bf16")
+
+
+def test_sp_entry_full_size_workload5_sampled():
+    """Workload 5 at full size (T = 16384, H = 12288, 8 sequence slices), the
+    launch bench.py --sp-entry times; the norm is row-wise, so sampled rows --
+    including the first and last row of every slice -- are checked one by one
+    against the oracle."""
+    from tensor_transformer_layers_amd import configs
+    w = configs.CONFIGS[5]
+    say(f"sp entry full size: {w.name}")
+    X = inputs.make_x(w)
+    g = inputs.norm_gain(w)
+    per = w.T // w.n_slices
+    Xn = tp.rmsnorm_gather(torch.from_numpy(X).to(DEV, torch.bfloat16), torch.from_numpy(g).to(DEV, torch.bfloat16),
+                           inputs.NORM_EPS, w.n_slices)
+    torch.cuda.synchronize()
+    must = [r * per for r in range(w.n_slices)] + [r * per + per - 1 for r in range(w.n_slices)]
+    rows = inputs.sample_rows(w.T, 512, w.seed + 5, must=must)
+    ref = O.rmsnorm(X[rows].astype(np.float64), g, inputs.NORM_EPS)
+    _check_norm(Xn[torch.from_numpy(rows).to(DEV)], ref, "bf16")
