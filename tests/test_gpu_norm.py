@@ -3,11 +3,12 @@ RMSNorm of each sequence slice into the gathered buffer (the all-gather
 stand-in), alone and feeding the MLP sublayer with a reduce-scatter.
 
 Tolerances.  The norm is elementwise after one row statistic, so each output
-element is compared with the oracle's fp64 value: within one bf16 step
-(2^-8 relative) for bf16 output -- the device rounds its fp32 value once, the
-reference is exact -- and within 1e-5 relative for fp32 output (fp32 sum of
-squares and the hardware reciprocal square root).  A small absolute floor
-(2^-20 of the row-set maximum) covers outputs that round to zero.  The MLP
+element is compared with the oracle's fp64 value.  bf16 output: the device
+rounds its fp32 value once (round-to-nearest-even: under 2^-8 relative), and
+that fp32 value carries a few fp32 ulps of evaluation error, so the bound is
+2^-8 + 2^-20 relative.  fp32 output: 1e-5 relative (fp32 sum of squares and
+the hardware reciprocal square root).  A small absolute floor (2^-20 of the
+row-set maximum) covers outputs that round to zero.  The MLP
 built on top keeps the suite's bf16 bound (normwise 2e-2).
 """
 import sys
@@ -42,7 +43,7 @@ def _tdt(dt):
 
 def _check_norm(y_dev, ref, dt):
     y = y_dev.float().cpu().numpy().astype(np.float64)
-    rel = 2.0 ** -8 if dt == "bf16" else 1e-5
+    rel = 2.0 ** -8 + 2.0 ** -20 if dt == "bf16" else 1e-5
     floor = 2.0 ** -20 * float(np.max(np.abs(ref)))
     bad = np.abs(y - ref) > rel * np.abs(ref) + floor
     assert not bad.any(), f"{int(bad.sum())} elements off, worst |d| = {float(np.max(np.abs(y - ref))):.3e}"
