@@ -38,3 +38,32 @@ def workload(kind, host, batch=None, seq=None, heads=None, rows=None):
     if kind == "attn":
         return attention(host["X"], host["Wq"], host["Wk"], host["Wv"], host["Wo"], batch, seq, heads, rows)
     raise ValueError(kind)
+
+
+def mlp_gelu_backward(X, A, a, B, dY, act="gelu"):
+    """Full backward of the GELU MLP on storage-layout weights (A [F x H],
+    B [H x F]); gradients come back in that same storage layout
+    (dA [F x H], dB [H x F])."""
+    g = O.mlp_backward(X, A.T, a, B.T, dY, act=act)
+    return {"dX": g["dX"], "dA": g["dA"].T, "da": g["da"], "dB": g["dB"].T, "db": g["db"]}
+
+
+def mlp_gelu_backward_sample(X, A, a, B, dY, rows, feats):
+    """Sampled entries of the same gradients (storage layout), each from the
+    definition in ``tp_oracle.mlp_backward`` restricted to what it needs:
+    dX[rows, :] needs dZ on those token rows only; dA[feats, :], da[feats]
+    and dB[:, feats] need the pre-activation of those features over all
+    tokens only; db is the full column sum of dY."""
+    X64 = np.asarray(X, dtype=np.float64)
+    dY64 = np.asarray(dY, dtype=np.float64)
+    A64 = np.asarray(A, dtype=np.float64)
+    B64 = np.asarray(B, dtype=np.float64)
+    a64 = None if a is None else np.asarray(a, dtype=np.float64)
+    rows = np.asarray(rows)
+    feats = np.asarray(feats)
+    Zr = O.linear(X64[rows], A64.T, a64)
+    dZr = (dY64[rows] @ B64) * O.gelu_grad(Zr)
+    Zf = O.linear(X64, A64[feats].T, None if a64 is None else a64[feats])
+    dZf = (dY64 @ B64[:, feats]) * O.gelu_grad(Zf)
+    return {"dX": dZr @ A64, "dA": dZf.T @ X64, "da": dZf.sum(axis=0),
+            "dB": dY64.T @ O.gelu(Zf), "db": dY64.sum(axis=0)}

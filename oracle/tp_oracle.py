@@ -42,6 +42,7 @@ __all__ = [
     "mlp_swiglu_sharded", "attention_block_sharded", "rs_slice",
     "reduce_partials_fp32", "to_bf16", "attention_block_rows",
     "rmsnorm", "seq_slices", "all_gather_rows", "sp_entry", "rmsnorm_hidden_split",
+    "gelu_grad", "mlp_backward", "mlp_backward_sharded",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -352,6 +353,88 @@ def rmsnorm_hidden_split(X_parts, g_parts, eps):
         ss = ss + np.sum(x * x, axis=-1, keepdims=True)
     inv = 1.0 / np.sqrt(ss / H + eps)
     return [x * inv * _f64(gp)[None, :] for x, gp in zip(X_parts, g_parts)]
+
+
+# --------------------------------------------------------------------------
+# backward of the MLP pair
+# --------------------------------------------------------------------------
+_INV_SQRT_2PI = 1.0 / math.sqrt(2.0 * math.pi)
+
+
+def gelu_grad(z):
+    """Derivative of the exact GELU: d/dz [z Phi(z)] = Phi(z) + z phi(z),
+    phi the standard normal density (product rule on the erf form of
+    ``gelu``)."""
+    z = _f64(z)
+    return 0.5 * (1.0 + erf(z / _SQRT2)) + z * np.exp(-0.5 * z * z) * _INV_SQRT_2PI
+
+
+def _act_and_grad(act):
+    if act == "gelu":
+        return gelu, gelu_grad
+    if act == "none":
+        return (lambda z: _f64(z)), (lambda z: np.ones_like(_f64(z)))
+    raise ValueError(act)
+
+
+def mlp_backward(X, A, a, B, dY, act="gelu"):
+    """Gradients of the unsharded MLP Y = act(X A + a) B + b for an upstream
+    gradient dY (the gradient of the scalar sum(dY * Y)):
+
+        Z = X A + a,  Hd = act(Z)
+        dB = Hd^T dY,  db = column sums of dY
+        dZ = (dY B^T) * act'(Z)
+        dA = X^T dZ,   da = column sums of dZ,   dX = dZ A^T
+
+    Math layout as everywhere here (A [H x F], B [F x H]).  ``a`` may be
+    None (no column bias; da is then still returned).  Returns a dict with
+    dX, dA, da, dB, db.
+    """
+    f, fp = _act_and_grad(act)
+    X, A, B, dY = _f64(X), _f64(A), _f64(B), _f64(dY)
+    Z = linear(X, A, a)
+    Hd = f(Z)
+    dZ = (dY @ B.T) * fp(Z)
+    return {"dX": dZ @ A.T, "dA": X.T @ dZ, "da": dZ.sum(axis=0),
+            "dB": Hd.T @ dY, "db": dY.sum(axis=0)}
+
+
+def mlp_backward_sharded(X, A, a, B, dY, N, act="gelu"):
+    """The backward of the paired layer over N shards, each shard's work
+    written out.
+
+    The gradient of the full output reaches every shard whole (the forward's
+    sum was an all-reduce), so shard i forms dH_i = dY B_i^T for its own
+    intermediate slice, dZ_i = dH_i * act'(Z_i) on that slice, and its local
+    weight gradients dA_i = X^T dZ_i, da_i, dB_i = H_i^T dY with no exchange.
+    Its input gradient dZ_i A_i^T is only a partial of the full dX (X was
+    replicated in the forward), so the N partials are summed: the all-reduce
+    of the column layer's backward ([Scratch] section 4: identity in the
+    forward, all-reduce in the backward; [Blog] 4.1: the input-gradient
+    reduction needs an all-reduce).  The row bias gradient is the column sum
+    of dY, formed once and not per shard ([Basics] bias remark: the row bias
+    enters once).  Partials are summed in shard order.
+
+    Returns the unsharded-layout gradients (dA with the shards' columns
+    side by side, dB with their rows stacked) plus the list of dX partials.
+    """
+    f, fp = _act_and_grad(act)
+    X, dY = _f64(X), _f64(dY)
+    As = column_shards(A, N)
+    Bs = row_shards(B, N)
+    s = As[0].shape[1]
+    a_s = [None] * N if a is None else [_f64(a)[i * s:(i + 1) * s] for i in range(N)]
+    dA, da, dB, parts = [], [], [], []
+    for Ai, ai, Bi in zip(As, a_s, Bs):
+        Zi = linear(X, Ai, ai)
+        dZi = (dY @ Bi.T) * fp(Zi)
+        dA.append(X.T @ dZi)
+        da.append(dZi.sum(axis=0))
+        dB.append(f(Zi).T @ dY)
+        parts.append(dZi @ Ai.T)
+    return {"dX": _fold(parts), "dA": np.concatenate(dA, axis=1),
+            "da": np.concatenate(da), "dB": np.concatenate(dB, axis=0),
+            "db": dY.sum(axis=0), "dX_parts": parts}
 
 
 # --------------------------------------------------------------------------
