@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "TFLOP/s per sharded TP MLP/attn layer fwd on 1 GPU; % of bf16 MFMA peak"
+METRIC_BWD = "TFLOP/s per sharded TP MLP layer bwd on 1 GPU; % of bf16 MFMA peak"
 PEAK_BF16 = 2.5e15     # dense MFMA, bf16
 PEAK_F32 = 157.3e12    # dense MFMA, fp32
 PEAK_HBM = 8.0e12      # bytes/s
@@ -64,10 +65,59 @@ def kernel_work(w, name, shards_per_launch, rows_reduced):
             return (w.batch * hl * c * 4.0 * w.head_dim * w.seq * (w.seq + 1) / 2, es * 4 * c * T * hd)
         if name == "attn_out_gemm":
             return 2.0 * T * hd * H * c, es * (c * T * hd + c * H * hd) + 4 * c * T * H
+    if name.startswith("bwd_"):
+        return backward_kernel_work(w, name, shards_per_launch)
     if name == "reduce_partials":
         return 0.0, 4 * N * rows_reduced * H + es * rows_reduced * H + (es * H if w.sigma_bias else 0)
     if name == "rmsnorm_gather":  # square, add, two scalings per element; X read once, Y written once
         return 4.0 * T * H, es * (2 * T * H + H)
+    raise KeyError(name)
+
+
+def backward_splits(T, Fc, H):
+    """Split-K factor of the backward's token-axis GEMMs (the rule of
+    tp_mlp_backward: at least ~2 workgroups per CU, K per split >= 512 and a
+    multiple of 8)."""
+    big = ((Fc + 255) // 256) * ((H + 255) // 256)
+    tiles = big if big >= 256 else ((Fc + 127) // 128) * ((H + 127) // 128)
+    s = 1
+    while s < 16 and tiles * s < 512 and T // (2 * s) >= 512:
+        s *= 2
+    while s > 1 and T % (8 * s):
+        s //= 2
+    return s
+
+
+def backward_flops(w, c):
+    """Algorithmic FLOP of the MLP pair's backward over c shards: dH, dX, dA
+    and dB, each 2*T*H*(c*Fs).  The recomputed column product (another
+    2*T*H*c*Fs) is work this implementation adds and is not counted."""
+    return 8.0 * w.T * w.H * w.Fs * c
+
+
+def backward_kernel_work(w, name, c):
+    """Algorithmic (flops, bytes) of one launch of a backward kernel over c
+    shards (bf16 operands, fp32 weight gradients)."""
+    T, H, N = w.T, w.H, w.N
+    Fc = w.Fs * c
+    S = backward_splits(T, Fc, H)
+    bias = w.sigma_bias is not None
+    if name == "bwd_recompute_gemm":
+        return 2.0 * T * H * Fc, 2 * (T * H + Fc * H + T * Fc) + (2 * Fc if bias else 0)
+    if name == "bwd_dz_gemm":  # reads the stored pre-activation beside the accumulators
+        return 2.0 * T * H * Fc, 2 * (T * H + Fc * H + 2 * T * Fc)
+    if name == "bwd_dx_gemm":
+        return 2.0 * T * Fc * H, 2 * (T * Fc + H * Fc) + 4 * c * T * H
+    if name in ("bwd_da_gemm", "bwd_db_gemm"):
+        return 2.0 * T * Fc * H, 2 * (T * Fc + T * H) + 4 * S * Fc * H
+    if name == "bwd_transpose":  # X, dY, A, B, act(Z), dZ: each read once and written once
+        return 0.0, 2 * 2 * (2 * T * H + 2 * Fc * H + 2 * T * Fc) / 6
+    if name == "bwd_bias_rowsum":  # da (when the workload has biases) and db
+        launches = [(Fc, T)] if bias else []
+        launches.append((H, T))
+        return 0.0, sum(2 * r * t + 4 * r for r, t in launches) / len(launches)
+    if name == "bwd_splitk_reduce":  # dA and dB
+        return 0.0, 4 * S * Fc * H + 4 * Fc * H
     raise KeyError(name)
 
 
@@ -90,6 +140,9 @@ KERNEL_SOURCES = {
     "mlp_column_gemm": "gemm.hip", "mlp_row_gemm": "gemm.hip", "mlp_fused": "mlp_fused.hip", "attn_qk_gemm": "gemm.hip",
     "attn_vt_gemm": "gemm.hip", "attn_out_gemm": "gemm.hip", "attn_core": "attention.hip",
     "reduce_partials": "reduce.hip", "rmsnorm_gather": "norm.hip",
+    "bwd_transpose": "bwd.hip", "bwd_bias_rowsum": "bwd.hip", "bwd_recompute_gemm": "gemm.hip",
+    "bwd_dz_gemm": "gemm.hip", "bwd_dx_gemm": "gemm.hip", "bwd_da_gemm": "gemm.hip", "bwd_db_gemm": "gemm.hip",
+    "bwd_splitk_reduce": "reduce.hip",
 }
 
 
@@ -112,15 +165,31 @@ KERNEL_SYMBOL = {
     "mlp_column_gemm": "gemm_", "mlp_row_gemm": "gemm_", "mlp_fused": "mlp_fused_kernel",
     "attn_qk_gemm": "gemm_", "attn_vt_gemm": "gemm_", "attn_out_gemm": "gemm_",
     "attn_core": "attn_fwd_kernel", "reduce_partials": "reduce_kernel", "rmsnorm_gather": "rmsnorm_gather_kernel",
+    "bwd_transpose": "transpose_kernel", "bwd_bias_rowsum": "rowsum_kernel", "bwd_recompute_gemm": "gemm_",
+    "bwd_dz_gemm": "gemm_", "bwd_dx_gemm": "gemm_", "bwd_da_gemm": "gemm_", "bwd_db_gemm": "gemm_",
+    "bwd_splitk_reduce": "reduce_kernel",
 }
 
 
-def launch_order(w, sp_entry=False):
+def backward_launch_order(w):
+    """Kernels one backward step (all shards) launches, in order (the
+    sequence of tp_mlp_backward)."""
+    split = backward_splits(w.T, w.F, w.H) > 1
+    order = ["bwd_transpose"] * 4 + ["bwd_recompute_gemm", "bwd_dz_gemm"] + ["bwd_transpose"] * 2
+    order += ["bwd_dx_gemm", "bwd_da_gemm"] + (["bwd_splitk_reduce"] if split else [])
+    order += ["bwd_db_gemm"] + (["bwd_splitk_reduce"] if split else [])
+    order += ["bwd_bias_rowsum"] * (2 if w.sigma_bias is not None else 1)
+    return order + ["reduce_partials"]
+
+
+def launch_order(w, sp_entry=False, backward=False):
     """Kernels one step of workload w launches, in order.  A bf16 GELU MLP
     with hidden 256 or 512 and a shard width that is a multiple of 32 (at
     most 4096) runs the fused kernel; every other MLP the column and row
     GEMMs (the dispatch rule of tp_mlp_forward).  With the sequence-parallel
     entry side, the norm-and-gather kernel comes first."""
+    if backward:
+        return backward_launch_order(w)
     head = ["rmsnorm_gather"] if sp_entry else []
     if w.kind == "attn":
         return head + ["attn_qk_gemm", "attn_vt_gemm", "attn_core", "attn_out_gemm", "reduce_partials"]
@@ -148,7 +217,11 @@ def measured_traffic(kernel, workload_name):
     return None
 
 
-def write_traffic(w, share, pmc_dir, argv_line, sp_entry=False):
+def workload_tag(w, sp_entry=False, backward=False):
+    return w.name + ("_sp_entry" if sp_entry else "") + ("_backward" if backward else "")
+
+
+def write_traffic(w, share, pmc_dir, argv_line, sp_entry=False, backward=False):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
     WRITE_SIZE, each with --calib-copy) into profiles/traffic_<workload>.txt.
 
@@ -158,8 +231,8 @@ def write_traffic(w, share, pmc_dir, argv_line, sp_entry=False):
     import csv
     import collections
 
-    order = launch_order(w, sp_entry)
-    name = w.name + ("_sp_entry" if sp_entry else "")
+    order = launch_order(w, sp_entry, backward)
+    name = workload_tag(w, sp_entry, backward)
     per = {}
     factor = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -183,14 +256,15 @@ def write_traffic(w, share, pmc_dir, argv_line, sp_entry=False):
         "# Commands (from /tmp on the GPU host, REPO = repository root):",
         f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d DIR/FETCH_SIZE -o run -- python3 $REPO/bench.py {argv_line}",
         f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d DIR/WRITE_SIZE -o run -- python3 $REPO/bench.py {argv_line}",
-        f"#   python3 $REPO/bench.py --config {w.key} --share {share}{' --sp-entry' if sp_entry else ''} --traffic-from DIR",
+        f"#   python3 $REPO/bench.py --config {w.key} --share {share}{' --sp-entry' if sp_entry else ''}"
+        f"{' --backward' if backward else ''} --traffic-from DIR",
         "#",
         f"# Calibration (1 GiB device copy): FETCH_SIZE x {factor['FETCH_SIZE']:.4f}, WRITE_SIZE x {factor['WRITE_SIZE']:.4f}",
         "#",
         "# kernel                 FETCH_KiB      WRITE_KiB      read_bytes      write_bytes     total_bytes",
     ]
     out = {}
-    for k in order:
+    for k in dict.fromkeys(order):
         if k not in per["FETCH_SIZE"]:
             continue
         rb = per["FETCH_SIZE"][k] * 1024.0 * factor["FETCH_SIZE"]
@@ -242,6 +316,35 @@ def cpu_baseline(w, host, seconds):
                       f"({done / w.T:.2f} passes), fp64 numpy/scipy, {el:.1f} s"}
 
 
+def cpu_baseline_backward(w, host, dY, seconds):
+    """fp64 oracle backward on seeded blocks of token rows of the same
+    workload (the weight gradients over those rows only); TFLOP/s counted
+    with the same algorithmic FLOP per row as the GPU figure."""
+    import numpy as np
+
+    from oracle import reference as R
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    chunk = 256
+    order = np.random.default_rng(w.seed + 97).permutation(w.T)
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        start = done % w.T
+        rows = np.sort(order[start:start + chunk])
+        R.mlp_gelu_backward(host["X"][rows], host["A"], host["a"], host["B"], dY[rows])
+        flops += len(rows) * backward_flops(w, w.N) / w.T
+        done += len(rows)
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"backward over {done} token rows in blocks of {chunk}, seeded order over the workload's "
+                      f"{w.T} ({done / w.T:.2f} passes), fp64 numpy/scipy, {el:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +358,9 @@ def main():
     ap.add_argument("--sp-entry", action="store_true",
                     help="MLP workloads with a reduce-scatter: start each step with the sequence-parallel entry "
                          "side (RMSNorm of every sequence slice into the gathered input, the all-gather stand-in)")
+    ap.add_argument("--backward", action="store_true",
+                    help="GELU MLP workloads (2, 5): time the backward of the pair instead (input, weight and "
+                         "bias gradients of every shard, then the input-gradient reduction)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -268,9 +374,9 @@ def main():
         from tensor_transformer_layers_amd import configs
 
         w = configs.CONFIGS[args.config]
-        argv = (f"--config {args.config} --share {args.share}{' --sp-entry' if args.sp_entry else ''} "
-                "--steps 3 --warmup 1 --no-cpu-baseline --calib-copy")
-        print(write_traffic(w, args.share, args.traffic_from, argv, args.sp_entry))
+        argv = (f"--config {args.config} --share {args.share}{' --sp-entry' if args.sp_entry else ''}"
+                f"{' --backward' if args.backward else ''} --steps 3 --warmup 1 --no-cpu-baseline --calib-copy")
+        print(write_traffic(w, args.share, args.traffic_from, argv, args.sp_entry, args.backward))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -290,9 +396,16 @@ def main():
         print("bench.py: --sp-entry needs an MLP workload with a reduce-scatter (--config 5) and --share layer",
               file=sys.stderr, flush=True)
         sys.exit(2)
+    if args.backward and (w.kind != "mlp_gelu" or w.dtype != "bf16" or args.share != "layer" or args.sp_entry):
+        print("bench.py: --backward needs a bf16 GELU MLP workload (--config 2 or 5) and --share layer",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
     log(f"workload {w.name}: generating seeded inputs")
     host = inputs.make_inputs(w)
     d = workloads.device_inputs(w, host)
+    if args.backward:
+        dY_host = inputs.grad_output(w)
+        dY = workloads.to_device(dY_host, d["X"].dtype)
     if args.sp_entry:
         # X holds the n_slices sequence slices of the sublayer input; each step
         # normalizes them into Xn, the gathered input of the column GEMM
@@ -300,7 +413,11 @@ def main():
         x_slices = d["X"]
         d = dict(d, X=torch.empty_like(x_slices))
         tp.rmsnorm_gather(x_slices, gain, inputs.NORM_EPS, w.n_slices, out=d["X"])
-    Y, ws = workloads.forward(w, d)  # allocates Y and the workspace once
+    if args.backward:
+        grads, ws = workloads.backward(w, d, dY)  # allocates the gradients and the workspace once
+        Y = grads["dX"]
+    else:
+        Y, ws = workloads.forward(w, d)  # allocates Y and the workspace once
     torch.cuda.synchronize()
     rank_slice = 0 if w.n_slices > 1 else -1
     Yr = None
@@ -310,6 +427,9 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
+        if args.backward:
+            workloads.backward(w, d, dY, grads=grads, ws=ws, stream=stream)
+            return
         if args.sp_entry:
             tp.rmsnorm_gather(x_slices, gain, inputs.NORM_EPS, w.n_slices, out=d["X"], stream=stream)
         if args.share == "layer":
@@ -376,6 +496,8 @@ def main():
     flops = w.flops_layer() if args.share == "layer" else w.flops_shard()
     if args.sp_entry:
         flops += kernel_work(w, "rmsnorm_gather", 1, 0)[0]
+    if args.backward:
+        flops = backward_flops(w, w.N)
     value = flops / (ms_step / 1e3) / 1e12
 
     kernels = {}
@@ -393,10 +515,10 @@ def main():
     roof["kernel"] = dom
     roof["avg_us"] = round(avg * 1e6, 2)
     roof["algorithmic"] = {"flop": f, "bytes": b}
-    roof["traffic"] = measured_traffic(dom, w.name + ("_sp_entry" if args.sp_entry else ""))
+    roof["traffic"] = measured_traffic(dom, workload_tag(w, args.sp_entry, args.backward))
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if args.backward else METRIC,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -415,6 +537,9 @@ def main():
             "reduce_scatter_slices": w.n_slices, "seed": w.seed,
             **({"sp_entry": {"norm": "rmsnorm", "eps": inputs.NORM_EPS, "gain": inputs.NORM_GAIN_RECIPE}}
                if args.sp_entry else {}),
+            **({"pass": "backward", "upstream_gradient": inputs.GRAD_RECIPE,
+                "flop_counted": "8*T*H*F (dH, dX, dA, dB); the recomputed column product is extra and not counted",
+                "split_k": backward_splits(w.T, w.F, w.H)} if args.backward else {}),
         },
         "pct_of_bf16_mfma_peak": round(100 * value * 1e12 / PEAK_BF16, 2) if w.dtype == "bf16" else None,
         "roofline": roof,
@@ -424,9 +549,14 @@ def main():
     }
     if not args.no_cpu_baseline:
         del d, Y, ws
+        if args.backward:
+            del grads, dY
         torch.cuda.empty_cache()
         log(f"cpu baseline: fp64 oracle for ~{args.cpu_seconds:.0f} s")
-        out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
+        if args.backward:
+            out["cpu_baseline"] = cpu_baseline_backward(w, host, dY_host, args.cpu_seconds)
+        else:
+            out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -192,6 +192,50 @@ tp_status tp_mlp_forward(void* stream, const tp_mlp_desc* d, void* ws, size_t ws
 tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t ws_bytes);
 
 /*
+ * Backward of the MLP pair over shards [shard_begin, shard_begin + shard_count)
+ * (bf16, activation GELU or NONE), given the forward's input X, its weights and
+ * the gradient dY of its output.  Per shard i, with no exchange:
+ *   Z_i  = X A_i^T + a_i            (recomputed: the forward keeps no
+ *                                    intermediate -- activation recomputation,
+ *                                    2kiu.com blog post, section 5.3)
+ *   dZ_i = (dY B_i) * act'(Z_i)     (dY reaches every shard whole)
+ *   dA_i = dZ_i^T X,  da_i = column sums of dZ_i
+ *   dB_i = dY^T act(Z_i),           the shard's columns of dB
+ *   dX_i = dZ_i A_i                 (a partial: X was replicated)
+ * then, when the range covers all N shards, dX = ((dX_0 + dX_1) + ...) in
+ * shard order, one RNE cast: the all-reduce of the column layer's backward
+ * ("大模型分布式训练篇——从零实现 Tensor Para...", section 4: identity forward,
+ * all-reduce backward; blog post, section 4.1).  db = column sums of dY, once
+ * (the row bias enters once: listing of "Tensor Parallelism基础").
+ * Storage order as in the forward: A [F x H], B [H x F] (out-in); gradients
+ * come back in the same layout.  Weight and bias gradients are fp32.
+ * Z_i and dZ_i are rounded to bf16 once (as a bf16 forward would store its
+ * linear outputs), act(Z_i) is evaluated from the rounded Z_i.
+ */
+typedef struct {
+  tp_dtype dt;     /* TP_BF16                                                   */
+  tp_act act;      /* TP_ACT_GELU or TP_ACT_NONE                                */
+  int64_t T, H, F; /* T, H, F/N multiples of 8                                  */
+  int N, shard_begin, shard_count;
+  const void* X;   /* [T x H] bf16                                              */
+  const void* A;   /* [F x H] bf16                                              */
+  const void* a;   /* [F] bf16 or NULL                                          */
+  const void* B;   /* [H x F] bf16                                              */
+  const void* dY;  /* [T x H] bf16                                              */
+  void* dX;        /* [T x H] bf16, written when shard_count == N, else unused  */
+  float* dA;       /* [F x H]: rows of the shard range written                  */
+  float* da;       /* [F] (entries of the range) or NULL to skip                */
+  float* dB;       /* [H x F]: columns of the shard range written               */
+  float* db;       /* [H] or NULL to skip                                       */
+} tp_mlp_bwd_desc;
+
+/* Workspace bytes for tp_mlp_backward (0 when the descriptor is invalid).
+ * The fp32 dX partial slab comes first (slot i = shard i, each [T x H]): with
+ * shard_count < N the partials of the range stay there, as in the forward. */
+size_t tp_mlp_backward_workspace_size(const tp_mlp_bwd_desc* d);
+tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size_t ws_bytes);
+
+/*
  * Local causal attention alone (the middle step of tp_attn_forward), for
  * `heads` heads of width 128 over `batch` sequences of length `seq`:
  *   QK  [batch*seq x ldqk]: head h's query at columns h*128.., its key at

@@ -440,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
       const int c = lane & 15;
       const int n = n0 + wn * C::WN + 64 * h + 4 * c;
       float bias[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (C::EPI != EPI_PARTIAL) {
+      if constexpr (C::EPI != EPI_PARTIAL && C::EPI != EPI_GELU_BWD) {
         if (p.bias) {
           const bf16* bp = static_cast<const bf16*>(p.bias) + bz * p.sBias;
           for (int e = 0; e < 4; ++e) bias[e] = n + e < p.N ? static_cast<float>(bp[n + e]) : 0.0f;
@@ -461,10 +461,22 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
               for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = v[e];
           } else {
             bf16x4 o;
+            if constexpr (C::EPI == EPI_GELU_BWD) {
+              // dZ = dH * GELU'(Z) at the same (m, n); n is a multiple of 4
+              const bf16* zp = static_cast<const bf16*>(p.aux) + bz * p.sAux + (int64_t)m * p.ldaux + n;
+              bf16x4 z = {};
+              if (n + 3 < p.N)
+                z = *reinterpret_cast<const bf16x4*>(zp);
+              else
+                for (int e = 0; e < 4 && n + e < p.N; ++e) z[e] = zp[e];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float x = v[e] + bias[e];
-              o[e] = to_bf16(C::EPI == EPI_GELU ? gelu_bf16out(x) : x);
+              for (int e = 0; e < 4; ++e) o[e] = to_bf16(v[e] * gelu_grad(static_cast<float>(z[e])));
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float x = v[e] + bias[e];
+                o[e] = to_bf16(C::EPI == EPI_GELU ? gelu_bf16out(x) : x);
+              }
             }
             bf16* dst = static_cast<bf16*>(p.C) + off;
             if (n + 3 < p.N)
@@ -605,6 +617,7 @@ hipError_t launch_gemm_bf16(const GemmParams& p, Epilogue epi, hipStream_t s) {
     case EPI_GELU: return launch_bf16_epi<EPI_GELU>(p, s);
     case EPI_PARTIAL: return launch_bf16_epi<EPI_PARTIAL>(p, s);
     case EPI_SWIGLU: return launch_bf16_epi<EPI_SWIGLU>(p, s);
+    case EPI_GELU_BWD: return launch_bf16_epi<EPI_GELU_BWD>(p, s);
   }
   return hipErrorInvalidValue;
 }

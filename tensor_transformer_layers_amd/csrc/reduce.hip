@@ -31,7 +31,7 @@ __device__ __forceinline__ floatx4 ld_nt(const float* p) {
 
 constexpr int kU = 4;  // 16-byte stretches per thread per trip
 
-template <bool OUT_BF16, int NP>
+template <bool OUT_BF16, int NP, bool STRIDED = false>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceParams p, int64_t n4) {
   const int np = NP > 0 ? NP : p.n_parts;
   const float* const src0 = p.P + p.row0 * p.H;
@@ -76,13 +76,15 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceParams p, int64_
           acc[u] += *reinterpret_cast<const floatx4*>(static_cast<const float*>(p.bias) + c);
         }
       }
+      // output rows of width H at pitch ldy (the 4 outputs share a row)
+      const int64_t eo = STRIDED ? (e / p.H) * p.ldy + e % p.H : e;
       if constexpr (OUT_BF16) {
         bf16x4 o;
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = to_bf16(acc[u][j]);
-        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.Y) + e) = o;
+        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.Y) + eo) = o;
       } else {
-        *reinterpret_cast<floatx4*>(static_cast<float*>(p.Y) + e) = acc[u];
+        *reinterpret_cast<floatx4*>(static_cast<float*>(p.Y) + eo) = acc[u];
       }
     }
   }
@@ -98,6 +100,10 @@ hipError_t launch_typed(const ReduceParams& p, hipStream_t s) {
   const int64_t per_block = (int64_t)kThreads * kU;
   const int64_t blocks = std::min<int64_t>((n4 + per_block - 1) / per_block, int64_t(1) << 30);
   const dim3 g((unsigned)blocks), b(kThreads);
+  if (p.ldy != p.H) {  // pitched output rows (a block of a wider matrix)
+    launch_kernel((reduce_kernel<OUT_BF16, 0, true>), g, b, 0, s, p, n4);
+    return hipGetLastError();
+  }
   switch (p.n_parts) {
     case 1: launch_kernel((reduce_kernel<OUT_BF16, 1>), g, b, 0, s, p, n4); break;
     case 2: launch_kernel((reduce_kernel<OUT_BF16, 2>), g, b, 0, s, p, n4); break;

@@ -16,6 +16,8 @@
 
 namespace {
 
+typedef uint16_t bf16_t;  // bf16 storage on the host side (pointer arithmetic only)
+
 thread_local std::string g_err;
 
 tp_status fail(tp_status s, const char* fmt, ...) {
@@ -182,6 +184,7 @@ tp_status run_reduce(hipStream_t s, tp_dtype out_dt, int n_parts, int64_t T, int
   r.row0 = slice < 0 ? 0 : (int64_t)slice * (T / n_slices);
   r.bias = bias;
   r.Y = Y;
+  r.ldy = H;
   KernelTimer kt("reduce_partials", s);
   const hipError_t e = tp::launch_reduce(r, out_dt == TP_BF16, s);
   kt.stop();
@@ -355,6 +358,87 @@ tp_status validate_attn(const tp_attn_desc* d, AttnShape* sh) {
   sh->vt_off = sh->qk_off + align256(c * T * 2 * hd * 2);
   sh->o_off = sh->vt_off + align256(c * hd * T * 2);
   sh->total = sh->o_off + align256(c * T * hd * 2);
+  return TP_OK;
+}
+
+// ------------------------------------------------------- MLP backward desc
+// Workspace (256-byte aligned pieces, bf16 unless noted), Fc = shard_count*Fs:
+//   P    N x [T x H] fp32   dX partials, slot i = shard i
+//   Z    [T x Fc] (ld zld)  recomputed pre-activation
+//   dZ   [T x Fc] (ld zld)
+//   XT, dYT [H x T];  HT, dZT [Fc x T];  AT [H x Fc];  BT [Fc x H]
+//   K    S x [Fc x H] fp32  split-K partials of the weight gradients
+struct BwdShape {
+  int64_t Fs, Fc, zld;
+  int splits;  // split-K factor of the token-axis contractions
+  size_t p_bytes, z_off, dz_off, xt_off, dyt_off, ht_off, dzt_off, at_off, bt_off, k_off, total;
+};
+
+// Weight gradients contract over all T tokens into a small [Fc x H] output
+// when the hidden size is narrow.  Split the token axis so that the launch
+// has at least ~2 workgroups per CU; each split's K stays a multiple of 8.
+int bwd_splits(int64_t T, int64_t Fc, int64_t H) {
+  const int64_t big = ((Fc + 255) / 256) * ((H + 255) / 256);
+  const int64_t tiles = big >= 256 ? big : ((Fc + 127) / 128) * ((H + 127) / 128);
+  int s = 1;
+  while (s < 16 && tiles * s < 512 && T / (2 * s) >= 512) s *= 2;
+  while (s > 1 && T % (8 * s)) s /= 2;
+  return s;
+}
+
+tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
+  if (!d) return fail(TP_ERR_NULL, "descriptor is NULL");
+  TP_TRY(check_dtype(d->dt));
+  if (d->dt != TP_BF16) return fail(TP_ERR_DTYPE, "backward path is bf16-only");
+  if (d->act != TP_ACT_GELU && d->act != TP_ACT_NONE)
+    return fail(TP_ERR_DTYPE, "backward activation %d: only GELU and NONE are built", (int)d->act);
+  if (d->T < 0 || d->H <= 0 || d->F <= 0 || d->N <= 0)
+    return fail(TP_ERR_SHAPE, "T=%lld H=%lld F=%lld N=%d", (long long)d->T, (long long)d->H, (long long)d->F,
+                d->N);
+  if (d->F % d->N)
+    return fail(TP_ERR_DIVISIBILITY,
+                "intermediate F=%lld is not divisible by N=%d shards (shard would be %lld + %lld/%d columns)",
+                (long long)d->F, d->N, (long long)(d->F / d->N), (long long)(d->F % d->N), d->N);
+  if (d->shard_begin < 0 || d->shard_count < 1 || d->shard_begin + d->shard_count > d->N)
+    return fail(TP_ERR_SHAPE, "shard range [%d, %d) outside [0, %d)", d->shard_begin,
+                d->shard_begin + d->shard_count, d->N);
+  const int64_t Fs = d->F / d->N, Fc = Fs * d->shard_count;
+  *sh = BwdShape{};
+  sh->Fs = Fs;
+  sh->Fc = Fc;
+  sh->zld = Fc;
+  sh->splits = 1;
+  if (d->T == 0) return TP_OK;  // empty input: nothing to read, write or stage
+  if (d->T % 8) return fail(TP_ERR_ALIGN, "T=%lld is not a multiple of 8", (long long)d->T);
+  if (d->H % 8) return fail(TP_ERR_ALIGN, "hidden H=%lld is not a multiple of 8", (long long)d->H);
+  if (Fs % 8) return fail(TP_ERR_ALIGN, "shard width F/N=%lld is not a multiple of 8", (long long)Fs);
+  TP_TRY(check_matrix("X", d->X, d->T, d->H, d->H, 8));
+  TP_TRY(check_matrix("A", d->A, d->F, d->H, d->H, 8));
+  TP_TRY(check_matrix("B", d->B, d->H, d->F, d->F, 8));
+  TP_TRY(check_matrix("dY", d->dY, d->T, d->H, d->H, 8));
+  TP_TRY(check_matrix("dA", d->dA, d->F, d->H, d->H, 4));
+  TP_TRY(check_matrix("dB", d->dB, d->H, d->F, d->F, 4));
+  if (d->a && !aligned16(d->a)) return fail(TP_ERR_ALIGN, "a is not 16-byte aligned");
+  if (d->da && !aligned16(d->da)) return fail(TP_ERR_ALIGN, "da is not 16-byte aligned");
+  if (d->db && !aligned16(d->db)) return fail(TP_ERR_ALIGN, "db is not 16-byte aligned");
+  if (d->shard_count == d->N) {
+    if (!d->dX) return fail(TP_ERR_NULL, "dX is NULL");
+    if (!aligned16(d->dX)) return fail(TP_ERR_ALIGN, "dX is not 16-byte aligned");
+  }
+  if (d->T > kIntMax || d->F > kIntMax) return fail(TP_ERR_SHAPE, "size exceeds 2^31-1");
+  const size_t T = (size_t)d->T, H = (size_t)d->H, fc = (size_t)Fc;
+  sh->splits = bwd_splits(d->T, Fc, d->H);
+  sh->p_bytes = align256((size_t)d->N * T * H * sizeof(float));
+  sh->z_off = sh->p_bytes;
+  sh->dz_off = sh->z_off + align256(T * fc * 2);
+  sh->xt_off = sh->dz_off + align256(T * fc * 2);
+  sh->dyt_off = sh->xt_off + align256(H * T * 2);
+  sh->ht_off = sh->dyt_off + align256(H * T * 2);
+  sh->dzt_off = sh->ht_off + align256(fc * T * 2);
+  sh->at_off = sh->dzt_off + align256(fc * T * 2);
+  sh->bt_off = sh->at_off + align256(H * fc * 2);
+  sh->k_off = sh->bt_off + align256(fc * H * 2);
+  sh->total = sh->k_off + (sh->splits > 1 ? align256((size_t)sh->splits * fc * H * sizeof(float)) : 0);
   return TP_OK;
 }
 
@@ -552,6 +636,115 @@ tp_status tp_mlp_forward(void* stream, const tp_mlp_desc* d, void* ws, size_t ws
 
   if (c < d->N) return ok();
   return run_reduce(s, d->dt, d->N, T, H, P, T * H, d->b, d->Y, d->n_slices, d->slice);
+}
+
+size_t tp_mlp_backward_workspace_size(const tp_mlp_bwd_desc* d) {
+  BwdShape sh;
+  return validate_mlp_bwd(d, &sh) == TP_OK ? sh.total : 0;
+}
+
+tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size_t ws_bytes) {
+  BwdShape sh;
+  TP_TRY(validate_mlp_bwd(d, &sh));
+  if (d->T == 0) return ok();
+  TP_TRY(check_ws(ws, ws_bytes, sh.total));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t T = d->T, H = d->H, F = d->F, Fs = sh.Fs, Fc = sh.Fc;
+  const int c = d->shard_count, i0 = d->shard_begin, S = sh.splits;
+  const bool gelu = d->act == TP_ACT_GELU;
+  if (log_enabled())
+    fprintf(stderr, "[tp] mlp backward bf16 act=%d N=%d shards [%d,%d): T=%lld H=%lld Fs=%lld, split-K %d%s\n",
+            (int)d->act, d->N, i0, i0 + c, (long long)T, (long long)H, (long long)Fs, S,
+            c == d->N ? " ; reduce dX" : "");
+  char* base = static_cast<char*>(ws);
+  float* P = reinterpret_cast<float*>(base);
+  bf16_t* Z = reinterpret_cast<bf16_t*>(base + sh.z_off);
+  bf16_t* dZ = reinterpret_cast<bf16_t*>(base + sh.dz_off);
+  bf16_t* XT = reinterpret_cast<bf16_t*>(base + sh.xt_off);
+  bf16_t* dYT = reinterpret_cast<bf16_t*>(base + sh.dyt_off);
+  bf16_t* HT = reinterpret_cast<bf16_t*>(base + sh.ht_off);
+  bf16_t* dZT = reinterpret_cast<bf16_t*>(base + sh.dzt_off);
+  bf16_t* AT = reinterpret_cast<bf16_t*>(base + sh.at_off);
+  bf16_t* BT = reinterpret_cast<bf16_t*>(base + sh.bt_off);
+  float* K = reinterpret_cast<float*>(base + sh.k_off);
+  const bf16_t* A_r = static_cast<const bf16_t*>(d->A) + (size_t)i0 * Fs * H;  // range rows of A
+  const bf16_t* B_r = static_cast<const bf16_t*>(d->B) + (size_t)i0 * Fs;      // range columns of B
+  const bf16_t* a_r = d->a ? static_cast<const bf16_t*>(d->a) + (size_t)i0 * Fs : nullptr;
+
+  auto transpose = [&](const char* name, const void* in, int64_t ld_in, void* out, int64_t ld_out, int64_t R,
+                       int64_t C, bool act) -> tp_status {
+    tp::TransposeParams t{in, ld_in, out, ld_out, R, C};
+    KernelTimer kt(name, s);
+    const hipError_t e = tp::launch_transpose(t, act, s);
+    kt.stop();
+    return hip_status(e, name);
+  };
+  auto rowsum = [&](const char* name, const void* in, int64_t ld, float* out, int64_t R, int64_t C) -> tp_status {
+    tp::RowSumParams r{in, ld, out, R, C};
+    KernelTimer kt(name, s);
+    const hipError_t e = tp::launch_rowsum(r, s);
+    kt.stop();
+    return hip_status(e, name);
+  };
+  // C[M x N] (+)= A[M x T] B[N x T]^T over the token axis, split-K when the
+  // output is small; the splits' partials fold in split order.
+  auto token_gemm = [&](const char* name, const void* Aop, const void* Bop, int64_t M, int64_t N, float* C,
+                        int64_t ldc) -> tp_status {
+    if (S == 1) {
+      const tp::GemmParams g = gemm(Aop, T, 0, Bop, T, 0, C, ldc, 0, M, N, T, 1);
+      return hip_status(launch(name, TP_BF16, g, tp::EPI_PARTIAL, s), name);
+    }
+    const int64_t kc = T / S;
+    const tp::GemmParams g = gemm(Aop, T, kc, Bop, T, kc, K, N, M * N, M, N, kc, S);
+    TP_TRY(hip_status(launch(name, TP_BF16, g, tp::EPI_PARTIAL, s), name));
+    tp::ReduceParams r{};
+    r.P = K;
+    r.part_stride = M * N;
+    r.n_parts = S;
+    r.rows = M;
+    r.H = N;
+    r.row0 = 0;
+    r.bias = nullptr;
+    r.Y = C;
+    r.ldy = ldc;
+    KernelTimer kt("bwd_splitk_reduce", s);
+    const hipError_t e = tp::launch_reduce(r, false, s);
+    kt.stop();
+    return hip_status(e, "bwd_splitk_reduce");
+  };
+
+  // operands contiguous along each contraction
+  TP_TRY(transpose("bwd_transpose", d->X, H, XT, T, T, H, false));    // XT  [H x T]
+  TP_TRY(transpose("bwd_transpose", d->dY, H, dYT, T, T, H, false));  // dYT [H x T]
+  TP_TRY(transpose("bwd_transpose", A_r, H, AT, Fc, Fc, H, false));   // AT  [H x Fc]
+  TP_TRY(transpose("bwd_transpose", B_r, F, BT, H, H, Fc, false));    // BT  [Fc x H]
+
+  // Z = X A_r^T + a_r, the range's pre-activation (all shards side by side)
+  tp::GemmParams zg = gemm(d->X, H, 0, A_r, H, 0, Z, sh.zld, 0, T, Fc, H, 1);
+  zg.bias = a_r;
+  TP_TRY(hip_status(launch("bwd_recompute_gemm", TP_BF16, zg, tp::EPI_STORE, s), "bwd_recompute_gemm"));
+  // dZ = (dY B_r) * act'(Z)
+  tp::GemmParams dg = gemm(d->dY, H, 0, BT, H, 0, dZ, sh.zld, 0, T, Fc, H, 1);
+  dg.aux = Z;
+  dg.ldaux = sh.zld;
+  TP_TRY(hip_status(launch("bwd_dz_gemm", TP_BF16, dg, gelu ? tp::EPI_GELU_BWD : tp::EPI_STORE, s), "bwd_dz_gemm"));
+  // HT = act(Z)^T, dZT = dZ^T
+  TP_TRY(transpose("bwd_transpose", Z, sh.zld, HT, T, T, Fc, gelu));
+  TP_TRY(transpose("bwd_transpose", dZ, sh.zld, dZT, T, T, Fc, false));
+
+  // dX partial of each shard into its slab slot: dZ_i A_i (K = Fs)
+  const tp::GemmParams xg = gemm(dZ, sh.zld, Fs, AT, Fc, Fs, P + (size_t)i0 * T * H, H, T * H, T, H, Fs, c);
+  TP_TRY(hip_status(launch("bwd_dx_gemm", TP_BF16, xg, tp::EPI_PARTIAL, s), "bwd_dx_gemm"));
+  // dA rows of the range: dZ^T X  (M = Fc, N = H, contraction over T)
+  TP_TRY(token_gemm("bwd_da_gemm", dZT, XT, Fc, H, d->dA + (size_t)i0 * Fs * H, H));
+  // dB columns of the range: dY^T act(Z)  (M = H, N = Fc)
+  TP_TRY(token_gemm("bwd_db_gemm", dYT, HT, H, Fc, d->dB + (size_t)i0 * Fs, F));
+  // bias gradients: column sums of dZ (range) and of dY (once)
+  if (d->da) TP_TRY(rowsum("bwd_bias_rowsum", dZT, T, d->da + (size_t)i0 * Fs, Fc, T));
+  if (d->db) TP_TRY(rowsum("bwd_bias_rowsum", dYT, T, d->db, H, T));
+
+  if (c < d->N) return ok();
+  return run_reduce(s, TP_BF16, d->N, T, H, P, T * H, nullptr, d->dX, 1, -1);
 }
 
 tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t ws_bytes) {

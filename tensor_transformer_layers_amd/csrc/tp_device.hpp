@@ -48,6 +48,12 @@ __device__ __forceinline__ float gelu_bf16out(float z) {
   return fmaxf(z, 0.0f) - fabsf(q);
 }
 
+// Slope of the exact GELU: d/dz [z Phi(z)] = Phi(z) + z phi(z), with
+// Phi(z) = (1 + erf(z / sqrt 2)) / 2 and phi(z) = e^(-z^2/2) / sqrt(2 pi).
+__device__ __forceinline__ float gelu_grad(float z) {
+  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) + z * 0.39894228040143268f * __expf(-0.5f * z * z);
+}
+
 // SiLU for bf16 outputs: g / (1 + e^-g) with the hardware exponential and
 // reciprocal (relative error ~1e-6, far below bf16 resolution).
 __device__ __forceinline__ float silu_bf16out(float g) {

@@ -31,12 +31,14 @@ enum Epilogue : int {
   EPI_GELU = 1,    // C = GELU(acc + bias)          out dtype = input dtype
   EPI_PARTIAL = 2, // C = acc                       out fp32 (row partial)
   EPI_SWIGLU = 3,  // C = SiLU(acc_gate) * acc_up   out bf16
+  EPI_GELU_BWD = 4,  // C = acc * GELU'(Z), Z = aux   out bf16 (bf16 path only)
 };
 
 // C[M x N] = A[M x K] * B[N x K]^T, batched over `batch` problems whose
 // pointers advance by sA/sB/sC/sBias elements.  Both operands are K-contiguous.
 // For EPI_SWIGLU, B holds gate rows at B and up rows at B + upOff; N is the
-// output width (gate rows used: N).
+// output width (gate rows used: N).  For EPI_GELU_BWD, aux is a bf16 matrix of
+// the output's shape (ld ldaux, advancing by sAux per problem).
 struct GemmParams {
   const void* A;
   int64_t lda, sA;
@@ -47,6 +49,8 @@ struct GemmParams {
   const void* bias;  // [N] per batch or nullptr
   int64_t sBias;
   int64_t upOff;
+  const void* aux;
+  int64_t ldaux, sAux;
   int M, N, K;
   int batch;
 };
@@ -79,6 +83,7 @@ bool mlp_fused_supported(int64_t H, int64_t Fs);
 hipError_t launch_mlp_fused(const FusedMlpParams& p, hipStream_t s);
 
 // Y[rows x H] = fold_k P[k][row0 + r, :] (+ bias), see tp_reduce_partials.
+// Output row r is written at Y + r*ldy (ldy == H: contiguous).
 struct ReduceParams {
   const float* P;
   int64_t part_stride;
@@ -86,6 +91,7 @@ struct ReduceParams {
   int64_t rows, H, row0;
   const void* bias;
   void* Y;
+  int64_t ldy;
 };
 hipError_t launch_reduce(const ReduceParams& p, bool out_bf16, hipStream_t s);
 
@@ -120,5 +126,28 @@ struct AttnParams {
   float scale_log2e;  // log2(e) / sqrt(head_dim)
 };
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
+
+
+// Layout kernels of the MLP pair's backward (bwd.hip), bf16 only.
+//   out[c][r] = op(in[r][c]) for in [R x C] (ld_in), out [C x R] (ld_out);
+//   op = identity, or GELU (the activation recomputed from a stored
+//   pre-activation, rounded to bf16).  R, C, ld_in, ld_out multiples of 8.
+struct TransposeParams {
+  const void* in;
+  int64_t ld_in;
+  void* out;
+  int64_t ld_out;
+  int64_t R, C;
+};
+hipError_t launch_transpose(const TransposeParams& p, bool gelu, hipStream_t s);
+
+//   out[r] = sum over c of in[r][c], fp32, in a fixed order.  C a multiple of 8.
+struct RowSumParams {
+  const void* in;
+  int64_t ld;
+  float* out;
+  int64_t R, C;
+};
+hipError_t launch_rowsum(const RowSumParams& p, hipStream_t s);
 
 }  // namespace tp

@@ -141,3 +141,14 @@ def norm_gain(w: Workload) -> np.ndarray:
     """The RMSNorm gain [H] of workload w (recipe above)."""
     g = np.float32(1.0) + draw(np.random.SeedSequence([w.seed, 1]), (w.H,), 0.1)
     return round_to_dtype(g.astype(np.float32), w.dtype)
+
+
+# Backward of the MLP pair: the upstream gradient dY [T x H] of the sublayer
+# output.  The pages fix no values for it: N(0, 1) per element, rounded to the
+# workload dtype, drawn from its own stream of the seed.
+GRAD_RECIPE = "N(0, 1) per element of dY [T x H], rounded to the workload dtype, SeedSequence([seed, 2])"
+
+
+def grad_output(w: Workload) -> np.ndarray:
+    """The upstream gradient dY [T x H] of workload w (recipe above)."""
+    return round_to_dtype(draw(np.random.SeedSequence([w.seed, 2]), (w.T, w.H), 1.0), w.dtype)

@@ -46,6 +46,16 @@ class AttnDesc(ctypes.Structure):
     ]
 
 
+class MlpBwdDesc(ctypes.Structure):
+    _fields_ = [
+        ("dt", _int), ("act", _int),
+        ("T", _i64), ("H", _i64), ("F", _i64),
+        ("N", _int), ("shard_begin", _int), ("shard_count", _int),
+        ("X", _vp), ("A", _vp), ("a", _vp), ("B", _vp), ("dY", _vp),
+        ("dX", _vp), ("dA", _vp), ("da", _vp), ("dB", _vp), ("db", _vp),
+    ]
+
+
 _SIGS = {
     "tp_column_linear": (_int, [_vp, _int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64]),
     "tp_row_linear_partial": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]),
@@ -58,6 +68,8 @@ _SIGS = {
     "tp_attn_partials_offset": (_sz, [ctypes.POINTER(AttnDesc)]),
     "tp_mlp_forward": (_int, [_vp, ctypes.POINTER(MlpDesc), _vp, _sz]),
     "tp_attn_forward": (_int, [_vp, ctypes.POINTER(AttnDesc), _vp, _sz]),
+    "tp_mlp_backward_workspace_size": (_sz, [ctypes.POINTER(MlpBwdDesc)]),
+    "tp_mlp_backward": (_int, [_vp, ctypes.POINTER(MlpBwdDesc), _vp, _sz]),
     "tp_attn_local": (_int, [_vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp, _i64]),
     "tp_timing_enable": (_int, [_int]),
     "tp_timing_read": (_int, [_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
@@ -129,6 +141,14 @@ def tp_mlp_forward(stream, desc: MlpDesc, ws, ws_bytes) -> int:
 
 def tp_attn_forward(stream, desc: AttnDesc, ws, ws_bytes) -> int:
     return lib().tp_attn_forward(stream, ctypes.byref(desc), ws, ws_bytes)
+
+
+def tp_mlp_backward(stream, desc: MlpBwdDesc, ws, ws_bytes) -> int:
+    return lib().tp_mlp_backward(stream, ctypes.byref(desc), ws, ws_bytes)
+
+
+def tp_mlp_backward_workspace_size(desc: MlpBwdDesc) -> int:
+    return lib().tp_mlp_backward_workspace_size(ctypes.byref(desc))
 
 
 def tp_attn_local(*args) -> int:
@@ -288,6 +308,41 @@ def mlp_forward(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, ws=None, shard_begin=
         ws = alloc_workspace(need, X.device)
     check(tp_mlp_forward(_stream(stream), d, _ptr(ws), ws.numel()))
     return Y, ws
+
+
+def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=None, grads=None, ws=None,
+                 need_da=True, need_db=True, stream=None):
+    """Backward of the MLP pair over a shard range; returns (grads, workspace).
+    ``grads`` holds dX (bf16 [T x H], filled when the range covers all N
+    shards), dA (fp32 [F x H]), da (fp32 [F] or None), dB (fp32 [H x F]) and
+    db (fp32 [H] or None); missing entries are allocated."""
+    torch = _torch()
+    T, H = X.shape
+    F = A.shape[0]
+    cnt = N if shard_count is None else shard_count
+    g = dict(grads or {})
+    dev = X.device
+    g.setdefault("dX", torch.empty((T, H), dtype=X.dtype, device=dev) if cnt == N else None)
+    g.setdefault("dA", torch.zeros((F, H), dtype=torch.float32, device=dev))
+    g.setdefault("da", torch.zeros((F,), dtype=torch.float32, device=dev) if need_da else None)
+    g.setdefault("dB", torch.zeros((H, F), dtype=torch.float32, device=dev))
+    g.setdefault("db", torch.zeros((H,), dtype=torch.float32, device=dev) if need_db else None)
+    d = MlpBwdDesc()
+    d.dt = _dt(X)
+    d.act = act
+    d.T, d.H, d.F = T, H, F
+    d.N, d.shard_begin, d.shard_count = N, shard_begin, cnt
+    d.X, d.A, d.a, d.B, d.dY = _ptr(X), _ptr(A), _ptr(a), _ptr(B), _ptr(dY)
+    d.dX, d.dA, d.da, d.dB, d.db = (_ptr(g[k]) for k in ("dX", "dA", "da", "dB", "db"))
+    need = tp_mlp_backward_workspace_size(d)
+    if need == 0:
+        if T == 0:
+            return g, ws
+        raise TPError(TP_ERR_SHAPE, last_error())
+    if ws is None or ws.numel() < need:
+        ws = alloc_workspace(need, dev)
+    check(tp_mlp_backward(_stream(stream), d, _ptr(ws), ws.numel()))
+    return g, ws
 
 
 def mlp_partials(ws, N, T, H):

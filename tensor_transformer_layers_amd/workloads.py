@@ -78,3 +78,12 @@ def reduce_slab(w: Workload, d: dict, ws, Y=None, slice=-1, stream=None):
     bias = d.get("b") if w.kind != "attn" else d.get("bo")
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     return tp.reduce_partials(P, bias, out_dtype=dt, n_slices=w.n_slices, slice=slice, out=Y, stream=stream)
+
+
+def backward(w: Workload, d: dict, dY, grads=None, ws=None, shard_begin=0, shard_count=None, stream=None):
+    """One backward pass of the GELU MLP sublayer over a shard range."""
+    if w.kind != "mlp_gelu":
+        raise ValueError(f"the backward is built for the GELU MLP only, not {w.kind}")
+    return tp.mlp_backward(d["X"], d["A"], d["a"], d["B"], dY, w.N, act=tp.TP_ACT_GELU,
+                           shard_begin=shard_begin, shard_count=shard_count, grads=grads, ws=ws,
+                           need_da=d["a"] is not None, need_db=d["b"] is not None, stream=stream)

@@ -201,3 +201,78 @@ def test_rmsnorm_gather_validation(L):
     assert call(ss=16 * 512 + 4) == tp.TP_ERR_ALIGN
     assert call(sl=4) == tp.TP_ERR_SHAPE
     assert call(Y=FAKE + 8) == tp.TP_ERR_ALIGN
+
+
+# ------------------------------------------------------------ MLP backward
+def _bwd(**kw):
+    d = tp.MlpBwdDesc()
+    d.dt, d.act = tp.TP_BF16, tp.TP_ACT_GELU
+    d.T, d.H, d.F, d.N = 256, 512, 2048, 4
+    d.shard_begin, d.shard_count = 0, 4
+    d.X = d.A = d.a = d.B = d.dY = d.dX = d.dA = d.da = d.dB = d.db = FAKE
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_mlp_backward_workspace_size_is_host_only(L):
+    T, H, F, N = 256, 512, 2048, 4
+    need = tp.tp_mlp_backward_workspace_size(_bwd())
+    # dX partial slab, Z and dZ, the transposes of X, dY, act(Z), dZ, A, B
+    base = N * T * H * 4 + 2 * T * F * 2 + 2 * H * T * 2 + 2 * F * T * 2 + 2 * H * F * 2
+    assert need >= base
+    extra = need - base  # split-K partials of the weight gradients
+    assert extra % (F * H * 4) == 0 and extra // (F * H * 4) in (0, 2, 4, 8, 16)
+    one = tp.tp_mlp_backward_workspace_size(_bwd(shard_count=1, shard_begin=3))
+    assert one < need
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(F=2050), tp.TP_ERR_DIVISIBILITY, "not divisible by N=4"),
+    (dict(T=260), tp.TP_ERR_ALIGN, "T=260 is not a multiple of 8"),
+    (dict(dt=tp.TP_F32), tp.TP_ERR_DTYPE, "bf16-only"),
+    (dict(act=tp.TP_ACT_SWIGLU), tp.TP_ERR_DTYPE, "only GELU and NONE"),
+    (dict(dY=None), tp.TP_ERR_NULL, "dY is NULL"),
+    (dict(dA=None), tp.TP_ERR_NULL, "dA is NULL"),
+    (dict(dX=None), tp.TP_ERR_NULL, "dX is NULL"),
+    (dict(dB=FAKE + 4), tp.TP_ERR_ALIGN, "dB is not 16-byte aligned"),
+    (dict(da=FAKE + 4), tp.TP_ERR_ALIGN, "da is not 16-byte aligned"),
+    (dict(shard_begin=3, shard_count=2), tp.TP_ERR_SHAPE, "shard range"),
+])
+def test_mlp_backward_rejects_before_launch(L, kw, status, needle):
+    d = _bwd(**kw)
+    assert tp.tp_mlp_backward_workspace_size(d) == 0
+    s = tp.tp_mlp_backward(None, d, FAKE, 1 << 40)
+    assert s == status, tp.last_error()
+    assert needle in tp.last_error()
+
+
+def test_mlp_backward_partial_range_needs_no_dx(L):
+    d = _bwd(dX=None, shard_begin=1, shard_count=2)
+    assert tp.tp_mlp_backward_workspace_size(d) > 0
+
+
+def test_mlp_backward_small_workspace_and_empty_input(L):
+    d = _bwd()
+    need = tp.tp_mlp_backward_workspace_size(d)
+    assert tp.tp_mlp_backward(None, d, FAKE, need - 1) == tp.TP_ERR_WORKSPACE
+    assert tp.tp_mlp_backward(None, _bwd(T=0), None, 0) == tp.TP_OK
+
+
+@pytest.mark.parametrize("T,H,F,N,c", [
+    (16384, 512, 2048, 4, 4), (16384, 512, 2048, 4, 1), (16384, 12288, 49152, 8, 8),
+    (2048, 520, 320, 8, 8), (4096, 256, 1024, 4, 4), (264, 136, 288, 4, 4), (1000, 64, 128, 2, 2),
+])
+def test_bench_split_rule_matches_library(L, T, H, F, N, c):
+    """bench.py's copy of the backward's split-K rule (used to name kernels
+    in profiler output) agrees with the library's, read off the workspace."""
+    import bench
+
+    d = _bwd(T=T, H=H, F=F, N=N, shard_count=c)
+    Fc = F // N * c
+    align = lambda x: (x + 255) // 256 * 256
+    base = align(N * T * H * 4) + 2 * align(T * Fc * 2) + 2 * align(H * T * 2) + 2 * align(Fc * T * 2) \
+        + 2 * align(H * Fc * 2)
+    extra = tp.tp_mlp_backward_workspace_size(d) - base
+    S = bench.backward_splits(T, Fc, H)
+    assert extra == (align(S * Fc * H * 4) if S > 1 else 0)

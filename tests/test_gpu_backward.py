@@ -1,0 +1,172 @@
+"""Backward of the MLP pair: HIP path vs the fp64 CPU oracle, through the C ABI
+(gfx950 GPU required).
+
+Every gradient (dX, dA, da, dB, db) is held to the bf16 bound of the forward,
+max|G - O| / max|O| <= 2e-2 over the compared entries, and must be
+bit-identical run to run (no atomics; fixed-order folds).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import reference as R
+from oracle import tp_oracle as O
+from tensor_transformer_layers_amd import configs, inputs, tp, workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+DEV = "cuda"
+BF16_TOL = 2e-2
+KEYS = ("dX", "dA", "da", "dB", "db")
+
+
+def say(msg):
+    print(f"[gpu-test] {msg}", file=sys.stderr, flush=True)
+
+
+def dev(x, dtype=torch.bfloat16):
+    return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(DEV, dtype)
+
+
+def err(y, ref):
+    y = np.asarray(y, dtype=np.float64)
+    return float(np.max(np.abs(y - ref)) / np.max(np.abs(ref)))
+
+
+def _host(T, H, F, bias, seed):
+    rng = np.random.default_rng(seed)
+    r = lambda shape, s: inputs.round_to_dtype((rng.standard_normal(shape) * s).astype(np.float32), "bf16")
+    return {"X": r((T, H), 1.0), "A": r((F, H), 0.05), "a": r((F,), 0.05) if bias else None,
+            "B": r((H, F), 0.05), "dY": r((T, H), 1.0)}
+
+
+def _run(h, N, act=tp.TP_ACT_GELU, shard_begin=0, shard_count=None):
+    X, A, a, B, dY = (dev(h[k]) for k in ("X", "A", "a", "B", "dY"))
+    g, ws = tp.mlp_backward(X, A, a, B, dY, N, act=act, shard_begin=shard_begin, shard_count=shard_count,
+                            need_da=a is not None)
+    torch.cuda.synchronize()
+    return g, ws
+
+
+def _np(t):
+    return t.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("T,H,F,N,act,bias", [
+    (264, 136, 4 * 72, 4, tp.TP_ACT_GELU, True),     # ragged tiles in every dimension
+    (64, 64, 2 * 64, 2, tp.TP_ACT_NONE, False),
+    (2048, 520, 8 * 40, 8, tp.TP_ACT_GELU, True),    # split-K weight gradients (2 splits)
+    (4096, 256, 4 * 256, 4, tp.TP_ACT_GELU, False),
+    (8, 8, 8, 1, tp.TP_ACT_GELU, True),              # one shard, smallest sizes
+])
+def test_backward_vs_oracle(T, H, F, N, act, bias):
+    say(f"mlp_backward T={T} H={H} F={F} N={N} act={act} bias={bias}")
+    h = _host(T, H, F, bias, seed=T + H + F + N)
+    g, _ = _run(h, N, act)
+    g2, _ = _run(h, N, act)
+    ref = R.mlp_gelu_backward(h["X"], h["A"], h["a"], h["B"], h["dY"],
+                              act="gelu" if act == tp.TP_ACT_GELU else "none")
+    for k in KEYS:
+        if k == "da" and not bias:
+            assert g["da"] is None
+            continue
+        e = err(_np(g[k]), ref[k])
+        say(f"  {k}: err={e:.3e}")
+        assert e <= BF16_TOL, k
+        assert torch.equal(g[k], g2[k]), f"{k} not bit-identical run to run"
+
+
+def test_one_shard_range_matches_oracle_shard():
+    """A one-shard range writes only that shard's rows of dA, columns of dB and
+    entries of da, and leaves its dX partial in its slab slot."""
+    T, H, F, N, r = 520, 264, 4 * 96, 4, 2
+    say(f"mlp_backward one shard r={r} of N={N}")
+    h = _host(T, H, F, True, seed=77)
+    g, ws = _run(h, N, shard_begin=r, shard_count=1)
+    assert g["dX"] is None
+    sh = O.mlp_backward_sharded(h["X"], h["A"].T, h["a"], h["B"].T, h["dY"], N)
+    Fs = F // N
+    sl = slice(r * Fs, (r + 1) * Fs)
+    dA, da, dB = _np(g["dA"]), _np(g["da"]), _np(g["dB"])
+    assert err(dA[sl], sh["dA"][:, sl].T) <= BF16_TOL
+    assert err(da[sl], sh["da"][sl]) <= BF16_TOL
+    assert err(dB[:, sl], sh["dB"][sl].T) <= BF16_TOL
+    assert err(_np(g["db"]), sh["db"]) <= BF16_TOL
+    outside = np.ones(F, dtype=bool)
+    outside[sl] = False
+    assert not dA[outside].any() and not da[outside].any() and not dB[:, outside].any()
+    P = tp.mlp_partials(ws, N, T, H)[r]
+    assert err(_np(P), sh["dX_parts"][r]) <= BF16_TOL
+
+
+def test_shard_ranges_compose_to_full_run():
+    """Two half ranges plus the reduction over the slab give the full run's
+    bits (each shard's work does not depend on which range launched it)."""
+    T, H, F, N = 256, 128, 4 * 64, 4
+    h = _host(T, H, F, True, seed=78)
+    full, _ = _run(h, N)
+    X, A, a, B, dY = (dev(h[k]) for k in ("X", "A", "a", "B", "dY"))
+    g, ws = tp.mlp_backward(X, A, a, B, dY, N, shard_begin=0, shard_count=2)
+    g, ws = tp.mlp_backward(X, A, a, B, dY, N, shard_begin=2, shard_count=2, grads=g, ws=ws)
+    dX = tp.reduce_partials(tp.mlp_partials(ws, N, T, H), None, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(dX.view(torch.int16), full["dX"].view(torch.int16))
+    for k in ("dA", "da", "dB", "db"):
+        assert torch.equal(g[k], full[k]), k
+
+
+def test_zero_upstream_gradient_gives_zero_gradients():
+    T, H, F, N = 128, 64, 2 * 64, 2
+    h = _host(T, H, F, True, seed=79)
+    h["dY"] = np.zeros_like(h["dY"])
+    g, _ = _run(h, N)
+    for k in KEYS:
+        assert not g[k].float().abs().sum().item(), k
+
+
+def test_empty_tokens_is_noop():
+    h = _host(8, 64, 128, True, seed=80)
+    X = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    g, ws = tp.mlp_backward(X, dev(h["A"]), dev(h["a"]), dev(h["B"]), torch.empty_like(X), 2)
+    torch.cuda.synchronize()
+    assert ws is None and g["dX"].shape == (0, 64)
+    assert not g["dA"].any() and not g["dB"].any()
+
+
+@pytest.mark.parametrize("k", [2, 5])
+def test_backward_full_size(k):
+    """The GELU workloads at full size: all of workload 2 against the full
+    oracle; workload 5 on sampled token rows (dX) and features (dA, da, dB)
+    plus the whole db."""
+    w = configs.CONFIGS[k]
+    say(f"backward config {k} {w.name}: generating inputs")
+    host = inputs.make_inputs(w)
+    dY_h = inputs.grad_output(w)
+    d = workloads.device_inputs(w, host)
+    dY = dev(dY_h)
+    say(f"backward config {k}: all {w.N} shards")
+    g, ws = workloads.backward(w, d, dY)
+    torch.cuda.synchronize()
+    del ws
+    if k == 2:
+        say("backward config 2: full oracle")
+        ref = R.mlp_gelu_backward(host["X"], host["A"], host["a"], host["B"], dY_h)
+        got = {key: _np(g[key]) for key in KEYS}
+    else:
+        rows = inputs.sample_rows(w.T, 32, w.seed, [0, w.T - 1])
+        feats = inputs.sample_rows(w.F, 16, w.seed + 1, [0, w.F - 1])
+        say(f"backward config {k}: oracle on {len(rows)} rows and {len(feats)} features")
+        ref = R.mlp_gelu_backward_sample(host["X"], host["A"], host["a"], host["B"], dY_h, rows, feats)
+        ri = torch.from_numpy(rows).to(DEV)
+        fi = torch.from_numpy(feats).to(DEV)
+        got = {"dX": _np(g["dX"][ri]), "dA": _np(g["dA"][fi]), "da": _np(g["da"][fi]),
+               "dB": _np(g["dB"][:, fi]), "db": _np(g["db"])}
+    for key in KEYS:
+        e = err(got[key], ref[key])
+        say(f"backward config {k}: {key} err={e:.3e}")
+        assert e <= BF16_TOL, key
