@@ -76,13 +76,20 @@ def kernel_work(w, name, shards_per_launch, rows_reduced):
 
 def backward_splits(T, Fc, H):
     """Split-K factor of the backward's token-axis GEMMs (the rule of
-    tp_mlp_backward: at least ~2 workgroups per CU, K per split >= 512 and a
+    tp_mlp_backward: fill the chip with 256x256 tiles when up to 16 splits
+    get there, else with 128x128 tiles at ~2 per CU; K per split >= 512 and a
     multiple of 8)."""
     big = ((Fc + 255) // 256) * ((H + 255) // 256)
-    tiles = big if big >= 256 else ((Fc + 127) // 128) * ((H + 127) // 128)
+    if big >= 256:
+        return 1
     s = 1
-    while s < 16 and tiles * s < 512 and T // (2 * s) >= 512:
+    while s < 16 and big * s < 256 and T // (2 * s) >= 512:
         s *= 2
+    if big * s < 256:
+        small = ((Fc + 127) // 128) * ((H + 127) // 128)
+        s = 1
+        while s < 16 and small * s < 512 and T // (2 * s) >= 512:
+            s *= 2
     while s > 1 and T % (8 * s):
         s //= 2
     return s

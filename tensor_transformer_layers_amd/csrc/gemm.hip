@@ -100,9 +100,20 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
   // Problems that share nothing run one after another over the whole chip
   // (workgroups are dispatched in id order), each spread over all XCDs, so
   // that every XCD works on the same problem's operands at a time.
+  // With p.xcd_per_problem (many small problems, a multiple of 8 of them:
+  // the splits of a split-K product), each problem runs whole on one XCD
+  // instead, problem z on XCD z % 8, so its operand blocks are fetched into
+  // one L2 only.
   const int tps = vM * vN;
-  const int bz0 = (shareA || shareB) ? 0 : (int)blockIdx.x / tps;
-  const int t = (shareA || shareB) ? xcd_remap(blockIdx.x, gridDim.x) : xcd_remap((int)blockIdx.x - bz0 * tps, tps);
+  int bz0, t;
+  if (p.xcd_per_problem) {
+    const int xcd = (int)blockIdx.x % 8, local = (int)blockIdx.x / 8;
+    bz0 = (local / tps) * 8 + xcd;
+    t = local % tps;
+  } else {
+    bz0 = (shareA || shareB) ? 0 : (int)blockIdx.x / tps;
+    t = (shareA || shareB) ? xcd_remap(blockIdx.x, gridDim.x) : xcd_remap((int)blockIdx.x - bz0 * tps, tps);
+  }
   constexpr int GRP = 8;
   const int group = t / (GRP * vN);
   const int first_m = group * GRP;
@@ -396,6 +407,29 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
   constexpr bool SWI = C::EPI == EPI_SWIGLU;
 #pragma unroll
   for (int h = 0; h < C::TN / 2; ++h) {
+    // GELU' epilogue: the pre-activations of this phase's rows are read in
+    // blocks of ZB rows per lane, each block issued one block ahead of its
+    // use (the first before the accumulators go to LDS), so the load latency
+    // overlaps the staging and the previous block's arithmetic
+    constexpr int ZB = C::WM / 4 < 16 ? C::WM / 4 : 16;
+    const int zc_n = n0 + wn * C::WN + 64 * h + 4 * (lane & 15);
+    auto load_z = [&](int blk, bf16x4* z) {
+      const bf16* const zb = static_cast<const bf16*>(p.aux) + bz * p.sAux;
+#pragma unroll
+      for (int j = 0; j < ZB; ++j) {
+        const int m = m0 + wm * C::WM + (blk + j) * 4 + (lane >> 4);
+        z[j] = bf16x4{};
+        if (m < p.M && zc_n < p.N) {
+          const bf16* zp = zb + (int64_t)m * p.ldaux + zc_n;
+          if (zc_n + 3 < p.N)
+            z[j] = *reinterpret_cast<const bf16x4*>(zp);
+          else
+            for (int e = 0; e < 4 && zc_n + e < p.N; ++e) z[j][e] = zp[e];
+        }
+      }
+    };
+    bf16x4 zc[ZB];
+    if constexpr (C::EPI == EPI_GELU_BWD) load_z(0, zc);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int j = SWI ? h + half * (C::TN / 2) : 2 * h + half;
@@ -435,6 +469,37 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
             for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
         }
       }
+    } else if constexpr (C::EPI == EPI_GELU_BWD) {
+      // dZ = dH * GELU'(Z): 16 lanes per row, chunk c -> 4 outputs
+      static_assert((C::WM / 4) % ZB == 0, "row blocks");
+      const int c = lane & 15;
+      const int n = zc_n;
+#pragma unroll 1
+      for (int blk = 0; blk < C::WM / 4; blk += ZB) {
+        bf16x4 zn[ZB];
+        if (blk + ZB < C::WM / 4)
+          load_z(blk + ZB, zn);
+        else
+          for (int j = 0; j < ZB; ++j) zn[j] = bf16x4{};
+#pragma unroll
+        for (int j = 0; j < ZB; ++j) {
+          const int r = (blk + j) * 4 + (lane >> 4);
+          const int m = m0 + wm * C::WM + r;
+          const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
+          if (m < p.M && n < p.N) {
+            bf16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = to_bf16(v[e] * gelu_grad_bf16out(static_cast<float>(zc[j][e])));
+            bf16* dst = static_cast<bf16*>(p.C) + bz * p.sC + (int64_t)m * p.ldc + n;
+            if (n + 3 < p.N)
+              __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(dst));
+            else
+              for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < ZB; ++j) zc[j] = zn[j];
+      }
     } else {
       // 16 lanes per row: chunk c -> 4 outputs
       const int c = lane & 15;
@@ -461,22 +526,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
               for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = v[e];
           } else {
             bf16x4 o;
-            if constexpr (C::EPI == EPI_GELU_BWD) {
-              // dZ = dH * GELU'(Z) at the same (m, n); n is a multiple of 4
-              const bf16* zp = static_cast<const bf16*>(p.aux) + bz * p.sAux + (int64_t)m * p.ldaux + n;
-              bf16x4 z = {};
-              if (n + 3 < p.N)
-                z = *reinterpret_cast<const bf16x4*>(zp);
-              else
-                for (int e = 0; e < 4 && n + e < p.N; ++e) z[e] = zp[e];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) o[e] = to_bf16(v[e] * gelu_grad(static_cast<float>(z[e])));
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float x = v[e] + bias[e];
-                o[e] = to_bf16(C::EPI == EPI_GELU ? gelu_bf16out(x) : x);
-              }
+            for (int e = 0; e < 4; ++e) {
+              const float x = v[e] + bias[e];
+              o[e] = to_bf16(C::EPI == EPI_GELU ? gelu_bf16out(x) : x);
             }
             bf16* dst = static_cast<bf16*>(p.C) + off;
             if (n + 3 < p.N)

@@ -101,7 +101,10 @@ hipError_t launch_typed(const ReduceParams& p, hipStream_t s) {
   const int64_t blocks = std::min<int64_t>((n4 + per_block - 1) / per_block, int64_t(1) << 30);
   const dim3 g((unsigned)blocks), b(kThreads);
   if (p.ldy != p.H) {  // pitched output rows (a block of a wider matrix)
-    launch_kernel((reduce_kernel<OUT_BF16, 0, true>), g, b, 0, s, p, n4);
+    if (p.n_parts == 16)
+      launch_kernel((reduce_kernel<OUT_BF16, 16, true>), g, b, 0, s, p, n4);
+    else
+      launch_kernel((reduce_kernel<OUT_BF16, 0, true>), g, b, 0, s, p, n4);
     return hipGetLastError();
   }
   switch (p.n_parts) {
@@ -109,6 +112,7 @@ hipError_t launch_typed(const ReduceParams& p, hipStream_t s) {
     case 2: launch_kernel((reduce_kernel<OUT_BF16, 2>), g, b, 0, s, p, n4); break;
     case 4: launch_kernel((reduce_kernel<OUT_BF16, 4>), g, b, 0, s, p, n4); break;
     case 8: launch_kernel((reduce_kernel<OUT_BF16, 8>), g, b, 0, s, p, n4); break;
+    case 16: launch_kernel((reduce_kernel<OUT_BF16, 16>), g, b, 0, s, p, n4); break;
     default: launch_kernel((reduce_kernel<OUT_BF16, 0>), g, b, 0, s, p, n4); break;
   }
   return hipGetLastError();

@@ -376,12 +376,20 @@ struct BwdShape {
 
 // Weight gradients contract over all T tokens into a small [Fc x H] output
 // when the hidden size is narrow.  Split the token axis so that the launch
-// has at least ~2 workgroups per CU; each split's K stays a multiple of 8.
+// fills the chip: with 256x256 tiles (one per CU, the GEMM's choice once
+// there are 256 of them) when splitting up to 16 ways gets there, else with
+// 128x128 tiles at ~2 workgroups per CU.  Each split keeps K >= 512 and a
+// multiple of 8.
 int bwd_splits(int64_t T, int64_t Fc, int64_t H) {
   const int64_t big = ((Fc + 255) / 256) * ((H + 255) / 256);
-  const int64_t tiles = big >= 256 ? big : ((Fc + 127) / 128) * ((H + 127) / 128);
+  if (big >= 256) return 1;
   int s = 1;
-  while (s < 16 && tiles * s < 512 && T / (2 * s) >= 512) s *= 2;
+  while (s < 16 && big * s < 256 && T / (2 * s) >= 512) s *= 2;
+  if (big * s < 256) {
+    const int64_t small = ((Fc + 127) / 128) * ((H + 127) / 128);
+    s = 1;
+    while (s < 16 && small * s < 512 && T / (2 * s) >= 512) s *= 2;
+  }
   while (s > 1 && T % (8 * s)) s /= 2;
   return s;
 }
@@ -695,7 +703,8 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
       return hip_status(launch(name, TP_BF16, g, tp::EPI_PARTIAL, s), name);
     }
     const int64_t kc = T / S;
-    const tp::GemmParams g = gemm(Aop, T, kc, Bop, T, kc, K, N, M * N, M, N, kc, S);
+    tp::GemmParams g = gemm(Aop, T, kc, Bop, T, kc, K, N, M * N, M, N, kc, S);
+    g.xcd_per_problem = S % 8 == 0;  // each split's operand blocks stay in one XCD's L2
     TP_TRY(hip_status(launch(name, TP_BF16, g, tp::EPI_PARTIAL, s), name));
     tp::ReduceParams r{};
     r.P = K;

@@ -48,10 +48,24 @@ __device__ __forceinline__ float gelu_bf16out(float z) {
   return fmaxf(z, 0.0f) - fabsf(q);
 }
 
-// Slope of the exact GELU: d/dz [z Phi(z)] = Phi(z) + z phi(z), with
-// Phi(z) = (1 + erf(z / sqrt 2)) / 2 and phi(z) = e^(-z^2/2) / sqrt(2 pi).
-__device__ __forceinline__ float gelu_grad(float z) {
-  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) + z * 0.39894228040143268f * __expf(-0.5f * z * z);
+// Slope of the exact GELU for bf16 outputs:
+//   d/dz [z Phi(z)] = Phi(z) + z phi(z),  phi(z) = e^(-z^2/2) / sqrt(2 pi),
+// with the tail Phi(-|z|) = erfc(|z|/sqrt 2) / 2 from the same 7.1.26
+// expansion as gelu_bf16out (its folded constants), whose exponential
+// e^(-x^2), x = |z|/sqrt 2, is exactly e^(-z^2/2): one exp2 and one
+// reciprocal give both terms.  Absolute error ~1e-7, far below bf16
+// resolution.
+__device__ __forceinline__ float gelu_grad_bf16out(float z) {
+  const float u = fabsf(z) * (0.70710678118654752f * 1.2011224087864498f);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f / 1.2011224087864498f, u, 1.0f));
+  const float poly =
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f), 0.5f * 1.421413741f),
+                       0.5f * -0.284496736f),
+               0.5f * 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-u * u);  // e^(-z^2/2)
+  const float tail = poly * e;                     // Phi(-|z|)
+  const float Phi = z >= 0.0f ? 1.0f - tail : tail;
+  return fmaf(z * 0.39894228040143268f, e, Phi);
 }
 
 // SiLU for bf16 outputs: g / (1 + e^-g) with the hardware exponential and

@@ -53,6 +53,7 @@ struct GemmParams {
   int64_t ldaux, sAux;
   int M, N, K;
   int batch;
+  int xcd_per_problem;  // nonzero: batch % 8 == 0, each problem runs whole on one XCD
 };
 
 hipError_t launch_gemm_bf16(const GemmParams& p, Epilogue epi, hipStream_t s);

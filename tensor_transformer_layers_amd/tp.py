@@ -322,11 +322,17 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
     cnt = N if shard_count is None else shard_count
     g = dict(grads or {})
     dev = X.device
-    g.setdefault("dX", torch.empty((T, H), dtype=X.dtype, device=dev) if cnt == N else None)
-    g.setdefault("dA", torch.zeros((F, H), dtype=torch.float32, device=dev))
-    g.setdefault("da", torch.zeros((F,), dtype=torch.float32, device=dev) if need_da else None)
-    g.setdefault("dB", torch.zeros((H, F), dtype=torch.float32, device=dev))
-    g.setdefault("db", torch.zeros((H,), dtype=torch.float32, device=dev) if need_db else None)
+    f32 = torch.float32
+    if "dX" not in g:
+        g["dX"] = torch.empty((T, H), dtype=X.dtype, device=dev) if cnt == N else None
+    if "dA" not in g:
+        g["dA"] = torch.zeros((F, H), dtype=f32, device=dev)
+    if "da" not in g:
+        g["da"] = torch.zeros((F,), dtype=f32, device=dev) if need_da else None
+    if "dB" not in g:
+        g["dB"] = torch.zeros((H, F), dtype=f32, device=dev)
+    if "db" not in g:
+        g["db"] = torch.zeros((H,), dtype=f32, device=dev) if need_db else None
     d = MlpBwdDesc()
     d.dt = _dt(X)
     d.act = act
