@@ -658,7 +658,13 @@ hipError_t launch_bf16_epi(const GemmParams& p, hipStream_t s) {
   constexpr int kCUs = 256;
   const int out256 = (EPI == EPI_SWIGLU) ? 128 : 256;
   const int64_t big = (int64_t)((p.M + 255) / 256) * ((p.N + out256 - 1) / out256) * p.batch;
-  if (big >= kCUs) return launch_bf16_cfg<G<256, 256, 64, 2, kGemmSwizzleShift, EPI>>(p, s);
+  // The GELU' epilogue reads a bf16 tile of Z per output tile; with a short
+  // K (measured on the 16384 x 2048 x 512 product: 120 us on 256x256 tiles,
+  // 95-99 us on 128x128) two 128x128 workgroups per CU hide one's epilogue
+  // behind the other's MFMAs better than one 256x256 workgroup does.
+  const bool short_k_load_epilogue = EPI == EPI_GELU_BWD && p.K <= 2048;
+  if (big >= kCUs && !short_k_load_epilogue)
+    return launch_bf16_cfg<G<256, 256, 64, 2, kGemmSwizzleShift, EPI>>(p, s);
   return launch_bf16_cfg<G<128, 128, 64, 2, kGemmSwizzleShift, EPI>>(p, s);
 }
 
