@@ -43,6 +43,7 @@ __all__ = [
     "reduce_partials_fp32", "to_bf16", "attention_block_rows",
     "rmsnorm", "seq_slices", "all_gather_rows", "sp_entry", "rmsnorm_hidden_split",
     "gelu_grad", "mlp_backward", "mlp_backward_sharded",
+    "padded_vocab", "cross_entropy", "lm_head_ce", "vocab_parallel_ce",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -435,6 +436,80 @@ def mlp_backward_sharded(X, A, a, B, dY, N, act="gelu"):
     return {"dX": _fold(parts), "dA": np.concatenate(dA, axis=1),
             "da": np.concatenate(da), "dB": np.concatenate(dB, axis=0),
             "db": dY.sum(axis=0), "dX_parts": parts}
+
+
+# --------------------------------------------------------------------------
+# vocab-parallel output head and cross-entropy
+# --------------------------------------------------------------------------
+def padded_vocab(V, N, multiple=8):
+    """Vocab padded so that it splits into N equal shards whose width is a
+    multiple of ``multiple`` ([Blog] 6.2: pad the vocab to a size TP divides,
+    and drop the padding from the loss).  Returns (Vp, Vs)."""
+    Vs = -(-V // N)
+    Vs = -(-Vs // multiple) * multiple
+    return N * Vs, Vs
+
+
+def cross_entropy(logits, labels):
+    """Per-row cross-entropy of softmax(logits) at the label:
+    logsumexp(row) - row[label] (scipy's logsumexp)."""
+    from scipy.special import logsumexp
+
+    L = _f64(logits)
+    labels = np.asarray(labels)
+    return logsumexp(L, axis=1) - L[np.arange(L.shape[0]), labels]
+
+
+def lm_head_ce(X, E, labels, V):
+    """Unsharded output head and loss: logits = X E^T over the V real vocab
+    rows of E ([V' x H], V' >= V rows; rows past V are padding and take no
+    part), then the per-token cross-entropy."""
+    E = _f64(E)[:V]
+    return cross_entropy(_f64(X) @ E.T, labels)
+
+
+def vocab_parallel_ce(X, E, labels, V, N):
+    """The same loss with the vocab split over N shards ([Blog] 6.2: each
+    shard computes only its own vocab partition's logits and its part of the
+    loss, then an all-reduce combines them; padding is dropped from the loss).
+
+    Shard i owns padded vocab rows [i Vs, (i+1) Vs); entries >= V are padding
+    and are left out.  Per token, shard i forms its local maximum m_i, its
+    local sum s_i = sum exp(l - m_i) and its target logit z_i (0 when the
+    label is not in its partition).  The combine, in shard order, is
+        M = max_i m_i,  S = sum_i s_i exp(m_i - M),  target = sum_i z_i,
+        loss = log S + M - target.
+    A shard with no real vocab entries contributes nothing.
+    Returns (per-token losses, the per-shard (m, s, z) arrays).
+    """
+    X = _f64(X)
+    labels = np.asarray(labels)
+    Vp, Vs = padded_vocab(V, N)
+    T = X.shape[0]
+    ms, ss, zs = [], [], []
+    for i in range(N):
+        lo, hi = i * Vs, min((i + 1) * Vs, V)
+        if hi <= lo:
+            ms.append(np.full(T, -np.inf))
+            ss.append(np.zeros(T))
+            zs.append(np.zeros(T))
+            continue
+        L = X @ _f64(E)[lo:hi].T
+        m = L.max(axis=1)
+        ms.append(m)
+        ss.append(np.exp(L - m[:, None]).sum(axis=1))
+        own = (labels >= lo) & (labels < hi)
+        z = np.zeros(T)
+        z[own] = L[np.arange(T)[own], labels[own] - lo]
+        zs.append(z)
+    M = ms[0].copy()
+    for m in ms[1:]:
+        M = np.maximum(M, m)
+    S = np.zeros(T)
+    for m, s_ in zip(ms, ss):
+        S = S + s_ * np.exp(m - M)
+    target = _fold(zs)
+    return np.log(S) + M - target, (ms, ss, zs)
 
 
 # --------------------------------------------------------------------------

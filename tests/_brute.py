@@ -79,3 +79,13 @@ def rmsnorm(X, g, eps):
         inv = 1.0 / math.sqrt(ms + eps)
         out.append([v * inv * gg for v, gg in zip(row, g)])
     return out
+
+
+def cross_entropy(logits, labels):
+    """-log softmax at the label, per row, with plain loops."""
+    out = []
+    for row, y in zip(logits, labels):
+        m = max(row)
+        s = sum(math.exp(v - m) for v in row)
+        out.append(math.log(s) + m - row[y])
+    return out
