@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "TFLOP/s per sharded TP MLP/attn layer fwd on 1 GPU; % of bf16 MFMA peak"
 METRIC_BWD = "TFLOP/s per sharded TP MLP layer bwd on 1 GPU; % of bf16 MFMA peak"
+METRIC_VOCAB = "TFLOP/s of the vocab-parallel output head + cross-entropy fwd on 1 GPU; % of bf16 MFMA peak"
 PEAK_BF16 = 2.5e15     # dense MFMA, bf16
 PEAK_F32 = 157.3e12    # dense MFMA, fp32
 PEAK_HBM = 8.0e12      # bytes/s
@@ -67,6 +68,18 @@ def kernel_work(w, name, shards_per_launch, rows_reduced):
             return 2.0 * T * hd * H * c, es * (c * T * hd + c * H * hd) + 4 * c * T * H
     if name.startswith("bwd_"):
         return backward_kernel_work(w, name, shards_per_launch)
+    if w.kind == "vocab_ce":
+        c = shards_per_launch
+        Vs = -(-w.F // N)
+        Vs = -(-Vs // 8) * 8
+        if name == "vocab_logits_gemm":  # padded rows are computed too; the FLOP count is the real vocab's
+            return 2.0 * T * H * w.F * c / N, es * (T * H + c * Vs * H) + 4 * c * T * Vs
+        if name == "vocab_ce_stats":  # each real logit read once, one exponential each; labels; 3 stats out
+            return 0.0, 4 * T * min(c * Vs, w.F) + 4 * T + 12 * c * T
+        if name == "vocab_ce_combine":
+            return 0.0, 12 * N * T + 4 * T
+        if name == "vocab_ce_mean":
+            return 0.0, 4 * T + 4
     if name == "reduce_partials":
         return 0.0, 4 * N * rows_reduced * H + es * rows_reduced * H + (es * H if w.sigma_bias else 0)
     if name == "rmsnorm_gather":  # square, add, two scalings per element; X read once, Y written once
@@ -150,6 +163,8 @@ KERNEL_SOURCES = {
     "bwd_transpose": "bwd.hip", "bwd_bias_rowsum": "bwd.hip", "bwd_recompute_gemm": "gemm.hip",
     "bwd_dz_gemm": "gemm.hip", "bwd_dx_gemm": "gemm.hip", "bwd_da_gemm": "gemm.hip", "bwd_db_gemm": "gemm.hip",
     "bwd_splitk_reduce": "reduce.hip",
+    "vocab_logits_gemm": "gemm.hip", "vocab_ce_stats": "vocab.hip", "vocab_ce_combine": "vocab.hip",
+    "vocab_ce_mean": "vocab.hip",
 }
 
 
@@ -175,6 +190,8 @@ KERNEL_SYMBOL = {
     "bwd_transpose": "transpose_kernel", "bwd_bias_rowsum": "rowsum_kernel", "bwd_recompute_gemm": "gemm_",
     "bwd_dz_gemm": "gemm_", "bwd_dx_gemm": "gemm_", "bwd_da_gemm": "gemm_", "bwd_db_gemm": "gemm_",
     "bwd_splitk_reduce": "reduce_kernel",
+    "vocab_logits_gemm": "gemm_", "vocab_ce_stats": "ce_stats_kernel", "vocab_ce_combine": "ce_combine_kernel",
+    "vocab_ce_mean": "ce_mean_kernel",
 }
 
 
@@ -197,6 +214,8 @@ def launch_order(w, sp_entry=False, backward=False):
     entry side, the norm-and-gather kernel comes first."""
     if backward:
         return backward_launch_order(w)
+    if w.kind == "vocab_ce":
+        return ["vocab_logits_gemm", "vocab_ce_stats", "vocab_ce_combine", "vocab_ce_mean"]
     head = ["rmsnorm_gather"] if sp_entry else []
     if w.kind == "attn":
         return head + ["attn_qk_gemm", "attn_vt_gemm", "attn_core", "attn_out_gemm", "reduce_partials"]
@@ -245,8 +264,10 @@ def write_traffic(w, share, pmc_dir, argv_line, sp_entry=False, backward=False):
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         rows = list(csv.DictReader(open(os.path.join(pmc_dir, counter, "run_counter_collection.csv"))))
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        # the calibration copies are the run's last device copies (set-up may
+        # copy too, before the timed region)
         copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        big = max(copies, key=lambda r: int(r["Grid_Size"]))
+        big = copies[-1]
         factor[counter] = float(2 ** 30) / (float(big["Counter_Value"]) * 1024.0)
         ours = [r for r in rows if "tp::" in r["Kernel_Name"] or "_ZN2tp" in r["Kernel_Name"]]
         vals = collections.defaultdict(list)
@@ -360,7 +381,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed warmup steps (default: as many as fill about 0.5 s, at least 5); "
                          "the shader clock takes tens of ms to settle after idle")
-    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: GELU MLP bf16, T=16384, H=512, F=2048, N=4)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload 1..5 (default 2: GELU MLP bf16, T=16384, H=512, F=2048, N=4), or 6: the "
+                         "vocab-parallel output head + cross-entropy (T=16384, H=4096, V=150000, N=8)")
     ap.add_argument("--share", choices=["layer", "rank"], default="layer")
     ap.add_argument("--sp-entry", action="store_true",
                     help="MLP workloads with a reduce-scatter: start each step with the sequence-parallel entry "
@@ -380,7 +403,7 @@ def main():
     if args.traffic_from:
         from tensor_transformer_layers_amd import configs
 
-        w = configs.CONFIGS[args.config]
+        w = configs.workload(args.config)
         argv = (f"--config {args.config} --share {args.share}{' --sp-entry' if args.sp_entry else ''}"
                 f"{' --backward' if args.backward else ''} --steps 3 --warmup 1 --no-cpu-baseline --calib-copy")
         print(write_traffic(w, args.share, args.traffic_from, argv, args.sp_entry, args.backward))
@@ -398,7 +421,11 @@ def main():
     from tensor_transformer_layers_amd import configs, inputs, tp, workloads
 
     tp.lib()  # fails loudly if libtp.so is missing
-    w = configs.CONFIGS[args.config]
+    w = configs.workload(args.config)
+    if w.kind == "vocab_ce" and (args.share != "layer" or args.sp_entry or args.backward):
+        print("bench.py: the vocab cross-entropy workload (--config 6) runs with --share layer only",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
     if args.sp_entry and (w.kind == "attn" or w.n_slices < 2 or args.share != "layer"):
         print("bench.py: --sp-entry needs an MLP workload with a reduce-scatter (--config 5) and --share layer",
               file=sys.stderr, flush=True)
@@ -525,7 +552,7 @@ def main():
     roof["traffic"] = measured_traffic(dom, workload_tag(w, args.sp_entry, args.backward))
 
     out = {
-        "metric": METRIC_BWD if args.backward else METRIC,
+        "metric": METRIC_BWD if args.backward else METRIC_VOCAB if w.kind == "vocab_ce" else METRIC,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -539,7 +566,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name, "kind": w.kind, "tokens": w.T, "batch": w.batch, "seq": w.seq, "hidden": w.H,
-            "ffn": w.F if w.kind != "attn" else None, "heads": w.heads or None, "shards": w.N,
+            "ffn": w.F if w.kind in ("mlp_gelu", "mlp_swiglu") else None, "heads": w.heads or None, "shards": w.N,
+            **({"vocab": w.F, "vocab_padded": tp.tp_vocab_padded(w.F, w.N),
+                "labels": inputs.LABEL_RECIPE} if w.kind == "vocab_ce" else {}),
             "share": "all shards + reduction" if args.share == "layer" else "rank 0 shard + reduction",
             "reduce_scatter_slices": w.n_slices, "seed": w.seed,
             **({"sp_entry": {"norm": "rmsnorm", "eps": inputs.NORM_EPS, "gain": inputs.NORM_GAIN_RECIPE}}

@@ -236,6 +236,47 @@ size_t tp_mlp_backward_workspace_size(const tp_mlp_bwd_desc* d);
 tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size_t ws_bytes);
 
 /*
+ * Vocab-parallel output head and cross-entropy over shards [shard_begin,
+ * shard_begin + shard_count).  The vocab is padded to Vp = N*Vs entries
+ * (tp_vocab_padded: Vs = ceil(V/N) rounded up to a multiple of 8) so that it
+ * splits into N equal shards; entries >= V are padding and take no part in
+ * the loss (2kiu.com blog post, section 6.2: pad the vocab to a size TP
+ * divides and filter the padding out of the loss).  Shard i computes the
+ * logits of its partition, X E_i^T (fp32), and from them its part of the
+ * loss only: its maximum, its sum of exp(logit - maximum), and the label's
+ * logit if it owns the label (same section: no shard assembles the full
+ * logits; an all-reduce combines the parts).  When the range covers all N
+ * shards, the parts are folded in shard order (the all-reduce stand-in):
+ *   M = max_i m_i,  S = sum_i s_i exp(m_i - M),  loss[t] = log S + M - z_label
+ * and mean_loss = (sum over t of loss[t]) / T in a fixed order.
+ *
+ *   X        [T x H] bf16
+ *   E        [Vp x H] bf16 (out-in storage of the head / tied embedding); the
+ *            padding rows V .. Vp-1 must exist (any finite values)
+ *   labels   [T] int32 in [0, V); a label outside has no owner and its token's
+ *            loss is log S + M (no target term)
+ *   loss     [T] fp32, written when shard_count == N
+ *   mean_loss  [1] fp32 or NULL
+ * With shard_count < N the range's statistics stay in the workspace.
+ * H a multiple of 8.  Deterministic (fixed orders, no atomics).
+ */
+typedef struct {
+  tp_dtype dt;     /* TP_BF16                                                   */
+  int64_t T, H, V;
+  int N, shard_begin, shard_count;
+  const void* X;
+  const void* E;
+  const int32_t* labels;
+  float* loss;
+  float* mean_loss;
+} tp_vocab_ce_desc;
+
+/* Padded vocab size Vp for V entries over N shards (0 if V < 1 or N < 1). */
+int64_t tp_vocab_padded(int64_t V, int N);
+size_t tp_vocab_ce_workspace_size(const tp_vocab_ce_desc* d);
+tp_status tp_vocab_ce_forward(void* stream, const tp_vocab_ce_desc* d, void* ws, size_t ws_bytes);
+
+/*
  * Local causal attention alone (the middle step of tp_attn_forward), for
  * `heads` heads of width 128 over `batch` sequences of length `seq`:
  *   QK  [batch*seq x ldqk]: head h's query at columns h*128.., its key at

@@ -29,8 +29,20 @@ def attention(X, Wq, Wk, Wv, Wo, batch, seq, heads, rows=None, bo=None):
     return O.attention_block_rows(X, Wq.T, Wk.T, Wv.T, Wo.T, batch, seq, heads, np.asarray(rows), bo=bo)
 
 
+def vocab_ce(X, E, labels, V, rows=None):
+    """Per-token cross-entropy of the output head over the V real vocab rows
+    of E ([>= V x H] storage), on some token rows."""
+    if rows is None:
+        return O.lm_head_ce(X, E, labels, V)
+    rows = np.asarray(rows)
+    return O.lm_head_ce(X[rows], E, np.asarray(labels)[rows], V)
+
+
 def workload(kind, host, batch=None, seq=None, heads=None, rows=None):
-    """Expected output rows of one workload ("mlp_gelu" | "mlp_swiglu" | "attn")."""
+    """Expected output rows of one workload ("mlp_gelu" | "mlp_swiglu" |
+    "attn" | "vocab_ce": the per-token loss)."""
+    if kind == "vocab_ce":
+        return vocab_ce(host["X"], host["E"], host["labels"], host["E"].shape[0], rows)
     if kind == "mlp_gelu":
         return mlp_gelu(host["X"], host["A"], host["a"], host["B"], host["b"], rows)
     if kind == "mlp_swiglu":

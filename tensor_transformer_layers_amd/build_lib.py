@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libtp.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["gemm.hip", "mlp_fused.hip", "reduce.hip", "attention.hip", "norm.hip", "bwd.hip", "tp_api.cpp"]
+SOURCES = ["gemm.hip", "mlp_fused.hip", "reduce.hip", "attention.hip", "norm.hip", "bwd.hip", "vocab.hip", "tp_api.cpp"]
 
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from forming v_pk_*_f32 instructions.

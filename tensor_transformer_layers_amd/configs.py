@@ -22,12 +22,12 @@ from dataclasses import dataclass, field
 class Workload:
     key: int
     name: str
-    kind: str               # "mlp_gelu" | "mlp_swiglu" | "attn"
+    kind: str               # "mlp_gelu" | "mlp_swiglu" | "attn" | "vocab_ce"
     dtype: str              # "f32" | "bf16"  (inputs; accumulation is fp32)
     batch: int
     seq: int
     H: int                  # hidden
-    F: int                  # FFN / intermediate (attention: unused, = H)
+    F: int                  # FFN / intermediate (attention: unused, = H; vocab_ce: the vocab size)
     N: int                  # tensor-parallel shards
     sigma_x: float = 1.0
     sigma_w: float = 0.02
@@ -52,6 +52,8 @@ class Workload:
         and add counted as 2).  Causal attention counts the lower triangle
         with the diagonal: 4 * d * S(S+1)/2 per (batch, head)."""
         T, H = self.T, self.H
+        if self.kind == "vocab_ce":  # the head's product over the real vocab, one shard's share
+            return 2.0 * T * H * self.F / self.N
         if self.kind == "mlp_gelu":
             return 2.0 * T * H * self.Fs * 2
         if self.kind == "mlp_swiglu":
@@ -83,6 +85,23 @@ CONFIGS: dict[int, Workload] = {
                 batch=8, seq=2048, H=12288, F=49152, N=8, n_slices=8,
                 sigma_w=0.01, sigma_bias=0.01, seed=20260005),
 }
+
+# Beyond the five: the vocab-parallel output head and cross-entropy of the
+# blog post at 2kiu.com (section 6.2) at the 7B hidden size, with the
+# ~150k-entry vocab "张量并行" names in its vocab-parallel paragraph (not a
+# multiple of 8 shards x 8, so it is padded), 8 x 2048 tokens.
+EXTRA: dict[int, Workload] = {
+    6: Workload(6, "vocab_ce_bf16_T16384_H4096_V150000_N8", "vocab_ce", "bf16",
+                batch=8, seq=2048, H=4096, F=150000, N=8,
+                sigma_w=0.02, sigma_bias=None, seed=20260006),
+}
+
+
+def workload(key: int) -> Workload:
+    """Workload ``key``: one of the five of the path, or an extra one."""
+    if key in CONFIGS:
+        return CONFIGS[key]
+    return EXTRA[key]
 
 
 def scaled(w: Workload, **kw) -> Workload:

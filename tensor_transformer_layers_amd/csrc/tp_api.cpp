@@ -450,6 +450,53 @@ tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
   return TP_OK;
 }
 
+// ------------------------------------------------------- vocab-parallel CE
+// Workspace: logits of the shard range, shard_count x [T x Vs] fp32, then the
+// statistics m, s, z, each N x [T] fp32 (slot i = shard i).
+struct VocabShape {
+  int64_t Vp, Vs;
+  size_t logits_bytes, m_off, s_off, z_off, total;
+};
+
+int64_t vocab_shard_width(int64_t V, int N) {
+  const int64_t vs = (V + N - 1) / N;
+  return (vs + 7) / 8 * 8;
+}
+
+tp_status validate_vocab(const tp_vocab_ce_desc* d, VocabShape* sh) {
+  if (!d) return fail(TP_ERR_NULL, "descriptor is NULL");
+  TP_TRY(check_dtype(d->dt));
+  if (d->dt != TP_BF16) return fail(TP_ERR_DTYPE, "vocab-parallel cross-entropy is bf16-only");
+  if (d->T < 0 || d->H <= 0 || d->V <= 0 || d->N <= 0)
+    return fail(TP_ERR_SHAPE, "T=%lld H=%lld V=%lld N=%d", (long long)d->T, (long long)d->H, (long long)d->V, d->N);
+  if (d->shard_begin < 0 || d->shard_count < 1 || d->shard_begin + d->shard_count > d->N)
+    return fail(TP_ERR_SHAPE, "shard range [%d, %d) outside [0, %d)", d->shard_begin,
+                d->shard_begin + d->shard_count, d->N);
+  *sh = VocabShape{};
+  sh->Vs = vocab_shard_width(d->V, d->N);
+  sh->Vp = sh->Vs * d->N;
+  if (d->T == 0) return TP_OK;  // empty input: nothing to read or write
+  if (d->H % 8) return fail(TP_ERR_ALIGN, "hidden H=%lld is not a multiple of 8", (long long)d->H);
+  TP_TRY(check_matrix("X", d->X, d->T, d->H, d->H, 8));
+  TP_TRY(check_matrix("E", d->E, sh->Vp, d->H, d->H, 8));
+  if (!d->labels) return fail(TP_ERR_NULL, "labels is NULL");
+  if (!aligned16(d->labels)) return fail(TP_ERR_ALIGN, "labels is not 16-byte aligned");
+  if (d->shard_count == d->N) {
+    if (!d->loss) return fail(TP_ERR_NULL, "loss is NULL");
+    if (!aligned16(d->loss)) return fail(TP_ERR_ALIGN, "loss is not 16-byte aligned");
+  }
+  if (d->mean_loss && (reinterpret_cast<uintptr_t>(d->mean_loss) & 3u))
+    return fail(TP_ERR_ALIGN, "mean_loss is not 4-byte aligned");
+  if (d->T > kIntMax || sh->Vs > kIntMax) return fail(TP_ERR_SHAPE, "size exceeds 2^31-1");
+  const size_t T = (size_t)d->T;
+  sh->logits_bytes = align256((size_t)d->shard_count * T * sh->Vs * sizeof(float));
+  sh->m_off = sh->logits_bytes;
+  sh->s_off = sh->m_off + align256((size_t)d->N * T * sizeof(float));
+  sh->z_off = sh->s_off + align256((size_t)d->N * T * sizeof(float));
+  sh->total = sh->z_off + align256((size_t)d->N * T * sizeof(float));
+  return TP_OK;
+}
+
 tp_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (!ws) return fail(TP_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (!aligned16(ws)) return fail(TP_ERR_ALIGN, "workspace is not 16-byte aligned");
@@ -754,6 +801,82 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
 
   if (c < d->N) return ok();
   return run_reduce(s, TP_BF16, d->N, T, H, P, T * H, nullptr, d->dX, 1, -1);
+}
+
+int64_t tp_vocab_padded(int64_t V, int N) {
+  if (V < 1 || N < 1) return 0;
+  return vocab_shard_width(V, N) * N;
+}
+
+size_t tp_vocab_ce_workspace_size(const tp_vocab_ce_desc* d) {
+  VocabShape sh;
+  return validate_vocab(d, &sh) == TP_OK ? sh.total : 0;
+}
+
+tp_status tp_vocab_ce_forward(void* stream, const tp_vocab_ce_desc* d, void* ws, size_t ws_bytes) {
+  VocabShape sh;
+  TP_TRY(validate_vocab(d, &sh));
+  if (d->T == 0) return ok();
+  TP_TRY(check_ws(ws, ws_bytes, sh.total));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t T = d->T, H = d->H, Vs = sh.Vs;
+  const int c = d->shard_count, i0 = d->shard_begin;
+  if (log_enabled())
+    fprintf(stderr, "[tp] vocab ce bf16 N=%d shards [%d,%d): X[%lld x %lld] E_i[%lld x %lld] V=%lld (padded %lld)%s\n",
+            d->N, i0, i0 + c, (long long)T, (long long)H, (long long)Vs, (long long)H, (long long)d->V,
+            (long long)sh.Vp, c == d->N ? " ; combine" : "");
+  char* base = static_cast<char*>(ws);
+  float* logits = reinterpret_cast<float*>(base);
+  float* m = reinterpret_cast<float*>(base + sh.m_off);
+  float* sm = reinterpret_cast<float*>(base + sh.s_off);
+  float* z = reinterpret_cast<float*>(base + sh.z_off);
+
+  // logits of every shard in range (X shared: one launch)
+  const tp::GemmParams g = gemm(d->X, H, 0, static_cast<const bf16_t*>(d->E) + (size_t)i0 * Vs * H, H, Vs * H,
+                                logits, Vs, T * Vs, T, Vs, H, c);
+  TP_TRY(hip_status(launch("vocab_logits_gemm", TP_BF16, g, tp::EPI_PARTIAL, s), "vocab_logits_gemm"));
+
+  tp::CeStatsParams st{};
+  st.logits = logits;
+  st.sL = T * Vs;
+  st.ldl = Vs;
+  st.labels = d->labels;
+  st.m = m;
+  st.s = sm;
+  st.z = z;
+  st.T = T;
+  st.V = d->V;
+  st.Vs = Vs;
+  st.shard0 = i0;
+  st.shards = c;
+  {
+    KernelTimer kt("vocab_ce_stats", s);
+    const hipError_t e = tp::launch_ce_stats(st, s);
+    kt.stop();
+    TP_TRY(hip_status(e, "vocab_ce_stats"));
+  }
+  if (c < d->N) return ok();
+
+  tp::CeCombineParams cb{};
+  cb.m = m;
+  cb.s = sm;
+  cb.z = z;
+  cb.loss = d->loss;
+  cb.T = T;
+  cb.N = d->N;
+  {
+    KernelTimer kt("vocab_ce_combine", s);
+    const hipError_t e = tp::launch_ce_combine(cb, s);
+    kt.stop();
+    TP_TRY(hip_status(e, "vocab_ce_combine"));
+  }
+  if (d->mean_loss) {
+    KernelTimer kt("vocab_ce_mean", s);
+    const hipError_t e = tp::launch_ce_mean(d->loss, T, d->mean_loss, s);
+    kt.stop();
+    TP_TRY(hip_status(e, "vocab_ce_mean"));
+  }
+  return ok();
 }
 
 tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t ws_bytes) {

@@ -151,4 +151,29 @@ struct RowSumParams {
 };
 hipError_t launch_rowsum(const RowSumParams& p, hipStream_t s);
 
+// Vocab-parallel cross-entropy (vocab.hip).  Shard s of the launch is global
+// shard shard0 + s, owning vocab ids [(shard0+s)*Vs, (shard0+s+1)*Vs); ids
+// >= V are padding.  Its logits row t is at logits + s*sL + t*ldl (fp32).
+// Statistics go to slot (shard0+s)*T + t of m (max), s (sum of exp(l - max))
+// and z (the label's logit, 0 when the shard does not own the label).
+struct CeStatsParams {
+  const float* logits;
+  int64_t sL, ldl;
+  const int32_t* labels;
+  float *m, *s, *z;
+  int64_t T, V, Vs;
+  int shard0, shards;
+};
+hipError_t launch_ce_stats(const CeStatsParams& p, hipStream_t s);
+
+// loss[t] = log S + M - target from the N shards' statistics (slots i*T + t).
+struct CeCombineParams {
+  const float *m, *s, *z;
+  float* loss;
+  int64_t T;
+  int N;
+};
+hipError_t launch_ce_combine(const CeCombineParams& p, hipStream_t s);
+hipError_t launch_ce_mean(const float* loss, int64_t T, float* mean, hipStream_t s);
+
 }  // namespace tp

@@ -35,6 +35,7 @@ TENSORS = {
     "mlp_gelu": ["X", "A", "a", "B", "b"],
     "mlp_swiglu": ["X", "Wg", "Wu", "Wd"],
     "attn": ["X", "Wq", "Wk", "Wv", "Wo"],
+    "vocab_ce": ["X", "E"],
 }
 
 
@@ -88,6 +89,8 @@ def shapes(w: Workload) -> dict:
         return {"X": (T, H), "Wg": (F, H), "Wu": (F, H), "Wd": (H, F)}
     if w.kind == "attn":
         return {"X": (T, H), "Wq": (H, H), "Wk": (H, H), "Wv": (H, H), "Wo": (H, H)}
+    if w.kind == "vocab_ce":  # E: the output head over the real vocab, [V x H]
+        return {"X": (T, H), "E": (F, H)}
     raise ValueError(w.kind)
 
 
@@ -111,6 +114,9 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
         else:
             sigma = w.sigma_w
         out[name] = round_to_dtype(draw(ss, shp[name], sigma), w.dtype)
+    if w.kind == "vocab_ce":
+        out["labels"] = labels(w) if seed == w.seed else \
+            np.random.default_rng(np.random.SeedSequence([seed, 3])).integers(0, w.F, size=w.T).astype(np.int32)
     return out
 
 
@@ -152,3 +158,14 @@ GRAD_RECIPE = "N(0, 1) per element of dY [T x H], rounded to the workload dtype,
 def grad_output(w: Workload) -> np.ndarray:
     """The upstream gradient dY [T x H] of workload w (recipe above)."""
     return round_to_dtype(draw(np.random.SeedSequence([w.seed, 2]), (w.T, w.H), 1.0), w.dtype)
+
+
+# Vocab-parallel cross-entropy: the target token of each row, uniform over the
+# real vocab, from its own stream of the seed.
+LABEL_RECIPE = "uniform integers in [0, V), SeedSequence([seed, 3])"
+
+
+def labels(w: Workload) -> np.ndarray:
+    """Target ids [T] (int32) of workload w (recipe above)."""
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, 3]))
+    return rng.integers(0, w.F, size=w.T).astype(np.int32)

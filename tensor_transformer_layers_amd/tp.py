@@ -56,6 +56,15 @@ class MlpBwdDesc(ctypes.Structure):
     ]
 
 
+class VocabCeDesc(ctypes.Structure):
+    _fields_ = [
+        ("dt", _int),
+        ("T", _i64), ("H", _i64), ("V", _i64),
+        ("N", _int), ("shard_begin", _int), ("shard_count", _int),
+        ("X", _vp), ("E", _vp), ("labels", _vp), ("loss", _vp), ("mean_loss", _vp),
+    ]
+
+
 _SIGS = {
     "tp_column_linear": (_int, [_vp, _int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64]),
     "tp_row_linear_partial": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]),
@@ -70,6 +79,9 @@ _SIGS = {
     "tp_attn_forward": (_int, [_vp, ctypes.POINTER(AttnDesc), _vp, _sz]),
     "tp_mlp_backward_workspace_size": (_sz, [ctypes.POINTER(MlpBwdDesc)]),
     "tp_mlp_backward": (_int, [_vp, ctypes.POINTER(MlpBwdDesc), _vp, _sz]),
+    "tp_vocab_padded": (_i64, [_i64, _int]),
+    "tp_vocab_ce_workspace_size": (_sz, [ctypes.POINTER(VocabCeDesc)]),
+    "tp_vocab_ce_forward": (_int, [_vp, ctypes.POINTER(VocabCeDesc), _vp, _sz]),
     "tp_attn_local": (_int, [_vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp, _i64]),
     "tp_timing_enable": (_int, [_int]),
     "tp_timing_read": (_int, [_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
@@ -149,6 +161,18 @@ def tp_mlp_backward(stream, desc: MlpBwdDesc, ws, ws_bytes) -> int:
 
 def tp_mlp_backward_workspace_size(desc: MlpBwdDesc) -> int:
     return lib().tp_mlp_backward_workspace_size(ctypes.byref(desc))
+
+
+def tp_vocab_padded(V: int, N: int) -> int:
+    return lib().tp_vocab_padded(V, N)
+
+
+def tp_vocab_ce_workspace_size(desc: VocabCeDesc) -> int:
+    return lib().tp_vocab_ce_workspace_size(ctypes.byref(desc))
+
+
+def tp_vocab_ce_forward(stream, desc: VocabCeDesc, ws, ws_bytes) -> int:
+    return lib().tp_vocab_ce_forward(stream, ctypes.byref(desc), ws, ws_bytes)
 
 
 def tp_attn_local(*args) -> int:
@@ -349,6 +373,45 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
         ws = alloc_workspace(need, dev)
     check(tp_mlp_backward(_stream(stream), d, _ptr(ws), ws.numel()))
     return g, ws
+
+
+def vocab_ce_forward(X, E, labels, V, N, shard_begin=0, shard_count=None, loss=None, mean=None, ws=None,
+                     stream=None):
+    """Vocab-parallel output head and cross-entropy; returns (loss [T] fp32
+    or None for a partial shard range, mean [1] fp32 or None, workspace).
+    E must have tp_vocab_padded(V, N) rows; labels are int32."""
+    torch = _torch()
+    T, H = X.shape
+    cnt = N if shard_count is None else shard_count
+    if loss is None and cnt == N:
+        loss = torch.empty((T,), dtype=torch.float32, device=X.device)
+    if mean is None and cnt == N:
+        mean = torch.empty((1,), dtype=torch.float32, device=X.device)
+    d = VocabCeDesc()
+    d.dt = _dt(X)
+    d.T, d.H, d.V = T, H, V
+    d.N, d.shard_begin, d.shard_count = N, shard_begin, cnt
+    d.X, d.E, d.labels, d.loss, d.mean_loss = _ptr(X), _ptr(E), _ptr(labels), _ptr(loss), _ptr(mean)
+    need = tp_vocab_ce_workspace_size(d)
+    if need == 0:
+        if T == 0:
+            return loss, mean, ws
+        raise TPError(TP_ERR_SHAPE, last_error())
+    if ws is None or ws.numel() < need:
+        ws = alloc_workspace(need, X.device)
+    check(tp_vocab_ce_forward(_stream(stream), d, _ptr(ws), ws.numel()))
+    return loss, mean, ws
+
+
+def vocab_ce_stats(ws, N, T, Vs, shard_count):
+    """Views (m, s, z), each [N x T] fp32, of the statistics in a vocab
+    cross-entropy workspace (after the logits of the shard range)."""
+    torch = _torch()
+    align = lambda x: (x + 255) // 256 * 256
+    off = align(shard_count * T * Vs * 4)
+    step = align(N * T * 4)
+    f = lambda o: ws[o:o + N * T * 4].view(torch.float32).view(N, T)
+    return f(off), f(off + step), f(off + 2 * step)
 
 
 def mlp_partials(ws, N, T, H):

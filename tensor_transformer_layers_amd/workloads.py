@@ -51,6 +51,15 @@ def device_inputs(w: Workload, host: dict, device="cuda") -> dict:
         del Wq, Wk, Wv
         d["Wo"] = to_device(host["Wo"], dt, device)
         d["bo"] = None
+    elif w.kind == "vocab_ce":
+        d["X"] = to_device(host["X"], dt, device)
+        # padding rows (zeros) added on the host: one upload, no device copy
+        Vp = tp.tp_vocab_padded(w.F, w.N)
+        E = np.zeros((Vp, w.H), dtype=np.float32)
+        E[: w.F] = host["E"]
+        d["E"] = to_device(E, dt, device)
+        del E
+        d["labels"] = torch.from_numpy(np.ascontiguousarray(host["labels"])).to(device)
     else:
         raise ValueError(w.kind)
     return d
@@ -61,7 +70,15 @@ def act_of(w: Workload) -> int:
 
 
 def forward(w: Workload, d: dict, Y=None, ws=None, shard_begin=0, shard_count=None, slice=-1, stream=None):
-    """One pass of the sublayer over shards [shard_begin, shard_begin+count)."""
+    """One pass of the sublayer over shards [shard_begin, shard_begin+count).
+    For the vocab cross-entropy, Y is the per-token loss."""
+    if w.kind == "vocab_ce":
+        loss, mean, ws = tp.vocab_ce_forward(d["X"], d["E"], d["labels"], w.F, w.N, shard_begin=shard_begin,
+                                             shard_count=shard_count, loss=Y, mean=d.get("mean"), ws=ws,
+                                             stream=stream)
+        if mean is not None:
+            d["mean"] = mean
+        return loss, ws
     if w.kind == "attn":
         return tp.attn_forward(d["X"], d["Wqkv"], d["Wo"], d["bo"], w.batch, w.seq, w.heads, w.N, Y=Y, ws=ws,
                                shard_begin=shard_begin, shard_count=shard_count, n_slices=w.n_slices,

@@ -276,3 +276,55 @@ def test_bench_split_rule_matches_library(L, T, H, F, N, c):
     extra = tp.tp_mlp_backward_workspace_size(d) - base
     S = bench.backward_splits(T, Fc, H)
     assert extra == (align(S * Fc * H * 4) if S > 1 else 0)
+
+
+# ------------------------------------------------------------ vocab-parallel CE
+def _vce(**kw):
+    d = tp.VocabCeDesc()
+    d.dt = tp.TP_BF16
+    d.T, d.H, d.V, d.N = 256, 512, 1000, 8
+    d.shard_begin, d.shard_count = 0, 8
+    d.X = d.E = d.labels = d.loss = d.mean_loss = FAKE
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_vocab_padding_matches_oracle(L):
+    from oracle import tp_oracle as O
+    for V in (1, 7, 1000, 50257, 150000):
+        for N in (1, 2, 3, 8):
+            assert tp.tp_vocab_padded(V, N) == O.padded_vocab(V, N)[0]
+    assert tp.tp_vocab_padded(0, 8) == 0
+
+
+def test_vocab_ce_workspace_size_is_host_only(L):
+    T, N = 256, 8
+    Vs = 128  # ceil(1000 / 8) = 125 -> 128
+    align = lambda x: (x + 255) // 256 * 256
+    assert tp.tp_vocab_ce_workspace_size(_vce()) == align(N * T * Vs * 4) + 3 * align(N * T * 4)
+    assert tp.tp_vocab_ce_workspace_size(_vce(shard_count=1, loss=None)) == align(T * Vs * 4) + 3 * align(N * T * 4)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dt=tp.TP_F32), tp.TP_ERR_DTYPE, "bf16-only"),
+    (dict(V=0), tp.TP_ERR_SHAPE, "V=0"),
+    (dict(H=516), tp.TP_ERR_ALIGN, "H=516 is not a multiple of 8"),
+    (dict(labels=None), tp.TP_ERR_NULL, "labels is NULL"),
+    (dict(loss=None), tp.TP_ERR_NULL, "loss is NULL"),
+    (dict(E=FAKE + 8), tp.TP_ERR_ALIGN, "E is not 16-byte aligned"),
+    (dict(mean_loss=FAKE + 2), tp.TP_ERR_ALIGN, "mean_loss"),
+    (dict(shard_begin=7, shard_count=2), tp.TP_ERR_SHAPE, "shard range"),
+])
+def test_vocab_ce_rejects_before_launch(L, kw, status, needle):
+    d = _vce(**kw)
+    assert tp.tp_vocab_ce_workspace_size(d) == 0
+    assert tp.tp_vocab_ce_forward(None, d, FAKE, 1 << 40) == status, tp.last_error()
+    assert needle in tp.last_error()
+
+
+def test_vocab_ce_small_workspace_and_empty_input(L):
+    d = _vce()
+    need = tp.tp_vocab_ce_workspace_size(d)
+    assert tp.tp_vocab_ce_forward(None, d, FAKE, need - 1) == tp.TP_ERR_WORKSPACE
+    assert tp.tp_vocab_ce_forward(None, _vce(T=0), None, 0) == tp.TP_OK
