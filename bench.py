@@ -391,6 +391,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="GELU MLP workloads (2, 5): time the backward of the pair instead (input, weight and "
                          "bias gradients of every shard, then the input-gradient reduction)")
+    ap.add_argument("--overlap", type=int, default=0, metavar="K",
+                    help="MLP workloads, --share layer: cut the tokens into K row blocks and overlap the reduction "
+                         "of block k (on a second stream) with the products of block k+1")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -426,6 +429,11 @@ def main():
         print("bench.py: the vocab cross-entropy workload (--config 6) runs with --share layer only",
               file=sys.stderr, flush=True)
         sys.exit(2)
+    if args.overlap and (w.kind not in ("mlp_gelu", "mlp_swiglu") or args.share != "layer" or args.backward
+                         or w.T % args.overlap):
+        print("bench.py: --overlap K needs an MLP workload, --share layer and K dividing the token count",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
     if args.sp_entry and (w.kind == "attn" or w.n_slices < 2 or args.share != "layer"):
         print("bench.py: --sp-entry needs an MLP workload with a reduce-scatter (--config 5) and --share layer",
               file=sys.stderr, flush=True)
@@ -459,8 +467,14 @@ def main():
         rows = w.T // w.n_slices if w.n_slices > 1 else w.T
         Yr = torch.empty((rows, w.H), dtype=Y.dtype, device=Y.device)
     stream = torch.cuda.current_stream()
+    stream2 = torch.cuda.Stream() if args.overlap else None  # default priority
 
     def step():
+        if args.overlap:
+            if args.sp_entry:
+                tp.rmsnorm_gather(x_slices, gain, inputs.NORM_EPS, w.n_slices, out=d["X"], stream=stream)
+            workloads.forward_overlap(w, d, args.overlap, stream2, Y=Y, ws=ws, stream=stream)
+            return
         if args.backward:
             workloads.backward(w, d, dY, grads=grads, ws=ws, stream=stream)
             return
@@ -534,15 +548,19 @@ def main():
         flops = backward_flops(w, w.N)
     value = flops / (ms_step / 1e3) / 1e12
 
+    # with --overlap each launch covers one row block of T/K tokens
+    wk = configs.scaled(w, batch=1, seq=w.T // args.overlap) if args.overlap else w
+    if args.overlap:
+        rows_red = wk.T
     kernels = {}
     for name, (ms, n) in kern.items():
-        f, b = kernel_work(w, name, shards, rows_red)
+        f, b = kernel_work(wk, name, shards, rows_red)
         avg = ms / n / 1e3
         kernels[name] = {"avg_us": round(avg * 1e6, 2), "launches": n,
                          "share": round(ms / sum(v[0] for v in kern.values()), 4),
                          **roofline(w, name, f, b, avg)}
     dom = max(kern, key=lambda k: kern[k][0])
-    f, b = kernel_work(w, dom, shards, rows_red)
+    f, b = kernel_work(wk, dom, shards, rows_red)
     avg = kern[dom][0] / kern[dom][1] / 1e3
     roof = roofline(w, dom, f, b, avg)
     src_hash = kernel_source_hash()
@@ -573,6 +591,7 @@ def main():
             "reduce_scatter_slices": w.n_slices, "seed": w.seed,
             **({"sp_entry": {"norm": "rmsnorm", "eps": inputs.NORM_EPS, "gain": inputs.NORM_GAIN_RECIPE}}
                if args.sp_entry else {}),
+            **({"overlap_chunks": args.overlap} if args.overlap else {}),
             **({"pass": "backward", "upstream_gradient": inputs.GRAD_RECIPE,
                 "flop_counted": "8*T*H*F (dH, dX, dA, dB); the recomputed column product is extra and not counted",
                 "split_k": backward_splits(w.T, w.F, w.H)} if args.backward else {}),

@@ -186,6 +186,21 @@ size_t tp_attn_partials_offset(const tp_attn_desc* d);
  */
 tp_status tp_mlp_forward(void* stream, const tp_mlp_desc* d, void* ws, size_t ws_bytes);
 
+/*
+ * The same sublayer with the reduction overlapped ("大模型分布式训练篇——从零实现
+ * Tensor Para...", section 3: compute/communication overlap).  The token axis
+ * is cut into `chunks` equal row blocks.  Block k's shard products run on
+ * `stream`; as soon as they are done, the fold of block k's rows runs on
+ * `stream2` while block k+1 computes.  `stream` waits for `stream2` at the
+ * end, so work the caller enqueues on `stream` afterwards sees Y complete.
+ * The result is bit-identical to tp_mlp_forward (same kernels, same per-row
+ * fold).  Needs the whole shard range (shard_count == N), slice == -1, T a
+ * multiple of chunks (1..64), and two distinct streams.  Calls that overlap on
+ * the same workspace race.
+ */
+tp_status tp_mlp_forward_overlap(void* stream, void* stream2, const tp_mlp_desc* d, int chunks, void* ws,
+                                 size_t ws_bytes);
+
 /* QKV projection of the shard's heads, causal softmax attention per local
  * head (scale 1/sqrt(head_dim), diagonal kept), row-parallel output
  * projection into the partial slab, then the reduction as for the MLP. */

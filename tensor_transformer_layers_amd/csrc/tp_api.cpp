@@ -42,6 +42,7 @@ size_t esize(tp_dtype dt) { return dt == TP_BF16 ? 2 : 4; }
 const char* dt_name(tp_dtype dt) { return dt == TP_BF16 ? "bf16" : "f32"; }
 
 constexpr int64_t kIntMax = 0x7fffffff;
+constexpr int kMaxOverlapChunks = 64;
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool log_enabled() {
@@ -621,6 +622,90 @@ size_t tp_attn_partials_offset(const tp_attn_desc* d) {
   return 0;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The shard products of token rows [row0, row0 + rows) for every shard in the
+// descriptor's range: their partial rows land at the same rows of each
+// shard's slab slot (and of the intermediate), so row blocks computed in any
+// order fill the slab exactly as one call over all rows does.
+tp_status mlp_rows(hipStream_t s, const tp_mlp_desc* d, const MlpShape& sh, void* ws, int64_t row0, int64_t rows) {
+  const int64_t T = d->T, H = d->H, Fs = sh.Fs;
+  const int c = d->shard_count, i0 = d->shard_begin;
+  char* base = static_cast<char*>(ws);
+  float* P = reinterpret_cast<float*>(base) + (size_t)row0 * H;
+  const size_t es = esize(d->dt);
+  void* Hs = base + sh.h_offset + (size_t)row0 * sh.h_ld * es;
+  const void* X = static_cast<const char*>(d->X) + (size_t)row0 * H * es;
+
+  // Narrow hidden sizes: one kernel per shard range computes the column
+  // product, the activation and the row partial with the intermediate kept
+  // on chip (it never needs to leave the shard).
+  if (d->dt == TP_BF16 && d->act != TP_ACT_SWIGLU && tp::mlp_fused_supported(H, Fs)) {
+    tp::FusedMlpParams f{};
+    f.X = X;
+    f.ldx = H;
+    f.A = static_cast<const char*>(d->A) + (size_t)i0 * Fs * H * es;
+    f.lda = H;
+    f.sA = Fs * H;
+    f.bias = d->a ? static_cast<const char*>(d->a) + (size_t)i0 * Fs * es : nullptr;
+    f.sBias = Fs;
+    f.B = static_cast<const char*>(d->B) + (size_t)i0 * Fs * es;
+    f.ldb = d->F;
+    f.sB = Fs;
+    f.P = P + (size_t)i0 * T * H;
+    f.ldp = H;
+    f.sP = T * H;
+    f.T = (int)rows;
+    f.H = (int)H;
+    f.Fs = (int)Fs;
+    f.shards = c;
+    f.act = d->act == TP_ACT_GELU ? tp::FUSED_GELU : tp::FUSED_NONE;
+    KernelTimer kt("mlp_fused", s);
+    const hipError_t e = tp::launch_mlp_fused(f, s);
+    kt.stop();
+    return hip_status(e, "mlp fused launch");
+  }
+
+  // column GEMM + activation for every shard in range (X shared, one launch)
+  tp::GemmParams col = gemm(X, H, 0, static_cast<const char*>(d->A) + (size_t)i0 * sh.a_rows * H * es, H,
+                            sh.a_rows * H, Hs, sh.h_ld, T * sh.h_ld, rows, Fs, H, c);
+  if (d->a) {
+    col.bias = static_cast<const char*>(d->a) + (size_t)i0 * Fs * es;
+    col.sBias = Fs;
+  }
+  col.upOff = Fs * H;
+  const tp::Epilogue ce = d->act == TP_ACT_SWIGLU ? tp::EPI_SWIGLU : d->act == TP_ACT_GELU ? tp::EPI_GELU : tp::EPI_STORE;
+  TP_TRY(hip_status(launch("mlp_column_gemm", d->dt, col, ce, s), "mlp column launch"));
+
+  // row partial of every shard into its slot of the fp32 slab
+  const tp::GemmParams row = gemm(Hs, sh.h_ld, T * sh.h_ld, static_cast<const char*>(d->B) + (size_t)i0 * Fs * es, d->F,
+                                  Fs, P + (size_t)i0 * T * H, H, T * H, rows, H, Fs, c);
+  return hip_status(launch("mlp_row_gemm", d->dt, row, tp::EPI_PARTIAL, s), "mlp row launch");
+}
+
+// Events that order the overlapped forward's two streams, reused call to call
+// (a wait takes the event's state at the time it is enqueued).
+std::mutex g_evmu;
+std::vector<hipEvent_t> g_overlap_events;
+
+tp_status overlap_events(int n, hipEvent_t* out) {
+  std::lock_guard<std::mutex> g(g_evmu);
+  while ((int)g_overlap_events.size() < n) {
+    hipEvent_t e = nullptr;
+    const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (r != hipSuccess) return hip_status(r, "overlap event create");
+    g_overlap_events.push_back(e);
+  }
+  for (int i = 0; i < n; ++i) out[i] = g_overlap_events[i];
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 tp_status tp_mlp_forward(void* stream, const tp_mlp_desc* d, void* ws, size_t ws_bytes) {
   MlpShape sh;
   TP_TRY(validate_mlp(d, &sh));
@@ -636,61 +721,40 @@ tp_status tp_mlp_forward(void* stream, const tp_mlp_desc* d, void* ws, size_t ws
             dt_name(d->dt), (int)d->act, d->N, i0, i0 + c, (long long)T, (long long)H, (long long)sh.a_rows,
             (long long)H, (long long)T, (long long)Fs, (long long)H, (long long)Fs, (long long)T, (long long)H,
             c == d->N ? " ; reduce" : "");
-  if (T == 0) return ok();
-  char* base = static_cast<char*>(ws);
-  float* P = reinterpret_cast<float*>(base);
-  void* Hs = base + sh.h_offset;
-  const size_t es = esize(d->dt);
-
-  // Narrow hidden sizes: one kernel per shard range computes the column
-  // product, the activation and the row partial with the intermediate kept
-  // on chip (it never needs to leave the shard).
-  if (d->dt == TP_BF16 && d->act != TP_ACT_SWIGLU && tp::mlp_fused_supported(H, Fs)) {
-    tp::FusedMlpParams f{};
-    f.X = d->X;
-    f.ldx = H;
-    f.A = static_cast<const char*>(d->A) + (size_t)i0 * Fs * H * es;
-    f.lda = H;
-    f.sA = Fs * H;
-    f.bias = d->a ? static_cast<const char*>(d->a) + (size_t)i0 * Fs * es : nullptr;
-    f.sBias = Fs;
-    f.B = static_cast<const char*>(d->B) + (size_t)i0 * Fs * es;
-    f.ldb = d->F;
-    f.sB = Fs;
-    f.P = P + (size_t)i0 * T * H;
-    f.ldp = H;
-    f.sP = T * H;
-    f.T = (int)T;
-    f.H = (int)H;
-    f.Fs = (int)Fs;
-    f.shards = c;
-    f.act = d->act == TP_ACT_GELU ? tp::FUSED_GELU : tp::FUSED_NONE;
-    KernelTimer kt("mlp_fused", s);
-    const hipError_t e = tp::launch_mlp_fused(f, s);
-    kt.stop();
-    TP_TRY(hip_status(e, "mlp fused launch"));
-    if (c < d->N) return ok();
-    return run_reduce(s, d->dt, d->N, T, H, P, T * H, d->b, d->Y, d->n_slices, d->slice);
-  }
-
-  // column GEMM + activation for every shard in range (X shared, one launch)
-  tp::GemmParams col = gemm(d->X, H, 0, static_cast<const char*>(d->A) + (size_t)i0 * sh.a_rows * H * es, H,
-                            sh.a_rows * H, Hs, sh.h_ld, T * sh.h_ld, T, Fs, H, c);
-  if (d->a) {
-    col.bias = static_cast<const char*>(d->a) + (size_t)i0 * Fs * es;
-    col.sBias = Fs;
-  }
-  col.upOff = Fs * H;
-  const tp::Epilogue ce = d->act == TP_ACT_SWIGLU ? tp::EPI_SWIGLU : d->act == TP_ACT_GELU ? tp::EPI_GELU : tp::EPI_STORE;
-  TP_TRY(hip_status(launch("mlp_column_gemm", d->dt, col, ce, s), "mlp column launch"));
-
-  // row partial of every shard into its slot of the fp32 slab
-  const tp::GemmParams row = gemm(Hs, sh.h_ld, T * sh.h_ld, static_cast<const char*>(d->B) + (size_t)i0 * Fs * es, d->F, Fs,
-                                  P + (size_t)i0 * T * H, H, T * H, T, H, Fs, c);
-  TP_TRY(hip_status(launch("mlp_row_gemm", d->dt, row, tp::EPI_PARTIAL, s), "mlp row launch"));
-
+  TP_TRY(mlp_rows(s, d, sh, ws, 0, T));
   if (c < d->N) return ok();
-  return run_reduce(s, d->dt, d->N, T, H, P, T * H, d->b, d->Y, d->n_slices, d->slice);
+  return run_reduce(s, d->dt, d->N, T, H, reinterpret_cast<float*>(ws), T * H, d->b, d->Y, d->n_slices, d->slice);
+}
+
+tp_status tp_mlp_forward_overlap(void* stream, void* stream2, const tp_mlp_desc* d, int chunks, void* ws,
+                                 size_t ws_bytes) {
+  MlpShape sh;
+  TP_TRY(validate_mlp(d, &sh));
+  if (d->shard_count != d->N) return fail(TP_ERR_SHAPE, "the overlapped forward needs the whole shard range");
+  if (d->slice != -1) return fail(TP_ERR_SHAPE, "the overlapped forward writes every row (slice must be -1)");
+  if (chunks < 1 || chunks > kMaxOverlapChunks)
+    return fail(TP_ERR_SHAPE, "chunks=%d outside [1, %d]", chunks, kMaxOverlapChunks);
+  if (d->T % chunks)
+    return fail(TP_ERR_DIVISIBILITY, "T=%lld tokens do not split into %d chunks", (long long)d->T, chunks);
+  if (d->T == 0) return ok();
+  if (stream2 == stream) return fail(TP_ERR_SHAPE, "stream2 must differ from stream");
+  TP_TRY(check_ws(ws, ws_bytes, sh.total));
+  const hipStream_t s = static_cast<hipStream_t>(stream), s2 = static_cast<hipStream_t>(stream2);
+  hipEvent_t ev[kMaxOverlapChunks + 1];
+  TP_TRY(overlap_events(chunks + 1, ev));
+  const int64_t T = d->T, H = d->H, rows = T / chunks;
+  const size_t es = esize(d->dt);
+  for (int k = 0; k < chunks; ++k) {
+    TP_TRY(mlp_rows(s, d, sh, ws, k * rows, rows));
+    TP_TRY(hip_status(hipEventRecord(ev[k], s), "overlap event record"));
+    TP_TRY(hip_status(hipStreamWaitEvent(s2, ev[k], 0), "overlap stream wait"));
+    // rows of block k of the fold, as slice k of `chunks` slices
+    void* Yk = static_cast<char*>(d->Y) + (size_t)k * rows * H * es;
+    TP_TRY(run_reduce(s2, d->dt, d->N, T, H, reinterpret_cast<float*>(ws), T * H, d->b, Yk, chunks, k));
+  }
+  TP_TRY(hip_status(hipEventRecord(ev[chunks], s2), "overlap event record"));
+  TP_TRY(hip_status(hipStreamWaitEvent(s, ev[chunks], 0), "overlap stream wait"));
+  return ok();
 }
 
 size_t tp_mlp_backward_workspace_size(const tp_mlp_bwd_desc* d) {

@@ -76,6 +76,7 @@ _SIGS = {
     "tp_mlp_partials_offset": (_sz, [ctypes.POINTER(MlpDesc)]),
     "tp_attn_partials_offset": (_sz, [ctypes.POINTER(AttnDesc)]),
     "tp_mlp_forward": (_int, [_vp, ctypes.POINTER(MlpDesc), _vp, _sz]),
+    "tp_mlp_forward_overlap": (_int, [_vp, _vp, ctypes.POINTER(MlpDesc), _int, _vp, _sz]),
     "tp_attn_forward": (_int, [_vp, ctypes.POINTER(AttnDesc), _vp, _sz]),
     "tp_mlp_backward_workspace_size": (_sz, [ctypes.POINTER(MlpBwdDesc)]),
     "tp_mlp_backward": (_int, [_vp, ctypes.POINTER(MlpBwdDesc), _vp, _sz]),
@@ -149,6 +150,10 @@ def tp_rmsnorm_gather(*args) -> int:
 
 def tp_mlp_forward(stream, desc: MlpDesc, ws, ws_bytes) -> int:
     return lib().tp_mlp_forward(stream, ctypes.byref(desc), ws, ws_bytes)
+
+
+def tp_mlp_forward_overlap(stream, stream2, desc: MlpDesc, chunks, ws, ws_bytes) -> int:
+    return lib().tp_mlp_forward_overlap(stream, stream2, ctypes.byref(desc), chunks, ws, ws_bytes)
 
 
 def tp_attn_forward(stream, desc: AttnDesc, ws, ws_bytes) -> int:
@@ -412,6 +417,26 @@ def vocab_ce_stats(ws, N, T, Vs, shard_count):
     step = align(N * T * 4)
     f = lambda o: ws[o:o + N * T * 4].view(torch.float32).view(N, T)
     return f(off), f(off + step), f(off + 2 * step)
+
+
+def mlp_forward_overlap(X, A, a, B, b, N, chunks, stream2, act=TP_ACT_GELU, Y=None, ws=None, stream=None):
+    """The whole MLP sublayer with the reduction of row block k overlapped
+    with the products of block k+1 on ``stream2`` (a torch stream other than
+    the current one); returns (Y, workspace)."""
+    torch = _torch()
+    T, H = X.shape
+    if Y is None:
+        Y = torch.empty((T, H), dtype=X.dtype, device=X.device)
+    d = mlp_desc(X, A, a, B, b, N, act, Y)
+    need = tp_mlp_workspace_size(d)
+    if need == 0:
+        if T == 0:
+            return Y, ws
+        raise TPError(TP_ERR_SHAPE, last_error())
+    if ws is None or ws.numel() < need:
+        ws = alloc_workspace(need, X.device)
+    check(tp_mlp_forward_overlap(_stream(stream), stream2.cuda_stream, d, chunks, _ptr(ws), ws.numel()))
+    return Y, ws
 
 
 def mlp_partials(ws, N, T, H):

@@ -88,6 +88,15 @@ def forward(w: Workload, d: dict, Y=None, ws=None, shard_begin=0, shard_count=No
                           stream=stream)
 
 
+def forward_overlap(w: Workload, d: dict, chunks, stream2, Y=None, ws=None, stream=None):
+    """All shards of an MLP sublayer with the reduction of each row block
+    overlapped with the next block's products on ``stream2``."""
+    if w.kind not in ("mlp_gelu", "mlp_swiglu"):
+        raise ValueError(f"the overlapped forward is built for the MLP sublayers, not {w.kind}")
+    return tp.mlp_forward_overlap(d["X"], d["A"], d["a"], d["B"], d["b"], w.N, chunks, stream2, act=act_of(w), Y=Y,
+                                  ws=ws, stream=stream)
+
+
 def reduce_slab(w: Workload, d: dict, ws, Y=None, slice=-1, stream=None):
     """The reduction step alone over the partial slab of a workspace."""
     torch = _torch()

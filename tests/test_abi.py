@@ -328,3 +328,27 @@ def test_vocab_ce_small_workspace_and_empty_input(L):
     need = tp.tp_vocab_ce_workspace_size(d)
     assert tp.tp_vocab_ce_forward(None, d, FAKE, need - 1) == tp.TP_ERR_WORKSPACE
     assert tp.tp_vocab_ce_forward(None, _vce(T=0), None, 0) == tp.TP_OK
+
+
+# ------------------------------------------------------------ overlapped forward
+@pytest.mark.parametrize("kw,chunks,status,needle", [
+    (dict(), 0, tp.TP_ERR_SHAPE, "chunks=0"),
+    (dict(), 65, tp.TP_ERR_SHAPE, "chunks=65"),
+    (dict(), 3, tp.TP_ERR_DIVISIBILITY, "do not split into 3 chunks"),
+    (dict(shard_count=2), 2, tp.TP_ERR_SHAPE, "whole shard range"),
+    (dict(n_slices=4, slice=1), 2, tp.TP_ERR_SHAPE, "slice must be -1"),
+    (dict(F=2050), 2, tp.TP_ERR_DIVISIBILITY, "not divisible by N=4"),
+])
+def test_mlp_forward_overlap_rejects_before_launch(L, kw, chunks, status, needle):
+    d = _mlp(**kw)
+    s = tp.tp_mlp_forward_overlap(None, FAKE, d, chunks, FAKE, 1 << 40)
+    assert s == status, tp.last_error()
+    assert needle in tp.last_error()
+
+
+def test_mlp_forward_overlap_needs_two_streams_and_workspace(L):
+    d = _mlp()
+    assert tp.tp_mlp_forward_overlap(FAKE, FAKE, d, 2, FAKE, 1 << 40) == tp.TP_ERR_SHAPE
+    assert "stream2 must differ" in tp.last_error()
+    need = tp.tp_mlp_workspace_size(d)
+    assert tp.tp_mlp_forward_overlap(None, FAKE, d, 2, FAKE, need - 1) == tp.TP_ERR_WORKSPACE
