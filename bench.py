@@ -72,10 +72,12 @@ def kernel_work(w, name, shards_per_launch, rows_reduced):
         c = shards_per_launch
         Vs = -(-w.F // N)
         Vs = -(-Vs // 8) * 8
-        if name == "vocab_logits_gemm":  # padded rows are computed too; the FLOP count is the real vocab's
-            return 2.0 * T * H * w.F * c / N, es * (T * H + c * Vs * H) + 4 * c * T * Vs
-        if name == "vocab_ce_stats":  # each real logit read once, one exponential each; labels; 3 stats out
-            return 0.0, 4 * T * min(c * Vs, w.F) + 4 * T + 12 * c * T
+        cps = -(-Vs // 64)
+        if name == "vocab_logits_gemm":  # padded rows are computed too; the FLOP count is the real vocab's.
+            # The epilogue writes 3 statistics per (token, 64-column chunk) instead of the logits.
+            return 2.0 * T * H * w.F * c / N, es * (T * H + c * Vs * H) + 4 * T + 12 * c * cps * T
+        if name == "vocab_ce_fold":  # the chunk statistics read once, 3 per-shard statistics out
+            return 0.0, 12 * c * cps * T + 12 * c * T
         if name == "vocab_ce_combine":
             return 0.0, 12 * N * T + 4 * T
         if name == "vocab_ce_mean":
@@ -163,7 +165,7 @@ KERNEL_SOURCES = {
     "bwd_transpose": "bwd.hip", "bwd_bias_rowsum": "bwd.hip", "bwd_recompute_gemm": "gemm.hip",
     "bwd_dz_gemm": "gemm.hip", "bwd_dx_gemm": "gemm.hip", "bwd_da_gemm": "gemm.hip", "bwd_db_gemm": "gemm.hip",
     "bwd_splitk_reduce": "reduce.hip",
-    "vocab_logits_gemm": "gemm.hip", "vocab_ce_stats": "vocab.hip", "vocab_ce_combine": "vocab.hip",
+    "vocab_logits_gemm": "gemm.hip", "vocab_ce_fold": "vocab.hip", "vocab_ce_combine": "vocab.hip",
     "vocab_ce_mean": "vocab.hip",
 }
 
@@ -190,7 +192,7 @@ KERNEL_SYMBOL = {
     "bwd_transpose": "transpose_kernel", "bwd_bias_rowsum": "rowsum_kernel", "bwd_recompute_gemm": "gemm_",
     "bwd_dz_gemm": "gemm_", "bwd_dx_gemm": "gemm_", "bwd_da_gemm": "gemm_", "bwd_db_gemm": "gemm_",
     "bwd_splitk_reduce": "reduce_kernel",
-    "vocab_logits_gemm": "gemm_", "vocab_ce_stats": "ce_stats_kernel", "vocab_ce_combine": "ce_combine_kernel",
+    "vocab_logits_gemm": "gemm_", "vocab_ce_fold": "ce_fold_kernel", "vocab_ce_combine": "ce_combine_kernel",
     "vocab_ce_mean": "ce_mean_kernel",
 }
 
@@ -215,7 +217,7 @@ def launch_order(w, sp_entry=False, backward=False):
     if backward:
         return backward_launch_order(w)
     if w.kind == "vocab_ce":
-        return ["vocab_logits_gemm", "vocab_ce_stats", "vocab_ce_combine", "vocab_ce_mean"]
+        return ["vocab_logits_gemm", "vocab_ce_fold", "vocab_ce_combine", "vocab_ce_mean"]
     head = ["rmsnorm_gather"] if sp_entry else []
     if w.kind == "attn":
         return head + ["attn_qk_gemm", "attn_vt_gemm", "attn_core", "attn_out_gemm", "reduce_partials"]

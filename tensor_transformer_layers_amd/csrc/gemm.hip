@@ -37,6 +37,8 @@
 //    same XCD (shared L2), in groups of 8 M-tiles.
 //
 // fp32 path: 64x64 tiles, v_mfma_f32_16x16x4_f32, used for fp32 workloads.
+#include <math.h>
+
 #include <type_traits>
 
 #include "tp_device.hpp"
@@ -401,6 +403,19 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
   // c ^ (r & 15) (conflict-free for both the column writes and the row reads).
   // Phase h takes subtiles (2h, 2h+1), or for SwiGLU the gate subtile h and
   // its up subtile h + TN/2.
+  // EPI_CE_STATS: the label of each of this lane's epilogue rows, as a
+  // shard-local column (out-of-range values simply match no column), loaded
+  // once per tile before the staging
+  int ce_label[C::EPI == EPI_CE_STATS ? C::WM / 4 : 1];
+  if constexpr (C::EPI == EPI_CE_STATS) {
+    const int64_t vbase = (int64_t)(p.ce.shard0 + bz) * p.N;
+#pragma unroll
+    for (int it = 0; it < C::WM / 4; ++it) {
+      const int m = m0 + wm * C::WM + it * 4 + (lane >> 4);
+      const int64_t y = m < p.M ? (int64_t)p.ce.labels[m] - vbase : -1;
+      ce_label[it] = (y >= 0 && y < p.N) ? (int)y : -1000000;
+    }
+  }
   lds_barrier();  // every wave is done with the operand stages
   char* const ep = smem + w * (C::WM * 256);
   static_assert(4 * C::WM * 256 <= C::LDS_BYTES, "epilogue staging fits the operand stages");
@@ -500,12 +515,51 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
 #pragma unroll
         for (int j = 0; j < ZB; ++j) zc[j] = zn[j];
       }
+    } else if constexpr (C::EPI == EPI_CE_STATS) {
+      // Cross-entropy statistics of this phase's 64 logit columns per token
+      // row (16 lanes per row, 4 logits each): the max over the row's real
+      // vocab ids, then the sum of exp(l - max) against it, and the label's
+      // logit.  Lane 0 of each row group writes the three values; the logits
+      // themselves are never stored.
+      const int c = lane & 15;
+      const int ncol0 = n0 + wn * C::WN + 64 * h;  // first column of the 64-column chunk
+      const int n = ncol0 + 4 * c;
+      const int64_t vbase = (int64_t)(p.ce.shard0 + bz) * p.N;  // vocab id of the shard's column 0
+      const int lim = (int)min((int64_t)p.N, max((int64_t)0, p.ce.V - vbase));  // columns >= lim: padding
+      const int k = ncol0 / 64;
+      float* const st = p.ce.stats + ((int64_t)bz * p.ce.cps + k) * p.M;
+      const auto fmax_ = [](float a, float b) { return fmaxf(a, b); };
+      const auto add_ = [](float a, float b) { return a + b; };
+#pragma unroll 4
+      for (int it = 0; it < C::WM / 4; ++it) {
+        const int r = it * 4 + (lane >> 4);
+        const int m = m0 + wm * C::WM + r;
+        const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < lim) mx = fmaxf(mx, v[e]);
+        mx = row16_reduce(mx, fmax_);
+        float sum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < lim) sum += __expf(v[e] - mx);
+        const int y = ce_label[it] - n;  // label column relative to this lane's first logit
+        const float z = (y >= 0 && y < 4 && n + y < lim) ? (y == 0 ? v[0] : y == 1 ? v[1] : y == 2 ? v[2] : v[3]) : 0.0f;
+        sum = row16_reduce(sum, add_);
+        const float zr = row16_reduce(z, add_);  // one lane of the row holds the label, if any
+        if (c == 0 && m < p.M && k < p.ce.cps) {
+          st[m] = mx;
+          st[m + p.ce.astride] = sum;
+          st[m + 2 * p.ce.astride] = zr;
+        }
+      }
     } else {
       // 16 lanes per row: chunk c -> 4 outputs
       const int c = lane & 15;
       const int n = n0 + wn * C::WN + 64 * h + 4 * c;
       float bias[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (C::EPI != EPI_PARTIAL && C::EPI != EPI_GELU_BWD) {
+      if constexpr (C::EPI != EPI_PARTIAL && C::EPI != EPI_GELU_BWD && C::EPI != EPI_CE_STATS) {
         if (p.bias) {
           const bf16* bp = static_cast<const bf16*>(p.bias) + bz * p.sBias;
           for (int e = 0; e < 4; ++e) bias[e] = n + e < p.N ? static_cast<float>(bp[n + e]) : 0.0f;
@@ -677,6 +731,7 @@ hipError_t launch_gemm_bf16(const GemmParams& p, Epilogue epi, hipStream_t s) {
     case EPI_PARTIAL: return launch_bf16_epi<EPI_PARTIAL>(p, s);
     case EPI_SWIGLU: return launch_bf16_epi<EPI_SWIGLU>(p, s);
     case EPI_GELU_BWD: return launch_bf16_epi<EPI_GELU_BWD>(p, s);
+    case EPI_CE_STATS: return launch_bf16_epi<EPI_CE_STATS>(p, s);
   }
   return hipErrorInvalidValue;
 }

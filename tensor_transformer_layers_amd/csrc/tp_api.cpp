@@ -452,11 +452,14 @@ tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
 }
 
 // ------------------------------------------------------- vocab-parallel CE
-// Workspace: logits of the shard range, shard_count x [T x Vs] fp32, then the
-// statistics m, s, z, each N x [T] fp32 (slot i = shard i).
+// Workspace: the per-(token, 64-column chunk) statistics of the shard range
+// written by the logits GEMM's epilogue -- three arrays (max, sum, label
+// logit) of shard_count*cps*T floats each -- then the per-shard statistics
+// m, s, z, each N x [T] fp32 (slot i = shard i).
 struct VocabShape {
   int64_t Vp, Vs;
-  size_t logits_bytes, m_off, s_off, z_off, total;
+  int cps;  // 64-column chunks per shard
+  size_t chunk_bytes, m_off, s_off, z_off, total;
 };
 
 int64_t vocab_shard_width(int64_t V, int N) {
@@ -490,8 +493,9 @@ tp_status validate_vocab(const tp_vocab_ce_desc* d, VocabShape* sh) {
     return fail(TP_ERR_ALIGN, "mean_loss is not 4-byte aligned");
   if (d->T > kIntMax || sh->Vs > kIntMax) return fail(TP_ERR_SHAPE, "size exceeds 2^31-1");
   const size_t T = (size_t)d->T;
-  sh->logits_bytes = align256((size_t)d->shard_count * T * sh->Vs * sizeof(float));
-  sh->m_off = sh->logits_bytes;
+  sh->cps = (int)((sh->Vs + 63) / 64);
+  sh->chunk_bytes = align256(3 * (size_t)d->shard_count * sh->cps * T * sizeof(float));
+  sh->m_off = sh->chunk_bytes;
   sh->s_off = sh->m_off + align256((size_t)d->N * T * sizeof(float));
   sh->z_off = sh->s_off + align256((size_t)d->N * T * sizeof(float));
   sh->total = sh->z_off + align256((size_t)d->N * T * sizeof(float));
@@ -890,34 +894,39 @@ tp_status tp_vocab_ce_forward(void* stream, const tp_vocab_ce_desc* d, void* ws,
             d->N, i0, i0 + c, (long long)T, (long long)H, (long long)Vs, (long long)H, (long long)d->V,
             (long long)sh.Vp, c == d->N ? " ; combine" : "");
   char* base = static_cast<char*>(ws);
-  float* logits = reinterpret_cast<float*>(base);
+  float* chunks = reinterpret_cast<float*>(base);
+  const int64_t astride = (int64_t)c * sh.cps * T;
   float* m = reinterpret_cast<float*>(base + sh.m_off);
   float* sm = reinterpret_cast<float*>(base + sh.s_off);
   float* z = reinterpret_cast<float*>(base + sh.z_off);
 
-  // logits of every shard in range (X shared: one launch)
-  const tp::GemmParams g = gemm(d->X, H, 0, static_cast<const bf16_t*>(d->E) + (size_t)i0 * Vs * H, H, Vs * H,
-                                logits, Vs, T * Vs, T, Vs, H, c);
-  TP_TRY(hip_status(launch("vocab_logits_gemm", TP_BF16, g, tp::EPI_PARTIAL, s), "vocab_logits_gemm"));
+  // logits of every shard in range (X shared: one launch), reduced in the
+  // epilogue to per-chunk statistics; no logit is stored
+  tp::GemmParams g = gemm(d->X, H, 0, static_cast<const bf16_t*>(d->E) + (size_t)i0 * Vs * H, H, Vs * H, nullptr,
+                          Vs, 0, T, Vs, H, c);
+  g.ce.labels = d->labels;
+  g.ce.stats = chunks;
+  g.ce.astride = astride;
+  g.ce.V = d->V;
+  g.ce.shard0 = i0;
+  g.ce.cps = sh.cps;
+  TP_TRY(hip_status(launch("vocab_logits_gemm", TP_BF16, g, tp::EPI_CE_STATS, s), "vocab_logits_gemm"));
 
-  tp::CeStatsParams st{};
-  st.logits = logits;
-  st.sL = T * Vs;
-  st.ldl = Vs;
-  st.labels = d->labels;
-  st.m = m;
-  st.s = sm;
-  st.z = z;
-  st.T = T;
-  st.V = d->V;
-  st.Vs = Vs;
-  st.shard0 = i0;
-  st.shards = c;
+  tp::CeFoldParams fp{};
+  fp.stats = chunks;
+  fp.astride = astride;
+  fp.T = T;
+  fp.m = m;
+  fp.s = sm;
+  fp.z = z;
+  fp.shard0 = i0;
+  fp.shards = c;
+  fp.cps = sh.cps;
   {
-    KernelTimer kt("vocab_ce_stats", s);
-    const hipError_t e = tp::launch_ce_stats(st, s);
+    KernelTimer kt("vocab_ce_fold", s);
+    const hipError_t e = tp::launch_ce_fold(fp, s);
     kt.stop();
-    TP_TRY(hip_status(e, "vocab_ce_stats"));
+    TP_TRY(hip_status(e, "vocab_ce_fold"));
   }
   if (c < d->N) return ok();
 

@@ -74,6 +74,41 @@ __device__ __forceinline__ float silu_bf16out(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
+// Running (max, sum of exp(x - max)) pairs of the cross-entropy statistics.
+// A pair with max = -inf holds nothing (sum 0); the side that holds the new
+// max keeps its sum unscaled, so -inf never meets -inf in an exponential.
+struct MaxSum {
+  float m, s;
+};
+
+__device__ __forceinline__ MaxSum ms_merge(MaxSum a, MaxSum b) {
+  const float mx = fmaxf(a.m, b.m);
+  const float sa = a.m == mx ? a.s : a.s * __expf(a.m - mx);
+  const float sb = b.m == mx ? b.s : b.s * __expf(b.m - mx);
+  return {mx, sa + sb};
+}
+
+// Value of another lane of the same 16-lane DPP row (CTRL: a DPP control --
+// quad_perm, row_half_mirror, row_mirror -- that stays inside the row).
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Reduction over each 16-lane row: lanes xor 1, then xor 2 (quad_perm
+// [1,0,3,2] and [2,3,0,1]) give every lane its quad's value; the half-row
+// mirror (lane i <-> 7-i) joins the two quads of each half, the row mirror
+// (i <-> 15-i) the two halves.  Every lane of the row ends with the result;
+// the order of the operations is fixed.
+template <class Op>
+__device__ __forceinline__ float row16_reduce(float x, Op op) {
+  x = op(x, dpp_row<0xB1>(x));
+  x = op(x, dpp_row<0x4E>(x));
+  x = op(x, dpp_row<0x141>(x));
+  x = op(x, dpp_row<0x140>(x));
+  return x;
+}
+
 // fp32 -> bf16, IEEE round-to-nearest-even (the compiler emits gfx950's
 // v_cvt_pk_bf16_f32, which rounds to nearest even).
 __device__ __forceinline__ bf16 to_bf16(float x) { return static_cast<bf16>(x); }

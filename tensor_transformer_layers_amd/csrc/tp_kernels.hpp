@@ -32,6 +32,21 @@ enum Epilogue : int {
   EPI_PARTIAL = 2, // C = acc                       out fp32 (row partial)
   EPI_SWIGLU = 3,  // C = SiLU(acc_gate) * acc_up   out bf16
   EPI_GELU_BWD = 4,  // C = acc * GELU'(Z), Z = aux   out bf16 (bf16 path only)
+  EPI_CE_STATS = 5,  // no C: per (row, 64-column chunk) cross-entropy statistics of the logits acc
+};
+
+// EPI_CE_STATS: problem z of the batch is vocab shard ce_shard0 + z, whose
+// column n is vocab id (ce_shard0 + z)*N + n; ids >= ce_V are padding.  For
+// every token row m and 64-column chunk k of the shard (k < ce_cps), the
+// epilogue writes, at index (z*ce_cps + k)*M + m of three arrays ce_stats,
+// ce_stats + ce_astride, ce_stats + 2*ce_astride: the chunk's max logit
+// (-inf if it holds no real id), the sum of exp(logit - max), and the
+// logit of ce_labels[m] if the chunk holds that id (else 0).
+struct CeEpilogue {
+  const int32_t* labels;
+  float* stats;
+  int64_t astride, V;
+  int shard0, cps;
 };
 
 // C[M x N] = A[M x K] * B[N x K]^T, batched over `batch` problems whose
@@ -54,6 +69,7 @@ struct GemmParams {
   int M, N, K;
   int batch;
   int xcd_per_problem;  // nonzero: batch % 8 == 0, each problem runs whole on one XCD
+  CeEpilogue ce;        // EPI_CE_STATS only
 };
 
 hipError_t launch_gemm_bf16(const GemmParams& p, Epilogue epi, hipStream_t s);
@@ -151,20 +167,17 @@ struct RowSumParams {
 };
 hipError_t launch_rowsum(const RowSumParams& p, hipStream_t s);
 
-// Vocab-parallel cross-entropy (vocab.hip).  Shard s of the launch is global
-// shard shard0 + s, owning vocab ids [(shard0+s)*Vs, (shard0+s+1)*Vs); ids
-// >= V are padding.  Its logits row t is at logits + s*sL + t*ldl (fp32).
-// Statistics go to slot (shard0+s)*T + t of m (max), s (sum of exp(l - max))
-// and z (the label's logit, 0 when the shard does not own the label).
-struct CeStatsParams {
-  const float* logits;
-  int64_t sL, ldl;
-  const int32_t* labels;
+// Vocab-parallel cross-entropy (vocab.hip).
+// Folds the per-chunk statistics of the GEMM epilogue (layout of CeEpilogue,
+// shards local to the launch) into the per-shard ones, chunk order, slot
+// (shard0 + s)*T + t of m, s, z.
+struct CeFoldParams {
+  const float* stats;
+  int64_t astride, T;
   float *m, *s, *z;
-  int64_t T, V, Vs;
-  int shard0, shards;
+  int shard0, shards, cps;
 };
-hipError_t launch_ce_stats(const CeStatsParams& p, hipStream_t s);
+hipError_t launch_ce_fold(const CeFoldParams& p, hipStream_t s);
 
 // loss[t] = log S + M - target from the N shards' statistics (slots i*T + t).
 struct CeCombineParams {

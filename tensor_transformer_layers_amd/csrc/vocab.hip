@@ -1,8 +1,8 @@
-// Vocab-parallel cross-entropy after the output head (the logits of each
-// shard's vocab partition come from the GEMM kernel):
-//   ce_stats_kernel    per (shard, token): max, sum of exp(l - max) over the
-//                      shard's real vocab entries, and the label's logit when
-//                      the shard owns the label
+// Vocab-parallel cross-entropy after the output head.  The logits never
+// reach memory: the GEMM's EPI_CE_STATS epilogue reduces each shard's logits
+// to statistics per (token, 64-column chunk) -- max, sum of exp(l - max), and
+// the label's logit when the chunk holds the label.  Then:
+//   ce_fold_kernel     per (shard, token): the fold of its chunks, in order
 //   ce_combine_kernel  per token: the fold over shards in shard order,
 //                      loss = log S + M - target
 //   ce_mean_kernel     the mean over tokens, in a fixed order
@@ -10,8 +10,7 @@
 // vocab partition's logits and its part of the loss, an all-reduce combines
 // them, and the vocab padding is left out of the loss.
 //
-// All three are deterministic (fixed orders, no atomics).  ce_stats_kernel is
-// HBM-bound (each fp32 logit read once, one exponential per logit).
+// All are deterministic (fixed orders, no atomics).
 #include <math.h>
 
 #include "tp_device.hpp"
@@ -21,60 +20,27 @@ namespace tp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWavesPerBlock = kThreads / kWave;
 
-// Running (max, sum of exp(x - max)) pairs.  A pair with max = -inf holds
-// nothing (sum 0); the scale of a side is 1 when it holds the new max, so
-// -inf never meets -inf in an exponential.
-struct MaxSum {
-  float m, s;
-};
-
-__device__ __forceinline__ MaxSum ms_merge(MaxSum a, MaxSum b) {
-  const float mx = fmaxf(a.m, b.m);
-  const float sa = a.m == mx ? a.s : a.s * __expf(a.m - mx);
-  const float sb = b.m == mx ? b.s : b.s * __expf(b.m - mx);
-  return {mx, sa + sb};
-}
-
-__device__ __forceinline__ MaxSum ms_add(MaxSum a, float x) {
-  if (x > a.m) return {x, a.s * __expf(a.m - x) + 1.0f};  // a.m = -inf: a.s = 0
-  return {a.m, a.s + __expf(x - a.m)};
-}
-
-// One wave per (shard, token) row of logits.  Lane l takes the 16-byte
-// pieces l, l + 64, ... of the row's real entries in order, then an xor
-// butterfly merges the lanes.
-__global__ __launch_bounds__(kThreads) void ce_stats_kernel(CeStatsParams p) {
-  const int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (row >= (int64_t)p.shards * p.T) return;  // whole waves leave together
-  const int lane = lane_id();
-  const int s = (int)(row / p.T);
-  const int64_t t = row - (int64_t)s * p.T;
-  const int64_t base = (int64_t)(p.shard0 + s) * p.Vs;  // first vocab id of the shard
-  const int64_t valid = min((int64_t)p.Vs, max((int64_t)0, p.V - base));
-  const float* const L = p.logits + (int64_t)s * p.sL + t * p.ldl;
+// One thread per (shard, token): the fold of the shard's 64-column chunk
+// statistics in chunk order (consecutive threads read consecutive tokens).
+__global__ __launch_bounds__(kThreads) void ce_fold_kernel(CeFoldParams p) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (int64_t)p.shards * p.T) return;
+  const int s = (int)(i / p.T);
+  const int64_t t = i - (int64_t)s * p.T;
+  const float* const m = p.stats + (int64_t)s * p.cps * p.T + t;
   MaxSum acc = {-INFINITY, 0.0f};
-  const int64_t full4 = valid / 4;
-  for (int64_t q = lane; q < full4; q += kWave) {
-    const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(L + 4 * q));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc = ms_add(acc, v[e]);
+  float z = 0.0f;
+#pragma unroll 4
+  for (int k = 0; k < p.cps; ++k) {
+    const int64_t o = (int64_t)k * p.T;
+    acc = ms_merge(acc, {m[o], m[o + p.astride]});
+    z += m[o + 2 * p.astride];
   }
-  for (int64_t c = 4 * full4 + lane; c < valid; c += kWave) acc = ms_add(acc, L[c]);
-#pragma unroll
-  for (int o = kWave / 2; o >= 1; o >>= 1) {
-    const MaxSum other = {__shfl_xor(acc.m, o), __shfl_xor(acc.s, o)};
-    acc = ms_merge(acc, other);
-  }
-  if (lane == 0) {
-    const int64_t y = (int64_t)p.labels[t] - base;
-    const float z = (y >= 0 && y < valid) ? L[y] : 0.0f;
-    const int64_t slot = (int64_t)(p.shard0 + s) * p.T + t;
-    p.m[slot] = acc.m;
-    p.s[slot] = acc.s;
-    p.z[slot] = z;
-  }
+  const int64_t slot = (int64_t)(p.shard0 + s) * p.T + t;
+  p.m[slot] = acc.m;
+  p.s[slot] = acc.s;
+  p.z[slot] = z;
 }
 
 // One thread per token: the fold over the N shards' statistics in order.
@@ -108,12 +74,11 @@ __global__ __launch_bounds__(kThreads) void ce_mean_kernel(const float* loss, in
 
 }  // namespace
 
-hipError_t launch_ce_stats(const CeStatsParams& p, hipStream_t s) {
-  const int64_t rows = (int64_t)p.shards * p.T;
-  const int64_t grid = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
+hipError_t launch_ce_fold(const CeFoldParams& p, hipStream_t s) {
+  const int64_t grid = ((int64_t)p.shards * p.T + kThreads - 1) / kThreads;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  launch_kernel(ce_stats_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  launch_kernel(ce_fold_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

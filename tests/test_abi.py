@@ -300,10 +300,10 @@ def test_vocab_padding_matches_oracle(L):
 
 def test_vocab_ce_workspace_size_is_host_only(L):
     T, N = 256, 8
-    Vs = 128  # ceil(1000 / 8) = 125 -> 128
+    cps = 2  # Vs = ceil(1000 / 8) = 125 -> 128 columns: two 64-column chunks
     align = lambda x: (x + 255) // 256 * 256
-    assert tp.tp_vocab_ce_workspace_size(_vce()) == align(N * T * Vs * 4) + 3 * align(N * T * 4)
-    assert tp.tp_vocab_ce_workspace_size(_vce(shard_count=1, loss=None)) == align(T * Vs * 4) + 3 * align(N * T * 4)
+    assert tp.tp_vocab_ce_workspace_size(_vce()) == align(3 * N * cps * T * 4) + 3 * align(N * T * 4)
+    assert tp.tp_vocab_ce_workspace_size(_vce(shard_count=1, loss=None)) == align(3 * cps * T * 4) + 3 * align(N * T * 4)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
