@@ -79,3 +79,26 @@ def mlp_gelu_backward_sample(X, A, a, B, dY, rows, feats):
     dZf = (dY64 @ B64[:, feats]) * O.gelu_grad(Zf)
     return {"dX": dZr @ A64, "dA": dZf.T @ X64, "da": dZf.sum(axis=0),
             "dB": dY64.T @ O.gelu(Zf), "db": dY64.sum(axis=0)}
+
+
+def mlp_swiglu_backward(X, Wg, Wu, Wd, dY):
+    """SwiGLU backward on storage-layout weights (Wg, Wu [I x H], Wd [H x I]);
+    gradients in the same layout."""
+    g = O.mlp_swiglu_backward(X, Wg.T, Wu.T, Wd.T, dY)
+    return {"dX": g["dX"], "dWg": g["dWg"].T, "dWu": g["dWu"].T, "dWd": g["dWd"].T, "db": g["db"]}
+
+
+def mlp_swiglu_backward_sample(X, Wg, Wu, Wd, dY, rows, feats):
+    """Sampled entries (storage layout): dX[rows, :]; dWg[feats, :],
+    dWu[feats, :] and dWd[:, feats] for intermediate features ``feats``."""
+    X64, dY64 = np.asarray(X, dtype=np.float64), np.asarray(dY, dtype=np.float64)
+    Wg64, Wu64, Wd64 = (np.asarray(a, dtype=np.float64) for a in (Wg, Wu, Wd))
+    rows, feats = np.asarray(rows), np.asarray(feats)
+    Gr, Ur = X64[rows] @ Wg64.T, X64[rows] @ Wu64.T
+    dHr = dY64[rows] @ Wd64
+    dGr, dUr = dHr * Ur * O.silu_grad(Gr), dHr * O.silu(Gr)
+    Gf, Uf = X64 @ Wg64[feats].T, X64 @ Wu64[feats].T
+    dHf = dY64 @ Wd64[:, feats]
+    dGf, dUf = dHf * Uf * O.silu_grad(Gf), dHf * O.silu(Gf)
+    return {"dX": dGr @ Wg64 + dUr @ Wu64, "dWg": dGf.T @ X64, "dWu": dUf.T @ X64,
+            "dWd": dY64.T @ (O.silu(Gf) * Uf), "db": dY64.sum(axis=0)}

@@ -44,6 +44,7 @@ __all__ = [
     "rmsnorm", "seq_slices", "all_gather_rows", "sp_entry", "rmsnorm_hidden_split",
     "gelu_grad", "mlp_backward", "mlp_backward_sharded",
     "padded_vocab", "cross_entropy", "lm_head_ce", "vocab_parallel_ce",
+    "silu_grad", "mlp_swiglu_backward", "mlp_swiglu_backward_sharded",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -436,6 +437,55 @@ def mlp_backward_sharded(X, A, a, B, dY, N, act="gelu"):
     return {"dX": _fold(parts), "dA": np.concatenate(dA, axis=1),
             "da": np.concatenate(da), "dB": np.concatenate(dB, axis=0),
             "db": dY.sum(axis=0), "dX_parts": parts}
+
+
+def silu_grad(g):
+    """Derivative of SiLU: d/dg [g sigmoid(g)] = sigmoid(g) (1 + g (1 - sigmoid(g)))."""
+    g = _f64(g)
+    sg = expit(g)
+    return sg * (1.0 + g * (1.0 - sg))
+
+
+def mlp_swiglu_backward(X, Wg, Wu, Wd, dY):
+    """Gradients of the unsharded SwiGLU MLP Y = (SiLU(X Wg) * (X Wu)) Wd for
+    an upstream gradient dY (no biases):
+
+        G = X Wg, U = X Wu, Hd = SiLU(G) * U
+        dWd = Hd^T dY,  dH = dY Wd^T
+        dG = dH * U * SiLU'(G),  dU = dH * SiLU(G)
+        dWg = X^T dG,  dWu = X^T dU,  dX = dG Wg^T + dU Wu^T
+
+    Math layout (Wg, Wu [H x I], Wd [I x H])."""
+    X, Wg, Wu, Wd, dY = (_f64(a) for a in (X, Wg, Wu, Wd, dY))
+    G, U = X @ Wg, X @ Wu
+    dH = dY @ Wd.T
+    dG = dH * U * silu_grad(G)
+    dU = dH * silu(G)
+    return {"dX": dG @ Wg.T + dU @ Wu.T, "dWg": X.T @ dG, "dWu": X.T @ dU, "dWd": (silu(G) * U).T @ dY,
+            "db": dY.sum(axis=0)}
+
+
+def mlp_swiglu_backward_sharded(X, fused_blocks, Wd, dY, N):
+    """The SwiGLU backward over N shards from the per-shard fused [gate | up]
+    blocks: shard i forms dH_i = dY Wd_i^T, the gradient of its block
+    dZ_i = [dG_i | dU_i], the block's weight gradient X^T dZ_i, its rows of
+    dWd, and the input-gradient partial dZ_i F_i^T; the partials are summed
+    in shard order (the column layer's backward all-reduce, [Scratch] 4)."""
+    X, dY = _f64(X), _f64(dY)
+    Wds = row_shards(Wd, N)
+    dF, dWd, parts = [], [], []
+    for Fi, Wdi in zip(fused_blocks, Wds):
+        Fi = _f64(Fi)
+        Z = X @ Fi
+        s = Z.shape[1] // 2
+        G, U = Z[:, :s], Z[:, s:]
+        dH = dY @ Wdi.T
+        dZ = np.concatenate([dH * U * silu_grad(G), dH * silu(G)], axis=1)
+        dF.append(X.T @ dZ)
+        dWd.append((silu(G) * U).T @ dY)
+        parts.append(dZ @ Fi.T)
+    return {"dX": _fold(parts), "dF": dF, "dWd": np.concatenate(dWd, axis=0), "db": dY.sum(axis=0),
+            "dX_parts": parts}
 
 
 # --------------------------------------------------------------------------

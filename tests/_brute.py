@@ -89,3 +89,4 @@ def cross_entropy(logits, labels):
         s = sum(math.exp(v - m) for v in row)
         out.append(math.log(s) + m - row[y])
     return out
+

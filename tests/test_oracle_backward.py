@@ -198,3 +198,100 @@ def test_planted_backward_mistakes_are_caught(kind):
     fd = _fd_grads(X, A, a, B, b, dY)
     assert _matches_fd(O.mlp_backward_sharded(X, A, a, B, dY, 2), fd)
     assert not _matches_fd(_mutant(kind, X, A, a, B, dY), fd)
+
+
+# ------------------------------------------------------------------ SwiGLU
+def _swiglu_loss(dY, X, Wg, Wu, Wd):
+    Y = brute.mlp_swiglu(X.tolist(), Wg.tolist(), Wu.tolist(), Wd.tolist())
+    return sum(dy * y for dr, yr in zip(dY.tolist(), Y) for dy, y in zip(dr, yr))
+
+
+def _swiglu_fd(X, Wg, Wu, Wd, dY, h=1e-5):
+    args = {"X": X, "Wg": Wg, "Wu": Wu, "Wd": Wd}
+    out = {}
+    for name, arr in args.items():
+        g = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + h
+            lp = _swiglu_loss(dY, **args)
+            arr[idx] = keep - h
+            lm = _swiglu_loss(dY, **args)
+            arr[idx] = keep
+            g[idx] = (lp - lm) / (2 * h)
+        out["d" + name] = g
+    return out
+
+
+def _swiglu_tiny(seed, T=3, H=4, I=6):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((T, H)), rng.standard_normal((H, I)) * 0.7, rng.standard_normal((H, I)) * 0.7,
+            rng.standard_normal((I, H)) * 0.7, rng.standard_normal((T, H)))
+
+
+def test_silu_grad_matches_finite_differences_of_brute_silu():
+    h = 1e-5
+    for g in np.linspace(-8.0, 8.0, 81):
+        fd = (brute.silu(g + h) - brute.silu(g - h)) / (2 * h)
+        assert abs(O.silu_grad(g) - fd) <= 1e-9
+    assert O.silu_grad(0.0) == 0.5
+    # SiLU(g) - SiLU(-g) = g  =>  SiLU'(g) + SiLU'(-g) = 1
+    z = np.linspace(-10, 10, 101)
+    assert np.max(np.abs(O.silu_grad(z) + O.silu_grad(-z) - 1.0)) <= 1e-15
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_swiglu_backward_matches_finite_differences(seed):
+    X, Wg, Wu, Wd, dY = _swiglu_tiny(seed)
+    fd = _swiglu_fd(X, Wg, Wu, Wd, dY)
+    g = O.mlp_swiglu_backward(X, Wg, Wu, Wd, dY)
+    for k in ("dX", "dWg", "dWu", "dWd"):
+        assert _close(g[k], fd[k], 1e-7), k
+
+
+def test_swiglu_sharded_backward_equals_unsharded():
+    X, Wg, Wu, Wd, dY = _swiglu_tiny(2, T=5, H=6, I=8)
+    full = O.mlp_swiglu_backward(X, Wg, Wu, Wd, dY)
+    for N in (1, 2, 4):
+        blocks = O.swiglu_fused_blocks(Wg, Wu, N)
+        sh = O.mlp_swiglu_backward_sharded(X, blocks, Wd, dY, N)
+        s = Wg.shape[1] // N
+        for i in range(N):  # block i's gradient is [dWg columns i | dWu columns i]
+            want = np.concatenate([full["dWg"][:, i * s:(i + 1) * s], full["dWu"][:, i * s:(i + 1) * s]], axis=1)
+            assert _close(sh["dF"][i], want, 1e-12)
+        assert _close(sh["dX"], full["dX"], 1e-12) and _close(sh["dWd"], full["dWd"], 1e-12)
+
+
+def test_swiglu_storage_and_sampled_forms():
+    X, Wg, Wu, Wd, dY = _swiglu_tiny(3, T=12, H=8, I=10)
+    full = O.mlp_swiglu_backward(X, Wg, Wu, Wd, dY)
+    st = R.mlp_swiglu_backward(X, Wg.T.copy(), Wu.T.copy(), Wd.T.copy(), dY)
+    assert _close(st["dWg"], full["dWg"].T, 1e-14) and _close(st["dWd"], full["dWd"].T, 1e-14)
+    rows, feats = [0, 7, 11], [0, 3, 9]
+    sm = R.mlp_swiglu_backward_sample(X, Wg.T.copy(), Wu.T.copy(), Wd.T.copy(), dY, rows, feats)
+    assert _close(sm["dX"], st["dX"][rows], 1e-12)
+    assert _close(sm["dWg"], st["dWg"][feats], 1e-12) and _close(sm["dWu"], st["dWu"][feats], 1e-12)
+    assert _close(sm["dWd"], st["dWd"][:, feats], 1e-12)
+
+
+@pytest.mark.parametrize("kind", ["gate_slope_without_up", "up_gradient_with_slope", "naive_block_split"])
+def test_planted_swiglu_backward_mistakes_are_caught(kind):
+    X, Wg, Wu, Wd, dY = _swiglu_tiny(4)
+    fd = _swiglu_fd(X, Wg, Wu, Wd, dY)
+    G, U = X @ Wg, X @ Wu
+    dH = dY @ Wd.T
+    if kind == "gate_slope_without_up":
+        dG, dU = dH * O.silu_grad(G), dH * O.silu(G)
+        got = {"dWg": X.T @ dG}
+        key = "dWg"
+    elif kind == "up_gradient_with_slope":
+        dU = dH * O.silu_grad(G)
+        got = {"dWu": X.T @ dU}
+        key = "dWu"
+    else:  # splitting [Wg | Wu] into N column blocks hands gate-only columns to shard 0
+        N = 2
+        naive = [np.concatenate([Wg, Wu], axis=1)[:, i * Wg.shape[1]:(i + 1) * Wg.shape[1]] for i in range(N)]
+        sh = O.mlp_swiglu_backward_sharded(X, naive, Wd, dY, N)
+        got = {"dX": sh["dX"]}
+        key = "dX"
+    assert not _close(got[key], fd[key], 1e-3)
