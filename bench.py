@@ -111,35 +111,43 @@ def backward_splits(T, Fc, H):
 
 
 def backward_flops(w, c):
-    """Algorithmic FLOP of the MLP pair's backward over c shards: dH, dX, dA
-    and dB, each 2*T*H*(c*Fs).  The recomputed column product (another
-    2*T*H*c*Fs) is work this implementation adds and is not counted."""
-    return 8.0 * w.T * w.H * w.Fs * c
+    """Algorithmic FLOP of the MLP pair's backward over c shards: GELU: dH,
+    dX, dA and dB, each 2*T*H*(c*Fs); SwiGLU: dH 2*T*H*Fc, dX and the fused
+    dA 2*T*H*(2 Fc) each, dB 2*T*H*Fc.  The recomputed column product is work
+    this implementation adds and is not counted."""
+    Fc = w.Fs * c
+    if w.kind == "mlp_swiglu":
+        return 12.0 * w.T * w.H * Fc
+    return 8.0 * w.T * w.H * Fc
 
 
 def backward_kernel_work(w, name, c):
     """Algorithmic (flops, bytes) of one launch of a backward kernel over c
-    shards (bf16 operands, fp32 weight gradients)."""
-    T, H, N = w.T, w.H, w.N
+    shards (bf16 operands, fp32 weight gradients).  Fz = the columns of Z:
+    Fc, or 2*Fc ([gate | up]) for SwiGLU."""
+    T, H = w.T, w.H
     Fc = w.Fs * c
-    S = backward_splits(T, Fc, H)
+    swi = w.kind == "mlp_swiglu"
+    Fz = 2 * Fc if swi else Fc
+    S = backward_splits(T, Fz, H)
     bias = w.sigma_bias is not None
     if name == "bwd_recompute_gemm":
-        return 2.0 * T * H * Fc, 2 * (T * H + Fc * H + T * Fc) + (2 * Fc if bias else 0)
-    if name == "bwd_dz_gemm":  # reads the stored pre-activation beside the accumulators
-        return 2.0 * T * H * Fc, 2 * (T * H + Fc * H + 2 * T * Fc)
+        return 2.0 * T * H * Fz, 2 * (T * H + Fz * H + T * Fz) + (2 * Fc if bias else 0)
+    if name == "bwd_dz_gemm":  # reads the stored pre-activation beside the accumulators (SwiGLU: also writes H)
+        return 2.0 * T * H * Fc, 2 * (T * H + Fc * H + 2 * T * Fz + (T * Fc if swi else 0))
     if name == "bwd_dx_gemm":
-        return 2.0 * T * Fc * H, 2 * (T * Fc + H * Fc) + 4 * c * T * H
-    if name in ("bwd_da_gemm", "bwd_db_gemm"):
+        return 2.0 * T * Fz * H, 2 * (T * Fz + H * Fz) + 4 * c * T * H
+    if name == "bwd_da_gemm":
+        return 2.0 * T * Fz * H, 2 * (T * Fz + T * H) + 4 * S * Fz * H
+    if name == "bwd_db_gemm":
         return 2.0 * T * Fc * H, 2 * (T * Fc + T * H) + 4 * S * Fc * H
     if name == "bwd_transpose":  # X, dY, A, B, act(Z), dZ: each read once and written once
-        return 0.0, 2 * 2 * (2 * T * H + 2 * Fc * H + 2 * T * Fc) / 6
-    if name == "bwd_bias_rowsum":  # da (when the workload has biases) and db
-        launches = [(Fc, T)] if bias else []
-        launches.append((H, T))
-        return 0.0, sum(2 * r * t + 4 * r for r, t in launches) / len(launches)
+        return 0.0, 2 * 2 * (2 * T * H + Fz * H + Fc * H + T * Fc + T * Fz) / 6
+    if name == "bwd_bias_rowsum":  # da (when the workload has a column bias) and db (row bias)
+        launches = ([(Fc, T)] if bias and not swi else []) + ([(H, T)] if bias else [])
+        return 0.0, sum(2 * r * t + 4 * r for r, t in launches) / max(1, len(launches))
     if name == "bwd_splitk_reduce":  # dA and dB
-        return 0.0, 4 * S * Fc * H + 4 * Fc * H
+        return 0.0, (4 * S * Fz * H + 4 * Fz * H + 4 * S * Fc * H + 4 * Fc * H) / 2
     raise KeyError(name)
 
 
@@ -200,11 +208,12 @@ KERNEL_SYMBOL = {
 def backward_launch_order(w):
     """Kernels one backward step (all shards) launches, in order (the
     sequence of tp_mlp_backward)."""
-    split = backward_splits(w.T, w.F, w.H) > 1
+    split = backward_splits(w.T, 2 * w.F if w.kind == "mlp_swiglu" else w.F, w.H) > 1
     order = ["bwd_transpose"] * 4 + ["bwd_recompute_gemm", "bwd_dz_gemm"] + ["bwd_transpose"] * 2
     order += ["bwd_dx_gemm", "bwd_da_gemm"] + (["bwd_splitk_reduce"] if split else [])
     order += ["bwd_db_gemm"] + (["bwd_splitk_reduce"] if split else [])
-    order += ["bwd_bias_rowsum"] * (2 if w.sigma_bias is not None else 1)
+    bias = w.sigma_bias is not None
+    order += ["bwd_bias_rowsum"] * ((1 if bias and w.kind == "mlp_gelu" else 0) + (1 if bias else 0))
     return order + ["reduce_partials"]
 
 
@@ -366,7 +375,10 @@ def cpu_baseline_backward(w, host, dY, seconds):
     while time.perf_counter() - t0 < seconds:
         start = done % w.T
         rows = np.sort(order[start:start + chunk])
-        R.mlp_gelu_backward(host["X"][rows], host["A"], host["a"], host["B"], dY[rows])
+        if w.kind == "mlp_swiglu":
+            R.mlp_swiglu_backward(host["X"][rows], host["Wg"], host["Wu"], host["Wd"], dY[rows])
+        else:
+            R.mlp_gelu_backward(host["X"][rows], host["A"], host["a"], host["B"], dY[rows])
         flops += len(rows) * backward_flops(w, w.N) / w.T
         done += len(rows)
     el = time.perf_counter() - t0
@@ -440,8 +452,9 @@ def main():
         print("bench.py: --sp-entry needs an MLP workload with a reduce-scatter (--config 5) and --share layer",
               file=sys.stderr, flush=True)
         sys.exit(2)
-    if args.backward and (w.kind != "mlp_gelu" or w.dtype != "bf16" or args.share != "layer" or args.sp_entry):
-        print("bench.py: --backward needs a bf16 GELU MLP workload (--config 2 or 5) and --share layer",
+    if args.backward and (w.kind not in ("mlp_gelu", "mlp_swiglu") or w.dtype != "bf16" or args.share != "layer"
+                          or args.sp_entry):
+        print("bench.py: --backward needs a bf16 MLP workload (--config 2, 3 or 5) and --share layer",
               file=sys.stderr, flush=True)
         sys.exit(2)
     log(f"workload {w.name}: generating seeded inputs")
@@ -595,8 +608,10 @@ def main():
                if args.sp_entry else {}),
             **({"overlap_chunks": args.overlap} if args.overlap else {}),
             **({"pass": "backward", "upstream_gradient": inputs.GRAD_RECIPE,
-                "flop_counted": "8*T*H*F (dH, dX, dA, dB); the recomputed column product is extra and not counted",
-                "split_k": backward_splits(w.T, w.F, w.H)} if args.backward else {}),
+                "flop_counted": ("12*T*H*I (dH, dX, fused dA, dB)" if w.kind == "mlp_swiglu" else
+                                 "8*T*H*F (dH, dX, dA, dB)") + "; the recomputed column product is extra and not counted",
+                "split_k": backward_splits(w.T, 2 * w.F if w.kind == "mlp_swiglu" else w.F, w.H)}
+               if args.backward else {}),
         },
         "pct_of_bf16_mfma_peak": round(100 * value * 1e12 / PEAK_BF16, 2) if w.dtype == "bf16" else None,
         "roofline": roof,

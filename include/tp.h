@@ -226,19 +226,24 @@ tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t 
  * come back in the same layout.  Weight and bias gradients are fp32.
  * Z_i and dZ_i are rounded to bf16 once (as a bf16 forward would store its
  * linear outputs), act(Z_i) is evaluated from the rounded Z_i.
+ * SwiGLU (blog post section 3.2): A holds the N fused blocks [2F/N x H] of the
+ * forward (gate rows, then up rows); Z_i = [G_i | U_i], dH_i = dY B_i,
+ * dZ_i = [dH_i U_i SiLU'(G_i) | dH_i SiLU(G_i)], dA comes back in the same
+ * fused-block layout ([2F x H]), dB_i = dY^T (SiLU(G_i) U_i); a and da must
+ * be NULL.
  */
 typedef struct {
   tp_dtype dt;     /* TP_BF16                                                   */
-  tp_act act;      /* TP_ACT_GELU or TP_ACT_NONE                                */
+  tp_act act;      /* TP_ACT_GELU, TP_ACT_NONE, or TP_ACT_SWIGLU (see below)    */
   int64_t T, H, F; /* T, H, F/N multiples of 8                                  */
   int N, shard_begin, shard_count;
   const void* X;   /* [T x H] bf16                                              */
-  const void* A;   /* [F x H] bf16                                              */
+  const void* A;   /* [F x H] bf16 ([2F x H] fused blocks for SwiGLU)           */
   const void* a;   /* [F] bf16 or NULL                                          */
   const void* B;   /* [H x F] bf16                                              */
   const void* dY;  /* [T x H] bf16                                              */
   void* dX;        /* [T x H] bf16, written when shard_count == N, else unused  */
-  float* dA;       /* [F x H]: rows of the shard range written                  */
+  float* dA;       /* [F x H] ([2F x H] SwiGLU): rows of the shard range written */
   float* da;       /* [F] (entries of the range) or NULL to skip                */
   float* dB;       /* [H x F]: columns of the shard range written               */
   float* db;       /* [H] or NULL to skip                                       */

@@ -515,6 +515,60 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
 #pragma unroll
         for (int j = 0; j < ZB; ++j) zc[j] = zn[j];
       }
+    } else if constexpr (C::EPI == EPI_SWIGLU_BWD) {
+      // SwiGLU backward from dH (the accumulators) and the stored gate G and
+      // up U of the same token and feature:
+      //   dG = dH U SiLU'(G),  dU = dH SiLU(G),  H = SiLU(G) U
+      // with SiLU'(g) = s (1 + g (1 - s)), s = sigmoid(g) (hardware exp and
+      // reciprocal).  16 lanes per row, 4 features each.
+      const int c = lane & 15;
+      const int n = n0 + wn * C::WN + 64 * h + 4 * c;
+      const bf16* const zb = static_cast<const bf16*>(p.aux) + bz * p.sAux;
+      bf16* const cb = static_cast<bf16*>(p.C) + bz * p.sC;
+      bf16* const hb = static_cast<bf16*>(p.C2) + bz * p.sC2;
+#pragma unroll 4
+      for (int it = 0; it < C::WM / 4; ++it) {
+        const int r = it * 4 + (lane >> 4);
+        const int m = m0 + wm * C::WM + r;
+        const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
+        if (m < p.M && n < p.N) {
+          const bf16* zp = zb + (int64_t)m * p.ldaux + n;
+          bf16x4 g4 = {}, u4 = {};
+          const bool full = n + 3 < p.N;
+          if (full) {
+            g4 = *reinterpret_cast<const bf16x4*>(zp);
+            u4 = *reinterpret_cast<const bf16x4*>(zp + p.upOff);
+          } else {
+            for (int e = 0; e < 4 && n + e < p.N; ++e) {
+              g4[e] = zp[e];
+              u4[e] = zp[e + p.upOff];
+            }
+          }
+          bf16x4 og, ou, oh;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float g = static_cast<float>(g4[e]), u = static_cast<float>(u4[e]);
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+            const float si = g * sg;
+            og[e] = to_bf16(v[e] * u * (sg * fmaf(g, 1.0f - sg, 1.0f)));
+            ou[e] = to_bf16(v[e] * si);
+            oh[e] = to_bf16(si * u);
+          }
+          bf16* const dg = cb + (int64_t)m * p.ldc + n;
+          bf16* const hh = hb + (int64_t)m * p.ldc2 + n;
+          if (full) {
+            __builtin_nontemporal_store(og, reinterpret_cast<bf16x4*>(dg));
+            __builtin_nontemporal_store(ou, reinterpret_cast<bf16x4*>(dg + p.upOff));
+            __builtin_nontemporal_store(oh, reinterpret_cast<bf16x4*>(hh));
+          } else {
+            for (int e = 0; e < 4 && n + e < p.N; ++e) {
+              dg[e] = og[e];
+              dg[e + p.upOff] = ou[e];
+              hh[e] = oh[e];
+            }
+          }
+        }
+      }
     } else if constexpr (C::EPI == EPI_CE_STATS) {
       // Cross-entropy statistics of this phase's 64 logit columns per token
       // row (16 lanes per row, 4 logits each): the max over the row's real
@@ -559,7 +613,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
       const int c = lane & 15;
       const int n = n0 + wn * C::WN + 64 * h + 4 * c;
       float bias[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (C::EPI != EPI_PARTIAL && C::EPI != EPI_GELU_BWD && C::EPI != EPI_CE_STATS) {
+      if constexpr (C::EPI != EPI_PARTIAL && C::EPI != EPI_GELU_BWD && C::EPI != EPI_CE_STATS &&
+                    C::EPI != EPI_SWIGLU_BWD) {
         if (p.bias) {
           const bf16* bp = static_cast<const bf16*>(p.bias) + bz * p.sBias;
           for (int e = 0; e < 4; ++e) bias[e] = n + e < p.N ? static_cast<float>(bp[n + e]) : 0.0f;
@@ -732,6 +787,7 @@ hipError_t launch_gemm_bf16(const GemmParams& p, Epilogue epi, hipStream_t s) {
     case EPI_SWIGLU: return launch_bf16_epi<EPI_SWIGLU>(p, s);
     case EPI_GELU_BWD: return launch_bf16_epi<EPI_GELU_BWD>(p, s);
     case EPI_CE_STATS: return launch_bf16_epi<EPI_CE_STATS>(p, s);
+    case EPI_SWIGLU_BWD: return launch_bf16_epi<EPI_SWIGLU_BWD>(p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -365,14 +365,17 @@ tp_status validate_attn(const tp_attn_desc* d, AttnShape* sh) {
 // ------------------------------------------------------- MLP backward desc
 // Workspace (256-byte aligned pieces, bf16 unless noted), Fc = shard_count*Fs:
 //   P    N x [T x H] fp32   dX partials, slot i = shard i
-//   Z    [T x Fc] (ld zld)  recomputed pre-activation
-//   dZ   [T x Fc] (ld zld)
-//   XT, dYT [H x T];  HT, dZT [Fc x T];  AT [H x Fc];  BT [Fc x H]
-//   K    S x [Fc x H] fp32  split-K partials of the weight gradients
+//   Z    [T x Fz] (ld zld)  recomputed pre-activation (Fz = Fc, or 2*Fc for
+//                           SwiGLU: each shard's [gate | up] columns)
+//   dZ   [T x Fz] (ld zld)
+//   Hs   [T x Fc]           SwiGLU only: SiLU(gate)*up, written by the dZ epilogue
+//   XT, dYT [H x T];  HT [Fc x T];  dZT [Fz x T];  AT [H x Fz];  BT [Fc x H]
+//   K    S x [Fz x H] fp32  split-K partials of the weight gradients
 struct BwdShape {
   int64_t Fs, Fc, zld;
-  int splits;  // split-K factor of the token-axis contractions
-  size_t p_bytes, z_off, dz_off, xt_off, dyt_off, ht_off, dzt_off, at_off, bt_off, k_off, total;
+  int64_t Fz;   // columns of Z and dZ: Fc, or 2*Fc for SwiGLU ([gate | up] per shard)
+  int splits;   // split-K factor of the token-axis contractions
+  size_t p_bytes, z_off, dz_off, h_off, xt_off, dyt_off, ht_off, dzt_off, at_off, bt_off, k_off, total;
 };
 
 // Weight gradients contract over all T tokens into a small [Fc x H] output
@@ -399,8 +402,10 @@ tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
   if (!d) return fail(TP_ERR_NULL, "descriptor is NULL");
   TP_TRY(check_dtype(d->dt));
   if (d->dt != TP_BF16) return fail(TP_ERR_DTYPE, "backward path is bf16-only");
-  if (d->act != TP_ACT_GELU && d->act != TP_ACT_NONE)
-    return fail(TP_ERR_DTYPE, "backward activation %d: only GELU and NONE are built", (int)d->act);
+  if (d->act != TP_ACT_GELU && d->act != TP_ACT_NONE && d->act != TP_ACT_SWIGLU)
+    return fail(TP_ERR_DTYPE, "backward activation %d unknown", (int)d->act);
+  if (d->act == TP_ACT_SWIGLU && (d->a || d->da))
+    return fail(TP_ERR_SHAPE, "SwiGLU has no column bias: a and da must be NULL");
   if (d->T < 0 || d->H <= 0 || d->F <= 0 || d->N <= 0)
     return fail(TP_ERR_SHAPE, "T=%lld H=%lld F=%lld N=%d", (long long)d->T, (long long)d->H, (long long)d->F,
                 d->N);
@@ -412,20 +417,23 @@ tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
     return fail(TP_ERR_SHAPE, "shard range [%d, %d) outside [0, %d)", d->shard_begin,
                 d->shard_begin + d->shard_count, d->N);
   const int64_t Fs = d->F / d->N, Fc = Fs * d->shard_count;
+  const bool swiglu = d->act == TP_ACT_SWIGLU;
   *sh = BwdShape{};
   sh->Fs = Fs;
   sh->Fc = Fc;
-  sh->zld = Fc;
+  sh->Fz = swiglu ? 2 * Fc : Fc;
+  sh->zld = sh->Fz;
   sh->splits = 1;
   if (d->T == 0) return TP_OK;  // empty input: nothing to read, write or stage
   if (d->T % 8) return fail(TP_ERR_ALIGN, "T=%lld is not a multiple of 8", (long long)d->T);
   if (d->H % 8) return fail(TP_ERR_ALIGN, "hidden H=%lld is not a multiple of 8", (long long)d->H);
   if (Fs % 8) return fail(TP_ERR_ALIGN, "shard width F/N=%lld is not a multiple of 8", (long long)Fs);
   TP_TRY(check_matrix("X", d->X, d->T, d->H, d->H, 8));
-  TP_TRY(check_matrix("A", d->A, d->F, d->H, d->H, 8));
+  const int64_t a_rows = swiglu ? 2 * d->F : d->F;
+  TP_TRY(check_matrix("A", d->A, a_rows, d->H, d->H, 8));
   TP_TRY(check_matrix("B", d->B, d->H, d->F, d->F, 8));
   TP_TRY(check_matrix("dY", d->dY, d->T, d->H, d->H, 8));
-  TP_TRY(check_matrix("dA", d->dA, d->F, d->H, d->H, 4));
+  TP_TRY(check_matrix("dA", d->dA, a_rows, d->H, d->H, 4));
   TP_TRY(check_matrix("dB", d->dB, d->H, d->F, d->F, 4));
   if (d->a && !aligned16(d->a)) return fail(TP_ERR_ALIGN, "a is not 16-byte aligned");
   if (d->da && !aligned16(d->da)) return fail(TP_ERR_ALIGN, "da is not 16-byte aligned");
@@ -435,19 +443,20 @@ tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
     if (!aligned16(d->dX)) return fail(TP_ERR_ALIGN, "dX is not 16-byte aligned");
   }
   if (d->T > kIntMax || d->F > kIntMax) return fail(TP_ERR_SHAPE, "size exceeds 2^31-1");
-  const size_t T = (size_t)d->T, H = (size_t)d->H, fc = (size_t)Fc;
-  sh->splits = bwd_splits(d->T, Fc, d->H);
+  const size_t T = (size_t)d->T, H = (size_t)d->H, fc = (size_t)Fc, fz = (size_t)sh->Fz;
+  sh->splits = bwd_splits(d->T, sh->Fz, d->H);
   sh->p_bytes = align256((size_t)d->N * T * H * sizeof(float));
   sh->z_off = sh->p_bytes;
-  sh->dz_off = sh->z_off + align256(T * fc * 2);
-  sh->xt_off = sh->dz_off + align256(T * fc * 2);
+  sh->dz_off = sh->z_off + align256(T * fz * 2);
+  sh->h_off = sh->dz_off + align256(T * fz * 2);
+  sh->xt_off = sh->h_off + (swiglu ? align256(T * fc * 2) : 0);
   sh->dyt_off = sh->xt_off + align256(H * T * 2);
   sh->ht_off = sh->dyt_off + align256(H * T * 2);
   sh->dzt_off = sh->ht_off + align256(fc * T * 2);
-  sh->at_off = sh->dzt_off + align256(fc * T * 2);
-  sh->bt_off = sh->at_off + align256(H * fc * 2);
+  sh->at_off = sh->dzt_off + align256(fz * T * 2);
+  sh->bt_off = sh->at_off + align256(H * fz * 2);
   sh->k_off = sh->bt_off + align256(fc * H * 2);
-  sh->total = sh->k_off + (sh->splits > 1 ? align256((size_t)sh->splits * fc * H * sizeof(float)) : 0);
+  sh->total = sh->k_off + (sh->splits > 1 ? align256((size_t)sh->splits * fz * H * sizeof(float)) : 0);
   return TP_OK;
 }
 
@@ -772,9 +781,10 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
   if (d->T == 0) return ok();
   TP_TRY(check_ws(ws, ws_bytes, sh.total));
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t T = d->T, H = d->H, F = d->F, Fs = sh.Fs, Fc = sh.Fc;
+  const int64_t T = d->T, H = d->H, F = d->F, Fs = sh.Fs, Fc = sh.Fc, Fz = sh.Fz;
   const int c = d->shard_count, i0 = d->shard_begin, S = sh.splits;
-  const bool gelu = d->act == TP_ACT_GELU;
+  const bool gelu = d->act == TP_ACT_GELU, swiglu = d->act == TP_ACT_SWIGLU;
+  const int64_t zs = swiglu ? 2 * Fs : Fs;  // Z / dZ / A columns per shard
   if (log_enabled())
     fprintf(stderr, "[tp] mlp backward bf16 act=%d N=%d shards [%d,%d): T=%lld H=%lld Fs=%lld, split-K %d%s\n",
             (int)d->act, d->N, i0, i0 + c, (long long)T, (long long)H, (long long)Fs, S,
@@ -783,6 +793,7 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
   float* P = reinterpret_cast<float*>(base);
   bf16_t* Z = reinterpret_cast<bf16_t*>(base + sh.z_off);
   bf16_t* dZ = reinterpret_cast<bf16_t*>(base + sh.dz_off);
+  bf16_t* Hs = reinterpret_cast<bf16_t*>(base + sh.h_off);
   bf16_t* XT = reinterpret_cast<bf16_t*>(base + sh.xt_off);
   bf16_t* dYT = reinterpret_cast<bf16_t*>(base + sh.dyt_off);
   bf16_t* HT = reinterpret_cast<bf16_t*>(base + sh.ht_off);
@@ -790,7 +801,7 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
   bf16_t* AT = reinterpret_cast<bf16_t*>(base + sh.at_off);
   bf16_t* BT = reinterpret_cast<bf16_t*>(base + sh.bt_off);
   float* K = reinterpret_cast<float*>(base + sh.k_off);
-  const bf16_t* A_r = static_cast<const bf16_t*>(d->A) + (size_t)i0 * Fs * H;  // range rows of A
+  const bf16_t* A_r = static_cast<const bf16_t*>(d->A) + (size_t)i0 * zs * H;  // range rows of A
   const bf16_t* B_r = static_cast<const bf16_t*>(d->B) + (size_t)i0 * Fs;      // range columns of B
   const bf16_t* a_r = d->a ? static_cast<const bf16_t*>(d->a) + (size_t)i0 * Fs : nullptr;
 
@@ -809,7 +820,7 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
     kt.stop();
     return hip_status(e, name);
   };
-  // C[M x N] (+)= A[M x T] B[N x T]^T over the token axis, split-K when the
+  // C[M x N] = A[M x T] B[N x T]^T over the token axis, split-K when the
   // output is small; the splits' partials fold in split order.
   auto token_gemm = [&](const char* name, const void* Aop, const void* Bop, int64_t M, int64_t N, float* C,
                         int64_t ldc) -> tp_status {
@@ -840,27 +851,40 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
   // operands contiguous along each contraction
   TP_TRY(transpose("bwd_transpose", d->X, H, XT, T, T, H, false));    // XT  [H x T]
   TP_TRY(transpose("bwd_transpose", d->dY, H, dYT, T, T, H, false));  // dYT [H x T]
-  TP_TRY(transpose("bwd_transpose", A_r, H, AT, Fc, Fc, H, false));   // AT  [H x Fc]
+  TP_TRY(transpose("bwd_transpose", A_r, H, AT, Fz, Fz, H, false));   // AT  [H x Fz]
   TP_TRY(transpose("bwd_transpose", B_r, F, BT, H, H, Fc, false));    // BT  [Fc x H]
 
-  // Z = X A_r^T + a_r, the range's pre-activation (all shards side by side)
-  tp::GemmParams zg = gemm(d->X, H, 0, A_r, H, 0, Z, sh.zld, 0, T, Fc, H, 1);
+  // Z = X A_r^T (+ a_r), the range's pre-activation (all shards side by side)
+  tp::GemmParams zg = gemm(d->X, H, 0, A_r, H, 0, Z, sh.zld, 0, T, Fz, H, 1);
   zg.bias = a_r;
   TP_TRY(hip_status(launch("bwd_recompute_gemm", TP_BF16, zg, tp::EPI_STORE, s), "bwd_recompute_gemm"));
-  // dZ = (dY B_r) * act'(Z)
-  tp::GemmParams dg = gemm(d->dY, H, 0, BT, H, 0, dZ, sh.zld, 0, T, Fc, H, 1);
-  dg.aux = Z;
-  dg.ldaux = sh.zld;
-  TP_TRY(hip_status(launch("bwd_dz_gemm", TP_BF16, dg, gelu ? tp::EPI_GELU_BWD : tp::EPI_STORE, s), "bwd_dz_gemm"));
-  // HT = act(Z)^T, dZT = dZ^T
-  TP_TRY(transpose("bwd_transpose", Z, sh.zld, HT, T, T, Fc, gelu));
-  TP_TRY(transpose("bwd_transpose", dZ, sh.zld, dZT, T, T, Fc, false));
+  if (swiglu) {
+    // per shard: dH = dY B_i; [dG | dU] and H = SiLU(G) U from the stored [G | U]
+    tp::GemmParams dg = gemm(d->dY, H, 0, BT, H, Fs * H, dZ, sh.zld, zs, T, Fs, H, c);
+    dg.aux = Z;
+    dg.ldaux = sh.zld;
+    dg.sAux = zs;
+    dg.upOff = Fs;
+    dg.C2 = Hs;
+    dg.ldc2 = Fc;
+    dg.sC2 = Fs;
+    TP_TRY(hip_status(launch("bwd_dz_gemm", TP_BF16, dg, tp::EPI_SWIGLU_BWD, s), "bwd_dz_gemm"));
+    TP_TRY(transpose("bwd_transpose", Hs, Fc, HT, T, T, Fc, false));
+  } else {
+    // dZ = (dY B_r) * act'(Z)
+    tp::GemmParams dg = gemm(d->dY, H, 0, BT, H, 0, dZ, sh.zld, 0, T, Fc, H, 1);
+    dg.aux = Z;
+    dg.ldaux = sh.zld;
+    TP_TRY(hip_status(launch("bwd_dz_gemm", TP_BF16, dg, gelu ? tp::EPI_GELU_BWD : tp::EPI_STORE, s), "bwd_dz_gemm"));
+    TP_TRY(transpose("bwd_transpose", Z, sh.zld, HT, T, T, Fc, gelu));  // HT = act(Z)^T
+  }
+  TP_TRY(transpose("bwd_transpose", dZ, sh.zld, dZT, T, T, Fz, false));  // dZT [Fz x T]
 
-  // dX partial of each shard into its slab slot: dZ_i A_i (K = Fs)
-  const tp::GemmParams xg = gemm(dZ, sh.zld, Fs, AT, Fc, Fs, P + (size_t)i0 * T * H, H, T * H, T, H, Fs, c);
+  // dX partial of each shard into its slab slot: dZ_i A_i (K = zs)
+  const tp::GemmParams xg = gemm(dZ, sh.zld, zs, AT, Fz, zs, P + (size_t)i0 * T * H, H, T * H, T, H, zs, c);
   TP_TRY(hip_status(launch("bwd_dx_gemm", TP_BF16, xg, tp::EPI_PARTIAL, s), "bwd_dx_gemm"));
-  // dA rows of the range: dZ^T X  (M = Fc, N = H, contraction over T)
-  TP_TRY(token_gemm("bwd_da_gemm", dZT, XT, Fc, H, d->dA + (size_t)i0 * Fs * H, H));
+  // dA rows of the range: dZ^T X  (M = Fz, N = H, contraction over T)
+  TP_TRY(token_gemm("bwd_da_gemm", dZT, XT, Fz, H, d->dA + (size_t)i0 * zs * H, H));
   // dB columns of the range: dY^T act(Z)  (M = H, N = Fc)
   TP_TRY(token_gemm("bwd_db_gemm", dYT, HT, H, Fc, d->dB + (size_t)i0 * Fs, F));
   // bias gradients: column sums of dZ (range) and of dY (once)

@@ -343,11 +343,14 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
                  need_da=True, need_db=True, stream=None):
     """Backward of the MLP pair over a shard range; returns (grads, workspace).
     ``grads`` holds dX (bf16 [T x H], filled when the range covers all N
-    shards), dA (fp32 [F x H]), da (fp32 [F] or None), dB (fp32 [H x F]) and
-    db (fp32 [H] or None); missing entries are allocated."""
+    shards), dA (fp32, A's shape: [F x H], or the [2F x H] fused blocks for
+    SwiGLU), da (fp32 [F] or None; always None for SwiGLU), dB (fp32
+    [H x F]) and db (fp32 [H] or None); missing entries are allocated."""
     torch = _torch()
     T, H = X.shape
-    F = A.shape[0]
+    F = B.shape[1]
+    if act == TP_ACT_SWIGLU:
+        need_da = False  # no column bias
     cnt = N if shard_count is None else shard_count
     g = dict(grads or {})
     dev = X.device
@@ -355,7 +358,7 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
     if "dX" not in g:
         g["dX"] = torch.empty((T, H), dtype=X.dtype, device=dev) if cnt == N else None
     if "dA" not in g:
-        g["dA"] = torch.zeros((F, H), dtype=f32, device=dev)
+        g["dA"] = torch.zeros(tuple(A.shape), dtype=f32, device=dev)
     if "da" not in g:
         g["da"] = torch.zeros((F,), dtype=f32, device=dev) if need_da else None
     if "dB" not in g:

@@ -107,9 +107,9 @@ def reduce_slab(w: Workload, d: dict, ws, Y=None, slice=-1, stream=None):
 
 
 def backward(w: Workload, d: dict, dY, grads=None, ws=None, shard_begin=0, shard_count=None, stream=None):
-    """One backward pass of the GELU MLP sublayer over a shard range."""
-    if w.kind != "mlp_gelu":
-        raise ValueError(f"the backward is built for the GELU MLP only, not {w.kind}")
-    return tp.mlp_backward(d["X"], d["A"], d["a"], d["B"], dY, w.N, act=tp.TP_ACT_GELU,
+    """One backward pass of the MLP sublayer (GELU or SwiGLU) over a shard range."""
+    if w.kind not in ("mlp_gelu", "mlp_swiglu"):
+        raise ValueError(f"the backward is built for the MLP sublayers, not {w.kind}")
+    return tp.mlp_backward(d["X"], d["A"], d["a"], d["B"], dY, w.N, act=act_of(w),
                            shard_begin=shard_begin, shard_count=shard_count, grads=grads, ws=ws,
                            need_da=d["a"] is not None, need_db=d["b"] is not None, stream=stream)

@@ -231,7 +231,8 @@ def test_mlp_backward_workspace_size_is_host_only(L):
     (dict(F=2050), tp.TP_ERR_DIVISIBILITY, "not divisible by N=4"),
     (dict(T=260), tp.TP_ERR_ALIGN, "T=260 is not a multiple of 8"),
     (dict(dt=tp.TP_F32), tp.TP_ERR_DTYPE, "bf16-only"),
-    (dict(act=tp.TP_ACT_SWIGLU), tp.TP_ERR_DTYPE, "only GELU and NONE"),
+    (dict(act=tp.TP_ACT_SWIGLU), tp.TP_ERR_SHAPE, "a and da must be NULL"),
+    (dict(act=9), tp.TP_ERR_DTYPE, "activation 9 unknown"),
     (dict(dY=None), tp.TP_ERR_NULL, "dY is NULL"),
     (dict(dA=None), tp.TP_ERR_NULL, "dA is NULL"),
     (dict(dX=None), tp.TP_ERR_NULL, "dX is NULL"),
@@ -245,6 +246,15 @@ def test_mlp_backward_rejects_before_launch(L, kw, status, needle):
     s = tp.tp_mlp_backward(None, d, FAKE, 1 << 40)
     assert s == status, tp.last_error()
     assert needle in tp.last_error()
+
+
+def test_mlp_backward_swiglu_workspace(L):
+    """SwiGLU keeps [gate | up] per shard (twice the columns of Z, dZ and
+    their transposes) plus SiLU(gate)*up."""
+    T, H, F, N = 256, 512, 2048, 4
+    gelu = tp.tp_mlp_backward_workspace_size(_bwd(a=None, da=None))
+    swi = tp.tp_mlp_backward_workspace_size(_bwd(act=tp.TP_ACT_SWIGLU, a=None, da=None))
+    assert swi > gelu + 3 * T * F * 2
 
 
 def test_mlp_backward_partial_range_needs_no_dx(L):

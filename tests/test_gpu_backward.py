@@ -170,3 +170,77 @@ def test_backward_full_size(k):
         e = err(got[key], ref[key])
         say(f"backward config {k}: {key} err={e:.3e}")
         assert e <= BF16_TOL, key
+
+
+# ------------------------------------------------------------------ SwiGLU
+def _swiglu_host(T, H, I, seed):
+    rng = np.random.default_rng(seed)
+    r = lambda shape, s: inputs.round_to_dtype((rng.standard_normal(shape) * s).astype(np.float32), "bf16")
+    return {"X": r((T, H), 1.0), "Wg": r((I, H), 0.05), "Wu": r((I, H), 0.05), "Wd": r((H, I), 0.05),
+            "dY": r((T, H), 1.0)}
+
+
+def _fused(Wg, Wu, N):
+    """Per-shard [gate | up] row blocks, as the forward takes them."""
+    I, H = Wg.shape
+    s = I // N
+    return np.concatenate([np.concatenate([Wg[i * s:(i + 1) * s], Wu[i * s:(i + 1) * s]]) for i in range(N)])
+
+
+def _unfuse(dA, N):
+    """Fused-block gradient [2I x H] back to (dWg, dWu), each [I x H]."""
+    blocks = dA.reshape(N, 2, -1, dA.shape[1])
+    return blocks[:, 0].reshape(-1, dA.shape[1]), blocks[:, 1].reshape(-1, dA.shape[1])
+
+
+@pytest.mark.parametrize("T,H,I,N", [
+    (264, 136, 4 * 40, 4),     # ragged tiles
+    (2048, 512, 8 * 48, 8),    # split-K weight gradients
+    (304, 256, 2 * 64, 2),
+])
+def test_swiglu_backward_vs_oracle(T, H, I, N):
+    say(f"swiglu backward T={T} H={H} I={I} N={N}")
+    h = _swiglu_host(T, H, I, seed=T + H + I)
+    A = dev(_fused(h["Wg"], h["Wu"], N))
+    X, Wd, dY = dev(h["X"]), dev(h["Wd"]), dev(h["dY"])
+    g, _ = tp.mlp_backward(X, A, None, Wd, dY, N, act=tp.TP_ACT_SWIGLU, need_db=True)
+    g2, _ = tp.mlp_backward(X, A, None, Wd, dY, N, act=tp.TP_ACT_SWIGLU, need_db=True)
+    torch.cuda.synchronize()
+    ref = R.mlp_swiglu_backward(h["X"], h["Wg"], h["Wu"], h["Wd"], h["dY"])
+    assert g["da"] is None
+    dWg, dWu = _unfuse(_np(g["dA"]), N)
+    got = {"dX": _np(g["dX"]), "dWg": dWg, "dWu": dWu, "dWd": _np(g["dB"]), "db": _np(g["db"])}
+    for k in ("dX", "dWg", "dWu", "dWd", "db"):
+        e = err(got[k], ref[k])
+        say(f"  {k}: err={e:.3e}")
+        assert e <= BF16_TOL, k
+    for k in ("dX", "dA", "dB", "db"):
+        assert torch.equal(g[k], g2[k]), f"{k} not bit-identical run to run"
+
+
+def test_swiglu_backward_full_size():
+    """The SwiGLU workload (T=32768, H=4096, I=11008, N=8) on sampled token
+    rows (dX) and intermediate features (dWg, dWu, dWd)."""
+    w = configs.CONFIGS[3]
+    say(f"backward config 3 {w.name}: generating inputs")
+    host = inputs.make_inputs(w)
+    dY_h = inputs.grad_output(w)
+    d = workloads.device_inputs(w, host)
+    say("backward config 3: all 8 shards")
+    g, ws = workloads.backward(w, d, dev(dY_h))
+    torch.cuda.synchronize()
+    del ws
+    rows = inputs.sample_rows(w.T, 16, w.seed, [0, w.T - 1])
+    feats = inputs.sample_rows(w.F, 12, w.seed + 1, [0, w.F - 1])
+    say(f"backward config 3: oracle on {len(rows)} rows and {len(feats)} features")
+    ref = R.mlp_swiglu_backward_sample(host["X"], host["Wg"], host["Wu"], host["Wd"], dY_h, rows, feats)
+    Fs = w.F // w.N
+    blk, off = feats // Fs, feats % Fs
+    gate_rows = torch.from_numpy(blk * 2 * Fs + off).to(DEV)
+    up_rows = torch.from_numpy(blk * 2 * Fs + Fs + off).to(DEV)
+    got = {"dX": _np(g["dX"][torch.from_numpy(rows).to(DEV)]), "dWg": _np(g["dA"][gate_rows]),
+           "dWu": _np(g["dA"][up_rows]), "dWd": _np(g["dB"][:, torch.from_numpy(feats).to(DEV)])}
+    for key in ("dX", "dWg", "dWu", "dWd"):
+        e = err(got[key], ref[key])
+        say(f"backward config 3: {key} err={e:.3e}")
+        assert e <= BF16_TOL, key
