@@ -320,6 +320,65 @@ def write_traffic(w, share, pmc_dir, argv_line, sp_entry=False, backward=False):
     return path
 
 
+def mfma_path(tag):
+    return os.path.join(ROOT, "profiles", f"mfma_{tag}.txt")
+
+
+def write_mfma(w, share, pmc_dir, argv_line, sp_entry=False, backward=False):
+    """Turn one rocprofv3 --pmc run of this script with the derived counters
+    MfmaFlopsBF16 (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) and MfmaUtil (MFMA-busy
+    SIMD cycles / (active GPU cycles x SIMDs)) into profiles/mfma_<workload>.txt:
+    per kernel, the matrix-core FLOP executed per launch against the
+    algorithmic FLOP, and the share of time the matrix cores were busy."""
+    import csv
+    import collections
+
+    order = launch_order(w, sp_entry, backward)
+    tag = workload_tag(w, sp_entry, backward)
+    rows = list(csv.DictReader(open(os.path.join(pmc_dir, "run_counter_collection.csv"))))
+    per = collections.defaultdict(dict)  # dispatch -> counter -> value
+    names = {}
+    for r in rows:
+        per[int(r["Dispatch_Id"])][r["Counter_Name"]] = float(r["Counter_Value"])
+        names[int(r["Dispatch_Id"])] = r["Kernel_Name"]
+    ours = [d for d in sorted(per) if "tp::" in names[d] or "_ZN2tp" in names[d]]
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for i, dsp in enumerate(ours):
+        k = order[i % len(order)]
+        if KERNEL_SYMBOL[k] not in names[dsp]:
+            raise RuntimeError(f"dispatch {dsp}: expected {k} ({KERNEL_SYMBOL[k]}), profiler has {names[dsp][:120]}")
+        for c, v in per[dsp].items():
+            vals[k][c].append(v)
+    shards = w.N if share == "layer" else 1
+    lines = [
+        f"# Matrix-core work and busy share per launch: {tag} ({share})",
+        "#",
+        "# Command (from /tmp on the GPU host, REPO = repository root):",
+        f"#   rocprofv3 --pmc MfmaFlopsBF16 MfmaUtil -f csv -d DIR -o run -- python3 $REPO/bench.py {argv_line}",
+        f"#   python3 $REPO/bench.py --config {w.key} --share {share}{' --sp-entry' if sp_entry else ''}"
+        f"{' --backward' if backward else ''} --mfma-from DIR",
+        "#",
+        "# MfmaFlopsBF16 = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (executed matrix FLOP, padding and recomputation",
+        "# included); MfmaUtil = 100 * sum(SQ_VALU_MFMA_BUSY_CYCLES) / (GRBM_GUI_ACTIVE * SIMDs), the share of",
+        "# the kernel's active cycles the matrix cores were busy, at whatever clock the chip ran.",
+        "#",
+        "# kernel                 mfma_flop_per_launch   algorithmic_flop   executed/algorithmic   mfma_busy_%",
+    ]
+    for k in dict.fromkeys(order):
+        if k not in vals:
+            continue
+        fl = sum(vals[k].get("MfmaFlopsBF16", [0.0])) / max(1, len(vals[k].get("MfmaFlopsBF16", [0.0])))
+        ut = vals[k].get("MfmaUtil", [])
+        ut = sum(ut) / len(ut) if ut else float("nan")
+        alg = kernel_work(w, k, shards, w.T if share == "layer" or w.n_slices == 1 else w.T // w.n_slices)[0]
+        ratio = fl / alg if alg else float("nan")
+        lines.append(f"# {k:22s} {fl:20.4e} {alg:18.4e} {ratio:22.4f} {ut:13.2f}")
+    path = mfma_path(tag)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
 def cpu_baseline(w, host, seconds):
     """fp64 oracle on a bounded, seeded sample of token rows of the same
     workload; TFLOP/s counted with the same algorithmic FLOP per row."""
@@ -412,10 +471,22 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (PMC traffic calibration)")
+    ap.add_argument("--mfma-from", metavar="DIR",
+                    help="write profiles/mfma_<workload>.txt from a rocprofv3 --pmc MfmaFlopsBF16 MfmaUtil csv run "
+                         "under DIR and exit; runs on the host, no GPU")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="write profiles/traffic_<workload>.txt from rocprofv3 --pmc csv runs under DIR "
                          "(DIR/FETCH_SIZE, DIR/WRITE_SIZE) and exit; runs on the host, no GPU")
     args = ap.parse_args()
+
+    if args.mfma_from:
+        from tensor_transformer_layers_amd import configs
+
+        w = configs.workload(args.config)
+        argv = (f"--config {args.config} --share {args.share}{' --sp-entry' if args.sp_entry else ''}"
+                f"{' --backward' if args.backward else ''} --steps 3 --warmup 1 --no-cpu-baseline")
+        print(write_mfma(w, args.share, args.mfma_from, argv, args.sp_entry, args.backward))
+        return
 
     if args.traffic_from:
         from tensor_transformer_layers_amd import configs
