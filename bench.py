@@ -236,8 +236,8 @@ def launch_order(w, sp_entry=False, backward=False):
     return head + ["mlp_column_gemm", "mlp_row_gemm", "reduce_partials"]
 
 
-def traffic_path(workload_name):
-    return os.path.join(ROOT, "profiles", f"traffic_{workload_name}.txt")
+def traffic_path(workload_name, out_dir=None):
+    return os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"traffic_{workload_name}.txt")
 
 
 def measured_traffic(kernel, workload_name):
@@ -258,7 +258,7 @@ def workload_tag(w, sp_entry=False, backward=False):
     return w.name + ("_sp_entry" if sp_entry else "") + ("_backward" if backward else "")
 
 
-def write_traffic(w, share, pmc_dir, argv_line, sp_entry=False, backward=False):
+def write_traffic(w, share, pmc_dir, argv_line, sp_entry=False, backward=False, out_dir=None):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
     WRITE_SIZE, each with --calib-copy) into profiles/traffic_<workload>.txt.
 
@@ -314,17 +314,17 @@ def write_traffic(w, share, pmc_dir, argv_line, sp_entry=False, backward=False):
     lines.append("# traffic_bytes <kernel> <bytes per launch> <hash of that kernel's sources>")
     for k, v in out.items():
         lines.append(f"traffic_bytes {k} {v:.0f} {kernel_source_hash(k)}")
-    path = traffic_path(name)
+    path = traffic_path(name, out_dir)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     return path
 
 
-def mfma_path(tag):
-    return os.path.join(ROOT, "profiles", f"mfma_{tag}.txt")
+def mfma_path(tag, out_dir=None):
+    return os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"mfma_{tag}.txt")
 
 
-def write_mfma(w, share, pmc_dir, argv_line, sp_entry=False, backward=False):
+def write_mfma(w, share, pmc_dir, argv_line, sp_entry=False, backward=False, out_dir=None):
     """Turn one rocprofv3 --pmc run of this script with the derived counters
     MfmaFlopsBF16 (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) and MfmaUtil (MFMA-busy
     SIMD cycles / (active GPU cycles x SIMDs)) into profiles/mfma_<workload>.txt:
@@ -373,7 +373,7 @@ def write_mfma(w, share, pmc_dir, argv_line, sp_entry=False, backward=False):
         alg = kernel_work(w, k, shards, w.T if share == "layer" or w.n_slices == 1 else w.T // w.n_slices)[0]
         ratio = fl / alg if alg else float("nan")
         lines.append(f"# {k:22s} {fl:20.4e} {alg:18.4e} {ratio:22.4f} {ut:13.2f}")
-    path = mfma_path(tag)
+    path = mfma_path(tag, out_dir)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     return path
