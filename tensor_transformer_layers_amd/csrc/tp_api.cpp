@@ -136,6 +136,12 @@ tp_status check_matrix(const char* name, const void* p, int64_t rows, int64_t co
   if (ld % vec) return fail(TP_ERR_ALIGN, "%s: leading dimension %lld is not a multiple of %lld", name,
                             (long long)ld, (long long)vec);
   if (rows > kIntMax || cols > kIntMax) return fail(TP_ERR_SHAPE, "%s: dimension exceeds 2^31-1", name);
+  // the kernels address a tile of up to 256 rows through one buffer resource
+  // with 32-bit byte offsets
+  const int64_t es = 16 / vec;
+  if (ld * es * 256 >= (int64_t(1) << 32))
+    return fail(TP_ERR_SHAPE, "%s: leading dimension %lld too large (256 rows of it exceed 4 GiB of offsets)", name,
+                (long long)ld);
   return TP_OK;
 }
 
@@ -350,6 +356,13 @@ tp_status validate_attn(const tp_attn_desc* d, AttnShape* sh) {
     if (!aligned16(d->Y)) return fail(TP_ERR_ALIGN, "Y is not 16-byte aligned");
   }
   if (T > kIntMax) return fail(TP_ERR_SHAPE, "batch*seq exceeds 2^31-1");
+  // the staged V^T rows (T keys each) and one sequence's Q|K rows are
+  // addressed with 32-bit byte offsets
+  if (T * 2 * 256 >= (int64_t(1) << 32))
+    return fail(TP_ERR_SHAPE, "batch*seq=%lld exceeds the %lld-token limit of the staged V^T", (long long)T,
+                (long long)((int64_t(1) << 32) / 512 - 1));
+  if (d->seq * 2 * hd * 2 >= (int64_t(1) << 32))
+    return fail(TP_ERR_SHAPE, "seq=%lld too long for the staged Q|K rows", (long long)d->seq);
   const size_t c = (size_t)d->shard_count;
   sh->T = T;
   sh->hl = hl;
@@ -1052,6 +1065,9 @@ tp_status tp_attn_local(void* stream, int64_t batch, int64_t seq, int heads, int
   TP_TRY(check_matrix("Vt", Vt, hd, T, ldvt, 8));
   TP_TRY(check_matrix("O", O, T, hd, ldo, 8));
   if (T > kIntMax) return fail(TP_ERR_SHAPE, "batch*seq exceeds 2^31-1");
+  // one sequence's keys and one head's V^T rows are addressed with 32-bit byte offsets
+  if (seq * ldqk * 2 >= (int64_t(1) << 32))
+    return fail(TP_ERR_SHAPE, "seq=%lld x ldqk=%lld exceeds 4 GiB of offsets", (long long)seq, (long long)ldqk);
   if (T == 0) return ok();
   tp::AttnParams a{};
   a.QK = QK;

@@ -362,3 +362,25 @@ def test_mlp_forward_overlap_needs_two_streams_and_workspace(L):
     assert "stream2 must differ" in tp.last_error()
     need = tp.tp_mlp_workspace_size(d)
     assert tp.tp_mlp_forward_overlap(None, FAKE, d, 2, FAKE, need - 1) == tp.TP_ERR_WORKSPACE
+
+
+# ------------------------------------------------------------ size limits
+def test_leading_dimension_limit(L):
+    """A 256-row tile of an operand is addressed with 32-bit byte offsets: a
+    bf16 leading dimension of 2^23 is refused before any launch."""
+    big = 1 << 23
+    s = tp.tp_column_linear(None, tp.TP_BF16, tp.TP_ACT_NONE, 64, 64, 64, FAKE, big, FAKE, 64, None, FAKE, 64)
+    assert s == tp.TP_ERR_SHAPE and "leading dimension" in tp.last_error()
+    s = tp.tp_column_linear(None, tp.TP_BF16, tp.TP_ACT_NONE, 64, 64, 64, FAKE, big - 8, FAKE, 64, None, None, 64)
+    assert s == tp.TP_ERR_NULL  # the largest accepted ld passes the size check
+
+
+def test_attention_token_limit(L):
+    d = tp.AttnDesc()
+    d.dt = tp.TP_BF16
+    d.batch, d.seq, d.hidden = 4097, 4096, 4096  # 16.8M tokens
+    d.heads, d.head_dim, d.N, d.shard_begin, d.shard_count = 32, 128, 8, 0, 8
+    d.X = d.Wqkv = d.Wo = d.Y = FAKE
+    d.n_slices, d.slice = 1, -1
+    assert tp.tp_attn_workspace_size(d) == 0
+    assert "token limit" in tp.last_error()
