@@ -131,6 +131,8 @@ def backward_kernel_work(w, name, c):
     Fz = 2 * Fc if swi else Fc
     S = backward_splits(T, Fz, H)
     bias = w.sigma_bias is not None
+    if name == "bwd_fused_gemm":  # both passes: the recomputed pre-activation and dH; writes dZ and H
+        return 4.0 * T * H * Fc, 2 * (2 * T * H + 2 * Fc * H + 2 * T * Fc) + (2 * Fc if bias else 0)
     if name == "bwd_recompute_gemm":
         return 2.0 * T * H * Fz, 2 * (T * H + Fz * H + T * Fz) + (2 * Fc if bias else 0)
     if name == "bwd_dz_gemm":  # reads the stored pre-activation beside the accumulators (SwiGLU: also writes H)
@@ -172,7 +174,7 @@ KERNEL_SOURCES = {
     "reduce_partials": "reduce.hip", "rmsnorm_gather": "norm.hip",
     "bwd_transpose": "bwd.hip", "bwd_bias_rowsum": "bwd.hip", "bwd_recompute_gemm": "gemm.hip",
     "bwd_dz_gemm": "gemm.hip", "bwd_dx_gemm": "gemm.hip", "bwd_da_gemm": "gemm.hip", "bwd_db_gemm": "gemm.hip",
-    "bwd_splitk_reduce": "reduce.hip",
+    "bwd_splitk_reduce": "reduce.hip", "bwd_fused_gemm": "gemm.hip",
     "vocab_logits_gemm": "gemm.hip", "vocab_ce_fold": "vocab.hip", "vocab_ce_combine": "vocab.hip",
     "vocab_ce_mean": "vocab.hip",
 }
@@ -199,7 +201,7 @@ KERNEL_SYMBOL = {
     "attn_core": "attn_fwd_kernel", "reduce_partials": "reduce_kernel", "rmsnorm_gather": "rmsnorm_gather_kernel",
     "bwd_transpose": "transpose_kernel", "bwd_bias_rowsum": "rowsum_kernel", "bwd_recompute_gemm": "gemm_",
     "bwd_dz_gemm": "gemm_", "bwd_dx_gemm": "gemm_", "bwd_da_gemm": "gemm_", "bwd_db_gemm": "gemm_",
-    "bwd_splitk_reduce": "reduce_kernel",
+    "bwd_splitk_reduce": "reduce_kernel", "bwd_fused_gemm": "gemm_",
     "vocab_logits_gemm": "gemm_", "vocab_ce_fold": "ce_fold_kernel", "vocab_ce_combine": "ce_combine_kernel",
     "vocab_ce_mean": "ce_mean_kernel",
 }
@@ -209,7 +211,10 @@ def backward_launch_order(w):
     """Kernels one backward step (all shards) launches, in order (the
     sequence of tp_mlp_backward)."""
     split = backward_splits(w.T, 2 * w.F if w.kind == "mlp_swiglu" else w.F, w.H) > 1
-    order = ["bwd_transpose"] * 4 + ["bwd_recompute_gemm", "bwd_dz_gemm"] + ["bwd_transpose"] * 2
+    # GELU with H <= 2048 runs the recomputation and dZ as one two-pass kernel
+    fused = w.kind == "mlp_gelu" and w.H <= 2048
+    order = ["bwd_transpose"] * 4 + (["bwd_fused_gemm"] if fused else ["bwd_recompute_gemm", "bwd_dz_gemm"])
+    order += ["bwd_transpose"] * 2
     order += ["bwd_dx_gemm", "bwd_da_gemm"] + (["bwd_splitk_reduce"] if split else [])
     order += ["bwd_db_gemm"] + (["bwd_splitk_reduce"] if split else [])
     bias = w.sigma_bias is not None

@@ -80,8 +80,15 @@ __device__ __forceinline__ int swz(int r) {
   return (r >> C::SH) & (C::CPR - 1);
 }
 
+// Waves per SIMD the register allocation must allow: the two-pass GELU
+// kernel runs on 128x128 tiles and needs two workgroups per CU to hide its
+// epilogues; every other variant leaves the choice to the compiler.
 template <class C>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
+constexpr int kWavesPerEu = C::EPI == EPI_GELU_FUSED ? 2 : 1;
+
+template <class C>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<C>)))
+void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -133,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
   // read as zero
   const bf16* const Ab = static_cast<const bf16*>(p.A) + bz * p.sA + (int64_t)m0 * p.lda;
   const uint32_t a_rows = (uint32_t)min(C::BM, p.M - m0);
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(Ab, a_rows * (uint32_t)p.lda * 2u);
+  __amdgpu_buffer_rsrc_t rA = make_rsrc(Ab, a_rows * (uint32_t)p.lda * 2u);
   const bf16* const Bb = static_cast<const bf16*>(p.B) + bz * p.sB + (int64_t)n0 * p.ldb;
   __amdgpu_buffer_rsrc_t rB;
   int b_row0;  // first B-tile row this wave loads, relative to its buffer
@@ -240,12 +247,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
   };
 
   floatx16 acc[C::TN][C::TM];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int j = 0; j < C::TN; ++j)
+    for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
+      for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+        for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
+  };
+  zero_acc();
 
   bf16x8 af[2][C::TM], bfg[2][C::TN];
   auto load_frags = [&](auto stg, int kk, int buf) {
@@ -365,34 +375,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
     }
   };
 
-  // prologue: tile 0, the boundary part of tile 1, then tile 0's first fragments
-  if (has_tail)
-    issue_partial();
-  else
-    issue(I0{}, 0);
-  {
-    const bool live = 1 < nk;
-    const __amdgpu_buffer_rsrc_t ra = live ? rA : rZ;
-    const __amdgpu_buffer_rsrc_t rb = live ? rB : rZ;
-    const uint32_t so = live ? (uint32_t)k_begin(1) * 2u : 0u;
-#pragma unroll
-    for (int g = 0; g < kBoundaryLoads; ++g) dma_one(I1{}, g, ra, rb, so);
-  }
-  wait_vmcnt<kBoundaryLoads>();
-  if (has_tail) clear_partial();
-  lds_barrier();
-  load_frags(I0{}, 0, 0);
-
-
-  // two tiles per trip so that the stages are compile-time constants
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    body(I0{}, kt);
-    body(I1{}, kt + 1);
-  }
-  if (kt < nk) body(I0{}, kt);
-  wait_vmcnt<0>();  // no load may still target this workgroup's LDS when it exits
-
   // ---------------------------------------------------------------- epilogue
   // The accumulators go through LDS so that the output leaves in full row
   // segments (16 lanes per 256-byte fp32 row piece, 8-byte bf16 pieces) from
@@ -403,257 +385,336 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p, int t
   // c ^ (r & 15) (conflict-free for both the column writes and the row reads).
   // Phase h takes subtiles (2h, 2h+1), or for SwiGLU the gate subtile h and
   // its up subtile h + TN/2.
-  // EPI_CE_STATS: the label of each of this lane's epilogue rows, as a
-  // shard-local column (out-of-range values simply match no column), loaded
-  // once per tile before the staging
-  int ce_label[C::EPI == EPI_CE_STATS ? C::WM / 4 : 1];
-  if constexpr (C::EPI == EPI_CE_STATS) {
-    const int64_t vbase = (int64_t)(p.ce.shard0 + bz) * p.N;
-#pragma unroll
-    for (int it = 0; it < C::WM / 4; ++it) {
-      const int m = m0 + wm * C::WM + it * 4 + (lane >> 4);
-      const int64_t y = m < p.M ? (int64_t)p.ce.labels[m] - vbase : -1;
-      ce_label[it] = (y >= 0 && y < p.N) ? (int)y : -1000000;
-    }
-  }
-  lds_barrier();  // every wave is done with the operand stages
-  char* const ep = smem + w * (C::WM * 256);
-  static_assert(4 * C::WM * 256 <= C::LDS_BYTES, "epilogue staging fits the operand stages");
-  constexpr bool SWI = C::EPI == EPI_SWIGLU;
-#pragma unroll
-  for (int h = 0; h < C::TN / 2; ++h) {
-    // GELU' epilogue: the pre-activations of this phase's rows are read in
-    // blocks of ZB rows per lane, each block issued one block ahead of its
-    // use (the first before the accumulators go to LDS), so the load latency
-    // overlaps the staging and the previous block's arithmetic
-    constexpr int ZB = C::WM / 4 < 16 ? C::WM / 4 : 16;
-    const int zc_n = n0 + wn * C::WN + 64 * h + 4 * (lane & 15);
-    auto load_z = [&](int blk, bf16x4* z) {
-      const bf16* const zb = static_cast<const bf16*>(p.aux) + bz * p.sAux;
-#pragma unroll
-      for (int j = 0; j < ZB; ++j) {
-        const int m = m0 + wm * C::WM + (blk + j) * 4 + (lane >> 4);
-        z[j] = bf16x4{};
-        if (m < p.M && zc_n < p.N) {
-          const bf16* zp = zb + (int64_t)m * p.ldaux + zc_n;
-          if (zc_n + 3 < p.N)
-            z[j] = *reinterpret_cast<const bf16x4*>(zp);
-          else
-            for (int e = 0; e < 4 && zc_n + e < p.N; ++e) z[j][e] = zp[e];
-        }
+  auto epilogue = [&](auto mode_tag, void* outC, int64_t out_ldc, int64_t out_sC,
+                      const void* out_bias) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    // EPI_CE_STATS: the label of each of this lane's epilogue rows, as a
+    // shard-local column (out-of-range values simply match no column), loaded
+    // once per tile before the staging
+    int ce_label[MODE == EPI_CE_STATS ? C::WM / 4 : 1];
+    if constexpr (MODE == EPI_CE_STATS) {
+      const int64_t vbase = (int64_t)(p.ce.shard0 + bz) * p.N;
+  #pragma unroll
+      for (int it = 0; it < C::WM / 4; ++it) {
+        const int m = m0 + wm * C::WM + it * 4 + (lane >> 4);
+        const int64_t y = m < p.M ? (int64_t)p.ce.labels[m] - vbase : -1;
+        ce_label[it] = (y >= 0 && y < p.N) ? (int)y : -1000000;
       }
-    };
-    bf16x4 zc[ZB];
-    if constexpr (C::EPI == EPI_GELU_BWD) load_z(0, zc);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int j = SWI ? h + half * (C::TN / 2) : 2 * h + half;
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int r = i * 32 + l32;
-          const int c = half * 8 + 2 * g + lh;  // 16-byte chunk: columns 4c .. 4c+3
-          const floatx4 v = {acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]};
-          *reinterpret_cast<floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4)) = v;
-        }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-
-    if constexpr (SWI) {
-      // 8 lanes per row: gate chunk c, up chunk c + 8 -> 4 outputs
-      const int c = lane & 7;
-      const int n = n0 + wn * (C::BN / 4) + 32 * h + 4 * c;
-      bf16* Cp = static_cast<bf16*>(p.C) + bz * p.sC;
-#pragma unroll 2
-      for (int it = 0; it < C::WM / 8; ++it) {
-        const int r = it * 8 + (lane >> 3);
-        const int m = m0 + wm * C::WM + r;
-        const floatx4 gv = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
-        const floatx4 uv = *reinterpret_cast<const floatx4*>(ep + r * 256 + (((c + 8) ^ (r & 15)) << 4));
-        if (m < p.M && n < p.N) {
-          bf16x4 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = to_bf16(silu_bf16out(gv[e]) * uv[e]);
-          bf16* dst = Cp + (int64_t)m * p.ldc + n;
-          if (n + 3 < p.N)
-            __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(dst));
-          else
-            for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
-        }
-      }
-    } else if constexpr (C::EPI == EPI_GELU_BWD) {
-      // dZ = dH * GELU'(Z): 16 lanes per row, chunk c -> 4 outputs
-      static_assert((C::WM / 4) % ZB == 0, "row blocks");
-      const int c = lane & 15;
-      const int n = zc_n;
-#pragma unroll 1
-      for (int blk = 0; blk < C::WM / 4; blk += ZB) {
-        bf16x4 zn[ZB];
-        if (blk + ZB < C::WM / 4)
-          load_z(blk + ZB, zn);
-        else
-          for (int j = 0; j < ZB; ++j) zn[j] = bf16x4{};
-#pragma unroll
+    lds_barrier();  // every wave is done with the operand stages
+    char* const ep = smem + w * (C::WM * 256);
+    static_assert(4 * C::WM * 256 <= C::LDS_BYTES, "epilogue staging fits the operand stages");
+    constexpr bool SWI = MODE == EPI_SWIGLU;
+  #pragma unroll
+    for (int h = 0; h < C::TN / 2; ++h) {
+      // GELU' epilogue: the pre-activations of this phase's rows are read in
+      // blocks of ZB rows per lane, each block issued one block ahead of its
+      // use (the first before the accumulators go to LDS), so the load latency
+      // overlaps the staging and the previous block's arithmetic
+      constexpr int ZB = C::WM / 4 < 16 ? C::WM / 4 : 16;
+      const int zc_n = n0 + wn * C::WN + 64 * h + 4 * (lane & 15);
+      auto load_z = [&](int blk, bf16x4* z) {
+        const bf16* const zb = static_cast<const bf16*>(p.aux) + bz * p.sAux;
+  #pragma unroll
         for (int j = 0; j < ZB; ++j) {
-          const int r = (blk + j) * 4 + (lane >> 4);
-          const int m = m0 + wm * C::WM + r;
-          const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
-          if (m < p.M && n < p.N) {
-            bf16x4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = to_bf16(v[e] * gelu_grad_bf16out(static_cast<float>(zc[j][e])));
-            bf16* dst = static_cast<bf16*>(p.C) + bz * p.sC + (int64_t)m * p.ldc + n;
-            if (n + 3 < p.N)
-              __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(dst));
+          const int m = m0 + wm * C::WM + (blk + j) * 4 + (lane >> 4);
+          z[j] = bf16x4{};
+          if (m < p.M && zc_n < p.N) {
+            const bf16* zp = zb + (int64_t)m * p.ldaux + zc_n;
+            if (zc_n + 3 < p.N)
+              z[j] = *reinterpret_cast<const bf16x4*>(zp);
             else
-              for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
+              for (int e = 0; e < 4 && zc_n + e < p.N; ++e) z[j][e] = zp[e];
           }
         }
-#pragma unroll
-        for (int j = 0; j < ZB; ++j) zc[j] = zn[j];
-      }
-    } else if constexpr (C::EPI == EPI_SWIGLU_BWD) {
-      // SwiGLU backward from dH (the accumulators) and the stored gate G and
-      // up U of the same token and feature:
-      //   dG = dH U SiLU'(G),  dU = dH SiLU(G),  H = SiLU(G) U
-      // with SiLU'(g) = s (1 + g (1 - s)), s = sigmoid(g) (hardware exp and
-      // reciprocal).  16 lanes per row, 4 features each.
-      const int c = lane & 15;
-      const int n = n0 + wn * C::WN + 64 * h + 4 * c;
-      const bf16* const zb = static_cast<const bf16*>(p.aux) + bz * p.sAux;
-      bf16* const cb = static_cast<bf16*>(p.C) + bz * p.sC;
-      bf16* const hb = static_cast<bf16*>(p.C2) + bz * p.sC2;
-#pragma unroll 4
-      for (int it = 0; it < C::WM / 4; ++it) {
-        const int r = it * 4 + (lane >> 4);
-        const int m = m0 + wm * C::WM + r;
-        const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
-        if (m < p.M && n < p.N) {
-          const bf16* zp = zb + (int64_t)m * p.ldaux + n;
-          bf16x4 g4 = {}, u4 = {};
-          const bool full = n + 3 < p.N;
-          if (full) {
-            g4 = *reinterpret_cast<const bf16x4*>(zp);
-            u4 = *reinterpret_cast<const bf16x4*>(zp + p.upOff);
-          } else {
-            for (int e = 0; e < 4 && n + e < p.N; ++e) {
-              g4[e] = zp[e];
-              u4[e] = zp[e + p.upOff];
-            }
+      };
+      bf16x4 zc[ZB];
+      if constexpr (MODE == EPI_GELU_BWD) load_z(0, zc);
+  #pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int j = SWI ? h + half * (C::TN / 2) : 2 * h + half;
+  #pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+  #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int r = i * 32 + l32;
+            const int c = half * 8 + 2 * g + lh;  // 16-byte chunk: columns 4c .. 4c+3
+            const floatx4 v = {acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]};
+            *reinterpret_cast<floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4)) = v;
           }
-          bf16x4 og, ou, oh;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float g = static_cast<float>(g4[e]), u = static_cast<float>(u4[e]);
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-            const float si = g * sg;
-            og[e] = to_bf16(v[e] * u * (sg * fmaf(g, 1.0f - sg, 1.0f)));
-            ou[e] = to_bf16(v[e] * si);
-            oh[e] = to_bf16(si * u);
-          }
-          bf16* const dg = cb + (int64_t)m * p.ldc + n;
-          bf16* const hh = hb + (int64_t)m * p.ldc2 + n;
-          if (full) {
-            __builtin_nontemporal_store(og, reinterpret_cast<bf16x4*>(dg));
-            __builtin_nontemporal_store(ou, reinterpret_cast<bf16x4*>(dg + p.upOff));
-            __builtin_nontemporal_store(oh, reinterpret_cast<bf16x4*>(hh));
-          } else {
-            for (int e = 0; e < 4 && n + e < p.N; ++e) {
-              dg[e] = og[e];
-              dg[e + p.upOff] = ou[e];
-              hh[e] = oh[e];
-            }
-          }
-        }
       }
-    } else if constexpr (C::EPI == EPI_CE_STATS) {
-      // Cross-entropy statistics of this phase's 64 logit columns per token
-      // row (16 lanes per row, 4 logits each): the max over the row's real
-      // vocab ids, then the sum of exp(l - max) against it, and the label's
-      // logit.  Lane 0 of each row group writes the three values; the logits
-      // themselves are never stored.
-      const int c = lane & 15;
-      const int ncol0 = n0 + wn * C::WN + 64 * h;  // first column of the 64-column chunk
-      const int n = ncol0 + 4 * c;
-      const int64_t vbase = (int64_t)(p.ce.shard0 + bz) * p.N;  // vocab id of the shard's column 0
-      const int lim = (int)min((int64_t)p.N, max((int64_t)0, p.ce.V - vbase));  // columns >= lim: padding
-      const int k = ncol0 / 64;
-      float* const st = p.ce.stats + ((int64_t)bz * p.ce.cps + k) * p.M;
-      const auto fmax_ = [](float a, float b) { return fmaxf(a, b); };
-      const auto add_ = [](float a, float b) { return a + b; };
-#pragma unroll 4
-      for (int it = 0; it < C::WM / 4; ++it) {
-        const int r = it * 4 + (lane >> 4);
-        const int m = m0 + wm * C::WM + r;
-        const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < lim) mx = fmaxf(mx, v[e]);
-        mx = row16_reduce(mx, fmax_);
-        float sum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < lim) sum += __expf(v[e] - mx);
-        const int y = ce_label[it] - n;  // label column relative to this lane's first logit
-        const float z = (y >= 0 && y < 4 && n + y < lim) ? (y == 0 ? v[0] : y == 1 ? v[1] : y == 2 ? v[2] : v[3]) : 0.0f;
-        sum = row16_reduce(sum, add_);
-        const float zr = row16_reduce(z, add_);  // one lane of the row holds the label, if any
-        if (c == 0 && m < p.M && k < p.ce.cps) {
-          st[m] = mx;
-          st[m + p.ce.astride] = sum;
-          st[m + 2 * p.ce.astride] = zr;
-        }
-      }
-    } else {
-      // 16 lanes per row: chunk c -> 4 outputs
-      const int c = lane & 15;
-      const int n = n0 + wn * C::WN + 64 * h + 4 * c;
-      float bias[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (C::EPI != EPI_PARTIAL && C::EPI != EPI_GELU_BWD && C::EPI != EPI_CE_STATS &&
-                    C::EPI != EPI_SWIGLU_BWD) {
-        if (p.bias) {
-          const bf16* bp = static_cast<const bf16*>(p.bias) + bz * p.sBias;
-          for (int e = 0; e < 4; ++e) bias[e] = n + e < p.N ? static_cast<float>(bp[n + e]) : 0.0f;
-        }
-      }
-#pragma unroll 2
-      for (int it = 0; it < C::WM / 4; ++it) {
-        const int r = it * 4 + (lane >> 4);
-        const int m = m0 + wm * C::WM + r;
-        const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
-        if (m < p.M && n < p.N) {
-          const int64_t off = bz * p.sC + (int64_t)m * p.ldc + n;
-          if constexpr (C::EPI == EPI_PARTIAL) {
-            float* dst = static_cast<float*>(p.C) + off;
-            if (n + 3 < p.N)
-              __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(dst));  // read once, much later
-            else
-              for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = v[e];
-          } else {
-            bf16x4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float x = v[e] + bias[e];
-              o[e] = to_bf16(C::EPI == EPI_GELU ? gelu_bf16out(x) : x);
-            }
-            bf16* dst = static_cast<bf16*>(p.C) + off;
-            if (n + 3 < p.N)
-              __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(dst));
-            else
-              for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
-          }
-        }
-      }
-    }
-    if (h + 1 < C::TN / 2) {  // the next phase reuses the region
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+
+      if constexpr (SWI) {
+        // 8 lanes per row: gate chunk c, up chunk c + 8 -> 4 outputs
+        const int c = lane & 7;
+        const int n = n0 + wn * (C::BN / 4) + 32 * h + 4 * c;
+        bf16* Cp = static_cast<bf16*>(outC) + bz * out_sC;
+  #pragma unroll 2
+        for (int it = 0; it < C::WM / 8; ++it) {
+          const int r = it * 8 + (lane >> 3);
+          const int m = m0 + wm * C::WM + r;
+          const floatx4 gv = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
+          const floatx4 uv = *reinterpret_cast<const floatx4*>(ep + r * 256 + (((c + 8) ^ (r & 15)) << 4));
+          if (m < p.M && n < p.N) {
+            bf16x4 o;
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = to_bf16(silu_bf16out(gv[e]) * uv[e]);
+            bf16* dst = Cp + (int64_t)m * out_ldc + n;
+            if (n + 3 < p.N)
+              __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(dst));
+            else
+              for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
+          }
+        }
+      } else if constexpr (MODE == EPI_GELU_BWD) {
+        // dZ = dH * GELU'(Z): 16 lanes per row, chunk c -> 4 outputs
+        static_assert((C::WM / 4) % ZB == 0, "row blocks");
+        const int c = lane & 15;
+        const int n = zc_n;
+  #pragma unroll 1
+        for (int blk = 0; blk < C::WM / 4; blk += ZB) {
+          bf16x4 zn[ZB];
+          if (blk + ZB < C::WM / 4)
+            load_z(blk + ZB, zn);
+          else
+            for (int j = 0; j < ZB; ++j) zn[j] = bf16x4{};
+  #pragma unroll
+          for (int j = 0; j < ZB; ++j) {
+            const int r = (blk + j) * 4 + (lane >> 4);
+            const int m = m0 + wm * C::WM + r;
+            const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
+            if (m < p.M && n < p.N) {
+              bf16x4 o;
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = to_bf16(v[e] * gelu_grad_bf16out(static_cast<float>(zc[j][e])));
+              bf16* dst = static_cast<bf16*>(outC) + bz * out_sC + (int64_t)m * out_ldc + n;
+              if (n + 3 < p.N)
+                __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(dst));
+              else
+                for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
+            }
+          }
+  #pragma unroll
+          for (int j = 0; j < ZB; ++j) zc[j] = zn[j];
+        }
+      } else if constexpr (MODE == EPI_SWIGLU_BWD) {
+        // SwiGLU backward from dH (the accumulators) and the stored gate G and
+        // up U of the same token and feature:
+        //   dG = dH U SiLU'(G),  dU = dH SiLU(G),  H = SiLU(G) U
+        // with SiLU'(g) = s (1 + g (1 - s)), s = sigmoid(g) (hardware exp and
+        // reciprocal).  16 lanes per row, 4 features each.
+        const int c = lane & 15;
+        const int n = n0 + wn * C::WN + 64 * h + 4 * c;
+        const bf16* const zb = static_cast<const bf16*>(p.aux) + bz * p.sAux;
+        bf16* const cb = static_cast<bf16*>(outC) + bz * out_sC;
+        bf16* const hb = static_cast<bf16*>(p.C2) + bz * p.sC2;
+  #pragma unroll 4
+        for (int it = 0; it < C::WM / 4; ++it) {
+          const int r = it * 4 + (lane >> 4);
+          const int m = m0 + wm * C::WM + r;
+          const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
+          if (m < p.M && n < p.N) {
+            const bf16* zp = zb + (int64_t)m * p.ldaux + n;
+            bf16x4 g4 = {}, u4 = {};
+            const bool full = n + 3 < p.N;
+            if (full) {
+              g4 = *reinterpret_cast<const bf16x4*>(zp);
+              u4 = *reinterpret_cast<const bf16x4*>(zp + p.upOff);
+            } else {
+              for (int e = 0; e < 4 && n + e < p.N; ++e) {
+                g4[e] = zp[e];
+                u4[e] = zp[e + p.upOff];
+              }
+            }
+            bf16x4 og, ou, oh;
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float g = static_cast<float>(g4[e]), u = static_cast<float>(u4[e]);
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+              const float si = g * sg;
+              og[e] = to_bf16(v[e] * u * (sg * fmaf(g, 1.0f - sg, 1.0f)));
+              ou[e] = to_bf16(v[e] * si);
+              oh[e] = to_bf16(si * u);
+            }
+            bf16* const dg = cb + (int64_t)m * out_ldc + n;
+            bf16* const hh = hb + (int64_t)m * p.ldc2 + n;
+            if (full) {
+              __builtin_nontemporal_store(og, reinterpret_cast<bf16x4*>(dg));
+              __builtin_nontemporal_store(ou, reinterpret_cast<bf16x4*>(dg + p.upOff));
+              __builtin_nontemporal_store(oh, reinterpret_cast<bf16x4*>(hh));
+            } else {
+              for (int e = 0; e < 4 && n + e < p.N; ++e) {
+                dg[e] = og[e];
+                dg[e + p.upOff] = ou[e];
+                hh[e] = oh[e];
+              }
+            }
+          }
+        }
+      } else if constexpr (MODE == EPI_CE_STATS) {
+        // Cross-entropy statistics of this phase's 64 logit columns per token
+        // row (16 lanes per row, 4 logits each): the max over the row's real
+        // vocab ids, then the sum of exp(l - max) against it, and the label's
+        // logit.  Lane 0 of each row group writes the three values; the logits
+        // themselves are never stored.
+        const int c = lane & 15;
+        const int ncol0 = n0 + wn * C::WN + 64 * h;  // first column of the 64-column chunk
+        const int n = ncol0 + 4 * c;
+        const int64_t vbase = (int64_t)(p.ce.shard0 + bz) * p.N;  // vocab id of the shard's column 0
+        const int lim = (int)min((int64_t)p.N, max((int64_t)0, p.ce.V - vbase));  // columns >= lim: padding
+        const int k = ncol0 / 64;
+        float* const st = p.ce.stats + ((int64_t)bz * p.ce.cps + k) * p.M;
+        const auto fmax_ = [](float a, float b) { return fmaxf(a, b); };
+        const auto add_ = [](float a, float b) { return a + b; };
+  #pragma unroll 4
+        for (int it = 0; it < C::WM / 4; ++it) {
+          const int r = it * 4 + (lane >> 4);
+          const int m = m0 + wm * C::WM + r;
+          const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
+          float mx = -INFINITY;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < lim) mx = fmaxf(mx, v[e]);
+          mx = row16_reduce(mx, fmax_);
+          float sum = 0.0f;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < lim) sum += __expf(v[e] - mx);
+          const int y = ce_label[it] - n;  // label column relative to this lane's first logit
+          const float z = (y >= 0 && y < 4 && n + y < lim) ? (y == 0 ? v[0] : y == 1 ? v[1] : y == 2 ? v[2] : v[3]) : 0.0f;
+          sum = row16_reduce(sum, add_);
+          const float zr = row16_reduce(z, add_);  // one lane of the row holds the label, if any
+          if (c == 0 && m < p.M && k < p.ce.cps) {
+            st[m] = mx;
+            st[m + p.ce.astride] = sum;
+            st[m + 2 * p.ce.astride] = zr;
+          }
+        }
+      } else {
+        // 16 lanes per row: chunk c -> 4 outputs
+        const int c = lane & 15;
+        const int n = n0 + wn * C::WN + 64 * h + 4 * c;
+        float bias[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (MODE != EPI_PARTIAL && MODE != EPI_GELU_BWD && MODE != EPI_CE_STATS &&
+                      MODE != EPI_SWIGLU_BWD) {
+          if (out_bias) {
+            const bf16* bp = static_cast<const bf16*>(out_bias) + bz * p.sBias;
+            for (int e = 0; e < 4; ++e) bias[e] = n + e < p.N ? static_cast<float>(bp[n + e]) : 0.0f;
+          }
+        }
+  #pragma unroll 2
+        for (int it = 0; it < C::WM / 4; ++it) {
+          const int r = it * 4 + (lane >> 4);
+          const int m = m0 + wm * C::WM + r;
+          const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
+          if (m < p.M && n < p.N) {
+            const int64_t off = bz * out_sC + (int64_t)m * out_ldc + n;
+            if constexpr (MODE == EPI_PARTIAL) {
+              float* dst = static_cast<float*>(outC) + off;
+              if (n + 3 < p.N)
+                __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(dst));  // read once, much later
+              else
+                for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = v[e];
+            } else {
+              bf16x4 o;
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float x = v[e] + bias[e];
+                o[e] = to_bf16(MODE == EPI_GELU ? gelu_bf16out(x) : x);
+              }
+              bf16* dst = static_cast<bf16*>(outC) + off;
+              if (n + 3 < p.N)
+                __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(dst));
+              else
+                for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
+            }
+          }
+        }
+      }
+      if (h + 1 < C::TN / 2) {  // the next phase reuses the region
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      }
     }
+  };
+
+  // EPI_GELU_FUSED runs the k loop twice (see below); every other epilogue once.
+  constexpr int kPasses = C::EPI == EPI_GELU_FUSED ? 2 : 1;
+  floatx16 gp[C::EPI == EPI_GELU_FUSED ? C::TN : 1][C::EPI == EPI_GELU_FUSED ? C::TM : 1];
+  for (int pass = 0; pass < kPasses; ++pass) {
+    if constexpr (C::EPI == EPI_GELU_FUSED) {
+      if (pass == 1) {
+        lds_barrier();  // every wave is done with the staging region before pass 2 fills the stages
+        zero_acc();
+        rA = make_rsrc(static_cast<const bf16*>(p.A2) + bz * p.sA + (int64_t)m0 * p.lda, a_rows * (uint32_t)p.lda * 2u);
+        rB = make_rsrc(static_cast<const bf16*>(p.B2) + bz * p.sB + (int64_t)n0 * p.ldb,
+                       (uint32_t)min(C::BN, p.N - n0) * (uint32_t)p.ldb * 2u);
+      }
+    }
+    // prologue: tile 0, the boundary part of tile 1, then tile 0's first fragments
+    if (has_tail)
+      issue_partial();
+    else
+      issue(I0{}, 0);
+    {
+      const bool live = 1 < nk;
+      const __amdgpu_buffer_rsrc_t ra = live ? rA : rZ;
+      const __amdgpu_buffer_rsrc_t rb = live ? rB : rZ;
+      const uint32_t so = live ? (uint32_t)k_begin(1) * 2u : 0u;
+  #pragma unroll
+      for (int g = 0; g < kBoundaryLoads; ++g) dma_one(I1{}, g, ra, rb, so);
+    }
+    wait_vmcnt<kBoundaryLoads>();
+    if (has_tail) clear_partial();
+    lds_barrier();
+    load_frags(I0{}, 0, 0);
+
+
+    // two tiles per trip so that the stages are compile-time constants
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      body(I0{}, kt);
+      body(I1{}, kt + 1);
+    }
+    if (kt < nk) body(I0{}, kt);
+    wait_vmcnt<0>();  // no load may still target this workgroup's LDS when it exits
+    if constexpr (C::EPI == EPI_GELU_FUSED) {
+      if (pass == 0) {
+        // dZ = (dY B) * GELU'(X A^T + a) and H = GELU(X A^T + a) from two
+        // passes over the same k range: pass 1 (A = X, B = A rows) leaves the
+        // pre-activation in the accumulators; its slope is kept in registers
+        // and H goes out through the GELU epilogue; pass 2 (A2 = dY, B2 = B^T
+        // rows) computes dH, which is scaled by the slope and stored.  The
+        // pre-activation never leaves the chip.
+        const bf16* const bias = static_cast<const bf16*>(p.bias) + bz * p.sBias;
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int n = n0 + wn * C::WN + j * 32 + 8 * g + 4 * lh + e;
+              const float b = (p.bias && n < p.N) ? static_cast<float>(bias[n]) : 0.0f;
+#pragma unroll
+              for (int i = 0; i < C::TM; ++i) gp[j][i][4 * g + e] = gelu_grad_bf16out(acc[j][i][4 * g + e] + b);
+            }
+        epilogue(std::integral_constant<int, EPI_GELU>{}, p.C2, p.ldc2, p.sC2, p.bias);
+      }
+    }
+  }
+
+  if constexpr (C::EPI == EPI_GELU_FUSED) {
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) acc[j][i] *= gp[j][i];
+    epilogue(std::integral_constant<int, EPI_STORE>{}, p.C, p.ldc, p.sC, nullptr);
+  } else {
+    epilogue(std::integral_constant<int, C::EPI>{}, p.C, p.ldc, p.sC, p.bias);
   }
 }
 
@@ -791,6 +852,7 @@ hipError_t launch_gemm_bf16(const GemmParams& p, Epilogue epi, hipStream_t s) {
     case EPI_GELU_BWD: return launch_bf16_epi<EPI_GELU_BWD>(p, s);
     case EPI_CE_STATS: return launch_bf16_epi<EPI_CE_STATS>(p, s);
     case EPI_SWIGLU_BWD: return launch_bf16_epi<EPI_SWIGLU_BWD>(p, s);
+    case EPI_GELU_FUSED: return launch_bf16_cfg<G<128, 128, 64, 2, kGemmSwizzleShift, EPI_GELU_FUSED>>(p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -411,6 +411,11 @@ int bwd_splits(int64_t T, int64_t Fc, int64_t H) {
   return s;
 }
 
+// GELU with a short contraction (H <= 2048): the recomputed pre-activation
+// and dZ come from one two-pass kernel that keeps the pre-activation on chip
+// (its separate round trip through HBM dominates at narrow hidden sizes).
+bool bwd_fused_gelu(const tp_mlp_bwd_desc* d) { return d->act == TP_ACT_GELU && d->H <= 2048; }
+
 tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
   if (!d) return fail(TP_ERR_NULL, "descriptor is NULL");
   TP_TRY(check_dtype(d->dt));
@@ -462,7 +467,7 @@ tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
   sh->z_off = sh->p_bytes;
   sh->dz_off = sh->z_off + align256(T * fz * 2);
   sh->h_off = sh->dz_off + align256(T * fz * 2);
-  sh->xt_off = sh->h_off + (swiglu ? align256(T * fc * 2) : 0);
+  sh->xt_off = sh->h_off + (swiglu || bwd_fused_gelu(d) ? align256(T * fc * 2) : 0);
   sh->dyt_off = sh->xt_off + align256(H * T * 2);
   sh->ht_off = sh->dyt_off + align256(H * T * 2);
   sh->dzt_off = sh->ht_off + align256(fc * T * 2);
@@ -471,6 +476,31 @@ tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
   sh->k_off = sh->bt_off + align256(fc * H * 2);
   sh->total = sh->k_off + (sh->splits > 1 ? align256((size_t)sh->splits * fz * H * sizeof(float)) : 0);
   return TP_OK;
+}
+
+// The backward after dZ (and its transpose) exist: the input-gradient
+// partials, the weight and bias gradients, and the fold of the partials.
+template <class TokenGemm, class RowSum>
+tp_status bwd_tail(hipStream_t s, const tp_mlp_bwd_desc* d, const BwdShape& sh, void* ws, const void* dZ,
+                   const void* dZT, const void* XT, const void* dYT, const void* HT, const void* AT,
+                   TokenGemm& token_gemm, RowSum& rowsum) {
+  const int64_t T = d->T, H = d->H, F = d->F, Fs = sh.Fs, Fc = sh.Fc, Fz = sh.Fz;
+  const int c = d->shard_count, i0 = d->shard_begin;
+  const int64_t zs = d->act == TP_ACT_SWIGLU ? 2 * Fs : Fs;
+  float* P = static_cast<float*>(ws);
+  // dX partial of each shard into its slab slot: dZ_i A_i (K = zs)
+  const tp::GemmParams xg = gemm(dZ, sh.zld, zs, AT, Fz, zs, P + (size_t)i0 * T * H, H, T * H, T, H, zs, c);
+  TP_TRY(hip_status(launch("bwd_dx_gemm", TP_BF16, xg, tp::EPI_PARTIAL, s), "bwd_dx_gemm"));
+  // dA rows of the range: dZ^T X  (M = Fz, N = H, contraction over T)
+  TP_TRY(token_gemm("bwd_da_gemm", dZT, XT, Fz, H, d->dA + (size_t)i0 * zs * H, H));
+  // dB columns of the range: dY^T act(Z)  (M = H, N = Fc)
+  TP_TRY(token_gemm("bwd_db_gemm", dYT, HT, H, Fc, d->dB + (size_t)i0 * Fs, F));
+  // bias gradients: column sums of dZ (range) and of dY (once)
+  if (d->da) TP_TRY(rowsum("bwd_bias_rowsum", dZT, T, d->da + (size_t)i0 * Fs, Fc, T));
+  if (d->db) TP_TRY(rowsum("bwd_bias_rowsum", dYT, T, d->db, H, T));
+
+  if (c < d->N) return ok();
+  return run_reduce(s, TP_BF16, d->N, T, H, P, T * H, nullptr, d->dX, 1, -1);
 }
 
 // ------------------------------------------------------- vocab-parallel CE
@@ -867,6 +897,19 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
   TP_TRY(transpose("bwd_transpose", A_r, H, AT, Fz, Fz, H, false));   // AT  [H x Fz]
   TP_TRY(transpose("bwd_transpose", B_r, F, BT, H, H, Fc, false));    // BT  [Fc x H]
 
+  if (bwd_fused_gelu(d)) {
+    // dZ = (dY B_r) * GELU'(X A_r^T + a_r) and H = GELU(X A_r^T + a_r) in one kernel
+    tp::GemmParams fg = gemm(d->X, H, 0, A_r, H, 0, dZ, sh.zld, 0, T, Fc, H, 1);
+    fg.bias = a_r;
+    fg.A2 = d->dY;
+    fg.B2 = BT;
+    fg.C2 = Hs;
+    fg.ldc2 = Fc;
+    TP_TRY(hip_status(launch("bwd_fused_gemm", TP_BF16, fg, tp::EPI_GELU_FUSED, s), "bwd_fused_gemm"));
+    TP_TRY(transpose("bwd_transpose", Hs, Fc, HT, T, T, Fc, false));
+    TP_TRY(transpose("bwd_transpose", dZ, sh.zld, dZT, T, T, Fz, false));  // dZT [Fz x T]
+    return bwd_tail(s, d, sh, ws, dZ, dZT, XT, dYT, HT, AT, token_gemm, rowsum);
+  }
   // Z = X A_r^T (+ a_r), the range's pre-activation (all shards side by side)
   tp::GemmParams zg = gemm(d->X, H, 0, A_r, H, 0, Z, sh.zld, 0, T, Fz, H, 1);
   zg.bias = a_r;
@@ -892,20 +935,7 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
     TP_TRY(transpose("bwd_transpose", Z, sh.zld, HT, T, T, Fc, gelu));  // HT = act(Z)^T
   }
   TP_TRY(transpose("bwd_transpose", dZ, sh.zld, dZT, T, T, Fz, false));  // dZT [Fz x T]
-
-  // dX partial of each shard into its slab slot: dZ_i A_i (K = zs)
-  const tp::GemmParams xg = gemm(dZ, sh.zld, zs, AT, Fz, zs, P + (size_t)i0 * T * H, H, T * H, T, H, zs, c);
-  TP_TRY(hip_status(launch("bwd_dx_gemm", TP_BF16, xg, tp::EPI_PARTIAL, s), "bwd_dx_gemm"));
-  // dA rows of the range: dZ^T X  (M = Fz, N = H, contraction over T)
-  TP_TRY(token_gemm("bwd_da_gemm", dZT, XT, Fz, H, d->dA + (size_t)i0 * zs * H, H));
-  // dB columns of the range: dY^T act(Z)  (M = H, N = Fc)
-  TP_TRY(token_gemm("bwd_db_gemm", dYT, HT, H, Fc, d->dB + (size_t)i0 * Fs, F));
-  // bias gradients: column sums of dZ (range) and of dY (once)
-  if (d->da) TP_TRY(rowsum("bwd_bias_rowsum", dZT, T, d->da + (size_t)i0 * Fs, Fc, T));
-  if (d->db) TP_TRY(rowsum("bwd_bias_rowsum", dYT, T, d->db, H, T));
-
-  if (c < d->N) return ok();
-  return run_reduce(s, TP_BF16, d->N, T, H, P, T * H, nullptr, d->dX, 1, -1);
+  return bwd_tail(s, d, sh, ws, dZ, dZT, XT, dYT, HT, AT, token_gemm, rowsum);
 }
 
 int64_t tp_vocab_padded(int64_t V, int N) {

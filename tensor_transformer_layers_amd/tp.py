@@ -424,6 +424,26 @@ def vocab_ce_stats(ws, N, T, Vs, shard_count):
     return f(off), f(off + step), f(off + 2 * step)
 
 
+def mlp_forward_overlap(X, A, a, B, b, N, chunks, stream2, act=TP_ACT_GELU, Y=None, ws=None, stream=None):
+    """The whole MLP sublayer with the reduction of row block k overlapped
+    with the products of block k+1 on ``stream2`` (a torch stream other than
+    the current one); returns (Y, workspace)."""
+    torch = _torch()
+    T, H = X.shape
+    if Y is None:
+        Y = torch.empty((T, H), dtype=X.dtype, device=X.device)
+    d = mlp_desc(X, A, a, B, b, N, act, Y)
+    need = tp_mlp_workspace_size(d)
+    if need == 0:
+        if T == 0:
+            return Y, ws
+        raise TPError(TP_ERR_SHAPE, last_error())
+    if ws is None or ws.numel() < need:
+        ws = alloc_workspace(need, X.device)
+    check(tp_mlp_forward_overlap(_stream(stream), stream2.cuda_stream, d, chunks, _ptr(ws), ws.numel()))
+    return Y, ws
+
+
 def mlp_partials(ws, N, T, H):
     """View of the fp32 partial slab at the start of an MLP/attention workspace."""
     torch = _torch()

@@ -218,8 +218,9 @@ def _bwd(**kw):
 def test_mlp_backward_workspace_size_is_host_only(L):
     T, H, F, N = 256, 512, 2048, 4
     need = tp.tp_mlp_backward_workspace_size(_bwd())
-    # dX partial slab, Z and dZ, the transposes of X, dY, act(Z), dZ, A, B
-    base = N * T * H * 4 + 2 * T * F * 2 + 2 * H * T * 2 + 2 * F * T * 2 + 2 * H * F * 2
+    # dX partial slab, Z and dZ, act(Z) (the two-pass GELU kernel at H <= 2048
+    # writes it), the transposes of X, dY, act(Z), dZ, A, B
+    base = N * T * H * 4 + 3 * T * F * 2 + 2 * H * T * 2 + 2 * F * T * 2 + 2 * H * F * 2
     assert need >= base
     extra = need - base  # split-K partials of the weight gradients
     assert extra % (F * H * 4) == 0 and extra // (F * H * 4) in (0, 2, 4, 8, 16)
@@ -281,7 +282,8 @@ def test_bench_split_rule_matches_library(L, T, H, F, N, c):
     d = _bwd(T=T, H=H, F=F, N=N, shard_count=c)
     Fc = F // N * c
     align = lambda x: (x + 255) // 256 * 256
-    base = align(N * T * H * 4) + 2 * align(T * Fc * 2) + 2 * align(H * T * 2) + 2 * align(Fc * T * 2) \
+    fused_h = align(T * Fc * 2) if H <= 2048 else 0  # act(Z) of the two-pass GELU kernel
+    base = align(N * T * H * 4) + 2 * align(T * Fc * 2) + fused_h + 2 * align(H * T * 2) + 2 * align(Fc * T * 2) \
         + 2 * align(H * Fc * 2)
     extra = tp.tp_mlp_backward_workspace_size(d) - base
     S = bench.backward_splits(T, Fc, H)
@@ -384,3 +386,17 @@ def test_attention_token_limit(L):
     d.n_slices, d.slice = 1, -1
     assert tp.tp_attn_workspace_size(d) == 0
     assert "token limit" in tp.last_error()
+
+
+def test_binding_has_every_helper_the_workloads_call():
+    """workloads.py and bench.py reach the library through these helpers."""
+    import inspect
+    import re as _re
+
+    from tensor_transformer_layers_amd import workloads
+
+    src = inspect.getsource(workloads)
+    called = set(_re.findall(r"\btp\.([a-z_0-9]+)\(", src))
+    assert called, "no binding calls found"
+    missing = sorted(n for n in called if not hasattr(tp, n))
+    assert not missing, missing

@@ -21,12 +21,15 @@ def test_kernel_flops_add_up_to_the_workload(k):
 
 @pytest.mark.parametrize("k", [2, 3, 5])
 def test_backward_kernel_flops_cover_the_counted_work(k):
-    """The GEMMs' FLOP minus the recomputed product equals the counted
-    backward FLOP."""
+    """The FLOP of the launched GEMMs minus the recomputed column product
+    equals the counted backward FLOP (fused two-pass kernel or not)."""
     w = configs.workload(k)
-    names = ("bwd_dz_gemm", "bwd_dx_gemm", "bwd_da_gemm", "bwd_db_gemm")
-    total = sum(bench.kernel_work(w, n, w.N, w.T)[0] for n in names)
-    assert abs(total - bench.backward_flops(w, w.N)) <= 1e-9 * total
+    order = bench.backward_launch_order(w)
+    assert ("bwd_fused_gemm" in order) == (k == 2)
+    total = sum(bench.kernel_work(w, n, w.N, w.T)[0] * order.count(n) for n in dict.fromkeys(order))
+    fz = 2 * w.F if w.kind == "mlp_swiglu" else w.F
+    recompute = 2.0 * w.T * w.H * fz
+    assert abs(total - recompute - bench.backward_flops(w, w.N)) <= 1e-9 * total
 
 
 def test_fused_path_rule():
