@@ -742,19 +742,19 @@ tp_status mlp_rows(hipStream_t s, const tp_mlp_desc* d, const MlpShape& sh, void
 }
 
 // Events that order the overlapped forward's two streams, reused call to call
-// (a wait takes the event's state at the time it is enqueued).
-std::mutex g_evmu;
-std::vector<hipEvent_t> g_overlap_events;
+// by the calling thread (a wait takes the event's state at the time it is
+// enqueued, so re-recording later is safe); each thread has its own, so calls
+// from different threads never share an event.
+thread_local std::vector<hipEvent_t> t_overlap_events;
 
 tp_status overlap_events(int n, hipEvent_t* out) {
-  std::lock_guard<std::mutex> g(g_evmu);
-  while ((int)g_overlap_events.size() < n) {
+  while ((int)t_overlap_events.size() < n) {
     hipEvent_t e = nullptr;
     const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
     if (r != hipSuccess) return hip_status(r, "overlap event create");
-    g_overlap_events.push_back(e);
+    t_overlap_events.push_back(e);
   }
-  for (int i = 0; i < n; ++i) out[i] = g_overlap_events[i];
+  for (int i = 0; i < n; ++i) out[i] = t_overlap_events[i];
   return TP_OK;
 }
 
