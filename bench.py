@@ -613,6 +613,18 @@ def main():
     wall = time.perf_counter() - wall0
     ms_step = e0.elapsed_time(e1) / args.steps
 
+    # timed region 1b: the same steps with an event between steps, for the
+    # spread of single-step times (median, min, max)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record(stream)
+    for i in range(args.steps):
+        step()
+        marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    step_stats = {"median": round(per_step[len(per_step) // 2], 5), "min": round(per_step[0], 5),
+                  "max": round(per_step[-1], 5)}
+
     # timed region 2: the same steps with a HIP event pair around every kernel
     tp.tp_timing_reset()
     tp.tp_timing_enable(1)
@@ -668,6 +680,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "step_ms": step_stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
