@@ -230,6 +230,19 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _same_dtype(ref, **named):
+    """The C ABI takes untyped pointers: check here that every tensor has the
+    dtype of ``ref`` (and is contiguous), so a mismatch fails loudly instead
+    of being reinterpreted."""
+    for name, t in named.items():
+        if t is None:
+            continue
+        if t.dtype != ref.dtype:
+            raise TypeError(f"{name} is {t.dtype}, expected {ref.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
 def _ld(t) -> int:
     if t.dim() != 2 or t.stride(1) != 1:
         raise ValueError("expected a row-major 2-D tensor (unit column stride)")
@@ -324,6 +337,7 @@ def mlp_forward(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, ws=None, shard_begin=
     """Whole MLP sublayer; returns (Y, workspace).  Y is None for partial
     shard ranges (the partials are in the workspace slab)."""
     torch = _torch()
+    _same_dtype(X, A=A, a=a, B=B, b=b, Y=Y)
     T, H = X.shape
     cnt = N if shard_count is None else shard_count
     if Y is None and cnt == N:
@@ -347,6 +361,7 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
     SwiGLU), da (fp32 [F] or None; always None for SwiGLU), dB (fp32
     [H x F]) and db (fp32 [H] or None); missing entries are allocated."""
     torch = _torch()
+    _same_dtype(X, A=A, a=a, B=B, dY=dY)
     T, H = X.shape
     F = B.shape[1]
     if act == TP_ACT_SWIGLU:
@@ -389,6 +404,9 @@ def vocab_ce_forward(X, E, labels, V, N, shard_begin=0, shard_count=None, loss=N
     or None for a partial shard range, mean [1] fp32 or None, workspace).
     E must have tp_vocab_padded(V, N) rows; labels are int32."""
     torch = _torch()
+    _same_dtype(X, E=E)
+    if labels.dtype != torch.int32:
+        raise TypeError(f"labels are {labels.dtype}, expected torch.int32")
     T, H = X.shape
     cnt = N if shard_count is None else shard_count
     if loss is None and cnt == N:

@@ -400,3 +400,19 @@ def test_binding_has_every_helper_the_workloads_call():
     assert called, "no binding calls found"
     missing = sorted(n for n in called if not hasattr(tp, n))
     assert not missing, missing
+
+
+def test_binding_rejects_mismatched_dtypes():
+    """The ctypes layer checks dtypes before passing untyped pointers on."""
+    import torch
+
+    X = torch.zeros((16, 64), dtype=torch.bfloat16)
+    A = torch.zeros((128, 64), dtype=torch.float32)
+    B = torch.zeros((64, 128), dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="A is torch.float32"):
+        tp.mlp_backward(X, A, None, B, X.clone(), 2)
+    with pytest.raises(TypeError, match="labels"):
+        tp.vocab_ce_forward(X, torch.zeros((64, 64), dtype=torch.bfloat16), torch.zeros(16, dtype=torch.int64),
+                            50, 2)
+    with pytest.raises(TypeError, match="B is torch.float32"):
+        tp.mlp_forward(X, B.t().contiguous(), None, B.float(), None, 2)
