@@ -212,7 +212,7 @@ def backward_launch_order(w):
     sequence of tp_mlp_backward)."""
     split = backward_splits(w.T, 2 * w.F if w.kind == "mlp_swiglu" else w.F, w.H) > 1
     # GELU with H <= 2048 runs the recomputation and dZ as one two-pass kernel
-    fused = w.kind == "mlp_gelu" and w.H <= 2048
+    fused = w.kind == "mlp_gelu" and w.H <= 2048 and w.dtype == "bf16"
     order = ["bwd_transpose"] * 4 + (["bwd_fused_gemm"] if fused else ["bwd_recompute_gemm", "bwd_dz_gemm"])
     order += ["bwd_transpose"] * 2
     order += ["bwd_dx_gemm", "bwd_da_gemm"] + (["bwd_splitk_reduce"] if split else [])
@@ -528,9 +528,8 @@ def main():
         print("bench.py: --sp-entry needs an MLP workload with a reduce-scatter (--config 5) and --share layer",
               file=sys.stderr, flush=True)
         sys.exit(2)
-    if args.backward and (w.kind not in ("mlp_gelu", "mlp_swiglu") or w.dtype != "bf16" or args.share != "layer"
-                          or args.sp_entry):
-        print("bench.py: --backward needs a bf16 MLP workload (--config 2, 3 or 5) and --share layer",
+    if args.backward and (w.kind not in ("mlp_gelu", "mlp_swiglu") or args.share != "layer" or args.sp_entry):
+        print("bench.py: --backward needs an MLP workload (--config 1, 2, 3 or 5) and --share layer",
               file=sys.stderr, flush=True)
         sys.exit(2)
     log(f"workload {w.name}: generating seeded inputs")

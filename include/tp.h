@@ -224,8 +224,10 @@ tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t 
  * (the row bias enters once: listing of "Tensor Parallelism基础").
  * Storage order as in the forward: A [F x H], B [H x F] (out-in); gradients
  * come back in the same layout.  Weight and bias gradients are fp32.
- * Z_i and dZ_i are rounded to bf16 once (as a bf16 forward would store its
- * linear outputs), act(Z_i) is evaluated from the rounded Z_i.
+ * bf16: Z_i and dZ_i are rounded to bf16 once (as a bf16 forward would store
+ * its linear outputs), act(Z_i) is evaluated from the rounded Z_i (at H <= 2048
+ * one two-pass kernel keeps Z_i on chip in fp32 instead).  fp32: everything
+ * stays fp32.
  * SwiGLU (blog post section 3.2): A holds the N fused blocks [2F/N x H] of the
  * forward (gate rows, then up rows); Z_i = [G_i | U_i], dH_i = dY B_i,
  * dZ_i = [dH_i U_i SiLU'(G_i) | dH_i SiLU(G_i)], dA comes back in the same
@@ -233,16 +235,16 @@ tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t 
  * be NULL.
  */
 typedef struct {
-  tp_dtype dt;     /* TP_BF16                                                   */
+  tp_dtype dt;     /* TP_BF16, or TP_F32 (GELU / NONE; all buffers fp32)        */
   tp_act act;      /* TP_ACT_GELU, TP_ACT_NONE, or TP_ACT_SWIGLU (see below)    */
   int64_t T, H, F; /* T, H, F/N multiples of 8                                  */
   int N, shard_begin, shard_count;
-  const void* X;   /* [T x H] bf16                                              */
-  const void* A;   /* [F x H] bf16 ([2F x H] fused blocks for SwiGLU)           */
-  const void* a;   /* [F] bf16 or NULL                                          */
-  const void* B;   /* [H x F] bf16                                              */
-  const void* dY;  /* [T x H] bf16                                              */
-  void* dX;        /* [T x H] bf16, written when shard_count == N, else unused  */
+  const void* X;   /* [T x H] dt                                                */
+  const void* A;   /* [F x H] dt ([2F x H] fused blocks for SwiGLU)             */
+  const void* a;   /* [F] dt or NULL                                            */
+  const void* B;   /* [H x F] dt                                                */
+  const void* dY;  /* [T x H] dt                                                */
+  void* dX;        /* [T x H] dt, written when shard_count == N, else unused    */
   float* dA;       /* [F x H] ([2F x H] SwiGLU): rows of the shard range written */
   float* da;       /* [F] (entries of the range) or NULL to skip                */
   float* dB;       /* [H x F]: columns of the shard range written               */

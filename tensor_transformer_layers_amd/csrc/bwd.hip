@@ -18,42 +18,53 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTile = 64;          // 64 x 64 elements per workgroup
-constexpr int kPitch = kTile + 8;  // LDS row pitch in elements: rows stay 16-byte aligned
 
-// Thread t moves 16-byte chunk (t & 7) of tile rows (t >> 3) and (t >> 3) + 32:
-// 8 lanes cover one 128-byte row segment, in and out.  The tile is written
-// to LDS transposed (element by element) and read back in 16-byte rows.
-template <bool GELU>
+// Thread t moves 16-byte chunk (t % CH) of tile rows (t / CH) + (256 / CH) j,
+// CH = the chunks per 64-element row (8 for bf16, 16 for fp32): the lanes of
+// a row cover one contiguous row segment, in and out.  The tile is written to
+// LDS transposed (element by element) and read back in 16-byte rows.  With
+// GELU, the activation is applied on the way (fp32: erf form with the device
+// erff; bf16: the 7.1.26 form, rounded to bf16).
+template <typename E, bool GELU>
 __global__ __launch_bounds__(kThreads) void transpose_kernel(TransposeParams p, int tilesC) {
-  __shared__ __attribute__((aligned(16))) bf16 tile[kTile * kPitch];
+  constexpr int VE = 16 / sizeof(E);                     // elements per 16-byte chunk
+  constexpr int CH = kTile / VE;                         // chunks per tile row
+  constexpr int PITCH = kTile + VE;                      // 16-byte aligned LDS rows
+  constexpr int RSTEP = kThreads / CH, NJ = kTile / RSTEP;
+  typedef E ev __attribute__((ext_vector_type(VE)));
+  __shared__ __attribute__((aligned(16))) E tile[kTile * PITCH];
   const int tr = (int)blockIdx.x / tilesC, tc = (int)blockIdx.x % tilesC;
   const int64_t r0 = (int64_t)tr * kTile, c0 = (int64_t)tc * kTile;
-  const int chunk = threadIdx.x & 7, rr = threadIdx.x >> 3;
-  const bf16* const in = static_cast<const bf16*>(p.in);
-  bf16x8 v[2];
+  const int chunk = threadIdx.x % CH, rr = threadIdx.x / CH;
+  const E* const in = static_cast<const E*>(p.in);
+  ev v[NJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {  // both loads in flight before any LDS write
-    const int64_t gr = r0 + rr + 32 * j, gc = c0 + chunk * 8;
-    v[j] = bf16x8{};
-    if (gr < p.R && gc < p.C) v[j] = *reinterpret_cast<const bf16x8*>(in + gr * p.ld_in + gc);
+  for (int j = 0; j < NJ; ++j) {  // every load in flight before any LDS write
+    const int64_t gr = r0 + rr + RSTEP * j, gc = c0 + chunk * VE;
+    v[j] = ev{};
+    if (gr < p.R && gc < p.C) v[j] = *reinterpret_cast<const ev*>(in + gr * p.ld_in + gc);
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bf16 x = v[j][e];
-      if constexpr (GELU) x = to_bf16(gelu_bf16out(static_cast<float>(x)));
-      tile[(chunk * 8 + e) * kPitch + rr + 32 * j] = x;
+    for (int e = 0; e < VE; ++e) {
+      E x = v[j][e];
+      if constexpr (GELU) {
+        if constexpr (sizeof(E) == 4)
+          x = gelu_erf(x);
+        else
+          x = to_bf16(gelu_bf16out(static_cast<float>(x)));
+      }
+      tile[(chunk * VE + e) * PITCH + rr + RSTEP * j] = x;
     }
   __syncthreads();
-  bf16* const out = static_cast<bf16*>(p.out);
+  E* const out = static_cast<E*>(p.out);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int oc = rr + 32 * j;  // output row c0 + oc = input column
-    const int64_t go = c0 + oc, gi = r0 + chunk * 8;
+  for (int j = 0; j < NJ; ++j) {
+    const int oc = rr + RSTEP * j;  // output row c0 + oc = input column
+    const int64_t go = c0 + oc, gi = r0 + chunk * VE;
     if (go < p.C && gi < p.R)
-      *reinterpret_cast<bf16x8*>(out + go * p.ld_out + gi) =
-          *reinterpret_cast<const bf16x8*>(&tile[oc * kPitch + chunk * 8]);
+      *reinterpret_cast<ev*>(out + go * p.ld_out + gi) = *reinterpret_cast<const ev*>(&tile[oc * PITCH + chunk * VE]);
   }
 }
 
@@ -62,17 +73,20 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(TransposeParams p, 
 // The order is fixed, so the sums are bit-identical run to run.
 constexpr int kRowsPerBlock = kThreads / kWave;
 
+template <typename E>
 __global__ __launch_bounds__(kThreads) void rowsum_kernel(RowSumParams p) {
+  constexpr int VE = 16 / sizeof(E);
+  typedef E ev __attribute__((ext_vector_type(VE)));
   const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (r >= p.R) return;  // whole waves leave together
   const int lane = lane_id();
-  const bf16* const row = static_cast<const bf16*>(p.in) + r * p.ld;
+  const E* const row = static_cast<const E*>(p.in) + r * p.ld;
   float acc = 0.0f;
 #pragma unroll 4
-  for (int64_t c = lane * 8; c < p.C; c += 8 * kWave) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(row + c);
+  for (int64_t c = lane * VE; c < p.C; c += VE * kWave) {
+    const ev v = *reinterpret_cast<const ev*>(row + c);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += static_cast<float>(v[e]);
+    for (int e = 0; e < VE; ++e) acc += static_cast<float>(v[e]);
   }
 #pragma unroll
   for (int o = kWave / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
@@ -81,22 +95,30 @@ __global__ __launch_bounds__(kThreads) void rowsum_kernel(RowSumParams p) {
 
 }  // namespace
 
-hipError_t launch_transpose(const TransposeParams& p, bool gelu, hipStream_t s) {
+hipError_t launch_transpose(const TransposeParams& p, bool gelu, bool f32, hipStream_t s) {
   const int64_t tilesR = (p.R + kTile - 1) / kTile, tilesC = (p.C + kTile - 1) / kTile;
   const int64_t grid = tilesR * tilesC;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (gelu)
-    launch_kernel(transpose_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, p, (int)tilesC);
+  const dim3 g((unsigned)grid), b(kThreads);
+  if (f32 && gelu)
+    launch_kernel(transpose_kernel<float, true>, g, b, 0, s, p, (int)tilesC);
+  else if (f32)
+    launch_kernel(transpose_kernel<float, false>, g, b, 0, s, p, (int)tilesC);
+  else if (gelu)
+    launch_kernel(transpose_kernel<bf16, true>, g, b, 0, s, p, (int)tilesC);
   else
-    launch_kernel(transpose_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, p, (int)tilesC);
+    launch_kernel(transpose_kernel<bf16, false>, g, b, 0, s, p, (int)tilesC);
   return hipGetLastError();
 }
 
-hipError_t launch_rowsum(const RowSumParams& p, hipStream_t s) {
+hipError_t launch_rowsum(const RowSumParams& p, bool f32, hipStream_t s) {
   const int64_t grid = (p.R + kRowsPerBlock - 1) / kRowsPerBlock;
   if (grid <= 0) return hipSuccess;
-  launch_kernel(rowsum_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  if (f32)
+    launch_kernel(rowsum_kernel<float>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  else
+    launch_kernel(rowsum_kernel<bf16>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

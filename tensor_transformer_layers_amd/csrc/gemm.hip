@@ -790,7 +790,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p, int ti
     const int n = n0 + wn * 32 + j * 16 + l16;
     if (n >= p.N) continue;
     float bias = 0.0f;
-    if constexpr (EPI != EPI_PARTIAL) {
+    if constexpr (EPI != EPI_PARTIAL && EPI != EPI_GELU_BWD) {
       if (p.bias) bias = static_cast<const float*>(p.bias)[bz * p.sBias + n];
     }
 #pragma unroll
@@ -805,6 +805,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p, int ti
           *out = gelu_erf(x + bias);
         else if constexpr (EPI == EPI_STORE)
           *out = x + bias;
+        else if constexpr (EPI == EPI_GELU_BWD)  // dZ = dH * GELU'(Z), Z from aux
+          *out = x * gelu_grad_erf(static_cast<const float*>(p.aux)[bz * p.sAux + (int64_t)m * p.ldaux + n]);
         else
           *out = x;
       }
@@ -870,6 +872,9 @@ hipError_t launch_gemm_f32(const GemmParams& p, Epilogue epi, hipStream_t s) {
       break;
     case EPI_PARTIAL:
       launch_kernel(gemm_f32_kernel<EPI_PARTIAL>, dim3((unsigned)grid), dim3(kThreads), 0, s, p, tilesM, tilesN);
+      break;
+    case EPI_GELU_BWD:
+      launch_kernel(gemm_f32_kernel<EPI_GELU_BWD>, dim3((unsigned)grid), dim3(kThreads), 0, s, p, tilesM, tilesN);
       break;
     default:
       return hipErrorInvalidValue;

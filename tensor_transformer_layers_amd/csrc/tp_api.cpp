@@ -414,14 +414,14 @@ int bwd_splits(int64_t T, int64_t Fc, int64_t H) {
 // GELU with a short contraction (H <= 2048): the recomputed pre-activation
 // and dZ come from one two-pass kernel that keeps the pre-activation on chip
 // (its separate round trip through HBM dominates at narrow hidden sizes).
-bool bwd_fused_gelu(const tp_mlp_bwd_desc* d) { return d->act == TP_ACT_GELU && d->H <= 2048; }
+bool bwd_fused_gelu(const tp_mlp_bwd_desc* d) { return d->dt == TP_BF16 && d->act == TP_ACT_GELU && d->H <= 2048; }
 
 tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
   if (!d) return fail(TP_ERR_NULL, "descriptor is NULL");
   TP_TRY(check_dtype(d->dt));
-  if (d->dt != TP_BF16) return fail(TP_ERR_DTYPE, "backward path is bf16-only");
   if (d->act != TP_ACT_GELU && d->act != TP_ACT_NONE && d->act != TP_ACT_SWIGLU)
     return fail(TP_ERR_DTYPE, "backward activation %d unknown", (int)d->act);
+  if (d->act == TP_ACT_SWIGLU && d->dt != TP_BF16) return fail(TP_ERR_DTYPE, "SwiGLU backward is bf16-only");
   if (d->act == TP_ACT_SWIGLU && (d->a || d->da))
     return fail(TP_ERR_SHAPE, "SwiGLU has no column bias: a and da must be NULL");
   if (d->T < 0 || d->H <= 0 || d->F <= 0 || d->N <= 0)
@@ -446,11 +446,12 @@ tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
   if (d->T % 8) return fail(TP_ERR_ALIGN, "T=%lld is not a multiple of 8", (long long)d->T);
   if (d->H % 8) return fail(TP_ERR_ALIGN, "hidden H=%lld is not a multiple of 8", (long long)d->H);
   if (Fs % 8) return fail(TP_ERR_ALIGN, "shard width F/N=%lld is not a multiple of 8", (long long)Fs);
-  TP_TRY(check_matrix("X", d->X, d->T, d->H, d->H, 8));
   const int64_t a_rows = swiglu ? 2 * d->F : d->F;
-  TP_TRY(check_matrix("A", d->A, a_rows, d->H, d->H, 8));
-  TP_TRY(check_matrix("B", d->B, d->H, d->F, d->F, 8));
-  TP_TRY(check_matrix("dY", d->dY, d->T, d->H, d->H, 8));
+  const int64_t vec = vec_of(d->dt);
+  TP_TRY(check_matrix("X", d->X, d->T, d->H, d->H, vec));
+  TP_TRY(check_matrix("A", d->A, a_rows, d->H, d->H, vec));
+  TP_TRY(check_matrix("B", d->B, d->H, d->F, d->F, vec));
+  TP_TRY(check_matrix("dY", d->dY, d->T, d->H, d->H, vec));
   TP_TRY(check_matrix("dA", d->dA, a_rows, d->H, d->H, 4));
   TP_TRY(check_matrix("dB", d->dB, d->H, d->F, d->F, 4));
   if (d->a && !aligned16(d->a)) return fail(TP_ERR_ALIGN, "a is not 16-byte aligned");
@@ -461,19 +462,19 @@ tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
     if (!aligned16(d->dX)) return fail(TP_ERR_ALIGN, "dX is not 16-byte aligned");
   }
   if (d->T > kIntMax || d->F > kIntMax) return fail(TP_ERR_SHAPE, "size exceeds 2^31-1");
-  const size_t T = (size_t)d->T, H = (size_t)d->H, fc = (size_t)Fc, fz = (size_t)sh->Fz;
+  const size_t T = (size_t)d->T, H = (size_t)d->H, fc = (size_t)Fc, fz = (size_t)sh->Fz, es = esize(d->dt);
   sh->splits = bwd_splits(d->T, sh->Fz, d->H);
   sh->p_bytes = align256((size_t)d->N * T * H * sizeof(float));
   sh->z_off = sh->p_bytes;
-  sh->dz_off = sh->z_off + align256(T * fz * 2);
-  sh->h_off = sh->dz_off + align256(T * fz * 2);
-  sh->xt_off = sh->h_off + (swiglu || bwd_fused_gelu(d) ? align256(T * fc * 2) : 0);
-  sh->dyt_off = sh->xt_off + align256(H * T * 2);
-  sh->ht_off = sh->dyt_off + align256(H * T * 2);
-  sh->dzt_off = sh->ht_off + align256(fc * T * 2);
-  sh->at_off = sh->dzt_off + align256(fz * T * 2);
-  sh->bt_off = sh->at_off + align256(H * fz * 2);
-  sh->k_off = sh->bt_off + align256(fc * H * 2);
+  sh->dz_off = sh->z_off + align256(T * fz * es);
+  sh->h_off = sh->dz_off + align256(T * fz * es);
+  sh->xt_off = sh->h_off + (swiglu || bwd_fused_gelu(d) ? align256(T * fc * es) : 0);
+  sh->dyt_off = sh->xt_off + align256(H * T * es);
+  sh->ht_off = sh->dyt_off + align256(H * T * es);
+  sh->dzt_off = sh->ht_off + align256(fc * T * es);
+  sh->at_off = sh->dzt_off + align256(fz * T * es);
+  sh->bt_off = sh->at_off + align256(H * fz * es);
+  sh->k_off = sh->bt_off + align256(fc * H * es);
   sh->total = sh->k_off + (sh->splits > 1 ? align256((size_t)sh->splits * fz * H * sizeof(float)) : 0);
   return TP_OK;
 }
@@ -490,7 +491,7 @@ tp_status bwd_tail(hipStream_t s, const tp_mlp_bwd_desc* d, const BwdShape& sh, 
   float* P = static_cast<float*>(ws);
   // dX partial of each shard into its slab slot: dZ_i A_i (K = zs)
   const tp::GemmParams xg = gemm(dZ, sh.zld, zs, AT, Fz, zs, P + (size_t)i0 * T * H, H, T * H, T, H, zs, c);
-  TP_TRY(hip_status(launch("bwd_dx_gemm", TP_BF16, xg, tp::EPI_PARTIAL, s), "bwd_dx_gemm"));
+  TP_TRY(hip_status(launch("bwd_dx_gemm", d->dt, xg, tp::EPI_PARTIAL, s), "bwd_dx_gemm"));
   // dA rows of the range: dZ^T X  (M = Fz, N = H, contraction over T)
   TP_TRY(token_gemm("bwd_da_gemm", dZT, XT, Fz, H, d->dA + (size_t)i0 * zs * H, H));
   // dB columns of the range: dY^T act(Z)  (M = H, N = Fc)
@@ -500,7 +501,7 @@ tp_status bwd_tail(hipStream_t s, const tp_mlp_bwd_desc* d, const BwdShape& sh, 
   if (d->db) TP_TRY(rowsum("bwd_bias_rowsum", dYT, T, d->db, H, T));
 
   if (c < d->N) return ok();
-  return run_reduce(s, TP_BF16, d->N, T, H, P, T * H, nullptr, d->dX, 1, -1);
+  return run_reduce(s, d->dt, d->N, T, H, P, T * H, nullptr, d->dX, 1, -1);
 }
 
 // ------------------------------------------------------- vocab-parallel CE
@@ -828,38 +829,41 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
   const int c = d->shard_count, i0 = d->shard_begin, S = sh.splits;
   const bool gelu = d->act == TP_ACT_GELU, swiglu = d->act == TP_ACT_SWIGLU;
   const int64_t zs = swiglu ? 2 * Fs : Fs;  // Z / dZ / A columns per shard
+  const tp_dtype dt = d->dt;
+  const bool f32 = dt == TP_F32;
+  const size_t es = esize(dt);
   if (log_enabled())
-    fprintf(stderr, "[tp] mlp backward bf16 act=%d N=%d shards [%d,%d): T=%lld H=%lld Fs=%lld, split-K %d%s\n",
-            (int)d->act, d->N, i0, i0 + c, (long long)T, (long long)H, (long long)Fs, S,
+    fprintf(stderr, "[tp] mlp backward %s act=%d N=%d shards [%d,%d): T=%lld H=%lld Fs=%lld, split-K %d%s\n",
+            dt_name(dt), (int)d->act, d->N, i0, i0 + c, (long long)T, (long long)H, (long long)Fs, S,
             c == d->N ? " ; reduce dX" : "");
   char* base = static_cast<char*>(ws);
   float* P = reinterpret_cast<float*>(base);
-  bf16_t* Z = reinterpret_cast<bf16_t*>(base + sh.z_off);
-  bf16_t* dZ = reinterpret_cast<bf16_t*>(base + sh.dz_off);
-  bf16_t* Hs = reinterpret_cast<bf16_t*>(base + sh.h_off);
-  bf16_t* XT = reinterpret_cast<bf16_t*>(base + sh.xt_off);
-  bf16_t* dYT = reinterpret_cast<bf16_t*>(base + sh.dyt_off);
-  bf16_t* HT = reinterpret_cast<bf16_t*>(base + sh.ht_off);
-  bf16_t* dZT = reinterpret_cast<bf16_t*>(base + sh.dzt_off);
-  bf16_t* AT = reinterpret_cast<bf16_t*>(base + sh.at_off);
-  bf16_t* BT = reinterpret_cast<bf16_t*>(base + sh.bt_off);
+  char* Z = base + sh.z_off;
+  char* dZ = base + sh.dz_off;
+  char* Hs = base + sh.h_off;
+  char* XT = base + sh.xt_off;
+  char* dYT = base + sh.dyt_off;
+  char* HT = base + sh.ht_off;
+  char* dZT = base + sh.dzt_off;
+  char* AT = base + sh.at_off;
+  char* BT = base + sh.bt_off;
   float* K = reinterpret_cast<float*>(base + sh.k_off);
-  const bf16_t* A_r = static_cast<const bf16_t*>(d->A) + (size_t)i0 * zs * H;  // range rows of A
-  const bf16_t* B_r = static_cast<const bf16_t*>(d->B) + (size_t)i0 * Fs;      // range columns of B
-  const bf16_t* a_r = d->a ? static_cast<const bf16_t*>(d->a) + (size_t)i0 * Fs : nullptr;
+  const char* A_r = static_cast<const char*>(d->A) + (size_t)i0 * zs * H * es;  // range rows of A
+  const char* B_r = static_cast<const char*>(d->B) + (size_t)i0 * Fs * es;      // range columns of B
+  const char* a_r = d->a ? static_cast<const char*>(d->a) + (size_t)i0 * Fs * es : nullptr;
 
   auto transpose = [&](const char* name, const void* in, int64_t ld_in, void* out, int64_t ld_out, int64_t R,
                        int64_t C, bool act) -> tp_status {
     tp::TransposeParams t{in, ld_in, out, ld_out, R, C};
     KernelTimer kt(name, s);
-    const hipError_t e = tp::launch_transpose(t, act, s);
+    const hipError_t e = tp::launch_transpose(t, act, f32, s);
     kt.stop();
     return hip_status(e, name);
   };
   auto rowsum = [&](const char* name, const void* in, int64_t ld, float* out, int64_t R, int64_t C) -> tp_status {
     tp::RowSumParams r{in, ld, out, R, C};
     KernelTimer kt(name, s);
-    const hipError_t e = tp::launch_rowsum(r, s);
+    const hipError_t e = tp::launch_rowsum(r, f32, s);
     kt.stop();
     return hip_status(e, name);
   };
@@ -869,12 +873,12 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
                         int64_t ldc) -> tp_status {
     if (S == 1) {
       const tp::GemmParams g = gemm(Aop, T, 0, Bop, T, 0, C, ldc, 0, M, N, T, 1);
-      return hip_status(launch(name, TP_BF16, g, tp::EPI_PARTIAL, s), name);
+      return hip_status(launch(name, dt, g, tp::EPI_PARTIAL, s), name);
     }
     const int64_t kc = T / S;
     tp::GemmParams g = gemm(Aop, T, kc, Bop, T, kc, K, N, M * N, M, N, kc, S);
     g.xcd_per_problem = S % 8 == 0;  // each split's operand blocks stay in one XCD's L2
-    TP_TRY(hip_status(launch(name, TP_BF16, g, tp::EPI_PARTIAL, s), name));
+    TP_TRY(hip_status(launch(name, dt, g, tp::EPI_PARTIAL, s), name));
     tp::ReduceParams r{};
     r.P = K;
     r.part_stride = M * N;
@@ -913,7 +917,7 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
   // Z = X A_r^T (+ a_r), the range's pre-activation (all shards side by side)
   tp::GemmParams zg = gemm(d->X, H, 0, A_r, H, 0, Z, sh.zld, 0, T, Fz, H, 1);
   zg.bias = a_r;
-  TP_TRY(hip_status(launch("bwd_recompute_gemm", TP_BF16, zg, tp::EPI_STORE, s), "bwd_recompute_gemm"));
+  TP_TRY(hip_status(launch("bwd_recompute_gemm", dt, zg, tp::EPI_STORE, s), "bwd_recompute_gemm"));
   if (swiglu) {
     // per shard: dH = dY B_i; [dG | dU] and H = SiLU(G) U from the stored [G | U]
     tp::GemmParams dg = gemm(d->dY, H, 0, BT, H, Fs * H, dZ, sh.zld, zs, T, Fs, H, c);
@@ -931,7 +935,7 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
     tp::GemmParams dg = gemm(d->dY, H, 0, BT, H, 0, dZ, sh.zld, 0, T, Fc, H, 1);
     dg.aux = Z;
     dg.ldaux = sh.zld;
-    TP_TRY(hip_status(launch("bwd_dz_gemm", TP_BF16, dg, gelu ? tp::EPI_GELU_BWD : tp::EPI_STORE, s), "bwd_dz_gemm"));
+    TP_TRY(hip_status(launch("bwd_dz_gemm", dt, dg, gelu ? tp::EPI_GELU_BWD : tp::EPI_STORE, s), "bwd_dz_gemm"));
     TP_TRY(transpose("bwd_transpose", Z, sh.zld, HT, T, T, Fc, gelu));  // HT = act(Z)^T
   }
   TP_TRY(transpose("bwd_transpose", dZ, sh.zld, dZT, T, T, Fz, false));  // dZT [Fz x T]

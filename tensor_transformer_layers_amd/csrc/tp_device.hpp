@@ -23,6 +23,12 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
 }
 
+// Slope of the exact GELU for fp32 outputs: Phi(z) + z phi(z) with the
+// device erff and expf.
+__device__ __forceinline__ float gelu_grad_erf(float z) {
+  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) + z * 0.39894228040143268f * expf(-0.5f * z * z);
+}
+
 // SiLU with beta = 1: g * sigmoid(g) = g / (1 + e^-g).
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 

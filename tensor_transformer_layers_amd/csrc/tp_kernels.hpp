@@ -151,10 +151,10 @@ struct AttnParams {
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 
 
-// Layout kernels of the MLP pair's backward (bwd.hip), bf16 only.
+// Layout kernels of the MLP pair's backward (bwd.hip), bf16 or fp32.
 //   out[c][r] = op(in[r][c]) for in [R x C] (ld_in), out [C x R] (ld_out);
 //   op = identity, or GELU (the activation recomputed from a stored
-//   pre-activation, rounded to bf16).  R, C, ld_in, ld_out multiples of 8.
+//   pre-activation).  R, C, ld_in, ld_out multiples of 8 (bf16) or 4 (fp32).
 struct TransposeParams {
   const void* in;
   int64_t ld_in;
@@ -162,16 +162,17 @@ struct TransposeParams {
   int64_t ld_out;
   int64_t R, C;
 };
-hipError_t launch_transpose(const TransposeParams& p, bool gelu, hipStream_t s);
+hipError_t launch_transpose(const TransposeParams& p, bool gelu, bool f32, hipStream_t s);
 
-//   out[r] = sum over c of in[r][c], fp32, in a fixed order.  C a multiple of 8.
+//   out[r] = sum over c of in[r][c] (bf16 or fp32 in), fp32, in a fixed order.
+//   C a multiple of 8 (bf16) or 4 (fp32).
 struct RowSumParams {
   const void* in;
   int64_t ld;
   float* out;
   int64_t R, C;
 };
-hipError_t launch_rowsum(const RowSumParams& p, hipStream_t s);
+hipError_t launch_rowsum(const RowSumParams& p, bool f32, hipStream_t s);
 
 // Vocab-parallel cross-entropy (vocab.hip).
 // Folds the per-chunk statistics of the GEMM epilogue (layout of CeEpilogue,

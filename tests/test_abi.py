@@ -231,7 +231,7 @@ def test_mlp_backward_workspace_size_is_host_only(L):
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(F=2050), tp.TP_ERR_DIVISIBILITY, "not divisible by N=4"),
     (dict(T=260), tp.TP_ERR_ALIGN, "T=260 is not a multiple of 8"),
-    (dict(dt=tp.TP_F32), tp.TP_ERR_DTYPE, "bf16-only"),
+    (dict(dt=tp.TP_F32, act=tp.TP_ACT_SWIGLU, a=None, da=None), tp.TP_ERR_DTYPE, "SwiGLU backward is bf16-only"),
     (dict(act=tp.TP_ACT_SWIGLU), tp.TP_ERR_SHAPE, "a and da must be NULL"),
     (dict(act=9), tp.TP_ERR_DTYPE, "activation 9 unknown"),
     (dict(dY=None), tp.TP_ERR_NULL, "dY is NULL"),

@@ -244,3 +244,46 @@ def test_swiglu_backward_full_size():
         e = err(got[key], ref[key])
         say(f"backward config 3: {key} err={e:.3e}")
         assert e <= BF16_TOL, key
+
+
+# ------------------------------------------------------------------ fp32
+F32_TOL = 1e-4
+
+
+@pytest.mark.parametrize("T,H,F,N,bias", [
+    (136, 72, 2 * 48, 2, True),     # ragged tiles
+    (512, 256, 4 * 64, 4, False),
+])
+def test_backward_f32_vs_oracle(T, H, F, N, bias):
+    say(f"mlp_backward fp32 T={T} H={H} F={F} N={N} bias={bias}")
+    rng = np.random.default_rng(T + H + F)
+    h = {"X": rng.standard_normal((T, H)).astype(np.float32),
+         "A": (rng.standard_normal((F, H)) * 0.05).astype(np.float32),
+         "a": (rng.standard_normal(F) * 0.05).astype(np.float32) if bias else None,
+         "B": (rng.standard_normal((H, F)) * 0.05).astype(np.float32),
+         "dY": rng.standard_normal((T, H)).astype(np.float32)}
+    X, A, a, B, dY = (dev(h[k], torch.float32) for k in ("X", "A", "a", "B", "dY"))
+    g, _ = tp.mlp_backward(X, A, a, B, dY, N, need_da=bias)
+    torch.cuda.synchronize()
+    ref = R.mlp_gelu_backward(h["X"], h["A"], h["a"], h["B"], h["dY"])
+    for k in KEYS:
+        if k == "da" and not bias:
+            continue
+        e = err(_np(g[k]), ref[k])
+        say(f"  {k}: err={e:.3e}")
+        assert e <= F32_TOL, k
+
+
+def test_backward_f32_full_size_workload_1():
+    """The fp32 workload (T=128, H=512, F=2048, N=2) against the full oracle."""
+    w = configs.CONFIGS[1]
+    host = inputs.make_inputs(w)
+    dY_h = inputs.grad_output(w)
+    d = workloads.device_inputs(w, host)
+    g, _ = workloads.backward(w, d, dev(dY_h, torch.float32))
+    torch.cuda.synchronize()
+    ref = R.mlp_gelu_backward(host["X"], host["A"], host["a"], host["B"], dY_h)
+    for k in KEYS:
+        e = err(_np(g[k]), ref[k])
+        say(f"backward config 1: {k} err={e:.3e}")
+        assert e <= F32_TOL, k
