@@ -45,6 +45,7 @@ __all__ = [
     "gelu_grad", "mlp_backward", "mlp_backward_sharded",
     "padded_vocab", "cross_entropy", "lm_head_ce", "vocab_parallel_ce",
     "silu_grad", "mlp_swiglu_backward", "mlp_swiglu_backward_sharded",
+    "vocab_parallel_embedding",
 ]
 
 _SQRT2 = math.sqrt(2.0)
@@ -560,6 +561,29 @@ def vocab_parallel_ce(X, E, labels, V, N):
         S = S + s_ * np.exp(m - M)
     target = _fold(zs)
     return np.log(S) + M - target, (ms, ss, zs)
+
+
+def vocab_parallel_embedding(ids, E, V, N):
+    """Input side of the vocab split ([Blog] 6.2: the embedding matrix
+    (vocab, hidden) is split along the vocab like the output head;
+    [Wiki] practice section: vocab-parallel embedding).  Shard i owns padded
+    vocab rows [i Vs, (i+1) Vs) and looks up only the ids it owns, writing
+    zero rows for the others; the N partials are summed in shard order (the
+    all-reduce), so every token gets exactly its own row.  Rows >= V are
+    padding and never read; an id outside [0, V) has no owner and gets a
+    zero row.  Returns (rows [T x H], list of per-shard partials)."""
+    ids = np.asarray(ids)
+    E = _f64(E)
+    Vp, Vs = padded_vocab(V, N)
+    T, H = ids.shape[0], E.shape[1]
+    parts = []
+    for i in range(N):
+        lo, hi = i * Vs, min((i + 1) * Vs, V)
+        own = (ids >= lo) & (ids < hi)
+        P = np.zeros((T, H))
+        P[own] = E[ids[own]]
+        parts.append(P)
+    return _fold(parts), parts
 
 
 # --------------------------------------------------------------------------

@@ -127,3 +127,39 @@ def test_planted_vocab_mistakes_are_caught(kind):
     want = O.lm_head_ce(X, E, labels, V)
     assert np.max(np.abs(O.vocab_parallel_ce(X, E, labels, V, N)[0] - want)) <= 1e-12
     assert np.max(np.abs(_mutant(kind, X, E, labels, V, N) - want)) > 1e-3
+
+
+# ------------------------------------------------------------------ embedding (input side)
+@pytest.mark.parametrize("V,N", [(37, 4), (64, 8), (9, 8), (1000, 3)])
+def test_vocab_parallel_embedding_is_the_plain_lookup(V, N):
+    rng = np.random.default_rng(V + N)
+    Vp, Vs = O.padded_vocab(V, N)
+    E = rng.standard_normal((Vp, 6))
+    E[V:] = np.nan  # padding rows must never be read
+    ids = rng.integers(0, V, 50)
+    Y, parts = O.vocab_parallel_embedding(ids, E, V, N)
+    assert np.array_equal(Y, E[ids])  # exact: one nonzero term per element
+    nonzero = np.stack([np.any(p != 0, axis=1) for p in parts])
+    assert np.all(nonzero.sum(axis=0) == 1)  # exactly one owner per token
+
+
+def test_vocab_parallel_embedding_out_of_range_ids_give_zero_rows():
+    V, N = 20, 4
+    Vp, _ = O.padded_vocab(V, N)
+    E = np.arange(Vp * 3, dtype=float).reshape(Vp, 3) + 1.0
+    Y, _ = O.vocab_parallel_embedding(np.array([-1, 0, 19, 20, Vp + 5]), E, V, N)
+    assert np.array_equal(Y[[0, 3, 4]], np.zeros((3, 3)))
+    assert np.array_equal(Y[[1, 2]], E[[0, 19]])
+
+
+def test_planted_embedding_mistake_padding_owned():
+    """A shard that also owns the padding rows of its range would read them."""
+    V, N = 37, 4
+    Vp, Vs = O.padded_vocab(V, N)
+    E = np.ones((Vp, 2))
+    E[V:] = np.nan
+    ids = np.array([V + 1])  # a padding id, as a buggy tokenizer could emit
+    Y, _ = O.vocab_parallel_embedding(ids, E, V, N)
+    assert np.all(Y == 0)
+    wrong = E[ids]  # looking up without the range check
+    assert np.isnan(wrong).all()
