@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "TFLOP/s per sharded TP MLP/attn layer fwd on 1 GPU; % of bf16 MFMA peak"
 METRIC_BWD = "TFLOP/s per sharded TP MLP layer bwd on 1 GPU; % of bf16 MFMA peak"
 METRIC_VOCAB = "TFLOP/s of the vocab-parallel output head + cross-entropy fwd on 1 GPU; % of bf16 MFMA peak"
+METRIC_EMBED = "GB/s (algorithmic bytes) of the vocab-parallel embedding lookup fwd on 1 GPU; % of HBM peak"
 PEAK_BF16 = 2.5e15     # dense MFMA, bf16
 PEAK_F32 = 157.3e12    # dense MFMA, fp32
 PEAK_HBM = 8.0e12      # bytes/s
@@ -82,6 +83,10 @@ def kernel_work(w, name, shards_per_launch, rows_reduced):
             return 0.0, 12 * N * T + 4 * T
         if name == "vocab_ce_mean":
             return 0.0, 4 * T + 4
+    if w.kind == "vocab_embed" and name == "vocab_embed_partial":
+        # ids read by every shard, each token's own row read once (by its
+        # owner; c/N of the tokens on average), one fp32 partial per shard out
+        return 0.0, 4 * c * T + es * T * H * c / N + 4 * c * T * H
     if name == "reduce_partials":
         return 0.0, 4 * N * rows_reduced * H + es * rows_reduced * H + (es * H if w.sigma_bias else 0)
     if name == "rmsnorm_gather":  # square, add, two scalings per element; X read once, Y written once
@@ -176,7 +181,7 @@ KERNEL_SOURCES = {
     "bwd_dz_gemm": "gemm.hip", "bwd_dx_gemm": "gemm.hip", "bwd_da_gemm": "gemm.hip", "bwd_db_gemm": "gemm.hip",
     "bwd_splitk_reduce": "reduce.hip", "bwd_fused_gemm": "gemm.hip",
     "vocab_logits_gemm": "gemm.hip", "vocab_ce_fold": "vocab.hip", "vocab_ce_combine": "vocab.hip",
-    "vocab_ce_mean": "vocab.hip",
+    "vocab_ce_mean": "vocab.hip", "vocab_embed_partial": "vocab.hip",
 }
 
 
@@ -203,7 +208,7 @@ KERNEL_SYMBOL = {
     "bwd_dz_gemm": "gemm_", "bwd_dx_gemm": "gemm_", "bwd_da_gemm": "gemm_", "bwd_db_gemm": "gemm_",
     "bwd_splitk_reduce": "reduce_kernel", "bwd_fused_gemm": "gemm_",
     "vocab_logits_gemm": "gemm_", "vocab_ce_fold": "ce_fold_kernel", "vocab_ce_combine": "ce_combine_kernel",
-    "vocab_ce_mean": "ce_mean_kernel",
+    "vocab_ce_mean": "ce_mean_kernel", "vocab_embed_partial": "embed_partial_kernel",
 }
 
 
@@ -232,6 +237,8 @@ def launch_order(w, sp_entry=False, backward=False):
         return backward_launch_order(w)
     if w.kind == "vocab_ce":
         return ["vocab_logits_gemm", "vocab_ce_fold", "vocab_ce_combine", "vocab_ce_mean"]
+    if w.kind == "vocab_embed":
+        return ["vocab_embed_partial", "reduce_partials"]
     head = ["rmsnorm_gather"] if sp_entry else []
     if w.kind == "attn":
         return head + ["attn_qk_gemm", "attn_vt_gemm", "attn_core", "attn_out_gemm", "reduce_partials"]
@@ -396,6 +403,8 @@ def cpu_baseline(w, host, seconds):
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
+    if w.kind == "vocab_embed":
+        return cpu_baseline_embed(w, host, seconds, cores)
     chunk = 256 if w.kind != "attn" else 8
     order = np.random.default_rng(w.seed + 98).permutation(w.T)  # seeded order of all token rows
     done, flops = 0, 0.0
@@ -417,6 +426,29 @@ def cpu_baseline(w, host, seconds):
     return {"value": round(flops / el / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done} token rows in seeded order over the workload's {w.T} "
                       f"({done / w.T:.2f} passes), fp64 numpy/scipy, {el:.1f} s"}
+
+
+def cpu_baseline_embed(w, host, seconds, cores):
+    """fp64 oracle lookup (every shard's masked lookup, then the fold) on
+    seeded blocks of 2048 token rows; GB/s counted with the same algorithmic
+    bytes per token as the GPU figure."""
+    import numpy as np
+
+    from oracle import reference as R
+
+    order = np.random.default_rng(w.seed + 98).permutation(w.T)
+    per_token = sum(kernel_work(w, k, w.N, w.T)[1] for k in launch_order(w)) / w.T
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        start = done % w.T
+        rows = np.sort(order[start:start + 2048])
+        R.workload(w.kind, host, rows=rows, N=w.N)
+        done += len(rows)
+    el = time.perf_counter() - t0
+    return {"value": round(done * per_token / el / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} token rows in seeded blocks of 2048 over the workload's {w.T}, fp64 numpy "
+                      f"(each call converts the table to fp64), {el:.1f} s"}
 
 
 def cpu_baseline_backward(w, host, dY, seconds):
@@ -460,8 +492,9 @@ def main():
                     help="untimed warmup steps (default: as many as fill about 0.5 s, at least 5); "
                          "the shader clock takes tens of ms to settle after idle")
     ap.add_argument("--config", type=int, default=2,
-                    help="workload 1..5 (default 2: GELU MLP bf16, T=16384, H=512, F=2048, N=4), or 6: the "
-                         "vocab-parallel output head + cross-entropy (T=16384, H=4096, V=150000, N=8)")
+                    help="workload 1..5 (default 2: GELU MLP bf16, T=16384, H=512, F=2048, N=4), 6: the "
+                         "vocab-parallel output head + cross-entropy (T=16384, H=4096, V=150000, N=8), or 7: the "
+                         "vocab-parallel embedding lookup (same sizes)")
     ap.add_argument("--share", choices=["layer", "rank"], default="layer")
     ap.add_argument("--sp-entry", action="store_true",
                     help="MLP workloads with a reduce-scatter: start each step with the sequence-parallel entry "
@@ -515,8 +548,8 @@ def main():
 
     tp.lib()  # fails loudly if libtp.so is missing
     w = configs.workload(args.config)
-    if w.kind == "vocab_ce" and (args.share != "layer" or args.sp_entry or args.backward):
-        print("bench.py: the vocab cross-entropy workload (--config 6) runs with --share layer only",
+    if w.kind in ("vocab_ce", "vocab_embed") and (args.share != "layer" or args.sp_entry or args.backward):
+        print("bench.py: the vocab workloads (--config 6, 7) run with --share layer only",
               file=sys.stderr, flush=True)
         sys.exit(2)
     if args.overlap and (w.kind not in ("mlp_gelu", "mlp_swiglu") or args.share != "layer" or args.backward
@@ -649,6 +682,9 @@ def main():
     if args.backward:
         flops = backward_flops(w, w.N)
     value = flops / (ms_step / 1e3) / 1e12
+    if w.kind == "vocab_embed":  # a lookup: algorithmic bytes of the step (every kernel) per second
+        step_bytes = sum(kernel_work(w, k, shards, rows_red)[1] for k in launch_order(w))
+        value = step_bytes / (ms_step / 1e3) / 1e9
 
     # with --overlap each launch covers one row block of T/K tokens
     wk = configs.scaled(w, batch=1, seq=w.T // args.overlap) if args.overlap else w
@@ -672,9 +708,10 @@ def main():
     roof["traffic"] = measured_traffic(dom, workload_tag(w, args.sp_entry, args.backward))
 
     out = {
-        "metric": METRIC_BWD if args.backward else METRIC_VOCAB if w.kind == "vocab_ce" else METRIC,
+        "metric": (METRIC_BWD if args.backward else METRIC_VOCAB if w.kind == "vocab_ce" else
+                   METRIC_EMBED if w.kind == "vocab_embed" else METRIC),
         "value": round(value, 3),
-        "unit": "TFLOP/s",
+        "unit": "GB/s" if w.kind == "vocab_embed" else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -690,6 +727,9 @@ def main():
             "ffn": w.F if w.kind in ("mlp_gelu", "mlp_swiglu") else None, "heads": w.heads or None, "shards": w.N,
             **({"vocab": w.F, "vocab_padded": tp.tp_vocab_padded(w.F, w.N),
                 "labels": inputs.LABEL_RECIPE} if w.kind == "vocab_ce" else {}),
+            **({"vocab": w.F, "vocab_padded": tp.tp_vocab_padded(w.F, w.N), "ids": inputs.ID_RECIPE,
+                "bytes_counted": "ids per shard, each token's row once, N fp32 partials written and read, "
+                                 "the rows written"} if w.kind == "vocab_embed" else {}),
             "share": "all shards + reduction" if args.share == "layer" else "rank 0 shard + reduction",
             "reduce_scatter_slices": w.n_slices, "seed": w.seed,
             **({"sp_entry": {"norm": "rmsnorm", "eps": inputs.NORM_EPS, "gain": inputs.NORM_GAIN_RECIPE}}
@@ -701,7 +741,9 @@ def main():
                 "split_k": backward_splits(w.T, 2 * w.F if w.kind == "mlp_swiglu" else w.F, w.H)}
                if args.backward else {}),
         },
-        "pct_of_bf16_mfma_peak": round(100 * value * 1e12 / PEAK_BF16, 2) if w.dtype == "bf16" else None,
+        "pct_of_bf16_mfma_peak": (round(100 * value * 1e12 / PEAK_BF16, 2)
+                                  if w.dtype == "bf16" and w.kind != "vocab_embed" else None),
+        **({"pct_of_hbm_peak": round(100 * value * 1e9 / PEAK_HBM, 2)} if w.kind == "vocab_embed" else {}),
         "roofline": roof,
         "kernels": kernels,
         "kernel_source_hash": src_hash,

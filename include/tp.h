@@ -299,6 +299,32 @@ size_t tp_vocab_ce_workspace_size(const tp_vocab_ce_desc* d);
 tp_status tp_vocab_ce_forward(void* stream, const tp_vocab_ce_desc* d, void* ws, size_t ws_bytes);
 
 /*
+ * Vocab-parallel embedding lookup (the input side of the vocab split; blog
+ * post at 2kiu.com, section 6.2: the embedding matrix is split along the
+ * vocab like the output head, padded so TP divides it; "张量并行", practice
+ * section: vocab-parallel embedding).  Shard i owns padded vocab rows
+ * [i*Vs, (i+1)*Vs) (Vs as in tp_vocab_padded) and looks up only the ids it
+ * owns, writing zero rows for the others -- one fp32 partial [T x H] per
+ * shard, slot i of the workspace slab.  When the range covers all N shards
+ * the partials are folded in shard order (the all-reduce stand-in) and cast
+ * once: Y[t] = E[ids[t]] exactly.  Rows >= V of E are never read; an id
+ * outside [0, V) has no owner and gets a zero row.
+ *
+ *   ids  [T] int32;  E [Vp x H] dt (Vp = tp_vocab_padded(V, N));  Y [T x H] dt
+ * dt is TP_BF16 or TP_F32; H a multiple of 8.
+ */
+typedef struct {
+  tp_dtype dt;
+  int64_t T, H, V;
+  int N, shard_begin, shard_count;
+  const int32_t* ids;
+  const void* E;
+  void* Y;
+} tp_vocab_embed_desc;
+size_t tp_vocab_embed_workspace_size(const tp_vocab_embed_desc* d);
+tp_status tp_vocab_embed_forward(void* stream, const tp_vocab_embed_desc* d, void* ws, size_t ws_bytes);
+
+/*
  * Local causal attention alone (the middle step of tp_attn_forward), for
  * `heads` heads of width 128 over `batch` sequences of length `seq`:
  *   QK  [batch*seq x ldqk]: head h's query at columns h*128.., its key at

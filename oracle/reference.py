@@ -38,9 +38,20 @@ def vocab_ce(X, E, labels, V, rows=None):
     return O.lm_head_ce(X[rows], E, np.asarray(labels)[rows], V)
 
 
-def workload(kind, host, batch=None, seq=None, heads=None, rows=None):
+def vocab_embed(E, ids, V, N, rows=None):
+    """Embedding rows of the vocab-parallel lookup for the token rows
+    ``rows`` (all if None); E is the table over the real vocab, [V x H]."""
+    ids = np.asarray(ids)
+    if rows is not None:
+        ids = ids[rows]
+    return O.vocab_parallel_embedding(ids, E, V, N)[0]
+
+
+def workload(kind, host, batch=None, seq=None, heads=None, rows=None, N=None):
     """Expected output rows of one workload ("mlp_gelu" | "mlp_swiglu" |
-    "attn" | "vocab_ce": the per-token loss)."""
+    "attn" | "vocab_ce": the per-token loss | "vocab_embed": N shards)."""
+    if kind == "vocab_embed":
+        return vocab_embed(host["E"], host["ids"], host["E"].shape[0], N, rows)
     if kind == "vocab_ce":
         return vocab_ce(host["X"], host["E"], host["labels"], host["E"].shape[0], rows)
     if kind == "mlp_gelu":

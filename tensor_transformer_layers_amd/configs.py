@@ -22,12 +22,12 @@ from dataclasses import dataclass, field
 class Workload:
     key: int
     name: str
-    kind: str               # "mlp_gelu" | "mlp_swiglu" | "attn" | "vocab_ce"
+    kind: str               # "mlp_gelu" | "mlp_swiglu" | "attn" | "vocab_ce" | "vocab_embed"
     dtype: str              # "f32" | "bf16"  (inputs; accumulation is fp32)
     batch: int
     seq: int
     H: int                  # hidden
-    F: int                  # FFN / intermediate (attention: unused, = H; vocab_ce: the vocab size)
+    F: int                  # FFN / intermediate (attention: unused, = H; vocab_*: the vocab size)
     N: int                  # tensor-parallel shards
     sigma_x: float = 1.0
     sigma_w: float = 0.02
@@ -52,6 +52,8 @@ class Workload:
         and add counted as 2).  Causal attention counts the lower triangle
         with the diagonal: 4 * d * S(S+1)/2 per (batch, head)."""
         T, H = self.T, self.H
+        if self.kind == "vocab_embed":  # a lookup: no arithmetic
+            return 0.0
         if self.kind == "vocab_ce":  # the head's product over the real vocab, one shard's share
             return 2.0 * T * H * self.F / self.N
         if self.kind == "mlp_gelu":
@@ -94,6 +96,11 @@ EXTRA: dict[int, Workload] = {
     6: Workload(6, "vocab_ce_bf16_T16384_H4096_V150000_N8", "vocab_ce", "bf16",
                 batch=8, seq=2048, H=4096, F=150000, N=8,
                 sigma_w=0.02, sigma_bias=None, seed=20260006),
+    # the input side of the same split: the vocab-parallel embedding lookup
+    # of those 8 x 2048 tokens in the same padded 150k x 4096 table
+    7: Workload(7, "vocab_embed_bf16_T16384_H4096_V150000_N8", "vocab_embed", "bf16",
+                batch=8, seq=2048, H=4096, F=150000, N=8,
+                sigma_w=0.02, sigma_bias=None, seed=20260007),
 }
 
 

@@ -555,6 +555,27 @@ tp_status validate_vocab(const tp_vocab_ce_desc* d, VocabShape* sh) {
   return TP_OK;
 }
 
+tp_status validate_embed(const tp_vocab_embed_desc* d, size_t* need) {
+  if (!d) return fail(TP_ERR_NULL, "descriptor is NULL");
+  TP_TRY(check_dtype(d->dt));
+  if (d->T < 0 || d->H <= 0 || d->V <= 0 || d->N <= 0)
+    return fail(TP_ERR_SHAPE, "T=%lld H=%lld V=%lld N=%d", (long long)d->T, (long long)d->H, (long long)d->V, d->N);
+  if (d->shard_begin < 0 || d->shard_count < 1 || d->shard_begin + d->shard_count > d->N)
+    return fail(TP_ERR_SHAPE, "shard range [%d, %d) outside [0, %d)", d->shard_begin,
+                d->shard_begin + d->shard_count, d->N);
+  *need = 0;
+  if (d->T == 0) return TP_OK;
+  if (d->H % 8) return fail(TP_ERR_ALIGN, "hidden H=%lld is not a multiple of 8", (long long)d->H);
+  const int64_t vec = vec_of(d->dt);
+  TP_TRY(check_matrix("E", d->E, vocab_shard_width(d->V, d->N) * d->N, d->H, d->H, vec));
+  if (!d->ids) return fail(TP_ERR_NULL, "ids is NULL");
+  if (!aligned16(d->ids)) return fail(TP_ERR_ALIGN, "ids is not 16-byte aligned");
+  if (d->shard_count == d->N) TP_TRY(check_matrix("Y", d->Y, d->T, d->H, d->H, vec));
+  if (d->T > kIntMax) return fail(TP_ERR_SHAPE, "T exceeds 2^31-1");
+  *need = align256((size_t)d->N * d->T * d->H * sizeof(float));
+  return TP_OK;
+}
+
 tp_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (!ws) return fail(TP_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (!aligned16(ws)) return fail(TP_ERR_ALIGN, "workspace is not 16-byte aligned");
@@ -1021,6 +1042,40 @@ tp_status tp_vocab_ce_forward(void* stream, const tp_vocab_ce_desc* d, void* ws,
     TP_TRY(hip_status(e, "vocab_ce_mean"));
   }
   return ok();
+}
+
+size_t tp_vocab_embed_workspace_size(const tp_vocab_embed_desc* d) {
+  size_t need = 0;
+  return validate_embed(d, &need) == TP_OK ? need : 0;
+}
+
+tp_status tp_vocab_embed_forward(void* stream, const tp_vocab_embed_desc* d, void* ws, size_t ws_bytes) {
+  size_t need = 0;
+  TP_TRY(validate_embed(d, &need));
+  if (d->T == 0) return ok();
+  TP_TRY(check_ws(ws, ws_bytes, need));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t T = d->T, H = d->H;
+  float* P = static_cast<float*>(ws);
+  tp::EmbedParams e{};
+  e.ids = d->ids;
+  e.E = d->E;
+  e.P = P + (size_t)d->shard_begin * T * H;
+  e.sP = T * H;
+  e.T = T;
+  e.H = H;
+  e.V = d->V;
+  e.Vs = vocab_shard_width(d->V, d->N);
+  e.shard0 = d->shard_begin;
+  e.shards = d->shard_count;
+  {
+    KernelTimer kt("vocab_embed_partial", s);
+    const hipError_t r = tp::launch_embed_partial(e, d->dt == TP_F32, s);
+    kt.stop();
+    TP_TRY(hip_status(r, "vocab_embed_partial"));
+  }
+  if (d->shard_count < d->N) return ok();
+  return run_reduce(s, d->dt, d->N, T, H, P, T * H, nullptr, d->Y, 1, -1);
 }
 
 tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t ws_bytes) {

@@ -196,4 +196,17 @@ struct CeCombineParams {
 hipError_t launch_ce_combine(const CeCombineParams& p, hipStream_t s);
 hipError_t launch_ce_mean(const float* loss, int64_t T, float* mean, hipStream_t s);
 
+// Vocab-parallel embedding, one partial per shard of the launch: partial s
+// (at P + s*sP, [T x H] fp32) holds row ids[t] of E for the tokens whose id
+// lies in [(shard0+s)*Vs, min(+Vs, V)) and zeros elsewhere.  H a multiple of
+// 8 (bf16) or 4 (fp32).
+struct EmbedParams {
+  const int32_t* ids;
+  const void* E;
+  float* P;
+  int64_t sP, T, H, V, Vs;
+  int shard0, shards;
+};
+hipError_t launch_embed_partial(const EmbedParams& p, bool f32, hipStream_t s);
+
 }  // namespace tp

@@ -6,6 +6,9 @@
 //   ce_combine_kernel  per token: the fold over shards in shard order,
 //                      loss = log S + M - target
 //   ce_mean_kernel     the mean over tokens, in a fixed order
+//   embed_partial_kernel  the input side: each shard's masked lookup of the
+//                      token ids it owns (zero rows elsewhere), folded after
+//                      by the reduction kernel
 // The blog post at 2kiu.com, section 6.2: each shard computes only its own
 // vocab partition's logits and its part of the loss, an all-reduce combines
 // them, and the vocab padding is left out of the loss.
@@ -20,6 +23,37 @@ namespace tp {
 namespace {
 
 constexpr int kThreads = 256;
+
+// Input side: one wave per (shard, token) row of the partial slab.  The
+// shard that owns the token's id copies its embedding row (converted to
+// fp32); every other shard writes a zero row.  Lane l moves elements
+// 4l .. 4l+3 of each 256-element stretch, so every store instruction of the
+// wave writes one contiguous 1 KiB span.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void embed_partial_kernel(EmbedParams p) {
+  typedef E ev __attribute__((ext_vector_type(4)));
+  constexpr int kRows = kThreads / kWave;
+  const int64_t row = (int64_t)blockIdx.x * kRows + (threadIdx.x >> 6);
+  if (row >= (int64_t)p.shards * p.T) return;  // whole waves leave together
+  const int lane = lane_id();
+  const int s = (int)(row / p.T);
+  const int64_t t = row - (int64_t)s * p.T;
+  const int64_t lo = (int64_t)(p.shard0 + s) * p.Vs, hi = min(lo + p.Vs, p.V);
+  const int64_t id = p.ids[t];
+  const bool own = id >= lo && id < hi;
+  const E* const src = static_cast<const E*>(p.E) + (own ? id : 0) * p.H;
+  float* const dst = p.P + (int64_t)s * p.sP + t * p.H;
+#pragma unroll 4
+  for (int64_t c = (int64_t)lane * 4; c < p.H; c += 4 * kWave) {
+    floatx4 o = {0.f, 0.f, 0.f, 0.f};
+    if (own) {
+      const ev v = *reinterpret_cast<const ev*>(src + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = static_cast<float>(v[e]);
+    }
+    *reinterpret_cast<floatx4*>(dst + c) = o;
+  }
+}
 
 // One thread per (shard, token): the fold of the shard's 64-column chunk
 // statistics in chunk order (consecutive threads read consecutive tokens).
@@ -73,6 +107,18 @@ __global__ __launch_bounds__(kThreads) void ce_mean_kernel(const float* loss, in
 }
 
 }  // namespace
+
+hipError_t launch_embed_partial(const EmbedParams& p, bool f32, hipStream_t s) {
+  constexpr int kRows = kThreads / kWave;
+  const int64_t grid = ((int64_t)p.shards * p.T + kRows - 1) / kRows;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  if (f32)
+    launch_kernel(embed_partial_kernel<float>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  else
+    launch_kernel(embed_partial_kernel<bf16>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_ce_fold(const CeFoldParams& p, hipStream_t s) {
   const int64_t grid = ((int64_t)p.shards * p.T + kThreads - 1) / kThreads;

@@ -36,6 +36,7 @@ TENSORS = {
     "mlp_swiglu": ["X", "Wg", "Wu", "Wd"],
     "attn": ["X", "Wq", "Wk", "Wv", "Wo"],
     "vocab_ce": ["X", "E"],
+    "vocab_embed": ["E"],
 }
 
 
@@ -91,6 +92,8 @@ def shapes(w: Workload) -> dict:
         return {"X": (T, H), "Wq": (H, H), "Wk": (H, H), "Wv": (H, H), "Wo": (H, H)}
     if w.kind == "vocab_ce":  # E: the output head over the real vocab, [V x H]
         return {"X": (T, H), "E": (F, H)}
+    if w.kind == "vocab_embed":  # E: the embedding table over the real vocab, [V x H]
+        return {"E": (F, H)}
     raise ValueError(w.kind)
 
 
@@ -117,6 +120,8 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
     if w.kind == "vocab_ce":
         out["labels"] = labels(w) if seed == w.seed else \
             np.random.default_rng(np.random.SeedSequence([seed, 3])).integers(0, w.F, size=w.T).astype(np.int32)
+    if w.kind == "vocab_embed":
+        out["ids"] = token_ids(w, seed)
     return out
 
 
@@ -168,4 +173,16 @@ LABEL_RECIPE = "uniform integers in [0, V), SeedSequence([seed, 3])"
 def labels(w: Workload) -> np.ndarray:
     """Target ids [T] (int32) of workload w (recipe above)."""
     rng = np.random.default_rng(np.random.SeedSequence([w.seed, 3]))
+    return rng.integers(0, w.F, size=w.T).astype(np.int32)
+
+
+# Vocab-parallel embedding: the token id of each row, uniform over the real
+# vocab, from its own stream of the seed.
+ID_RECIPE = "uniform integers in [0, V), SeedSequence([seed, 4])"
+
+
+def token_ids(w: Workload, seed: int | None = None) -> np.ndarray:
+    """Token ids [T] (int32) of workload w (recipe above)."""
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 4]))
     return rng.integers(0, w.F, size=w.T).astype(np.int32)

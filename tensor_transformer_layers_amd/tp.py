@@ -65,6 +65,15 @@ class VocabCeDesc(ctypes.Structure):
     ]
 
 
+class VocabEmbedDesc(ctypes.Structure):
+    _fields_ = [
+        ("dt", _int),
+        ("T", _i64), ("H", _i64), ("V", _i64),
+        ("N", _int), ("shard_begin", _int), ("shard_count", _int),
+        ("ids", _vp), ("E", _vp), ("Y", _vp),
+    ]
+
+
 _SIGS = {
     "tp_column_linear": (_int, [_vp, _int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64]),
     "tp_row_linear_partial": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]),
@@ -83,6 +92,8 @@ _SIGS = {
     "tp_vocab_padded": (_i64, [_i64, _int]),
     "tp_vocab_ce_workspace_size": (_sz, [ctypes.POINTER(VocabCeDesc)]),
     "tp_vocab_ce_forward": (_int, [_vp, ctypes.POINTER(VocabCeDesc), _vp, _sz]),
+    "tp_vocab_embed_workspace_size": (_sz, [ctypes.POINTER(VocabEmbedDesc)]),
+    "tp_vocab_embed_forward": (_int, [_vp, ctypes.POINTER(VocabEmbedDesc), _vp, _sz]),
     "tp_attn_local": (_int, [_vp, _i64, _i64, _int, _int, _vp, _i64, _i64, _vp, _i64, _vp, _i64]),
     "tp_timing_enable": (_int, [_int]),
     "tp_timing_read": (_int, [_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
@@ -178,6 +189,14 @@ def tp_vocab_ce_workspace_size(desc: VocabCeDesc) -> int:
 
 def tp_vocab_ce_forward(stream, desc: VocabCeDesc, ws, ws_bytes) -> int:
     return lib().tp_vocab_ce_forward(stream, ctypes.byref(desc), ws, ws_bytes)
+
+
+def tp_vocab_embed_workspace_size(desc: VocabEmbedDesc) -> int:
+    return lib().tp_vocab_embed_workspace_size(ctypes.byref(desc))
+
+
+def tp_vocab_embed_forward(stream, desc: VocabEmbedDesc, ws, ws_bytes) -> int:
+    return lib().tp_vocab_embed_forward(stream, ctypes.byref(desc), ws, ws_bytes)
 
 
 def tp_attn_local(*args) -> int:
@@ -440,6 +459,43 @@ def vocab_ce_stats(ws, N, T, Vs, shard_count):
     step = align(N * T * 4)
     f = lambda o: ws[o:o + N * T * 4].view(torch.float32).view(N, T)
     return f(off), f(off + step), f(off + 2 * step)
+
+
+def vocab_embed_forward(ids, E, V, N, shard_begin=0, shard_count=None, Y=None, ws=None, stream=None):
+    """Vocab-parallel embedding lookup; returns (Y [T x H] or None for a
+    partial shard range, workspace).  E must have tp_vocab_padded(V, N) rows;
+    ids are int32.  The per-shard fp32 partials are slot i of the workspace
+    (vocab_embed_partials)."""
+    torch = _torch()
+    if ids.dtype != torch.int32:
+        raise TypeError(f"ids are {ids.dtype}, expected torch.int32")
+    T, H = ids.shape[0], E.shape[1]
+    cnt = N if shard_count is None else shard_count
+    if Y is None and cnt == N:
+        Y = torch.empty((T, H), dtype=E.dtype, device=E.device)
+    if Y is not None:
+        _same_dtype(E, Y=Y)
+    d = VocabEmbedDesc()
+    d.dt = _dt(E)
+    d.T, d.H, d.V = T, H, V
+    d.N, d.shard_begin, d.shard_count = N, shard_begin, cnt
+    d.ids, d.E, d.Y = _ptr(ids), _ptr(E), _ptr(Y)
+    need = tp_vocab_embed_workspace_size(d)
+    if need == 0:
+        if T == 0:
+            check(tp_vocab_embed_forward(_stream(stream), d, None, 0))
+            return Y, ws
+        raise TPError(TP_ERR_SHAPE, last_error())
+    if ws is None or ws.numel() < need:
+        ws = alloc_workspace(need, E.device)
+    check(tp_vocab_embed_forward(_stream(stream), d, _ptr(ws), ws.numel()))
+    return Y, ws
+
+
+def vocab_embed_partials(ws, N, T, H):
+    """View [N x T x H] fp32 of the per-shard partials in an embedding
+    workspace."""
+    return ws[:N * T * H * 4].view(_torch().float32).view(N, T, H)
 
 
 def mlp_forward_overlap(X, A, a, B, b, N, chunks, stream2, act=TP_ACT_GELU, Y=None, ws=None, stream=None):

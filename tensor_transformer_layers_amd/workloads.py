@@ -60,6 +60,13 @@ def device_inputs(w: Workload, host: dict, device="cuda") -> dict:
         d["E"] = to_device(E, dt, device)
         del E
         d["labels"] = torch.from_numpy(np.ascontiguousarray(host["labels"])).to(device)
+    elif w.kind == "vocab_embed":
+        Vp = tp.tp_vocab_padded(w.F, w.N)
+        E = np.zeros((Vp, w.H), dtype=np.float32)
+        E[: w.F] = host["E"]
+        d["E"] = to_device(E, dt, device)
+        del E
+        d["ids"] = torch.from_numpy(np.ascontiguousarray(host["ids"])).to(device)
     else:
         raise ValueError(w.kind)
     return d
@@ -71,7 +78,11 @@ def act_of(w: Workload) -> int:
 
 def forward(w: Workload, d: dict, Y=None, ws=None, shard_begin=0, shard_count=None, slice=-1, stream=None):
     """One pass of the sublayer over shards [shard_begin, shard_begin+count).
-    For the vocab cross-entropy, Y is the per-token loss."""
+    For the vocab cross-entropy, Y is the per-token loss; for the embedding,
+    the looked-up rows."""
+    if w.kind == "vocab_embed":
+        return tp.vocab_embed_forward(d["ids"], d["E"], w.F, w.N, shard_begin=shard_begin,
+                                      shard_count=shard_count, Y=Y, ws=ws, stream=stream)
     if w.kind == "vocab_ce":
         loss, mean, ws = tp.vocab_ce_forward(d["X"], d["E"], d["labels"], w.F, w.N, shard_begin=shard_begin,
                                              shard_count=shard_count, loss=Y, mean=d.get("mean"), ws=ws,

@@ -342,6 +342,50 @@ def test_vocab_ce_small_workspace_and_empty_input(L):
     assert tp.tp_vocab_ce_forward(None, _vce(T=0), None, 0) == tp.TP_OK
 
 
+def _vemb(**kw):
+    d = tp.VocabEmbedDesc()
+    d.dt = tp.TP_BF16
+    d.T, d.H, d.V, d.N = 256, 512, 1000, 8
+    d.shard_begin, d.shard_count = 0, 8
+    d.ids = d.E = d.Y = FAKE
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_vocab_embed_workspace_size_is_host_only(L):
+    align = lambda x: (x + 255) // 256 * 256
+    for kw in ({}, dict(shard_count=1, Y=None), dict(dt=tp.TP_F32)):
+        assert tp.tp_vocab_embed_workspace_size(_vemb(**kw)) == align(8 * 256 * 512 * 4)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dt=7), tp.TP_ERR_DTYPE, ""),
+    (dict(V=0), tp.TP_ERR_SHAPE, "V=0"),
+    (dict(H=516), tp.TP_ERR_ALIGN, "H=516 is not a multiple of 8"),
+    (dict(ids=None), tp.TP_ERR_NULL, "ids is NULL"),
+    (dict(ids=FAKE + 4), tp.TP_ERR_ALIGN, "ids is not 16-byte aligned"),
+    (dict(Y=None), tp.TP_ERR_NULL, "Y is NULL"),
+    (dict(E=FAKE + 8), tp.TP_ERR_ALIGN, "E is not 16-byte aligned"),
+    (dict(shard_begin=7, shard_count=2), tp.TP_ERR_SHAPE, "shard range"),
+])
+def test_vocab_embed_rejects_before_launch(L, kw, status, needle):
+    d = _vemb(**kw)
+    assert tp.tp_vocab_embed_workspace_size(d) == 0
+    assert tp.tp_vocab_embed_forward(None, d, FAKE, 1 << 40) == status, tp.last_error()
+    assert needle in tp.last_error()
+
+
+def test_vocab_embed_small_workspace_and_empty_input(L):
+    d = _vemb()
+    need = tp.tp_vocab_embed_workspace_size(d)
+    assert tp.tp_vocab_embed_forward(None, d, FAKE, need - 1) == tp.TP_ERR_WORKSPACE
+    assert tp.tp_vocab_embed_forward(None, _vemb(T=0), None, 0) == tp.TP_OK
+    # a partial shard range writes no Y, so Y may be NULL
+    d = _vemb(shard_begin=2, shard_count=3, Y=None)
+    assert tp.tp_vocab_embed_forward(None, d, FAKE, need - 1) == tp.TP_ERR_WORKSPACE
+
+
 # ------------------------------------------------------------ overlapped forward
 @pytest.mark.parametrize("kw,chunks,status,needle", [
     (dict(), 0, tp.TP_ERR_SHAPE, "chunks=0"),
@@ -416,3 +460,7 @@ def test_binding_rejects_mismatched_dtypes():
                             50, 2)
     with pytest.raises(TypeError, match="B is torch.float32"):
         tp.mlp_forward(X, B.t().contiguous(), None, B.float(), None, 2)
+    with pytest.raises(TypeError, match="ids"):
+        tp.vocab_embed_forward(torch.zeros(16, dtype=torch.int64), B, 50, 2)
+    with pytest.raises(TypeError, match="Y is torch.float32"):
+        tp.vocab_embed_forward(torch.zeros(16, dtype=torch.int32), B, 50, 2, Y=A)
