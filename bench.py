@@ -85,8 +85,11 @@ def kernel_work(w, name, shards_per_launch, rows_reduced):
             return 0.0, 4 * T + 4
     if w.kind == "vocab_embed" and name == "vocab_embed_partial":
         # ids read by every shard, each token's own row read once (by its
-        # owner; c/N of the tokens on average), one fp32 partial per shard out
-        return 0.0, 4 * c * T + es * T * H * c / N + 4 * c * T * H
+        # owner; c/N of the tokens on average), one partial per shard out, in
+        # the table's type
+        return 0.0, 4 * c * T + es * T * H * c / N + es * c * T * H
+    if w.kind == "vocab_embed" and name == "vocab_embed_fold":  # N partials in, the rows out
+        return 0.0, es * N * T * H + es * T * H
     if name == "reduce_partials":
         return 0.0, 4 * N * rows_reduced * H + es * rows_reduced * H + (es * H if w.sigma_bias else 0)
     if name == "rmsnorm_gather":  # square, add, two scalings per element; X read once, Y written once
@@ -181,7 +184,7 @@ KERNEL_SOURCES = {
     "bwd_dz_gemm": "gemm.hip", "bwd_dx_gemm": "gemm.hip", "bwd_da_gemm": "gemm.hip", "bwd_db_gemm": "gemm.hip",
     "bwd_splitk_reduce": "reduce.hip", "bwd_fused_gemm": "gemm.hip",
     "vocab_logits_gemm": "gemm.hip", "vocab_ce_fold": "vocab.hip", "vocab_ce_combine": "vocab.hip",
-    "vocab_ce_mean": "vocab.hip", "vocab_embed_partial": "vocab.hip",
+    "vocab_ce_mean": "vocab.hip", "vocab_embed_partial": "vocab.hip", "vocab_embed_fold": "vocab.hip",
 }
 
 
@@ -209,6 +212,7 @@ KERNEL_SYMBOL = {
     "bwd_splitk_reduce": "reduce_kernel", "bwd_fused_gemm": "gemm_",
     "vocab_logits_gemm": "gemm_", "vocab_ce_fold": "ce_fold_kernel", "vocab_ce_combine": "ce_combine_kernel",
     "vocab_ce_mean": "ce_mean_kernel", "vocab_embed_partial": "embed_partial_kernel",
+    "vocab_embed_fold": "embed_fold_kernel",
 }
 
 
@@ -238,7 +242,7 @@ def launch_order(w, sp_entry=False, backward=False):
     if w.kind == "vocab_ce":
         return ["vocab_logits_gemm", "vocab_ce_fold", "vocab_ce_combine", "vocab_ce_mean"]
     if w.kind == "vocab_embed":
-        return ["vocab_embed_partial", "reduce_partials"]
+        return ["vocab_embed_partial", "vocab_embed_fold"]
     head = ["rmsnorm_gather"] if sp_entry else []
     if w.kind == "attn":
         return head + ["attn_qk_gemm", "attn_vt_gemm", "attn_core", "attn_out_gemm", "reduce_partials"]
@@ -728,8 +732,8 @@ def main():
             **({"vocab": w.F, "vocab_padded": tp.tp_vocab_padded(w.F, w.N),
                 "labels": inputs.LABEL_RECIPE} if w.kind == "vocab_ce" else {}),
             **({"vocab": w.F, "vocab_padded": tp.tp_vocab_padded(w.F, w.N), "ids": inputs.ID_RECIPE,
-                "bytes_counted": "ids per shard, each token's row once, N fp32 partials written and read, "
-                                 "the rows written"} if w.kind == "vocab_embed" else {}),
+                "bytes_counted": "ids per shard, each token's row once, N partials in the table's type "
+                                 "written and read, the rows written"} if w.kind == "vocab_embed" else {}),
             "share": "all shards + reduction" if args.share == "layer" else "rank 0 shard + reduction",
             "reduce_scatter_slices": w.n_slices, "seed": w.seed,
             **({"sp_entry": {"norm": "rmsnorm", "eps": inputs.NORM_EPS, "gain": inputs.NORM_GAIN_RECIPE}}

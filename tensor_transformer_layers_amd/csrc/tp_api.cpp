@@ -572,7 +572,7 @@ tp_status validate_embed(const tp_vocab_embed_desc* d, size_t* need) {
   if (!aligned16(d->ids)) return fail(TP_ERR_ALIGN, "ids is not 16-byte aligned");
   if (d->shard_count == d->N) TP_TRY(check_matrix("Y", d->Y, d->T, d->H, d->H, vec));
   if (d->T > kIntMax) return fail(TP_ERR_SHAPE, "T exceeds 2^31-1");
-  *need = align256((size_t)d->N * d->T * d->H * sizeof(float));
+  *need = align256((size_t)d->N * d->T * d->H * (d->dt == TP_F32 ? 4 : 2));
   return TP_OK;
 }
 
@@ -1056,11 +1056,12 @@ tp_status tp_vocab_embed_forward(void* stream, const tp_vocab_embed_desc* d, voi
   TP_TRY(check_ws(ws, ws_bytes, need));
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t T = d->T, H = d->H;
-  float* P = static_cast<float*>(ws);
+  const bool f32 = d->dt == TP_F32;
+  char* const P = static_cast<char*>(ws);
   tp::EmbedParams e{};
   e.ids = d->ids;
   e.E = d->E;
-  e.P = P + (size_t)d->shard_begin * T * H;
+  e.P = P + (size_t)d->shard_begin * T * H * (f32 ? 4 : 2);
   e.sP = T * H;
   e.T = T;
   e.H = H;
@@ -1070,12 +1071,22 @@ tp_status tp_vocab_embed_forward(void* stream, const tp_vocab_embed_desc* d, voi
   e.shards = d->shard_count;
   {
     KernelTimer kt("vocab_embed_partial", s);
-    const hipError_t r = tp::launch_embed_partial(e, d->dt == TP_F32, s);
+    const hipError_t r = tp::launch_embed_partial(e, f32, s);
     kt.stop();
     TP_TRY(hip_status(r, "vocab_embed_partial"));
   }
   if (d->shard_count < d->N) return ok();
-  return run_reduce(s, d->dt, d->N, T, H, P, T * H, nullptr, d->Y, 1, -1);
+  tp::EmbedFoldParams f{};
+  f.P = P;
+  f.sP = T * H;
+  f.n = T * H;
+  f.N = d->N;
+  f.Y = d->Y;
+  KernelTimer kt("vocab_embed_fold", s);
+  const hipError_t r = tp::launch_embed_fold(f, f32, s);
+  kt.stop();
+  TP_TRY(hip_status(r, "vocab_embed_fold"));
+  return ok();
 }
 
 tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t ws_bytes) {

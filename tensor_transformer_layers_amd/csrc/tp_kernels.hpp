@@ -196,17 +196,27 @@ struct CeCombineParams {
 hipError_t launch_ce_combine(const CeCombineParams& p, hipStream_t s);
 hipError_t launch_ce_mean(const float* loss, int64_t T, float* mean, hipStream_t s);
 
-// Vocab-parallel embedding, one partial per shard of the launch: partial s
-// (at P + s*sP, [T x H] fp32) holds row ids[t] of E for the tokens whose id
-// lies in [(shard0+s)*Vs, min(+Vs, V)) and zeros elsewhere.  H a multiple of
-// 8 (bf16) or 4 (fp32).
+// Vocab-parallel embedding, one partial per shard of the launch, in the
+// table's type: partial s (at P + s*sP elements, [T x H]) holds row ids[t]
+// of E for the tokens whose id lies in [(shard0+s)*Vs, min(+Vs, V)) and
+// zeros elsewhere.  H a multiple of 8.
 struct EmbedParams {
   const int32_t* ids;
   const void* E;
-  float* P;
+  void* P;
   int64_t sP, T, H, V, Vs;
   int shard0, shards;
 };
 hipError_t launch_embed_partial(const EmbedParams& p, bool f32, hipStream_t s);
+
+// Y[j] = fold over k < N in order of P[k*sP + j] (fp32 adds), cast to the
+// table's type; n = T*H elements, a multiple of 8.
+struct EmbedFoldParams {
+  const void* P;
+  int64_t sP, n;
+  int N;
+  void* Y;
+};
+hipError_t launch_embed_fold(const EmbedFoldParams& p, bool f32, hipStream_t s);
 
 }  // namespace tp

@@ -7,8 +7,8 @@
 //                      loss = log S + M - target
 //   ce_mean_kernel     the mean over tokens, in a fixed order
 //   embed_partial_kernel  the input side: each shard's masked lookup of the
-//                      token ids it owns (zero rows elsewhere), folded after
-//                      by the reduction kernel
+//                      token ids it owns (zero rows elsewhere)
+//   embed_fold_kernel  the fold of those partials in shard order
 // The blog post at 2kiu.com, section 6.2: each shard computes only its own
 // vocab partition's logits and its part of the loss, an all-reduce combines
 // them, and the vocab padding is left out of the loss.
@@ -25,13 +25,15 @@ namespace {
 constexpr int kThreads = 256;
 
 // Input side: one wave per (shard, token) row of the partial slab.  The
-// shard that owns the token's id copies its embedding row (converted to
-// fp32); every other shard writes a zero row.  Lane l moves elements
-// 4l .. 4l+3 of each 256-element stretch, so every store instruction of the
-// wave writes one contiguous 1 KiB span.
+// shard that owns the token's id copies its embedding row; every other shard
+// writes a zero row.  The partials keep the table's type (each holds table
+// entries and zeros, so the fold's sums are exact in any precision).  Lane l
+// moves the 16-byte vector l of each 1 KiB stretch: every load and store
+// instruction of the wave covers one contiguous KiB.
 template <typename E>
 __global__ __launch_bounds__(kThreads) void embed_partial_kernel(EmbedParams p) {
-  typedef E ev __attribute__((ext_vector_type(4)));
+  constexpr int VE = 16 / sizeof(E);
+  typedef E ev __attribute__((ext_vector_type(VE)));
   constexpr int kRows = kThreads / kWave;
   const int64_t row = (int64_t)blockIdx.x * kRows + (threadIdx.x >> 6);
   if (row >= (int64_t)p.shards * p.T) return;  // whole waves leave together
@@ -42,17 +44,44 @@ __global__ __launch_bounds__(kThreads) void embed_partial_kernel(EmbedParams p) 
   const int64_t id = p.ids[t];
   const bool own = id >= lo && id < hi;
   const E* const src = static_cast<const E*>(p.E) + (own ? id : 0) * p.H;
-  float* const dst = p.P + (int64_t)s * p.sP + t * p.H;
+  E* const dst = static_cast<E*>(p.P) + (int64_t)s * p.sP + t * p.H;
 #pragma unroll 4
-  for (int64_t c = (int64_t)lane * 4; c < p.H; c += 4 * kWave) {
-    floatx4 o = {0.f, 0.f, 0.f, 0.f};
-    if (own) {
-      const ev v = *reinterpret_cast<const ev*>(src + c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = static_cast<float>(v[e]);
-    }
-    *reinterpret_cast<floatx4*>(dst + c) = o;
+  for (int64_t c = (int64_t)lane * VE; c < p.H; c += (int64_t)VE * kWave) {
+    ev v = ev{};
+    if (own) v = *reinterpret_cast<const ev*>(src + c);
+    *reinterpret_cast<ev*>(dst + c) = v;
   }
+}
+
+// The embedding's all-reduce stand-in: thread i folds 16-byte vector i of
+// the N partials in shard order ((P0 + P1) + P2) + ... in fp32, then casts
+// back to the table's type (exact: one term per element is nonzero).  All
+// loads of a group of 8 shards are issued before its adds.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void embed_fold_kernel(EmbedFoldParams p) {
+  constexpr int VE = 16 / sizeof(E);
+  typedef E ev __attribute__((ext_vector_type(VE)));
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i * VE >= p.n) return;
+  const E* const src = static_cast<const E*>(p.P) + i * VE;
+  float acc[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = 0.0f;
+  for (int k0 = 0; k0 < p.N; k0 += 8) {
+    ev v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k0 + k < p.N) v[k] = __builtin_nontemporal_load(reinterpret_cast<const ev*>(src + (k0 + k) * p.sP));
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k0 + k < p.N)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[e] += static_cast<float>(v[k][e]);
+  }
+  ev o;
+#pragma unroll
+  for (int e = 0; e < VE; ++e) o[e] = static_cast<E>(acc[e]);
+  *reinterpret_cast<ev*>(static_cast<E*>(p.Y) + i * VE) = o;
 }
 
 // One thread per (shard, token): the fold of the shard's 64-column chunk
@@ -117,6 +146,18 @@ hipError_t launch_embed_partial(const EmbedParams& p, bool f32, hipStream_t s) {
     launch_kernel(embed_partial_kernel<float>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   else
     launch_kernel(embed_partial_kernel<bf16>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_fold(const EmbedFoldParams& p, bool f32, hipStream_t s) {
+  const int64_t vecs = p.n / (f32 ? 4 : 8);
+  const int64_t grid = (vecs + kThreads - 1) / kThreads;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  if (f32)
+    launch_kernel(embed_fold_kernel<float>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  else
+    launch_kernel(embed_fold_kernel<bf16>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

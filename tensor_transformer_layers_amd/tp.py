@@ -464,8 +464,8 @@ def vocab_ce_stats(ws, N, T, Vs, shard_count):
 def vocab_embed_forward(ids, E, V, N, shard_begin=0, shard_count=None, Y=None, ws=None, stream=None):
     """Vocab-parallel embedding lookup; returns (Y [T x H] or None for a
     partial shard range, workspace).  E must have tp_vocab_padded(V, N) rows;
-    ids are int32.  The per-shard fp32 partials are slot i of the workspace
-    (vocab_embed_partials)."""
+    ids are int32.  The per-shard partials, in E's dtype, are slot i of the
+    workspace (vocab_embed_partials)."""
     torch = _torch()
     if ids.dtype != torch.int32:
         raise TypeError(f"ids are {ids.dtype}, expected torch.int32")
@@ -492,10 +492,11 @@ def vocab_embed_forward(ids, E, V, N, shard_begin=0, shard_count=None, Y=None, w
     return Y, ws
 
 
-def vocab_embed_partials(ws, N, T, H):
-    """View [N x T x H] fp32 of the per-shard partials in an embedding
-    workspace."""
-    return ws[:N * T * H * 4].view(_torch().float32).view(N, T, H)
+def vocab_embed_partials(ws, N, T, H, dtype):
+    """View [N x T x H] (``dtype``, the table's) of the per-shard partials in
+    an embedding workspace."""
+    es = _torch().empty((), dtype=dtype).element_size()
+    return ws[:N * T * H * es].view(dtype).view(N, T, H)
 
 
 def mlp_forward_overlap(X, A, a, B, b, N, chunks, stream2, act=TP_ACT_GELU, Y=None, ws=None, stream=None):

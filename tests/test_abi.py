@@ -355,8 +355,10 @@ def _vemb(**kw):
 
 def test_vocab_embed_workspace_size_is_host_only(L):
     align = lambda x: (x + 255) // 256 * 256
-    for kw in ({}, dict(shard_count=1, Y=None), dict(dt=tp.TP_F32)):
-        assert tp.tp_vocab_embed_workspace_size(_vemb(**kw)) == align(8 * 256 * 512 * 4)
+    # one partial per shard in the table's type
+    for kw in ({}, dict(shard_count=1, Y=None)):
+        assert tp.tp_vocab_embed_workspace_size(_vemb(**kw)) == align(8 * 256 * 512 * 2)
+    assert tp.tp_vocab_embed_workspace_size(_vemb(dt=tp.TP_F32)) == align(8 * 256 * 512 * 4)
 
 
 @pytest.mark.parametrize("kw,status,needle", [

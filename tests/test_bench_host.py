@@ -21,14 +21,14 @@ def test_kernel_flops_add_up_to_the_workload(k):
 
 def test_embedding_bytes_and_cpu_baseline():
     """The embedding step's algorithmic bytes: ids once per shard, each row
-    read once, N fp32 partials written, then read by the fold, and the rows
-    written.  The CPU baseline runs the oracle on a small copy of the
+    read once, N partials (bf16, the table's type) written, then read by
+    the fold, and the rows written.  The CPU baseline runs the oracle on a small copy of the
     workload and reports GB/s with those bytes per token."""
     w = configs.workload(7)
-    assert bench.launch_order(w) == ["vocab_embed_partial", "reduce_partials"]
+    assert bench.launch_order(w) == ["vocab_embed_partial", "vocab_embed_fold"]
     T, H, N = w.T, w.H, w.N
     total = sum(bench.kernel_work(w, n, N, T)[1] for n in bench.launch_order(w))
-    assert total == 4 * N * T + 2 * T * H + 4 * N * T * H + 4 * N * T * H + 2 * T * H
+    assert total == 4 * N * T + 2 * T * H + 2 * N * T * H + 2 * N * T * H + 2 * T * H
     assert w.flops_layer() == 0.0
     from tensor_transformer_layers_amd import inputs
     small = configs.scaled(w, batch=1, seq=4096, H=64, F=1000)

@@ -1,9 +1,9 @@
 """Vocab-parallel embedding lookup (the input side of the vocab split): HIP
 path vs the fp64 CPU oracle, through the C ABI (gfx950 GPU required).
 
-Every output element is the fold of N fp32 partials of which at most one is
-nonzero, and the nonzero one is a table entry converted exactly to fp32, so
-the result must equal the oracle bit for bit (bf16 and fp32 tables).
+Every output element is the fp32 fold of N partials (in the table's type) of
+which at most one is nonzero, and the nonzero one is a table entry, so the
+result must equal the oracle bit for bit (bf16 and fp32 tables).
 """
 import sys
 
@@ -82,13 +82,13 @@ def test_one_shard_range_partials():
     E, ids = _case(T, H, V, N, seed=11, dt="bf16")
     Ed, Id = _dev(E, ids, "bf16")
     _, ws = tp.vocab_embed_forward(Id, Ed, V, N)  # fills every slot
-    parts = tp.vocab_embed_partials(ws, N, T, H)
+    parts = tp.vocab_embed_partials(ws, N, T, H, torch.bfloat16)
     parts.fill_(-5.0)
     Y, ws = tp.vocab_embed_forward(Id, Ed, V, N, shard_begin=2, shard_count=3, ws=ws)
     torch.cuda.synchronize()
     assert Y is None
     _, ref_parts = O.vocab_parallel_embedding(ids, E.astype(np.float64), V, N)
-    got = parts.cpu().numpy().astype(np.float64)
+    got = parts.float().cpu().numpy().astype(np.float64)
     for i in range(N):
         if 2 <= i < 5:
             assert np.array_equal(got[i], ref_parts[i]), i
