@@ -25,8 +25,9 @@
  *   names the offending argument and, for divisibility errors, the shard
  *   shapes (the fail-fast divisibility check of the blog post at 2kiu.com,
  *   section 6.1).  No call aborts or throws across the ABI.
- * - Alignment: device pointers 16-byte aligned; bf16 leading dimensions and
- *   contraction sizes multiples of 8 elements, fp32 ones multiples of 4.
+ * - Alignment: device pointers 16-byte aligned (int32 token ids and labels:
+ *   4-byte); bf16 leading dimensions and contraction sizes multiples of 8
+ *   elements, fp32 ones multiples of 4.
  * - All kernels are deterministic: no atomics, fixed summation order.
  */
 #ifndef TP_H_

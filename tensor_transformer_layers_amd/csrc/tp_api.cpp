@@ -36,6 +36,7 @@ tp_status ok() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int64_t vec_of(tp_dtype dt) { return dt == TP_BF16 ? 8 : 4; }
 size_t esize(tp_dtype dt) { return dt == TP_BF16 ? 2 : 4; }
@@ -537,7 +538,7 @@ tp_status validate_vocab(const tp_vocab_ce_desc* d, VocabShape* sh) {
   TP_TRY(check_matrix("X", d->X, d->T, d->H, d->H, 8));
   TP_TRY(check_matrix("E", d->E, sh->Vp, d->H, d->H, 8));
   if (!d->labels) return fail(TP_ERR_NULL, "labels is NULL");
-  if (!aligned16(d->labels)) return fail(TP_ERR_ALIGN, "labels is not 16-byte aligned");
+  if (!aligned4(d->labels)) return fail(TP_ERR_ALIGN, "labels is not 4-byte aligned");
   if (d->shard_count == d->N) {
     if (!d->loss) return fail(TP_ERR_NULL, "loss is NULL");
     if (!aligned16(d->loss)) return fail(TP_ERR_ALIGN, "loss is not 16-byte aligned");
@@ -569,7 +570,7 @@ tp_status validate_embed(const tp_vocab_embed_desc* d, size_t* need) {
   const int64_t vec = vec_of(d->dt);
   TP_TRY(check_matrix("E", d->E, vocab_shard_width(d->V, d->N) * d->N, d->H, d->H, vec));
   if (!d->ids) return fail(TP_ERR_NULL, "ids is NULL");
-  if (!aligned16(d->ids)) return fail(TP_ERR_ALIGN, "ids is not 16-byte aligned");
+  if (!aligned4(d->ids)) return fail(TP_ERR_ALIGN, "ids is not 4-byte aligned");
   if (d->shard_count == d->N) TP_TRY(check_matrix("Y", d->Y, d->T, d->H, d->H, vec));
   if (d->T > kIntMax) return fail(TP_ERR_SHAPE, "T exceeds 2^31-1");
   *need = align256((size_t)d->N * d->T * d->H * (d->dt == TP_F32 ? 4 : 2));

@@ -323,6 +323,7 @@ def test_vocab_ce_workspace_size_is_host_only(L):
     (dict(V=0), tp.TP_ERR_SHAPE, "V=0"),
     (dict(H=516), tp.TP_ERR_ALIGN, "H=516 is not a multiple of 8"),
     (dict(labels=None), tp.TP_ERR_NULL, "labels is NULL"),
+    (dict(labels=FAKE + 2), tp.TP_ERR_ALIGN, "labels is not 4-byte aligned"),
     (dict(loss=None), tp.TP_ERR_NULL, "loss is NULL"),
     (dict(E=FAKE + 8), tp.TP_ERR_ALIGN, "E is not 16-byte aligned"),
     (dict(mean_loss=FAKE + 2), tp.TP_ERR_ALIGN, "mean_loss"),
@@ -366,7 +367,7 @@ def test_vocab_embed_workspace_size_is_host_only(L):
     (dict(V=0), tp.TP_ERR_SHAPE, "V=0"),
     (dict(H=516), tp.TP_ERR_ALIGN, "H=516 is not a multiple of 8"),
     (dict(ids=None), tp.TP_ERR_NULL, "ids is NULL"),
-    (dict(ids=FAKE + 4), tp.TP_ERR_ALIGN, "ids is not 16-byte aligned"),
+    (dict(ids=FAKE + 2), tp.TP_ERR_ALIGN, "ids is not 4-byte aligned"),
     (dict(Y=None), tp.TP_ERR_NULL, "Y is NULL"),
     (dict(E=FAKE + 8), tp.TP_ERR_ALIGN, "E is not 16-byte aligned"),
     (dict(shard_begin=7, shard_count=2), tp.TP_ERR_SHAPE, "shard range"),

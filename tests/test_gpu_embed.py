@@ -126,3 +126,16 @@ def test_vocab_embed_full_size():
     ref, _ = O.vocab_parallel_embedding(Id.cpu().numpy()[rows], E, V, N)
     got = Y[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
     assert np.array_equal(got, ref)
+
+
+def test_ids_at_an_element_offset():
+    """ids need only int32 alignment: a view starting one element in."""
+    T, H, V, N = 99, 128, 500, 4
+    E, ids = _case(T + 1, H, V, N, seed=21, dt="bf16")
+    Ed, Id = _dev(E, ids, "bf16")
+    view = Id[1:]
+    assert view.data_ptr() % 16 == 4
+    Y, _ = tp.vocab_embed_forward(view, Ed, V, N)
+    torch.cuda.synchronize()
+    ref, _ = O.vocab_parallel_embedding(ids[1:], E.astype(np.float64), V, N)
+    assert np.array_equal(Y.float().cpu().numpy().astype(np.float64), ref)

@@ -132,3 +132,17 @@ def test_vocab_ce_full_size():
     e = err(got, ref)
     say(f"vocab config: loss err={e:.3e}")
     assert e <= TOL
+
+
+def test_labels_at_an_element_offset():
+    """labels need only int32 alignment: a view starting one element in."""
+    T, H, V, N = 130, 64, 1000, 4
+    X, E, labels = _case(T, H, V, N, seed=17)
+    Xd, Ed, _ = _dev(X, E, labels)
+    Lbig = torch.from_numpy(np.concatenate([[0], labels]).astype(np.int32)).to(DEV)
+    view = Lbig[1:]
+    assert view.data_ptr() % 16 == 4
+    loss, _, _ = tp.vocab_ce_forward(Xd, Ed, view, V, N)
+    torch.cuda.synchronize()
+    ref = O.lm_head_ce(X, E, labels, V)
+    assert err(loss.cpu().numpy(), ref) <= TOL
