@@ -29,7 +29,8 @@ constexpr int kThreads = 256;
 // writes a zero row.  The partials keep the table's type (each holds table
 // entries and zeros, so the fold's sums are exact in any precision).  Lane l
 // moves the 16-byte vector l of each 1 KiB stretch: every load and store
-// instruction of the wave covers one contiguous KiB.
+// instruction of the wave covers one contiguous KiB.  Non-temporal stores:
+// the slab is read once, by the fold.
 template <typename E>
 __global__ __launch_bounds__(kThreads) void embed_partial_kernel(EmbedParams p) {
   constexpr int VE = 16 / sizeof(E);
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void embed_partial_kernel(EmbedParams p) 
   for (int64_t c = (int64_t)lane * VE; c < p.H; c += (int64_t)VE * kWave) {
     ev v = ev{};
     if (own) v = *reinterpret_cast<const ev*>(src + c);
-    *reinterpret_cast<ev*>(dst + c) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<ev*>(dst + c));
   }
 }
 
