@@ -49,6 +49,8 @@ def _dev(E, ids, dt):
     (64, 520, 9, 8),        # six shards hold only padding; H not a multiple of 512
     (1000, 1024, 50257, 8),
     (300, 256, 4096, 1),
+    (1, 8, 3, 8),           # one token, the smallest hidden size, V < N
+    (5, 8, 1, 1),           # a one-entry vocab on one shard
 ])
 def test_vocab_embed_vs_oracle(T, H, V, N, dt):
     say(f"vocab_embed dt={dt} T={T} H={H} V={V} N={N}")

@@ -55,6 +55,7 @@ def _dev(X, E, labels):
     (64, 64, 9, 8),         # six shards hold only padding
     (1000, 512, 50257, 8),
     (300, 256, 4096, 1),
+    (1, 64, 3, 8),          # one token, V < N: seven shards hold only padding
 ])
 def test_vocab_ce_vs_oracle(T, H, V, N):
     say(f"vocab_ce T={T} H={H} V={V} N={N}")
