@@ -54,35 +54,53 @@ __global__ __launch_bounds__(kThreads) void embed_partial_kernel(EmbedParams p) 
   }
 }
 
-// The embedding's all-reduce stand-in: thread i folds 16-byte vector i of
-// the N partials in shard order ((P0 + P1) + P2) + ... in fp32, then casts
-// back to the table's type (exact: one term per element is nonzero).  All
-// loads of a group of 8 shards are issued before its adds.
+// The embedding's all-reduce stand-in: thread i folds 16-byte vectors
+// i + u * 256 (u < kFoldU, within its workgroup's span) of the N partials in
+// shard order ((P0 + P1) + P2) + ... in fp32, then casts back to the table's
+// type (exact: one term per element is nonzero).  All loads of a group of 8
+// shards are issued before its adds.
+constexpr int kFoldU = 4;
+
 template <typename E>
 __global__ __launch_bounds__(kThreads) void embed_fold_kernel(EmbedFoldParams p) {
   constexpr int VE = 16 / sizeof(E);
   typedef E ev __attribute__((ext_vector_type(VE)));
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i * VE >= p.n) return;
-  const E* const src = static_cast<const E*>(p.P) + i * VE;
-  float acc[VE];
+  const int64_t nv = p.n / VE;
+  const int64_t base = (int64_t)blockIdx.x * kThreads * kFoldU + threadIdx.x;
+  const E* const src = static_cast<const E*>(p.P);
+  float acc[kFoldU][VE];
 #pragma unroll
-  for (int e = 0; e < VE; ++e) acc[e] = 0.0f;
+  for (int u = 0; u < kFoldU; ++u)
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[u][e] = 0.0f;
   for (int k0 = 0; k0 < p.N; k0 += 8) {
-    ev v[8];
+    ev v[8][kFoldU];
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      if (k0 + k < p.N) v[k] = __builtin_nontemporal_load(reinterpret_cast<const ev*>(src + (k0 + k) * p.sP));
+#pragma unroll
+      for (int u = 0; u < kFoldU; ++u) {
+        const int64_t i = base + u * kThreads;
+        if (k0 + k < p.N && i < nv)
+          v[k][u] = __builtin_nontemporal_load(reinterpret_cast<const ev*>(src + (k0 + k) * p.sP + i * VE));
+      }
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       if (k0 + k < p.N)
 #pragma unroll
-        for (int e = 0; e < VE; ++e) acc[e] += static_cast<float>(v[k][e]);
-  }
-  ev o;
+        for (int u = 0; u < kFoldU; ++u)
 #pragma unroll
-  for (int e = 0; e < VE; ++e) o[e] = static_cast<E>(acc[e]);
-  *reinterpret_cast<ev*>(static_cast<E*>(p.Y) + i * VE) = o;
+          for (int e = 0; e < VE; ++e) acc[u][e] += static_cast<float>(v[k][u][e]);
+  }
+#pragma unroll
+  for (int u = 0; u < kFoldU; ++u) {
+    const int64_t i = base + u * kThreads;
+    if (i < nv) {
+      ev o;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) o[e] = static_cast<E>(acc[u][e]);
+      *reinterpret_cast<ev*>(static_cast<E*>(p.Y) + i * VE) = o;
+    }
+  }
 }
 
 // One thread per (shard, token): the fold of the shard's 64-column chunk
@@ -152,7 +170,7 @@ hipError_t launch_embed_partial(const EmbedParams& p, bool f32, hipStream_t s) {
 
 hipError_t launch_embed_fold(const EmbedFoldParams& p, bool f32, hipStream_t s) {
   const int64_t vecs = p.n / (f32 ? 4 : 8);
-  const int64_t grid = (vecs + kThreads - 1) / kThreads;
+  const int64_t grid = (vecs + kThreads * kFoldU - 1) / (kThreads * kFoldU);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (f32)
