@@ -395,6 +395,88 @@ def write_mfma(w, share, pmc_dir, argv_line, sp_entry=False, backward=False, out
     return path
 
 
+def trace_path(tag, out_dir=None):
+    return os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"kernels_{tag}.md")
+
+
+def write_trace(w, share, trace_dir, argv_line, steps, sp_entry=False, backward=False, out_dir=None):
+    """Turn one rocprofv3 --kernel-trace --stats csv run of this script into
+    profiles/kernels_<workload>.md: per library kernel (matched by launch
+    order within a step), the dispatch count and the average, min and max
+    duration over every dispatch, and the average over the last ``steps``
+    steps (the timed region in which bench.py attaches HIP events to each
+    launch, whose averages the JSON line reports)."""
+    import csv
+    import collections
+
+    order = launch_order(w, sp_entry, backward)
+    tag = workload_tag(w, sp_entry, backward) + ("_rank0" if share == "rank" else "")
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    ours = [r for r in rows if "tp::" in r["Kernel_Name"] or "_ZN2tp" in r["Kernel_Name"]]
+    if len(ours) % len(order):
+        raise RuntimeError(f"{len(ours)} library dispatches is not a whole number of {len(order)}-kernel steps")
+    durs = collections.defaultdict(list)
+    names = {}
+    for i, r in enumerate(ours):
+        k = order[i % len(order)]
+        if KERNEL_SYMBOL[k] not in r["Kernel_Name"]:
+            raise RuntimeError(f"dispatch {r['Dispatch_Id']}: expected {k} ({KERNEL_SYMBOL[k]}), "
+                               f"profiler has {r['Kernel_Name'][:120]}")
+        durs[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        names[k] = r["Kernel_Name"]
+    nsteps = len(ours) // len(order)
+    per_step = collections.Counter(order)
+    agent = ""
+    ap = os.path.join(trace_dir, "run_agent_info.csv")
+    if os.path.exists(ap):
+        for a in csv.DictReader(open(ap)):
+            if a.get("Agent_Type", a.get("Type", "")).upper().endswith("GPU") or a.get("Name", "").startswith("gfx"):
+                agent = (f"{a.get('Name', '')}, {a.get('Cu_Count', a.get('Compute_Unit_Count', '?'))} CUs, "
+                         f"max engine clock {a.get('Max_Engine_Clk_Fcompute', a.get('Max_Clock_Freq', '?'))} MHz")
+                break
+
+    def short(n):
+        import re
+        n = n.replace("void ", "").replace("tp::(anonymous namespace)::", "")
+        return re.sub(r"\(tp::[A-Za-z]+Params[^)]*\)", "", n).replace("(tp::GemmParams, int, int)", "")
+
+    shards = w.N if share == "layer" else 1
+    rows_red = w.T if (share == "layer" or w.n_slices == 1) else w.T // w.n_slices
+    lines = [
+        f"# Kernel trace: {tag} ({'all shards + reduction' if share == 'layer' else 'rank 0 shard + reduction'})",
+        "",
+        "Commands (from /tmp on the GPU host, REPO = repository root):",
+        "",
+        f"    rocprofv3 --kernel-trace --stats -f csv -d DIR -o run -- python3 $REPO/bench.py {argv_line}",
+        f"    python3 $REPO/bench.py {argv_line.split(' --steps')[0]} --trace-from DIR",
+        "",
+        f"{len(ours)} library dispatches = {nsteps} steps of {len(order)} kernels (set-up pass, warm-up, and "
+        f"the three timed passes of {steps} steps each).  'Timed avg' is the mean over the last {steps} steps, "
+        "the pass in which bench.py times each launch with HIP events.",
+        "",
+        "| Kernel | Role | Calls | Avg all (us) | Timed avg (us) | Min (us) | Max (us) | Achieved | Roofline frac |",
+        "|---|---|---|---|---|---|---|---|---|",
+    ]
+    for k in dict.fromkeys(order):
+        d = durs[k]
+        last = d[-steps * per_step[k]:]
+        avg_t = sum(last) / len(last)
+        f, b = kernel_work(w, k, shards, rows_red)
+        rf = roofline(w, k, f, b, avg_t / 1e6)
+        lines.append(f"| `{short(names[k])}` | {k} | {len(d)} | {sum(d) / len(d):.2f} | {avg_t:.2f} | "
+                     f"{min(d):.2f} | {max(d):.2f} | {rf['achieved']} {rf['unit']} | {rf['frac']:.4f} |")
+    lines += ["", f"Algorithmic work per launch and peaks as in bench.py (bf16 MFMA {PEAK_BF16 / 1e12:.0f} TFLOP/s, "
+              f"HBM {PEAK_HBM / 1e9:.0f} GB/s).  Kernel sources hash: "
+              + ", ".join(f"{k} {kernel_source_hash(k)}" for k in dict.fromkeys(order)) + "."]
+    if agent:
+        lines.append(f"Agent: {agent}.")
+    path = trace_path(tag, out_dir)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
 def cpu_baseline(w, host, seconds):
     """fp64 oracle on a bounded, seeded sample of token rows of the same
     workload; TFLOP/s counted with the same algorithmic FLOP per row."""
@@ -493,10 +575,13 @@ def main():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default: as many as fill about 0.5 s, at least 20)")
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed warmup steps (default: as many as fill about 0.5 s, at least 5); "
-                         "the shader clock takes tens of ms to settle after idle")
-    ap.add_argument("--config", type=int, default=2,
-                    help="workload 1..5 (default 2: GELU MLP bf16, T=16384, H=512, F=2048, N=4), 6: the "
+                    help="untimed warmup steps, a minimum: warm-up always runs for at least --warmup-seconds "
+                         "of wall time as well, since the shader clock takes tens of ms to settle after idle")
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="minimum wall time of the warm-up (default 0.5 s)")
+    ap.add_argument("--config", type=int, default=5,
+                    help="workload 1..5 (default 5: the 175B-shaped GELU MLP bf16, T=16384, H=12288, F=49152, "
+                         "N=8, partial sums reduce-scattered into 8 sequence slices), 6: the "
                          "vocab-parallel output head + cross-entropy (T=16384, H=4096, V=150000, N=8), or 7: the "
                          "vocab-parallel embedding lookup (same sizes)")
     ap.add_argument("--share", choices=["layer", "rank"], default="layer")
@@ -516,6 +601,9 @@ def main():
     ap.add_argument("--mfma-from", metavar="DIR",
                     help="write profiles/mfma_<workload>.txt from a rocprofv3 --pmc MfmaFlopsBF16 MfmaUtil csv run "
                          "under DIR and exit; runs on the host, no GPU")
+    ap.add_argument("--trace-from", metavar="DIR",
+                    help="write profiles/kernels_<workload>.md from a rocprofv3 --kernel-trace --stats csv run of "
+                         "this script (same --config/--share/--steps flags) under DIR and exit; runs on the host")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="write profiles/traffic_<workload>.txt from rocprofv3 --pmc csv runs under DIR "
                          "(DIR/FETCH_SIZE, DIR/WRITE_SIZE) and exit; runs on the host, no GPU")
@@ -528,6 +616,18 @@ def main():
         argv = (f"--config {args.config} --share {args.share}{' --sp-entry' if args.sp_entry else ''}"
                 f"{' --backward' if args.backward else ''} --steps 3 --warmup 1 --no-cpu-baseline")
         print(write_mfma(w, args.share, args.mfma_from, argv, args.sp_entry, args.backward))
+        return
+
+    if args.trace_from:
+        from tensor_transformer_layers_amd import configs
+
+        w = configs.workload(args.config)
+        if args.steps is None or args.overlap:
+            print("bench.py --trace-from needs the --steps of the profiled run (and no --overlap)", file=sys.stderr)
+            sys.exit(2)
+        argv = (f"--config {args.config} --share {args.share}{' --sp-entry' if args.sp_entry else ''}"
+                f"{' --backward' if args.backward else ''} --steps {args.steps} --no-cpu-baseline")
+        print(write_trace(w, args.share, args.trace_from, argv, args.steps, args.sp_entry, args.backward))
         return
 
     if args.traffic_from:
@@ -613,28 +713,32 @@ def main():
             workloads.forward(w, d, ws=ws, shard_begin=0, shard_count=1, stream=stream)
             workloads.reduce_slab(w, d, ws, Y=Yr, slice=rank_slice, stream=stream)
 
-    if args.steps is None or args.warmup is None:
-        # size the defaults by time: after idle the shader clock ramps for
-        # tens of ms (measured 1.3 -> 1.9 GHz over ~30 ms on the large GEMMs,
-        # 2.05 -> 2.3 GHz over ~40 ms on workload 2), so a fixed small step
-        # count would time the ramp instead of the steady state
-        for _ in range(2):
-            step()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(3):
-            step()
-        torch.cuda.synchronize()
-        est = (time.perf_counter() - t0) / 3
-        fill = max(1, int(0.5 / max(est, 1e-6)))
-        if args.warmup is None:
-            args.warmup = max(5, fill)
-        if args.steps is None:
-            args.steps = max(20, fill)
-    log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        step()
+    # Warm-up by time as well as by count: after idle the shader clock ramps
+    # for tens of ms (measured 1.3 -> 1.9 GHz over ~30 ms on the large GEMMs,
+    # 2.05 -> 2.3 GHz over ~40 ms on the hidden-512 workload), so a small step
+    # count alone would time the ramp instead of the steady state.  --warmup
+    # is a minimum number of steps; the warm-up goes on until it has also
+    # filled --warmup-seconds of wall time.
+    warm_min = 5 if args.warmup is None else max(0, args.warmup)
+    log(f"warmup: at least {warm_min} steps and {args.warmup_seconds:.2f} s")
     torch.cuda.synchronize()
+    tw0 = time.perf_counter()
+    warm_done = 0
+    est = None
+    while warm_done < warm_min or time.perf_counter() - tw0 < args.warmup_seconds:
+        step()
+        warm_done += 1
+        if warm_done == 3 or (warm_done >= warm_min and warm_done % 4 == 0):
+            torch.cuda.synchronize()  # keep the queue short so that wall time tracks GPU time
+            if est is None and warm_done == 3:
+                est = (time.perf_counter() - tw0) / 3
+    torch.cuda.synchronize()
+    warm_s = time.perf_counter() - tw0
+    if est is None:
+        est = warm_s / max(1, warm_done)
+    if args.steps is None:
+        args.steps = max(20, int(0.5 / max(est, 1e-6)))
+    log(f"warmup done: {warm_done} steps in {warm_s:.3f} s")
 
     # timed region 1: the steps alone
     log(f"timing {args.steps} steps")
@@ -718,7 +822,9 @@ def main():
         "unit": "GB/s" if w.kind == "vocab_embed" else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warm_done,
+        "warmup_requested": args.warmup,
+        "warmup_s": round(warm_s, 3),
         "ms_per_step": round(ms_step, 5),
         "step_ms": step_stats,
         "higher_is_better": True,

@@ -305,12 +305,13 @@ tp_status tp_vocab_ce_forward(void* stream, const tp_vocab_ce_desc* d, void* ws,
  * vocab like the output head, padded so TP divides it; "张量并行", practice
  * section: vocab-parallel embedding).  Shard i owns padded vocab rows
  * [i*Vs, (i+1)*Vs) (Vs as in tp_vocab_padded) and looks up only the ids it
- * owns, writing zero rows for the others -- one partial [T x H] per shard in
- * the table's type dt, slot i of the workspace slab.  When the range covers
- * all N shards the partials are folded in shard order in fp32 (the
- * all-reduce stand-in) and cast back to dt: one term per element is nonzero,
- * so Y[t] = E[ids[t]] exactly.  Rows >= V of E are never read; an id
- * outside [0, V) has no owner and gets a zero row.
+ * owns, writing rows of -0.0 (the IEEE additive identity) for the others --
+ * one partial [T x H] per shard in the table's type dt, slot i of the
+ * workspace slab.  When the range covers all N shards the partials are
+ * folded in shard order in fp32 from -0.0 (the all-reduce stand-in) and cast
+ * back to dt: at most one term per element is not -0.0, so Y[t] = E[ids[t]]
+ * bit for bit, signed zeros included.  Rows >= V of E are never read; an id
+ * outside [0, V) has no owner and gets a row of -0.0.
  *
  *   ids  [T] int32;  E [Vp x H] dt (Vp = tp_vocab_padded(V, N));  Y [T x H] dt
  * dt is TP_BF16 or TP_F32; H a multiple of 8.

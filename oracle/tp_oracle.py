@@ -571,7 +571,11 @@ def vocab_parallel_embedding(ids, E, V, N):
     zero rows for the others; the N partials are summed in shard order (the
     all-reduce), so every token gets exactly its own row.  Rows >= V are
     padding and never read; an id outside [0, V) has no owner and gets a
-    zero row.  Returns (rows [T x H], list of per-shard partials)."""
+    zero row.  The rows a shard does not own hold -0.0, the additive identity
+    of IEEE arithmetic (x + (-0.0) == x bit for bit, a stored -0.0 included),
+    so the sum reproduces the table's bits exactly, signed zeros too; an
+    unowned id gets a -0.0 row.  Returns (rows [T x H], list of per-shard
+    partials)."""
     ids = np.asarray(ids)
     E = _f64(E)
     Vp, Vs = padded_vocab(V, N)
@@ -580,7 +584,7 @@ def vocab_parallel_embedding(ids, E, V, N):
     for i in range(N):
         lo, hi = i * Vs, min((i + 1) * Vs, V)
         own = (ids >= lo) & (ids < hi)
-        P = np.zeros((T, H))
+        P = np.full((T, H), -0.0)
         P[own] = E[ids[own]]
         parts.append(P)
     return _fold(parts), parts

@@ -26,8 +26,10 @@ constexpr int kThreads = 256;
 
 // Input side: one wave per (shard, token) row of the partial slab.  The
 // shard that owns the token's id copies its embedding row; every other shard
-// writes a zero row.  The partials keep the table's type (each holds table
-// entries and zeros, so the fold's sums are exact in any precision).  Lane l
+// writes a row of -0.0, the additive identity of IEEE arithmetic (x + -0 is
+// x for every x, a stored -0.0 included, where +0 would turn -0.0 into
+// +0.0).  The partials keep the table's type (each holds table entries and
+// signed zeros, so the fold's sums are exact in any precision).  Lane l
 // moves the 16-byte vector l of each 1 KiB stretch: every load and store
 // instruction of the wave covers one contiguous KiB.  Non-temporal stores:
 // the slab is read once, by the fold.
@@ -46,9 +48,12 @@ __global__ __launch_bounds__(kThreads) void embed_partial_kernel(EmbedParams p) 
   const bool own = id >= lo && id < hi;
   const E* const src = static_cast<const E*>(p.E) + (own ? id : 0) * p.H;
   E* const dst = static_cast<E*>(p.P) + (int64_t)s * p.sP + t * p.H;
+  ev nz;
+#pragma unroll
+  for (int e = 0; e < VE; ++e) nz[e] = static_cast<E>(-0.0f);
 #pragma unroll 4
   for (int64_t c = (int64_t)lane * VE; c < p.H; c += (int64_t)VE * kWave) {
-    ev v = ev{};
+    ev v = nz;
     if (own) v = *reinterpret_cast<const ev*>(src + c);
     __builtin_nontemporal_store(v, reinterpret_cast<ev*>(dst + c));
   }
@@ -56,9 +61,10 @@ __global__ __launch_bounds__(kThreads) void embed_partial_kernel(EmbedParams p) 
 
 // The embedding's all-reduce stand-in: thread i folds 16-byte vectors
 // i + u * 256 (u < kFoldU, within its workgroup's span) of the N partials in
-// shard order ((P0 + P1) + P2) + ... in fp32, then casts back to the table's
-// type (exact: one term per element is nonzero).  All loads of a group of 8
-// shards are issued before its adds.
+// shard order ((-0 + P0) + P1) + ... in fp32, then casts back to the table's
+// type (exact: at most one term per element is not -0.0, and starting from
+// -0.0 keeps the sign of a stored zero).  All loads of a group of 8 shards
+// are issued before its adds.
 constexpr int kFoldU = 4;
 
 template <typename E>
@@ -72,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void embed_fold_kernel(EmbedFoldParams p)
 #pragma unroll
   for (int u = 0; u < kFoldU; ++u)
 #pragma unroll
-    for (int e = 0; e < VE; ++e) acc[u][e] = 0.0f;
+    for (int e = 0; e < VE; ++e) acc[u][e] = -0.0f;
   for (int k0 = 0; k0 < p.N; k0 += 8) {
     ev v[8][kFoldU];
 #pragma unroll

@@ -262,6 +262,38 @@ def _same_dtype(ref, **named):
             raise ValueError(f"{name} must be contiguous")
 
 
+def _expect(name, t, shape, dtype=None, device=None, contiguous=True):
+    """The C ABI sees only pointers and the sizes the caller passes, so a
+    tensor smaller than those sizes would be read or written out of bounds.
+    Check here, before the C call, that ``t`` has exactly ``shape`` (a tuple
+    of ints), the expected dtype and device, and, unless ``contiguous`` is
+    False, a contiguous layout."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} is {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _rows_2d(name, t, cols, dtype=None, device=None):
+    """``t`` is a 2-D row-major view with ``cols`` columns (a leading
+    dimension of at least ``cols``, unit column stride)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dim() != 2 or t.shape[1] != cols or t.stride(1) != 1 or (t.shape[0] > 1 and t.stride(0) < cols):
+        raise ValueError(f"{name} must be a row-major [rows x {cols}] view, got shape {tuple(t.shape)} "
+                         f"strides {tuple(t.stride())}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} is {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
 def _ld(t) -> int:
     if t.dim() != 2 or t.stride(1) != 1:
         raise ValueError("expected a row-major 2-D tensor (unit column stride)")
@@ -277,10 +309,21 @@ def _stream(stream=None):
 def column_linear(X, W, bias=None, act=TP_ACT_GELU, out=None, stream=None):
     """Y_i = act(X W_i^T + bias_i); W is [Ns x K] ([2Ns x K] for SwiGLU)."""
     torch = _torch()
+    if X.dim() != 2 or W.dim() != 2:
+        raise ValueError("X and W must be 2-D")
     T, K = X.shape
+    if act == TP_ACT_SWIGLU and W.shape[0] % 2:
+        raise ValueError(f"SwiGLU W holds [gate | up] rows: an even row count, got {W.shape[0]}")
     Ns = W.shape[0] // 2 if act == TP_ACT_SWIGLU else W.shape[0]
+    _rows_2d("X", X, K, device=X.device)
+    _rows_2d("W", W, K, dtype=X.dtype, device=X.device)
+    if bias is not None:
+        _expect("bias", bias, (Ns,), X.dtype, X.device)
     if out is None:
         out = torch.empty((T, Ns), dtype=X.dtype, device=X.device)
+    _rows_2d("out", out, Ns, dtype=X.dtype, device=X.device)
+    if out.shape[0] != T:
+        raise ValueError(f"out has {out.shape[0]} rows, expected {T}")
     check(tp_column_linear(_stream(stream), _dt(X), act, T, K, Ns, _ptr(X), _ld(X), _ptr(W), _ld(W),
                            _ptr(bias), _ptr(out), _ld(out)))
     return out
@@ -289,10 +332,17 @@ def column_linear(X, W, bias=None, act=TP_ACT_GELU, out=None, stream=None):
 def row_linear_partial(X, W, out=None, stream=None):
     """P_i = X_i W_i^T in fp32; W is [Nout x Ks]."""
     torch = _torch()
+    if X.dim() != 2 or W.dim() != 2:
+        raise ValueError("X and W must be 2-D")
     T, Ks = X.shape
     Nout = W.shape[0]
+    _rows_2d("X", X, Ks, device=X.device)
+    _rows_2d("W", W, Ks, dtype=X.dtype, device=X.device)
     if out is None:
         out = torch.empty((T, Nout), dtype=torch.float32, device=X.device)
+    _rows_2d("out", out, Nout, dtype=torch.float32, device=X.device)
+    if out.shape[0] != T:
+        raise ValueError(f"out has {out.shape[0]} rows, expected {T}")
     check(tp_row_linear_partial(_stream(stream), _dt(X), T, Ks, Nout, _ptr(X), _ld(X), _ptr(W), _ld(W),
                                 _ptr(out), _ld(out)))
     return out
@@ -301,12 +351,21 @@ def row_linear_partial(X, W, out=None, stream=None):
 def reduce_partials(P, bias=None, out_dtype=None, n_slices=1, slice=-1, out=None, n_parts=None, stream=None):
     """Fixed-order sum of P[0..n) ([n x T x H] fp32) + bias, cast to out_dtype."""
     torch = _torch()
+    if P.dim() != 3 or P.dtype != torch.float32:
+        raise ValueError(f"P must be an fp32 [n x T x H] tensor, got {P.dtype} {tuple(P.shape)}")
     n, T, H = P.shape
+    if not P[0].is_contiguous() or (n > 1 and P.stride(0) < T * H):
+        raise ValueError("each partial P[k] must be a contiguous [T x H] block, the blocks not overlapping")
+    if n_parts is not None and not 0 <= n_parts <= n:
+        raise ValueError(f"n_parts = {n_parts} exceeds the {n} partials of P")
     n = n if n_parts is None else n_parts
     out_dtype = out_dtype or (bias.dtype if bias is not None else torch.bfloat16)
+    if bias is not None:
+        _expect("bias", bias, (H,), out_dtype, P.device)
     rows = T if slice < 0 else T // n_slices
     if out is None:
         out = torch.empty((rows, H), dtype=out_dtype, device=P.device)
+    _expect("out", out, (rows, H), out_dtype, P.device)
     odt = TP_BF16 if out_dtype == torch.bfloat16 else TP_F32
     check(tp_reduce_partials(_stream(stream), odt, n, T, H, _ptr(P), P.stride(0), _ptr(bias), _ptr(out),
                              n_slices, slice))
@@ -319,14 +378,43 @@ def rmsnorm_gather(X, gamma, eps, n_slices, out=None, slice=-1, slice_stride=Non
     None).  With ``slice_stride`` the slices are read at X + r*slice_stride
     elements instead (X then holds the first slice's [T/n x H] rows)."""
     torch = _torch()
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
     rows, H = X.shape
+    _rows_2d("X", X, H, device=X.device)
+    if slice_stride is not None and n_slices > 1 and slice_stride < rows * X.stride(0):
+        raise ValueError(f"slice_stride {slice_stride} is shorter than one slice ({rows} rows)")
     T = rows if slice_stride is None else rows * n_slices
     stride = (T // n_slices) * X.stride(0) if slice_stride is None else slice_stride
+    _expect("gamma", gamma, (H,), X.dtype, X.device)
     if out is None:
         out = torch.empty((T, H), dtype=X.dtype, device=X.device)
+    _rows_2d("out", out, H, dtype=X.dtype, device=X.device)
+    if out.shape[0] != T:
+        raise ValueError(f"out has {out.shape[0]} rows, expected {T}")
     check(tp_rmsnorm_gather(_stream(stream), _dt(X), n_slices, T, H, _ptr(X), stride, _ld(X), _ptr(gamma),
                             float(eps), _ptr(out), _ld(out), slice))
     return out
+
+
+def _check_mlp(X, A, a, B, b, act, Y=None, rows=None):
+    """Shapes of the MLP operands in the ABI's storage: X [T x H]; A [F x H]
+    ([2F x H] of per-shard [gate | up] blocks for SwiGLU); a [F] or None;
+    B [H x F]; b [H] or None; Y [rows x H] when given.  Returns (T, H, F)."""
+    if X.dim() != 2 or B.dim() != 2:
+        raise ValueError("X and B must be 2-D")
+    T, H = X.shape
+    F = B.shape[1]
+    _expect("X", X, (T, H))
+    _expect("B", B, (H, F), X.dtype, X.device)
+    _expect("A", A, ((2 * F if act == TP_ACT_SWIGLU else F), H), X.dtype, X.device)
+    if a is not None:
+        _expect("a", a, (F,), X.dtype, X.device)
+    if b is not None:
+        _expect("b", b, (H,), X.dtype, X.device)
+    if Y is not None:
+        _expect("Y", Y, (T if rows is None else rows, H), X.dtype, X.device)
+    return T, H, F
 
 
 def mlp_desc(X, A, a, B, b, N, act, Y=None, shard_begin=0, shard_count=None, n_slices=1, slice=-1, F=None):
@@ -357,11 +445,13 @@ def mlp_forward(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, ws=None, shard_begin=
     shard ranges (the partials are in the workspace slab)."""
     torch = _torch()
     _same_dtype(X, A=A, a=a, B=B, b=b, Y=Y)
-    T, H = X.shape
+    T, H, _ = _check_mlp(X, A, a, B, b, act)
     cnt = N if shard_count is None else shard_count
+    rows = T if slice < 0 or n_slices < 1 else T // n_slices
     if Y is None and cnt == N:
-        rows = T if slice < 0 else T // n_slices
         Y = torch.empty((rows, H), dtype=X.dtype, device=X.device)
+    if Y is not None:
+        _expect("Y", Y, (rows, H), X.dtype, X.device)
     d = mlp_desc(X, A, a, B, b, N, act, Y, shard_begin, cnt, n_slices, slice)
     need = tp_mlp_workspace_size(d)
     if need == 0:
@@ -381,8 +471,8 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
     [H x F]) and db (fp32 [H] or None); missing entries are allocated."""
     torch = _torch()
     _same_dtype(X, A=A, a=a, B=B, dY=dY)
-    T, H = X.shape
-    F = B.shape[1]
+    T, H, F = _check_mlp(X, A, a, B, None, act)
+    _expect("dY", dY, (T, H), X.dtype, X.device)
     if act == TP_ACT_SWIGLU:
         need_da = False  # no column bias
     cnt = N if shard_count is None else shard_count
@@ -399,6 +489,14 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
         g["dB"] = torch.zeros((H, F), dtype=f32, device=dev)
     if "db" not in g:
         g["db"] = torch.zeros((H,), dtype=f32, device=dev) if need_db else None
+    if g["dX"] is not None:
+        _expect("dX", g["dX"], (T, H), X.dtype, dev)
+    _expect("dA", g["dA"], tuple(A.shape), f32, dev)
+    if g["da"] is not None:
+        _expect("da", g["da"], (F,), f32, dev)
+    _expect("dB", g["dB"], (H, F), f32, dev)
+    if g["db"] is not None:
+        _expect("db", g["db"], (H,), f32, dev)
     d = MlpBwdDesc()
     d.dt = _dt(X)
     d.act = act
@@ -426,12 +524,22 @@ def vocab_ce_forward(X, E, labels, V, N, shard_begin=0, shard_count=None, loss=N
     _same_dtype(X, E=E)
     if labels.dtype != torch.int32:
         raise TypeError(f"labels are {labels.dtype}, expected torch.int32")
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
     T, H = X.shape
+    if N >= 1 and V >= 1:
+        # the head's product reads every padded row: E must hold them all
+        _expect("E", E, (tp_vocab_padded(V, N), H), X.dtype, X.device)
+    _expect("labels", labels, (T,), torch.int32, X.device)
     cnt = N if shard_count is None else shard_count
     if loss is None and cnt == N:
         loss = torch.empty((T,), dtype=torch.float32, device=X.device)
     if mean is None and cnt == N:
         mean = torch.empty((1,), dtype=torch.float32, device=X.device)
+    if loss is not None:
+        _expect("loss", loss, (T,), torch.float32, X.device)
+    if mean is not None:
+        _expect("mean", mean, (1,), torch.float32, X.device)
     d = VocabCeDesc()
     d.dt = _dt(X)
     d.T, d.H, d.V = T, H, V
@@ -469,12 +577,20 @@ def vocab_embed_forward(ids, E, V, N, shard_begin=0, shard_count=None, Y=None, w
     torch = _torch()
     if ids.dtype != torch.int32:
         raise TypeError(f"ids are {ids.dtype}, expected torch.int32")
+    if ids.dim() != 1:
+        raise ValueError(f"ids must be 1-D, got shape {tuple(ids.shape)}")
+    if E.dim() != 2:
+        raise ValueError("E must be 2-D")
     T, H = ids.shape[0], E.shape[1]
+    _expect("ids", ids, (T,), torch.int32, E.device)
+    if N >= 1 and V >= 1:
+        _expect("E", E, (tp_vocab_padded(V, N), H), None, E.device)
     cnt = N if shard_count is None else shard_count
     if Y is None and cnt == N:
         Y = torch.empty((T, H), dtype=E.dtype, device=E.device)
     if Y is not None:
         _same_dtype(E, Y=Y)
+        _expect("Y", Y, (T, H), E.dtype, E.device)
     d = VocabEmbedDesc()
     d.dt = _dt(E)
     d.T, d.H, d.V = T, H, V
@@ -504,9 +620,11 @@ def mlp_forward_overlap(X, A, a, B, b, N, chunks, stream2, act=TP_ACT_GELU, Y=No
     with the products of block k+1 on ``stream2`` (a torch stream other than
     the current one); returns (Y, workspace)."""
     torch = _torch()
-    T, H = X.shape
+    _same_dtype(X, A=A, a=a, B=B, b=b, Y=Y)
+    T, H, _ = _check_mlp(X, A, a, B, b, act)
     if Y is None:
         Y = torch.empty((T, H), dtype=X.dtype, device=X.device)
+    _expect("Y", Y, (T, H), X.dtype, X.device)
     d = mlp_desc(X, A, a, B, b, N, act, Y)
     need = tp_mlp_workspace_size(d)
     if need == 0:
@@ -542,11 +660,23 @@ def attn_desc(X, Wqkv, Wo, bo, batch, seq, heads, N, Y=None, shard_begin=0, shar
 def attn_forward(X, Wqkv, Wo, bo, batch, seq, heads, N, Y=None, ws=None, shard_begin=0, shard_count=None,
                  n_slices=1, slice=-1, stream=None):
     torch = _torch()
+    _same_dtype(X, Wqkv=Wqkv, Wo=Wo, bo=bo, Y=Y)
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
     T, Hd = X.shape
+    if T != batch * seq:
+        raise ValueError(f"X has {T} rows, expected batch*seq = {batch * seq}")
+    _expect("X", X, (T, Hd))
+    _expect("Wqkv", Wqkv, (3 * heads * 128, Hd), X.dtype, X.device)
+    _expect("Wo", Wo, (Hd, heads * 128), X.dtype, X.device)
+    if bo is not None:
+        _expect("bo", bo, (Hd,), X.dtype, X.device)
     cnt = N if shard_count is None else shard_count
+    rows = T if slice < 0 or n_slices < 1 else T // n_slices
     if Y is None and cnt == N:
-        rows = T if slice < 0 else T // n_slices
         Y = torch.empty((rows, Hd), dtype=X.dtype, device=X.device)
+    if Y is not None:
+        _expect("Y", Y, (rows, Hd), X.dtype, X.device)
     d = attn_desc(X, Wqkv, Wo, bo, batch, seq, heads, N, Y, shard_begin, cnt, n_slices, slice)
     need = tp_attn_workspace_size(d)
     if need == 0:
@@ -560,8 +690,21 @@ def attn_forward(X, Wqkv, Wo, bo, batch, seq, heads, N, Y=None, ws=None, shard_b
 def attn_local(QK, k_col0, Vt, batch, seq, heads, out=None, stream=None):
     torch = _torch()
     T = batch * seq
+    if QK.dim() != 2 or Vt.dim() != 2:
+        raise ValueError("QK and Vt must be 2-D")
+    _rows_2d("QK", QK, QK.shape[1], device=QK.device)
+    _rows_2d("Vt", Vt, Vt.shape[1], dtype=QK.dtype, device=QK.device)
+    if QK.shape[0] != T or k_col0 < heads * 128 or QK.shape[1] < k_col0 + heads * 128:
+        raise ValueError(f"QK must be [batch*seq = {T} x >= k_col0 + heads*128] with Q in columns "
+                         f"[0, heads*128) and K from column k_col0 >= heads*128, got {tuple(QK.shape)}, "
+                         f"k_col0 = {k_col0}")
+    if Vt.shape[0] != heads * 128 or Vt.shape[1] < T:
+        raise ValueError(f"Vt must be [heads*128 = {heads * 128} x >= {T}], got {tuple(Vt.shape)}")
     if out is None:
         out = torch.empty((T, heads * 128), dtype=QK.dtype, device=QK.device)
+    _rows_2d("out", out, heads * 128, dtype=QK.dtype, device=QK.device)
+    if out.shape[0] != T:
+        raise ValueError(f"out has {out.shape[0]} rows, expected {T}")
     check(tp_attn_local(_stream(stream), batch, seq, heads, 128, _ptr(QK), _ld(QK), k_col0, _ptr(Vt), _ld(Vt),
                         _ptr(out), _ld(out)))
     return out

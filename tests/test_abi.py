@@ -467,3 +467,93 @@ def test_binding_rejects_mismatched_dtypes():
         tp.vocab_embed_forward(torch.zeros(16, dtype=torch.int64), B, 50, 2)
     with pytest.raises(TypeError, match="Y is torch.float32"):
         tp.vocab_embed_forward(torch.zeros(16, dtype=torch.int32), B, 50, 2, Y=A)
+
+
+def test_binding_rejects_wrong_shapes_before_the_c_call():
+    """The C ABI sees only pointers and sizes, so a tensor smaller than the
+    sizes it implies would be read or written out of bounds.  The binding
+    checks every shape first (CPU tensors: nothing here reaches HIP)."""
+    import torch
+
+    bf = torch.bfloat16
+    T, H, F, N = 16, 64, 128, 2
+    X = torch.zeros((T, H), dtype=bf)
+    A = torch.zeros((F, H), dtype=bf)
+    B = torch.zeros((H, F), dtype=bf)
+    # MLP: A must be [F x H] (GELU) or [2F x H] (SwiGLU), biases [F] and [H], Y [T x H]
+    with pytest.raises(ValueError, match="A has shape"):
+        tp.mlp_forward(X, A[:F - 8], None, B, None, N)
+    with pytest.raises(ValueError, match="A has shape"):
+        tp.mlp_forward(X, A, None, B, None, N, act=tp.TP_ACT_SWIGLU)
+    with pytest.raises(ValueError, match="a has shape"):
+        tp.mlp_forward(X, A, torch.zeros(F - 1, dtype=bf), B, None, N)
+    with pytest.raises(ValueError, match="b has shape"):
+        tp.mlp_forward(X, A, None, B, torch.zeros(H + 1, dtype=bf), N)
+    with pytest.raises(ValueError, match="Y has shape"):
+        tp.mlp_forward(X, A, None, B, None, N, Y=torch.zeros((T - 1, H), dtype=bf))
+    with pytest.raises(ValueError, match="Y has shape"):  # one RS slice is T / n_slices rows
+        tp.mlp_forward(X, A, None, B, None, N, Y=torch.zeros((T, H), dtype=bf), n_slices=2, slice=1)
+    with pytest.raises(ValueError, match="B has shape"):
+        tp.mlp_forward_overlap(X, A, None, B[:, :F - 8].contiguous()[:H - 8], None, N, 2, None)
+    with pytest.raises(ValueError, match="contiguous"):
+        tp.mlp_forward(X.t().contiguous().t(), A, None, B, None, N)
+    # backward: dY [T x H], gradient buffers of the operands' shapes
+    with pytest.raises(ValueError, match="dY has shape"):
+        tp.mlp_backward(X, A, None, B, X[: T - 2], N)
+    with pytest.raises(ValueError, match="dB has shape"):
+        tp.mlp_backward(X, A, None, B, X.clone(), N, grads={"dB": torch.zeros((H, F - 8))})
+    # vocab head: E must hold every padded row, labels 1-D int32 of length T
+    Vp = tp.tp_vocab_padded(100, N)
+    E = torch.zeros((Vp, H), dtype=bf)
+    lab = torch.zeros(T, dtype=torch.int32)
+    with pytest.raises(ValueError, match="E has shape"):
+        tp.vocab_ce_forward(X, E[:100].contiguous(), lab, 100, N)
+    with pytest.raises(ValueError, match="labels has shape"):
+        tp.vocab_ce_forward(X, E, lab[: T - 1], 100, N)
+    with pytest.raises(ValueError, match="labels has shape"):
+        tp.vocab_ce_forward(X, E, lab.view(2, T // 2), 100, N)
+    with pytest.raises(ValueError, match="labels must be contiguous"):
+        tp.vocab_ce_forward(X, E, torch.zeros(2 * T, dtype=torch.int32)[::2], 100, N)
+    # embedding: ids 1-D contiguous int32, E padded
+    ids = torch.zeros(T, dtype=torch.int32)
+    with pytest.raises(ValueError, match="ids must be 1-D"):
+        tp.vocab_embed_forward(ids.view(2, T // 2), E, 100, N)
+    with pytest.raises(ValueError, match="ids must be contiguous"):
+        tp.vocab_embed_forward(torch.zeros(2 * T, dtype=torch.int32)[::2], E, 100, N)
+    with pytest.raises(ValueError, match="E has shape"):
+        tp.vocab_embed_forward(ids, E[: Vp - 8].contiguous(), 100, N)
+    with pytest.raises(ValueError, match="Y has shape"):
+        tp.vocab_embed_forward(ids, E, 100, N, Y=torch.zeros((T, H - 8), dtype=bf))
+    # linear pieces, the reduction and the norm
+    with pytest.raises(ValueError, match="W must be"):
+        tp.column_linear(X, torch.zeros((F, H - 8), dtype=bf))
+    with pytest.raises(ValueError, match="bias has shape"):
+        tp.column_linear(X, A, bias=torch.zeros(F + 8, dtype=bf))
+    with pytest.raises(ValueError, match="out has 15 rows"):
+        tp.row_linear_partial(X, B.t().contiguous()[:, :H].contiguous(), out=torch.zeros((T - 1, F)))
+    P = torch.zeros((N, T, H))
+    with pytest.raises(ValueError, match="bias has shape"):
+        tp.reduce_partials(P, bias=torch.zeros(H - 8, dtype=bf))
+    with pytest.raises(ValueError, match="out has shape"):
+        tp.reduce_partials(P, out=torch.zeros((T, H), dtype=bf), n_slices=2, slice=0)
+    with pytest.raises(ValueError, match="n_parts"):
+        tp.reduce_partials(P, n_parts=N + 1)
+    with pytest.raises(ValueError, match="fp32"):
+        tp.reduce_partials(P.to(bf))
+    with pytest.raises(ValueError, match="gamma has shape"):
+        tp.rmsnorm_gather(X, torch.zeros(H - 8, dtype=bf), 1e-6, 2)
+    # attention: Wqkv [3*heads*128 x hidden], Wo [hidden x heads*128], X [batch*seq x hidden]
+    hid, heads = 256, 2
+    Xa = torch.zeros((2 * 8, hid), dtype=bf)
+    Wqkv = torch.zeros((3 * heads * 128, hid), dtype=bf)
+    Wo = torch.zeros((hid, heads * 128), dtype=bf)
+    with pytest.raises(ValueError, match="batch\\*seq"):
+        tp.attn_forward(Xa, Wqkv, Wo, None, 2, 9, heads, 2)
+    with pytest.raises(ValueError, match="Wqkv has shape"):
+        tp.attn_forward(Xa, Wqkv[:-8].contiguous(), Wo, None, 2, 8, heads, 2)
+    with pytest.raises(ValueError, match="Wo has shape"):
+        tp.attn_forward(Xa, Wqkv, Wo[:, :-8].contiguous(), None, 2, 8, heads, 2)
+    with pytest.raises(ValueError, match="QK must be"):
+        tp.attn_local(torch.zeros((16, 300), dtype=bf), 256, torch.zeros((256, 16), dtype=bf), 2, 8, 2)
+    with pytest.raises(ValueError, match="Vt must be"):
+        tp.attn_local(torch.zeros((16, 512), dtype=bf), 256, torch.zeros((256, 15), dtype=bf), 2, 8, 2)

@@ -297,18 +297,19 @@ def test_fused_mlp_matches_separate_kernels():
 
 # ------------------------------------------------------------------ the five workloads at full size
 def _sample_rows(w):
+    """Token rows the full-size check compares: every row where the fp64
+    oracle finishes in seconds (workloads 1, 2 and the attention block,
+    whose rows need their whole causal prefix anyway), else 1024 seeded rows
+    that include the first and last token and the first and last row of
+    every reduce-scatter slice (the MLP is token-wise, so a row's oracle
+    value needs no other row)."""
+    if w.kind == "attn" or (w.T <= 16384 and w.kind == "mlp_gelu" and w.H <= 512):
+        return None  # the full oracle
     must = [0, w.T - 1]
     if w.n_slices > 1:
         s = w.T // w.n_slices
         must += [r * s for r in range(w.n_slices)] + [r * s + s - 1 for r in range(w.n_slices)]
-    if w.kind == "attn":
-        must += [w.seq - 1, w.seq, w.seq + 1]
-        count = 48
-    else:
-        count = 256
-    if w.T <= 16384 and w.kind == "mlp_gelu" and w.H <= 512:
-        return None  # small enough for the full oracle
-    return inputs.sample_rows(w.T, count, w.seed, must)
+    return inputs.sample_rows(w.T, 1024, w.seed, must)
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])

@@ -143,6 +143,23 @@ def test_vocab_parallel_embedding_is_the_plain_lookup(V, N):
     assert np.all(nonzero.sum(axis=0) == 1)  # exactly one owner per token
 
 
+def test_vocab_parallel_embedding_keeps_signed_zeros():
+    """The lookup returns the table's bits, signed zeros included: a stored
+    -0.0 comes back as -0.0 and +0.0 as +0.0 (the non-owning shards' rows
+    are -0.0, the additive identity, so the fold adds nothing to either)."""
+    V, N = 37, 4
+    Vp, _ = O.padded_vocab(V, N)
+    E = np.random.default_rng(5).standard_normal((Vp, 4))
+    E[3] = [-0.0, 0.0, -0.0, 1.5]
+    E[30] = [0.0, -0.0, 2.0, -0.0]
+    ids = np.array([3, 30, 3, 12])
+    Y, _ = O.vocab_parallel_embedding(ids, E, V, N)
+    assert np.array_equal(Y.view(np.uint64), E[ids].view(np.uint64))
+    # the plainer fold from +0.0 would lose the sign of every stored -0.0
+    plus = np.zeros_like(Y) + Y
+    assert not np.array_equal(plus.view(np.uint64), E[ids].view(np.uint64))
+
+
 def test_vocab_parallel_embedding_out_of_range_ids_give_zero_rows():
     V, N = 20, 4
     Vp, _ = O.padded_vocab(V, N)
