@@ -202,6 +202,29 @@ tp_status tp_mlp_forward(void* stream, const tp_mlp_desc* d, void* ws, size_t ws
 tp_status tp_mlp_forward_overlap(void* stream, void* stream2, const tp_mlp_desc* d, int chunks, void* ws,
                                  size_t ws_bytes);
 
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: the same
+ * sublayer as tp_mlp_forward (same kernels, same bits), with no workspace
+ * argument.  Its partial slab and intermediate live in a library-owned,
+ * file-scope static device array of TP_NOALLOC_SCRATCH_BYTES, one copy per
+ * GPU the library runs on, held until the process ends; the call itself
+ * allocates and frees nothing.
+ *   - Needs the whole shard range (shard_count == N): a partial range would
+ *     leave its partials in a buffer the caller cannot see.
+ *   - Fails with TP_ERR_WORKSPACE, before any HIP call, when the workspace
+ *     tp_mlp_workspace_size(d) reports exceeds TP_NOALLOC_SCRATCH_BYTES.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (nothing in it needs to start at zero: each call
+ *     writes every byte it reads).  Calls that overlap on one GPU -- on two
+ *     streams, or from two threads -- race on it.
+ *   - The array is resolved on the GPU of `stream` (the current device for
+ *     the null stream) on that GPU's first call; errors of that lookup are
+ *     returned as TP_ERR_HIP.
+ */
+#define TP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+tp_status tp_mlp_forward_noalloc(void* stream, const tp_mlp_desc* d);
+
 /* QKV projection of the shard's heads, causal softmax attention per local
  * head (scale 1/sqrt(head_dim), diagonal kept), row-parallel output
  * projection into the partial slab, then the reduction as for the MLP. */

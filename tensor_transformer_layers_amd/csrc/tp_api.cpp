@@ -836,6 +836,69 @@ tp_status tp_mlp_forward_overlap(void* stream, void* stream2, const tp_mlp_desc*
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of tp_mlp_forward_noalloc: a file-scope device array, one copy
+// per GPU.  Host code never passes the array's name to a kernel (on the host
+// it names a stand-in, not the device copy): each device's address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) char scratch[TP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+tp_status noalloc_scratch(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "noalloc: device of the stream");
+  if (dev < 0 || dev >= kMaxDevices) return fail(TP_ERR_HIP, "noalloc: device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    TP_TRY(hip_status(hipGetDevice(&cur), "noalloc: current device"));
+    if (cur != dev) TP_TRY(hip_status(hipSetDevice(dev), "noalloc: select the stream's device"));
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess && r != hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return hip_status(e, "noalloc: hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(TP_ERR_HIP, "noalloc: hipGetSymbolAddress(scratch) gave NULL on device %d", dev);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tp_status tp_mlp_forward_noalloc(void* stream, const tp_mlp_desc* d) {
+  MlpShape sh;
+  TP_TRY(validate_mlp(d, &sh));
+  if (d->shard_count != d->N)
+    return fail(TP_ERR_SHAPE, "the allocation-free forward needs the whole shard range (shard_count %d != N %d)",
+                d->shard_count, d->N);
+  if (d->T == 0) return ok();
+  if (sh.total > TP_NOALLOC_SCRATCH_BYTES)
+    return fail(TP_ERR_WORKSPACE,
+                "the allocation-free forward needs %zu bytes of workspace, more than its %zu-byte static scratch "
+                "(T=%lld H=%lld F=%lld N=%d); use tp_mlp_forward with a caller workspace",
+                sh.total, (size_t)TP_NOALLOC_SCRATCH_BYTES, (long long)d->T, (long long)d->H, (long long)d->F,
+                d->N);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  TP_TRY(noalloc_scratch(s, &ws));
+  TP_TRY(mlp_rows(s, d, sh, ws, 0, d->T));
+  return run_reduce(s, d->dt, d->N, d->T, d->H, reinterpret_cast<float*>(ws), d->T * d->H, d->b, d->Y, d->n_slices,
+                    d->slice);
+}
+
 size_t tp_mlp_backward_workspace_size(const tp_mlp_bwd_desc* d) {
   BwdShape sh;
   return validate_mlp_bwd(d, &sh) == TP_OK ? sh.total : 0;
@@ -859,7 +922,6 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
             dt_name(dt), (int)d->act, d->N, i0, i0 + c, (long long)T, (long long)H, (long long)Fs, S,
             c == d->N ? " ; reduce dX" : "");
   char* base = static_cast<char*>(ws);
-  float* P = reinterpret_cast<float*>(base);
   char* Z = base + sh.z_off;
   char* dZ = base + sh.dz_off;
   char* Hs = base + sh.h_off;

@@ -86,6 +86,7 @@ _SIGS = {
     "tp_attn_partials_offset": (_sz, [ctypes.POINTER(AttnDesc)]),
     "tp_mlp_forward": (_int, [_vp, ctypes.POINTER(MlpDesc), _vp, _sz]),
     "tp_mlp_forward_overlap": (_int, [_vp, _vp, ctypes.POINTER(MlpDesc), _int, _vp, _sz]),
+    "tp_mlp_forward_noalloc": (_int, [_vp, ctypes.POINTER(MlpDesc)]),
     "tp_attn_forward": (_int, [_vp, ctypes.POINTER(AttnDesc), _vp, _sz]),
     "tp_mlp_backward_workspace_size": (_sz, [ctypes.POINTER(MlpBwdDesc)]),
     "tp_mlp_backward": (_int, [_vp, ctypes.POINTER(MlpBwdDesc), _vp, _sz]),
@@ -165,6 +166,14 @@ def tp_mlp_forward(stream, desc: MlpDesc, ws, ws_bytes) -> int:
 
 def tp_mlp_forward_overlap(stream, stream2, desc: MlpDesc, chunks, ws, ws_bytes) -> int:
     return lib().tp_mlp_forward_overlap(stream, stream2, ctypes.byref(desc), chunks, ws, ws_bytes)
+
+
+def tp_mlp_forward_noalloc(stream, desc: MlpDesc) -> int:
+    return lib().tp_mlp_forward_noalloc(stream, ctypes.byref(desc))
+
+
+# TP_NOALLOC_SCRATCH_BYTES of include/tp.h: the static scratch of tp_mlp_forward_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def tp_attn_forward(stream, desc: AttnDesc, ws, ws_bytes) -> int:
@@ -460,6 +469,23 @@ def mlp_forward(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, ws=None, shard_begin=
         ws = alloc_workspace(need, X.device)
     check(tp_mlp_forward(_stream(stream), d, _ptr(ws), ws.numel()))
     return Y, ws
+
+
+def mlp_forward_noalloc(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, n_slices=1, slice=-1, stream=None):
+    """The whole MLP sublayer through tp_mlp_forward_noalloc: no workspace,
+    the library's static per-GPU scratch instead (at most
+    NOALLOC_SCRATCH_BYTES of workspace; calls that overlap on one GPU race).
+    Allocates only Y, and only when it is None."""
+    torch = _torch()
+    _same_dtype(X, A=A, a=a, B=B, b=b, Y=Y)
+    T, H, _ = _check_mlp(X, A, a, B, b, act)
+    rows = T if slice < 0 or n_slices < 1 else T // n_slices
+    if Y is None:
+        Y = torch.empty((rows, H), dtype=X.dtype, device=X.device)
+    _expect("Y", Y, (rows, H), X.dtype, X.device)
+    d = mlp_desc(X, A, a, B, b, N, act, Y, 0, N, n_slices, slice)
+    check(tp_mlp_forward_noalloc(_stream(stream), d))
+    return Y
 
 
 def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=None, grads=None, ws=None,

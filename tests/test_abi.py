@@ -557,3 +557,23 @@ def test_binding_rejects_wrong_shapes_before_the_c_call():
         tp.attn_local(torch.zeros((16, 300), dtype=bf), 256, torch.zeros((256, 16), dtype=bf), 2, 8, 2)
     with pytest.raises(ValueError, match="Vt must be"):
         tp.attn_local(torch.zeros((16, 512), dtype=bf), 256, torch.zeros((256, 15), dtype=bf), 2, 8, 2)
+
+
+def test_mlp_forward_noalloc_rejects_before_any_hip_call(L):
+    """The allocation-free forward validates like tp_mlp_forward, then
+    refuses a partial shard range and any problem whose workspace exceeds its
+    static scratch -- all before touching the GPU."""
+    assert tp.NOALLOC_SCRATCH_BYTES == 64 << 20
+    hdr = open(HEADER).read()
+    assert re.search(r"#define TP_NOALLOC_SCRATCH_BYTES \(\(size_t\)64 << 20\)", hdr)
+    d = _mlp(F=2050)
+    assert tp.tp_mlp_forward_noalloc(None, d) == tp.TP_ERR_DIVISIBILITY
+    d = _mlp(shard_count=1)
+    assert tp.tp_mlp_forward_noalloc(None, d) == tp.TP_ERR_SHAPE
+    assert "whole shard range" in tp.last_error()
+    d = _mlp(T=16384, H=512, F=2048, N=4, shard_count=4)  # 128 MiB of partials
+    assert tp.tp_mlp_workspace_size(d) > tp.NOALLOC_SCRATCH_BYTES
+    assert tp.tp_mlp_forward_noalloc(None, d) == tp.TP_ERR_WORKSPACE
+    assert "static scratch" in tp.last_error()
+    d = _mlp(T=0)
+    assert tp.tp_mlp_forward_noalloc(None, d) == tp.TP_OK  # empty input: nothing to do
