@@ -42,6 +42,7 @@ __all__ = [
     "mlp_swiglu_sharded", "attention_block_sharded", "rs_slice",
     "reduce_partials_fp32", "to_bf16", "attention_block_rows",
     "rmsnorm", "seq_slices", "all_gather_rows", "sp_entry", "rmsnorm_hidden_split",
+    "layernorm", "sp_entry_layernorm", "merge_moments", "layernorm_hidden_split",
     "gelu_grad", "mlp_backward", "mlp_backward_sharded",
     "padded_vocab", "cross_entropy", "lm_head_ce", "vocab_parallel_ce",
     "silu_grad", "mlp_swiglu_backward", "mlp_swiglu_backward_sharded",
@@ -356,6 +357,68 @@ def rmsnorm_hidden_split(X_parts, g_parts, eps):
         ss = ss + np.sum(x * x, axis=-1, keepdims=True)
     inv = 1.0 / np.sqrt(ss / H + eps)
     return [x * inv * _f64(gp)[None, :] for x, gp in zip(X_parts, g_parts)]
+
+
+def layernorm(X, g, b, eps):
+    """LayerNorm over the hidden (last) axis: each row minus its mean, times
+    1/sqrt(variance + eps), then times the gain g plus the shift b (b may be
+    None).  The variance is the biased one (the mean of squared deviations,
+    divided by H).
+
+    [Blog] 3.3: LayerNorm needs the mean and the variance of the *whole*
+    hidden vector.  eps is not given by the pages; it is an argument here.
+    """
+    X = _f64(X)
+    mean = np.mean(X, axis=-1, keepdims=True)
+    var = np.mean((X - mean) ** 2, axis=-1, keepdims=True)
+    y = (X - mean) / np.sqrt(var + eps) * _f64(g)[None, :]
+    return y if b is None else y + _f64(b)[None, :]
+
+
+def sp_entry_layernorm(X, g, b, eps, n_slices):
+    """The sequence-parallel entry side with LayerNorm: each rank's sequence
+    slice normalized on its own (the norm is row-wise -- [Blog] 4.3), then the
+    all-gather along the sequence ([Blog] 4.3, [Wiki] Megatron-SP)."""
+    return all_gather_rows([layernorm(s, g, b, eps) for s in seq_slices(X, n_slices)])
+
+
+def merge_moments(a, b):
+    """Count, mean and sum of squared deviations of the union of two sets,
+    from those of each set (the pairwise update of Chan, Golub and LeVeque):
+    with d = mean_b - mean_a and n = n_a + n_b,
+        mean = mean_a + d n_b / n,   M2 = M2_a + M2_b + d^2 n_a n_b / n.
+    Exact in exact arithmetic: it follows from expanding the squared
+    deviations of each set about the union's mean."""
+    na, ma, qa = a
+    nb, mb, qb = b
+    n = na + nb
+    d = mb - ma
+    return n, ma + d * (nb / n), qa + qb + d * d * (na * nb / n)
+
+
+def layernorm_hidden_split(X_parts, g_parts, b_parts, eps):
+    """LayerNorm of an input split along hidden across ranks ([Blog] 3.3: keep
+    the norm's input split, reduce the local statistics to the global mean
+    and variance, then correct by a formula).  Each part's local statistics
+    (its count, mean and sum of squared deviations about its own mean), merged
+    over the parts in part order by ``merge_moments`` (the all-reduce of a
+    few numbers per row), then each part normalized locally with the global
+    mean and variance.  Equals ``layernorm`` of the concatenation."""
+    X_parts = [_f64(x) for x in X_parts]
+    stats = []
+    for x in X_parts:
+        m = np.mean(x, axis=-1, keepdims=True)
+        stats.append((x.shape[-1], m, np.sum((x - m) ** 2, axis=-1, keepdims=True)))
+    n, mean, m2 = stats[0]
+    for st in stats[1:]:
+        n, mean, m2 = merge_moments((n, mean, m2), st)
+    inv = 1.0 / np.sqrt(m2 / n + eps)
+    b_parts = b_parts if b_parts is not None else [None] * len(X_parts)
+    out = []
+    for x, gp, bp in zip(X_parts, g_parts, b_parts):
+        y = (x - mean) * inv * _f64(gp)[None, :]
+        out.append(y if bp is None else y + _f64(bp)[None, :])
+    return out
 
 
 # --------------------------------------------------------------------------

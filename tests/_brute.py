@@ -90,3 +90,15 @@ def cross_entropy(logits, labels):
         out.append(math.log(s) + m - row[y])
     return out
 
+
+
+def layernorm(X, g, b, eps):
+    """Plain loops: mean, biased variance, then (x - mean)/sqrt(var + eps)*g + b."""
+    out = []
+    for row in X:
+        n = len(row)
+        mean = sum(row) / n
+        var = sum((v - mean) ** 2 for v in row) / n
+        inv = 1.0 / math.sqrt(var + eps)
+        out.append([(v - mean) * inv * gg + bb for v, gg, bb in zip(row, g, b)])
+    return out

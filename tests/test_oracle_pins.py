@@ -351,3 +351,117 @@ def test_rmsnorm_hidden_split_equals_unsplit():
     for N in (1, 2, 4, 8):
         parts = O.rmsnorm_hidden_split(np.split(X, N, axis=1), np.split(g, N), 0.5)
         assert np.allclose(np.concatenate(parts, axis=1), full, rtol=1e-15, atol=0)
+
+
+# ------------------------------------------------- LayerNorm and the hidden-split norms
+def test_layernorm_hand_worked(golden_dir):
+    """LayerNorm values worked by hand (tests/golden/layernorm_hand_worked.json)."""
+    with open(os.path.join(golden_dir, "layernorm_hand_worked.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        y = O.layernorm(np.array([c["x"]]), np.array(c["g"]), np.array(c["b"]), c["eps"])[0]
+        assert np.allclose(y, c["y"], rtol=1e-14, atol=1e-15), c["work"]
+
+
+def test_layernorm_invariants():
+    """eps = 0, unit gain, no shift: every output row has mean 0 and mean
+    square 1; the norm is invariant to adding a constant to a row and to
+    positive scaling; negating a row negates the output; b shifts it."""
+    rng = np.random.default_rng(21)
+    X = rng.normal(size=(9, 24)) * 3.0 + 7.0
+    one = np.ones(24)
+    Y = O.layernorm(X, one, None, 0.0)
+    assert np.allclose(np.mean(Y, axis=1), 0.0, atol=1e-14)
+    assert np.allclose(np.mean(Y * Y, axis=1), 1.0, rtol=1e-13)
+    shift = rng.normal(size=(9, 1)) * 100.0
+    assert np.allclose(O.layernorm(X + shift, one, None, 0.0), Y, atol=1e-11)
+    alpha = rng.uniform(0.1, 10.0, size=(9, 1))
+    assert np.allclose(O.layernorm(alpha * X, one, None, 0.0), Y, atol=1e-12)
+    assert np.allclose(O.layernorm(-X, one, None, 0.0), -Y, atol=1e-14)
+    b = rng.normal(size=24)
+    assert np.allclose(O.layernorm(X, one, b, 0.0), Y + b[None, :], atol=1e-14)
+    # eps only rescales: mean square var / (var + eps)
+    var = np.var(X, axis=1)
+    Ye = O.layernorm(X, one, None, 2.0)
+    assert np.allclose(np.mean(Ye * Ye, axis=1), var / (var + 2.0), rtol=1e-13)
+
+
+def test_layernorm_matches_brute_force():
+    rng = np.random.default_rng(22)
+    X = rng.normal(size=(5, 7)) + 3.0
+    g, b = rng.normal(size=7), rng.normal(size=7)
+    ref = brute.layernorm(X.tolist(), g.tolist(), b.tolist(), 1e-3)
+    assert np.allclose(O.layernorm(X, g, b, 1e-3), ref, rtol=1e-13, atol=1e-14)
+
+
+def test_merge_moments_is_the_statistic_of_the_union():
+    """The pairwise update gives the count, mean and sum of squared
+    deviations of the concatenation, for unequal parts and any split point."""
+    rng = np.random.default_rng(23)
+    x = rng.normal(size=37) * 4.0 + 10.0
+    for cut in (1, 5, 18, 36):
+        a, b = x[:cut], x[cut:]
+        n, m, q = O.merge_moments((len(a), a.mean(), np.sum((a - a.mean()) ** 2)),
+                                  (len(b), b.mean(), np.sum((b - b.mean()) ** 2)))
+        assert n == len(x)
+        assert np.isclose(m, x.mean(), rtol=1e-14)
+        assert np.isclose(q, np.sum((x - x.mean()) ** 2), rtol=1e-12)
+    # on small integers every quantity is exact: the merge of [1, 2] and [4, 7]
+    n, m, q = O.merge_moments((2, 1.5, 0.5), (2, 5.5, 4.5))
+    assert (n, m, q) == (4, 3.5, 21.0)  # mean 14/4; deviations -2.5, -1.5, 0.5, 3.5 -> 6.25+2.25+0.25+12.25
+
+
+def test_sp_entry_layernorm_equals_full_norm_bitwise():
+    rng = np.random.default_rng(24)
+    X = rng.normal(size=(24, 16))
+    g, b = rng.normal(size=16), rng.normal(size=16)
+    full = O.layernorm(X, g, b, 1e-5)
+    for n in (1, 2, 3, 4, 8):
+        assert np.array_equal(O.sp_entry_layernorm(X, g, b, 1e-5, n), full)
+
+
+def test_layernorm_hidden_split_equals_unsplit():
+    """Blog post section 3.3: local statistics, one small reduction of them,
+    local normalization -- the parts concatenate to the unsplit norm, for
+    equal and unequal parts, with and without a shift."""
+    rng = np.random.default_rng(25)
+    X = rng.normal(size=(6, 48)) * 2.0 + 5.0
+    g, b = rng.normal(size=48), rng.normal(size=48)
+    full = O.layernorm(X, g, b, 0.25)
+    for N in (1, 2, 3, 4, 8):
+        parts = O.layernorm_hidden_split(np.split(X, N, axis=1), np.split(g, N), np.split(b, N), 0.25)
+        assert np.allclose(np.concatenate(parts, axis=1), full, rtol=0, atol=1e-13)
+    cuts = [5, 17, 40]
+    parts = O.layernorm_hidden_split(np.split(X, cuts, axis=1), np.split(g, cuts), None, 0.25)
+    assert np.allclose(np.concatenate(parts, axis=1), O.layernorm(X, g, None, 0.25), rtol=0, atol=1e-13)
+
+
+def test_planted_hidden_split_norm_mistakes():
+    """What the split norm must not do: normalize each part with its own
+    statistics (the mistake the blog post warns of in section 3.3), merge
+    without the deviation-of-means term, or sum squares about each part's
+    own mean and forget the parts' spread."""
+    rng = np.random.default_rng(26)
+    X = rng.normal(size=(4, 32))
+    X[:, 16:] += 3.0  # the two halves have different means
+    g, b = np.ones(32), np.zeros(32)
+    want = O.layernorm(X, g, b, 1e-6)
+    Xp = np.split(X, 2, axis=1)
+    local = np.concatenate([O.layernorm(x, np.ones(16), None, 1e-6) for x in Xp], axis=1)
+    assert np.max(np.abs(local - want)) > 0.5
+
+    saved = O.merge_moments
+
+    def no_spread(a, c):  # drops the d^2 n_a n_b / n term
+        n, m, q = saved(a, c)
+        d = c[1] - a[1]
+        return n, m, q - d * d * (a[0] * c[0] / n)
+
+    try:
+        O.merge_moments = no_spread
+        wrong = np.concatenate(O.layernorm_hidden_split(Xp, [np.ones(16)] * 2, None, 1e-6), axis=1)
+    finally:
+        O.merge_moments = saved
+    assert np.max(np.abs(wrong - want)) > 0.5
+    right = np.concatenate(O.layernorm_hidden_split(Xp, [np.ones(16)] * 2, None, 1e-6), axis=1)
+    assert np.allclose(right, want, atol=1e-13)
