@@ -31,6 +31,7 @@ METRIC = "TFLOP/s per sharded TP MLP/attn layer fwd on 1 GPU; % of bf16 MFMA pea
 METRIC_BWD = "TFLOP/s per sharded TP MLP layer bwd on 1 GPU; % of bf16 MFMA peak"
 METRIC_VOCAB = "TFLOP/s of the vocab-parallel output head + cross-entropy fwd on 1 GPU; % of bf16 MFMA peak"
 METRIC_EMBED = "GB/s (algorithmic bytes) of the vocab-parallel embedding lookup fwd on 1 GPU; % of HBM peak"
+METRIC_NORM = "GB/s (algorithmic bytes) of the hidden-split norm (local statistics, their fold, local scaling) on 1 GPU; % of HBM peak"
 PEAK_BF16 = 2.5e15     # dense MFMA, bf16
 PEAK_F32 = 157.3e12    # dense MFMA, fp32
 PEAK_HBM = 8.0e12      # bytes/s
@@ -90,10 +91,19 @@ def kernel_work(w, name, shards_per_launch, rows_reduced):
         return 0.0, 4 * c * T + es * T * H * c / N + es * c * T * H
     if w.kind == "vocab_embed" and name == "vocab_embed_fold":  # N partials in, the rows out
         return 0.0, es * N * T * H + es * T * H
+    if w.kind.startswith("norm_split"):
+        Hs = H // N
+        if name == "norm_split_stats":  # each shard's slices read once, one statistic pair per (shard, row) out
+            return 0.0, es * c * T * Hs + 8 * c * T
+        if name == "norm_split_apply":  # the slices again, the outputs, N statistic pairs per (shard, row), g (b)
+            nb = 2 if w.kind == "norm_split_layer" else 1
+            return 0.0, 2 * es * c * T * Hs + 8 * N * c * T + nb * es * c * Hs
     if name == "reduce_partials":
         return 0.0, 4 * N * rows_reduced * H + es * rows_reduced * H + (es * H if w.sigma_bias else 0)
     if name == "rmsnorm_gather":  # square, add, two scalings per element; X read once, Y written once
         return 4.0 * T * H, es * (2 * T * H + H)
+    if name == "layernorm_gather":  # sum, deviation, square, add, scale, gain, shift; X once, Y once
+        return 7.0 * T * H, es * (2 * T * H + 2 * H)
     raise KeyError(name)
 
 
@@ -185,6 +195,7 @@ KERNEL_SOURCES = {
     "bwd_splitk_reduce": "reduce.hip", "bwd_fused_gemm": "gemm.hip",
     "vocab_logits_gemm": "gemm.hip", "vocab_ce_fold": "vocab.hip", "vocab_ce_combine": "vocab.hip",
     "vocab_ce_mean": "vocab.hip", "vocab_embed_partial": "vocab.hip", "vocab_embed_fold": "vocab.hip",
+    "layernorm_gather": "norm.hip", "norm_split_stats": "norm.hip", "norm_split_apply": "norm.hip",
 }
 
 
@@ -213,6 +224,8 @@ KERNEL_SYMBOL = {
     "vocab_logits_gemm": "gemm_", "vocab_ce_fold": "ce_fold_kernel", "vocab_ce_combine": "ce_combine_kernel",
     "vocab_ce_mean": "ce_mean_kernel", "vocab_embed_partial": "embed_partial_kernel",
     "vocab_embed_fold": "embed_fold_kernel",
+    "layernorm_gather": "rmsnorm_gather_kernel", "norm_split_stats": "norm_split_stats_kernel",
+    "norm_split_apply": "norm_split_apply_kernel",
 }
 
 
@@ -243,7 +256,10 @@ def launch_order(w, sp_entry=False, backward=False):
         return ["vocab_logits_gemm", "vocab_ce_fold", "vocab_ce_combine", "vocab_ce_mean"]
     if w.kind == "vocab_embed":
         return ["vocab_embed_partial", "vocab_embed_fold"]
-    head = ["rmsnorm_gather"] if sp_entry else []
+    if w.kind.startswith("norm_split"):
+        return ["norm_split_stats", "norm_split_apply"]
+    # sp_entry: False, or the entry norm ("rms" / True: RMSNorm; "layer": LayerNorm)
+    head = ([("layernorm_gather" if sp_entry == "layer" else "rmsnorm_gather")] if sp_entry else [])
     if w.kind == "attn":
         return head + ["attn_qk_gemm", "attn_vt_gemm", "attn_core", "attn_out_gemm", "reduce_partials"]
     Fs = w.F // w.N
@@ -271,7 +287,8 @@ def measured_traffic(kernel, workload_name):
 
 
 def workload_tag(w, sp_entry=False, backward=False):
-    return w.name + ("_sp_entry" if sp_entry else "") + ("_backward" if backward else "")
+    return (w.name + ("_sp_entry" if sp_entry else "") + ("_layernorm" if sp_entry == "layer" else "")
+            + ("_backward" if backward else ""))
 
 
 def write_traffic(w, share, pmc_dir, argv_line, sp_entry=False, backward=False, out_dir=None):
@@ -311,7 +328,8 @@ def write_traffic(w, share, pmc_dir, argv_line, sp_entry=False, backward=False, 
         "# Commands (from /tmp on the GPU host, REPO = repository root):",
         f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d DIR/FETCH_SIZE -o run -- python3 $REPO/bench.py {argv_line}",
         f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d DIR/WRITE_SIZE -o run -- python3 $REPO/bench.py {argv_line}",
-        f"#   python3 $REPO/bench.py --config {w.key} --share {share}{' --sp-entry' if sp_entry else ''}"
+        f"#   python3 $REPO/bench.py --config {w.key} --share {share}"
+        f"{(' --sp-entry' + (' --norm layer' if sp_entry == 'layer' else '')) if sp_entry else ''}"
         f"{' --backward' if backward else ''} --traffic-from DIR",
         "#",
         f"# Calibration (1 GiB device copy): FETCH_SIZE x {factor['FETCH_SIZE']:.4f}, WRITE_SIZE x {factor['WRITE_SIZE']:.4f}",
@@ -371,7 +389,8 @@ def write_mfma(w, share, pmc_dir, argv_line, sp_entry=False, backward=False, out
         "#",
         "# Command (from /tmp on the GPU host, REPO = repository root):",
         f"#   rocprofv3 --pmc MfmaFlopsBF16 MfmaUtil -f csv -d DIR -o run -- python3 $REPO/bench.py {argv_line}",
-        f"#   python3 $REPO/bench.py --config {w.key} --share {share}{' --sp-entry' if sp_entry else ''}"
+        f"#   python3 $REPO/bench.py --config {w.key} --share {share}"
+        f"{(' --sp-entry' + (' --norm layer' if sp_entry == 'layer' else '')) if sp_entry else ''}"
         f"{' --backward' if backward else ''} --mfma-from DIR",
         "#",
         "# MfmaFlopsBF16 = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (executed matrix FLOP, padding and recomputation",
@@ -491,6 +510,8 @@ def cpu_baseline(w, host, seconds):
         cores = len(os.sched_getaffinity(0))
     if w.kind == "vocab_embed":
         return cpu_baseline_embed(w, host, seconds, cores)
+    if w.kind.startswith("norm_split"):
+        return cpu_baseline_norm(w, host, seconds, cores)
     chunk = 256 if w.kind != "attn" else 8
     order = np.random.default_rng(w.seed + 98).permutation(w.T)  # seeded order of all token rows
     done, flops = 0, 0.0
@@ -535,6 +556,27 @@ def cpu_baseline_embed(w, host, seconds, cores):
     return {"value": round(done * per_token / el / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done} token rows in seeded blocks of 2048 over the workload's {w.T}, fp64 numpy "
                       f"(each call converts the table to fp64), {el:.1f} s"}
+
+
+def cpu_baseline_norm(w, host, seconds, cores):
+    """fp64 oracle hidden-split norm on seeded blocks of 1024 token rows;
+    GB/s counted with the same algorithmic bytes per token as the GPU figure."""
+    import numpy as np
+
+    from oracle import reference as R
+
+    order = np.random.default_rng(w.seed + 98).permutation(w.T)
+    per_token = sum(kernel_work(w, k, w.N, w.T)[1] for k in launch_order(w)) / w.T
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        start = done % w.T
+        rows = np.sort(order[start:start + 1024])
+        R.workload(w.kind, host, rows=rows, N=w.N, eps=1e-6)
+        done += len(rows)
+    el = time.perf_counter() - t0
+    return {"value": round(done * per_token / el / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} token rows in seeded blocks of 1024 over the workload's {w.T}, fp64 numpy, {el:.1f} s"}
 
 
 def cpu_baseline_backward(w, host, dY, seconds):
@@ -588,6 +630,8 @@ def main():
     ap.add_argument("--sp-entry", action="store_true",
                     help="MLP workloads with a reduce-scatter: start each step with the sequence-parallel entry "
                          "side (RMSNorm of every sequence slice into the gathered input, the all-gather stand-in)")
+    ap.add_argument("--norm", choices=["rms", "layer"], default="rms",
+                    help="with --sp-entry: the entry norm, RMSNorm (default) or LayerNorm")
     ap.add_argument("--backward", action="store_true",
                     help="GELU MLP workloads (2, 5): time the backward of the pair instead (input, weight and "
                          "bias gradients of every shard, then the input-gradient reduction)")
@@ -608,12 +652,15 @@ def main():
                     help="write profiles/traffic_<workload>.txt from rocprofv3 --pmc csv runs under DIR "
                          "(DIR/FETCH_SIZE, DIR/WRITE_SIZE) and exit; runs on the host, no GPU")
     args = ap.parse_args()
+    if args.sp_entry:
+        args.sp_entry = args.norm  # the entry norm's kind travels with the flag
+    sp_flags = (" --sp-entry" + (" --norm layer" if args.sp_entry == "layer" else "")) if args.sp_entry else ""
 
     if args.mfma_from:
         from tensor_transformer_layers_amd import configs
 
         w = configs.workload(args.config)
-        argv = (f"--config {args.config} --share {args.share}{' --sp-entry' if args.sp_entry else ''}"
+        argv = (f"--config {args.config} --share {args.share}{sp_flags}"
                 f"{' --backward' if args.backward else ''} --steps 3 --warmup 1 --no-cpu-baseline")
         print(write_mfma(w, args.share, args.mfma_from, argv, args.sp_entry, args.backward))
         return
@@ -625,7 +672,7 @@ def main():
         if args.steps is None or args.overlap:
             print("bench.py --trace-from needs the --steps of the profiled run (and no --overlap)", file=sys.stderr)
             sys.exit(2)
-        argv = (f"--config {args.config} --share {args.share}{' --sp-entry' if args.sp_entry else ''}"
+        argv = (f"--config {args.config} --share {args.share}{sp_flags}"
                 f"{' --backward' if args.backward else ''} --steps {args.steps} --no-cpu-baseline")
         print(write_trace(w, args.share, args.trace_from, argv, args.steps, args.sp_entry, args.backward))
         return
@@ -634,7 +681,7 @@ def main():
         from tensor_transformer_layers_amd import configs
 
         w = configs.workload(args.config)
-        argv = (f"--config {args.config} --share {args.share}{' --sp-entry' if args.sp_entry else ''}"
+        argv = (f"--config {args.config} --share {args.share}{sp_flags}"
                 f"{' --backward' if args.backward else ''} --steps 3 --warmup 1 --no-cpu-baseline --calib-copy")
         print(write_traffic(w, args.share, args.traffic_from, argv, args.sp_entry, args.backward))
         return
@@ -654,6 +701,10 @@ def main():
     w = configs.workload(args.config)
     if w.kind in ("vocab_ce", "vocab_embed") and (args.share != "layer" or args.sp_entry or args.backward):
         print("bench.py: the vocab workloads (--config 6, 7) run with --share layer only",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    if w.kind.startswith("norm_split") and (args.share != "layer" or args.sp_entry or args.backward or args.overlap):
+        print("bench.py: the hidden-split norm workloads (--config 8, 9) run with --share layer only",
               file=sys.stderr, flush=True)
         sys.exit(2)
     if args.overlap and (w.kind not in ("mlp_gelu", "mlp_swiglu") or args.share != "layer" or args.backward
@@ -679,9 +730,17 @@ def main():
         # X holds the n_slices sequence slices of the sublayer input; each step
         # normalizes them into Xn, the gathered input of the column GEMM
         gain = workloads.to_device(inputs.norm_gain(w), d["X"].dtype)
+        shift = workloads.to_device(inputs.norm_shift(w), d["X"].dtype) if args.sp_entry == "layer" else None
         x_slices = d["X"]
         d = dict(d, X=torch.empty_like(x_slices))
-        tp.rmsnorm_gather(x_slices, gain, inputs.NORM_EPS, w.n_slices, out=d["X"])
+
+        def entry_norm(stream=None):
+            if args.sp_entry == "layer":
+                tp.layernorm_gather(x_slices, gain, shift, inputs.NORM_EPS, w.n_slices, out=d["X"], stream=stream)
+            else:
+                tp.rmsnorm_gather(x_slices, gain, inputs.NORM_EPS, w.n_slices, out=d["X"], stream=stream)
+
+        entry_norm()
     if args.backward:
         grads, ws = workloads.backward(w, d, dY)  # allocates the gradients and the workspace once
         Y = grads["dX"]
@@ -699,14 +758,14 @@ def main():
     def step():
         if args.overlap:
             if args.sp_entry:
-                tp.rmsnorm_gather(x_slices, gain, inputs.NORM_EPS, w.n_slices, out=d["X"], stream=stream)
+                entry_norm(stream)
             workloads.forward_overlap(w, d, args.overlap, stream2, Y=Y, ws=ws, stream=stream)
             return
         if args.backward:
             workloads.backward(w, d, dY, grads=grads, ws=ws, stream=stream)
             return
         if args.sp_entry:
-            tp.rmsnorm_gather(x_slices, gain, inputs.NORM_EPS, w.n_slices, out=d["X"], stream=stream)
+            entry_norm(stream)
         if args.share == "layer":
             workloads.forward(w, d, Y=Y, ws=ws, stream=stream)
         else:
@@ -786,11 +845,12 @@ def main():
     rows_red = w.T if (args.share == "layer" or w.n_slices == 1) else w.T // w.n_slices
     flops = w.flops_layer() if args.share == "layer" else w.flops_shard()
     if args.sp_entry:
-        flops += kernel_work(w, "rmsnorm_gather", 1, 0)[0]
+        flops += kernel_work(w, "layernorm_gather" if args.sp_entry == "layer" else "rmsnorm_gather", 1, 0)[0]
     if args.backward:
         flops = backward_flops(w, w.N)
     value = flops / (ms_step / 1e3) / 1e12
-    if w.kind == "vocab_embed":  # a lookup: algorithmic bytes of the step (every kernel) per second
+    bytes_metric = w.kind == "vocab_embed" or w.kind.startswith("norm_split")
+    if bytes_metric:  # no arithmetic to speak of: algorithmic bytes of the step (every kernel) per second
         step_bytes = sum(kernel_work(w, k, shards, rows_red)[1] for k in launch_order(w))
         value = step_bytes / (ms_step / 1e3) / 1e9
 
@@ -817,9 +877,10 @@ def main():
 
     out = {
         "metric": (METRIC_BWD if args.backward else METRIC_VOCAB if w.kind == "vocab_ce" else
-                   METRIC_EMBED if w.kind == "vocab_embed" else METRIC),
+                   METRIC_EMBED if w.kind == "vocab_embed" else
+                   METRIC_NORM if w.kind.startswith("norm_split") else METRIC),
         "value": round(value, 3),
-        "unit": "GB/s" if w.kind == "vocab_embed" else "TFLOP/s",
+        "unit": "GB/s" if bytes_metric else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": warm_done,
@@ -840,9 +901,17 @@ def main():
             **({"vocab": w.F, "vocab_padded": tp.tp_vocab_padded(w.F, w.N), "ids": inputs.ID_RECIPE,
                 "bytes_counted": "ids per shard, each token's row once, N partials in the table's type "
                                  "written and read, the rows written"} if w.kind == "vocab_embed" else {}),
+            **({"norm": "layernorm" if w.kind == "norm_split_layer" else "rmsnorm", "eps": inputs.NORM_EPS,
+                "features_per_shard": w.H // w.N,
+                "bytes_counted": "each kernel's inputs read once and outputs written once: the slices twice "
+                                 "(statistics, then scaling), the outputs once, the statistics slab written "
+                                 "once and read N times per (shard, row), gain (and shift)"}
+               if w.kind.startswith("norm_split") else {}),
             "share": "all shards + reduction" if args.share == "layer" else "rank 0 shard + reduction",
             "reduce_scatter_slices": w.n_slices, "seed": w.seed,
-            **({"sp_entry": {"norm": "rmsnorm", "eps": inputs.NORM_EPS, "gain": inputs.NORM_GAIN_RECIPE}}
+            **({"sp_entry": {"norm": "layernorm" if args.sp_entry == "layer" else "rmsnorm", "eps": inputs.NORM_EPS,
+                             "gain": inputs.NORM_GAIN_RECIPE,
+                             **({"shift": inputs.NORM_SHIFT_RECIPE} if args.sp_entry == "layer" else {})}}
                if args.sp_entry else {}),
             **({"overlap_chunks": args.overlap} if args.overlap else {}),
             **({"pass": "backward", "upstream_gradient": inputs.GRAD_RECIPE,
@@ -852,8 +921,8 @@ def main():
                if args.backward else {}),
         },
         "pct_of_bf16_mfma_peak": (round(100 * value * 1e12 / PEAK_BF16, 2)
-                                  if w.dtype == "bf16" and w.kind != "vocab_embed" else None),
-        **({"pct_of_hbm_peak": round(100 * value * 1e9 / PEAK_HBM, 2)} if w.kind == "vocab_embed" else {}),
+                                  if w.dtype == "bf16" and not bytes_metric else None),
+        **({"pct_of_hbm_peak": round(100 * value * 1e9 / PEAK_HBM, 2)} if bytes_metric else {}),
         "roofline": roof,
         "kernels": kernels,
         "kernel_source_hash": src_hash,

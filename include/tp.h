@@ -134,6 +134,67 @@ tp_status tp_rmsnorm_gather(void* stream, tp_dtype dt, int n_slices, int64_t T, 
                             const void* X, int64_t slice_stride, int64_t ldx, const void* gamma,
                             float eps, void* Y, int64_t ldy, int slice);
 
+/*
+ * The same entry side with LayerNorm (the blog post, section 3.3, names
+ * LayerNorm beside RMSNorm: it needs the mean and the variance of the whole
+ * hidden vector, so it too runs exactly on sequence slices):
+ *
+ *   Y[r*T/n + t, :] = (X_r[t, :] - m) / sqrt(v + eps) * gamma + beta
+ *
+ * with m the row's mean and v its mean squared deviation from m (the biased
+ * variance).  Arguments as tp_rmsnorm_gather; beta [H] (same dtype) or NULL
+ * for no shift.  The statistics are fp32 sums in a fixed order: the values
+ * first, then the squared deviations from their mean (two passes over the
+ * row held on chip, so no cancellation between a sum of squares and a
+ * squared mean); bit-identical run to run; one RNE cast.
+ */
+tp_status tp_layernorm_gather(void* stream, tp_dtype dt, int n_slices, int64_t T, int64_t H, const void* X,
+                              int64_t slice_stride, int64_t ldx, const void* gamma, const void* beta, float eps,
+                              void* Y, int64_t ldy, int slice);
+
+/*
+ * Norm of an input split along hidden across N shards (2kiu.com blog post,
+ * section 3.3: keep the norm's input split along hidden, reduce the small
+ * local statistics to the global ones, correct by a formula, scale locally).
+ * Shard i holds columns [i*H/N, (i+1)*H/N) of X and writes the same columns
+ * of Y.  Two steps, the two sides of the statistic's all-reduce:
+ *   1. for each shard in [shard_begin, shard_begin + shard_count) and row t,
+ *      the shard's local statistic into slot (i, t) of the workspace slab
+ *      (N x T x 2 fp32):
+ *        TP_NORM_RMS    its sum of squares
+ *        TP_NORM_LAYER  its mean m_i and sum of squared deviations q_i
+ *   2. each shard of the range folds the N slots of the row in shard order
+ *      -- RMS: sums added; LAYER: (count, mean, q) merged by the pairwise
+ *      update d = m_i - m, n' = n + H/N, m += d (H/N)/n',
+ *      q += q_i + d^2 n (H/N)/n' -- and scales its own columns:
+ *        RMS    Y = X / sqrt(sum/H + eps) * gamma
+ *        LAYER  Y = (X - m) / sqrt(q/H + eps) * gamma + beta
+ * Every shard folds the same slots in the same order, so every shard uses
+ * the same bits (the broadcast of the reduced statistic).  With
+ * shard_count < N, step 2 reads the other shards' slots as they are in the
+ * slab (left there by earlier calls): one rank's share.
+ *   X, Y   [T x H] (ldx, ldy), dt;  gamma [H] dt;  beta [H] dt or NULL (must
+ *          be NULL for RMS);  eps finite, >= 0
+ * H/N a multiple of 8 (bf16) or 4 (fp32), at most 16384 (bf16) / 8192 (fp32).
+ */
+typedef enum { TP_NORM_RMS = 0, TP_NORM_LAYER = 1 } tp_norm_kind;
+typedef struct {
+  tp_dtype dt;
+  tp_norm_kind kind;
+  int64_t T, H;
+  int N, shard_begin, shard_count;
+  const void* X;
+  int64_t ldx;
+  const void* gamma;
+  const void* beta;
+  float eps;
+  void* Y;
+  int64_t ldy;
+} tp_norm_split_desc;
+/* Workspace bytes (the N x T x 2 fp32 statistics slab), 0 when invalid. */
+size_t tp_norm_split_workspace_size(const tp_norm_split_desc* d);
+tp_status tp_norm_hidden_split(void* stream, const tp_norm_split_desc* d, void* ws, size_t ws_bytes);
+
 /* Whole MLP sublayer over shards [shard_begin, shard_begin + shard_count). */
 typedef struct {
   tp_dtype dt;      /* TP_F32 or TP_BF16 (inputs, intermediate and output)      */
@@ -273,6 +334,12 @@ typedef struct {
   float* da;       /* [F] (entries of the range) or NULL to skip                */
   float* dB;       /* [H x F]: columns of the shard range written               */
   float* db;       /* [H] or NULL to skip                                       */
+  int n_slices, slice; /* the dX fold's layout, as in tp_reduce_partials: 1, -1 for
+                       the all-reduce; n_slices > 1 and slice = r for rank r's
+                       reduce-scatter slice along the sequence (dX then holds
+                       the T/n_slices rows r*T/n_slices ..), the backward of the
+                       sequence-parallel all-gather ("张量并行", Megatron-SP
+                       section); slice = -1 writes every slice          */
 } tp_mlp_bwd_desc;
 
 /* Workspace bytes for tp_mlp_backward (0 when the descriptor is invalid).

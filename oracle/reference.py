@@ -47,11 +47,29 @@ def vocab_embed(E, ids, V, N, rows=None):
     return O.vocab_parallel_embedding(ids, E, V, N)[0]
 
 
-def workload(kind, host, batch=None, seq=None, heads=None, rows=None, N=None):
+def norm_split(kind, X, g, b, eps, N, rows=None):
+    """The hidden-split norm ("norm_split_layer" | "norm_split_rms") of the
+    rows ``rows`` of X (all if None) over N equal parts of the hidden axis.
+    Row-wise, so a row's value needs no other row."""
+    Xr = np.asarray(X)
+    if rows is not None:
+        Xr = Xr[np.asarray(rows)]
+    parts = np.split(Xr.astype(np.float64), N, axis=1)
+    gp = np.split(np.asarray(g, dtype=np.float64), N)
+    if kind == "norm_split_layer":
+        bp = None if b is None else np.split(np.asarray(b, dtype=np.float64), N)
+        return np.concatenate(O.layernorm_hidden_split(parts, gp, bp, eps), axis=1)
+    return np.concatenate(O.rmsnorm_hidden_split(parts, gp, eps), axis=1)
+
+
+def workload(kind, host, batch=None, seq=None, heads=None, rows=None, N=None, eps=1e-6):
     """Expected output rows of one workload ("mlp_gelu" | "mlp_swiglu" |
-    "attn" | "vocab_ce": the per-token loss | "vocab_embed": N shards)."""
+    "attn" | "vocab_ce": the per-token loss | "vocab_embed": N shards |
+    "norm_split_layer" / "norm_split_rms": N shards, eps)."""
     if kind == "vocab_embed":
         return vocab_embed(host["E"], host["ids"], host["E"].shape[0], N, rows)
+    if kind.startswith("norm_split"):
+        return norm_split(kind, host["X"], host["g"], host["b"] if kind == "norm_split_layer" else None, eps, N, rows)
     if kind == "vocab_ce":
         return vocab_ce(host["X"], host["E"], host["labels"], host["E"].shape[0], rows)
     if kind == "mlp_gelu":

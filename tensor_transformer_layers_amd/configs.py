@@ -22,7 +22,8 @@ from dataclasses import dataclass, field
 class Workload:
     key: int
     name: str
-    kind: str               # "mlp_gelu" | "mlp_swiglu" | "attn" | "vocab_ce" | "vocab_embed"
+    kind: str               # "mlp_gelu" | "mlp_swiglu" | "attn" | "vocab_ce" | "vocab_embed" |
+                            # "norm_split_layer" | "norm_split_rms"
     dtype: str              # "f32" | "bf16"  (inputs; accumulation is fp32)
     batch: int
     seq: int
@@ -53,6 +54,8 @@ class Workload:
         with the diagonal: 4 * d * S(S+1)/2 per (batch, head)."""
         T, H = self.T, self.H
         if self.kind == "vocab_embed":  # a lookup: no arithmetic
+            return 0.0
+        if self.kind.startswith("norm_split"):  # HBM-bound: measured in bytes, not FLOP
             return 0.0
         if self.kind == "vocab_ce":  # the head's product over the real vocab, one shard's share
             return 2.0 * T * H * self.F / self.N
@@ -102,6 +105,16 @@ EXTRA: dict[int, Workload] = {
                 batch=8, seq=2048, H=4096, F=150000, N=8,
                 sigma_w=0.02, sigma_bias=None, seed=20260007),
 }
+
+
+# The norm at a sublayer boundary when its input stays split along hidden
+# (the blog post at 2kiu.com, section 3.3): the 175B-shaped layer's hidden
+# size, 12288, over 8 shards (1536 features each), 8 x 2048 tokens.  Gain
+# 1 + N(0, 0.1^2); LayerNorm shift N(0, 0.1^2).
+EXTRA[8] = Workload(8, "layernorm_split_bf16_T16384_H12288_N8", "norm_split_layer", "bf16",
+                    batch=8, seq=2048, H=12288, F=12288, N=8, sigma_bias=0.1, seed=20260008)
+EXTRA[9] = Workload(9, "rmsnorm_split_bf16_T16384_H12288_N8", "norm_split_rms", "bf16",
+                    batch=8, seq=2048, H=12288, F=12288, N=8, sigma_bias=None, seed=20260009)
 
 
 def workload(key: int) -> Workload:

@@ -223,6 +223,40 @@ tp_status validate_norm(tp_dtype dt, int n_slices, int64_t T, int64_t H, const v
   return TP_OK;
 }
 
+tp_status validate_norm_split(const tp_norm_split_desc* d, size_t* need) {
+  if (!d) return fail(TP_ERR_NULL, "descriptor is NULL");
+  TP_TRY(check_dtype(d->dt));
+  if (d->kind != TP_NORM_RMS && d->kind != TP_NORM_LAYER) return fail(TP_ERR_DTYPE, "norm kind %d unknown", (int)d->kind);
+  if (d->T < 0 || d->H <= 0 || d->N <= 0)
+    return fail(TP_ERR_SHAPE, "T=%lld H=%lld N=%d", (long long)d->T, (long long)d->H, d->N);
+  if (d->H % d->N)
+    return fail(TP_ERR_DIVISIBILITY, "hidden H=%lld is not divisible by N=%d shards (shard would be %lld + %lld/%d)",
+                (long long)d->H, d->N, (long long)(d->H / d->N), (long long)(d->H % d->N), d->N);
+  if (d->shard_begin < 0 || d->shard_count < 1 || d->shard_begin + d->shard_count > d->N)
+    return fail(TP_ERR_SHAPE, "shard range [%d, %d) outside [0, %d)", d->shard_begin,
+                d->shard_begin + d->shard_count, d->N);
+  const int64_t vec = vec_of(d->dt), Hs = d->H / d->N;
+  if (Hs % vec)
+    return fail(TP_ERR_ALIGN, "shard width H/N=%lld is not a multiple of %lld (%s)", (long long)Hs, (long long)vec,
+                dt_name(d->dt));
+  const int64_t hmax = tp::rmsnorm_max_hidden(d->dt == TP_BF16);
+  if (Hs > hmax)
+    return fail(TP_ERR_SHAPE, "shard width H/N=%lld exceeds the norm kernel's limit %lld", (long long)Hs, (long long)hmax);
+  if (!(d->eps >= 0.0f) || !std::isfinite(d->eps))
+    return fail(TP_ERR_SHAPE, "eps=%g must be finite and >= 0", (double)d->eps);
+  if (d->kind == TP_NORM_RMS && d->beta) return fail(TP_ERR_SHAPE, "RMSNorm takes no beta (must be NULL)");
+  *need = 0;
+  if (d->T == 0) return TP_OK;  // empty input: nothing to read or write
+  TP_TRY(check_matrix("X", d->X, d->T, d->H, d->ldx, vec));
+  TP_TRY(check_matrix("Y", d->Y, d->T, d->H, d->ldy, vec));
+  if (!d->gamma) return fail(TP_ERR_NULL, "gamma is NULL");
+  if (!aligned16(d->gamma)) return fail(TP_ERR_ALIGN, "gamma is not 16-byte aligned");
+  if (d->beta && !aligned16(d->beta)) return fail(TP_ERR_ALIGN, "beta is not 16-byte aligned");
+  if (d->T > kIntMax || (int64_t)d->N * d->T > kIntMax) return fail(TP_ERR_SHAPE, "N*T exceeds 2^31-1");
+  *need = align256((size_t)d->N * d->T * 2 * sizeof(float));
+  return TP_OK;
+}
+
 tp::GemmParams gemm(const void* A, int64_t lda, int64_t sA, const void* B, int64_t ldb, int64_t sB, void* C,
                     int64_t ldc, int64_t sC, int64_t M, int64_t N, int64_t K, int batch) {
   tp::GemmParams p{};
@@ -443,6 +477,7 @@ tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
   sh->Fz = swiglu ? 2 * Fc : Fc;
   sh->zld = sh->Fz;
   sh->splits = 1;
+  TP_TRY(check_slices(d->T, d->n_slices, d->slice));
   if (d->T == 0) return TP_OK;  // empty input: nothing to read, write or stage
   if (d->T % 8) return fail(TP_ERR_ALIGN, "T=%lld is not a multiple of 8", (long long)d->T);
   if (d->H % 8) return fail(TP_ERR_ALIGN, "hidden H=%lld is not a multiple of 8", (long long)d->H);
@@ -502,7 +537,7 @@ tp_status bwd_tail(hipStream_t s, const tp_mlp_bwd_desc* d, const BwdShape& sh, 
   if (d->db) TP_TRY(rowsum("bwd_bias_rowsum", dYT, T, d->db, H, T));
 
   if (c < d->N) return ok();
-  return run_reduce(s, d->dt, d->N, T, H, P, T * H, nullptr, d->dX, 1, -1);
+  return run_reduce(s, d->dt, d->N, T, H, P, T * H, nullptr, d->dX, d->n_slices, d->slice);
 }
 
 // ------------------------------------------------------- vocab-parallel CE
@@ -678,6 +713,85 @@ tp_status tp_rmsnorm_gather(void* stream, tp_dtype dt, int n_slices, int64_t T, 
   const hipError_t e = tp::launch_rmsnorm_gather(p, dt == TP_BF16, s);
   kt.stop();
   TP_TRY(hip_status(e, "rmsnorm_gather launch"));
+  return ok();
+}
+
+tp_status tp_layernorm_gather(void* stream, tp_dtype dt, int n_slices, int64_t T, int64_t H, const void* X,
+                              int64_t slice_stride, int64_t ldx, const void* gamma, const void* beta, float eps,
+                              void* Y, int64_t ldy, int slice) {
+  TP_TRY(validate_norm(dt, n_slices, T, H, X, slice_stride, ldx, gamma, eps, Y, ldy, slice));
+  if (beta && !aligned16(beta)) return fail(TP_ERR_ALIGN, "beta is not 16-byte aligned");
+  if (T == 0) return ok();
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  tp::NormParams p{};
+  p.X = X;
+  p.slice_stride = slice_stride;
+  p.ldx = ldx;
+  p.gamma = gamma;
+  p.beta = beta;
+  p.layer = 1;
+  p.Y = Y;
+  p.ldy = ldy;
+  p.slice_rows = T / n_slices;
+  p.rows = slice < 0 ? T : p.slice_rows;
+  p.slice = slice;
+  p.H = (int)H;
+  p.inv_h = 1.0f / (float)H;
+  p.eps = eps;
+  if (log_enabled())
+    fprintf(stderr, "[tp] layernorm_gather %s: %d slices of [%lld x %lld] -> Y[%lld x %lld]%s\n", dt_name(dt),
+            n_slices, (long long)p.slice_rows, (long long)H, (long long)T, (long long)H,
+            slice >= 0 ? " (one slice)" : "");
+  KernelTimer kt("layernorm_gather", s);
+  const hipError_t e = tp::launch_rmsnorm_gather(p, dt == TP_BF16, s);
+  kt.stop();
+  TP_TRY(hip_status(e, "layernorm_gather launch"));
+  return ok();
+}
+
+size_t tp_norm_split_workspace_size(const tp_norm_split_desc* d) {
+  size_t need = 0;
+  return validate_norm_split(d, &need) == TP_OK ? need : 0;
+}
+
+tp_status tp_norm_hidden_split(void* stream, const tp_norm_split_desc* d, void* ws, size_t ws_bytes) {
+  size_t need = 0;
+  TP_TRY(validate_norm_split(d, &need));
+  if (d->T == 0) return ok();
+  TP_TRY(check_ws(ws, ws_bytes, need));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  tp::NormSplitParams p{};
+  p.X = d->X;
+  p.ldx = d->ldx;
+  p.gamma = d->gamma;
+  p.beta = d->beta;
+  p.Y = d->Y;
+  p.ldy = d->ldy;
+  p.stats = static_cast<float*>(ws);
+  p.T = d->T;
+  p.Hs = (int)(d->H / d->N);
+  p.N = d->N;
+  p.shard0 = d->shard_begin;
+  p.shards = d->shard_count;
+  p.inv_hs = 1.0f / (float)p.Hs;
+  p.inv_h = 1.0f / (float)d->H;
+  p.eps = d->eps;
+  p.layer = d->kind == TP_NORM_LAYER;
+  if (log_enabled())
+    fprintf(stderr, "[tp] norm_hidden_split %s %s: T=%lld H=%lld N=%d shards [%d,%d)\n", dt_name(d->dt),
+            p.layer ? "layernorm" : "rmsnorm", (long long)d->T, (long long)d->H, d->N, d->shard_begin,
+            d->shard_begin + d->shard_count);
+  const bool bf = d->dt == TP_BF16;
+  {
+    KernelTimer kt("norm_split_stats", s);
+    const hipError_t e = tp::launch_norm_split_stats(p, bf, s);
+    kt.stop();
+    TP_TRY(hip_status(e, "norm_split_stats launch"));
+  }
+  KernelTimer kt("norm_split_apply", s);
+  const hipError_t e = tp::launch_norm_split_apply(p, bf, s);
+  kt.stop();
+  TP_TRY(hip_status(e, "norm_split_apply launch"));
   return ok();
 }
 

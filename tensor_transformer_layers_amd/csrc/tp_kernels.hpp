@@ -118,7 +118,7 @@ struct ReduceParams {
 };
 hipError_t launch_reduce(const ReduceParams& p, bool out_bf16, hipStream_t s);
 
-// RMSNorm of sequence slices into the gathered buffer.  Row `row` of the
+// RMSNorm or LayerNorm of sequence slices into the gathered buffer.  Row `row` of the
 // launch is row t of slice r (r = slice if slice >= 0, else row / slice_rows),
 // read at X + r*slice_stride + t*ldx and written at Y + (r*slice_rows + t)*ldy.
 struct NormParams {
@@ -132,9 +132,33 @@ struct NormParams {
   int64_t slice;       // -1: every slice
   int H;
   float inv_h, eps;
+  const void* beta;    // LayerNorm shift [H] or nullptr
+  int layer;           // 0: RMSNorm, 1: LayerNorm
 };
 int64_t rmsnorm_max_hidden(bool bf16_io);
 hipError_t launch_rmsnorm_gather(const NormParams& p, bool bf16_io, hipStream_t s);
+
+// Norm of an input split along hidden into N slices of Hs = H/N columns
+// (slice i = columns [i Hs, (i+1) Hs) of X and Y).  Stats: for shards
+// [shard0, shard0 + shards) and every row t, the slice's statistic into
+// stats[2 (i T + t) .. +1] (RMSNorm: sum of squares, 0; LayerNorm: mean, sum
+// of squared deviations).  Apply: for the same shards, the fold of all N
+// statistics of the row in shard order, then the slice scaled into Y.
+struct NormSplitParams {
+  const void* X;
+  int64_t ldx;
+  const void* gamma;   // [H]
+  const void* beta;    // [H] or nullptr (LayerNorm only)
+  void* Y;
+  int64_t ldy;
+  float* stats;        // [N x T x 2]
+  int64_t T;
+  int Hs, N, shard0, shards;
+  float inv_hs, inv_h, eps;
+  int layer;
+};
+hipError_t launch_norm_split_stats(const NormSplitParams& p, bool bf16_io, hipStream_t s);
+hipError_t launch_norm_split_apply(const NormSplitParams& p, bool bf16_io, hipStream_t s);
 
 // Causal attention over local heads (head_dim 128), batched over `nshards`
 // problems advancing by sQK / sVt / sO elements.

@@ -37,6 +37,8 @@ TENSORS = {
     "attn": ["X", "Wq", "Wk", "Wv", "Wo"],
     "vocab_ce": ["X", "E"],
     "vocab_embed": ["E"],
+    "norm_split_layer": ["X", "g", "b"],
+    "norm_split_rms": ["X", "g", "b"],
 }
 
 
@@ -94,6 +96,8 @@ def shapes(w: Workload) -> dict:
         return {"X": (T, H), "E": (F, H)}
     if w.kind == "vocab_embed":  # E: the embedding table over the real vocab, [V x H]
         return {"E": (F, H)}
+    if w.kind.startswith("norm_split"):  # the norm's input, gain and shift
+        return {"X": (T, H), "g": (H,), "b": (H,)}
     raise ValueError(w.kind)
 
 
@@ -107,6 +111,10 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
     shp = shapes(w)
     out = {}
     for name, ss in zip(names, kids):
+        if name == "g":  # a norm gain: 1 + N(0, 0.1^2)
+            g = np.float32(1.0) + draw(ss, shp[name], 0.1)
+            out[name] = round_to_dtype(g.astype(np.float32), w.dtype)
+            continue
         if name in ("a", "b"):
             if w.sigma_bias is None:
                 out[name] = None
@@ -146,6 +154,14 @@ def sample_rows(T: int, count: int, seed: int, must=()) -> np.ndarray:
 # rounded to the workload dtype, drawn from its own stream of the seed.
 NORM_EPS = 1e-6
 NORM_GAIN_RECIPE = "1 + N(0, 0.1^2) per feature, rounded to the workload dtype, SeedSequence([seed, 1])"
+
+
+NORM_SHIFT_RECIPE = "N(0, 0.1^2) per feature, rounded to the workload dtype, SeedSequence([seed, 5])"
+
+
+def norm_shift(w: Workload) -> np.ndarray:
+    """The LayerNorm shift [H] of workload w's entry side (recipe above)."""
+    return round_to_dtype(draw(np.random.SeedSequence([w.seed, 5]), (w.H,), 0.1), w.dtype)
 
 
 def norm_gain(w: Workload) -> np.ndarray:

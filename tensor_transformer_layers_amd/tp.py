@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libtp.so")
 TP_OK, TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_DIVISIBILITY, TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_WORKSPACE, TP_ERR_HIP = range(8)
 TP_F32, TP_BF16 = 0, 1
 TP_ACT_NONE, TP_ACT_GELU, TP_ACT_SWIGLU = 0, 1, 2
+TP_NORM_RMS, TP_NORM_LAYER = 0, 1
 
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
@@ -53,6 +54,17 @@ class MlpBwdDesc(ctypes.Structure):
         ("N", _int), ("shard_begin", _int), ("shard_count", _int),
         ("X", _vp), ("A", _vp), ("a", _vp), ("B", _vp), ("dY", _vp),
         ("dX", _vp), ("dA", _vp), ("da", _vp), ("dB", _vp), ("db", _vp),
+        ("n_slices", _int), ("slice", _int),
+    ]
+
+
+class NormSplitDesc(ctypes.Structure):
+    _fields_ = [
+        ("dt", _int), ("kind", _int),
+        ("T", _i64), ("H", _i64),
+        ("N", _int), ("shard_begin", _int), ("shard_count", _int),
+        ("X", _vp), ("ldx", _i64), ("gamma", _vp), ("beta", _vp), ("eps", ctypes.c_float),
+        ("Y", _vp), ("ldy", _i64),
     ]
 
 
@@ -80,6 +92,10 @@ _SIGS = {
     "tp_reduce_partials": (_int, [_vp, _int, _int, _i64, _i64, _vp, _i64, _vp, _vp, _int, _int]),
     "tp_rmsnorm_gather": (_int, [_vp, _int, _int, _i64, _i64, _vp, _i64, _i64, _vp, ctypes.c_float, _vp, _i64,
                                  _int]),
+    "tp_layernorm_gather": (_int, [_vp, _int, _int, _i64, _i64, _vp, _i64, _i64, _vp, _vp, ctypes.c_float, _vp,
+                                   _i64, _int]),
+    "tp_norm_split_workspace_size": (_sz, [ctypes.POINTER(NormSplitDesc)]),
+    "tp_norm_hidden_split": (_int, [_vp, ctypes.POINTER(NormSplitDesc), _vp, _sz]),
     "tp_mlp_workspace_size": (_sz, [ctypes.POINTER(MlpDesc)]),
     "tp_attn_workspace_size": (_sz, [ctypes.POINTER(AttnDesc)]),
     "tp_mlp_partials_offset": (_sz, [ctypes.POINTER(MlpDesc)]),
@@ -158,6 +174,18 @@ def tp_reduce_partials(*args) -> int:
 
 def tp_rmsnorm_gather(*args) -> int:
     return lib().tp_rmsnorm_gather(*args)
+
+
+def tp_layernorm_gather(*args) -> int:
+    return lib().tp_layernorm_gather(*args)
+
+
+def tp_norm_split_workspace_size(desc: NormSplitDesc) -> int:
+    return lib().tp_norm_split_workspace_size(ctypes.byref(desc))
+
+
+def tp_norm_hidden_split(stream, desc: NormSplitDesc, ws, ws_bytes) -> int:
+    return lib().tp_norm_hidden_split(stream, ctypes.byref(desc), ws, ws_bytes)
 
 
 def tp_mlp_forward(stream, desc: MlpDesc, ws, ws_bytes) -> int:
@@ -426,6 +454,77 @@ def _check_mlp(X, A, a, B, b, act, Y=None, rows=None):
     return T, H, F
 
 
+def layernorm_gather(X, gamma, beta, eps, n_slices, out=None, slice=-1, slice_stride=None, stream=None):
+    """LayerNorm of each of the n_slices sequence slices of X into the
+    gathered [T x H] buffer ``out`` (arguments as rmsnorm_gather; beta [H]
+    or None)."""
+    torch = _torch()
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
+    rows, H = X.shape
+    _rows_2d("X", X, H, device=X.device)
+    if slice_stride is not None and n_slices > 1 and slice_stride < rows * X.stride(0):
+        raise ValueError(f"slice_stride {slice_stride} is shorter than one slice ({rows} rows)")
+    T = rows if slice_stride is None else rows * n_slices
+    stride = (T // n_slices) * X.stride(0) if slice_stride is None else slice_stride
+    _expect("gamma", gamma, (H,), X.dtype, X.device)
+    if beta is not None:
+        _expect("beta", beta, (H,), X.dtype, X.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=X.dtype, device=X.device)
+    _rows_2d("out", out, H, dtype=X.dtype, device=X.device)
+    if out.shape[0] != T:
+        raise ValueError(f"out has {out.shape[0]} rows, expected {T}")
+    check(tp_layernorm_gather(_stream(stream), _dt(X), n_slices, T, H, _ptr(X), stride, _ld(X), _ptr(gamma),
+                              _ptr(beta), float(eps), _ptr(out), _ld(out), slice))
+    return out
+
+
+def norm_hidden_split(X, gamma, beta, eps, N, kind=TP_NORM_LAYER, shard_begin=0, shard_count=None, out=None,
+                      ws=None, stream=None):
+    """Norm of X [T x H] split along hidden over N shards (shard i = columns
+    [i H/N, (i+1) H/N)): local statistics, their fold in shard order, local
+    scaling.  Returns (Y, workspace); the workspace holds the N x T x 2 fp32
+    statistics slab (norm_split_stats)."""
+    torch = _torch()
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
+    T, H = X.shape
+    _rows_2d("X", X, H, device=X.device)
+    _expect("gamma", gamma, (H,), X.dtype, X.device)
+    if beta is not None:
+        _expect("beta", beta, (H,), X.dtype, X.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=X.dtype, device=X.device)
+    _rows_2d("out", out, H, dtype=X.dtype, device=X.device)
+    if out.shape[0] != T:
+        raise ValueError(f"out has {out.shape[0]} rows, expected {T}")
+    d = NormSplitDesc()
+    d.dt, d.kind = _dt(X), kind
+    d.T, d.H = T, H
+    d.N, d.shard_begin = N, shard_begin
+    d.shard_count = N if shard_count is None else shard_count
+    d.X, d.ldx, d.gamma, d.beta, d.eps = _ptr(X), _ld(X), _ptr(gamma), _ptr(beta), float(eps)
+    d.Y, d.ldy = _ptr(out), _ld(out)
+    need = tp_norm_split_workspace_size(d)
+    if need == 0:
+        if T == 0:
+            return out, ws
+        raise TPError(TP_ERR_SHAPE, last_error())
+    if ws is None or ws.numel() < need:
+        ws = alloc_workspace(need, X.device)
+    check(tp_norm_hidden_split(_stream(stream), d, _ptr(ws), ws.numel()))
+    return out, ws
+
+
+def norm_split_stats(ws, N, T):
+    """View [N x T x 2] fp32 of the statistics slab of a hidden-split norm
+    workspace (RMSNorm: sum of squares, 0; LayerNorm: mean, sum of squared
+    deviations)."""
+    torch = _torch()
+    return ws[: N * T * 2 * 4].view(torch.float32).view(N, T, 2)
+
+
 def mlp_desc(X, A, a, B, b, N, act, Y=None, shard_begin=0, shard_count=None, n_slices=1, slice=-1, F=None):
     T, H = X.shape
     if F is None:
@@ -489,12 +588,13 @@ def mlp_forward_noalloc(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, n_slices=1, s
 
 
 def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=None, grads=None, ws=None,
-                 need_da=True, need_db=True, stream=None):
+                 need_da=True, need_db=True, n_slices=1, slice=-1, stream=None):
     """Backward of the MLP pair over a shard range; returns (grads, workspace).
     ``grads`` holds dX (bf16 [T x H], filled when the range covers all N
-    shards), dA (fp32, A's shape: [F x H], or the [2F x H] fused blocks for
-    SwiGLU), da (fp32 [F] or None; always None for SwiGLU), dB (fp32
-    [H x F]) and db (fp32 [H] or None); missing entries are allocated."""
+    shards; with n_slices > 1 and slice = r, rank r's reduce-scatter slice,
+    [T/n_slices x H]), dA (fp32, A's shape: [F x H], or the [2F x H] fused
+    blocks for SwiGLU), da (fp32 [F] or None; always None for SwiGLU), dB
+    (fp32 [H x F]) and db (fp32 [H] or None); missing entries are allocated."""
     torch = _torch()
     _same_dtype(X, A=A, a=a, B=B, dY=dY)
     T, H, F = _check_mlp(X, A, a, B, None, act)
@@ -505,8 +605,9 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
     g = dict(grads or {})
     dev = X.device
     f32 = torch.float32
+    dx_rows = T if slice < 0 or n_slices < 1 else T // n_slices
     if "dX" not in g:
-        g["dX"] = torch.empty((T, H), dtype=X.dtype, device=dev) if cnt == N else None
+        g["dX"] = torch.empty((dx_rows, H), dtype=X.dtype, device=dev) if cnt == N else None
     if "dA" not in g:
         g["dA"] = torch.zeros(tuple(A.shape), dtype=f32, device=dev)
     if "da" not in g:
@@ -516,7 +617,7 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
     if "db" not in g:
         g["db"] = torch.zeros((H,), dtype=f32, device=dev) if need_db else None
     if g["dX"] is not None:
-        _expect("dX", g["dX"], (T, H), X.dtype, dev)
+        _expect("dX", g["dX"], (dx_rows, H), X.dtype, dev)
     _expect("dA", g["dA"], tuple(A.shape), f32, dev)
     if g["da"] is not None:
         _expect("da", g["da"], (F,), f32, dev)
@@ -530,6 +631,7 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
     d.N, d.shard_begin, d.shard_count = N, shard_begin, cnt
     d.X, d.A, d.a, d.B, d.dY = _ptr(X), _ptr(A), _ptr(a), _ptr(B), _ptr(dY)
     d.dX, d.dA, d.da, d.dB, d.db = (_ptr(g[k]) for k in ("dX", "dA", "da", "dB", "db"))
+    d.n_slices, d.slice = n_slices, slice
     need = tp_mlp_backward_workspace_size(d)
     if need == 0:
         if T == 0:

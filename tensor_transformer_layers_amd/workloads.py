@@ -60,6 +60,9 @@ def device_inputs(w: Workload, host: dict, device="cuda") -> dict:
         d["E"] = to_device(E, dt, device)
         del E
         d["labels"] = torch.from_numpy(np.ascontiguousarray(host["labels"])).to(device)
+    elif w.kind.startswith("norm_split"):
+        for k in ("X", "g", "b"):
+            d[k] = to_device(host[k], dt, device)
     elif w.kind == "vocab_embed":
         Vp = tp.tp_vocab_padded(w.F, w.N)
         E = np.zeros((Vp, w.H), dtype=np.float32)
@@ -80,6 +83,11 @@ def forward(w: Workload, d: dict, Y=None, ws=None, shard_begin=0, shard_count=No
     """One pass of the sublayer over shards [shard_begin, shard_begin+count).
     For the vocab cross-entropy, Y is the per-token loss; for the embedding,
     the looked-up rows."""
+    if w.kind.startswith("norm_split"):
+        from .inputs import NORM_EPS
+        kind = tp.TP_NORM_LAYER if w.kind == "norm_split_layer" else tp.TP_NORM_RMS
+        return tp.norm_hidden_split(d["X"], d["g"], d["b"], NORM_EPS, w.N, kind=kind, shard_begin=shard_begin,
+                                    shard_count=shard_count, out=Y, ws=ws, stream=stream)
     if w.kind == "vocab_embed":
         return tp.vocab_embed_forward(d["ids"], d["E"], w.F, w.N, shard_begin=shard_begin,
                                       shard_count=shard_count, Y=Y, ws=ws, stream=stream)

@@ -210,6 +210,7 @@ def _bwd(**kw):
     d.T, d.H, d.F, d.N = 256, 512, 2048, 4
     d.shard_begin, d.shard_count = 0, 4
     d.X = d.A = d.a = d.B = d.dY = d.dX = d.dA = d.da = d.dB = d.db = FAKE
+    d.n_slices, d.slice = 1, -1
     for k, v in kw.items():
         setattr(d, k, v)
     return d
@@ -577,3 +578,66 @@ def test_mlp_forward_noalloc_rejects_before_any_hip_call(L):
     assert "static scratch" in tp.last_error()
     d = _mlp(T=0)
     assert tp.tp_mlp_forward_noalloc(None, d) == tp.TP_OK  # empty input: nothing to do
+
+
+def test_layernorm_gather_validation(L):
+    f = tp.tp_layernorm_gather
+    ok = dict(dt=tp.TP_BF16, n=4, T=64, H=512, X=FAKE, ss=16 * 512, ldx=512, g=FAKE, b=FAKE, eps=1e-6, Y=FAKE,
+              ldy=512, sl=-1)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(None, a["dt"], a["n"], a["T"], a["H"], a["X"], a["ss"], a["ldx"], a["g"], a["b"], a["eps"], a["Y"],
+                 a["ldy"], a["sl"])
+    assert call(T=0) == tp.TP_OK
+    assert call(T=66) == tp.TP_ERR_DIVISIBILITY
+    assert call(H=516) == tp.TP_ERR_ALIGN
+    assert call(H=16392, ss=16 * 16392, ldx=16392, ldy=16392) == tp.TP_ERR_SHAPE
+    assert call(eps=-1.0) == tp.TP_ERR_SHAPE
+    assert call(g=None) == tp.TP_ERR_NULL and "gamma" in tp.last_error()
+    assert call(b=FAKE + 4) == tp.TP_ERR_ALIGN and "beta" in tp.last_error()
+    assert call(sl=4) == tp.TP_ERR_SHAPE
+
+
+def _nsplit(**kw):
+    d = tp.NormSplitDesc()
+    d.dt, d.kind = tp.TP_BF16, tp.TP_NORM_LAYER
+    d.T, d.H, d.N, d.shard_begin, d.shard_count = 64, 4096, 8, 0, 8
+    d.X = d.gamma = d.beta = d.Y = FAKE
+    d.ldx = d.ldy = 4096
+    d.eps = 1e-5
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_norm_hidden_split_workspace_and_validation(L):
+    """The statistics slab is N x T x 2 fp32; every bad argument is refused
+    before any HIP call."""
+    assert tp.tp_norm_split_workspace_size(_nsplit()) == 8 * 64 * 2 * 4
+    assert tp.tp_norm_split_workspace_size(_nsplit(T=0)) == 0
+
+    def status(**kw):
+        return tp.tp_norm_hidden_split(None, _nsplit(**kw), FAKE, 1 << 20)
+    assert status(T=0) == tp.TP_OK
+    assert status(H=4100) == tp.TP_ERR_DIVISIBILITY and "not divisible by N=8" in tp.last_error()
+    assert status(H=8 * 12, ldx=96, ldy=96) == tp.TP_ERR_ALIGN and "shard width" in tp.last_error()
+    assert status(kind=7) == tp.TP_ERR_DTYPE
+    assert status(kind=tp.TP_NORM_RMS) == tp.TP_ERR_SHAPE and "beta" in tp.last_error()
+    assert status(shard_begin=6, shard_count=3) == tp.TP_ERR_SHAPE
+    assert status(N=1, shard_count=1, H=8 * 16392, ldx=8 * 16392, ldy=8 * 16392) == tp.TP_ERR_SHAPE
+    assert status(eps=float("nan")) == tp.TP_ERR_SHAPE
+    assert status(gamma=None) == tp.TP_ERR_NULL
+    assert status(beta=FAKE + 2) == tp.TP_ERR_ALIGN
+    assert status(Y=None) == tp.TP_ERR_NULL
+    assert status(ldx=4000) == tp.TP_ERR_SHAPE
+    assert tp.tp_norm_hidden_split(None, _nsplit(), FAKE, 100) == tp.TP_ERR_WORKSPACE
+    assert tp.tp_norm_hidden_split(None, _nsplit(), None, 1 << 20) == tp.TP_ERR_WORKSPACE
+
+
+def test_mlp_backward_slices_are_validated(L):
+    ws = tp.tp_mlp_backward_workspace_size(_bwd())
+    assert tp.tp_mlp_backward_workspace_size(_bwd(n_slices=4, slice=2)) == ws  # the fold's layout needs no space
+    assert tp.tp_mlp_backward(None, _bwd(n_slices=3), FAKE, ws) == tp.TP_ERR_DIVISIBILITY
+    assert tp.tp_mlp_backward(None, _bwd(n_slices=4, slice=4), FAKE, ws) == tp.TP_ERR_SHAPE
+    assert tp.tp_mlp_backward(None, _bwd(n_slices=0), FAKE, ws) == tp.TP_ERR_SHAPE
