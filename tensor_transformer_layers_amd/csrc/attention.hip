@@ -15,10 +15,13 @@
 // contiguous, by the QKV projection) feeds the A operand with one 16-byte
 // LDS read per lane.
 //
-// Workgroup = 8 waves x 32 queries (two waves per SIMD, so one wave's softmax
-// arithmetic overlaps the other's MFMAs), or 4 waves when the grid would not
-// fill the chip.  Key blocks of 128 (K [128 x 128] and V^T [128 x 128],
-// 64 KB) stream through a 2-stage LDS ring with the buffer-load-to-LDS path,
+// Workgroup = 8 waves x 32 queries (two waves per SIMD), or 4 waves when the
+// grid would not fill the chip.  Inside a wave each key block is split in two
+// halves of 64 keys and software-pipelined: the exponentials of one half run
+// between the MFMAs of the next product (S^T of half 1, then O^T of half 0),
+// so the matrix cores keep working through the softmax arithmetic.
+// Key blocks of 128 (K [128 x 128] and V^T [128 x 128], 64 KB) stream
+// through a 2-stage LDS ring with the buffer-load-to-LDS path,
 // one block ahead of use (128-key blocks halve the barriers per key against
 // 64-key blocks in a 4-stage ring of the same size); both are XOR-swizzled at
 // 16-byte granularity so the fragment reads of consecutive rows spread over
@@ -150,88 +153,162 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
 
     const char* ks_ = smem + st * ST_BYTES;
     const char* vs_ = ks_ + K_BYTES;
+    const bool diag = kb * BKEY + BKEY - 1 > qw;  // block reaches past the wave's first query
 
-    // S^T tile: rows = BKEY keys (TT 32-key MFMA tiles), columns = 32 queries
     floatx16 s[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[t][v] = 0.0f;
+    // K fragment of score tile t, k-step ks; V^T fragment of output tile i,
+    // logical key chunk ch
+    auto kfrag = [&](int t, int ks) __attribute__((always_inline)) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8*>(ks_ + t * 32 * 256 + ko + (kswz(lr, 2 * ks + lg) << 4));
+    };
+    auto vfrag = [&](int i, int ch) __attribute__((always_inline)) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8*>(vs_ + i * 32 * VROW + vo + (vswz(lr, ch) << 4));
+    };
+    // keys after the query are masked (only in blocks that straddle the
+    // wave's diagonal); key of tile t, register v: t*32 + 8*(v/4) + 4*lg + v%4
+    auto mask = [&](int half) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kstep = 0; kstep < D / 16; ++kstep)
-#pragma unroll
-      for (int t = 0; t < TT; ++t) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(ks_ + t * 32 * 256 + ko + (kswz(lr, 2 * kstep + lg) << 4));
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kstep], s[t], 0, 0, 0);
-      }
-
-    // mask keys after the query (blocks that straddle this wave's diagonal),
-    // block max of the raw scores; the scale into the log2 domain is positive,
-    // so it is applied after the max, fused into the exponent's argument
-    const bool diag = kb * BKEY + BKEY - 1 > qw;  // block reaches past the wave's first query
-    if (diag) {
-#pragma unroll
-      for (int t = 0; t < TT; ++t)
+      for (int tt = 0; tt < TT / 2; ++tt) {
+        const int t = half * (TT / 2) + tt;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kb * BKEY + t * 32 + ((v >> 2) << 3) + (lg << 2) + (v & 3);
           if (key > q) s[t][v] = -INFINITY;
         }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[t][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2e;
-    // The reference point of the exponentials moves only when the block max
-    // exceeds it by more than kLazy (log2 units): the softmax does not depend
-    // on the point, and weights up to 2^kLazy are exact enough in fp32 and
-    // bf16, so after the first blocks the accumulators are almost never
-    // rescaled.  The first block always moves it (m_run = -inf; key 0 is in
-    // block 0 for every query, so the new point is finite).
+      }
+    };
+    // max of the half's raw scores (the scale into the log2 domain is
+    // positive, so it is applied after the max, fused into the exponent's
+    // argument; the partner lane's half by a lane-half swap), then the lazy
+    // move of the reference point: it moves only when the max exceeds it by
+    // more than kLazy (log2 units) -- the softmax does not depend on the
+    // point, and weights up to 2^kLazy are exact enough in fp32 and bf16, so
+    // after the first keys the accumulators are almost never rescaled.  Key
+    // 0 is in half 0 of block 0 for every query, so the first move gives a
+    // finite point.
     constexpr float kLazy = 8.0f;
-    const float m_new = mx > m_run + kLazy ? mx : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first block, else 1 or < 2^-8
-    m_run = m_new;
-
-    bf16x8 pb[TT][2];
-    float psum = 0.0f;
+    auto new_point = [&](int half) __attribute__((always_inline)) -> float {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < TT; ++t)
+      for (int tt = 0; tt < TT / 2; ++tt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[t][v], p.scale_log2e, -m_new));
-        psum += e;
-        pb[t][v >> 3][v & 7] = to_bf16(e);
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[half * (TT / 2) + tt][v]);
+      const uint32_t mb = __builtin_bit_cast(uint32_t, mx);
+      const auto sw = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
+      mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * p.scale_log2e;
+      const float m_new = mx > m_run + kLazy ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 at the first move, else 1 or < 2^-8
+      m_run = m_new;
+      return alpha;
+    };
+    auto rescale = [&](float alpha) __attribute__((always_inline)) {
+      if (__ballot(alpha != 1.0f)) {  // some running max moved
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
       }
-    l_run = l_run * alpha + psum;
-    if (__ballot(alpha != 1.0f)) {  // some running max moved: rescale the accumulators
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-    }
-
-    // O^T += V^T P^T.  MFMA step c covers score tile t = c/2, accumulator
-    // rows v = 8*(c%2) .. +7: lane half lg holds keys t*32 + 16*(c%2) +
-    // 4*lg + {0..3} and the same + 8.  Two lane-half swaps give half lg the
+    };
+    // Exponentials of a half, packed to bf16 and permuted into the B operand
+    // of its O^T MFMAs.  O^T step c covers score tile t = c/2, accumulator
+    // rows v = 8*(c%2) .. +7, where lane half lg holds keys t*32 + 16*(c%2) +
+    // 4*lg + {0..3} and the same + 8; two lane-half swaps give half lg the
     // keys t*32 + 16*(c%2) + 8*lg + {0..7} instead, so that the A operand is
-    // one 16-byte read of V^T (logical chunk 4t + 2*(c%2) + lg).
+    // one 16-byte read of V^T (logical chunk 4t + 2*(c%2) + lg).  Element e
+    // (of 32) of the half is tile half*2 + e/16, register e%16; a finished
+    // group of 8 is permuted at once.  The empty asm statement pins each
+    // operand where it is made: without it the compiler sinks the chain
+    // into the block of its MFMAs, after the branch that follows.
+    bf16x8 pk[TT][2];
+    bf16x8 pb;
+    auto soft2 = [&](int half, int g, float& psum) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < 2 * TT; ++c) {
-      const int t = c >> 1, half = c & 1;
-      const u32x4 d = __builtin_bit_cast(u32x4, pb[t][half]);
-      const auto s0 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
-      const auto s1 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
-      const bf16x8 pk = __builtin_bit_cast(bf16x8, u32x4{s0[0], s1[0], s0[1], s1[1]});
-      const int ch = 4 * t + 2 * half + lg;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs_ + i * 32 * VROW + vo + (vswz(lr, ch) << 4));
-        o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk, o[i], 0, 0, 0);
+      for (int j = 0; j < 2; ++j) {
+        const int e = 2 * g + j, t = half * (TT / 2) + e / 16, v = e % 16;
+        const float x = __builtin_amdgcn_exp2f(fmaf(s[t][v], p.scale_log2e, -m_run));
+        psum += x;
+        pb[v & 7] = to_bf16(x);
       }
+      if (g % 4 == 3) {
+        const int e = 2 * g + 1, t = half * (TT / 2) + e / 16, hf = (e % 16) >> 3;
+        const u32x4 d = __builtin_bit_cast(u32x4, pb);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+        u32x4 k = u32x4{s0[0], s1[0], s0[1], s1[1]};
+        asm volatile("" : "+v"(k));
+        pk[t][hf] = __builtin_bit_cast(bf16x8, k);
+      }
+    };
+
+    // The block is processed in two halves of 64 keys (score tiles 0-1 and
+    // 2-3), software-pipelined inside the wave so that the matrix cores keep
+    // working through the softmax arithmetic:
+    //   steps  0..15  S^T of half 0
+    //   steps 16..31  S^T of half 1           one MFMA, then two exponentials of half 0
+    //   steps 32..47  O^T += V^T P^T, half 0  one MFMA, then two exponentials of half 1
+    //   steps 48..63  O^T += V^T P^T, half 1
+    // Each half updates the running max (lazily) and sum on its own: the same
+    // online softmax at a 64-key grain.  The LDS operand of step n (a K
+    // fragment for steps < 32, a V^T fragment after) is read kAhead steps
+    // ahead into a ring of registers, which covers the LDS latency (with the
+    // read one step ahead, each MFMA waited for its fragment).
+    constexpr int kAhead = 3;
+    auto frag = [&](int n) __attribute__((always_inline)) -> bf16x8 {
+      if (n < 32) {  // S^T step: tile 2*(n/16) + n%2, k-step (n%16)/2
+        const int g = n % 16;
+        return kfrag(2 * (n / 16) + g % 2, g / 2);
+      }
+      const int m = n - 32, c = 4 * (m / 16) + (m % 16) / 4;  // O^T step c, output tile m%4
+      return vfrag(m % 4, 4 * (c >> 1) + 2 * (c & 1) + lg);
+    };
+    bf16x8 ring[kAhead + 1];
+#pragma unroll
+    for (int n = 0; n < kAhead; ++n) ring[n] = frag(n);
+    auto next = [&](int n) __attribute__((always_inline)) {
+      if (n + kAhead < 64) ring[(n + kAhead) % (kAhead + 1)] = frag(n + kAhead);
+    };
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {  // S^T, half 0: tile g%2, k-step g/2
+      next(g);
+      s[g % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[g % (kAhead + 1)], qf[g / 2], s[g % 2], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (diag) mask(0);
+    const float alpha0 = new_point(0);
+    float psum0 = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {  // S^T, half 1: tile 2 + g%2, k-step g/2
+      const int n = 16 + g;
+      next(n);
+      s[2 + g % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[n % (kAhead + 1)], qf[g / 2], s[2 + g % 2], 0, 0, 0);
+      soft2(0, g, psum0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run = l_run * alpha0 + psum0;
+    rescale(alpha0);
+    if (diag) mask(1);
+    const float alpha1 = new_point(1);
+    float psum1 = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {  // O^T, half 0: step c = g/4 (tile c/2, rows 8 (c%2)), output tile g%4
+      const int n = 32 + g, c = g / 4, i = g % 4;
+      next(n);
+      o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[n % (kAhead + 1)], pk[c >> 1][c & 1], o[i], 0, 0, 0);
+      soft2(1, g, psum1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run = l_run * alpha1 + psum1;
+    rescale(alpha1);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {  // O^T, half 1: step c = 4 + g/4, output tile g%4
+      const int n = 48 + g, c = 4 + g / 4, i = g % 4;
+      next(n);
+      o[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[n % (kAhead + 1)], pk[c >> 1][c & 1], o[i], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   wait_vmcnt<0>();  // no load may still target this workgroup's LDS when it exits
