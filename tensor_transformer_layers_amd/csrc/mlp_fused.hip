@@ -7,17 +7,20 @@
 // post, section 2.3; "张量并行", MLP formula GELU(XA)B), so the shard-local
 // intermediate H_i never has to leave the chip: it lives in registers, 32
 // intermediate features at a time, between the two products.  The partials
-// are the same as those of the separate column and row kernels up to the
-// fp32 summation order inside the products.
+// equal those of the separate column and row kernels up to fp32 rounding
+// (summation order inside the products; the bias enters first here).
 //
 // Layout of the work (gfx950, 4 waves = one per SIMD, 1 workgroup per CU):
 //  * A workgroup owns 128 tokens of one shard; wave w owns tokens 32w..32w+31.
 //    Its X rows stay in VGPRs for the whole kernel (the MFMA's second operand
-//    of the column product), its [32 x H] fp32 partial in AGPRs.
+//    of the column product), its [32 x H] fp32 partial fills the 256 AGPRs.
 //  * The intermediate features are consumed in chunks of 32.  Per chunk, the
 //    column product H^T[32 f x 32 tok] = A_i[f rows] X^T is one chain of
-//    H/16 v_mfma_f32_32x32x16_bf16, the activation runs on its 16
-//    accumulators per lane, and the row product P += H B_i^T[f rows] is
+//    H/16 v_mfma_f32_32x32x16_bf16 that starts from the chunk's bias (the
+//    bias is the chain's initial accumulator, so no vector add is needed)
+//    and accumulates in VGPRs: with every AGPR holding the partial, the
+//    compiler would otherwise park a partial tile in VGPRs around each chain
+//    (48 register moves per chunk).  The row product P += H B_i^T[f rows] is
 //    2*H/32 MFMAs, the activated chunk being the MFMA's first operand.
 //  * The accumulator layout of the column product gives each lane one token
 //    and 16 features; two v_permlane32_swap per 16 features move them into
@@ -26,11 +29,16 @@
 //  * A_i and B_i chunks (32 KB each at H = 512) stream through a two-slot LDS
 //    ring by buffer loads to LDS, XOR-swizzled so that the 16-byte fragment
 //    reads are bank-conflict free; one barrier per chunk.
-//  * Software pipeline: each chunk step issues the column product of chunk c
-//    (with the loads of chunk c's B part and chunk c+1's A part between its
-//    MFMAs), then the row product of chunk c-1, between whose MFMAs the
-//    activation of chunk c runs: a wave hides a few vector instructions
-//    behind each of its own MFMAs.
+//  * Software pipeline.  The activation costs about as many vector cycles as
+//    the chunk's MFMAs take (a wave64 fp32 op issues every ~5 cycles, an exp
+//    or reciprocal every ~16; GELU is 11 ops + 2 of those per value, 16
+//    values per lane per chunk), and a wave's vector instructions run while
+//    its own MFMAs execute, so the activation is spread evenly over all of a
+//    step's MFMAs, one stage of one value per MFMA: each step issues the
+//    column product of chunk c (with the loads of chunk c's B part and chunk
+//    c+1's A part between its MFMAs) carrying the second half of chunk c-1's
+//    activation, then the row product of chunk c-1 carrying the first half
+//    of chunk c's.
 //  * Workgroups are renumbered so that the shards of a token block run on
 //    one XCD: X is read from HBM once per token block (it is the largest
 //    input; each shard's weights are 1 MB and stream chunk by chunk through
@@ -71,10 +79,19 @@ struct FC {
   static constexpr int B_DMA = H / 16 / 4;
   static constexpr int B_OFF = 2 * A_SLOT;
   static constexpr int BIAS_OFF = B_OFF + 2 * B_SLOT;
-  static constexpr int LDS = BIAS_OFF + kBiasMax * 2;
+  static constexpr int LDS = BIAS_OFF + kBiasMax * 4;  // fp32 bias
   static_assert((RPD == 1 || RPD == 2) && (kFC / 4) % RPD == 0, "A chunk rows per wave");
   static_assert(H % 64 == 0 && B_DMA >= 1, "B chunk rows per wave");
 };
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const bf16x2 v = {to_bf16(a), to_bf16(b)};
@@ -136,12 +153,20 @@ __global__ __launch_bounds__(kFThreads, 1) void mlp_fused_kernel(FusedMlpParams 
 
   // the shard's column bias into LDS (zeros without one)
   {
-    char* bl = smem + C::BIAS_OFF;
+    float* bl = reinterpret_cast<float*>(smem + C::BIAS_OFF);
     const bf16* bg = p.bias ? static_cast<const bf16*>(p.bias) + shard * p.sBias : nullptr;
     for (int i = tid; i < Fs / 8; i += kFThreads) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (bg) v = *reinterpret_cast<const u32x4*>(bg + 8 * i);
-      *reinterpret_cast<u32x4*>(bl + 16 * i) = v;
+      floatx4 lo = {0.0f, 0.0f, 0.0f, 0.0f}, hi = lo;
+      if (bg) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(bg + 8 * i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = static_cast<float>(v[e]);
+          hi[e] = static_cast<float>(v[4 + e]);
+        }
+      }
+      *reinterpret_cast<floatx4*>(bl + 8 * i) = lo;
+      *reinterpret_cast<floatx4*>(bl + 8 * i + 4) = hi;
     }
   }
 
@@ -170,88 +195,118 @@ __global__ __launch_bounds__(kFThreads, 1) void mlp_fused_kernel(FusedMlpParams 
   const int b_row = l32 * (kFC * 2);
   const int b_off0 = b_row + (((0 + lh) ^ ((l32 >> 2) & 3)) << 4);
   const int b_off1 = b_row + (((2 + lh) ^ ((l32 >> 2) & 3)) << 4);
-  const char* const bias_lane = smem + C::BIAS_OFF + 8 * lh;
+  const float* const bias_lane = reinterpret_cast<const float*>(smem + C::BIAS_OFF) + 4 * lh;
 
-  // One chunk step is a sequence of NM MFMAs: the column product of chunk c
-  // (k-blocks 0..KB1-1) into acc, then the row product of chunk c-1 (k-block
-  // 0 over the NT output tiles, then k-block 1) from hp, the activated chunk
-  // c-1.  The activation of chunk c runs during the row product and fills hc.
-  constexpr int NM = C::KB1 + 2 * C::NT;
-  constexpr int PD = 2;  // fragment reads run PD MFMAs ahead
-  // fragment of MFMA m; aslot / bslot are the byte offsets of the A and B
-  // ring slots in use
+  // The column product of a chunk accumulates in VGPRs (every AGPR holds
+  // the partial P): its MFMAs are written out with VGPR operands, and the
+  // hazards the compiler would otherwise handle are covered here.  The
+  // first MFMA of the chain takes C = 0 and an early-clobber destination (no
+  // overlap with its sources); each later one accumulates into exactly the
+  // registers it reads as C, which needs no wait states; before any vector
+  // instruction reads the result, col_done issues 21 wait states (an 8-pass
+  // MFMA result needs 11).
+  floatx16 acc, bvec;
+  auto col_mfma = [&](int m, const bf16x8& f) {
+    if (m == 0)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(acc) : "v"(f), "v"(xf[0]), "v"(bvec));
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(f), "v"(xf[m]));
+  };
+  auto col_done = [&]() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(acc)); };
   auto frag = [&](int m, int aslot, int bslot) -> bf16x8 {
     if (m < C::KB1)
       return *reinterpret_cast<const bf16x8*>(smem + aslot + ((m & 4) ? a_hi : a_lo) + 32 * m);
     const int n = (m - C::KB1) % C::NT, k = (m - C::KB1) / C::NT;
     return *reinterpret_cast<const bf16x8*>(smem + bslot + (k ? b_off1 : b_off0) + n * 32 * (kFC * 2));
   };
-  floatx16 acc;
-  u32x4 hp[2], hc[2];  // activated chunk (c-1, c) in the row product's operand layout
-  auto mfma = [&](int m, const bf16x8& f) {
-    if (m < C::KB1) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, xf[m], acc, 0, 0, 0);
-    } else {
-      const int n = (m - C::KB1) % C::NT, k = (m - C::KB1) / C::NT;
-      P[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, hp[k]), f, P[n], 0, 0, 0);
-    }
+  // row-product operands: hp0 / hp1 = features 0-15 / 16-31 of chunk c-1;
+  // hc0 = features 0-15 of chunk c (ready for the next step)
+  u32x4 hp0, hp1, hc0;
+  auto row_mfma = [&](int m, const bf16x8& f) {
+    const int n = (m - C::KB1) % C::NT, k = (m - C::KB1) / C::NT;
+    P[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k ? hp1 : hp0), f, P[n], 0, 0, 0);
   };
-  // Activation of accumulator registers 2e, 2e+1 of chunk c (register v of
-  // lane (l32, lh) holds feature 8(v/4) + 4lh + v%4), packed to bf16.
-  // Lane half 0 holds features {0-3, 8-11} (+16k), half 1 {4-7, 12-15}
-  // (+16k); once a 16-feature block is packed, two swaps give half h
-  // features 8h..8h+7 (+16k), the operand order.
-  uint32_t d[8];
-  // the chunk's bias pairs for this lane, read before the chunk's fragment
-  // reads so that waiting for them never waits for a fragment
-  uint32_t bias2[8];
+  // Activation in four stages per pair of accumulator registers, so that it
+  // spreads over the MFMAs: the first half of chunk c (registers 0-7) during
+  // the row product of chunk c-1, the second half (registers 8-15, kept in
+  // accs) during the column product of chunk c+1.  Register v of lane
+  // (l32, lh) holds feature 8(v/4) + 4lh + v%4; once a 16-feature half is
+  // packed, two swaps give lane half h features 8h..8h+7, the operand order.
+  float accs[8];
+  // the chunk's bias as the column product's initial accumulator: register
+  // v of lane (l32, lh) is feature 8(v/4) + 4lh + v%4
   auto load_bias = [&](int c) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint2 b = *reinterpret_cast<const uint2*>(bias_lane + (c * kFC + 8 * q) * 2);
-      bias2[2 * q] = b.x;
-      bias2[2 * q + 1] = b.y;
+      const floatx4 b = *reinterpret_cast<const floatx4*>(bias_lane + c * kFC + 8 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bvec[4 * q + e] = b[e];
     }
   };
-  auto act_pair = [&](int e, int c) {
-    const int v = 2 * e;
-    const uint32_t b2 = bias2[e];
-    const float z0 = acc[v] + __builtin_bit_cast(float, b2 << 16);
-    const float z1 = acc[v + 1] + __builtin_bit_cast(float, b2 & 0xffff0000u);
-    d[e] = GELU ? pack_bf16(gelu_bf16out(z0), gelu_bf16out(z1)) : pack_bf16(z0, z1);
-    if ((e & 3) == 3) {
-      const int k = e >> 2;
-      const auto s0 = __builtin_amdgcn_permlane32_swap(d[4 * k + 0], d[4 * k + 2], false, false);
-      const auto s1 = __builtin_amdgcn_permlane32_swap(d[4 * k + 1], d[4 * k + 3], false, false);
-      hc[k] = u32x4{s0[0], s1[0], s0[1], s1[1]};
+  // GELU of one register in four stages, the arithmetic of gelu_bf16out
+  float g_t, g_w, g_f, g_e, g_r0;
+  uint32_t d[4];
+  auto finish = [&](int i, float r) {
+    if (i & 1)
+      d[i >> 1] = pack_bf16(g_r0, r);
+    else
+      g_r0 = r;
+  };
+  auto act_stage = [&](int st, int i, float z) {
+    if constexpr (GELU) {
+      if (st == 0) {
+        g_t = __builtin_amdgcn_rcpf(fmaf(kGeluP, fabsf(z), 1.0f));
+        g_w = (z * kGeluNegHalfLog2e) * z;
+      } else if (st == 1) {
+        g_f = fmaf(g_t, fmaf(g_t, fmaf(g_t, fmaf(g_t, kGeluA5, kGeluA4), kGeluA3), kGeluA2), kGeluA1);
+      } else if (st == 2) {
+        g_f = g_t * g_f;
+        g_e = __builtin_amdgcn_exp2f(g_w);
+      } else {
+        finish(i, fmaf(-(fabsf(z) * g_f), g_e, fmaxf(z, 0.0f)));
+      }
+    } else {
+      if (st == 3) finish(i, z);
     }
+  };
+  auto swap_pack = [&]() -> u32x4 {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+    return u32x4{s0[0], s1[0], s0[1], s1[1]};
+  };
+  // stage j (0..31) of the first half (registers 0-7 of acc) or the second
+  // (accs); element j/4, stage j%4
+  auto act_slot = [&](int half, int j) {
+    const int i = j >> 2, st = j & 3;
+    act_stage(st, i, half ? accs[i] : acc[i]);
   };
   constexpr int kLoads = C::A_DMA + C::B_DMA;
   static_assert(2 * kLoads <= C::KB1, "load placement");
-  static_assert(2 * C::NT >= 16, "activation placement: one bf16 pair per two row-product MFMAs");
+  // 32 activation stages per half: SA per column / SB per row MFMA
+  constexpr int SA = 32 / C::KB1, SB = 32 / (2 * C::NT);
+  static_assert(SA >= 1 && SB >= 1 && SA * C::KB1 == 32 && SB * 2 * C::NT == 32, "activation placement");
+  constexpr int NM = C::KB1 + 2 * C::NT;
+  constexpr int PD = 2;  // fragment reads run PD MFMAs ahead
 
-  // chunk 0: column product and activation
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  // chunk 0: column product and the first half of its activation
   wait_vmcnt<0>();
   lds_barrier();
   if (nchunk > 1) issue_a(1, 1);
   issue_b(0, 0);
   load_bias(0);
+  static_for<0, C::KB1>([&](auto mc) { col_mfma(decltype(mc)::value, frag(decltype(mc)::value, 0, 0)); });
+  col_done();
+  static_for<0, 32>([&](auto jc) { act_slot(0, decltype(jc)::value); });
+  hc0 = swap_pack();
 #pragma unroll
-  for (int m = 0; m < C::KB1; ++m) mfma(m, frag(m, 0, 0));
-#pragma unroll
-  for (int e = 0; e < 8; ++e) act_pair(e, 0);
+  for (int v = 0; v < 8; ++v) accs[v] = acc[8 + v];
 
   // chunk c (1 <= c < nchunk): A_c is in A slot c&1, B_{c-1} in B slot
   // (c-1)&1; A_{c+1} and B_c are loaded during the step
   for (int c = 1; c < nchunk; ++c) {
     const int par = c & 1;
     const int aslot = par * C::A_SLOT, bslot = C::B_OFF + (par ^ 1) * C::B_SLOT;
-    hp[0] = hc[0];
-    hp[1] = hc[1];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+    hp0 = hc0;
     wait_vmcnt<0>();
     lds_barrier();
     const bool more = c + 1 < nchunk;
@@ -259,10 +314,13 @@ __global__ __launch_bounds__(kFThreads, 1) void mlp_fused_kernel(FusedMlpParams 
     bf16x8 fr[PD + 1];
 #pragma unroll
     for (int m = 0; m < PD; ++m) fr[m] = frag(m, aslot, bslot);
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
+    static_for<0, NM>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
       if (m + PD < NM) fr[(m + PD) % (PD + 1)] = frag(m + PD, aslot, bslot);
-      mfma(m, fr[m % (PD + 1)]);
+      if (m < C::KB1)
+        col_mfma(m, fr[m % (PD + 1)]);
+      else
+        row_mfma(m, fr[m % (PD + 1)]);
       if ((m & 1) && (m >> 1) < kLoads) {
         const int j = m >> 1;  // load j of chunk c+1's A part, then of chunk c's B part
         if (j < C::A_DMA)
@@ -270,22 +328,34 @@ __global__ __launch_bounds__(kFThreads, 1) void mlp_fused_kernel(FusedMlpParams 
         else
           dma_b(par, j - C::A_DMA, c);
       }
-      // the row product's MFMAs carry the activation of chunk c, one pair
-      // per two MFMAs (the first waits for the column product's last MFMA)
-      if (m >= C::KB1 && ((m - C::KB1) & 1) && ((m - C::KB1) >> 1) < 8) act_pair((m - C::KB1) >> 1, c);
+      // column product of chunk c: the second half of chunk c-1's
+      // activation; row product of chunk c-1: the first half of chunk c's
+      if (m < C::KB1) {
+        static_for<0, SA>([&](auto sc) { act_slot(1, m * SA + decltype(sc)::value); });
+        if (m == C::KB1 - 1) hp1 = swap_pack();
+      } else {
+        const int r = m - C::KB1;
+        if (r == 0) {
+          col_done();
+#pragma unroll
+          for (int v = 0; v < 8; ++v) accs[v] = acc[8 + v];
+        }
+        static_for<0, SB>([&](auto sc) { act_slot(0, r * SB + decltype(sc)::value); });
+        if (m == NM - 1) hc0 = swap_pack();
+      }
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   }
 
-  // last chunk's row product
+  // last chunk: the second half of its activation, then its row product
   {
     const int bslot = C::B_OFF + ((nchunk - 1) & 1) * C::B_SLOT;
-    hp[0] = hc[0];
-    hp[1] = hc[1];
+    hp0 = hc0;
+    static_for<0, 32>([&](auto jc) { act_slot(1, decltype(jc)::value); });
+    hp1 = swap_pack();
     wait_vmcnt<0>();
     lds_barrier();
-#pragma unroll
-    for (int m = C::KB1; m < NM; ++m) mfma(m, frag(m, 0, bslot));
+    static_for<C::KB1, NM>([&](auto mc) { row_mfma(decltype(mc)::value, frag(decltype(mc)::value, 0, bslot)); });
   }
 
   // P_i rows: register v of tile n holds token 8(v/4) + 4lh + v%4, output

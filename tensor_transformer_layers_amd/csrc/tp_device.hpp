@@ -35,23 +35,23 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 // GELU for bf16 outputs: the same exact (erf) form, with erf evaluated by the
 // rational-exponential approximation 7.1.26 of Abramowitz & Stegun, Handbook
 // of Mathematical Functions (absolute error <= 1.5e-7 in erf, far below bf16
-// resolution): erf(x) = 1 - t*(a1 + t*(a2 + t*(a3 + t*(a4 + t*a5)))) e^(-x^2),
-// t = 1 / (1 + p x), x >= 0.  With x = |z|/sqrt 2 and
-// q = z/2 * (1 - erf(x)), which carries the sign of z:
-//   GELU(z) = z - q  (z >= 0),   q  (z < 0),   i.e.  max(z, 0) - |q|,
-// which avoids cancelling 1 + erf near -1 for negative z.  The constants are
-// folded: with s = sqrt(log2 e) and u = x s, e^(-x^2) = 2^(-u^2) and
-// p x = (p/s) u; the coefficients carry the factor 1/2.  One exp2, one
-// reciprocal, no branch.
+// resolution): erfc(x) = t*(a1 + t*(a2 + t*(a3 + t*(a4 + t*a5)))) e^(-x^2),
+// t = 1 / (1 + p x), x >= 0.  With x = |z|/sqrt 2 the tail
+// Phi(-|z|) = erfc(x)/2 = f e^(-z^2/2), f = t (a1/2 + t (a2/2 + ...)), so
+//   GELU(z) = z Phi(z) = max(z, 0) - |z| f e^(-z^2/2)
+// (no cancellation of 1 + erf near -1).  Folded constants: p/sqrt 2, the
+// halved coefficients, and e^(-z^2/2) = 2^(-z^2 log2(e)/2).  One reciprocal,
+// one exp2, eleven other operations, no branch.
+constexpr float kGeluP = (float)(0.3275911 * 0.70710678118654752);
+constexpr float kGeluA1 = (float)(0.5 * 0.254829592), kGeluA2 = (float)(0.5 * -0.284496736),
+                kGeluA3 = (float)(0.5 * 1.421413741), kGeluA4 = (float)(0.5 * -1.453152027),
+                kGeluA5 = (float)(0.5 * 1.061405429);
+constexpr float kGeluNegHalfLog2e = (float)(-0.5 * 1.4426950408889634);
 __device__ __forceinline__ float gelu_bf16out(float z) {
-  const float u = fabsf(z) * (0.70710678118654752f * 1.2011224087864498f);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f / 1.2011224087864498f, u, 1.0f));
-  const float poly =
-      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f), 0.5f * 1.421413741f),
-                       0.5f * -0.284496736f),
-               0.5f * 0.254829592f);
-  const float q = z * poly * __builtin_amdgcn_exp2f(-u * u);
-  return fmaxf(z, 0.0f) - fabsf(q);
+  const float t = __builtin_amdgcn_rcpf(fmaf(kGeluP, fabsf(z), 1.0f));
+  const float f = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, kGeluA5, kGeluA4), kGeluA3), kGeluA2), kGeluA1);
+  const float e = __builtin_amdgcn_exp2f((z * kGeluNegHalfLog2e) * z);
+  return fmaf(-(fabsf(z) * f), e, fmaxf(z, 0.0f));
 }
 
 // Slope of the exact GELU for bf16 outputs:
@@ -62,14 +62,10 @@ __device__ __forceinline__ float gelu_bf16out(float z) {
 // reciprocal give both terms.  Absolute error ~1e-7, far below bf16
 // resolution.
 __device__ __forceinline__ float gelu_grad_bf16out(float z) {
-  const float u = fabsf(z) * (0.70710678118654752f * 1.2011224087864498f);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f / 1.2011224087864498f, u, 1.0f));
-  const float poly =
-      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f), 0.5f * 1.421413741f),
-                       0.5f * -0.284496736f),
-               0.5f * 0.254829592f);
-  const float e = __builtin_amdgcn_exp2f(-u * u);  // e^(-z^2/2)
-  const float tail = poly * e;                     // Phi(-|z|)
+  const float t = __builtin_amdgcn_rcpf(fmaf(kGeluP, fabsf(z), 1.0f));
+  const float f = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, kGeluA5, kGeluA4), kGeluA3), kGeluA2), kGeluA1);
+  const float e = __builtin_amdgcn_exp2f((z * kGeluNegHalfLog2e) * z);  // e^(-z^2/2)
+  const float tail = f * e;                                                // Phi(-|z|)
   const float Phi = z >= 0.0f ? 1.0f - tail : tail;
   return fmaf(z * 0.39894228040143268f, e, Phi);
 }

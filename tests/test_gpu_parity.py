@@ -275,8 +275,13 @@ def test_fused_mlp_vs_oracle(T, H, F, N, act, bias):
 
 def test_fused_mlp_matches_separate_kernels():
     """The fused kernel's partials against the column kernel (GELU epilogue)
-    followed by the row-partial kernel, shard by shard: the same products in
-    the same k order, so they agree to fp32 rounding."""
+    followed by the row-partial kernel, shard by shard.  The products run in
+    the same k order and the activation is the same arithmetic, but the fused
+    kernel adds the bias before the products (as the accumulator's initial
+    value) and the column kernel after, so a pre-activation can differ in its
+    last fp32 bit and, rarely, round to a neighbouring bf16 intermediate: one
+    such unit moves a partial by at most 2^-7 |h| |B|, under 4e-3 of max|P|
+    here.  A wrong operand, index or missing term would be of order 1."""
     T, H, F, N = 640, 512, 4 * 64, 4
     Fs = F // N
     say("fused vs separate kernels")
@@ -292,7 +297,7 @@ def test_fused_mlp_matches_separate_kernels():
         worst = max(worst, d)
         same = same and torch.equal(Pi, Pf[i])
     say(f"  max rel diff {worst:.3e}, bit-identical: {same}")
-    assert worst <= 1e-5
+    assert worst <= 4e-3
 
 
 # ------------------------------------------------------------------ the five workloads at full size
