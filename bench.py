@@ -229,13 +229,30 @@ KERNEL_SYMBOL = {
 }
 
 
-def backward_launch_order(w):
+def stored_preactivation(w):
+    """Whether the backward of workload w can take the forward's stored
+    pre-activation (tp_mlp_desc.Z): the bf16 GELU MLPs."""
+    return w.kind == "mlp_gelu" and w.dtype == "bf16"
+
+
+def backward_mode(w, recompute):
+    """The backward variant bench.py times: "stored" (the forward's
+    pre-activation) unless asked to recompute it or w cannot store it."""
+    return "recompute" if recompute or not stored_preactivation(w) else "stored"
+
+
+def backward_launch_order(w, mode="recompute"):
     """Kernels one backward step (all shards) launches, in order (the
-    sequence of tp_mlp_backward)."""
+    sequence of tp_mlp_backward): with the stored pre-activation, dZ reads it;
+    recomputing, GELU with H <= 2048 runs the recomputation and dZ as one
+    two-pass kernel, every other case a recomputing GEMM first."""
     split = backward_splits(w.T, 2 * w.F if w.kind == "mlp_swiglu" else w.F, w.H) > 1
-    # GELU with H <= 2048 runs the recomputation and dZ as one two-pass kernel
     fused = w.kind == "mlp_gelu" and w.H <= 2048 and w.dtype == "bf16"
-    order = ["bwd_transpose"] * 4 + (["bwd_fused_gemm"] if fused else ["bwd_recompute_gemm", "bwd_dz_gemm"])
+    if mode == "stored":
+        mid = ["bwd_dz_gemm"]
+    else:
+        mid = ["bwd_fused_gemm"] if fused else ["bwd_recompute_gemm", "bwd_dz_gemm"]
+    order = ["bwd_transpose"] * 4 + mid
     order += ["bwd_transpose"] * 2
     order += ["bwd_dx_gemm", "bwd_da_gemm"] + (["bwd_splitk_reduce"] if split else [])
     order += ["bwd_db_gemm"] + (["bwd_splitk_reduce"] if split else [])
@@ -251,7 +268,7 @@ def launch_order(w, sp_entry=False, backward=False):
     GEMMs (the dispatch rule of tp_mlp_forward).  With the sequence-parallel
     entry side, the norm-and-gather kernel comes first."""
     if backward:
-        return backward_launch_order(w)
+        return backward_launch_order(w, backward)
     if w.kind == "vocab_ce":
         return ["vocab_logits_gemm", "vocab_ce_fold", "vocab_ce_combine", "vocab_ce_mean"]
     if w.kind == "vocab_embed":
@@ -288,7 +305,7 @@ def measured_traffic(kernel, workload_name):
 
 def workload_tag(w, sp_entry=False, backward=False):
     return (w.name + ("_sp_entry" if sp_entry else "") + ("_layernorm" if sp_entry == "layer" else "")
-            + ("_backward" if backward else ""))
+            + ("_backward" if backward else "") + ("_recompute" if backward == "recompute" else ""))
 
 
 def write_traffic(w, share, pmc_dir, argv_line, sp_entry=False, backward=False, out_dir=None):
@@ -635,6 +652,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="GELU MLP workloads (2, 5): time the backward of the pair instead (input, weight and "
                          "bias gradients of every shard, then the input-gradient reduction)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="with --backward: recompute the pre-activation X A^T + a in the backward instead of taking "
+                         "the one the forward stored (the GELU bf16 workloads store it; the others always recompute)")
     ap.add_argument("--overlap", type=int, default=0, metavar="K",
                     help="MLP workloads, --share layer: cut the tokens into K row blocks and overlap the reduction "
                          "of block k (on a second stream) with the products of block k+1")
@@ -655,14 +675,16 @@ def main():
     if args.sp_entry:
         args.sp_entry = args.norm  # the entry norm's kind travels with the flag
     sp_flags = (" --sp-entry" + (" --norm layer" if args.sp_entry == "layer" else "")) if args.sp_entry else ""
+    bwd_flags = (" --backward" + (" --recompute" if args.recompute else "")) if args.backward else ""
 
     if args.mfma_from:
         from tensor_transformer_layers_amd import configs
 
         w = configs.workload(args.config)
         argv = (f"--config {args.config} --share {args.share}{sp_flags}"
-                f"{' --backward' if args.backward else ''} --steps 3 --warmup 1 --no-cpu-baseline")
-        print(write_mfma(w, args.share, args.mfma_from, argv, args.sp_entry, args.backward))
+                f"{bwd_flags} --steps 3 --warmup 1 --no-cpu-baseline")
+        print(write_mfma(w, args.share, args.mfma_from, argv, args.sp_entry,
+                         args.backward and backward_mode(w, args.recompute)))
         return
 
     if args.trace_from:
@@ -673,8 +695,9 @@ def main():
             print("bench.py --trace-from needs the --steps of the profiled run (and no --overlap)", file=sys.stderr)
             sys.exit(2)
         argv = (f"--config {args.config} --share {args.share}{sp_flags}"
-                f"{' --backward' if args.backward else ''} --steps {args.steps} --no-cpu-baseline")
-        print(write_trace(w, args.share, args.trace_from, argv, args.steps, args.sp_entry, args.backward))
+                f"{bwd_flags} --steps {args.steps} --no-cpu-baseline")
+        print(write_trace(w, args.share, args.trace_from, argv, args.steps, args.sp_entry,
+                          args.backward and backward_mode(w, args.recompute)))
         return
 
     if args.traffic_from:
@@ -682,8 +705,9 @@ def main():
 
         w = configs.workload(args.config)
         argv = (f"--config {args.config} --share {args.share}{sp_flags}"
-                f"{' --backward' if args.backward else ''} --steps 3 --warmup 1 --no-cpu-baseline --calib-copy")
-        print(write_traffic(w, args.share, args.traffic_from, argv, args.sp_entry, args.backward))
+                f"{bwd_flags} --steps 3 --warmup 1 --no-cpu-baseline --calib-copy")
+        print(write_traffic(w, args.share, args.traffic_from, argv, args.sp_entry,
+                            args.backward and backward_mode(w, args.recompute)))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -723,9 +747,15 @@ def main():
     log(f"workload {w.name}: generating seeded inputs")
     host = inputs.make_inputs(w)
     d = workloads.device_inputs(w, host)
+    bmode = None
+    Zst = None
     if args.backward:
         dY_host = inputs.grad_output(w)
         dY = workloads.to_device(dY_host, d["X"].dtype)
+        bmode = backward_mode(w, args.recompute)
+        if bmode == "stored":  # one training forward before the timed region writes Z
+            Zst = torch.empty((w.T, w.F), dtype=d["X"].dtype, device=d["X"].device)
+            tp.mlp_forward(d["X"], d["A"], d["a"], d["B"], d["b"], w.N, act=workloads.act_of(w), Z=Zst)
     if args.sp_entry:
         # X holds the n_slices sequence slices of the sublayer input; each step
         # normalizes them into Xn, the gathered input of the column GEMM
@@ -742,7 +772,7 @@ def main():
 
         entry_norm()
     if args.backward:
-        grads, ws = workloads.backward(w, d, dY)  # allocates the gradients and the workspace once
+        grads, ws = workloads.backward(w, d, dY, Z=Zst)  # allocates the gradients and the workspace once
         Y = grads["dX"]
     else:
         Y, ws = workloads.forward(w, d)  # allocates Y and the workspace once
@@ -762,7 +792,7 @@ def main():
             workloads.forward_overlap(w, d, args.overlap, stream2, Y=Y, ws=ws, stream=stream)
             return
         if args.backward:
-            workloads.backward(w, d, dY, grads=grads, ws=ws, stream=stream)
+            workloads.backward(w, d, dY, grads=grads, ws=ws, Z=Zst, stream=stream)
             return
         if args.sp_entry:
             entry_norm(stream)
@@ -873,7 +903,7 @@ def main():
     roof["kernel"] = dom
     roof["avg_us"] = round(avg * 1e6, 2)
     roof["algorithmic"] = {"flop": f, "bytes": b}
-    roof["traffic"] = measured_traffic(dom, workload_tag(w, args.sp_entry, args.backward))
+    roof["traffic"] = measured_traffic(dom, workload_tag(w, args.sp_entry, bmode or False))
 
     out = {
         "metric": (METRIC_BWD if args.backward else METRIC_VOCAB if w.kind == "vocab_ce" else
@@ -916,7 +946,12 @@ def main():
             **({"overlap_chunks": args.overlap} if args.overlap else {}),
             **({"pass": "backward", "upstream_gradient": inputs.GRAD_RECIPE,
                 "flop_counted": ("12*T*H*I (dH, dX, fused dA, dB)" if w.kind == "mlp_swiglu" else
-                                 "8*T*H*F (dH, dX, dA, dB)") + "; the recomputed column product is extra and not counted",
+                                 "8*T*H*F (dH, dX, dA, dB)")
+                                + ("; the recomputed column product is extra and not counted"
+                                   if bmode == "recompute" else ""),
+                "preactivation": ("stored by a training forward before the timed region (bf16 Z, read by the dZ "
+                                  "epilogue and the act(Z) transpose)" if bmode == "stored" else
+                                  "recomputed in every step (X A^T + a)"),
                 "split_k": backward_splits(w.T, 2 * w.F if w.kind == "mlp_swiglu" else w.F, w.H)}
                if args.backward else {}),
         },

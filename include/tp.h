@@ -209,6 +209,13 @@ typedef struct {
   const void* b;    /* [H] row bias or NULL (added once, after the sum)         */
   void* Y;          /* [T x H], or [T/n_slices x H] when slice >= 0             */
   int n_slices, slice;
+  void* Z;          /* [T x F] (ld F) or NULL.  When set (bf16, activation GELU or
+                       NONE), the forward also writes the range's pre-activation
+                       Z_i = X A_i^T + a_i (shard i = columns i*F/N..), rounded
+                       to bf16 once, so that tp_mlp_backward can take it instead
+                       of recomputing it (training keeps the activation's input).
+                       The fused narrow-hidden kernel keeps its intermediate on
+                       chip, so asking for Z selects the two-GEMM path there. */
 } tp_mlp_desc;
 
 /* Whole attention sublayer over shards [shard_begin, shard_begin + shard_count).
@@ -295,9 +302,9 @@ tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t 
  * Backward of the MLP pair over shards [shard_begin, shard_begin + shard_count)
  * (bf16, activation GELU or NONE), given the forward's input X, its weights and
  * the gradient dY of its output.  Per shard i, with no exchange:
- *   Z_i  = X A_i^T + a_i            (recomputed: the forward keeps no
- *                                    intermediate -- activation recomputation,
- *                                    2kiu.com blog post, section 5.3)
+ *   Z_i  = X A_i^T + a_i            (recomputed -- activation recomputation,
+ *                                    2kiu.com blog post, section 5.3 -- unless
+ *                                    the descriptor's Z holds the forward's)
  *   dZ_i = (dY B_i) * act'(Z_i)     (dY reaches every shard whole)
  *   dA_i = dZ_i^T X,  da_i = column sums of dZ_i
  *   dB_i = dY^T act(Z_i),           the shard's columns of dB
@@ -310,9 +317,11 @@ tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t 
  * Storage order as in the forward: A [F x H], B [H x F] (out-in); gradients
  * come back in the same layout.  Weight and bias gradients are fp32.
  * bf16: Z_i and dZ_i are rounded to bf16 once (as a bf16 forward would store
- * its linear outputs), act(Z_i) is evaluated from the rounded Z_i (at H <= 2048
- * one two-pass kernel keeps Z_i on chip in fp32 instead).  fp32: everything
- * stays fp32.
+ * its linear outputs), act(Z_i) is evaluated from the rounded Z_i (when it is
+ * recomputed at H <= 2048, one two-pass kernel keeps Z_i on chip in fp32
+ * instead).  fp32: everything stays fp32.  A stored Z (GELU or NONE) gives the
+ * same bits as recomputing it with the GEMM path: the forward's column product
+ * and the recomputation accumulate in the same order.
  * SwiGLU (blog post section 3.2): A holds the N fused blocks [2F/N x H] of the
  * forward (gate rows, then up rows); Z_i = [G_i | U_i], dH_i = dY B_i,
  * dZ_i = [dH_i U_i SiLU'(G_i) | dH_i SiLU(G_i)], dA comes back in the same
@@ -340,6 +349,9 @@ typedef struct {
                        the T/n_slices rows r*T/n_slices ..), the backward of the
                        sequence-parallel all-gather ("张量并行", Megatron-SP
                        section); slice = -1 writes every slice          */
+  const void* Z;   /* [T x F] dt (ld F) or NULL: the forward's pre-activation
+                      (tp_mlp_desc.Z), read for the range's columns instead of
+                      recomputing X A_i^T + a_i; GELU or NONE only            */
 } tp_mlp_bwd_desc;
 
 /* Workspace bytes for tp_mlp_backward (0 when the descriptor is invalid).

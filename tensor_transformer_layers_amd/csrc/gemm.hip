@@ -647,17 +647,25 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
               else
                 for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = v[e];
             } else {
-              bf16x4 o;
+              bf16x4 o, zo;
   #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const float x = v[e] + bias[e];
-                o[e] = to_bf16(MODE == EPI_GELU ? gelu_bf16out(x) : x);
+                o[e] = to_bf16(MODE == EPI_GELU || MODE == EPI_GELU_Z ? gelu_bf16out(x) : x);
+                zo[e] = to_bf16(x);
               }
               bf16* dst = static_cast<bf16*>(outC) + off;
               if (n + 3 < p.N)
                 __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(dst));
               else
                 for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
+              if constexpr (MODE == EPI_GELU_Z) {  // the pre-activation, for the backward
+                bf16* zdst = static_cast<bf16*>(p.C2) + bz * p.sC2 + (int64_t)m * p.ldc2 + n;
+                if (n + 3 < p.N)
+                  __builtin_nontemporal_store(zo, reinterpret_cast<bf16x4*>(zdst));
+                else
+                  for (int e = 0; e < 4 && n + e < p.N; ++e) zdst[e] = zo[e];
+              }
             }
           }
         }
@@ -877,6 +885,7 @@ hipError_t launch_gemm_bf16(const GemmParams& p, Epilogue epi, hipStream_t s) {
   switch (epi) {
     case EPI_STORE: return launch_bf16_epi<EPI_STORE>(p, s);
     case EPI_GELU: return launch_bf16_epi<EPI_GELU>(p, s);
+    case EPI_GELU_Z: return launch_bf16_epi<EPI_GELU_Z>(p, s);
     case EPI_PARTIAL: return launch_bf16_epi<EPI_PARTIAL>(p, s);
     case EPI_SWIGLU: return launch_bf16_epi<EPI_SWIGLU>(p, s);
     case EPI_GELU_BWD: return launch_bf16_epi<EPI_GELU_BWD>(p, s);

@@ -336,6 +336,11 @@ tp_status validate_mlp(const tp_mlp_desc* d, MlpShape* sh) {
     if (!d->Y) return fail(TP_ERR_NULL, "Y is NULL");
     if (!aligned16(d->Y)) return fail(TP_ERR_ALIGN, "Y is not 16-byte aligned");
   }
+  if (d->Z) {
+    if (d->dt != TP_BF16) return fail(TP_ERR_DTYPE, "the stored pre-activation Z is written by the bf16 path only");
+    if (d->act == TP_ACT_SWIGLU) return fail(TP_ERR_SHAPE, "no stored pre-activation Z for SwiGLU");
+    TP_TRY(check_matrix("Z", d->Z, d->T, d->F, d->F, vec));
+  }
   if (d->T > kIntMax) return fail(TP_ERR_SHAPE, "T exceeds 2^31-1");
   sh->Fs = Fs;
   sh->a_rows = a_rows;
@@ -449,7 +454,9 @@ int bwd_splits(int64_t T, int64_t Fc, int64_t H) {
 // GELU with a short contraction (H <= 2048): the recomputed pre-activation
 // and dZ come from one two-pass kernel that keeps the pre-activation on chip
 // (its separate round trip through HBM dominates at narrow hidden sizes).
-bool bwd_fused_gelu(const tp_mlp_bwd_desc* d) { return d->dt == TP_BF16 && d->act == TP_ACT_GELU && d->H <= 2048; }
+bool bwd_fused_gelu(const tp_mlp_bwd_desc* d) {
+  return d->dt == TP_BF16 && d->act == TP_ACT_GELU && d->H <= 2048 && !d->Z;
+}
 
 tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
   if (!d) return fail(TP_ERR_NULL, "descriptor is NULL");
@@ -497,12 +504,16 @@ tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
     if (!d->dX) return fail(TP_ERR_NULL, "dX is NULL");
     if (!aligned16(d->dX)) return fail(TP_ERR_ALIGN, "dX is not 16-byte aligned");
   }
+  if (d->Z) {
+    if (swiglu) return fail(TP_ERR_SHAPE, "no stored pre-activation Z for SwiGLU");
+    TP_TRY(check_matrix("Z", d->Z, d->T, d->F, d->F, vec));
+  }
   if (d->T > kIntMax || d->F > kIntMax) return fail(TP_ERR_SHAPE, "size exceeds 2^31-1");
   const size_t T = (size_t)d->T, H = (size_t)d->H, fc = (size_t)Fc, fz = (size_t)sh->Fz, es = esize(d->dt);
   sh->splits = bwd_splits(d->T, sh->Fz, d->H);
   sh->p_bytes = align256((size_t)d->N * T * H * sizeof(float));
   sh->z_off = sh->p_bytes;
-  sh->dz_off = sh->z_off + align256(T * fz * es);
+  sh->dz_off = sh->z_off + (d->Z ? 0 : align256(T * fz * es));  // no recomputed Z with a stored one
   sh->h_off = sh->dz_off + align256(T * fz * es);
   sh->xt_off = sh->h_off + (swiglu || bwd_fused_gelu(d) ? align256(T * fc * es) : 0);
   sh->dyt_off = sh->xt_off + align256(H * T * es);
@@ -835,7 +846,7 @@ tp_status mlp_rows(hipStream_t s, const tp_mlp_desc* d, const MlpShape& sh, void
   // Narrow hidden sizes: one kernel per shard range computes the column
   // product, the activation and the row partial with the intermediate kept
   // on chip (it never needs to leave the shard).
-  if (d->dt == TP_BF16 && d->act != TP_ACT_SWIGLU && tp::mlp_fused_supported(H, Fs)) {
+  if (d->dt == TP_BF16 && d->act != TP_ACT_SWIGLU && !d->Z && tp::mlp_fused_supported(H, Fs)) {
     tp::FusedMlpParams f{};
     f.X = X;
     f.ldx = H;
@@ -861,19 +872,33 @@ tp_status mlp_rows(hipStream_t s, const tp_mlp_desc* d, const MlpShape& sh, void
     return hip_status(e, "mlp fused launch");
   }
 
+  // The stored pre-activation's rows of this block, the range's columns:
+  // without an activation it is the intermediate itself (written there, read
+  // from there), with GELU a second output of the column GEMM.
+  void* Zr = d->Z ? static_cast<char*>(d->Z) + ((size_t)row0 * d->F + (size_t)i0 * Fs) * es : nullptr;
+  const bool z_is_h = Zr && d->act == TP_ACT_NONE;
+  void* Hc = z_is_h ? Zr : Hs;
+  const int64_t hld = z_is_h ? d->F : sh.h_ld, hstride = z_is_h ? Fs : T * sh.h_ld;
+
   // column GEMM + activation for every shard in range (X shared, one launch)
   tp::GemmParams col = gemm(X, H, 0, static_cast<const char*>(d->A) + (size_t)i0 * sh.a_rows * H * es, H,
-                            sh.a_rows * H, Hs, sh.h_ld, T * sh.h_ld, rows, Fs, H, c);
+                            sh.a_rows * H, Hc, hld, hstride, rows, Fs, H, c);
   if (d->a) {
     col.bias = static_cast<const char*>(d->a) + (size_t)i0 * Fs * es;
     col.sBias = Fs;
   }
   col.upOff = Fs * H;
-  const tp::Epilogue ce = d->act == TP_ACT_SWIGLU ? tp::EPI_SWIGLU : d->act == TP_ACT_GELU ? tp::EPI_GELU : tp::EPI_STORE;
+  tp::Epilogue ce = d->act == TP_ACT_SWIGLU ? tp::EPI_SWIGLU : d->act == TP_ACT_GELU ? tp::EPI_GELU : tp::EPI_STORE;
+  if (Zr && d->act == TP_ACT_GELU) {
+    ce = tp::EPI_GELU_Z;
+    col.C2 = Zr;
+    col.ldc2 = d->F;
+    col.sC2 = Fs;
+  }
   TP_TRY(hip_status(launch("mlp_column_gemm", d->dt, col, ce, s), "mlp column launch"));
 
   // row partial of every shard into its slot of the fp32 slab
-  const tp::GemmParams row = gemm(Hs, sh.h_ld, T * sh.h_ld, static_cast<const char*>(d->B) + (size_t)i0 * Fs * es, d->F,
+  const tp::GemmParams row = gemm(Hc, hld, hstride, static_cast<const char*>(d->B) + (size_t)i0 * Fs * es, d->F,
                                   Fs, P + (size_t)i0 * T * H, H, T * H, rows, H, Fs, c);
   return hip_status(launch("mlp_row_gemm", d->dt, row, tp::EPI_PARTIAL, s), "mlp row launch");
 }
@@ -1112,10 +1137,18 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
     TP_TRY(transpose("bwd_transpose", dZ, sh.zld, dZT, T, T, Fz, false));  // dZT [Fz x T]
     return bwd_tail(s, d, sh, ws, dZ, dZT, XT, dYT, HT, AT, token_gemm, rowsum);
   }
-  // Z = X A_r^T (+ a_r), the range's pre-activation (all shards side by side)
-  tp::GemmParams zg = gemm(d->X, H, 0, A_r, H, 0, Z, sh.zld, 0, T, Fz, H, 1);
-  zg.bias = a_r;
-  TP_TRY(hip_status(launch("bwd_recompute_gemm", dt, zg, tp::EPI_STORE, s), "bwd_recompute_gemm"));
+  // Z = X A_r^T (+ a_r), the range's pre-activation (all shards side by side):
+  // the forward's stored one, or recomputed
+  const void* Zp = Z;
+  int64_t zld = sh.zld;
+  if (d->Z) {
+    Zp = static_cast<const char*>(d->Z) + (size_t)i0 * Fs * es;
+    zld = F;
+  } else {
+    tp::GemmParams zg = gemm(d->X, H, 0, A_r, H, 0, Z, sh.zld, 0, T, Fz, H, 1);
+    zg.bias = a_r;
+    TP_TRY(hip_status(launch("bwd_recompute_gemm", dt, zg, tp::EPI_STORE, s), "bwd_recompute_gemm"));
+  }
   if (swiglu) {
     // per shard: dH = dY B_i; [dG | dU] and H = SiLU(G) U from the stored [G | U]
     tp::GemmParams dg = gemm(d->dY, H, 0, BT, H, Fs * H, dZ, sh.zld, zs, T, Fs, H, c);
@@ -1131,10 +1164,10 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
   } else {
     // dZ = (dY B_r) * act'(Z)
     tp::GemmParams dg = gemm(d->dY, H, 0, BT, H, 0, dZ, sh.zld, 0, T, Fc, H, 1);
-    dg.aux = Z;
-    dg.ldaux = sh.zld;
+    dg.aux = Zp;
+    dg.ldaux = zld;
     TP_TRY(hip_status(launch("bwd_dz_gemm", dt, dg, gelu ? tp::EPI_GELU_BWD : tp::EPI_STORE, s), "bwd_dz_gemm"));
-    TP_TRY(transpose("bwd_transpose", Z, sh.zld, HT, T, T, Fc, gelu));  // HT = act(Z)^T
+    TP_TRY(transpose("bwd_transpose", Zp, zld, HT, T, T, Fc, gelu));  // HT = act(Z)^T
   }
   TP_TRY(transpose("bwd_transpose", dZ, sh.zld, dZT, T, T, Fz, false));  // dZT [Fz x T]
   return bwd_tail(s, d, sh, ws, dZ, dZT, XT, dYT, HT, AT, token_gemm, rowsum);

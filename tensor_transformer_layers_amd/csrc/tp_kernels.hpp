@@ -35,6 +35,7 @@ enum Epilogue : int {
   EPI_CE_STATS = 5,  // no C: per (row, 64-column chunk) cross-entropy statistics of the logits acc
   EPI_SWIGLU_BWD = 6,  // acc = dH; G, U = aux at n, n + upOff: C[n] = dG, C[n + upOff] = dU, C2 = SiLU(G)*U
   EPI_GELU_FUSED = 7,  // two passes: Z = A B^T + bias, then dH = A2 B2^T; C = dH * GELU'(Z), C2 = GELU(Z)
+  EPI_GELU_Z = 8,      // C = GELU(acc + bias), C2 = acc + bias (the pre-activation, kept for the backward); bf16
 };
 
 // EPI_CE_STATS: problem z of the batch is vocab shard ce_shard0 + z, whose
@@ -72,7 +73,7 @@ struct GemmParams {
   int batch;
   int xcd_per_problem;  // nonzero: batch % 8 == 0, each problem runs whole on one XCD
   CeEpilogue ce;        // EPI_CE_STATS only
-  void* C2;             // EPI_SWIGLU_BWD, EPI_GELU_FUSED: second bf16 output (ld ldc2, advancing by sC2)
+  void* C2;             // EPI_SWIGLU_BWD, EPI_GELU_FUSED, EPI_GELU_Z: second bf16 output (ld ldc2, advancing by sC2)
   int64_t ldc2, sC2;
   const void* A2;       // EPI_GELU_FUSED: second pass operands (same ld and batch strides as A, B)
   const void* B2;

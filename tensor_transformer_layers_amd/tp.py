@@ -33,6 +33,7 @@ class MlpDesc(ctypes.Structure):
         ("X", _vp), ("A", _vp), ("a", _vp), ("B", _vp), ("b", _vp),
         ("Y", _vp),
         ("n_slices", _int), ("slice", _int),
+        ("Z", _vp),
     ]
 
 
@@ -55,6 +56,7 @@ class MlpBwdDesc(ctypes.Structure):
         ("X", _vp), ("A", _vp), ("a", _vp), ("B", _vp), ("dY", _vp),
         ("dX", _vp), ("dA", _vp), ("da", _vp), ("dB", _vp), ("db", _vp),
         ("n_slices", _int), ("slice", _int),
+        ("Z", _vp),
     ]
 
 
@@ -525,7 +527,8 @@ def norm_split_stats(ws, N, T):
     return ws[: N * T * 2 * 4].view(torch.float32).view(N, T, 2)
 
 
-def mlp_desc(X, A, a, B, b, N, act, Y=None, shard_begin=0, shard_count=None, n_slices=1, slice=-1, F=None):
+def mlp_desc(X, A, a, B, b, N, act, Y=None, shard_begin=0, shard_count=None, n_slices=1, slice=-1, F=None,
+             Z=None):
     T, H = X.shape
     if F is None:
         F = B.shape[1]
@@ -539,6 +542,7 @@ def mlp_desc(X, A, a, B, b, N, act, Y=None, shard_begin=0, shard_count=None, n_s
     d.X, d.A, d.a, d.B, d.b = _ptr(X), _ptr(A), _ptr(a), _ptr(B), _ptr(b)
     d.Y = _ptr(Y)
     d.n_slices, d.slice = n_slices, slice
+    d.Z = _ptr(Z)
     return d
 
 
@@ -548,9 +552,11 @@ def alloc_workspace(nbytes: int, device):
 
 
 def mlp_forward(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, ws=None, shard_begin=0, shard_count=None,
-                n_slices=1, slice=-1, stream=None):
+                n_slices=1, slice=-1, Z=None, stream=None):
     """Whole MLP sublayer; returns (Y, workspace).  Y is None for partial
-    shard ranges (the partials are in the workspace slab)."""
+    shard ranges (the partials are in the workspace slab).  Z ([T x F], X's
+    dtype, bf16 only) or None: also write the range's pre-activation there,
+    for mlp_backward(..., Z=Z)."""
     torch = _torch()
     _same_dtype(X, A=A, a=a, B=B, b=b, Y=Y)
     T, H, _ = _check_mlp(X, A, a, B, b, act)
@@ -560,7 +566,9 @@ def mlp_forward(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, ws=None, shard_begin=
         Y = torch.empty((rows, H), dtype=X.dtype, device=X.device)
     if Y is not None:
         _expect("Y", Y, (rows, H), X.dtype, X.device)
-    d = mlp_desc(X, A, a, B, b, N, act, Y, shard_begin, cnt, n_slices, slice)
+    if Z is not None:
+        _expect("Z", Z, (T, B.shape[1]), X.dtype, X.device)
+    d = mlp_desc(X, A, a, B, b, N, act, Y, shard_begin, cnt, n_slices, slice, Z=Z)
     need = tp_mlp_workspace_size(d)
     if need == 0:
         raise TPError(TP_ERR_SHAPE, last_error())
@@ -588,13 +596,15 @@ def mlp_forward_noalloc(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, n_slices=1, s
 
 
 def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=None, grads=None, ws=None,
-                 need_da=True, need_db=True, n_slices=1, slice=-1, stream=None):
+                 need_da=True, need_db=True, n_slices=1, slice=-1, Z=None, stream=None):
     """Backward of the MLP pair over a shard range; returns (grads, workspace).
     ``grads`` holds dX (bf16 [T x H], filled when the range covers all N
     shards; with n_slices > 1 and slice = r, rank r's reduce-scatter slice,
     [T/n_slices x H]), dA (fp32, A's shape: [F x H], or the [2F x H] fused
     blocks for SwiGLU), da (fp32 [F] or None; always None for SwiGLU), dB
-    (fp32 [H x F]) and db (fp32 [H] or None); missing entries are allocated."""
+    (fp32 [H x F]) and db (fp32 [H] or None); missing entries are allocated.
+    Z: the forward's stored pre-activation ([T x F], X's dtype; GELU or NONE)
+    to use instead of recomputing it, or None."""
     torch = _torch()
     _same_dtype(X, A=A, a=a, B=B, dY=dY)
     T, H, F = _check_mlp(X, A, a, B, None, act)
@@ -624,6 +634,8 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
     _expect("dB", g["dB"], (H, F), f32, dev)
     if g["db"] is not None:
         _expect("db", g["db"], (H,), f32, dev)
+    if Z is not None:
+        _expect("Z", Z, (T, F), X.dtype, dev)
     d = MlpBwdDesc()
     d.dt = _dt(X)
     d.act = act
@@ -632,6 +644,7 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
     d.X, d.A, d.a, d.B, d.dY = _ptr(X), _ptr(A), _ptr(a), _ptr(B), _ptr(dY)
     d.dX, d.dA, d.da, d.dB, d.db = (_ptr(g[k]) for k in ("dX", "dA", "da", "dB", "db"))
     d.n_slices, d.slice = n_slices, slice
+    d.Z = _ptr(Z)
     need = tp_mlp_backward_workspace_size(d)
     if need == 0:
         if T == 0:

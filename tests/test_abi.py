@@ -84,6 +84,9 @@ def test_mlp_workspace_size_is_host_only(L):
     (dict(n_slices=4, slice=4), tp.TP_ERR_SHAPE, "slice 4"),
     (dict(H=500), tp.TP_ERR_ALIGN, "hidden H=500"),
     (dict(Y=None), tp.TP_ERR_NULL, "Y is NULL"),
+    (dict(Z=FAKE, dt=tp.TP_F32), tp.TP_ERR_DTYPE, "bf16 path only"),
+    (dict(Z=FAKE, act=tp.TP_ACT_SWIGLU, a=None), tp.TP_ERR_SHAPE, "no stored pre-activation Z for SwiGLU"),
+    (dict(Z=FAKE + 8), tp.TP_ERR_ALIGN, "Z is not 16-byte aligned"),
 ])
 def test_mlp_validation(L, kw, status, needle):
     d = _mlp(**kw)
@@ -227,6 +230,10 @@ def test_mlp_backward_workspace_size_is_host_only(L):
     assert extra % (F * H * 4) == 0 and extra // (F * H * 4) in (0, 2, 4, 8, 16)
     one = tp.tp_mlp_backward_workspace_size(_bwd(shard_count=1, shard_begin=3))
     assert one < need
+    # with the forward's pre-activation supplied there is no recomputed Z, and
+    # (no two-pass kernel) no separate act(Z) slab either
+    stored = tp.tp_mlp_backward_workspace_size(_bwd(Z=FAKE))
+    assert stored == need - 2 * T * F * 2
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -241,6 +248,8 @@ def test_mlp_backward_workspace_size_is_host_only(L):
     (dict(dB=FAKE + 4), tp.TP_ERR_ALIGN, "dB is not 16-byte aligned"),
     (dict(da=FAKE + 4), tp.TP_ERR_ALIGN, "da is not 16-byte aligned"),
     (dict(shard_begin=3, shard_count=2), tp.TP_ERR_SHAPE, "shard range"),
+    (dict(Z=FAKE, act=tp.TP_ACT_SWIGLU, a=None, da=None), tp.TP_ERR_SHAPE, "no stored pre-activation Z for SwiGLU"),
+    (dict(Z=FAKE + 4), tp.TP_ERR_ALIGN, "Z is not 16-byte aligned"),
 ])
 def test_mlp_backward_rejects_before_launch(L, kw, status, needle):
     d = _bwd(**kw)

@@ -41,14 +41,23 @@ def test_embedding_bytes_and_cpu_baseline():
 @pytest.mark.parametrize("k", [2, 3, 5])
 def test_backward_kernel_flops_cover_the_counted_work(k):
     """The FLOP of the launched GEMMs minus the recomputed column product
-    equals the counted backward FLOP (fused two-pass kernel or not)."""
+    equals the counted backward FLOP (fused two-pass kernel or not); with the
+    stored pre-activation the launched GEMMs are exactly the counted work."""
     w = configs.workload(k)
-    order = bench.backward_launch_order(w)
+    order = bench.backward_launch_order(w, "recompute")
     assert ("bwd_fused_gemm" in order) == (k == 2)
     total = sum(bench.kernel_work(w, n, w.N, w.T)[0] * order.count(n) for n in dict.fromkeys(order))
     fz = 2 * w.F if w.kind == "mlp_swiglu" else w.F
     recompute = 2.0 * w.T * w.H * fz
     assert abs(total - recompute - bench.backward_flops(w, w.N)) <= 1e-9 * total
+    assert bench.backward_mode(w, False) == ("recompute" if k == 3 else "stored")
+    if bench.backward_mode(w, False) == "stored":
+        order = bench.backward_launch_order(w, "stored")
+        assert "bwd_recompute_gemm" not in order and "bwd_fused_gemm" not in order
+        total = sum(bench.kernel_work(w, n, w.N, w.T)[0] * order.count(n) for n in dict.fromkeys(order))
+        assert abs(total - bench.backward_flops(w, w.N)) <= 1e-9 * total
+        assert bench.workload_tag(w, backward="stored").endswith("_backward")
+        assert bench.workload_tag(w, backward="recompute").endswith("_backward_recompute")
 
 
 def test_fused_path_rule():

@@ -1,0 +1,129 @@
+"""The forward's stored pre-activation (tp_mlp_desc.Z) and the backward that
+takes it (tp_mlp_bwd_desc.Z) instead of recomputing X A^T + a, through the C
+ABI (gfx950 GPU required).
+
+  * Z against the fp64 definition X A^T + a: one bf16 rounding, so
+    max|Z - O| / max|O| <= 1e-2.
+  * Asking for Z leaves the forward's output as it was: bit for bit where
+    both runs take the two-GEMM path, within the bf16 bound of the oracle
+    where the narrow-hidden fused kernel served the run without Z.
+  * The backward with the stored Z against the fp64 oracle (bf16 bound 2e-2,
+    as for the recomputing backward), and bit for bit equal to the
+    recomputing backward where that one also runs the GEMM path (H > 2048, or
+    no activation): the forward's column product and the recomputation
+    accumulate the same products in the same order and round once.
+  * A shard range writes its own columns of Z and no others.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import reference as R
+from oracle import tp_oracle as O
+from tensor_transformer_layers_amd import inputs, tp
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+DEV = "cuda"
+BF16_TOL = 2e-2
+Z_TOL = 1e-2
+KEYS = ("dX", "dA", "da", "dB", "db")
+
+
+def say(msg):
+    print(f"[gpu-test] {msg}", file=sys.stderr, flush=True)
+
+
+def dev(x, dtype=torch.bfloat16):
+    return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(DEV, dtype)
+
+
+def err(y, ref):
+    y = np.asarray(y, dtype=np.float64)
+    return float(np.max(np.abs(y - ref)) / np.max(np.abs(ref)))
+
+
+def _np(t):
+    return t.float().cpu().numpy()
+
+
+def _host(T, H, F, bias, seed):
+    rng = np.random.default_rng(seed)
+    r = lambda shape, s: inputs.round_to_dtype((rng.standard_normal(shape) * s).astype(np.float32), "bf16")
+    return {"X": r((T, H), 1.0), "A": r((F, H), 0.05), "a": r((F,), 0.05) if bias else None,
+            "B": r((H, F), 0.05), "dY": r((T, H), 1.0)}
+
+
+def _zref(h):
+    z = h["X"].astype(np.float64) @ h["A"].astype(np.float64).T
+    return z if h["a"] is None else z + h["a"].astype(np.float64)
+
+
+@pytest.mark.parametrize("T,H,F,N,act,bias", [
+    (264, 136, 4 * 72, 4, tp.TP_ACT_GELU, True),     # narrow: fused forward, two-pass backward otherwise
+    (256, 2304, 4 * 64, 4, tp.TP_ACT_GELU, True),    # GEMM path both ways
+    (128, 2304, 2 * 64, 2, tp.TP_ACT_NONE, False),
+    (2048, 520, 8 * 40, 8, tp.TP_ACT_GELU, True),    # split-K weight gradients
+])
+def test_stored_preactivation(T, H, F, N, act, bias):
+    say(f"stored Z T={T} H={H} F={F} N={N} act={act} bias={bias}")
+    h = _host(T, H, F, bias, seed=7 * T + H + F + N)
+    X, A, a, B, dY = (dev(h[k]) for k in ("X", "A", "a", "B", "dY"))
+    Z = torch.empty((T, F), dtype=torch.bfloat16, device=DEV)
+    Y0, _ = tp.mlp_forward(X, A, a, B, None, N, act=act)
+    Y1, _ = tp.mlp_forward(X, A, a, B, None, N, act=act, Z=Z)
+    torch.cuda.synchronize()
+    e = err(_np(Z), _zref(h))
+    say(f"  Z err={e:.3e}")
+    assert e <= Z_TOL
+    yref = O.mlp_gelu(h["X"], h["A"].T, h["a"], h["B"].T, None) if act == tp.TP_ACT_GELU else \
+        O.linear(O.linear(h["X"], h["A"].T, h["a"]), h["B"].T, None)
+    e0, e1 = err(_np(Y0), yref), err(_np(Y1), yref)
+    say(f"  Y err without Z {e0:.3e}, with Z {e1:.3e}")
+    assert e0 <= BF16_TOL and e1 <= BF16_TOL
+    fused = H in (256, 512) and (F // N) % 32 == 0
+    if not fused:
+        assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
+
+    g0, _ = tp.mlp_backward(X, A, a, B, dY, N, act=act, need_da=bias)
+    g1, _ = tp.mlp_backward(X, A, a, B, dY, N, act=act, need_da=bias, Z=Z)
+    torch.cuda.synchronize()
+    ref = R.mlp_gelu_backward(h["X"], h["A"], h["a"], h["B"], h["dY"],
+                              act="gelu" if act == tp.TP_ACT_GELU else "none")
+    same_path = H > 2048 or act == tp.TP_ACT_NONE
+    for k in KEYS:
+        if k == "da" and not bias:
+            assert g1["da"] is None
+            continue
+        e = err(_np(g1[k]), ref[k])
+        say(f"  {k}: err={e:.3e}")
+        assert e <= BF16_TOL, k
+        if same_path:
+            assert torch.equal(g0[k], g1[k]), f"{k}: stored Z differs from the recomputation"
+
+
+def test_stored_preactivation_shard_range():
+    """Shards [1, 3) of 4 write their columns of Z and leave the rest alone;
+    a backward over the same range with that Z equals the recomputing one."""
+    T, H, F, N = 256, 2304, 4 * 64, 4
+    h = _host(T, H, F, True, seed=11)
+    X, A, a, B, dY = (dev(h[k]) for k in ("X", "A", "a", "B", "dY"))
+    Fs = F // N
+    Zfull = torch.empty((T, F), dtype=torch.bfloat16, device=DEV)
+    tp.mlp_forward(X, A, a, B, None, N, Z=Zfull)
+    Z = torch.full((T, F), float("nan"), dtype=torch.bfloat16, device=DEV)
+    tp.mlp_forward(X, A, a, B, None, N, shard_begin=1, shard_count=2, Z=Z)
+    torch.cuda.synchronize()
+    cols = slice(Fs, 3 * Fs)
+    assert torch.equal(Z[:, cols].view(torch.int16), Zfull[:, cols].view(torch.int16))
+    assert torch.isnan(Z[:, :Fs].float()).all() and torch.isnan(Z[:, 3 * Fs:].float()).all()
+    g0, _ = tp.mlp_backward(X, A, a, B, dY, N, shard_begin=1, shard_count=2)
+    g1, _ = tp.mlp_backward(X, A, a, B, dY, N, shard_begin=1, shard_count=2, Z=Z)
+    torch.cuda.synchronize()
+    for k in ("dA", "da", "dB", "db"):
+        assert torch.equal(g0[k], g1[k]), k
