@@ -107,11 +107,20 @@ def kernel_work(w, name, shards_per_launch, rows_reduced):
     raise KeyError(name)
 
 
-def backward_splits(T, Fc, H):
+def backward_direct(w):
+    """Whether tp_mlp_backward reads every operand as stored (K-outer GEMM
+    operands, column sums for the bias gradients): bf16 with T, H and the
+    shard's Z width multiples of 64 (the 32-bit buffer-range condition holds
+    at every workload here).  Otherwise the operands are transposed first."""
+    zs = 2 * (w.F // w.N) if w.kind == "mlp_swiglu" else w.F // w.N
+    return w.dtype == "bf16" and w.T % 64 == 0 and w.H % 64 == 0 and zs % 64 == 0
+
+
+def backward_splits(T, Fc, H, direct=False):
     """Split-K factor of the backward's token-axis GEMMs (the rule of
     tp_mlp_backward: fill the chip with 256x256 tiles when up to 16 splits
     get there, else with 128x128 tiles at ~2 per CU; K per split >= 512 and a
-    multiple of 8)."""
+    multiple of 8, of 64 on the direct path)."""
     big = ((Fc + 255) // 256) * ((H + 255) // 256)
     if big >= 256:
         return 1
@@ -124,6 +133,8 @@ def backward_splits(T, Fc, H):
         while s < 16 and small * s < 512 and T // (2 * s) >= 512:
             s *= 2
     while s > 1 and T % (8 * s):
+        s //= 2
+    while direct and s > 1 and (T // s) % 64:
         s //= 2
     return s
 
@@ -147,25 +158,34 @@ def backward_kernel_work(w, name, c):
     Fc = w.Fs * c
     swi = w.kind == "mlp_swiglu"
     Fz = 2 * Fc if swi else Fc
-    S = backward_splits(T, Fz, H)
+    direct = backward_direct(w)
+    S = backward_splits(T, Fz, H, direct)
     bias = w.sigma_bias is not None
     if name == "bwd_fused_gemm":  # both passes: the recomputed pre-activation and dH; writes dZ and H
         return 4.0 * T * H * Fc, 2 * (2 * T * H + 2 * Fc * H + 2 * T * Fc) + (2 * Fc if bias else 0)
     if name == "bwd_recompute_gemm":
         return 2.0 * T * H * Fz, 2 * (T * H + Fz * H + T * Fz) + (2 * Fc if bias else 0)
-    if name == "bwd_dz_gemm":  # reads the stored pre-activation beside the accumulators (SwiGLU: also writes H)
-        return 2.0 * T * H * Fc, 2 * (T * H + Fc * H + 2 * T * Fz + (T * Fc if swi else 0))
+    if name == "bwd_dz_gemm":  # reads the pre-activation beside the accumulators; writes act(Z) too (SwiGLU,
+        # and GELU on the direct path)
+        writes_act = swi or (direct and w.kind == "mlp_gelu")
+        return 2.0 * T * H * Fc, 2 * (T * H + Fc * H + 2 * T * Fz + (T * Fc if writes_act else 0))
     if name == "bwd_dx_gemm":
         return 2.0 * T * Fz * H, 2 * (T * Fz + H * Fz) + 4 * c * T * H
     if name == "bwd_da_gemm":
         return 2.0 * T * Fz * H, 2 * (T * Fz + T * H) + 4 * S * Fz * H
     if name == "bwd_db_gemm":
         return 2.0 * T * Fc * H, 2 * (T * Fc + T * H) + 4 * S * Fc * H
-    if name == "bwd_transpose":  # X, dY, A, B, act(Z), dZ: each read once and written once
+    if name == "bwd_transpose":
+        if direct:  # B's range columns, for the two-pass kernel's second operand
+            return 0.0, 2 * 2 * Fc * H
+        # X, dY, A, B, act(Z), dZ: each read once and written once
         return 0.0, 2 * 2 * (2 * T * H + Fz * H + Fc * H + T * Fc + T * Fz) / 6
-    if name == "bwd_bias_rowsum":  # da (when the workload has a column bias) and db (row bias)
-        launches = ([(Fc, T)] if bias and not swi else []) + ([(H, T)] if bias else [])
-        return 0.0, sum(2 * r * t + 4 * r for r, t in launches) / max(1, len(launches))
+    if name in ("bwd_bias_rowsum", "bwd_bias_colsum"):
+        # da (when the workload has a column bias) and db (row bias), each
+        # [T x C] read once and C floats written; a column sum is two launches
+        sums = ([Fc] if bias and not swi else []) + ([H] if bias else [])
+        per = 2 if name == "bwd_bias_colsum" else 1
+        return 0.0, sum(2 * T * cols + 4 * cols for cols in sums) / max(1, per * len(sums))
     if name == "bwd_splitk_reduce":  # dA and dB
         return 0.0, (4 * S * Fz * H + 4 * Fz * H + 4 * S * Fc * H + 4 * Fc * H) / 2
     raise KeyError(name)
@@ -190,7 +210,8 @@ KERNEL_SOURCES = {
     "mlp_column_gemm": "gemm.hip", "mlp_row_gemm": "gemm.hip", "mlp_fused": "mlp_fused.hip", "attn_qk_gemm": "gemm.hip",
     "attn_vt_gemm": "gemm.hip", "attn_out_gemm": "gemm.hip", "attn_core": "attention.hip",
     "reduce_partials": "reduce.hip", "rmsnorm_gather": "norm.hip",
-    "bwd_transpose": "bwd.hip", "bwd_bias_rowsum": "bwd.hip", "bwd_recompute_gemm": "gemm.hip",
+    "bwd_transpose": "bwd.hip", "bwd_bias_rowsum": "bwd.hip", "bwd_bias_colsum": "bwd.hip",
+    "bwd_recompute_gemm": "gemm.hip",
     "bwd_dz_gemm": "gemm.hip", "bwd_dx_gemm": "gemm.hip", "bwd_da_gemm": "gemm.hip", "bwd_db_gemm": "gemm.hip",
     "bwd_splitk_reduce": "reduce.hip", "bwd_fused_gemm": "gemm.hip",
     "vocab_logits_gemm": "gemm.hip", "vocab_ce_fold": "vocab.hip", "vocab_ce_combine": "vocab.hip",
@@ -218,7 +239,8 @@ KERNEL_SYMBOL = {
     "mlp_column_gemm": "gemm_", "mlp_row_gemm": "gemm_", "mlp_fused": "mlp_fused_kernel",
     "attn_qk_gemm": "gemm_", "attn_vt_gemm": "gemm_", "attn_out_gemm": "gemm_",
     "attn_core": "attn_fwd_kernel", "reduce_partials": "reduce_kernel", "rmsnorm_gather": "rmsnorm_gather_kernel",
-    "bwd_transpose": "transpose_kernel", "bwd_bias_rowsum": "rowsum_kernel", "bwd_recompute_gemm": "gemm_",
+    "bwd_transpose": "transpose_kernel", "bwd_bias_rowsum": "rowsum_kernel", "bwd_bias_colsum": "colsum_kernel",
+    "bwd_recompute_gemm": "gemm_",
     "bwd_dz_gemm": "gemm_", "bwd_dx_gemm": "gemm_", "bwd_da_gemm": "gemm_", "bwd_db_gemm": "gemm_",
     "bwd_splitk_reduce": "reduce_kernel", "bwd_fused_gemm": "gemm_",
     "vocab_logits_gemm": "gemm_", "vocab_ce_fold": "ce_fold_kernel", "vocab_ce_combine": "ce_combine_kernel",
@@ -245,19 +267,27 @@ def backward_launch_order(w, mode="recompute"):
     """Kernels one backward step (all shards) launches, in order (the
     sequence of tp_mlp_backward): with the stored pre-activation, dZ reads it;
     recomputing, GELU with H <= 2048 runs the recomputation and dZ as one
-    two-pass kernel, every other case a recomputing GEMM first."""
-    split = backward_splits(w.T, 2 * w.F if w.kind == "mlp_swiglu" else w.F, w.H) > 1
+    two-pass kernel, every other case a recomputing GEMM first.  On the
+    direct path the GEMMs read the operands as stored (only the two-pass
+    kernel needs B transposed) and each bias gradient is a column sum (two
+    launches); otherwise six transposes come first and the bias gradients
+    are row sums."""
+    direct = backward_direct(w)
+    split = backward_splits(w.T, 2 * w.F if w.kind == "mlp_swiglu" else w.F, w.H, direct) > 1
     fused = w.kind == "mlp_gelu" and w.H <= 2048 and w.dtype == "bf16"
     if mode == "stored":
         mid = ["bwd_dz_gemm"]
     else:
         mid = ["bwd_fused_gemm"] if fused else ["bwd_recompute_gemm", "bwd_dz_gemm"]
-    order = ["bwd_transpose"] * 4 + mid
-    order += ["bwd_transpose"] * 2
+    if direct:
+        order = (["bwd_transpose"] if mid == ["bwd_fused_gemm"] else []) + mid
+    else:
+        order = ["bwd_transpose"] * 4 + mid + ["bwd_transpose"] * 2
     order += ["bwd_dx_gemm", "bwd_da_gemm"] + (["bwd_splitk_reduce"] if split else [])
     order += ["bwd_db_gemm"] + (["bwd_splitk_reduce"] if split else [])
     bias = w.sigma_bias is not None
-    order += ["bwd_bias_rowsum"] * ((1 if bias and w.kind == "mlp_gelu" else 0) + (1 if bias else 0))
+    n_bias = (1 if bias and w.kind == "mlp_gelu" else 0) + (1 if bias else 0)
+    order += ["bwd_bias_colsum"] * (2 * n_bias) if direct else ["bwd_bias_rowsum"] * n_bias
     return order + ["reduce_partials"]
 
 
@@ -950,9 +980,11 @@ def main():
                                 + ("; the recomputed column product is extra and not counted"
                                    if bmode == "recompute" else ""),
                 "preactivation": ("stored by a training forward before the timed region (bf16 Z, read by the dZ "
-                                  "epilogue and the act(Z) transpose)" if bmode == "stored" else
-                                  "recomputed in every step (X A^T + a)"),
-                "split_k": backward_splits(w.T, 2 * w.F if w.kind == "mlp_swiglu" else w.F, w.H)}
+                                  "epilogue)" if bmode == "stored" else "recomputed in every step (X A^T + a)"),
+                "operands": ("read as stored (K-outer GEMM operands, column sums for the bias gradients)"
+                             if backward_direct(w) else "transposed first"),
+                "split_k": backward_splits(w.T, 2 * w.F if w.kind == "mlp_swiglu" else w.F, w.H,
+                                           backward_direct(w))}
                if args.backward else {}),
         },
         "pct_of_bf16_mfma_peak": (round(100 * value * 1e12 / PEAK_BF16, 2)

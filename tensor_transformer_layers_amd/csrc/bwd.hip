@@ -1,15 +1,19 @@
-// Layout kernels of the MLP pair's backward: a tiled transpose (optionally
-// applying GELU to a stored pre-activation on the way) and a fixed-order row
-// sum for the bias gradients.
+// Layout and reduction kernels of the MLP pair's backward: a tiled transpose
+// (optionally applying GELU to a stored pre-activation on the way), a
+// fixed-order row sum, and a fixed-order column sum for the bias gradients.
 //
 // The backward's contractions over the token axis (weight gradients
-// dA = X^T dZ and dB = H^T dY) and over the output axis of a weight (dH =
-// dY B, dX = dZ A) need operands that are contiguous along the contraction.
-// The GEMM kernel reads both operands K-contiguous, so each operand that is
-// not is transposed once into the workspace: HBM-bound copies, a few percent
-// of the backward's time at the large workloads.
+// dA = dZ^T X and dB = dY^T H) and over the output axis of a weight (dH =
+// dY B, dX = dZ A) read operands that are not contiguous along the
+// contraction.  The bf16 GEMM reads such operands as stored (K-outer, through
+// the transposing LDS read); the fp32 path, and shapes the K-outer GEMM does
+// not take, transpose them once into the workspace instead: HBM-bound copies.
+// The bias gradients are then row sums of the transposed dZ and dY, or
+// column sums of the untransposed ones.
 //
-// Both kernels are deterministic (no atomics, fixed summation order).
+// All kernels are deterministic (no atomics, fixed summation order).
+#include <algorithm>
+
 #include "tp_device.hpp"
 #include "tp_kernels.hpp"
 
@@ -93,7 +97,113 @@ __global__ __launch_bounds__(kThreads) void rowsum_kernel(RowSumParams p) {
   if (lane == 0) p.out[r] = acc;
 }
 
+// Column sums: a workgroup sums a strip of 16*VE columns (VE elements per 16
+// bytes) over one chunk of rows.  Lane l owns columns VE*(l % 16) .. +VE-1 of
+// the strip; wave w takes rows 4w + l/16 + 16j of the chunk (each load
+// instruction covers four 256-byte row segments), eight rows in flight per
+// lane.  Lanes l, l^16, l^32, l^48 then fold by an xor butterfly and the four
+// waves' sums add in wave order through LDS; the chunks' partials are folded
+// by a second launch of the same kernel over the fp32 partial matrix.  Every
+// order is fixed, so the sums are bit-identical run to run.
+constexpr int kColsumTargetGroups = 1024;  // ~4 per CU: enough loads in flight to stream from HBM
+constexpr int kColsumMaxChunks = 128;      // bounds the fold's depth
+constexpr int kColsumMinRows = 128;        // one full unrolled trip per wave
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void colsum_kernel(const E* in, int64_t ld, int64_t R, int64_t C,
+                                                          int64_t rows_per_chunk, int strips, float* dst) {
+  constexpr int VE = 16 / sizeof(E);
+  constexpr int SW = 16 * VE;  // columns per strip
+  constexpr int U = 8;         // rows in flight per lane
+  typedef E ev __attribute__((ext_vector_type(VE)));
+  __shared__ __attribute__((aligned(16))) float red[kThreads / kWave][SW];
+  const int strip = (int)blockIdx.x % strips, chunk = (int)blockIdx.x / strips;
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int64_t c = (int64_t)strip * SW + (lane & 15) * VE;
+  const int64_t r0 = (int64_t)chunk * rows_per_chunk;
+  const int64_t r1 = min(R, r0 + rows_per_chunk);
+  float acc[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = 0.0f;
+  if (c < C) {
+    const E* const col = in + c;
+    int64_t r = r0 + 4 * w + (lane >> 4);
+    for (; r + 16 * (U - 1) < r1; r += 16 * U) {
+      ev v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const ev*>(col + (r + 16 * u) * ld);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[e] += static_cast<float>(v[u][e]);
+    }
+    for (; r < r1; r += 16) {
+      const ev v = *reinterpret_cast<const ev*>(col + r * ld);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[e] += static_cast<float>(v[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < VE; ++e) {
+    acc[e] += __shfl_xor(acc[e], 16);
+    acc[e] += __shfl_xor(acc[e], 32);
+  }
+  if (lane < 16)
+#pragma unroll
+    for (int e = 0; e < VE; ++e) red[w][(lane & 15) * VE + e] = acc[e];
+  __syncthreads();
+  if (w == 0 && lane < 16 && c < C) {
+    float* const out = dst + (int64_t)chunk * C + c;
+#pragma unroll
+    for (int e0 = 0; e0 < VE; e0 += 4) {
+      floatx4 s;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = (lane & 15) * VE + e0 + e;
+        s[e] = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
+      }
+      *reinterpret_cast<floatx4*>(out + e0) = s;
+    }
+  }
+}
+
+// Rows per chunk of the first column-sum pass over [R x C]: about
+// kColsumTargetGroups workgroups, at most kColsumMaxChunks chunks of at least
+// kColsumMinRows rows, a multiple of 16 rows.
+int64_t colsum_rows_per_chunk(int64_t R, int64_t C) {
+  const int64_t strips = (C + 127) / 128;
+  int64_t chunks = (kColsumTargetGroups + strips - 1) / strips;
+  chunks = std::min<int64_t>(chunks, kColsumMaxChunks);
+  chunks = std::min<int64_t>(chunks, (R + kColsumMinRows - 1) / kColsumMinRows);
+  chunks = std::max<int64_t>(chunks, 1);
+  const int64_t rpc = (R + chunks - 1) / chunks;
+  return (rpc + 15) / 16 * 16;
+}
+
+int64_t colsum_chunk_count(int64_t R, int64_t C) {
+  const int64_t rpc = colsum_rows_per_chunk(R, C);
+  return (R + rpc - 1) / rpc;
+}
+
 }  // namespace
+
+size_t colsum_part_floats(int64_t R, int64_t C) {
+  return R > 0 && C > 0 ? (size_t)colsum_chunk_count(R, C) * (size_t)C : 0;
+}
+
+hipError_t launch_colsum(const ColSumParams& p, hipStream_t s) {
+  if (p.R <= 0 || p.C <= 0) return hipSuccess;
+  if (p.C % 8) return hipErrorInvalidValue;
+  const int64_t rpc = colsum_rows_per_chunk(p.R, p.C), chunks = colsum_chunk_count(p.R, p.C);
+  const int64_t strips1 = (p.C + 127) / 128, strips2 = (p.C + 63) / 64;
+  if (strips1 * chunks > 0x7fffffff || strips2 > 0x7fffffff) return hipErrorInvalidValue;
+  launch_kernel(colsum_kernel<bf16>, dim3((unsigned)(strips1 * chunks)), dim3(kThreads), 0, s,
+                static_cast<const bf16*>(p.in), p.ld, p.R, p.C, rpc, (int)strips1, p.part);
+  // fold the chunks' partials (fp32 [chunks x C]) in chunk order, one chunk of all rows
+  launch_kernel(colsum_kernel<float>, dim3((unsigned)strips2), dim3(kThreads), 0, s,
+                static_cast<const float*>(p.part), p.C, chunks, p.C, chunks, (int)strips2, p.out);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose(const TransposeParams& p, bool gelu, bool f32, hipStream_t s) {
   const int64_t tilesR = (p.R + kTile - 1) / kTile, tilesC = (p.C + kTile - 1) / kTile;

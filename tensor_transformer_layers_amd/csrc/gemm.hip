@@ -56,9 +56,12 @@ constexpr int kThreads = 256;
 // Swizzle shift of the LDS layout (16 consecutive rows hit 16 bank groups).
 constexpr int kGemmSwizzleShift = 1;
 
-template <int BM_, int BN_, int BK_, int S_, int SH_, int EPI_>
+// AKO_ / BKO_: the A (B) operand is stored K-outer, [K x M] ([K x N]) with
+// the M (N) index contiguous, instead of K-contiguous rows.
+template <int BM_, int BN_, int BK_, int S_, int SH_, int EPI_, bool AKO_ = false, bool BKO_ = false>
 struct G {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, SH = SH_, EPI = EPI_;
+  static constexpr bool AKO = AKO_, BKO = BKO_;
   static constexpr int CPR = BK / 8;         // 16-byte chunks per tile row
   static constexpr int RPI = 64 / CPR;       // tile rows one wave load instruction fills
   static constexpr int IA = BM / (4 * RPI);  // load instructions per wave per stage, A tile
@@ -76,7 +79,19 @@ struct G {
   static_assert(S >= 2 && (S - 2) * GROUP < 64, "vmcnt range");
   static_assert((32 >> SH) % CPR == 0, "swizzle must repeat every 32 rows");
   static_assert(EPI != EPI_SWIGLU || (TN % 2 == 0 && (BN / 4) % 32 == 0), "SwiGLU halves");
+  static_assert(!(AKO || BKO) || (BK == 64 && (BM == 128 || BM == 256) && (BN == 128 || BN == 256) &&
+                                  EPI != EPI_SWIGLU && EPI != EPI_GELU_FUSED), "K-outer operands");
 };
+
+// K-outer operand tiles in LDS: k row r of a tile (BMN columns, 2*BMN bytes)
+// at r * 2*BMN; its 64-byte blocks are XOR-ed with (r & 3) ^ 2*bit3(r) and
+// its 32-byte halves with bit3(r), so that the transposing fragment reads
+// (ds_read_b64_tr_b16: 16 lanes read 4 k rows x 16 columns) spread over the
+// banks.  As a mask on the 16-byte chunk index of the row (an involution):
+__device__ __forceinline__ int ko_chunk_mask(int r) {
+  const int b3 = (r >> 3) & 1;
+  return ((((r & 3) ^ (b3 << 1)) << 2) | (b3 << 1));
+}
 
 template <class C>
 __device__ __forceinline__ int swz(int r) {
@@ -92,7 +107,22 @@ constexpr int kWavesPerEu = C::EPI == EPI_GELU_FUSED ? 2 : 1;
 template <class C>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<C>)))
 void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  // The operand stages.  With a K-outer operand, one LDS array per stage: the
+  // compiler inserts a wait on every outstanding LDS-bound load before a
+  // transposing LDS read unless it can tell the two apart, and separate arrays
+  // let it see that the fragment reads of one stage never touch the stage the
+  // in-flight loads fill.  Otherwise one array (every stage offset then folds
+  // into the per-lane fragment offsets).
+  static_assert(C::S == 2 && C::LDS_BYTES == 2 * C::STAGE_BYTES, "two stages");
+  constexpr bool kStageArrays = C::AKO || C::BKO;
+  __shared__ __attribute__((aligned(1024))) char smem0[kStageArrays ? C::STAGE_BYTES : C::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem1[kStageArrays ? C::STAGE_BYTES : 1];  // unused otherwise
+  auto stage = [&](int st) __attribute__((always_inline)) -> char* {
+    if constexpr (kStageArrays)
+      return st ? smem1 : smem0;
+    else
+      return smem0 + st * C::STAGE_BYTES;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -165,10 +195,14 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
   const int n0 = tn * C::OUT_N;
 
   // buffer resources: each covers the tile's valid rows, so rows past M / N
-  // read as zero
-  const bf16* const Ab = static_cast<const bf16*>(p.A) + bz * p.sA + (int64_t)m0 * p.lda;
+  // read as zero.  A K-outer operand's resource ends after the tile's last
+  // valid column of k row K-1: columns past M (N) of earlier k rows read
+  // whatever lies there inside the matrix, which reaches only accumulator
+  // rows (columns) the epilogue never stores.
+  const bf16* const Ab = static_cast<const bf16*>(p.A) + bz * p.sA + (C::AKO ? (int64_t)m0 : (int64_t)m0 * p.lda);
   const uint32_t a_rows = (uint32_t)min(C::BM, p.M - m0);
-  __amdgpu_buffer_rsrc_t rA = make_rsrc(Ab, a_rows * (uint32_t)p.lda * 2u);
+  __amdgpu_buffer_rsrc_t rA =
+      make_rsrc(Ab, C::AKO ? (uint32_t)((int64_t)(p.K - 1) * p.lda * 2 + a_rows * 2) : a_rows * (uint32_t)p.lda * 2u);
   const bf16* const Bb = static_cast<const bf16*>(p.B) + bz * p.sB + (int64_t)n0 * p.ldb;
   __amdgpu_buffer_rsrc_t rB;
   int b_row0;  // first B-tile row this wave loads, relative to its buffer
@@ -177,6 +211,10 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
     const bool up = w >= 2;  // waves 0,1 load the gate half, waves 2,3 the up half
     rB = make_rsrc(up ? Bb + p.upOff : Bb, rows * (uint32_t)p.ldb * 2u);
     b_row0 = w * C::IB * C::RPI - (up ? C::BN / 2 : 0);
+  } else if constexpr (C::BKO) {
+    const int64_t cols = min(C::BN, p.N - n0);
+    rB = make_rsrc(static_cast<const bf16*>(p.B) + bz * p.sB + n0, (uint32_t)((int64_t)(p.K - 1) * p.ldb * 2 + cols * 2));
+    b_row0 = 0;
   } else {
     const uint32_t rows = (uint32_t)min(C::BN, p.N - n0);
     rB = make_rsrc(Bb, rows * (uint32_t)p.ldb * 2u);
@@ -189,21 +227,37 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
   int chA[C::IA], chB[C::IB];
 #pragma unroll
   for (int j = 0; j < C::IA; ++j) {
-    const int r = (w * C::IA + j) * C::RPI + lrow;  // tile row
-    chA[j] = lchunk ^ swz<C>(r);                     // logical chunk this lane fetches
-    voA[j] = (uint32_t)r * (uint32_t)p.lda * 2u + (uint32_t)chA[j] * 16u;
+    if constexpr (C::AKO) {  // instruction fills 1024 / (2*BM) k rows of 2*BM bytes
+      constexpr int cpr = C::BM * 2 / 16;
+      const int r = (w * C::IA + j) * (64 / cpr) + lane / cpr;
+      chA[j] = 0;
+      voA[j] = (uint32_t)r * (uint32_t)p.lda * 2u + (uint32_t)((lane % cpr) ^ ko_chunk_mask(r)) * 16u;
+    } else {
+      const int r = (w * C::IA + j) * C::RPI + lrow;  // tile row
+      chA[j] = lchunk ^ swz<C>(r);                     // logical chunk this lane fetches
+      voA[j] = (uint32_t)r * (uint32_t)p.lda * 2u + (uint32_t)chA[j] * 16u;
+    }
   }
 #pragma unroll
   for (int j = 0; j < C::IB; ++j) {
-    const int r = (w * C::IB + j) * C::RPI + lrow;
-    chB[j] = lchunk ^ swz<C>(r);
-    voB[j] = (uint32_t)(b_row0 + j * C::RPI + lrow) * (uint32_t)p.ldb * 2u + (uint32_t)chB[j] * 16u;
+    if constexpr (C::BKO) {
+      constexpr int cpr = C::BN * 2 / 16;
+      const int r = (w * C::IB + j) * (64 / cpr) + lane / cpr;
+      chB[j] = 0;
+      voB[j] = (uint32_t)r * (uint32_t)p.ldb * 2u + (uint32_t)((lane % cpr) ^ ko_chunk_mask(r)) * 16u;
+    } else {
+      const int r = (w * C::IB + j) * C::RPI + lrow;
+      chB[j] = lchunk ^ swz<C>(r);
+      voB[j] = (uint32_t)(b_row0 + j * C::RPI + lrow) * (uint32_t)p.ldb * 2u + (uint32_t)chB[j] * 16u;
+    }
   }
+  // byte offset of k-tile start k0 for each operand (K-outer: k0 rows)
+  const uint32_t kstepA = C::AKO ? (uint32_t)p.lda * 2u : 2u, kstepB = C::BKO ? (uint32_t)p.ldb * 2u : 2u;
 
   const int K = p.K;
   const int nk = (K + C::BK - 1) / C::BK;  // k-tiles
   const int nfull = K / C::BK;             // k-tiles with no chunk past K
-  const bool has_tail = nk > nfull;
+  const bool has_tail = !(C::AKO || C::BKO) && nk > nfull;  // K-outer operands: K % BK == 0 (host-checked)
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
@@ -220,16 +274,16 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
   const __amdgpu_buffer_rsrc_t rZ = make_rsrc(Ab, 0u);
   auto issue = [&](auto stg, int t) {
     constexpr int STG = decltype(stg)::value;
-    char* sa = smem + STG * C::STAGE_BYTES + w * C::IA * 1024;
-    char* sb = smem + STG * C::STAGE_BYTES + C::A_BYTES + w * C::IB * 1024;
+    char* sa = stage(STG) + w * C::IA * 1024;
+    char* sb = stage(STG) + C::A_BYTES + w * C::IB * 1024;
     const bool live = t < nk;
     const __amdgpu_buffer_rsrc_t ra = live ? rA : rZ;
     const __amdgpu_buffer_rsrc_t rb = live ? rB : rZ;
-    const uint32_t so = live ? (uint32_t)k_begin(t) * 2u : 0u;
+    const uint32_t soA = live ? (uint32_t)k_begin(t) * kstepA : 0u, soB = live ? (uint32_t)k_begin(t) * kstepB : 0u;
 #pragma unroll
-    for (int j = 0; j < C::IA; ++j) dma16(ra, sa + j * 1024, voA[j], so);
+    for (int j = 0; j < C::IA; ++j) dma16(ra, sa + j * 1024, voA[j], soA);
 #pragma unroll
-    for (int j = 0; j < C::IB; ++j) dma16(rb, sb + j * 1024, voB[j], so);
+    for (int j = 0; j < C::IB; ++j) dma16(rb, sb + j * 1024, voB[j], soB);
   };
   // The partial tile (tile 0 of stage 0): chunks past K read as zero through
   // the range check, and are also cleared once the loads have landed.
@@ -237,20 +291,20 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
     const int k0 = nfull * C::BK;
 #pragma unroll
     for (int j = 0; j < C::IA; ++j)
-      dma16(rA, smem + (w * C::IA + j) * 1024, k0 + 8 * chA[j] < K ? voA[j] : kOob, (uint32_t)k0 * 2u);
+      dma16(rA, smem0 + (w * C::IA + j) * 1024, k0 + 8 * chA[j] < K ? voA[j] : kOob, (uint32_t)k0 * 2u);
 #pragma unroll
     for (int j = 0; j < C::IB; ++j)
-      dma16(rB, smem + C::A_BYTES + (w * C::IB + j) * 1024, k0 + 8 * chB[j] < K ? voB[j] : kOob, (uint32_t)k0 * 2u);
+      dma16(rB, smem0 + C::A_BYTES + (w * C::IB + j) * 1024, k0 + 8 * chB[j] < K ? voB[j] : kOob, (uint32_t)k0 * 2u);
   };
   auto clear_partial = [&]() {
     const int k0 = nfull * C::BK;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < C::IA; ++j)
-      if (k0 + 8 * chA[j] >= K) *reinterpret_cast<u32x4*>(smem + (w * C::IA + j) * 1024 + lane * 16) = z;
+      if (k0 + 8 * chA[j] >= K) *reinterpret_cast<u32x4*>(smem0 + (w * C::IA + j) * 1024 + lane * 16) = z;
 #pragma unroll
     for (int j = 0; j < C::IB; ++j)
-      if (k0 + 8 * chB[j] >= K) *reinterpret_cast<u32x4*>(smem + C::A_BYTES + (w * C::IB + j) * 1024 + lane * 16) = z;
+      if (k0 + 8 * chB[j] >= K) *reinterpret_cast<u32x4*>(smem0 + C::A_BYTES + (w * C::IB + j) * 1024 + lane * 16) = z;
   };
 
   // Fragment addressing.  The swizzle of a fragment row depends on the lane
@@ -258,12 +312,13 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
   // subtile itself is a compile-time immediate.
   const int fsw = swz<C>(l32);
   const int b_wave_row = C::EPI == EPI_SWIGLU ? wn * (C::BN / 4) : wn * C::WN;
+  // relative to the stage's array (one array: to smem0, stage 1 at + STAGE_BYTES)
   int foA[2][C::KK], foB[2][C::KK];
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
-      const int f = l32 * (C::BK * 2) + (((2 * kk + lh) ^ fsw) << 4) + st * C::STAGE_BYTES;
+      const int f = l32 * (C::BK * 2) + (((2 * kk + lh) ^ fsw) << 4) + (kStageArrays ? 0 : st * C::STAGE_BYTES);
       foA[st][kk] = f + wm * C::WM * (C::BK * 2);
       foB[st][kk] = f + C::A_BYTES + b_wave_row * (C::BK * 2);
     }
@@ -272,6 +327,47 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
       return jn < C::TN / 2 ? jn * 32 : C::BN / 2 + (jn - C::TN / 2) * 32;
     else
       return jn * 32;
+  };
+  // K-outer fragments: two ds_read_b64_tr_b16, each giving a lane 4
+  // consecutive k of its row.  In each 16-lane group (G = lane / 16) lane
+  // 4j + q addresses k row 16kk + 8*lh + 4r + j (r = 0, 1: the read) at
+  // columns 16*(G & 1) + 4q .. +3 of the 32-column subtile; lane i of the
+  // group then holds column 16*(G & 1) + i, k = 16kk + 8*lh + 4r .. +3.  For
+  // those rows (r & 3) = j and bit3(r) = lh, so the swizzle is a lane
+  // constant: the per-subtile offsets below hold everything but the
+  // (stage, k-step, read) part.
+  const int ko_j = (lane & 15) >> 2, ko_q = lane & 3, ko_g1 = (lane >> 4) & 1;
+  const int ko_s1 = ko_j ^ (lh << 1);
+  int koA[C::AKO ? C::TM : 1], koB[C::BKO ? C::TN : 1];
+  if constexpr (C::AKO) {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+      koA[i] = (8 * lh + ko_j) * (C::BM * 2) + ((((wm * C::WM) / 32 + i) ^ ko_s1) << 6) + ((ko_g1 ^ lh) << 5) + 8 * ko_q;
+  }
+  if constexpr (C::BKO) {
+#pragma unroll
+    for (int jn = 0; jn < C::TN; ++jn)
+      koB[jn] = C::A_BYTES + (8 * lh + ko_j) * (C::BN * 2) + ((((wn * C::WN) / 32 + jn) ^ ko_s1) << 6) +
+                ((ko_g1 ^ lh) << 5) + 8 * ko_q;
+  }
+  auto tr_pair = [&](char* base, int off, int rowbytes) __attribute__((always_inline)) -> bf16x8 {
+    typedef short short4v __attribute__((ext_vector_type(4)));
+    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS short4v*)(base + off));
+    const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS short4v*)(base + off + 4 * rowbytes));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // fragment of A subtile i / B subtile jn, stage STG, k-step kk
+  auto frag_a = [&](int stg, int kk, int i) __attribute__((always_inline)) -> bf16x8 {
+    if constexpr (C::AKO)
+      return tr_pair(stage(stg), 16 * kk * (C::BM * 2) + koA[i], C::BM * 2);
+    else
+      return *reinterpret_cast<const bf16x8*>(stage(kStageArrays ? stg : 0) + foA[stg][kk] + i * 32 * (C::BK * 2));
+  };
+  auto frag_b = [&](int stg, int kk, int jn) __attribute__((always_inline)) -> bf16x8 {
+    if constexpr (C::BKO)
+      return tr_pair(stage(stg), 16 * kk * (C::BN * 2) + koB[jn], C::BN * 2);
+    else
+      return *reinterpret_cast<const bf16x8*>(stage(kStageArrays ? stg : 0) + foB[stg][kk] + brow(jn) * (C::BK * 2));
   };
 
   floatx16 acc[C::TN][C::TM];
@@ -289,11 +385,9 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
   auto load_frags = [&](auto stg, int kk, int buf) {
     constexpr int STG = decltype(stg)::value;
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-      af[buf][i] = *reinterpret_cast<const bf16x8*>(smem + foA[STG][kk] + i * 32 * (C::BK * 2));
+    for (int i = 0; i < C::TM; ++i) af[buf][i] = frag_a(STG, kk, i);
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-      bfg[buf][j] = *reinterpret_cast<const bf16x8*>(smem + foB[STG][kk] + brow(j) * (C::BK * 2));
+    for (int j = 0; j < C::TN; ++j) bfg[buf][j] = frag_b(STG, kk, j);
   };
   auto mfmas = [&](int buf) {
 #pragma unroll
@@ -316,12 +410,12 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
   // Load instruction g of this wave's group for a tile into stage STG
   // (g < IA: A-tile row block g, else B-tile row block g - IA).
   auto dma_one = [&](auto stg, int g, const __amdgpu_buffer_rsrc_t& ra, const __amdgpu_buffer_rsrc_t& rb,
-                     uint32_t so) {
+                     uint32_t soA, uint32_t soB) {
     constexpr int STG = decltype(stg)::value;
     if (g < C::IA)
-      dma16(ra, smem + STG * C::STAGE_BYTES + (w * C::IA + g) * 1024, voA[g], so);
+      dma16(ra, stage(STG) + (w * C::IA + g) * 1024, voA[g], soA);
     else
-      dma16(rb, smem + STG * C::STAGE_BYTES + C::A_BYTES + (w * C::IB + g - C::IA) * 1024, voB[g - C::IA], so);
+      dma16(rb, stage(STG) + C::A_BYTES + (w * C::IB + g - C::IA) * 1024, voB[g - C::IA], soB);
   };
   // A tile's load instructions are spread over the boundary step that frees
   // its stage and the first kParts-1 k-steps of the next tile.
@@ -340,7 +434,8 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
         const bool live = t + 1 < nk;
         const __amdgpu_buffer_rsrc_t ra = live ? rA : rZ;
         const __amdgpu_buffer_rsrc_t rb = live ? rB : rZ;
-        const uint32_t so = live ? (uint32_t)k_begin(t + 1) * 2u : 0u;
+        const uint32_t soA = live ? (uint32_t)k_begin(t + 1) * kstepA : 0u;
+        const uint32_t soB = live ? (uint32_t)k_begin(t + 1) * kstepB : 0u;
         constexpr int NMF = C::TM * C::TN;
         const int lo = kBoundaryLoads + kk * kStepLoads;
         const int nl = min(kStepLoads, C::GROUP - lo);
@@ -349,15 +444,14 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
           if (q < C::TM)
-            af[nb][q] = *reinterpret_cast<const bf16x8*>(smem + foA[STG][kk + 1] + q * 32 * (C::BK * 2));
+            af[nb][q] = frag_a(STG, kk + 1, q);
           else if (q < C::TM + C::TN)
-            bfg[nb][q - C::TM] =
-                *reinterpret_cast<const bf16x8*>(smem + foB[STG][kk + 1] + brow(q - C::TM) * (C::BK * 2));
+            bfg[nb][q - C::TM] = frag_b(STG, kk + 1, q - C::TM);
           if (q < NMF) {
             const int j = q / C::TM, i = q % C::TM;
             acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[cb][j], af[cb][i], acc[j][i], 0, 0, 0);
           }
-          if (q < nl) dma_one(NXT{}, lo + q, ra, rb, so);
+          if (q < nl) dma_one(NXT{}, lo + q, ra, rb, soA, soB);
           __builtin_amdgcn_sched_barrier(0);
         }
         continue;
@@ -382,7 +476,8 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
       const bool live = t + 2 < nk;
       const __amdgpu_buffer_rsrc_t ra = live ? rA : rZ;
       const __amdgpu_buffer_rsrc_t rb = live ? rB : rZ;
-      const uint32_t so = live ? (uint32_t)k_begin(t + 2) * 2u : 0u;
+      const uint32_t soA = live ? (uint32_t)k_begin(t + 2) * kstepA : 0u;
+      const uint32_t soB = live ? (uint32_t)k_begin(t + 2) * kstepB : 0u;
       constexpr int LB = (C::KK - 1) & 1;
       constexpr int NMF = C::TM * C::TN;
       constexpr int NQ = NMF > kBoundaryLoads ? NMF : kBoundaryLoads;
@@ -390,14 +485,14 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         if (q < C::TM)
-          af[0][q] = *reinterpret_cast<const bf16x8*>(smem + foA[NB][0] + q * 32 * (C::BK * 2));
+          af[0][q] = frag_a(NB, 0, q);
         else if (q < C::TM + C::TN)
-          bfg[0][q - C::TM] = *reinterpret_cast<const bf16x8*>(smem + foB[NB][0] + brow(q - C::TM) * (C::BK * 2));
+          bfg[0][q - C::TM] = frag_b(NB, 0, q - C::TM);
         if (q < NMF) {
           const int j = q / C::TM, i = q % C::TM;
           acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfg[LB][j], af[LB][i], acc[j][i], 0, 0, 0);
         }
-        if (q < kBoundaryLoads) dma_one(stg, q, ra, rb, so);
+        if (q < kBoundaryLoads) dma_one(stg, q, ra, rb, soA, soB);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -430,8 +525,9 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
       }
     }
     lds_barrier();  // every wave is done with the operand stages
-    char* const ep = smem + w * (C::WM * 256);
-    static_assert(4 * C::WM * 256 <= C::LDS_BYTES, "epilogue staging fits the operand stages");
+    // waves 0, 1 stage through the first operand stage, waves 2, 3 the second
+    char* const ep = stage(w >> 1) + (w & 1) * (C::WM * 256);
+    static_assert(2 * C::WM * 256 <= C::STAGE_BYTES, "epilogue staging fits the operand stages");
     constexpr bool SWI = MODE == EPI_SWIGLU;
   #pragma unroll
     for (int h = 0; h < C::TN / 2; ++h) {
@@ -523,6 +619,15 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
                 __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(dst));
               else
                 for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
+              if (p.C2) {  // GELU(Z) as well, the weight gradient's operand
+  #pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = to_bf16(gelu_bf16out(static_cast<float>(zc[j][e])));
+                bf16* dst2 = static_cast<bf16*>(p.C2) + bz * p.sC2 + (int64_t)m * p.ldc2 + n;
+                if (n + 3 < p.N)
+                  __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(dst2));
+                else
+                  for (int e = 0; e < 4 && n + e < p.N; ++e) dst2[e] = o[e];
+              }
             }
           }
   #pragma unroll
@@ -700,9 +805,10 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
       const bool live = 1 < nk;
       const __amdgpu_buffer_rsrc_t ra = live ? rA : rZ;
       const __amdgpu_buffer_rsrc_t rb = live ? rB : rZ;
-      const uint32_t so = live ? (uint32_t)k_begin(1) * 2u : 0u;
+      const uint32_t soA = live ? (uint32_t)k_begin(1) * kstepA : 0u;
+      const uint32_t soB = live ? (uint32_t)k_begin(1) * kstepB : 0u;
   #pragma unroll
-      for (int g = 0; g < kBoundaryLoads; ++g) dma_one(I1{}, g, ra, rb, so);
+      for (int g = 0; g < kBoundaryLoads; ++g) dma_one(I1{}, g, ra, rb, soA, soB);
     }
     wait_vmcnt<kBoundaryLoads>();
     if (has_tail) clear_partial();
@@ -859,7 +965,7 @@ hipError_t launch_bf16_cfg(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EPI>
+template <int EPI, bool AKO = false, bool BKO = false>
 hipError_t launch_bf16_epi(const GemmParams& p, hipStream_t s) {
   // 256x256 tiles (128x128 per wave) when they fill every CU at least once;
   // smaller problems take 128x128 tiles, two workgroups per CU.
@@ -875,13 +981,37 @@ hipError_t launch_bf16_epi(const GemmParams& p, hipStream_t s) {
   // product).
   const bool short_k_load_epilogue = (EPI == EPI_GELU_BWD && p.K <= 2048) || EPI == EPI_SWIGLU_BWD;
   if (big >= kCUs && !short_k_load_epilogue)
-    return launch_bf16_cfg<G<256, 256, 64, 2, kGemmSwizzleShift, EPI>>(p, s);
-  return launch_bf16_cfg<G<128, 128, 64, 2, kGemmSwizzleShift, EPI>>(p, s);
+    return launch_bf16_cfg<G<256, 256, 64, 2, kGemmSwizzleShift, EPI, AKO, BKO>>(p, s);
+  return launch_bf16_cfg<G<128, 128, 64, 2, kGemmSwizzleShift, EPI, AKO, BKO>>(p, s);
+}
+
+// Operands stored K-outer ([K x M] / [K x N], row pitch lda / ldb): the
+// backward's products over the token and hidden axes read them as stored.
+// K must be a multiple of 64 and (K-1)*ld*2 + 512 below 2^32 (the buffer
+// range); the host checks.  M and N may be ragged.
+template <int EPI>
+hipError_t launch_bf16_ko(const GemmParams& p, hipStream_t s) {
+  if constexpr (EPI == EPI_PARTIAL) {
+    if (p.a_ko && p.b_ko) return launch_bf16_epi<EPI, true, true>(p, s);
+    if (!p.a_ko && p.b_ko) return launch_bf16_epi<EPI, false, true>(p, s);
+  } else if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_STORE || EPI == EPI_SWIGLU_BWD) {
+    if (!p.a_ko && p.b_ko) return launch_bf16_epi<EPI, false, true>(p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmParams& p, Epilogue epi, hipStream_t s) {
+  if (p.a_ko || p.b_ko) {
+    switch (epi) {
+      case EPI_PARTIAL: return launch_bf16_ko<EPI_PARTIAL>(p, s);
+      case EPI_GELU_BWD: return launch_bf16_ko<EPI_GELU_BWD>(p, s);
+      case EPI_STORE: return launch_bf16_ko<EPI_STORE>(p, s);
+      case EPI_SWIGLU_BWD: return launch_bf16_ko<EPI_SWIGLU_BWD>(p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (epi) {
     case EPI_STORE: return launch_bf16_epi<EPI_STORE>(p, s);
     case EPI_GELU: return launch_bf16_epi<EPI_GELU>(p, s);

@@ -421,15 +421,44 @@ tp_status validate_attn(const tp_attn_desc* d, AttnShape* sh) {
 //   Z    [T x Fz] (ld zld)  recomputed pre-activation (Fz = Fc, or 2*Fc for
 //                           SwiGLU: each shard's [gate | up] columns)
 //   dZ   [T x Fz] (ld zld)
-//   Hs   [T x Fc]           SwiGLU only: SiLU(gate)*up, written by the dZ epilogue
+//   Hs   [T x Fc]           act(Z): SiLU(gate)*up or GELU(Z), written by the dZ
+//                           kernel's epilogue (SwiGLU, the two-pass GELU kernel,
+//                           and GELU on the direct path)
 //   XT, dYT [H x T];  HT [Fc x T];  dZT [Fz x T];  AT [H x Fz];  BT [Fc x H]
+//                           transposed operands: the transposing path only,
+//                           except BT for the two-pass GELU kernel
+//   CS   fp32               column-sum partials of da and db (direct path)
 //   K    S x [Fz x H] fp32  split-K partials of the weight gradients
+//
+// The direct path (bf16, shapes the K-outer GEMM takes) reads every operand
+// as stored: the GEMMs take dZ, X, dY, act(Z) and the weight rows K-outer, and
+// the bias gradients are column sums.  Otherwise (fp32, or a contraction
+// length not a multiple of 64) the operands are transposed first.
 struct BwdShape {
   int64_t Fs, Fc, zld;
   int64_t Fz;   // columns of Z and dZ: Fc, or 2*Fc for SwiGLU ([gate | up] per shard)
   int splits;   // split-K factor of the token-axis contractions
-  size_t p_bytes, z_off, dz_off, h_off, xt_off, dyt_off, ht_off, dzt_off, at_off, bt_off, k_off, total;
+  bool direct;  // operands read as stored (K-outer GEMM operands)
+  size_t p_bytes, z_off, dz_off, h_off, xt_off, dyt_off, ht_off, dzt_off, at_off, bt_off, cs_off, csb_off, k_off,
+      total;
 };
+
+// Whether the direct path takes the backward: bf16, every K-outer contraction
+// length (H for dH, the shard width for dX, the token split for dA and dB) a
+// multiple of 64, and every K-outer operand's span within a 32-bit buffer
+// range.  Lowers *splits until each token split is a multiple of 64.
+bool bwd_direct_ok(const tp_mlp_bwd_desc* d, int64_t zs, int64_t Fz, int64_t Fc, int* splits) {
+  if (d->dt != TP_BF16 || d->T % 64 || d->H % 64 || zs % 64) return false;
+  int S = *splits;
+  while (S > 1 && (d->T / S) % 64) S /= 2;
+  const int64_t kc = d->T / S;
+  const int64_t lim = (int64_t)0xFFFFFFFF - 1024;
+  auto fits = [&](int64_t k, int64_t ld) { return (k - 1) * ld * 2 + 512 <= lim; };
+  const int64_t wide = std::max(std::max(Fz, Fc), d->F);  // widest ld of dZ / act(Z) / a stored Z
+  if (!fits(d->H, d->F) || !fits(zs, d->H) || !fits(kc, d->H) || !fits(kc, wide)) return false;
+  *splits = S;
+  return true;
+}
 
 // Weight gradients contract over all T tokens into a small [Fc x H] output
 // when the hidden size is narrow.  Split the token axis so that the launch
@@ -511,17 +540,24 @@ tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
   if (d->T > kIntMax || d->F > kIntMax) return fail(TP_ERR_SHAPE, "size exceeds 2^31-1");
   const size_t T = (size_t)d->T, H = (size_t)d->H, fc = (size_t)Fc, fz = (size_t)sh->Fz, es = esize(d->dt);
   sh->splits = bwd_splits(d->T, sh->Fz, d->H);
+  const int64_t zs = swiglu ? 2 * Fs : Fs;
+  sh->direct = bwd_direct_ok(d, zs, sh->Fz, Fc, &sh->splits);
+  const bool fused = bwd_fused_gelu(d);
+  const bool tr = !sh->direct;  // transposed operands in the workspace
   sh->p_bytes = align256((size_t)d->N * T * H * sizeof(float));
   sh->z_off = sh->p_bytes;
   sh->dz_off = sh->z_off + (d->Z ? 0 : align256(T * fz * es));  // no recomputed Z with a stored one
   sh->h_off = sh->dz_off + align256(T * fz * es);
-  sh->xt_off = sh->h_off + (swiglu || bwd_fused_gelu(d) ? align256(T * fc * es) : 0);
-  sh->dyt_off = sh->xt_off + align256(H * T * es);
-  sh->ht_off = sh->dyt_off + align256(H * T * es);
-  sh->dzt_off = sh->ht_off + align256(fc * T * es);
-  sh->at_off = sh->dzt_off + align256(fz * T * es);
-  sh->bt_off = sh->at_off + align256(H * fz * es);
-  sh->k_off = sh->bt_off + align256(fc * H * es);
+  const bool hs = swiglu || fused || (sh->direct && d->act == TP_ACT_GELU);
+  sh->xt_off = sh->h_off + (hs ? align256(T * fc * es) : 0);
+  sh->dyt_off = sh->xt_off + (tr ? align256(H * T * es) : 0);
+  sh->ht_off = sh->dyt_off + (tr ? align256(H * T * es) : 0);
+  sh->dzt_off = sh->ht_off + (tr ? align256(fc * T * es) : 0);
+  sh->at_off = sh->dzt_off + (tr ? align256(fz * T * es) : 0);
+  sh->bt_off = sh->at_off + (tr ? align256(H * fz * es) : 0);
+  sh->cs_off = sh->bt_off + (tr || fused ? align256(fc * H * es) : 0);
+  sh->csb_off = sh->cs_off + (sh->direct ? align256(tp::colsum_part_floats(d->T, Fc) * sizeof(float)) : 0);
+  sh->k_off = sh->csb_off + (sh->direct ? align256(tp::colsum_part_floats(d->T, d->H) * sizeof(float)) : 0);
   sh->total = sh->k_off + (sh->splits > 1 ? align256((size_t)sh->splits * fz * H * sizeof(float)) : 0);
   return TP_OK;
 }
@@ -549,6 +585,140 @@ tp_status bwd_tail(hipStream_t s, const tp_mlp_bwd_desc* d, const BwdShape& sh, 
 
   if (c < d->N) return ok();
   return run_reduce(s, d->dt, d->N, T, H, P, T * H, nullptr, d->dX, d->n_slices, d->slice);
+}
+
+// The backward on the direct path: every operand read as stored.  dH = dY B_r
+// takes the range's columns of B K-outer ([H x Fc], ld F); dX_i = dZ_i A_i the
+// shard's rows of A K-outer ([zs x H]); dA = dZ^T X and dB = dY^T act(Z) take
+// both operands K-outer over the token axis.  The bias gradients are column
+// sums of dZ and dY.
+tp_status bwd_direct(hipStream_t s, const tp_mlp_bwd_desc* d, const BwdShape& sh, char* base) {
+  const int64_t T = d->T, H = d->H, F = d->F, Fs = sh.Fs, Fc = sh.Fc, Fz = sh.Fz;
+  const int c = d->shard_count, i0 = d->shard_begin, S = sh.splits;
+  const bool gelu = d->act == TP_ACT_GELU, swiglu = d->act == TP_ACT_SWIGLU;
+  const int64_t zs = swiglu ? 2 * Fs : Fs;
+  const size_t es = 2;
+  char* Z = base + sh.z_off;
+  char* dZ = base + sh.dz_off;
+  char* Hs = base + sh.h_off;
+  char* BT = base + sh.bt_off;
+  float* CSa = reinterpret_cast<float*>(base + sh.cs_off);
+  float* CSb = reinterpret_cast<float*>(base + sh.csb_off);
+  float* K = reinterpret_cast<float*>(base + sh.k_off);
+  float* P = reinterpret_cast<float*>(base);
+  const char* A_r = static_cast<const char*>(d->A) + (size_t)i0 * zs * H * es;  // range rows of A
+  const char* B_r = static_cast<const char*>(d->B) + (size_t)i0 * Fs * es;      // range columns of B
+  const char* a_r = d->a ? static_cast<const char*>(d->a) + (size_t)i0 * Fs * es : nullptr;
+
+  // act(Z), the B operand of dB: [T x Fc] at pitch hld
+  const void* Hop = Hs;
+  int64_t hld = Fc;
+  if (bwd_fused_gelu(d)) {
+    // the two-pass kernel reads its second operand K-contiguous: B_r^T once
+    tp::TransposeParams t{B_r, F, BT, H, H, Fc};
+    KernelTimer kt("bwd_transpose", s);
+    const hipError_t e = tp::launch_transpose(t, false, false, s);
+    kt.stop();
+    TP_TRY(hip_status(e, "bwd_transpose"));
+    tp::GemmParams fg = gemm(d->X, H, 0, A_r, H, 0, dZ, sh.zld, 0, T, Fc, H, 1);
+    fg.bias = a_r;
+    fg.A2 = d->dY;
+    fg.B2 = BT;
+    fg.C2 = Hs;
+    fg.ldc2 = Fc;
+    TP_TRY(hip_status(launch("bwd_fused_gemm", TP_BF16, fg, tp::EPI_GELU_FUSED, s), "bwd_fused_gemm"));
+  } else {
+    // Z = X A_r^T (+ a_r): the forward's stored one, or recomputed
+    const void* Zp = Z;
+    int64_t zld = sh.zld;
+    if (d->Z) {
+      Zp = static_cast<const char*>(d->Z) + (size_t)i0 * Fs * es;
+      zld = F;
+    } else {
+      tp::GemmParams zg = gemm(d->X, H, 0, A_r, H, 0, Z, sh.zld, 0, T, Fz, H, 1);
+      zg.bias = a_r;
+      TP_TRY(hip_status(launch("bwd_recompute_gemm", TP_BF16, zg, tp::EPI_STORE, s), "bwd_recompute_gemm"));
+    }
+    if (swiglu) {
+      // per shard: dH = dY B_i; [dG | dU] and SiLU(G) U from the stored [G | U]
+      tp::GemmParams dg = gemm(d->dY, H, 0, B_r, F, Fs, dZ, sh.zld, zs, T, Fs, H, c);
+      dg.b_ko = 1;
+      dg.aux = Z;
+      dg.ldaux = sh.zld;
+      dg.sAux = zs;
+      dg.upOff = Fs;
+      dg.C2 = Hs;
+      dg.ldc2 = Fc;
+      dg.sC2 = Fs;
+      TP_TRY(hip_status(launch("bwd_dz_gemm", TP_BF16, dg, tp::EPI_SWIGLU_BWD, s), "bwd_dz_gemm"));
+    } else {
+      // dZ = (dY B_r) * act'(Z); GELU(Z) written beside it for dB
+      tp::GemmParams dg = gemm(d->dY, H, 0, B_r, F, 0, dZ, sh.zld, 0, T, Fc, H, 1);
+      dg.b_ko = 1;
+      dg.aux = Zp;
+      dg.ldaux = zld;
+      if (gelu) {
+        dg.C2 = Hs;
+        dg.ldc2 = Fc;
+      } else {
+        Hop = Zp;
+        hld = zld;
+      }
+      TP_TRY(hip_status(launch("bwd_dz_gemm", TP_BF16, dg, gelu ? tp::EPI_GELU_BWD : tp::EPI_STORE, s),
+                        "bwd_dz_gemm"));
+    }
+  }
+  // dX partial of each shard into its slab slot: dZ_i A_i (K = zs), A_i K-outer
+  tp::GemmParams xg = gemm(dZ, sh.zld, zs, A_r, H, zs * H, P + (size_t)i0 * T * H, H, T * H, T, H, zs, c);
+  xg.b_ko = 1;
+  TP_TRY(hip_status(launch("bwd_dx_gemm", TP_BF16, xg, tp::EPI_PARTIAL, s), "bwd_dx_gemm"));
+
+  // C[M x N] = Aop^T Bop over the token axis, both [T x .] K-outer; split-K
+  // when the output is small, the splits' partials folded in split order
+  auto token_gemm = [&](const char* name, const void* Aop, int64_t lda, const void* Bop, int64_t ldb, int64_t M,
+                        int64_t N, float* C, int64_t ldc) -> tp_status {
+    if (S == 1) {
+      tp::GemmParams g = gemm(Aop, lda, 0, Bop, ldb, 0, C, ldc, 0, M, N, T, 1);
+      g.a_ko = g.b_ko = 1;
+      return hip_status(launch(name, TP_BF16, g, tp::EPI_PARTIAL, s), name);
+    }
+    const int64_t kc = T / S;
+    tp::GemmParams g = gemm(Aop, lda, kc * lda, Bop, ldb, kc * ldb, K, N, M * N, M, N, kc, S);
+    g.a_ko = g.b_ko = 1;
+    g.xcd_per_problem = S % 8 == 0;  // each split's operand blocks stay in one XCD's L2
+    TP_TRY(hip_status(launch(name, TP_BF16, g, tp::EPI_PARTIAL, s), name));
+    tp::ReduceParams r{};
+    r.P = K;
+    r.part_stride = M * N;
+    r.n_parts = S;
+    r.rows = M;
+    r.H = N;
+    r.row0 = 0;
+    r.bias = nullptr;
+    r.Y = C;
+    r.ldy = ldc;
+    KernelTimer kt("bwd_splitk_reduce", s);
+    const hipError_t e = tp::launch_reduce(r, false, s);
+    kt.stop();
+    return hip_status(e, "bwd_splitk_reduce");
+  };
+  // dA rows of the range: dZ^T X  (M = Fz, N = H)
+  TP_TRY(token_gemm("bwd_da_gemm", dZ, sh.zld, d->X, H, Fz, H, d->dA + (size_t)i0 * zs * H, H));
+  // dB columns of the range: dY^T act(Z)  (M = H, N = Fc)
+  TP_TRY(token_gemm("bwd_db_gemm", d->dY, H, Hop, hld, H, Fc, d->dB + (size_t)i0 * Fs, F));
+  // bias gradients: column sums of dZ (range) and of dY (once)
+  auto colsum = [&](const void* in, int64_t ld, int64_t C, float* part, float* out) -> tp_status {
+    tp::ColSumParams cp{in, ld, T, C, part, out};
+    KernelTimer kt("bwd_bias_colsum", s);
+    const hipError_t e = tp::launch_colsum(cp, s);
+    kt.stop();
+    return hip_status(e, "bwd_bias_colsum");
+  };
+  if (d->da) TP_TRY(colsum(dZ, sh.zld, Fc, CSa, d->da + (size_t)i0 * Fs));
+  if (d->db) TP_TRY(colsum(d->dY, H, H, CSb, d->db));
+
+  if (c < d->N) return ok();
+  return run_reduce(s, TP_BF16, d->N, T, H, P, T * H, nullptr, d->dX, d->n_slices, d->slice);
 }
 
 // ------------------------------------------------------- vocab-parallel CE
@@ -1057,9 +1227,10 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
   const bool f32 = dt == TP_F32;
   const size_t es = esize(dt);
   if (log_enabled())
-    fprintf(stderr, "[tp] mlp backward %s act=%d N=%d shards [%d,%d): T=%lld H=%lld Fs=%lld, split-K %d%s\n",
+    fprintf(stderr, "[tp] mlp backward %s act=%d N=%d shards [%d,%d): T=%lld H=%lld Fs=%lld, split-K %d, %s%s\n",
             dt_name(dt), (int)d->act, d->N, i0, i0 + c, (long long)T, (long long)H, (long long)Fs, S,
-            c == d->N ? " ; reduce dX" : "");
+            sh.direct ? "operands as stored" : "transposed operands", c == d->N ? " ; reduce dX" : "");
+  if (sh.direct) return bwd_direct(s, d, sh, static_cast<char*>(ws));
   char* base = static_cast<char*>(ws);
   char* Z = base + sh.z_off;
   char* dZ = base + sh.dz_off;

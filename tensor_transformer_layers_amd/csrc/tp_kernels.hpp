@@ -53,10 +53,11 @@ struct CeEpilogue {
 };
 
 // C[M x N] = A[M x K] * B[N x K]^T, batched over `batch` problems whose
-// pointers advance by sA/sB/sC/sBias elements.  Both operands are K-contiguous.
-// For EPI_SWIGLU, B holds gate rows at B and up rows at B + upOff; N is the
-// output width (gate rows used: N).  For EPI_GELU_BWD, aux is a bf16 matrix of
-// the output's shape (ld ldaux, advancing by sAux per problem).
+// pointers advance by sA/sB/sC/sBias elements.  Operands are K-contiguous
+// unless a_ko / b_ko say otherwise.  For EPI_SWIGLU, B holds gate rows at B
+// and up rows at B + upOff; N is the output width (gate rows used: N).  For
+// EPI_GELU_BWD, aux is a bf16 matrix of the output's shape (ld ldaux,
+// advancing by sAux per problem), and C2, when not null, receives GELU(aux).
 struct GemmParams {
   const void* A;
   int64_t lda, sA;
@@ -73,10 +74,14 @@ struct GemmParams {
   int batch;
   int xcd_per_problem;  // nonzero: batch % 8 == 0, each problem runs whole on one XCD
   CeEpilogue ce;        // EPI_CE_STATS only
-  void* C2;             // EPI_SWIGLU_BWD, EPI_GELU_FUSED, EPI_GELU_Z: second bf16 output (ld ldc2, advancing by sC2)
+  void* C2;             // EPI_SWIGLU_BWD, EPI_GELU_FUSED, EPI_GELU_Z, EPI_GELU_BWD: second bf16 output
+                        // (ld ldc2, advancing by sC2)
   int64_t ldc2, sC2;
   const void* A2;       // EPI_GELU_FUSED: second pass operands (same ld and batch strides as A, B)
   const void* B2;
+  int a_ko, b_ko;       // nonzero: A is stored K-outer ([K x M], row pitch lda), B likewise ([K x N], ldb);
+                        // bf16, EPI_PARTIAL (A and B, or B only), EPI_GELU_BWD / EPI_STORE /
+                        // EPI_SWIGLU_BWD (B only); K a multiple of 64, (K-1)*ld*2 + 512 < 2^32
 };
 
 hipError_t launch_gemm_bf16(const GemmParams& p, Epilogue epi, hipStream_t s);
@@ -198,6 +203,19 @@ struct RowSumParams {
   int64_t R, C;
 };
 hipError_t launch_rowsum(const RowSumParams& p, bool f32, hipStream_t s);
+
+//   out[c] = sum over r of in[r][c], bf16 in [R x C] (ld), fp32 out, in a
+//   fixed order: chunks of rows summed into part (colsum_part_floats(R, C)
+//   floats of workspace), then the chunks folded in order.  C a multiple of 8.
+struct ColSumParams {
+  const void* in;
+  int64_t ld;
+  int64_t R, C;
+  float* part;
+  float* out;
+};
+size_t colsum_part_floats(int64_t R, int64_t C);
+hipError_t launch_colsum(const ColSumParams& p, hipStream_t s);
 
 // Vocab-parallel cross-entropy (vocab.hip).
 // Folds the per-chunk statistics of the GEMM epilogue (layout of CeEpilogue,

@@ -221,19 +221,33 @@ def _bwd(**kw):
 
 def test_mlp_backward_workspace_size_is_host_only(L):
     T, H, F, N = 256, 512, 2048, 4
-    need = tp.tp_mlp_backward_workspace_size(_bwd())
-    # dX partial slab, Z and dZ, act(Z) (the two-pass GELU kernel at H <= 2048
-    # writes it), the transposes of X, dY, act(Z), dZ, A, B
-    base = N * T * H * 4 + 3 * T * F * 2 + 2 * H * T * 2 + 2 * F * T * 2 + 2 * H * F * 2
-    assert need >= base
-    extra = need - base  # split-K partials of the weight gradients
-    assert extra % (F * H * 4) == 0 and extra // (F * H * 4) in (0, 2, 4, 8, 16)
-    one = tp.tp_mlp_backward_workspace_size(_bwd(shard_count=1, shard_begin=3))
+    ws = tp.tp_mlp_backward_workspace_size
+    # bf16, every contraction a multiple of 64: operands read as stored.  dX
+    # partial slab, Z, dZ and act(Z) (the two-pass GELU kernel at H <= 2048
+    # writes it), B^T for that kernel's second pass, and the column-sum
+    # partials of the bias gradients (at most one row per 16 tokens)
+    need = ws(_bwd())
+    base = N * T * H * 4 + 3 * T * F * 2 + H * F * 2
+    assert base < need <= base + 4 * (F + H) * (T // 16) + 2 * 256
+    one = ws(_bwd(shard_count=1, shard_begin=3))
     assert one < need
-    # with the forward's pre-activation supplied there is no recomputed Z, and
-    # (no two-pass kernel) no separate act(Z) slab either
-    stored = tp.tp_mlp_backward_workspace_size(_bwd(Z=FAKE))
-    assert stored == need - 2 * T * F * 2
+    # with the forward's pre-activation supplied there is no recomputed Z and
+    # no two-pass kernel (so no B^T); act(Z) is still written, by the dZ GEMM
+    stored = ws(_bwd(Z=FAKE))
+    assert stored == need - T * F * 2 - H * F * 2
+
+    # a token count that is not a multiple of 64 (or fp32): the operands are
+    # transposed first -- X, dY, act(Z), dZ, A and B -- and the bias
+    # gradients are row sums of the transposes
+    Tt = 264
+    need_t = ws(_bwd(T=Tt))
+    base_t = N * Tt * H * 4 + 3 * Tt * F * 2 + 2 * H * Tt * 2 + 2 * F * Tt * 2 + 2 * H * F * 2
+    assert need_t >= base_t
+    extra = need_t - base_t  # split-K partials of the weight gradients
+    assert extra % (F * H * 4) == 0 and extra // (F * H * 4) in (0, 2, 4, 8, 16)
+    assert ws(_bwd(T=Tt, Z=FAKE)) == need_t - 2 * Tt * F * 2
+    f32 = ws(_bwd(dt=tp.TP_F32))
+    assert f32 >= N * T * H * 4 + 2 * T * F * 4 + 2 * H * T * 4 + 2 * F * T * 4 + 2 * H * F * 4
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -260,12 +274,12 @@ def test_mlp_backward_rejects_before_launch(L, kw, status, needle):
 
 
 def test_mlp_backward_swiglu_workspace(L):
-    """SwiGLU keeps [gate | up] per shard (twice the columns of Z, dZ and
-    their transposes) plus SiLU(gate)*up."""
+    """SwiGLU keeps [gate | up] per shard (twice the columns of Z and dZ)
+    plus SiLU(gate)*up, against GELU's dZ and GELU(Z) with a stored Z."""
     T, H, F, N = 256, 512, 2048, 4
-    gelu = tp.tp_mlp_backward_workspace_size(_bwd(a=None, da=None))
+    gelu = tp.tp_mlp_backward_workspace_size(_bwd(a=None, da=None, Z=FAKE))
     swi = tp.tp_mlp_backward_workspace_size(_bwd(act=tp.TP_ACT_SWIGLU, a=None, da=None))
-    assert swi > gelu + 3 * T * F * 2
+    assert swi == gelu + 3 * T * F * 2
 
 
 def test_mlp_backward_partial_range_needs_no_dx(L):
@@ -285,19 +299,31 @@ def test_mlp_backward_small_workspace_and_empty_input(L):
     (2048, 520, 320, 8, 8), (4096, 256, 1024, 4, 4), (264, 136, 288, 4, 4), (1000, 64, 128, 2, 2),
 ])
 def test_bench_split_rule_matches_library(L, T, H, F, N, c):
-    """bench.py's copy of the backward's split-K rule (used to name kernels
-    in profiler output) agrees with the library's, read off the workspace."""
+    """bench.py's copies of the backward's path and split-K rules (used to
+    name kernels in profiler output) agree with the library's, read off the
+    workspace."""
     import bench
+    from tensor_transformer_layers_amd.configs import Workload
 
     d = _bwd(T=T, H=H, F=F, N=N, shard_count=c)
     Fc = F // N * c
     align = lambda x: (x + 255) // 256 * 256
-    fused_h = align(T * Fc * 2) if H <= 2048 else 0  # act(Z) of the two-pass GELU kernel
-    base = align(N * T * H * 4) + 2 * align(T * Fc * 2) + fused_h + 2 * align(H * T * 2) + 2 * align(Fc * T * 2) \
-        + 2 * align(H * Fc * 2)
-    extra = tp.tp_mlp_backward_workspace_size(d) - base
-    S = bench.backward_splits(T, Fc, H)
-    assert extra == (align(S * Fc * H * 4) if S > 1 else 0)
+    w = Workload(key=0, name="t", kind="mlp_gelu", dtype="bf16", batch=1, seq=T, H=H, F=F, N=N, sigma_bias=0.02)
+    direct = bench.backward_direct(w)
+    S = bench.backward_splits(T, Fc, H, direct)
+    splitk = align(S * Fc * H * 4) if S > 1 else 0
+    need = tp.tp_mlp_backward_workspace_size(d)
+    if direct:
+        # slab, Z, dZ, act(Z), B^T (two-pass kernel at H <= 2048), column-sum partials
+        fused = H <= 2048
+        base = align(N * T * H * 4) + 3 * align(T * Fc * 2) + (align(H * Fc * 2) if fused else 0)
+        extra = need - base - splitk
+        assert 0 < extra <= 4 * (Fc + H) * (T // 16) + 2 * 256
+    else:
+        fused_h = align(T * Fc * 2) if H <= 2048 else 0  # act(Z) of the two-pass GELU kernel
+        base = align(N * T * H * 4) + 2 * align(T * Fc * 2) + fused_h + 2 * align(H * T * 2) \
+            + 2 * align(Fc * T * 2) + 2 * align(H * Fc * 2)
+        assert need - base == splitk
 
 
 # ------------------------------------------------------------ vocab-parallel CE

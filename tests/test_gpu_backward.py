@@ -57,12 +57,17 @@ def _np(t):
     return t.float().cpu().numpy()
 
 
+# T, H and the shard width all multiples of 64 (bf16): the GEMMs read every
+# operand as stored (K-outer) and the bias gradients are column sums; any
+# other shape transposes the operands first.
 @pytest.mark.parametrize("T,H,F,N,act,bias", [
-    (264, 136, 4 * 72, 4, tp.TP_ACT_GELU, True),     # ragged tiles in every dimension
-    (64, 64, 2 * 64, 2, tp.TP_ACT_NONE, False),
-    (2048, 520, 8 * 40, 8, tp.TP_ACT_GELU, True),    # split-K weight gradients (2 splits)
-    (4096, 256, 4 * 256, 4, tp.TP_ACT_GELU, False),
-    (8, 8, 8, 1, tp.TP_ACT_GELU, True),              # one shard, smallest sizes
+    (264, 136, 4 * 72, 4, tp.TP_ACT_GELU, True),     # transposed: ragged tiles in every dimension
+    (64, 64, 2 * 64, 2, tp.TP_ACT_NONE, False),      # as stored: one 64-row k-tile
+    (2048, 520, 8 * 40, 8, tp.TP_ACT_GELU, True),    # transposed: split-K weight gradients (2 splits)
+    (4096, 256, 4 * 256, 4, tp.TP_ACT_GELU, False),  # as stored: two-pass dZ kernel, split-K
+    (1024, 192, 4 * 320, 4, tp.TP_ACT_GELU, True),   # as stored: split-K, hidden narrower than a tile
+    (512, 128, 192, 1, tp.TP_ACT_GELU, True),        # as stored: shard width ragged against the tile
+    (8, 8, 8, 1, tp.TP_ACT_GELU, True),              # transposed: one shard, smallest sizes
 ])
 def test_backward_vs_oracle(T, H, F, N, act, bias):
     say(f"mlp_backward T={T} H={H} F={F} N={N} act={act} bias={bias}")
@@ -194,9 +199,10 @@ def _unfuse(dA, N):
 
 
 @pytest.mark.parametrize("T,H,I,N", [
-    (264, 136, 4 * 40, 4),     # ragged tiles
-    (2048, 512, 8 * 48, 8),    # split-K weight gradients
+    (264, 136, 4 * 40, 4),     # transposed operands: ragged tiles
+    (2048, 512, 8 * 48, 8),    # transposed operands (shard's [gate | up] width 96): split-K
     (304, 256, 2 * 64, 2),
+    (1024, 256, 4 * 96, 4),    # operands as stored: [gate | up] width 192, shard width ragged, split-K
 ])
 def test_swiglu_backward_vs_oracle(T, H, I, N):
     say(f"swiglu backward T={T} H={H} I={I} N={N}")

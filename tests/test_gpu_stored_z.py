@@ -69,6 +69,7 @@ def _zref(h):
     (256, 2304, 4 * 64, 4, tp.TP_ACT_GELU, True),    # GEMM path both ways
     (128, 2304, 2 * 64, 2, tp.TP_ACT_NONE, False),
     (2048, 520, 8 * 40, 8, tp.TP_ACT_GELU, True),    # split-K weight gradients
+    (2048, 256, 4 * 128, 4, tp.TP_ACT_GELU, True),   # operands as stored: GELU(Z) written by the dZ GEMM
 ])
 def test_stored_preactivation(T, H, F, N, act, bias):
     say(f"stored Z T={T} H={H} F={F} N={N} act={act} bias={bias}")
