@@ -28,7 +28,7 @@ constexpr int kTile = 64;          // 64 x 64 elements per workgroup
 // a row cover one contiguous row segment, in and out.  The tile is written to
 // LDS transposed (element by element) and read back in 16-byte rows.  With
 // GELU, the activation is applied on the way (fp32: erf form with the device
-// erff; bf16: the 7.1.26 form, rounded to bf16).
+// erff; bf16: gelu_bf16out, rounded to bf16).
 template <typename E, bool GELU>
 __global__ __launch_bounds__(kThreads) void transpose_kernel(TransposeParams p, int tilesC) {
   constexpr int VE = 16 / sizeof(E);                     // elements per 16-byte chunk

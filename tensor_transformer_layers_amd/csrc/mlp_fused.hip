@@ -254,16 +254,18 @@ __global__ __launch_bounds__(kFThreads, 1) void mlp_fused_kernel(FusedMlpParams 
   };
   auto act_stage = [&](int st, int i, float z) {
     if constexpr (GELU) {
+      // gelu_bf16out in four stages: the tail polynomial's Horner steps
+      // spread over the first three, its exp2 in the third
       if (st == 0) {
-        g_t = __builtin_amdgcn_rcpf(fmaf(kGeluP, fabsf(z), 1.0f));
-        g_w = (z * kGeluNegHalfLog2e) * z;
+        g_t = fminf(fabsf(z), kQxMax);
+        g_w = z * kGeluNegHalfLog2e;
+        g_f = fmaf(fmaf(kQc6, g_t, kQc5), g_t, kQc4);
       } else if (st == 1) {
-        g_f = fmaf(g_t, fmaf(g_t, fmaf(g_t, fmaf(g_t, kGeluA5, kGeluA4), kGeluA3), kGeluA2), kGeluA1);
+        g_f = fmaf(fmaf(fmaf(g_f, g_t, kQc3), g_t, kQc2), g_t, kQc1);
       } else if (st == 2) {
-        g_f = g_t * g_f;
-        g_e = __builtin_amdgcn_exp2f(g_w);
+        g_e = __builtin_amdgcn_exp2f(fmaf(g_w, z, fmaf(g_f, g_t, kQc0)));
       } else {
-        finish(i, fmaf(-(fabsf(z) * g_f), g_e, fmaxf(z, 0.0f)));
+        finish(i, fmaf(-fabsf(z), g_e, fmaxf(z, 0.0f)));
       }
     } else {
       if (st == 3) finish(i, z);

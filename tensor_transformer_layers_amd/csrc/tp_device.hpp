@@ -32,42 +32,42 @@ __device__ __forceinline__ float gelu_grad_erf(float z) {
 // SiLU with beta = 1: g * sigmoid(g) = g / (1 + e^-g).
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
-// GELU for bf16 outputs: the same exact (erf) form, with erf evaluated by the
-// rational-exponential approximation 7.1.26 of Abramowitz & Stegun, Handbook
-// of Mathematical Functions (absolute error <= 1.5e-7 in erf, far below bf16
-// resolution): erfc(x) = t*(a1 + t*(a2 + t*(a3 + t*(a4 + t*a5)))) e^(-x^2),
-// t = 1 / (1 + p x), x >= 0.  With x = |z|/sqrt 2 the tail
-// Phi(-|z|) = erfc(x)/2 = f e^(-z^2/2), f = t (a1/2 + t (a2/2 + ...)), so
-//   GELU(z) = z Phi(z) = max(z, 0) - |z| f e^(-z^2/2)
-// (no cancellation of 1 + erf near -1).  Folded constants: p/sqrt 2, the
-// halved coefficients, and e^(-z^2/2) = 2^(-z^2 log2(e)/2).  One reciprocal,
-// one exp2, eleven other operations, no branch.
-constexpr float kGeluP = (float)(0.3275911 * 0.70710678118654752);
-constexpr float kGeluA1 = (float)(0.5 * 0.254829592), kGeluA2 = (float)(0.5 * -0.284496736),
-                kGeluA3 = (float)(0.5 * 1.421413741), kGeluA4 = (float)(0.5 * -1.453152027),
-                kGeluA5 = (float)(0.5 * 1.061405429);
+// GELU for bf16 outputs: the same exact (erf) form, GELU(z) = z Phi(z), with
+// the Gaussian tail Q(x) = Phi(-x) = erfc(x / sqrt 2) / 2 (x >= 0) evaluated
+// as an exponential of a polynomial:
+//   Q(x) = 2^( -x^2 log2(e) / 2 + g(min(x, 5)) ),
+// g a degree-6 least-squares fit of (ln Q(x) + x^2/2) log2(e) on [0, 5] (a
+// smooth, slowly varying function: ln 1/2 at 0, about -ln(x sqrt(2 pi)) for
+// large x).  Relative error of Q <= 1.6e-5 on [0, 5] in fp32, absolute error
+// of GELU <= 2e-6 everywhere; past x = 5 (Q < 3e-7) the fit is held at 5.
+// csrc/gelu_tail_fit.py fits the coefficients and checks these bounds.  Then
+//   GELU(z) = max(z, 0) - |z| Q(|z|)
+// (no cancellation of 1 + erf near -1): one exp2 and ten other operations,
+// no reciprocal, no branch.
 constexpr float kGeluNegHalfLog2e = (float)(-0.5 * 1.4426950408889634);
+constexpr float kQc0 = -1.000011682510376f, kQc1 = -1.1509265899658203f, kQc2 = 0.2618351876735687f,
+                kQc3 = -0.052690327167510986f, kQc4 = 0.007775241509079933f, kQc5 = -0.000713575107511133f,
+                kQc6 = 2.9757440643152222e-05f;
+constexpr float kQxMax = 5.0f;
+// g(min(x, 5)) for x = |z|
+__device__ __forceinline__ float gauss_tail_poly(float x) {
+  const float u = fminf(x, kQxMax);
+  return fmaf(fmaf(fmaf(fmaf(fmaf(fmaf(kQc6, u, kQc5), u, kQc4), u, kQc3), u, kQc2), u, kQc1), u, kQc0);
+}
 __device__ __forceinline__ float gelu_bf16out(float z) {
-  const float t = __builtin_amdgcn_rcpf(fmaf(kGeluP, fabsf(z), 1.0f));
-  const float f = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, kGeluA5, kGeluA4), kGeluA3), kGeluA2), kGeluA1);
-  const float e = __builtin_amdgcn_exp2f((z * kGeluNegHalfLog2e) * z);
-  return fmaf(-(fabsf(z) * f), e, fmaxf(z, 0.0f));
+  const float q = __builtin_amdgcn_exp2f(fmaf(z * kGeluNegHalfLog2e, z, gauss_tail_poly(fabsf(z))));
+  return fmaf(-fabsf(z), q, fmaxf(z, 0.0f));
 }
 
 // Slope of the exact GELU for bf16 outputs:
 //   d/dz [z Phi(z)] = Phi(z) + z phi(z),  phi(z) = e^(-z^2/2) / sqrt(2 pi),
-// with the tail Phi(-|z|) = erfc(|z|/sqrt 2) / 2 from the same 7.1.26
-// expansion as gelu_bf16out (its folded constants), whose exponential
-// e^(-x^2), x = |z|/sqrt 2, is exactly e^(-z^2/2): one exp2 and one
-// reciprocal give both terms.  Absolute error ~1e-7, far below bf16
-// resolution.
+// with the tail Phi(-|z|) = Q(|z|) of gelu_bf16out (its fit and bounds) and
+// phi from a second exp2 of the same exponent's quadratic part.
 __device__ __forceinline__ float gelu_grad_bf16out(float z) {
-  const float t = __builtin_amdgcn_rcpf(fmaf(kGeluP, fabsf(z), 1.0f));
-  const float f = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, kGeluA5, kGeluA4), kGeluA3), kGeluA2), kGeluA1);
-  const float e = __builtin_amdgcn_exp2f((z * kGeluNegHalfLog2e) * z);  // e^(-z^2/2)
-  const float tail = f * e;                                                // Phi(-|z|)
-  const float Phi = z >= 0.0f ? 1.0f - tail : tail;
-  return fmaf(z * 0.39894228040143268f, e, Phi);
+  const float w = (z * kGeluNegHalfLog2e) * z;  // log2 e^(-z^2/2)
+  const float q = __builtin_amdgcn_exp2f(w + gauss_tail_poly(fabsf(z)));  // Phi(-|z|)
+  const float Phi = z >= 0.0f ? 1.0f - q : q;
+  return fmaf(z * 0.39894228040143268f, __builtin_amdgcn_exp2f(w), Phi);
 }
 
 // SiLU for bf16 outputs: g / (1 + e^-g) with the hardware exponential and
