@@ -291,6 +291,23 @@ def backward_launch_order(w, mode="recompute"):
     return order + ["reduce_partials"]
 
 
+def setup_launches(w, backward=False):
+    """Library kernels bench.py launches once before its steps: for the
+    stored-pre-activation backward, the training forward that writes Z (it
+    always takes the GEMM path: column GEMM with Z, row GEMM, reduction)."""
+    return ["mlp_column_gemm", "mlp_row_gemm", "reduce_partials"] if backward == "stored" else []
+
+
+def strip_setup(w, backward, ours, name_of):
+    """The library dispatches of a profiled run after the set-up launches,
+    which are checked by name and dropped."""
+    pre = setup_launches(w, backward)
+    for k, r in zip(pre, ours):
+        if KERNEL_SYMBOL[k] not in name_of(r):
+            raise RuntimeError(f"set-up dispatch: expected {k} ({KERNEL_SYMBOL[k]}), profiler has {name_of(r)[:120]}")
+    return ours[len(pre):]
+
+
 def launch_order(w, sp_entry=False, backward=False):
     """Kernels one step of workload w launches, in order.  A bf16 GELU MLP
     with hidden 256 or 512 and a shard width that is a multiple of 32 (at
@@ -361,6 +378,7 @@ def write_traffic(w, share, pmc_dir, argv_line, sp_entry=False, backward=False, 
         big = copies[-1]
         factor[counter] = float(2 ** 30) / (float(big["Counter_Value"]) * 1024.0)
         ours = [r for r in rows if "tp::" in r["Kernel_Name"] or "_ZN2tp" in r["Kernel_Name"]]
+        ours = strip_setup(w, backward, ours, lambda r: r["Kernel_Name"])
         vals = collections.defaultdict(list)
         for i, r in enumerate(ours):
             k = order[i % len(order)]
@@ -423,6 +441,7 @@ def write_mfma(w, share, pmc_dir, argv_line, sp_entry=False, backward=False, out
         per[int(r["Dispatch_Id"])][r["Counter_Name"]] = float(r["Counter_Value"])
         names[int(r["Dispatch_Id"])] = r["Kernel_Name"]
     ours = [d for d in sorted(per) if "tp::" in names[d] or "_ZN2tp" in names[d]]
+    ours = strip_setup(w, backward, ours, lambda d: names[d])
     vals = collections.defaultdict(lambda: collections.defaultdict(list))
     for i, dsp in enumerate(ours):
         k = order[i % len(order)]
@@ -480,6 +499,7 @@ def write_trace(w, share, trace_dir, argv_line, steps, sp_entry=False, backward=
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))))
     rows.sort(key=lambda r: int(r["Dispatch_Id"]))
     ours = [r for r in rows if "tp::" in r["Kernel_Name"] or "_ZN2tp" in r["Kernel_Name"]]
+    ours = strip_setup(w, backward, ours, lambda r: r["Kernel_Name"])
     if len(ours) % len(order):
         raise RuntimeError(f"{len(ours)} library dispatches is not a whole number of {len(order)}-kernel steps")
     durs = collections.defaultdict(list)

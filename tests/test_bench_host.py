@@ -131,3 +131,38 @@ def test_mfma_summary(tmp_path):
     assert float(lines["mlp_column_gemm"][4]) == pytest.approx(1.0)
     assert float(lines["mlp_column_gemm"][5]) == pytest.approx(60.0)
     assert float(lines["mlp_row_gemm"][5]) == pytest.approx(70.0)
+
+
+def test_stored_backward_summaries_skip_the_set_up_forward(tmp_path):
+    """The stored-pre-activation backward starts with one training forward
+    (column GEMM writing Z, row GEMM, reduction): the converters check and
+    drop those dispatches before matching steps, so a summary sees whole
+    backward steps only; a run without them is rejected."""
+    w = configs.workload(2)
+    order = bench.backward_launch_order(w, "stored")
+    assert bench.setup_launches(w, "stored") == ["mlp_column_gemm", "mlp_row_gemm", "reduce_partials"]
+    assert bench.setup_launches(w, "recompute") == []
+    sym = {"mlp_column_gemm": "gemm_bf16_kernel<G0>", "mlp_row_gemm": "gemm_bf16_kernel<G0>",
+           "reduce_partials": "reduce_kernel<r>"}
+    names = [sym[k] for k in bench.setup_launches(w, "stored")]
+    for _ in range(2):
+        names += [bench.KERNEL_SYMBOL[k] + "<x>" for k in order]
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = [{"Dispatch_Id": i + 1, "Kernel_Name": f"void tp::(anonymous namespace)::{n}", "Grid_Size": 1,
+                 "Counter_Name": counter, "Counter_Value": 7.0 if i < 3 else 1.0} for i, n in enumerate(names)]
+        rows.append({"Dispatch_Id": len(names) + 1, "Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 1,
+                     "Counter_Name": counter, "Counter_Value": 2 ** 20})
+        _write_counters(str(tmp_path / "pmc" / counter / "run_counter_collection.csv"), rows)
+    path = bench.write_traffic(w, "layer", str(tmp_path / "pmc"), "ARGS", backward="stored", out_dir=str(tmp_path))
+    vals = {l.split()[1]: float(l.split()[2]) for l in open(path) if l.startswith("traffic_bytes")}
+    assert set(vals) == set(order)
+    # every backward dispatch read 1 KiB x (2^30 / 2^30) and wrote 1 KiB; the set-up's 7 KiB never enter
+    assert all(v == pytest.approx(2 * 1024) for v in vals.values())
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = [{"Dispatch_Id": i + 1, "Kernel_Name": f"void tp::(anonymous namespace)::{n}", "Grid_Size": 1,
+                 "Counter_Name": counter, "Counter_Value": 1.0} for i, n in enumerate(names[3:])]
+        rows.append({"Dispatch_Id": len(names) + 1, "Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 1,
+                     "Counter_Name": counter, "Counter_Value": 2 ** 20})
+        _write_counters(str(tmp_path / "pmc2" / counter / "run_counter_collection.csv"), rows)
+    with pytest.raises(RuntimeError, match="set-up dispatch"):
+        bench.write_traffic(w, "layer", str(tmp_path / "pmc2"), "ARGS", backward="stored", out_dir=str(tmp_path))
