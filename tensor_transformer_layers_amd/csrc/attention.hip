@@ -277,8 +277,14 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
       s[g % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[g % (kAhead + 1)], qf[g / 2], s[g % 2], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // The serial parts of the online softmax (mask, max, reference point,
+    // rescale) run at wave priority 0, the rest at 1: while one wave of a
+    // SIMD is in them, the other wave's MFMAs take the issue slots first
+    // (measured at workload 4: 293 -> 286 us).
+    __builtin_amdgcn_s_setprio(0);
     if (diag) mask(0);
     const float alpha0 = new_point(0);
+    __builtin_amdgcn_s_setprio(1);
     float psum0 = 0.0f;
 #pragma unroll
     for (int g = 0; g < 16; ++g) {  // S^T, half 1: tile 2 + g%2, k-step g/2
@@ -288,10 +294,12 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
       soft2(0, g, psum0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     l_run = l_run * alpha0 + psum0;
     rescale(alpha0);
     if (diag) mask(1);
     const float alpha1 = new_point(1);
+    __builtin_amdgcn_s_setprio(1);
     float psum1 = 0.0f;
 #pragma unroll
     for (int g = 0; g < 16; ++g) {  // O^T, half 0: step c = g/4 (tile c/2, rows 8 (c%2)), output tile g%4
@@ -301,8 +309,10 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_kernel(AttnParams p) {
       soft2(1, g, psum1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     l_run = l_run * alpha1 + psum1;
     rescale(alpha1);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int g = 0; g < 16; ++g) {  // O^T, half 1: step c = 4 + g/4, output tile g%4
       const int n = 48 + g, c = 4 + g / 4, i = g % 4;
