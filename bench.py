@@ -253,8 +253,8 @@ KERNEL_SYMBOL = {
 
 def stored_preactivation(w):
     """Whether the backward of workload w can take the forward's stored
-    pre-activation (tp_mlp_desc.Z): the bf16 GELU MLPs."""
-    return w.kind == "mlp_gelu" and w.dtype == "bf16"
+    pre-activation (tp_mlp_desc.Z): the bf16 GELU and SwiGLU MLPs."""
+    return w.kind in ("mlp_gelu", "mlp_swiglu") and w.dtype == "bf16"
 
 
 def backward_mode(w, recompute):
@@ -804,7 +804,8 @@ def main():
         dY = workloads.to_device(dY_host, d["X"].dtype)
         bmode = backward_mode(w, args.recompute)
         if bmode == "stored":  # one training forward before the timed region writes Z
-            Zst = torch.empty((w.T, w.F), dtype=d["X"].dtype, device=d["X"].device)
+            zw = 2 * w.F if w.kind == "mlp_swiglu" else w.F  # SwiGLU: [gate | up] per shard
+            Zst = torch.empty((w.T, zw), dtype=d["X"].dtype, device=d["X"].device)
             tp.mlp_forward(d["X"], d["A"], d["a"], d["B"], d["b"], w.N, act=workloads.act_of(w), Z=Zst)
     if args.sp_entry:
         # X holds the n_slices sequence slices of the sublayer input; each step

@@ -209,13 +209,15 @@ typedef struct {
   const void* b;    /* [H] row bias or NULL (added once, after the sum)         */
   void* Y;          /* [T x H], or [T/n_slices x H] when slice >= 0             */
   int n_slices, slice;
-  void* Z;          /* [T x F] (ld F) or NULL.  When set (bf16, activation GELU or
-                       NONE), the forward also writes the range's pre-activation
-                       Z_i = X A_i^T + a_i (shard i = columns i*F/N..), rounded
-                       to bf16 once, so that tp_mlp_backward can take it instead
-                       of recomputing it (training keeps the activation's input).
-                       The fused narrow-hidden kernel keeps its intermediate on
-                       chip, so asking for Z selects the two-GEMM path there. */
+  void* Z;          /* [T x F] (ld F), SwiGLU [T x 2F] (ld 2F), or NULL.  When
+                       set (bf16), the forward also writes the range's
+                       pre-activation Z_i = X A_i^T + a_i (shard i = columns
+                       i*F/N.., SwiGLU: columns 2i*F/N.. holding [gate | up]
+                       of shard i), rounded to bf16 once, so that
+                       tp_mlp_backward can take it instead of recomputing it
+                       (training keeps the activation's input).  The fused
+                       narrow-hidden kernel keeps its intermediate on chip, so
+                       asking for Z selects the two-GEMM path there. */
 } tp_mlp_desc;
 
 /* Whole attention sublayer over shards [shard_begin, shard_begin + shard_count).
@@ -349,9 +351,10 @@ typedef struct {
                        the T/n_slices rows r*T/n_slices ..), the backward of the
                        sequence-parallel all-gather ("张量并行", Megatron-SP
                        section); slice = -1 writes every slice          */
-  const void* Z;   /* [T x F] dt (ld F) or NULL: the forward's pre-activation
-                      (tp_mlp_desc.Z), read for the range's columns instead of
-                      recomputing X A_i^T + a_i; GELU or NONE only            */
+  const void* Z;   /* [T x F] dt (ld F), SwiGLU [T x 2F] (ld 2F), or NULL: the
+                      forward's pre-activation (tp_mlp_desc.Z, same layout),
+                      read for the range's columns instead of recomputing
+                      X A_i^T + a_i                                            */
 } tp_mlp_bwd_desc;
 
 /* Workspace bytes for tp_mlp_backward (0 when the descriptor is invalid).

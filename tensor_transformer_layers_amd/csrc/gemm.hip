@@ -73,14 +73,14 @@ struct G {
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int KK = BK / 16;
-  static constexpr int OUT_N = EPI == EPI_SWIGLU ? BN / 2 : BN;
+  static constexpr int OUT_N = is_swiglu_fwd(EPI) ? BN / 2 : BN;
   static_assert(IA >= 1 && IB >= 1 && BM % (4 * RPI) == 0 && BN % (4 * RPI) == 0, "load split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(S >= 2 && (S - 2) * GROUP < 64, "vmcnt range");
   static_assert((32 >> SH) % CPR == 0, "swizzle must repeat every 32 rows");
-  static_assert(EPI != EPI_SWIGLU || (TN % 2 == 0 && (BN / 4) % 32 == 0), "SwiGLU halves");
+  static_assert(!is_swiglu_fwd(EPI) || (TN % 2 == 0 && (BN / 4) % 32 == 0), "SwiGLU halves");
   static_assert(!(AKO || BKO) || (BK == 64 && (BM == 128 || BM == 256) && (BN == 128 || BN == 256) &&
-                                  EPI != EPI_SWIGLU && EPI != EPI_GELU_FUSED), "K-outer operands");
+                                  !is_swiglu_fwd(EPI) && EPI != EPI_GELU_FUSED), "K-outer operands");
 };
 
 // K-outer operand tiles in LDS: k row r of a tile (BMN columns, 2*BMN bytes)
@@ -206,7 +206,7 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
   const bf16* const Bb = static_cast<const bf16*>(p.B) + bz * p.sB + (int64_t)n0 * p.ldb;
   __amdgpu_buffer_rsrc_t rB;
   int b_row0;  // first B-tile row this wave loads, relative to its buffer
-  if constexpr (C::EPI == EPI_SWIGLU) {
+  if constexpr (is_swiglu_fwd(C::EPI)) {
     const uint32_t rows = (uint32_t)min(C::BN / 2, p.N - n0);
     const bool up = w >= 2;  // waves 0,1 load the gate half, waves 2,3 the up half
     rB = make_rsrc(up ? Bb + p.upOff : Bb, rows * (uint32_t)p.ldb * 2u);
@@ -311,7 +311,7 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
   // only, so one per-lane offset per (stage, k-step) covers every subtile; the
   // subtile itself is a compile-time immediate.
   const int fsw = swz<C>(l32);
-  const int b_wave_row = C::EPI == EPI_SWIGLU ? wn * (C::BN / 4) : wn * C::WN;
+  const int b_wave_row = is_swiglu_fwd(C::EPI) ? wn * (C::BN / 4) : wn * C::WN;
   // relative to the stage's array (one array: to smem0, stage 1 at + STAGE_BYTES)
   int foA[2][C::KK], foB[2][C::KK];
 #pragma unroll
@@ -323,7 +323,7 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
       foB[st][kk] = f + C::A_BYTES + b_wave_row * (C::BK * 2);
     }
   auto brow = [](int jn) -> int {  // B-tile row of subtile jn, relative to the wave's first row
-    if constexpr (C::EPI == EPI_SWIGLU)
+    if constexpr (is_swiglu_fwd(C::EPI))
       return jn < C::TN / 2 ? jn * 32 : C::BN / 2 + (jn - C::TN / 2) * 32;
     else
       return jn * 32;
@@ -528,7 +528,7 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
     // waves 0, 1 stage through the first operand stage, waves 2, 3 the second
     char* const ep = stage(w >> 1) + (w & 1) * (C::WM * 256);
     static_assert(2 * C::WM * 256 <= C::STAGE_BYTES, "epilogue staging fits the operand stages");
-    constexpr bool SWI = MODE == EPI_SWIGLU;
+    constexpr bool SWI = is_swiglu_fwd(MODE);
   #pragma unroll
     for (int h = 0; h < C::TN / 2; ++h) {
       // GELU' epilogue: the pre-activations of this phase's rows are read in
@@ -591,6 +591,24 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
               __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(dst));
             else
               for (int e = 0; e < 4 && n + e < p.N; ++e) dst[e] = o[e];
+            if constexpr (MODE == EPI_SWIGLU_Z) {  // the pre-activations, for the backward: [gate | up]
+              bf16x4 zg, zu;
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                zg[e] = to_bf16(gv[e]);
+                zu[e] = to_bf16(uv[e]);
+              }
+              bf16* zdst = static_cast<bf16*>(p.C2) + bz * p.sC2 + (int64_t)m * p.ldc2 + n;
+              if (n + 3 < p.N) {
+                __builtin_nontemporal_store(zg, reinterpret_cast<bf16x4*>(zdst));
+                __builtin_nontemporal_store(zu, reinterpret_cast<bf16x4*>(zdst + p.N));
+              } else {
+                for (int e = 0; e < 4 && n + e < p.N; ++e) {
+                  zdst[e] = zg[e];
+                  zdst[p.N + e] = zu[e];
+                }
+              }
+            }
           }
         }
       } else if constexpr (MODE == EPI_GELU_BWD) {
@@ -970,7 +988,7 @@ hipError_t launch_bf16_epi(const GemmParams& p, hipStream_t s) {
   // 256x256 tiles (128x128 per wave) when they fill every CU at least once;
   // smaller problems take 128x128 tiles, two workgroups per CU.
   constexpr int kCUs = 256;
-  const int out256 = (EPI == EPI_SWIGLU) ? 128 : 256;
+  const int out256 = is_swiglu_fwd(EPI) ? 128 : 256;
   const int64_t big = (int64_t)((p.M + 255) / 256) * ((p.N + out256 - 1) / out256) * p.batch;
   // The GELU' epilogue reads a bf16 tile of Z per output tile; with a short
   // K (measured on the 16384 x 2048 x 512 product: 120 us on 256x256 tiles,
@@ -1018,6 +1036,7 @@ hipError_t launch_gemm_bf16(const GemmParams& p, Epilogue epi, hipStream_t s) {
     case EPI_GELU_Z: return launch_bf16_epi<EPI_GELU_Z>(p, s);
     case EPI_PARTIAL: return launch_bf16_epi<EPI_PARTIAL>(p, s);
     case EPI_SWIGLU: return launch_bf16_epi<EPI_SWIGLU>(p, s);
+    case EPI_SWIGLU_Z: return launch_bf16_epi<EPI_SWIGLU_Z>(p, s);
     case EPI_GELU_BWD: return launch_bf16_epi<EPI_GELU_BWD>(p, s);
     case EPI_CE_STATS: return launch_bf16_epi<EPI_CE_STATS>(p, s);
     case EPI_SWIGLU_BWD: return launch_bf16_epi<EPI_SWIGLU_BWD>(p, s);

@@ -338,8 +338,8 @@ tp_status validate_mlp(const tp_mlp_desc* d, MlpShape* sh) {
   }
   if (d->Z) {
     if (d->dt != TP_BF16) return fail(TP_ERR_DTYPE, "the stored pre-activation Z is written by the bf16 path only");
-    if (d->act == TP_ACT_SWIGLU) return fail(TP_ERR_SHAPE, "no stored pre-activation Z for SwiGLU");
-    TP_TRY(check_matrix("Z", d->Z, d->T, d->F, d->F, vec));
+    const int64_t zw = d->act == TP_ACT_SWIGLU ? 2 * d->F : d->F;  // SwiGLU: [gate | up] per shard
+    TP_TRY(check_matrix("Z", d->Z, d->T, zw, zw, vec));
   }
   if (d->T > kIntMax) return fail(TP_ERR_SHAPE, "T exceeds 2^31-1");
   sh->Fs = Fs;
@@ -454,7 +454,7 @@ bool bwd_direct_ok(const tp_mlp_bwd_desc* d, int64_t zs, int64_t Fz, int64_t Fc,
   const int64_t kc = d->T / S;
   const int64_t lim = (int64_t)0xFFFFFFFF - 1024;
   auto fits = [&](int64_t k, int64_t ld) { return (k - 1) * ld * 2 + 512 <= lim; };
-  const int64_t wide = std::max(std::max(Fz, Fc), d->F);  // widest ld of dZ / act(Z) / a stored Z
+  const int64_t wide = std::max(std::max(Fz, Fc), 2 * d->F);  // widest ld of dZ / act(Z) / a stored Z
   if (!fits(d->H, d->F) || !fits(zs, d->H) || !fits(kc, d->H) || !fits(kc, wide)) return false;
   *splits = S;
   return true;
@@ -534,8 +534,8 @@ tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
     if (!aligned16(d->dX)) return fail(TP_ERR_ALIGN, "dX is not 16-byte aligned");
   }
   if (d->Z) {
-    if (swiglu) return fail(TP_ERR_SHAPE, "no stored pre-activation Z for SwiGLU");
-    TP_TRY(check_matrix("Z", d->Z, d->T, d->F, d->F, vec));
+    const int64_t zw = swiglu ? 2 * d->F : d->F;  // SwiGLU: [gate | up] per shard
+    TP_TRY(check_matrix("Z", d->Z, d->T, zw, zw, vec));
   }
   if (d->T > kIntMax || d->F > kIntMax) return fail(TP_ERR_SHAPE, "size exceeds 2^31-1");
   const size_t T = (size_t)d->T, H = (size_t)d->H, fc = (size_t)Fc, fz = (size_t)sh->Fz, es = esize(d->dt);
@@ -632,8 +632,8 @@ tp_status bwd_direct(hipStream_t s, const tp_mlp_bwd_desc* d, const BwdShape& sh
     const void* Zp = Z;
     int64_t zld = sh.zld;
     if (d->Z) {
-      Zp = static_cast<const char*>(d->Z) + (size_t)i0 * Fs * es;
-      zld = F;
+      Zp = static_cast<const char*>(d->Z) + (size_t)i0 * zs * es;  // SwiGLU: [gate | up] blocks
+      zld = swiglu ? 2 * F : F;
     } else {
       tp::GemmParams zg = gemm(d->X, H, 0, A_r, H, 0, Z, sh.zld, 0, T, Fz, H, 1);
       zg.bias = a_r;
@@ -643,8 +643,8 @@ tp_status bwd_direct(hipStream_t s, const tp_mlp_bwd_desc* d, const BwdShape& sh
       // per shard: dH = dY B_i; [dG | dU] and SiLU(G) U from the stored [G | U]
       tp::GemmParams dg = gemm(d->dY, H, 0, B_r, F, Fs, dZ, sh.zld, zs, T, Fs, H, c);
       dg.b_ko = 1;
-      dg.aux = Z;
-      dg.ldaux = sh.zld;
+      dg.aux = Zp;
+      dg.ldaux = zld;
       dg.sAux = zs;
       dg.upOff = Fs;
       dg.C2 = Hs;
@@ -1045,7 +1045,9 @@ tp_status mlp_rows(hipStream_t s, const tp_mlp_desc* d, const MlpShape& sh, void
   // The stored pre-activation's rows of this block, the range's columns:
   // without an activation it is the intermediate itself (written there, read
   // from there), with GELU a second output of the column GEMM.
-  void* Zr = d->Z ? static_cast<char*>(d->Z) + ((size_t)row0 * d->F + (size_t)i0 * Fs) * es : nullptr;
+  const bool swiglu = d->act == TP_ACT_SWIGLU;
+  const int64_t zw = swiglu ? 2 * d->F : d->F, zs = swiglu ? 2 * Fs : Fs;  // Z row width, shard block width
+  void* Zr = d->Z ? static_cast<char*>(d->Z) + ((size_t)row0 * zw + (size_t)i0 * zs) * es : nullptr;
   const bool z_is_h = Zr && d->act == TP_ACT_NONE;
   void* Hc = z_is_h ? Zr : Hs;
   const int64_t hld = z_is_h ? d->F : sh.h_ld, hstride = z_is_h ? Fs : T * sh.h_ld;
@@ -1059,11 +1061,11 @@ tp_status mlp_rows(hipStream_t s, const tp_mlp_desc* d, const MlpShape& sh, void
   }
   col.upOff = Fs * H;
   tp::Epilogue ce = d->act == TP_ACT_SWIGLU ? tp::EPI_SWIGLU : d->act == TP_ACT_GELU ? tp::EPI_GELU : tp::EPI_STORE;
-  if (Zr && d->act == TP_ACT_GELU) {
-    ce = tp::EPI_GELU_Z;
+  if (Zr && d->act != TP_ACT_NONE) {  // GELU or SwiGLU: the pre-activation is a second output
+    ce = swiglu ? tp::EPI_SWIGLU_Z : tp::EPI_GELU_Z;
     col.C2 = Zr;
-    col.ldc2 = d->F;
-    col.sC2 = Fs;
+    col.ldc2 = zw;
+    col.sC2 = zs;
   }
   TP_TRY(hip_status(launch("mlp_column_gemm", d->dt, col, ce, s), "mlp column launch"));
 
@@ -1313,8 +1315,8 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
   const void* Zp = Z;
   int64_t zld = sh.zld;
   if (d->Z) {
-    Zp = static_cast<const char*>(d->Z) + (size_t)i0 * Fs * es;
-    zld = F;
+    Zp = static_cast<const char*>(d->Z) + (size_t)i0 * zs * es;  // SwiGLU: [gate | up] blocks
+    zld = swiglu ? 2 * F : F;
   } else {
     tp::GemmParams zg = gemm(d->X, H, 0, A_r, H, 0, Z, sh.zld, 0, T, Fz, H, 1);
     zg.bias = a_r;
@@ -1323,8 +1325,8 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
   if (swiglu) {
     // per shard: dH = dY B_i; [dG | dU] and H = SiLU(G) U from the stored [G | U]
     tp::GemmParams dg = gemm(d->dY, H, 0, BT, H, Fs * H, dZ, sh.zld, zs, T, Fs, H, c);
-    dg.aux = Z;
-    dg.ldaux = sh.zld;
+    dg.aux = Zp;
+    dg.ldaux = zld;
     dg.sAux = zs;
     dg.upOff = Fs;
     dg.C2 = Hs;

@@ -36,7 +36,11 @@ enum Epilogue : int {
   EPI_SWIGLU_BWD = 6,  // acc = dH; G, U = aux at n, n + upOff: C[n] = dG, C[n + upOff] = dU, C2 = SiLU(G)*U
   EPI_GELU_FUSED = 7,  // two passes: Z = A B^T + bias, then dH = A2 B2^T; C = dH * GELU'(Z), C2 = GELU(Z)
   EPI_GELU_Z = 8,      // C = GELU(acc + bias), C2 = acc + bias (the pre-activation, kept for the backward); bf16
+  EPI_SWIGLU_Z = 9,    // EPI_SWIGLU, and the pre-activations to C2: gate at column n, up at n + N; bf16
 };
+
+// The forward SwiGLU epilogues (gate and up rows side by side in one tile).
+constexpr bool is_swiglu_fwd(int epi) { return epi == EPI_SWIGLU || epi == EPI_SWIGLU_Z; }
 
 // EPI_CE_STATS: problem z of the batch is vocab shard ce_shard0 + z, whose
 // column n is vocab id (ce_shard0 + z)*N + n; ids >= ce_V are padding.  For

@@ -554,7 +554,8 @@ def alloc_workspace(nbytes: int, device):
 def mlp_forward(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, ws=None, shard_begin=0, shard_count=None,
                 n_slices=1, slice=-1, Z=None, stream=None):
     """Whole MLP sublayer; returns (Y, workspace).  Y is None for partial
-    shard ranges (the partials are in the workspace slab).  Z ([T x F], X's
+    shard ranges (the partials are in the workspace slab).  Z ([T x F], or
+    [T x 2F] for SwiGLU with shard i's [gate | up] in columns 2i*F/N..; X's
     dtype, bf16 only) or None: also write the range's pre-activation there,
     for mlp_backward(..., Z=Z)."""
     torch = _torch()
@@ -567,7 +568,8 @@ def mlp_forward(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, ws=None, shard_begin=
     if Y is not None:
         _expect("Y", Y, (rows, H), X.dtype, X.device)
     if Z is not None:
-        _expect("Z", Z, (T, B.shape[1]), X.dtype, X.device)
+        zw = B.shape[1] * (2 if act == TP_ACT_SWIGLU else 1)
+        _expect("Z", Z, (T, zw), X.dtype, X.device)
     d = mlp_desc(X, A, a, B, b, N, act, Y, shard_begin, cnt, n_slices, slice, Z=Z)
     need = tp_mlp_workspace_size(d)
     if need == 0:
@@ -603,8 +605,8 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
     [T/n_slices x H]), dA (fp32, A's shape: [F x H], or the [2F x H] fused
     blocks for SwiGLU), da (fp32 [F] or None; always None for SwiGLU), dB
     (fp32 [H x F]) and db (fp32 [H] or None); missing entries are allocated.
-    Z: the forward's stored pre-activation ([T x F], X's dtype; GELU or NONE)
-    to use instead of recomputing it, or None."""
+    Z: the forward's stored pre-activation ([T x F], SwiGLU [T x 2F]; X's
+    dtype) to use instead of recomputing it, or None."""
     torch = _torch()
     _same_dtype(X, A=A, a=a, B=B, dY=dY)
     T, H, F = _check_mlp(X, A, a, B, None, act)
@@ -635,7 +637,7 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
     if g["db"] is not None:
         _expect("db", g["db"], (H,), f32, dev)
     if Z is not None:
-        _expect("Z", Z, (T, F), X.dtype, dev)
+        _expect("Z", Z, (T, 2 * F if act == TP_ACT_SWIGLU else F), X.dtype, dev)
     d = MlpBwdDesc()
     d.dt = _dt(X)
     d.act = act

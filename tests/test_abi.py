@@ -85,7 +85,7 @@ def test_mlp_workspace_size_is_host_only(L):
     (dict(H=500), tp.TP_ERR_ALIGN, "hidden H=500"),
     (dict(Y=None), tp.TP_ERR_NULL, "Y is NULL"),
     (dict(Z=FAKE, dt=tp.TP_F32), tp.TP_ERR_DTYPE, "bf16 path only"),
-    (dict(Z=FAKE, act=tp.TP_ACT_SWIGLU, a=None), tp.TP_ERR_SHAPE, "no stored pre-activation Z for SwiGLU"),
+    (dict(Z=FAKE + 4, act=tp.TP_ACT_SWIGLU, a=None), tp.TP_ERR_ALIGN, "Z is not 16-byte aligned"),
     (dict(Z=FAKE + 8), tp.TP_ERR_ALIGN, "Z is not 16-byte aligned"),
 ])
 def test_mlp_validation(L, kw, status, needle):
@@ -262,7 +262,7 @@ def test_mlp_backward_workspace_size_is_host_only(L):
     (dict(dB=FAKE + 4), tp.TP_ERR_ALIGN, "dB is not 16-byte aligned"),
     (dict(da=FAKE + 4), tp.TP_ERR_ALIGN, "da is not 16-byte aligned"),
     (dict(shard_begin=3, shard_count=2), tp.TP_ERR_SHAPE, "shard range"),
-    (dict(Z=FAKE, act=tp.TP_ACT_SWIGLU, a=None, da=None), tp.TP_ERR_SHAPE, "no stored pre-activation Z for SwiGLU"),
+    (dict(Z=FAKE + 4, act=tp.TP_ACT_SWIGLU, a=None, da=None), tp.TP_ERR_ALIGN, "Z is not 16-byte aligned"),
     (dict(Z=FAKE + 4), tp.TP_ERR_ALIGN, "Z is not 16-byte aligned"),
 ])
 def test_mlp_backward_rejects_before_launch(L, kw, status, needle):
@@ -280,6 +280,9 @@ def test_mlp_backward_swiglu_workspace(L):
     gelu = tp.tp_mlp_backward_workspace_size(_bwd(a=None, da=None, Z=FAKE))
     swi = tp.tp_mlp_backward_workspace_size(_bwd(act=tp.TP_ACT_SWIGLU, a=None, da=None))
     assert swi == gelu + 3 * T * F * 2
+    # with the forward's [gate | up] pre-activation supplied, no recomputed Z slab
+    swi_z = tp.tp_mlp_backward_workspace_size(_bwd(act=tp.TP_ACT_SWIGLU, a=None, da=None, Z=FAKE))
+    assert swi_z == swi - T * 2 * F * 2
 
 
 def test_mlp_backward_partial_range_needs_no_dx(L):

@@ -50,7 +50,7 @@ def test_backward_kernel_flops_cover_the_counted_work(k):
     fz = 2 * w.F if w.kind == "mlp_swiglu" else w.F
     recompute = 2.0 * w.T * w.H * fz
     assert abs(total - recompute - bench.backward_flops(w, w.N)) <= 1e-9 * total
-    assert bench.backward_mode(w, False) == ("recompute" if k == 3 else "stored")
+    assert bench.backward_mode(w, False) == "stored"
     if bench.backward_mode(w, False) == "stored":
         order = bench.backward_launch_order(w, "stored")
         assert "bwd_recompute_gemm" not in order and "bwd_fused_gemm" not in order

@@ -13,6 +13,8 @@ ABI (gfx950 GPU required).
     no activation): the forward's column product and the recomputation
     accumulate the same products in the same order and round once.
   * A shard range writes its own columns of Z and no others.
+  * SwiGLU: Z holds each shard's [gate | up] pre-activations; the same
+    checks, with the backward bit for bit equal to the recomputing one.
 """
 import sys
 
@@ -128,3 +130,60 @@ def test_stored_preactivation_shard_range():
     torch.cuda.synchronize()
     for k in ("dA", "da", "dB", "db"):
         assert torch.equal(g0[k], g1[k]), k
+
+
+# ------------------------------------------------------------------ SwiGLU
+def _swiglu_host(T, H, I, seed):
+    rng = np.random.default_rng(seed)
+    r = lambda shape, s: inputs.round_to_dtype((rng.standard_normal(shape) * s).astype(np.float32), "bf16")
+    return {"X": r((T, H), 1.0), "Wg": r((I, H), 0.05), "Wu": r((I, H), 0.05), "Wd": r((H, I), 0.05),
+            "dY": r((T, H), 1.0)}
+
+
+def _fused_blocks(Wg, Wu, N):
+    """Per-shard [gate | up] row blocks, as the forward takes them."""
+    s = Wg.shape[0] // N
+    return np.concatenate([np.concatenate([Wg[i * s:(i + 1) * s], Wu[i * s:(i + 1) * s]]) for i in range(N)])
+
+
+@pytest.mark.parametrize("T,H,I,N", [
+    (264, 136, 4 * 40, 4),     # the backward transposes its operands
+    (1024, 256, 4 * 96, 4),    # the backward reads its operands as stored
+])
+def test_stored_preactivation_swiglu(T, H, I, N):
+    """SwiGLU: the forward writes each shard's [gate | up] pre-activations
+    (against the fp64 products, one bf16 rounding), asking for them leaves Y
+    unchanged bit for bit, and the backward that takes them equals the
+    recomputing one bit for bit (the recomputation runs the same products in
+    the same k order) and the oracle within the bf16 bound."""
+    say(f"stored Z swiglu T={T} H={H} I={I} N={N}")
+    h = _swiglu_host(T, H, I, seed=3 * T + H + I)
+    A = dev(_fused_blocks(h["Wg"], h["Wu"], N))
+    X, Wd, dY = dev(h["X"]), dev(h["Wd"]), dev(h["dY"])
+    Z = torch.empty((T, 2 * I), dtype=torch.bfloat16, device=DEV)
+    Y0, _ = tp.mlp_forward(X, A, None, Wd, None, N, act=tp.TP_ACT_SWIGLU)
+    Y1, _ = tp.mlp_forward(X, A, None, Wd, None, N, act=tp.TP_ACT_SWIGLU, Z=Z)
+    torch.cuda.synchronize()
+    assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
+    Is = I // N
+    x = h["X"].astype(np.float64)
+    zref = np.concatenate([np.concatenate([x @ h["Wg"][i * Is:(i + 1) * Is].astype(np.float64).T,
+                                           x @ h["Wu"][i * Is:(i + 1) * Is].astype(np.float64).T], axis=1)
+                           for i in range(N)], axis=1)
+    e = err(_np(Z), zref)
+    say(f"  Z err={e:.3e}")
+    assert e <= Z_TOL
+
+    g0, _ = tp.mlp_backward(X, A, None, Wd, dY, N, act=tp.TP_ACT_SWIGLU, need_db=True)
+    g1, _ = tp.mlp_backward(X, A, None, Wd, dY, N, act=tp.TP_ACT_SWIGLU, need_db=True, Z=Z)
+    torch.cuda.synchronize()
+    for k in ("dX", "dA", "dB", "db"):
+        assert torch.equal(g0[k], g1[k]), f"{k}: stored Z differs from the recomputation"
+    ref = R.mlp_swiglu_backward(h["X"], h["Wg"], h["Wu"], h["Wd"], h["dY"])
+    blocks = _np(g1["dA"]).reshape(N, 2, Is, H)
+    got = {"dX": _np(g1["dX"]), "dWg": blocks[:, 0].reshape(-1, H), "dWu": blocks[:, 1].reshape(-1, H),
+           "dWd": _np(g1["dB"]), "db": _np(g1["db"])}
+    for k in ("dX", "dWg", "dWu", "dWd", "db"):
+        e = err(got[k], ref[k])
+        say(f"  {k}: err={e:.3e}")
+        assert e <= BF16_TOL, k
