@@ -990,14 +990,16 @@ hipError_t launch_bf16_epi(const GemmParams& p, hipStream_t s) {
   constexpr int kCUs = 256;
   const int out256 = is_swiglu_fwd(EPI) ? 128 : 256;
   const int64_t big = (int64_t)((p.M + 255) / 256) * ((p.N + out256 - 1) / out256) * p.batch;
-  // The GELU' epilogue reads a bf16 tile of Z per output tile; with a short
-  // K (measured on the 16384 x 2048 x 512 product: 120 us on 256x256 tiles,
-  // 95-99 us on 128x128) two 128x128 workgroups per CU hide one's epilogue
-  // behind the other's MFMAs better than one 256x256 workgroup does.  The
-  // SwiGLU-backward epilogue (two loads, three stores per element) gains the
-  // same way even at K = 4096 (3.96 -> 3.80 ms on the 32768 x 8 x 1376 x 4096
-  // product).
-  const bool short_k_load_epilogue = (EPI == EPI_GELU_BWD && p.K <= 2048) || EPI == EPI_SWIGLU_BWD;
+  // The GELU' and SwiGLU-backward epilogues read bf16 tiles of Z beside the
+  // accumulators; with a short K (measured on the 16384 x 2048 x 512 GELU'
+  // product: 120 us on 256x256 tiles, 95-99 us on 128x128) two 128x128
+  // workgroups per CU hide one's epilogue behind the other's MFMAs better
+  // than one 256x256 workgroup does.  The SwiGLU-backward product
+  // (32768 x 8 x 1376 x 4096) gains the same way at any K when B is
+  // K-contiguous (3.96 -> 3.80 ms), but with B read K-outer it is faster on
+  // 256x256 tiles (3.79 vs 3.92 ms).
+  const bool short_k_load_epilogue =
+      (EPI == EPI_GELU_BWD && p.K <= 2048) || (EPI == EPI_SWIGLU_BWD && (p.K <= 2048 || !p.b_ko));
   if (big >= kCUs && !short_k_load_epilogue)
     return launch_bf16_cfg<G<256, 256, 64, 2, kGemmSwizzleShift, EPI, AKO, BKO>>(p, s);
   return launch_bf16_cfg<G<128, 128, 64, 2, kGemmSwizzleShift, EPI, AKO, BKO>>(p, s);
