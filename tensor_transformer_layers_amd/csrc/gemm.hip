@@ -554,6 +554,32 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
       };
       bf16x4 zc[ZB];
       if constexpr (MODE == EPI_GELU_BWD) load_z(0, zc);
+      // SwiGLU backward: the stored gate and up of the phase's rows, in blocks
+      // of GB rows per lane, each block issued one block ahead of its use
+      constexpr int GB = ZB < 8 ? ZB : 8;
+      auto load_gu = [&](int blk, bf16x4* g, bf16x4* u) {
+        const bf16* const gb = static_cast<const bf16*>(p.aux) + bz * p.sAux;
+  #pragma unroll
+        for (int j = 0; j < GB; ++j) {
+          const int m = m0 + wm * C::WM + (blk + j) * 4 + (lane >> 4);
+          g[j] = bf16x4{};
+          u[j] = bf16x4{};
+          if (m < p.M && zc_n < p.N) {
+            const bf16* zp = gb + (int64_t)m * p.ldaux + zc_n;
+            if (zc_n + 3 < p.N) {
+              g[j] = *reinterpret_cast<const bf16x4*>(zp);
+              u[j] = *reinterpret_cast<const bf16x4*>(zp + p.upOff);
+            } else {
+              for (int e = 0; e < 4 && zc_n + e < p.N; ++e) {
+                g[j][e] = zp[e];
+                u[j][e] = zp[e + p.upOff];
+              }
+            }
+          }
+        }
+      };
+      bf16x4 gc[MODE == EPI_SWIGLU_BWD ? GB : 1], uc[MODE == EPI_SWIGLU_BWD ? GB : 1];
+      if constexpr (MODE == EPI_SWIGLU_BWD) load_gu(0, gc, uc);
   #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int j = SWI ? h + half * (C::TN / 2) : 2 * h + half;
@@ -657,52 +683,54 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
         //   dG = dH U SiLU'(G),  dU = dH SiLU(G),  H = SiLU(G) U
         // with SiLU'(g) = s (1 + g (1 - s)), s = sigmoid(g) (hardware exp and
         // reciprocal).  16 lanes per row, 4 features each.
+        static_assert((C::WM / 4) % GB == 0, "row blocks");
         const int c = lane & 15;
-        const int n = n0 + wn * C::WN + 64 * h + 4 * c;
-        const bf16* const zb = static_cast<const bf16*>(p.aux) + bz * p.sAux;
+        const int n = zc_n;
         bf16* const cb = static_cast<bf16*>(outC) + bz * out_sC;
         bf16* const hb = static_cast<bf16*>(p.C2) + bz * p.sC2;
-  #pragma unroll 4
-        for (int it = 0; it < C::WM / 4; ++it) {
-          const int r = it * 4 + (lane >> 4);
-          const int m = m0 + wm * C::WM + r;
-          const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
-          if (m < p.M && n < p.N) {
-            const bf16* zp = zb + (int64_t)m * p.ldaux + n;
-            bf16x4 g4 = {}, u4 = {};
-            const bool full = n + 3 < p.N;
-            if (full) {
-              g4 = *reinterpret_cast<const bf16x4*>(zp);
-              u4 = *reinterpret_cast<const bf16x4*>(zp + p.upOff);
-            } else {
-              for (int e = 0; e < 4 && n + e < p.N; ++e) {
-                g4[e] = zp[e];
-                u4[e] = zp[e + p.upOff];
-              }
-            }
-            bf16x4 og, ou, oh;
+  #pragma unroll 1
+        for (int blk = 0; blk < C::WM / 4; blk += GB) {
+          bf16x4 gn[GB], un[GB];
+          if (blk + GB < C::WM / 4) {
+            load_gu(blk + GB, gn, un);
+          } else {
+            for (int j = 0; j < GB; ++j) gn[j] = un[j] = bf16x4{};
+          }
   #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float g = static_cast<float>(g4[e]), u = static_cast<float>(u4[e]);
-              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-              const float si = g * sg;
-              og[e] = to_bf16(v[e] * u * (sg * fmaf(g, 1.0f - sg, 1.0f)));
-              ou[e] = to_bf16(v[e] * si);
-              oh[e] = to_bf16(si * u);
-            }
-            bf16* const dg = cb + (int64_t)m * out_ldc + n;
-            bf16* const hh = hb + (int64_t)m * p.ldc2 + n;
-            if (full) {
-              __builtin_nontemporal_store(og, reinterpret_cast<bf16x4*>(dg));
-              __builtin_nontemporal_store(ou, reinterpret_cast<bf16x4*>(dg + p.upOff));
-              __builtin_nontemporal_store(oh, reinterpret_cast<bf16x4*>(hh));
-            } else {
-              for (int e = 0; e < 4 && n + e < p.N; ++e) {
-                dg[e] = og[e];
-                dg[e + p.upOff] = ou[e];
-                hh[e] = oh[e];
+          for (int j = 0; j < GB; ++j) {
+            const int r = (blk + j) * 4 + (lane >> 4);
+            const int m = m0 + wm * C::WM + r;
+            const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 256 + ((c ^ (r & 15)) << 4));
+            if (m < p.M && n < p.N) {
+              bf16x4 og, ou, oh;
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float g = static_cast<float>(gc[j][e]), u = static_cast<float>(uc[j][e]);
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+                const float si = g * sg;
+                og[e] = to_bf16(v[e] * u * (sg * fmaf(g, 1.0f - sg, 1.0f)));
+                ou[e] = to_bf16(v[e] * si);
+                oh[e] = to_bf16(si * u);
+              }
+              bf16* const dg = cb + (int64_t)m * out_ldc + n;
+              bf16* const hh = hb + (int64_t)m * p.ldc2 + n;
+              if (n + 3 < p.N) {
+                __builtin_nontemporal_store(og, reinterpret_cast<bf16x4*>(dg));
+                __builtin_nontemporal_store(ou, reinterpret_cast<bf16x4*>(dg + p.upOff));
+                __builtin_nontemporal_store(oh, reinterpret_cast<bf16x4*>(hh));
+              } else {
+                for (int e = 0; e < 4 && n + e < p.N; ++e) {
+                  dg[e] = og[e];
+                  dg[e + p.upOff] = ou[e];
+                  hh[e] = oh[e];
+                }
               }
             }
+          }
+  #pragma unroll
+          for (int j = 0; j < GB; ++j) {
+            gc[j] = gn[j];
+            uc[j] = un[j];
           }
         }
       } else if constexpr (MODE == EPI_CE_STATS) {
@@ -997,7 +1025,7 @@ hipError_t launch_bf16_epi(const GemmParams& p, hipStream_t s) {
   // than one 256x256 workgroup does.  The SwiGLU-backward product
   // (32768 x 8 x 1376 x 4096) gains the same way at any K when B is
   // K-contiguous (3.96 -> 3.80 ms), but with B read K-outer it is faster on
-  // 256x256 tiles (3.79 vs 3.92 ms).
+  // 256x256 tiles (3.22 vs 3.65 ms).
   const bool short_k_load_epilogue =
       (EPI == EPI_GELU_BWD && p.K <= 2048) || (EPI == EPI_SWIGLU_BWD && (p.K <= 2048 || !p.b_ko));
   if (big >= kCUs && !short_k_load_epilogue)
