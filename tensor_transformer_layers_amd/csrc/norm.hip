@@ -199,12 +199,15 @@ __global__ __launch_bounds__(NT) void norm_split_stats_kernel(NormSplitParams p)
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int part = wv % WPR;
-  const int64_t row = (int64_t)blockIdx.x * kRows + wv / WPR;  // (shard, token) slice
-  const int64_t rows = (int64_t)p.shards * p.T;
-  if (WPR == 1 && row >= rows) return;  // split rows keep every wave for the barriers
-  const bool live = row < rows;
-  const int64_t s = live ? row / p.T : 0;
-  const int64_t t = live ? row - s * p.T : 0;
+  // workgroup -> (block of kRows tokens, shard), every shard of a block
+  // before the next block, so that neighbouring workgroups read neighbouring
+  // memory
+  const int64_t blk = blockIdx.x / p.shards;
+  const int64_t s = blockIdx.x - blk * p.shards;
+  const int64_t t0 = blk * kRows + wv / WPR;
+  if (WPR == 1 && t0 >= p.T) return;  // split rows keep every wave for the barriers
+  const bool live = t0 < p.T;
+  const int64_t t = live ? t0 : 0;
   const int64_t shard = p.shard0 + s;
   const T* const x = static_cast<const T*>(p.X) + t * p.ldx + shard * p.Hs;
   V v[U];
@@ -225,51 +228,73 @@ __global__ __launch_bounds__(NT) void norm_split_stats_kernel(NormSplitParams p)
 
 // Hidden-split norm, second half: one wave per (shard, row) slice folds the
 // row's N statistics in shard order (every shard the same bits), then scales
-// its slice: 16-byte pieces, lanes striding by 1 KB.
-template <typename T, bool LAYER>
+// its slice: 16-byte pieces, lanes striding by 1 KB.  With U > 0 the slice
+// has at most U pieces per lane and every load (all pieces of x, gamma and
+// beta, and the statistics when N <= 8) is issued before the arithmetic.
+template <typename T, int U, bool LAYER>
 __global__ __launch_bounds__(256) void norm_split_apply_kernel(NormSplitParams p) {
   using V = typename Vec<T>::V;
   constexpr int E = Vec<T>::E;
+  constexpr int kMaxN = 8;
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= (int64_t)p.shards * p.T) return;
-  const int64_t s = row / p.T, t = row - s * p.T;
+  // workgroup -> (block of 4 tokens, shard), as in the statistics kernel
+  const int64_t blk = blockIdx.x / p.shards;
+  const int64_t s = blockIdx.x - blk * p.shards;
+  const int64_t t = blk * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;
   const int64_t shard = p.shard0 + s;
   const float2* const st = reinterpret_cast<const float2*>(p.stats) + t;
-  float mean = 0.0f, q;
-  if constexpr (!LAYER) {
-    q = st[0].x;
-    for (int i = 1; i < p.N; ++i) q += st[(int64_t)i * p.T].x;
-  } else {
-    const float c = (float)p.Hs;
-    float n = c;
-    float2 a = st[0];
-    mean = a.x;
-    q = a.y;
-    for (int i = 1; i < p.N; ++i) {
-      a = st[(int64_t)i * p.T];
-      const float n1 = n + c;
-      const float d = a.x - mean;
-      mean = fmaf(d, c / n1, mean);
-      q = q + a.y + d * d * (n * c / n1);
-      n = n1;
-    }
-  }
-  const float scale = __builtin_amdgcn_rsqf(q * p.inv_h + p.eps);
   const T* const x = static_cast<const T*>(p.X) + t * p.ldx + shard * p.Hs;
   T* const y = static_cast<T*>(p.Y) + t * p.ldy + shard * p.Hs;
   const T* const g = static_cast<const T*>(p.gamma) + shard * p.Hs;
   const T* const b = p.beta ? static_cast<const T*>(p.beta) + shard * p.Hs : nullptr;
-  for (int c = lane * E; c < p.Hs; c += 64 * E) {
-    const V xv = *reinterpret_cast<const V*>(x + c);
-    const V gv = *reinterpret_cast<const V*>(g + c);
-    V bv;
-    if (LAYER && b) {
-      bv = *reinterpret_cast<const V*>(b + c);
-    } else {
+  V xs[U > 0 ? U : 1], gs[U > 0 ? U : 1], bs[U > 0 ? U : 1];
+  if constexpr (U > 0) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) bv[e] = static_cast<T>(0.0f);
+    for (int u = 0; u < U; ++u) {
+      const int c = (u * 64 + lane) * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) xs[u][e] = gs[u][e] = bs[u][e] = static_cast<T>(0.0f);
+      if (c < p.Hs) {
+        xs[u] = *reinterpret_cast<const V*>(x + c);
+        gs[u] = *reinterpret_cast<const V*>(g + c);
+        if (LAYER && b) bs[u] = *reinterpret_cast<const V*>(b + c);
+      }
     }
+  }
+  // the N statistics of the token, folded in shard order
+  float mean = 0.0f, q;
+  const float cs = (float)p.Hs;
+  float n = cs;
+  auto merge = [&](float2 a) {
+    if constexpr (!LAYER) {
+      q += a.x;
+    } else {
+      const float n1 = n + cs;
+      const float d = a.x - mean;
+      mean = fmaf(d, cs / n1, mean);
+      q = q + a.y + d * d * (n * cs / n1);
+      n = n1;
+    }
+  };
+  {
+    const float2 a0 = st[0];
+    mean = LAYER ? a0.x : 0.0f;
+    q = LAYER ? a0.y : a0.x;
+  }
+  if (p.N <= kMaxN) {
+    float2 sv[kMaxN];
+#pragma unroll
+    for (int i = 1; i < kMaxN; ++i)
+      if (i < p.N) sv[i] = st[(int64_t)i * p.T];
+#pragma unroll
+    for (int i = 1; i < kMaxN; ++i)
+      if (i < p.N) merge(sv[i]);
+  } else {
+    for (int i = 1; i < p.N; ++i) merge(st[(int64_t)i * p.T]);
+  }
+  const float scale = __builtin_amdgcn_rsqf(q * p.inv_h + p.eps);
+  auto out = [&](const V& xv, const V& gv, const V& bv, int c) {
     V o;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -284,6 +309,26 @@ __global__ __launch_bounds__(256) void norm_split_apply_kernel(NormSplitParams p
         o[e] = f;
     }
     *reinterpret_cast<V*>(y + c) = o;
+  };
+  if constexpr (U > 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = (u * 64 + lane) * E;
+      if (c < p.Hs) out(xs[u], gs[u], bs[u], c);
+    }
+  } else {
+    for (int c = lane * E; c < p.Hs; c += 64 * E) {
+      const V xv = *reinterpret_cast<const V*>(x + c);
+      const V gv = *reinterpret_cast<const V*>(g + c);
+      V bv;
+      if (LAYER && b) {
+        bv = *reinterpret_cast<const V*>(b + c);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) bv[e] = static_cast<T>(0.0f);
+      }
+      out(xv, gv, bv, c);
+    }
   }
 }
 
@@ -298,8 +343,7 @@ hipError_t launch_shape(const NormParams& p, hipStream_t s) {
 template <typename T, int U, int WPR, bool LAYER, int NT = 256>
 hipError_t launch_split_shape(const NormSplitParams& p, hipStream_t s) {
   constexpr int kRows = NT / 64 / WPR;
-  const int64_t rows = (int64_t)p.shards * p.T;
-  const dim3 g((unsigned)((rows + kRows - 1) / kRows)), b(NT);
+  const dim3 g((unsigned)((p.T + kRows - 1) / kRows * p.shards)), b(NT);
   launch_kernel((norm_split_stats_kernel<T, U, WPR, NT, LAYER>), g, b, 0u, s, p);
   return hipGetLastError();
 }
@@ -338,8 +382,18 @@ struct SplitStatsLaunch {
 
 template <typename T, bool LAYER>
 hipError_t launch_split_apply(const NormSplitParams& p, hipStream_t s) {
-  const int64_t rows = (int64_t)p.shards * p.T;
-  launch_kernel((norm_split_apply_kernel<T, LAYER>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0u, s, p);
+  const dim3 g((unsigned)((p.T + 3) / 4 * p.shards)), b(256);
+  const int64_t pieces = (p.Hs + 64 * Vec<T>::E - 1) / (64 * Vec<T>::E);
+  if (pieces <= 1)
+    launch_kernel((norm_split_apply_kernel<T, 1, LAYER>), g, b, 0u, s, p);
+  else if (pieces <= 2)
+    launch_kernel((norm_split_apply_kernel<T, 2, LAYER>), g, b, 0u, s, p);
+  else if (pieces <= 3)
+    launch_kernel((norm_split_apply_kernel<T, 3, LAYER>), g, b, 0u, s, p);
+  else if (pieces <= 4)
+    launch_kernel((norm_split_apply_kernel<T, 4, LAYER>), g, b, 0u, s, p);
+  else
+    launch_kernel((norm_split_apply_kernel<T, 0, LAYER>), g, b, 0u, s, p);
   return hipGetLastError();
 }
 
