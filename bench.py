@@ -704,7 +704,7 @@ def main():
                          "bias gradients of every shard, then the input-gradient reduction)")
     ap.add_argument("--recompute", action="store_true",
                     help="with --backward: recompute the pre-activation X A^T + a in the backward instead of taking "
-                         "the one the forward stored (the GELU bf16 workloads store it; the others always recompute)")
+                         "the one the forward stored (the bf16 GELU and SwiGLU workloads store it; the others always recompute)")
     ap.add_argument("--overlap", type=int, default=0, metavar="K",
                     help="MLP workloads, --share layer: cut the tokens into K row blocks and overlap the reduction "
                          "of block k (on a second stream) with the products of block k+1")
