@@ -498,6 +498,13 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
     }
   };
 
+  // GELU' epilogue with one phase (128-column tiles): the pre-activations of
+  // the wave's whole output block -- the rows and columns its read-back loop
+  // visits, 4 features of one row per lane and row block -- are loaded before
+  // the k loop, so their latency hides behind it (WM/4 registers of 8 bytes).
+  constexpr bool kZAll = C::EPI == EPI_GELU_BWD && C::TN == 2;
+  bf16x4 zall[kZAll ? C::WM / 4 : 1];
+
   // ---------------------------------------------------------------- epilogue
   // The accumulators go through LDS so that the output leaves in full row
   // segments (16 lanes per 256-byte fp32 row piece, 8-byte bf16 pieces) from
@@ -553,7 +560,7 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
         }
       };
       bf16x4 zc[ZB];
-      if constexpr (MODE == EPI_GELU_BWD) load_z(0, zc);
+      if constexpr (MODE == EPI_GELU_BWD && !kZAll) load_z(0, zc);
       // SwiGLU backward: the stored gate and up of the phase's rows, in blocks
       // of GB rows per lane, each block issued one block ahead of its use
       constexpr int GB = ZB < 8 ? ZB : 8;
@@ -642,13 +649,21 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
         static_assert((C::WM / 4) % ZB == 0, "row blocks");
         const int c = lane & 15;
         const int n = zc_n;
+        static_assert(!kZAll || ZB == C::WM / 4, "one row block holds the whole phase");
   #pragma unroll 1
         for (int blk = 0; blk < C::WM / 4; blk += ZB) {
           bf16x4 zn[ZB];
-          if (blk + ZB < C::WM / 4)
+          if constexpr (kZAll) {
+  #pragma unroll
+            for (int j = 0; j < ZB; ++j) {
+              zc[j] = zall[j];
+              zn[j] = bf16x4{};
+            }
+          } else if (blk + ZB < C::WM / 4) {
             load_z(blk + ZB, zn);
-          else
+          } else {
             for (int j = 0; j < ZB; ++j) zn[j] = bf16x4{};
+          }
   #pragma unroll
           for (int j = 0; j < ZB; ++j) {
             const int r = (blk + j) * 4 + (lane >> 4);
@@ -828,6 +843,23 @@ void gemm_bf16_kernel(GemmParams p, int tilesM, int tilesN) {
       }
     }
   };
+
+  if constexpr (kZAll) {
+    const bf16* const zb = static_cast<const bf16*>(p.aux) + bz * p.sAux;
+    const int zn0 = n0 + wn * C::WN + 4 * (lane & 15);
+#pragma unroll
+    for (int j = 0; j < C::WM / 4; ++j) {
+      const int m = m0 + wm * C::WM + j * 4 + (lane >> 4);
+      zall[j] = bf16x4{};
+      if (m < p.M && zn0 < p.N) {
+        const bf16* zp = zb + (int64_t)m * p.ldaux + zn0;
+        if (zn0 + 3 < p.N)
+          zall[j] = *reinterpret_cast<const bf16x4*>(zp);
+        else
+          for (int e = 0; e < 4 && zn0 + e < p.N; ++e) zall[j][e] = zp[e];
+      }
+    }
+  }
 
   // EPI_GELU_FUSED runs the k loop twice (see below); every other epilogue once.
   constexpr int kPasses = C::EPI == EPI_GELU_FUSED ? 2 : 1;
