@@ -150,6 +150,17 @@ def backward_flops(w, c):
     return 8.0 * w.T * w.H * Fc
 
 
+def colsum_chunks(R, C):
+    """Row chunks of the library's two-launch column sum over [R x C] (its
+    chunking rule: about 1024 workgroups of one 128-column strip and one chunk,
+    at most 128 chunks of at least 128 rows, a multiple of 16 rows each)."""
+    strips = (C + 127) // 128
+    chunks = min((1024 + strips - 1) // strips, 128, (R + 127) // 128)
+    chunks = max(chunks, 1)
+    rpc = ((R + chunks - 1) // chunks + 15) // 16 * 16
+    return (R + rpc - 1) // rpc
+
+
 def backward_kernel_work(w, name, c):
     """Algorithmic (flops, bytes) of one launch of a backward kernel over c
     shards (bf16 operands, fp32 weight gradients).  Fz = the columns of Z:
@@ -180,12 +191,15 @@ def backward_kernel_work(w, name, c):
             return 0.0, 2 * 2 * Fc * H
         # X, dY, A, B, act(Z), dZ: each read once and written once
         return 0.0, 2 * 2 * (2 * T * H + Fz * H + Fc * H + T * Fc + T * Fz) / 6
-    if name in ("bwd_bias_rowsum", "bwd_bias_colsum"):
-        # da (when the workload has a column bias) and db (row bias), each
-        # [T x C] read once and C floats written; a column sum is two launches
-        sums = ([Fc] if bias and not swi else []) + ([H] if bias else [])
-        per = 2 if name == "bwd_bias_colsum" else 1
-        return 0.0, sum(2 * T * cols + 4 * cols for cols in sums) / max(1, per * len(sums))
+    # da (when the workload has a column bias) and db (row bias), each a sum
+    # over the T rows of a [T x C] bf16 matrix into C fp32 values
+    sums = ([Fc] if bias and not swi else []) + ([H] if bias else [])
+    if name == "bwd_bias_rowsum":  # one launch per sum: the matrix once, C floats out
+        return 0.0, sum(2 * T * cols + 4 * cols for cols in sums) / max(1, len(sums))
+    if name == "bwd_bias_colsum":  # both sums' chunk sums in one launch: each matrix once, the partials out
+        return 0.0, sum(2 * T * cols + 4 * colsum_chunks(T, cols) * cols for cols in sums)
+    if name == "bwd_bias_colsum_fold":  # both folds in one launch: the partials in, C floats out per sum
+        return 0.0, sum(4 * colsum_chunks(T, cols) * cols + 4 * cols for cols in sums)
     if name == "bwd_splitk_reduce":  # dA and dB
         return 0.0, (4 * S * Fz * H + 4 * Fz * H + 4 * S * Fc * H + 4 * Fc * H) / 2
     raise KeyError(name)
@@ -211,6 +225,7 @@ KERNEL_SOURCES = {
     "attn_vt_gemm": "gemm.hip", "attn_out_gemm": "gemm.hip", "attn_core": "attention.hip",
     "reduce_partials": "reduce.hip", "rmsnorm_gather": "norm.hip",
     "bwd_transpose": "bwd.hip", "bwd_bias_rowsum": "bwd.hip", "bwd_bias_colsum": "bwd.hip",
+    "bwd_bias_colsum_fold": "bwd.hip",
     "bwd_recompute_gemm": "gemm.hip",
     "bwd_dz_gemm": "gemm.hip", "bwd_dx_gemm": "gemm.hip", "bwd_da_gemm": "gemm.hip", "bwd_db_gemm": "gemm.hip",
     "bwd_splitk_reduce": "reduce.hip", "bwd_fused_gemm": "gemm.hip",
@@ -240,6 +255,7 @@ KERNEL_SYMBOL = {
     "attn_qk_gemm": "gemm_", "attn_vt_gemm": "gemm_", "attn_out_gemm": "gemm_",
     "attn_core": "attn_fwd_kernel", "reduce_partials": "reduce_kernel", "rmsnorm_gather": "rmsnorm_gather_kernel",
     "bwd_transpose": "transpose_kernel", "bwd_bias_rowsum": "rowsum_kernel", "bwd_bias_colsum": "colsum_kernel",
+    "bwd_bias_colsum_fold": "colsum_kernel",
     "bwd_recompute_gemm": "gemm_",
     "bwd_dz_gemm": "gemm_", "bwd_dx_gemm": "gemm_", "bwd_da_gemm": "gemm_", "bwd_db_gemm": "gemm_",
     "bwd_splitk_reduce": "reduce_kernel", "bwd_fused_gemm": "gemm_",
@@ -287,7 +303,10 @@ def backward_launch_order(w, mode="recompute"):
     order += ["bwd_db_gemm"] + (["bwd_splitk_reduce"] if split else [])
     bias = w.sigma_bias is not None
     n_bias = (1 if bias and w.kind == "mlp_gelu" else 0) + (1 if bias else 0)
-    order += ["bwd_bias_colsum"] * (2 * n_bias) if direct else ["bwd_bias_rowsum"] * n_bias
+    if direct:  # both column sums share their two launches
+        order += ["bwd_bias_colsum", "bwd_bias_colsum_fold"] if n_bias else []
+    else:
+        order += ["bwd_bias_rowsum"] * n_bias
     return order + ["reduce_partials"]
 
 

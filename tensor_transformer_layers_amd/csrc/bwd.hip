@@ -98,26 +98,45 @@ __global__ __launch_bounds__(kThreads) void rowsum_kernel(RowSumParams p) {
 }
 
 // Column sums: a workgroup sums a strip of 16*VE columns (VE elements per 16
-// bytes) over one chunk of rows.  Lane l owns columns VE*(l % 16) .. +VE-1 of
+// bytes) over one chunk of rows.  One launch serves up to two independent
+// sums (the backward's two bias gradients): workgroups [0, j0.groups) take
+// the first, the rest the second.  Lane l owns columns VE*(l % 16) .. +VE-1 of
 // the strip; wave w takes rows 4w + l/16 + 16j of the chunk (each load
 // instruction covers four 256-byte row segments), eight rows in flight per
 // lane.  Lanes l, l^16, l^32, l^48 then fold by an xor butterfly and the four
 // waves' sums add in wave order through LDS; the chunks' partials are folded
-// by a second launch of the same kernel over the fp32 partial matrix.  Every
-// order is fixed, so the sums are bit-identical run to run.
+// by a second launch of the same kernel over the fp32 partial matrices.  Every
+// order is fixed, so the sums are bit-identical run to run, and a sum's bits
+// do not depend on whether it shares its launches with another.
 constexpr int kColsumTargetGroups = 1024;  // ~4 per CU: enough loads in flight to stream from HBM
 constexpr int kColsumMaxChunks = 128;      // bounds the fold's depth
 constexpr int kColsumMinRows = 128;        // one full unrolled trip per wave
 
+// One column sum of a launch: in [R x C] (row pitch ld), rows_per_chunk rows
+// per chunk, strips strips of columns, groups = strips x chunks workgroups,
+// chunk k's sums to dst + k C.
+struct ColsumJob {
+  const void* in;
+  int64_t ld, R, C, rows_per_chunk;
+  int strips, groups;
+  float* dst;
+};
+
 template <typename E>
-__global__ __launch_bounds__(kThreads) void colsum_kernel(const E* in, int64_t ld, int64_t R, int64_t C,
-                                                          int64_t rows_per_chunk, int strips, float* dst) {
+__global__ __launch_bounds__(kThreads) void colsum_kernel(ColsumJob j0, ColsumJob j1) {
   constexpr int VE = 16 / sizeof(E);
   constexpr int SW = 16 * VE;  // columns per strip
   constexpr int U = 8;         // rows in flight per lane
   typedef E ev __attribute__((ext_vector_type(VE)));
   __shared__ __attribute__((aligned(16))) float red[kThreads / kWave][SW];
-  const int strip = (int)blockIdx.x % strips, chunk = (int)blockIdx.x / strips;
+  const bool second = (int)blockIdx.x >= j0.groups;
+  const ColsumJob& j = second ? j1 : j0;
+  const int bid = second ? (int)blockIdx.x - j0.groups : (int)blockIdx.x;
+  const E* const in = static_cast<const E*>(j.in);
+  const int64_t ld = j.ld, R = j.R, C = j.C, rows_per_chunk = j.rows_per_chunk;
+  const int strips = j.strips;
+  float* const dst = j.dst;
+  const int strip = bid % strips, chunk = bid / strips;
   const int lane = lane_id(), w = threadIdx.x >> 6;
   const int64_t c = (int64_t)strip * SW + (lane & 15) * VE;
   const int64_t r0 = (int64_t)chunk * rows_per_chunk;
@@ -191,17 +210,50 @@ size_t colsum_part_floats(int64_t R, int64_t C) {
   return R > 0 && C > 0 ? (size_t)colsum_chunk_count(R, C) * (size_t)C : 0;
 }
 
-hipError_t launch_colsum(const ColSumParams& p, hipStream_t s) {
-  if (p.R <= 0 || p.C <= 0) return hipSuccess;
-  if (p.C % 8) return hipErrorInvalidValue;
-  const int64_t rpc = colsum_rows_per_chunk(p.R, p.C), chunks = colsum_chunk_count(p.R, p.C);
-  const int64_t strips1 = (p.C + 127) / 128, strips2 = (p.C + 63) / 64;
-  if (strips1 * chunks > 0x7fffffff || strips2 > 0x7fffffff) return hipErrorInvalidValue;
-  launch_kernel(colsum_kernel<bf16>, dim3((unsigned)(strips1 * chunks)), dim3(kThreads), 0, s,
-                static_cast<const bf16*>(p.in), p.ld, p.R, p.C, rpc, (int)strips1, p.part);
-  // fold the chunks' partials (fp32 [chunks x C]) in chunk order, one chunk of all rows
-  launch_kernel(colsum_kernel<float>, dim3((unsigned)strips2), dim3(kThreads), 0, s,
-                static_cast<const float*>(p.part), p.C, chunks, p.C, chunks, (int)strips2, p.out);
+namespace {
+
+// The jobs of the two launches of up to two column sums: the chunk sums, and
+// the fold of the chunks' partials (fp32 [chunks x C]) in chunk order (one
+// chunk of all rows).  A job with no workgroups is never selected.
+hipError_t colsum_jobs(const ColSumParams* ps, int n, ColsumJob (&sums)[2], ColsumJob (&folds)[2], int64_t& g1,
+                       int64_t& g2) {
+  if (n < 0 || n > 2) return hipErrorInvalidValue;
+  sums[0] = sums[1] = folds[0] = folds[1] = ColsumJob{};
+  g1 = g2 = 0;
+  int k = 0;
+  for (int i = 0; i < n; ++i) {
+    const ColSumParams& p = ps[i];
+    if (p.R <= 0 || p.C <= 0) continue;
+    if (p.C % 8) return hipErrorInvalidValue;
+    const int64_t rpc = colsum_rows_per_chunk(p.R, p.C), chunks = colsum_chunk_count(p.R, p.C);
+    const int64_t strips1 = (p.C + 127) / 128, strips2 = (p.C + 63) / 64;
+    if (strips1 * chunks > 0x3fffffff || strips2 > 0x3fffffff) return hipErrorInvalidValue;
+    sums[k] = ColsumJob{p.in, p.ld, p.R, p.C, rpc, (int)strips1, (int)(strips1 * chunks), p.part};
+    folds[k] = ColsumJob{p.part, p.C, chunks, p.C, chunks, (int)strips2, (int)strips2, p.out};
+    g1 += strips1 * chunks;
+    g2 += strips2;
+    ++k;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_colsum_chunks(const ColSumParams* ps, int n, hipStream_t s) {
+  ColsumJob sums[2], folds[2];
+  int64_t g1, g2;
+  const hipError_t e = colsum_jobs(ps, n, sums, folds, g1, g2);
+  if (e != hipSuccess || g1 == 0) return e;
+  launch_kernel(colsum_kernel<bf16>, dim3((unsigned)g1), dim3(kThreads), 0, s, sums[0], sums[1]);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum_fold(const ColSumParams* ps, int n, hipStream_t s) {
+  ColsumJob sums[2], folds[2];
+  int64_t g1, g2;
+  const hipError_t e = colsum_jobs(ps, n, sums, folds, g1, g2);
+  if (e != hipSuccess || g2 == 0) return e;
+  launch_kernel(colsum_kernel<float>, dim3((unsigned)g2), dim3(kThreads), 0, s, folds[0], folds[1]);
   return hipGetLastError();
 }
 

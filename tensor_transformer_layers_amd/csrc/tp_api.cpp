@@ -706,16 +706,22 @@ tp_status bwd_direct(hipStream_t s, const tp_mlp_bwd_desc* d, const BwdShape& sh
   TP_TRY(token_gemm("bwd_da_gemm", dZ, sh.zld, d->X, H, Fz, H, d->dA + (size_t)i0 * zs * H, H));
   // dB columns of the range: dY^T act(Z)  (M = H, N = Fc)
   TP_TRY(token_gemm("bwd_db_gemm", d->dY, H, Hop, hld, H, Fc, d->dB + (size_t)i0 * Fs, F));
-  // bias gradients: column sums of dZ (range) and of dY (once)
-  auto colsum = [&](const void* in, int64_t ld, int64_t C, float* part, float* out) -> tp_status {
-    tp::ColSumParams cp{in, ld, T, C, part, out};
+  // bias gradients: column sums of dZ (range) and of dY (once), both in the
+  // same two launches
+  tp::ColSumParams cps[2];
+  int ncs = 0;
+  if (d->da) cps[ncs++] = tp::ColSumParams{dZ, sh.zld, T, Fc, CSa, d->da + (size_t)i0 * Fs};
+  if (d->db) cps[ncs++] = tp::ColSumParams{d->dY, H, T, H, CSb, d->db};
+  if (ncs > 0) {
     KernelTimer kt("bwd_bias_colsum", s);
-    const hipError_t e = tp::launch_colsum(cp, s);
+    hipError_t e = tp::launch_colsum_chunks(cps, ncs, s);
     kt.stop();
-    return hip_status(e, "bwd_bias_colsum");
-  };
-  if (d->da) TP_TRY(colsum(dZ, sh.zld, Fc, CSa, d->da + (size_t)i0 * Fs));
-  if (d->db) TP_TRY(colsum(d->dY, H, H, CSb, d->db));
+    TP_TRY(hip_status(e, "bwd_bias_colsum"));
+    KernelTimer kf("bwd_bias_colsum_fold", s);
+    e = tp::launch_colsum_fold(cps, ncs, s);
+    kf.stop();
+    TP_TRY(hip_status(e, "bwd_bias_colsum_fold"));
+  }
 
   if (c < d->N) return ok();
   return run_reduce(s, TP_BF16, d->N, T, H, P, T * H, nullptr, d->dX, d->n_slices, d->slice);

@@ -211,6 +211,9 @@ hipError_t launch_rowsum(const RowSumParams& p, bool f32, hipStream_t s);
 //   out[c] = sum over r of in[r][c], bf16 in [R x C] (ld), fp32 out, in a
 //   fixed order: chunks of rows summed into part (colsum_part_floats(R, C)
 //   floats of workspace), then the chunks folded in order.  C a multiple of 8.
+//   n (at most 2) independent sums share the two launches: the chunk sums
+//   (launch_colsum_chunks), then their fold (launch_colsum_fold, same ps);
+//   each sum's bits are those it has alone.
 struct ColSumParams {
   const void* in;
   int64_t ld;
@@ -219,7 +222,8 @@ struct ColSumParams {
   float* out;
 };
 size_t colsum_part_floats(int64_t R, int64_t C);
-hipError_t launch_colsum(const ColSumParams& p, hipStream_t s);
+hipError_t launch_colsum_chunks(const ColSumParams* ps, int n, hipStream_t s);
+hipError_t launch_colsum_fold(const ColSumParams* ps, int n, hipStream_t s);
 
 // Vocab-parallel cross-entropy (vocab.hip).
 // Folds the per-chunk statistics of the GEMM epilogue (layout of CeEpilogue,
