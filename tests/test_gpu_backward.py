@@ -86,6 +86,25 @@ def test_backward_vs_oracle(T, H, F, N, act, bias):
         assert torch.equal(g[k], g2[k]), f"{k} not bit-identical run to run"
 
 
+def test_bias_sums_alone_equal_shared():
+    """On the as-stored path the two bias gradients (column sums of dZ and of
+    dY) share their launches; each sum alone gives the same bits."""
+    T, H, F, N = 1024, 192, 4 * 320, 4
+    say(f"mlp_backward bias sums alone and shared T={T} H={H} F={F} N={N}")
+    h = _host(T, H, F, True, seed=91)
+    X, A, a, B, dY = (dev(h[k]) for k in ("X", "A", "a", "B", "dY"))
+    both, _ = tp.mlp_backward(X, A, a, B, dY, N, need_da=True, need_db=True)
+    only_a, _ = tp.mlp_backward(X, A, a, B, dY, N, need_da=True, need_db=False)
+    only_b, _ = tp.mlp_backward(X, A, a, B, dY, N, need_da=False, need_db=True)
+    torch.cuda.synchronize()
+    assert only_a["db"] is None and only_b["da"] is None
+    assert torch.equal(both["da"], only_a["da"])
+    assert torch.equal(both["db"], only_b["db"])
+    ref = R.mlp_gelu_backward(h["X"], h["A"], h["a"], h["B"], h["dY"], act="gelu")
+    assert err(_np(both["da"]), ref["da"]) <= BF16_TOL
+    assert err(_np(both["db"]), ref["db"]) <= BF16_TOL
+
+
 def test_one_shard_range_matches_oracle_shard():
     """A one-shard range writes only that shard's rows of dA, columns of dB and
     entries of da, and leaves its dX partial in its slab slot."""
