@@ -321,9 +321,9 @@ tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t 
  * bf16: Z_i and dZ_i are rounded to bf16 once (as a bf16 forward would store
  * its linear outputs), act(Z_i) is evaluated from the rounded Z_i (when it is
  * recomputed at H <= 2048, one two-pass kernel keeps Z_i on chip in fp32
- * instead).  fp32: everything stays fp32.  A stored Z (GELU or NONE) gives the
- * same bits as recomputing it with the GEMM path: the forward's column product
- * and the recomputation accumulate in the same order.
+ * instead).  fp32: everything stays fp32.  A stored Z (bf16: GELU, NONE or
+ * SwiGLU) gives the same bits as recomputing it with the GEMM path: the
+ * forward's column product and the recomputation accumulate in the same order.
  * SwiGLU (blog post section 3.2): A holds the N fused blocks [2F/N x H] of the
  * forward (gate rows, then up rows); Z_i = [G_i | U_i], dH_i = dY B_i,
  * dZ_i = [dH_i U_i SiLU'(G_i) | dH_i SiLU(G_i)], dA comes back in the same
