@@ -302,7 +302,8 @@ tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t 
 
 /*
  * Backward of the MLP pair over shards [shard_begin, shard_begin + shard_count)
- * (bf16, activation GELU or NONE), given the forward's input X, its weights and
+ * (activation GELU or NONE in bf16 or fp32; SwiGLU in bf16, see the end of
+ * this comment), given the forward's input X, its weights and
  * the gradient dY of its output.  Per shard i, with no exchange:
  *   Z_i  = X A_i^T + a_i            (recomputed -- activation recomputation,
  *                                    2kiu.com blog post, section 5.3 -- unless
