@@ -781,7 +781,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on ONE GPU (all N tensor-parallel shards on one device, "
+        print("bench.py: the library runs on ONE GPU (all N tensor-parallel shards on one device, "
               "an on-device reduction standing in for the all-reduce); --gpus above 1 is not supported.",
               file=sys.stderr, flush=True)
         sys.exit(2)
