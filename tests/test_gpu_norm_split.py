@@ -97,6 +97,8 @@ SPLIT = [
     ("bf16", "layer", 9, 64, 8, False),       # 8 features per shard: one piece, most lanes idle
     ("bf16", "layer", 16, 16384 * 2, 2, True),  # the widest shard (16384): 8 waves per slice
     ("bf16", "rms", 33, 520, 5, False),       # an odd shard count
+    ("bf16", "rms", 24, 4096, 2, False),      # 2048 per shard: four 1 KB pieces per lane in the scale pass
+    ("bf16", "layer", 12, 1152, 9, True),     # more than 8 shards: the statistics folded in a loop
     ("f32", "layer", 50, 2048, 4, True),
     ("f32", "rms", 50, 2048, 1, False),
 ]
