@@ -41,9 +41,10 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_work(w, name, shards_per_launch, rows_reduced):
+def kernel_work(w, name, shards_per_launch, rows_reduced, bmode=None):
     """Algorithmic (flops, bytes) of ONE launch of kernel `name` for workload w:
-    every input read once and every output written once."""
+    every input read once and every output written once.  bmode: the
+    backward variant ("stored" or "recompute") for the backward's kernels."""
     es = 2 if w.dtype == "bf16" else 4
     T, H, N = w.T, w.H, w.N
     c = shards_per_launch
@@ -69,7 +70,7 @@ def kernel_work(w, name, shards_per_launch, rows_reduced):
         if name == "attn_out_gemm":
             return 2.0 * T * hd * H * c, es * (c * T * hd + c * H * hd) + 4 * c * T * H
     if name.startswith("bwd_"):
-        return backward_kernel_work(w, name, shards_per_launch)
+        return backward_kernel_work(w, name, shards_per_launch, bmode)
     if w.kind == "vocab_ce":
         c = shards_per_launch
         Vs = -(-w.F // N)
@@ -161,10 +162,11 @@ def colsum_chunks(R, C):
     return (R + rpc - 1) // rpc
 
 
-def backward_kernel_work(w, name, c):
+def backward_kernel_work(w, name, c, bmode=None):
     """Algorithmic (flops, bytes) of one launch of a backward kernel over c
     shards (bf16 operands, fp32 weight gradients).  Fz = the columns of Z:
-    Fc, or 2*Fc ([gate | up]) for SwiGLU."""
+    Fc, or 2*Fc ([gate | up]) for SwiGLU.  bmode "stored": the forward's Z
+    (and, GELU, its activation) are read instead of recomputed."""
     T, H = w.T, w.H
     Fc = w.Fs * c
     swi = w.kind == "mlp_swiglu"
@@ -177,8 +179,8 @@ def backward_kernel_work(w, name, c):
     if name == "bwd_recompute_gemm":
         return 2.0 * T * H * Fz, 2 * (T * H + Fz * H + T * Fz) + (2 * Fc if bias else 0)
     if name == "bwd_dz_gemm":  # reads the pre-activation beside the accumulators; writes act(Z) too (SwiGLU,
-        # and GELU on the direct path)
-        writes_act = swi or (direct and w.kind == "mlp_gelu")
+        # and GELU on the direct path unless the forward's activation is read instead)
+        writes_act = swi or (direct and w.kind == "mlp_gelu" and not (bmode == "stored" and stored_activation(w)))
         return 2.0 * T * H * Fc, 2 * (T * H + Fc * H + 2 * T * Fz + (T * Fc if writes_act else 0))
     if name == "bwd_dx_gemm":
         return 2.0 * T * Fz * H, 2 * (T * Fz + H * Fz) + 4 * c * T * H
@@ -271,6 +273,12 @@ def stored_preactivation(w):
     """Whether the backward of workload w can take the forward's stored
     pre-activation (tp_mlp_desc.Z): the bf16 GELU and SwiGLU MLPs."""
     return w.kind in ("mlp_gelu", "mlp_swiglu") and w.dtype == "bf16"
+
+
+def stored_activation(w):
+    """Whether the stored-pre-activation backward of workload w also takes
+    the forward's activation (tp_mlp_desc.Hact) for dB: the bf16 GELU MLP."""
+    return w.kind == "mlp_gelu" and w.dtype == "bf16"
 
 
 def backward_mode(w, recompute):
@@ -567,7 +575,7 @@ def write_trace(w, share, trace_dir, argv_line, steps, sp_entry=False, backward=
         d = durs[k]
         last = d[-steps * per_step[k]:]
         avg_t = sum(last) / len(last)
-        f, b = kernel_work(w, k, shards, rows_red)
+        f, b = kernel_work(w, k, shards, rows_red, bmode=backward or None)
         rf = roofline(w, k, f, b, avg_t / 1e6)
         lines.append(f"| `{short(names[k])}` | {k} | {len(d)} | {sum(d) / len(d):.2f} | {avg_t:.2f} | "
                      f"{min(d):.2f} | {max(d):.2f} | {rf['achieved']} {rf['unit']} | {rf['frac']:.4f} |")
@@ -817,15 +825,17 @@ def main():
     host = inputs.make_inputs(w)
     d = workloads.device_inputs(w, host)
     bmode = None
-    Zst = None
+    Zst = Hst = None
     if args.backward:
         dY_host = inputs.grad_output(w)
         dY = workloads.to_device(dY_host, d["X"].dtype)
         bmode = backward_mode(w, args.recompute)
-        if bmode == "stored":  # one training forward before the timed region writes Z
+        if bmode == "stored":  # one training forward before the timed region writes Z (and, GELU, H)
             zw = 2 * w.F if w.kind == "mlp_swiglu" else w.F  # SwiGLU: [gate | up] per shard
             Zst = torch.empty((w.T, zw), dtype=d["X"].dtype, device=d["X"].device)
-            tp.mlp_forward(d["X"], d["A"], d["a"], d["B"], d["b"], w.N, act=workloads.act_of(w), Z=Zst)
+            if stored_activation(w):
+                Hst = torch.empty((w.T, w.F), dtype=d["X"].dtype, device=d["X"].device)
+            tp.mlp_forward(d["X"], d["A"], d["a"], d["B"], d["b"], w.N, act=workloads.act_of(w), Z=Zst, Hact=Hst)
     if args.sp_entry:
         # X holds the n_slices sequence slices of the sublayer input; each step
         # normalizes them into Xn, the gathered input of the column GEMM
@@ -842,7 +852,7 @@ def main():
 
         entry_norm()
     if args.backward:
-        grads, ws = workloads.backward(w, d, dY, Z=Zst)  # allocates the gradients and the workspace once
+        grads, ws = workloads.backward(w, d, dY, Z=Zst, Hact=Hst)  # allocates the gradients and the workspace once
         Y = grads["dX"]
     else:
         Y, ws = workloads.forward(w, d)  # allocates Y and the workspace once
@@ -862,7 +872,7 @@ def main():
             workloads.forward_overlap(w, d, args.overlap, stream2, Y=Y, ws=ws, stream=stream)
             return
         if args.backward:
-            workloads.backward(w, d, dY, grads=grads, ws=ws, Z=Zst, stream=stream)
+            workloads.backward(w, d, dY, grads=grads, ws=ws, Z=Zst, Hact=Hst, stream=stream)
             return
         if args.sp_entry:
             entry_norm(stream)
@@ -960,13 +970,13 @@ def main():
         rows_red = wk.T
     kernels = {}
     for name, (ms, n) in kern.items():
-        f, b = kernel_work(wk, name, shards, rows_red)
+        f, b = kernel_work(wk, name, shards, rows_red, bmode=bmode)
         avg = ms / n / 1e3
         kernels[name] = {"avg_us": round(avg * 1e6, 2), "launches": n,
                          "share": round(ms / sum(v[0] for v in kern.values()), 4),
                          **roofline(w, name, f, b, avg)}
     dom = max(kern, key=lambda k: kern[k][0])
-    f, b = kernel_work(wk, dom, shards, rows_red)
+    f, b = kernel_work(wk, dom, shards, rows_red, bmode=bmode)
     avg = kern[dom][0] / kern[dom][1] / 1e3
     roof = roofline(w, dom, f, b, avg)
     src_hash = kernel_source_hash()
@@ -1021,6 +1031,8 @@ def main():
                                    if bmode == "recompute" else ""),
                 "preactivation": ("stored by a training forward before the timed region (bf16 Z, read by the dZ "
                                   "epilogue)" if bmode == "stored" else "recomputed in every step (X A^T + a)"),
+                **({"activation": "stored by the same forward (bf16 GELU(Z), the B operand of dB)"}
+                   if bmode == "stored" and stored_activation(w) else {}),
                 "operands": ("read as stored (K-outer GEMM operands, column sums for the bias gradients)"
                              if backward_direct(w) else "transposed first"),
                 "split_k": backward_splits(w.T, 2 * w.F if w.kind == "mlp_swiglu" else w.F, w.H,

@@ -218,6 +218,14 @@ typedef struct {
                        (training keeps the activation's input).  The fused
                        narrow-hidden kernel keeps its intermediate on chip, so
                        asking for Z selects the two-GEMM path there. */
+  void* Hact;       /* [T x F] (ld F) or NULL (bf16, GELU or SwiGLU).  When set,
+                       the range's activated intermediate H_i = act(Z_i)
+                       (shard i = columns i*F/N..), rounded to bf16 once, is
+                       written there instead of into the workspace, and the
+                       row product reads it from there: the row layer's input,
+                       which a training forward keeps for the weight gradient
+                       (tp_mlp_backward's Hact).  Like Z, it selects the
+                       two-GEMM path at narrow hidden sizes. */
 } tp_mlp_desc;
 
 /* Whole attention sublayer over shards [shard_begin, shard_begin + shard_count).
@@ -325,6 +333,9 @@ tp_status tp_attn_forward(void* stream, const tp_attn_desc* d, void* ws, size_t 
  * instead).  fp32: everything stays fp32.  A stored Z (bf16: GELU, NONE or
  * SwiGLU) gives the same bits as recomputing it with the GEMM path: the
  * forward's column product and the recomputation accumulate in the same order.
+ * A stored Hact (GELU, with Z) replaces GELU(Z_i) in dB_i only: dB then uses
+ * the forward's activation of the unrounded pre-activation, so its bits
+ * differ from the Z-only run; every other gradient keeps its bits.
  * SwiGLU (blog post section 3.2): A holds the N fused blocks [2F/N x H] of the
  * forward (gate rows, then up rows); Z_i = [G_i | U_i], dH_i = dY B_i,
  * dZ_i = [dH_i U_i SiLU'(G_i) | dH_i SiLU(G_i)], dA comes back in the same
@@ -356,6 +367,11 @@ typedef struct {
                       forward's pre-activation (tp_mlp_desc.Z, same layout),
                       read for the range's columns instead of recomputing
                       X A_i^T + a_i                                            */
+  const void* Hact; /* [T x F] bf16 (ld F) or NULL: the forward's activated
+                      intermediate (tp_mlp_desc.Hact), the B operand of
+                      dB_i = dY^T H_i, read for the range's columns instead
+                      of evaluating GELU(Z_i) from the stored Z.  GELU only,
+                      and only together with Z.                                */
 } tp_mlp_bwd_desc;
 
 /* Workspace bytes for tp_mlp_backward (0 when the descriptor is invalid).

@@ -341,6 +341,12 @@ tp_status validate_mlp(const tp_mlp_desc* d, MlpShape* sh) {
     const int64_t zw = d->act == TP_ACT_SWIGLU ? 2 * d->F : d->F;  // SwiGLU: [gate | up] per shard
     TP_TRY(check_matrix("Z", d->Z, d->T, zw, zw, vec));
   }
+  if (d->Hact) {
+    if (d->dt != TP_BF16) return fail(TP_ERR_DTYPE, "the stored activation Hact is written by the bf16 path only");
+    if (d->act == TP_ACT_NONE)
+      return fail(TP_ERR_SHAPE, "Hact with no activation: the intermediate is the pre-activation (use Z)");
+    TP_TRY(check_matrix("Hact", d->Hact, d->T, d->F, d->F, vec));
+  }
   if (d->T > kIntMax) return fail(TP_ERR_SHAPE, "T exceeds 2^31-1");
   sh->Fs = Fs;
   sh->a_rows = a_rows;
@@ -537,6 +543,11 @@ tp_status validate_mlp_bwd(const tp_mlp_bwd_desc* d, BwdShape* sh) {
     const int64_t zw = swiglu ? 2 * d->F : d->F;  // SwiGLU: [gate | up] per shard
     TP_TRY(check_matrix("Z", d->Z, d->T, zw, zw, vec));
   }
+  if (d->Hact) {
+    if (d->act != TP_ACT_GELU || !d->Z)
+      return fail(TP_ERR_SHAPE, "the stored activation Hact is read with GELU and a stored Z only");
+    TP_TRY(check_matrix("Hact", d->Hact, d->T, d->F, d->F, vec));
+  }
   if (d->T > kIntMax || d->F > kIntMax) return fail(TP_ERR_SHAPE, "size exceeds 2^31-1");
   const size_t T = (size_t)d->T, H = (size_t)d->H, fc = (size_t)Fc, fz = (size_t)sh->Fz, es = esize(d->dt);
   sh->splits = bwd_splits(d->T, sh->Fz, d->H);
@@ -657,7 +668,10 @@ tp_status bwd_direct(hipStream_t s, const tp_mlp_bwd_desc* d, const BwdShape& sh
       dg.b_ko = 1;
       dg.aux = Zp;
       dg.ldaux = zld;
-      if (gelu) {
+      if (gelu && d->Hact) {  // the forward's activation: dZ alone
+        Hop = static_cast<const char*>(d->Hact) + (size_t)i0 * Fs * es;
+        hld = F;
+      } else if (gelu) {
         dg.C2 = Hs;
         dg.ldc2 = Fc;
       } else {
@@ -1022,7 +1036,7 @@ tp_status mlp_rows(hipStream_t s, const tp_mlp_desc* d, const MlpShape& sh, void
   // Narrow hidden sizes: one kernel per shard range computes the column
   // product, the activation and the row partial with the intermediate kept
   // on chip (it never needs to leave the shard).
-  if (d->dt == TP_BF16 && d->act != TP_ACT_SWIGLU && !d->Z && tp::mlp_fused_supported(H, Fs)) {
+  if (d->dt == TP_BF16 && d->act != TP_ACT_SWIGLU && !d->Z && !d->Hact && tp::mlp_fused_supported(H, Fs)) {
     tp::FusedMlpParams f{};
     f.X = X;
     f.ldx = H;
@@ -1054,9 +1068,13 @@ tp_status mlp_rows(hipStream_t s, const tp_mlp_desc* d, const MlpShape& sh, void
   const bool swiglu = d->act == TP_ACT_SWIGLU;
   const int64_t zw = swiglu ? 2 * d->F : d->F, zs = swiglu ? 2 * Fs : Fs;  // Z row width, shard block width
   void* Zr = d->Z ? static_cast<char*>(d->Z) + ((size_t)row0 * zw + (size_t)i0 * zs) * es : nullptr;
+  // the intermediate: the stored Z itself without an activation, the
+  // caller's Hact when given (row block, range columns), else the workspace
+  void* Ha = d->Hact ? static_cast<char*>(d->Hact) + ((size_t)row0 * d->F + (size_t)i0 * Fs) * es : nullptr;
   const bool z_is_h = Zr && d->act == TP_ACT_NONE;
-  void* Hc = z_is_h ? Zr : Hs;
-  const int64_t hld = z_is_h ? d->F : sh.h_ld, hstride = z_is_h ? Fs : T * sh.h_ld;
+  void* Hc = z_is_h ? Zr : Ha ? Ha : Hs;
+  const bool h_in_f = z_is_h || Ha;  // [T x F] layout, shard i at columns i*Fs
+  const int64_t hld = h_in_f ? d->F : sh.h_ld, hstride = h_in_f ? Fs : T * sh.h_ld;
 
   // column GEMM + activation for every shard in range (X shared, one launch)
   tp::GemmParams col = gemm(X, H, 0, static_cast<const char*>(d->A) + (size_t)i0 * sh.a_rows * H * es, H,
@@ -1235,9 +1253,10 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
   const bool f32 = dt == TP_F32;
   const size_t es = esize(dt);
   if (log_enabled())
-    fprintf(stderr, "[tp] mlp backward %s act=%d N=%d shards [%d,%d): T=%lld H=%lld Fs=%lld, split-K %d, %s%s\n",
+    fprintf(stderr, "[tp] mlp backward %s act=%d N=%d shards [%d,%d): T=%lld H=%lld Fs=%lld, split-K %d, %s%s%s\n",
             dt_name(dt), (int)d->act, d->N, i0, i0 + c, (long long)T, (long long)H, (long long)Fs, S,
-            sh.direct ? "operands as stored" : "transposed operands", c == d->N ? " ; reduce dX" : "");
+            sh.direct ? "operands as stored" : "transposed operands",
+            d->Z ? (d->Hact ? ", stored Z and H" : ", stored Z") : ", Z recomputed", c == d->N ? " ; reduce dX" : "");
   if (sh.direct) return bwd_direct(s, d, sh, static_cast<char*>(ws));
   char* base = static_cast<char*>(ws);
   char* Z = base + sh.z_off;
@@ -1346,7 +1365,11 @@ tp_status tp_mlp_backward(void* stream, const tp_mlp_bwd_desc* d, void* ws, size
     dg.aux = Zp;
     dg.ldaux = zld;
     TP_TRY(hip_status(launch("bwd_dz_gemm", dt, dg, gelu ? tp::EPI_GELU_BWD : tp::EPI_STORE, s), "bwd_dz_gemm"));
-    TP_TRY(transpose("bwd_transpose", Zp, zld, HT, T, T, Fc, gelu));  // HT = act(Z)^T
+    if (d->Hact)  // HT = H^T, the forward's activation
+      TP_TRY(transpose("bwd_transpose", static_cast<const char*>(d->Hact) + (size_t)i0 * Fs * es, F, HT, T, T, Fc,
+                       false));
+    else
+      TP_TRY(transpose("bwd_transpose", Zp, zld, HT, T, T, Fc, gelu));  // HT = act(Z)^T
   }
   TP_TRY(transpose("bwd_transpose", dZ, sh.zld, dZT, T, T, Fz, false));  // dZT [Fz x T]
   return bwd_tail(s, d, sh, ws, dZ, dZT, XT, dYT, HT, AT, token_gemm, rowsum);

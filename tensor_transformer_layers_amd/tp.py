@@ -34,6 +34,7 @@ class MlpDesc(ctypes.Structure):
         ("Y", _vp),
         ("n_slices", _int), ("slice", _int),
         ("Z", _vp),
+        ("Hact", _vp),
     ]
 
 
@@ -57,6 +58,7 @@ class MlpBwdDesc(ctypes.Structure):
         ("dX", _vp), ("dA", _vp), ("da", _vp), ("dB", _vp), ("db", _vp),
         ("n_slices", _int), ("slice", _int),
         ("Z", _vp),
+        ("Hact", _vp),
     ]
 
 
@@ -528,7 +530,7 @@ def norm_split_stats(ws, N, T):
 
 
 def mlp_desc(X, A, a, B, b, N, act, Y=None, shard_begin=0, shard_count=None, n_slices=1, slice=-1, F=None,
-             Z=None):
+             Z=None, Hact=None):
     T, H = X.shape
     if F is None:
         F = B.shape[1]
@@ -543,6 +545,7 @@ def mlp_desc(X, A, a, B, b, N, act, Y=None, shard_begin=0, shard_count=None, n_s
     d.Y = _ptr(Y)
     d.n_slices, d.slice = n_slices, slice
     d.Z = _ptr(Z)
+    d.Hact = _ptr(Hact)
     return d
 
 
@@ -552,12 +555,14 @@ def alloc_workspace(nbytes: int, device):
 
 
 def mlp_forward(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, ws=None, shard_begin=0, shard_count=None,
-                n_slices=1, slice=-1, Z=None, stream=None):
+                n_slices=1, slice=-1, Z=None, Hact=None, stream=None):
     """Whole MLP sublayer; returns (Y, workspace).  Y is None for partial
     shard ranges (the partials are in the workspace slab).  Z ([T x F], or
     [T x 2F] for SwiGLU with shard i's [gate | up] in columns 2i*F/N..; X's
     dtype, bf16 only) or None: also write the range's pre-activation there,
-    for mlp_backward(..., Z=Z)."""
+    for mlp_backward(..., Z=Z).  Hact ([T x F], X's dtype, bf16 GELU or
+    SwiGLU) or None: keep the range's activated intermediate there (the row
+    layer's input), for mlp_backward(..., Hact=Hact)."""
     torch = _torch()
     _same_dtype(X, A=A, a=a, B=B, b=b, Y=Y)
     T, H, _ = _check_mlp(X, A, a, B, b, act)
@@ -570,7 +575,9 @@ def mlp_forward(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, ws=None, shard_begin=
     if Z is not None:
         zw = B.shape[1] * (2 if act == TP_ACT_SWIGLU else 1)
         _expect("Z", Z, (T, zw), X.dtype, X.device)
-    d = mlp_desc(X, A, a, B, b, N, act, Y, shard_begin, cnt, n_slices, slice, Z=Z)
+    if Hact is not None:
+        _expect("Hact", Hact, (T, B.shape[1]), X.dtype, X.device)
+    d = mlp_desc(X, A, a, B, b, N, act, Y, shard_begin, cnt, n_slices, slice, Z=Z, Hact=Hact)
     need = tp_mlp_workspace_size(d)
     if need == 0:
         raise TPError(TP_ERR_SHAPE, last_error())
@@ -598,7 +605,7 @@ def mlp_forward_noalloc(X, A, a, B, b, N, act=TP_ACT_GELU, Y=None, n_slices=1, s
 
 
 def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=None, grads=None, ws=None,
-                 need_da=True, need_db=True, n_slices=1, slice=-1, Z=None, stream=None):
+                 need_da=True, need_db=True, n_slices=1, slice=-1, Z=None, Hact=None, stream=None):
     """Backward of the MLP pair over a shard range; returns (grads, workspace).
     ``grads`` holds dX (bf16 [T x H], filled when the range covers all N
     shards; with n_slices > 1 and slice = r, rank r's reduce-scatter slice,
@@ -606,7 +613,9 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
     blocks for SwiGLU), da (fp32 [F] or None; always None for SwiGLU), dB
     (fp32 [H x F]) and db (fp32 [H] or None); missing entries are allocated.
     Z: the forward's stored pre-activation ([T x F], SwiGLU [T x 2F]; X's
-    dtype) to use instead of recomputing it, or None."""
+    dtype) to use instead of recomputing it, or None.  Hact: the forward's
+    stored activation ([T x F], GELU with Z only), read for dB instead of
+    GELU(Z), or None."""
     torch = _torch()
     _same_dtype(X, A=A, a=a, B=B, dY=dY)
     T, H, F = _check_mlp(X, A, a, B, None, act)
@@ -638,6 +647,8 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
         _expect("db", g["db"], (H,), f32, dev)
     if Z is not None:
         _expect("Z", Z, (T, 2 * F if act == TP_ACT_SWIGLU else F), X.dtype, dev)
+    if Hact is not None:
+        _expect("Hact", Hact, (T, F), X.dtype, dev)
     d = MlpBwdDesc()
     d.dt = _dt(X)
     d.act = act
@@ -647,6 +658,7 @@ def mlp_backward(X, A, a, B, dY, N, act=TP_ACT_GELU, shard_begin=0, shard_count=
     d.dX, d.dA, d.da, d.dB, d.db = (_ptr(g[k]) for k in ("dX", "dA", "da", "dB", "db"))
     d.n_slices, d.slice = n_slices, slice
     d.Z = _ptr(Z)
+    d.Hact = _ptr(Hact)
     need = tp_mlp_backward_workspace_size(d)
     if need == 0:
         if T == 0:

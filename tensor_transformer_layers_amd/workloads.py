@@ -125,12 +125,14 @@ def reduce_slab(w: Workload, d: dict, ws, Y=None, slice=-1, stream=None):
     return tp.reduce_partials(P, bias, out_dtype=dt, n_slices=w.n_slices, slice=slice, out=Y, stream=stream)
 
 
-def backward(w: Workload, d: dict, dY, grads=None, ws=None, shard_begin=0, shard_count=None, Z=None, stream=None):
+def backward(w: Workload, d: dict, dY, grads=None, ws=None, shard_begin=0, shard_count=None, Z=None, Hact=None,
+             stream=None):
     """One backward pass of the MLP sublayer (GELU or SwiGLU) over a shard
     range; Z: the forward's stored pre-activation ([T x F]) or None to
-    recompute it."""
+    recompute it; Hact: the forward's stored activation (GELU, with Z) or
+    None."""
     if w.kind not in ("mlp_gelu", "mlp_swiglu"):
         raise ValueError(f"the backward is built for the MLP sublayers, not {w.kind}")
     return tp.mlp_backward(d["X"], d["A"], d["a"], d["B"], dY, w.N, act=act_of(w),
                            shard_begin=shard_begin, shard_count=shard_count, grads=grads, ws=ws,
-                           need_da=d["a"] is not None, need_db=d["b"] is not None, Z=Z, stream=stream)
+                           need_da=d["a"] is not None, need_db=d["b"] is not None, Z=Z, Hact=Hact, stream=stream)

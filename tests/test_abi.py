@@ -87,6 +87,9 @@ def test_mlp_workspace_size_is_host_only(L):
     (dict(Z=FAKE, dt=tp.TP_F32), tp.TP_ERR_DTYPE, "bf16 path only"),
     (dict(Z=FAKE + 4, act=tp.TP_ACT_SWIGLU, a=None), tp.TP_ERR_ALIGN, "Z is not 16-byte aligned"),
     (dict(Z=FAKE + 8), tp.TP_ERR_ALIGN, "Z is not 16-byte aligned"),
+    (dict(Hact=FAKE, dt=tp.TP_F32), tp.TP_ERR_DTYPE, "bf16 path only"),
+    (dict(Hact=FAKE, act=tp.TP_ACT_NONE), tp.TP_ERR_SHAPE, "intermediate is the pre-activation"),
+    (dict(Hact=FAKE + 8), tp.TP_ERR_ALIGN, "Hact is not 16-byte aligned"),
 ])
 def test_mlp_validation(L, kw, status, needle):
     d = _mlp(**kw)
@@ -264,6 +267,10 @@ def test_mlp_backward_workspace_size_is_host_only(L):
     (dict(shard_begin=3, shard_count=2), tp.TP_ERR_SHAPE, "shard range"),
     (dict(Z=FAKE + 4, act=tp.TP_ACT_SWIGLU, a=None, da=None), tp.TP_ERR_ALIGN, "Z is not 16-byte aligned"),
     (dict(Z=FAKE + 4), tp.TP_ERR_ALIGN, "Z is not 16-byte aligned"),
+    (dict(Hact=FAKE), tp.TP_ERR_SHAPE, "GELU and a stored Z only"),
+    (dict(Hact=FAKE, Z=FAKE, act=tp.TP_ACT_NONE), tp.TP_ERR_SHAPE, "GELU and a stored Z only"),
+    (dict(Hact=FAKE, Z=FAKE, act=tp.TP_ACT_SWIGLU, a=None, da=None), tp.TP_ERR_SHAPE, "GELU and a stored Z only"),
+    (dict(Hact=FAKE + 8, Z=FAKE), tp.TP_ERR_ALIGN, "Hact is not 16-byte aligned"),
 ])
 def test_mlp_backward_rejects_before_launch(L, kw, status, needle):
     d = _bwd(**kw)

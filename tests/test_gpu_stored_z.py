@@ -15,6 +15,10 @@ ABI (gfx950 GPU required).
   * A shard range writes its own columns of Z and no others.
   * SwiGLU: Z holds each shard's [gate | up] pre-activations; the same
     checks, with the backward bit for bit equal to the recomputing one.
+  * The stored activation (tp_mlp_desc.Hact / tp_mlp_bwd_desc.Hact): the
+    forward's output and Z keep their bits, H against the fp64 activation of
+    the fp64 pre-activation (one bf16 rounding), and a GELU backward that
+    reads it for dB keeps every other gradient's bits.
 """
 import sys
 
@@ -187,3 +191,66 @@ def test_stored_preactivation_swiglu(T, H, I, N):
         e = err(got[k], ref[k])
         say(f"  {k}: err={e:.3e}")
         assert e <= BF16_TOL, k
+
+
+# ------------------------------------------------------- stored activation
+@pytest.mark.parametrize("T,H,F,N,bias", [
+    (2048, 256, 4 * 128, 4, True),   # operands as stored, 128x128 dZ tiles: dZ alone, dB reads H
+    (256, 2304, 4 * 64, 4, True),    # operands as stored, 256x256 tiles
+    (264, 136, 4 * 72, 4, False),    # the backward transposes its operands: H^T instead of GELU(Z)^T
+])
+def test_stored_activation(T, H, F, N, bias):
+    """The forward also keeps its activated intermediate (tp_mlp_desc.Hact):
+    Y and Z keep their bits, H is GELU of the fp32 pre-activation rounded
+    once (against the fp64 GELU of X A^T + a), and the backward that takes it
+    for dB (tp_mlp_bwd_desc.Hact) leaves dX, dA, da and db bit for bit as
+    the Z-only backward has them, with dB within the bf16 bound."""
+    say(f"stored H T={T} H={H} F={F} N={N} bias={bias}")
+    h = _host(T, H, F, bias, seed=5 * T + H + F)
+    X, A, a, B, dY = (dev(h[k]) for k in ("X", "A", "a", "B", "dY"))
+    Z0 = torch.empty((T, F), dtype=torch.bfloat16, device=DEV)
+    Z1 = torch.empty_like(Z0)
+    Hh = torch.empty_like(Z0)
+    Y0, _ = tp.mlp_forward(X, A, a, B, None, N, Z=Z0)
+    Y1, _ = tp.mlp_forward(X, A, a, B, None, N, Z=Z1, Hact=Hh)
+    torch.cuda.synchronize()
+    assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
+    assert torch.equal(Z0.view(torch.int16), Z1.view(torch.int16))
+    href = O.gelu(_zref(h))
+    e = err(_np(Hh), href)
+    say(f"  H err={e:.3e}")
+    assert e <= Z_TOL
+
+    g0, _ = tp.mlp_backward(X, A, a, B, dY, N, need_da=bias, Z=Z0)
+    g1, _ = tp.mlp_backward(X, A, a, B, dY, N, need_da=bias, Z=Z0, Hact=Hh)
+    torch.cuda.synchronize()
+    for k in ("dX", "dA", "da", "db"):
+        if g0[k] is None:
+            assert g1[k] is None
+            continue
+        assert torch.equal(g0[k], g1[k]), f"{k}: changed by the stored activation"
+    ref = R.mlp_gelu_backward(h["X"], h["A"], h["a"], h["B"], h["dY"], act="gelu")
+    e = err(_np(g1["dB"]), ref["dB"])
+    say(f"  dB err={e:.3e}")
+    assert e <= BF16_TOL
+
+
+def test_stored_activation_swiglu_forward():
+    """SwiGLU forward with Hact: Y keeps its bits and H = SiLU(G) U (fp64
+    oracle, one bf16 rounding)."""
+    T, H, I, N = 264, 136, 4 * 40, 4
+    say(f"stored H swiglu forward T={T} H={H} I={I} N={N}")
+    h = _swiglu_host(T, H, I, seed=17)
+    A = dev(_fused_blocks(h["Wg"], h["Wu"], N))
+    X, Wd = dev(h["X"]), dev(h["Wd"])
+    Hh = torch.empty((T, I), dtype=torch.bfloat16, device=DEV)
+    Y0, _ = tp.mlp_forward(X, A, None, Wd, None, N, act=tp.TP_ACT_SWIGLU)
+    Y1, _ = tp.mlp_forward(X, A, None, Wd, None, N, act=tp.TP_ACT_SWIGLU, Hact=Hh)
+    torch.cuda.synchronize()
+    assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
+    x = h["X"].astype(np.float64)
+    g = x @ h["Wg"].astype(np.float64).T
+    u = x @ h["Wu"].astype(np.float64).T
+    e = err(_np(Hh), g / (1.0 + np.exp(-g)) * u)
+    say(f"  H err={e:.3e}")
+    assert e <= Z_TOL
